@@ -1,0 +1,195 @@
+"""fp64 CPU oracle for the Muon update and its Newton-Schulz orthogonalisation.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The GPU library never calls it
+and shares no code with it; it consumes the same seeded input bits and nothing
+else.
+
+What is computed, and where it comes from
+-----------------------------------------
+"Muon Meets Mamba: Spectral Optimization for State Space Models" (arXiv
+2608.03941, abstract): Muon orthogonalises the update of every weight matrix
+with a Newton-Schulz iteration, which amounts to steepest descent under the
+spectral norm.  "MuonSSM: Orthogonalizing State Space Models" (ICML 2026,
+method section "Newton-Schulz 轻量正交化") applies a light, single-step
+Newton-Schulz transform, with no explicit SVD, to low-rank value-key
+injections; its ablation ("Newton-Schulz 迭代次数") compares one step with
+five.  "An Isotropy-Preserving Spectral Cap for Muon" calls the same operation
+Muon's matrix-sign step.
+
+The pages leave the following open; the readings taken here are the plain ones
+(each is also listed in the design notes):
+
+* polynomial: odd polynomial p(x) = a x + b x^3 (+ c x^5), coefficients passed
+  in; the cubic (a, b) = (1.5, -0.5) is the default.  In matrix form one step
+  is X <- a X + b (X X^T) X + c (X X^T)(X X^T) X.
+* normalisation before the iteration: Frobenius, X0 = U / (||U||_F + eps), so
+  that every singular value of X0 is at most 1.
+* optimizer momentum (not stated on the pages): heavy-ball without dampening,
+  M' = beta M + G, with the Nesterov look-ahead U = G + beta M' (or U = M').
+* update: W' = W - lr * scale * O, O the orthogonalised update.
+* orientation: a tall matrix (m > n) is iterated as its transpose, so the Gram
+  matrix is formed on the short side; mathematically this is the same result.
+
+Everything runs in float64 with numpy; matrix products use numpy's matmul as a
+library primitive, with no blocking, fusion or reordering beyond the steps
+above.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+CUBIC = (1.5, -0.5)
+DEFAULT_EPS = 1e-7
+
+
+# ----------------------------------------------------------------------------
+# Exact widening of stored inputs
+# ----------------------------------------------------------------------------
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exact float64 values.
+
+    A bfloat16 number is the upper half of an IEEE binary32 number, so shifting
+    the 16 bits into the top of a 32-bit word gives the binary32 value exactly.
+    """
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def widen_f32(x: np.ndarray) -> np.ndarray:
+    """binary32 values -> exact float64 values."""
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Step 1-2: momentum buffer and the update direction
+# ----------------------------------------------------------------------------
+def momentum(M: np.ndarray, G: np.ndarray, beta: float) -> np.ndarray:
+    """New momentum buffer M' = beta * M + G (heavy-ball, no dampening)."""
+    return beta * M + G
+
+
+def update_direction(G: np.ndarray, M_new: np.ndarray, beta: float, nesterov: bool) -> np.ndarray:
+    """Direction fed to the orthogonalisation: G + beta * M' (Nesterov) or M'."""
+    return G + beta * M_new if nesterov else M_new
+
+
+# ----------------------------------------------------------------------------
+# Step 3-6: Newton-Schulz orthogonalisation of one matrix
+# ----------------------------------------------------------------------------
+def frobenius_normalize(X: np.ndarray, eps: float):
+    """X0 = X / (||X||_F + eps); returns (X0, nu) with nu = ||X||_F."""
+    nu = float(np.sqrt(np.sum(X * X)))
+    return X / (nu + eps), nu
+
+
+def step_coefficients(coeffs, steps: int, per_step: bool):
+    """List of (a, b, c) for every step; c = 0 for the cubic polynomial."""
+    c = np.asarray(coeffs, dtype=np.float64).ravel()
+    if per_step:
+        k = c.size // steps if steps else 0
+        rows = [c[i * k:(i + 1) * k] for i in range(steps)]
+    else:
+        rows = [c] * steps
+    out = []
+    for r in rows:
+        if r.size == 2:
+            out.append((float(r[0]), float(r[1]), 0.0))
+        elif r.size == 3:
+            out.append((float(r[0]), float(r[1]), float(r[2])))
+        else:
+            raise ValueError("each step needs 2 (cubic) or 3 (quintic) coefficients")
+    return out
+
+
+def ns_iterate(X: np.ndarray, steps: int, coeffs=CUBIC, per_step: bool = False) -> np.ndarray:
+    """Run `steps` Newton-Schulz steps on an already normalised s x l matrix X.
+
+    One step: A = X X^T (full s x s product), then
+    X <- a X + b (A X) + c (A (A X)).
+    """
+    for a, b, c in step_coefficients(coeffs, steps, per_step):
+        A = X @ X.T
+        AX = A @ X
+        Xn = a * X + b * AX
+        if c != 0.0:
+            Xn = Xn + c * (A @ AX)
+        X = Xn
+    return X
+
+
+def newton_schulz(U: np.ndarray, steps: int, coeffs=CUBIC, eps: float = DEFAULT_EPS,
+                  per_step: bool = False):
+    """Orthogonalise one m x n matrix; returns (O, nu).
+
+    The short side is made the row side (transpose when m > n), the matrix is
+    Frobenius-normalised, iterated, and transposed back.
+    """
+    U = np.asarray(U, dtype=np.float64)
+    tall = U.shape[0] > U.shape[1]
+    X = U.T if tall else U
+    X, nu = frobenius_normalize(X, eps)
+    X = ns_iterate(X, steps, coeffs, per_step)
+    return (X.T if tall else X), nu
+
+
+def ns_batched(X: np.ndarray, steps: int, coeffs=CUBIC, eps: float = DEFAULT_EPS,
+               per_step: bool = False) -> np.ndarray:
+    """Newton-Schulz on every matrix of a [batch, m, n] stack independently."""
+    X = np.asarray(X, dtype=np.float64)
+    out = np.empty_like(X)
+    for i in range(X.shape[0]):
+        out[i], _ = newton_schulz(X[i], steps, coeffs, eps, per_step)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Step 7: the whole optimizer step for one matrix
+# ----------------------------------------------------------------------------
+def muon_step(W, M, G, *, beta: float, lr: float, nesterov: bool = True, steps: int = 5,
+              coeffs=CUBIC, eps: float = DEFAULT_EPS, scale: float = 1.0, per_step: bool = False):
+    """One Muon step on one weight matrix.
+
+    Returns a dict with the new weight W', the new momentum M', the update O and
+    nu = ||U||_F of the direction before normalisation.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    M_new = momentum(M, G, beta)
+    U = update_direction(G, M_new, beta, nesterov)
+    O, nu = newton_schulz(U, steps, coeffs, eps, per_step)
+    W_new = W - lr * scale * O
+    return {"W": W_new, "M": M_new, "O": O, "nu": nu, "U": U}
+
+
+def muon_step_group(Ws, Ms, Gs, **kw):
+    """muon_step over a list of same-shape matrices (one parameter group)."""
+    return [muon_step(W, M, G, **kw) for W, M, G in zip(Ws, Ms, Gs)]
+
+
+# ----------------------------------------------------------------------------
+# Diagnostics (reported, never part of the update)
+# ----------------------------------------------------------------------------
+def orthogonality_error(O: np.ndarray) -> float:
+    """||X X^T - I_s||_F / sqrt(s) for the short-side orientation X of O."""
+    O = np.asarray(O, dtype=np.float64)
+    X = O.T if O.shape[0] > O.shape[1] else O
+    s = X.shape[0]
+    return float(np.linalg.norm(X @ X.T - np.eye(s)) / np.sqrt(s))
+
+
+def singular_values(O: np.ndarray) -> np.ndarray:
+    """Singular values, descending (LAPACK through numpy)."""
+    return np.linalg.svd(np.asarray(O, dtype=np.float64), compute_uv=False)
+
+
+def rel_frobenius(x: np.ndarray, ref: np.ndarray) -> float:
+    """||x - ref||_F / ||ref||_F (0 when both are zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(x - ref)
+    if den == 0.0:
+        return float(num)
+    return float(num / den)

@@ -1,0 +1,292 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+The pages print no worked numerical example of Muon or Newton-Schulz, so the
+oracle is pinned by hand-derived examples (tests/golden/worked_examples.json),
+closed forms on singular values, the polar factor from LAPACK's SVD,
+equivariances, and the low-rank structure of MuonSSM's injections.  Each pin
+is chosen so that a plausible slip in the oracle (a dropped or mis-signed
+polynomial term, a wrong normalisation, EMA instead of heavy-ball momentum, a
+missing Nesterov term, an ascent instead of a descent step, a transposed
+operand) fails at least one of them; test_planted_mistakes_are_caught checks
+that claim by planting those slips in copies of the oracle's steps.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as orc
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+
+
+def p_scalar(x, a=1.5, b=-0.5, c=0.0):
+    return a * x + b * x ** 3 + c * x ** 5
+
+
+def spectral_expected(U, s, V, steps, coeffs, eps):
+    """Closed form: NS_k(U diag(s) V^T) = U diag(p^k(s / (||s|| + eps))) V^T."""
+    x = np.asarray(s, dtype=np.float64) / (np.linalg.norm(s) + eps)
+    rows = coeffs if isinstance(coeffs[0], (tuple, list)) else [coeffs] * steps
+    for r in rows[:steps]:
+        x = p_scalar(x, *r)
+    return (U * x) @ V.T
+
+
+def haar(rng, n, k):
+    q, r = np.linalg.qr(rng.standard_normal((n, k)))
+    return q * np.sign(np.diag(r))
+
+
+# ---------------------------------------------------------------------------
+# Hand-derived examples
+# ---------------------------------------------------------------------------
+def test_worked_diag_example():
+    g = GOLD["diag_3x2"]
+    G = np.array(g["G"])
+    X0, nu = orc.frobenius_normalize(G, 0.0)
+    assert nu == g["nu"]
+    np.testing.assert_allclose(np.diag(X0[:, :2]), g["X0_diag"], rtol=0, atol=1e-15)
+    for k, key in ((1, "steps_1_diag"), (2, "steps_2_diag")):
+        O, _ = orc.newton_schulz(G, k, eps=0.0)
+        expect = np.zeros((2, 3))
+        expect[0, 0], expect[1, 1] = g[key]
+        np.testing.assert_allclose(O, expect, rtol=0, atol=1e-15)
+        # the tall orientation gives the transpose
+        Ot, _ = orc.newton_schulz(G.T, k, eps=0.0)
+        np.testing.assert_allclose(Ot, expect.T, rtol=0, atol=1e-15)
+
+
+def test_worked_momentum_example():
+    g = GOLD["momentum_2x2"]
+    M, G, beta = np.array(g["M"]), np.array(g["G"]), g["beta"]
+    Mn = orc.momentum(M, G, beta)
+    assert np.array_equal(Mn, np.array(g["M_new"]))
+    assert np.array_equal(orc.update_direction(G, Mn, beta, True), np.array(g["U_nesterov"]))
+    assert np.array_equal(orc.update_direction(G, Mn, beta, False), np.array(g["U_plain"]))
+    out = orc.muon_step(np.zeros((2, 2)), M, G, beta=beta, lr=0.0, steps=0, eps=0.0)
+    assert np.array_equal(out["M"], np.array(g["M_new"]))
+    assert np.array_equal(out["U"], np.array(g["U_nesterov"]))
+
+
+def test_worked_apply_example():
+    g = GOLD["apply_rank1"]
+    for steps in (0, 1, 5):
+        out = orc.muon_step(np.array(g["W"]), np.zeros((2, 2)), np.array(g["G"]), beta=g["beta"],
+                            lr=g["lr"], scale=g["scale"], steps=steps, eps=0.0)
+        np.testing.assert_allclose(out["O"], np.array(g["O"]), rtol=0, atol=1e-15)
+        np.testing.assert_allclose(out["W"], np.array(g["W_new"]), rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms on singular values
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n", [(24, 40), (40, 24), (16, 16)])
+@pytest.mark.parametrize("steps", [1, 3, 5, 8])
+def test_spectral_closed_form_cubic(m, n, steps):
+    rng = np.random.default_rng(100 + m + n + steps)
+    r = min(m, n)
+    U, V = haar(rng, m, r), haar(rng, n, r)
+    s = 10.0 ** (-3 * rng.random(r))
+    G = (U * s) @ V.T
+    O, nu = orc.newton_schulz(G, steps, eps=1e-7)
+    assert abs(nu - np.linalg.norm(s)) < 1e-12 * nu
+    np.testing.assert_allclose(O, spectral_expected(U, s, V, steps, (1.5, -0.5), 1e-7), atol=1e-12)
+
+
+def test_spectral_closed_form_quintic_and_per_step():
+    rng = np.random.default_rng(7)
+    m, n = 20, 36
+    U, V = haar(rng, m, m), haar(rng, n, m)
+    s = rng.uniform(0.05, 1.0, m)
+    G = (U * s) @ V.T
+    quint = (3.4445, -4.7750, 2.0315)
+    O, _ = orc.newton_schulz(G, 4, coeffs=quint, eps=0.0)
+    np.testing.assert_allclose(O, spectral_expected(U, s, V, 4, quint, 0.0), atol=1e-12)
+    per = [(1.5, -0.5, 0.0), (2.0, -1.5, 0.5), (1.2, -0.3, 0.1)]
+    O, _ = orc.newton_schulz(G, 3, coeffs=np.array(per).ravel(), eps=0.0, per_step=True)
+    np.testing.assert_allclose(O, spectral_expected(U, s, V, 3, per, 0.0), atol=1e-12)
+    per2 = [(1.5, -0.5), (1.875, -1.25)]
+    O, _ = orc.newton_schulz(G, 2, coeffs=np.array(per2).ravel(), eps=0.0, per_step=True)
+    np.testing.assert_allclose(O, spectral_expected(U, s, V, 2, per2, 0.0), atol=1e-12)
+
+
+def test_rank_one_fixed_point():
+    rng = np.random.default_rng(3)
+    u, v = rng.standard_normal(9), rng.standard_normal(14)
+    G = 37.5 * np.outer(u, v)
+    expect = np.outer(u, v) / (np.linalg.norm(u) * np.linalg.norm(v))
+    for steps in (0, 1, 5, 12):
+        O, _ = orc.newton_schulz(G, steps, eps=0.0)
+        np.testing.assert_allclose(O, expect, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Textbook routine: convergence to the polar factor
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n", [(6, 10), (10, 6), (8, 8)])
+def test_converges_to_polar_factor(m, n):
+    rng = np.random.default_rng(11 * m + n)
+    r = min(m, n)
+    U, V = haar(rng, m, r), haar(rng, n, r)
+    s = rng.uniform(1.0, 4.0, r)  # condition number <= 4
+    G = (U * s) @ V.T
+    O, _ = orc.newton_schulz(G, 30, eps=0.0)
+    Us, _, Vt = np.linalg.svd(G, full_matrices=False)
+    np.testing.assert_allclose(O, Us @ Vt, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+def test_normalisation_bounds():
+    rng = np.random.default_rng(5)
+    for shape in ((7, 30), (30, 7), (64, 128)):
+        X = rng.standard_normal(shape) * 100
+        X0, nu = orc.frobenius_normalize(X, 1e-7)
+        assert abs(np.linalg.norm(X0) - nu / (nu + 1e-7)) < 1e-14
+        assert np.linalg.svd(X0, compute_uv=False)[0] <= 1.0
+
+
+def test_equivariances():
+    rng = np.random.default_rng(9)
+    m, n, k = 12, 20, 5
+    G = rng.standard_normal((m, n))
+    O, _ = orc.newton_schulz(G, k, eps=0.0)
+    Q = haar(rng, m, m)
+    Qr = haar(rng, n, n)
+    np.testing.assert_allclose(orc.newton_schulz(Q @ G, k, eps=0.0)[0], Q @ O, atol=1e-13)
+    np.testing.assert_allclose(orc.newton_schulz(G @ Qr, k, eps=0.0)[0], O @ Qr, atol=1e-13)
+    np.testing.assert_allclose(orc.newton_schulz(G.T, k, eps=0.0)[0], O.T, atol=1e-14)
+    np.testing.assert_allclose(orc.newton_schulz(-G, k, eps=0.0)[0], -O, atol=1e-14)
+    np.testing.assert_allclose(orc.newton_schulz(3.7 * G, k, eps=0.0)[0], O, atol=1e-13)
+
+
+def test_condition_number_does_not_grow():
+    """'Muon Meets Mamba' (abstract): Muon lowers the condition number of the
+    projection it trains.  For the cubic on [0, 1], p(y)/p(x) <= y/x when x <= y,
+    so no Newton-Schulz step can raise sigma_max/sigma_min."""
+    rng = np.random.default_rng(13)
+    m, n = 16, 48
+    U, V = haar(rng, m, m), haar(rng, n, m)
+    s = 10.0 ** (-4 * rng.random(m))
+    G = (U * s) @ V.T
+    kappa = s.max() / s.min()
+    prev = kappa
+    for k in range(1, 9):
+        sv = np.linalg.svd(orc.newton_schulz(G, k, eps=0.0)[0], compute_uv=False)
+        assert sv[0] <= 1.0 + 1e-12
+        cur = sv[0] / sv[-1]
+        assert cur <= prev * (1 + 1e-9)
+        prev = cur
+    assert prev < kappa
+
+
+def test_null_space_preserved():
+    rng = np.random.default_rng(17)
+    m, n, r = 10, 18, 4
+    G = rng.standard_normal((m, r)) @ rng.standard_normal((r, n))
+    _, _, Vt = np.linalg.svd(G)
+    N = Vt[r:].T  # right null space
+    O, _ = orc.newton_schulz(G, 5, eps=1e-7)
+    assert np.abs(O @ N).max() < 1e-12
+    assert np.abs(N.T @ O.T @ np.ones(m)).max() < 1e-12
+
+
+def test_low_rank_injection_recurrence():
+    """MuonSSM's injections are sums of value-key outer products ("MuonSSM",
+    method section on momentum-augmented dynamics).  For X = V K^T every step
+    stays of the form V C K^T with an r x r core:
+    C0 = I / (nu + eps), nu^2 = tr((V^T V)(K^T K)),
+    C <- a C + b C (K^T K) C^T (V^T V) C."""
+    rng = np.random.default_rng(19)
+    V, K = rng.standard_normal((64, 8)), rng.standard_normal((128, 8))
+    X = V @ K.T
+    VtV, KtK = V.T @ V, K.T @ K
+    nu = np.sqrt(np.trace(VtV @ KtK))
+    for steps in (1, 3, 5):
+        C = np.eye(8) / (nu + 1e-7)
+        for _ in range(steps):
+            C = 1.5 * C - 0.5 * C @ KtK @ C.T @ VtV @ C
+        O, nu_o = orc.newton_schulz(X, steps, eps=1e-7)
+        assert abs(nu_o - nu) < 1e-10 * nu
+        np.testing.assert_allclose(O, V @ C @ K.T, atol=1e-12)
+    B = orc.ns_batched(np.stack([X, -2 * X, X.copy()]), 1)
+    np.testing.assert_allclose(B[1], -B[0], atol=1e-14)
+
+
+def test_zero_and_nan():
+    O, nu = orc.newton_schulz(np.zeros((4, 6)), 5)
+    assert nu == 0 and not O.any()
+    W = np.ones((4, 6))
+    out = orc.muon_step(W, np.zeros((4, 6)), np.zeros((4, 6)), beta=0.95, lr=0.02)
+    assert np.array_equal(out["W"], W)
+    G = np.ones((4, 6))
+    G[1, 2] = np.nan
+    assert np.isnan(orc.muon_step(W, np.zeros((4, 6)), G, beta=0.95, lr=0.02)["W"]).all()
+
+
+def test_widening_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x7F80, 0x0001, 0x4049, 0x7F7F], np.uint16)
+    vals = orc.widen_bf16(bits)
+    assert vals[0] == 1.0 and vals[1] == -1.0 and vals[2] == 0.0
+    assert np.signbit(vals[3]) and np.isinf(vals[4])
+    assert vals[5] == 2.0 ** -133
+    assert vals[6] == 3.140625
+    assert vals[7] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+# ---------------------------------------------------------------------------
+# Every planted slip must be caught by one of the pins above
+# ---------------------------------------------------------------------------
+def _ns_variant(U, steps, eps, slip):
+    U = np.asarray(U, dtype=np.float64)
+    tall = U.shape[0] > U.shape[1]
+    X = U.T if tall else U
+    nu = np.linalg.norm(X, 2) if slip == "spectral_norm" else np.sqrt(np.sum(X * X))
+    X = X / (nu + eps)
+    for _ in range(steps):
+        A = X @ X.T
+        if slip == "drop_b":
+            X = 1.5 * X
+        elif slip == "sign_b":
+            X = 1.5 * X + 0.5 * (A @ X)
+        elif slip == "transposed":
+            # Gram taken on the wrong side; it only type-checks for square X
+            X = 1.5 * X - 0.5 * ((X.T @ X) @ X)
+        else:
+            X = 1.5 * X - 0.5 * (A @ X)
+    return X.T if tall else X
+
+
+@pytest.mark.parametrize("slip", ["drop_b", "sign_b", "spectral_norm", "transposed"])
+def test_planted_mistakes_are_caught(slip):
+    g = GOLD["diag_3x2"]
+    G = np.array(g["G"])
+    expect = np.zeros((2, 3))
+    expect[0, 0], expect[1, 1] = g["steps_1_diag"]
+    assert np.allclose(_ns_variant(G, 1, 0.0, None), expect, atol=1e-15)
+    caught = False
+    if slip != "transposed":  # the wrong-side Gram does not type-check on a 2 x 3 matrix
+        caught = not np.allclose(_ns_variant(G, 1, 0.0, slip), expect, atol=1e-12)
+    rng = np.random.default_rng(1)
+    U, V = haar(rng, 9, 9), haar(rng, 9, 9)
+    s = rng.uniform(0.1, 1.0, 9)
+    Gs = (U * s) @ V.T  # square and not normal
+    closed = spectral_expected(U, s, V, 3, (1.5, -0.5), 0.0)
+    assert np.allclose(_ns_variant(Gs, 3, 0.0, None), closed, atol=1e-12)
+    caught = caught or not np.allclose(_ns_variant(Gs, 3, 0.0, slip), closed, atol=1e-12)
+    assert caught
+
+
+def test_planted_momentum_slips_are_caught():
+    g = GOLD["momentum_2x2"]
+    M, G, beta = np.array(g["M"]), np.array(g["G"]), g["beta"]
+    ema = beta * M + (1 - beta) * G
+    assert not np.array_equal(ema, np.array(g["M_new"]))
+    no_nesterov = ema
+    assert not np.array_equal(no_nesterov, np.array(g["U_nesterov"]))
+    a = GOLD["apply_rank1"]
+    ascent = np.array(a["W"]) + a["lr"] * a["scale"] * np.array(a["O"])
+    assert not np.allclose(ascent, np.array(a["W_new"]))
