@@ -1,0 +1,304 @@
+"""Benchmark of the Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_step]
+
+Default workload: one full Muon step over the Mamba-2-130M projection weights,
+24 out_proj (768 x 1536) + 24 in_proj (3352 x 768) matrices, bf16 gradients
+with singular values log-uniform in [1e-6, 1], fp32 weights and momentum,
+beta 0.95 Nesterov, lr 0.02, 5 cubic Newton-Schulz steps.  Inputs are seeded
+and synthetic (workloads.py) and resident in HBM before timing starts.
+
+Prints one JSON line: steps/s over exactly K timed steps (wall clock between
+two device synchronisations), per-kernel durations from HIP events recorded on
+the library's stream inside those same steps, the roofline of the dominant
+kernel, and the fp64 oracle timed on a bounded sample on the host cores.
+Other workloads (out_proj, in_proj, injections, single) are for exploration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Muon NS steps/s + TFLOP/s, MFMA util (Mamba-2-130M-shaped grads), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "spectral_optimizer_ssm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, files):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when none were taken or the kernel sources changed since."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = data.get(f"{kernel}@{workload}")
+    if not e or e.get("source_hash") != kernel_source_hash(files):
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# full Muon step (default)
+# ----------------------------------------------------------------------------
+def ns_flops(s, l):
+    """Algorithmic flops of one cubic step on an s x l iterate: symmetric Gram
+    s(s+1)l plus combine 2 s^2 l."""
+    return s * (s + 1) * l, 2 * s * s * l
+
+
+def bench_full_step(args, torch, mu, wl):
+    steps_ns = args.ns_steps
+    log(f"[bench] generating full-step inputs ({args.count}+{args.count} matrices)")
+    t0 = time.time()
+    w = wl.config4(count=args.count, steps=steps_ns)
+    log(f"[bench] generated in {time.time() - t0:.1f}s")
+    groups, devs = [], []
+    for g in w.groups:
+        G = torch.from_numpy(g.G.view(np.int16)).view(torch.bfloat16).cuda()
+        W = torch.from_numpy(g.W).cuda()
+        M = torch.from_numpy(g.M).cuda()
+        devs.append((G, W, M))
+        groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov))
+    ws = mu.muon_step(groups, steps=steps_ns)  # allocates the workspace once
+    torch.cuda.synchronize()
+    n_ev = sum(3 + 2 * steps_ns for _ in groups)
+
+    def make_events(k):
+        evs = []
+        for _ in range(k):
+            row = []
+            for _ in range(n_ev):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                row.append(e)
+            evs.append(row)
+        torch.cuda.synchronize()
+        return evs
+
+    for _ in range(args.warmup):
+        mu.muon_step(groups, steps=steps_ns, workspace=ws)
+    evs = make_events(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        mu.muon_step(groups, steps=steps_ns, workspace=ws, events=[e.cuda_event for e in evs[k]])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel durations from the events
+    dur = {"momentum": [], "gram": [], "combine": [], "apply": []}
+    per_group = []
+    for gi, g in enumerate(w.groups):
+        s, l = min(g.m, g.n), max(g.m, g.n)
+        per_group.append((g, s, l))
+    for k in range(args.steps):
+        row = evs[k]
+        base = 0
+        for gi, (g, s, l) in enumerate(per_group):
+            e = row[base:base + 3 + 2 * steps_ns]
+            dur["momentum"].append((gi, e[0].elapsed_time(e[1])))
+            for j in range(steps_ns):
+                dur["gram"].append((gi, e[1 + 2 * j].elapsed_time(e[2 + 2 * j])))
+                dur["combine"].append((gi, e[2 + 2 * j].elapsed_time(e[3 + 2 * j])))
+            dur["apply"].append((gi, e[-2].elapsed_time(e[-1])))
+            base += 3 + 2 * steps_ns
+
+    def flops_of(kind, gi):
+        g, s, l = per_group[gi]
+        fg, fc = ns_flops(s, l)
+        return g.count * (fg if kind == "gram" else fc)
+
+    def bytes_of(kind, gi):
+        g, s, l = per_group[gi]
+        per = 12 if kind == "momentum" else 10
+        return g.count * g.m * g.n * per
+
+    kernels = {}
+    for kind in ("gram", "combine"):
+        tot_ms = sum(d for _, d in dur[kind])
+        tot_f = sum(flops_of(kind, gi) for gi, _ in dur[kind])
+        n = len(dur[kind])
+        kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "flops_per_launch": tot_f / n,
+                         "tflops": tot_f / (tot_ms * 1e-3) / 1e12,
+                         "frac": tot_f / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    for kind in ("momentum", "apply"):
+        tot_ms = sum(d for _, d in dur[kind])
+        tot_b = sum(bytes_of(kind, gi) for gi, _ in dur[kind])
+        n = len(dur[kind])
+        kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "bytes_per_launch": tot_b / n,
+                         "gbs": tot_b / (tot_ms * 1e-3) / 1e9,
+                         "frac": tot_b / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    ns_ms = sum(d for _, d in dur["gram"]) / args.steps + sum(d for _, d in dur["combine"]) / args.steps
+    ns_flops_step = sum(sum(ns_flops(s, l)) * g.count for g, s, l in per_group) * steps_ns
+    ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
+
+    dom = "combine"
+    kd = kernels[dom]
+    roofline = {"bound": "mfma", "kernel": "combine_bf16_kernel", "achieved": round(kd["tflops"], 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kd["frac"], 4),
+                "traffic": measured_traffic("combine_bf16_kernel", "full_step", ["gemm_bf16.hip", "common.cuh"])}
+    result = {
+        "metric": METRIC, "value": round(1e3 / ms_per_step, 3), "unit": "steps/s",
+        "ms_per_step": round(ms_per_step, 4),
+        "ns_iters_per_s": round(steps_ns * 1e3 / ms_per_step, 2),
+        "ns_tflops": round(ns_tflops, 2), "mfma_util": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
+        "dtype": "bf16",
+        "config": {"workload": f"mamba2-130m-full-step: {args.count}x out_proj 768x1536 + "
+                               f"{args.count}x in_proj 3352x768, bf16 grads, fp32 W/M, "
+                               f"{steps_ns} cubic NS steps",
+                   "matrices": 2 * args.count, "ns_steps": steps_ns, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_full_step(w, steps_ns)
+    return result
+
+
+def cpu_baseline_full_step(w, steps_ns, budget_s=15.0):
+    """The fp64 oracle as it stands on a bounded sample: matrices alternately
+    from each group until ~budget_s of CPU work, scaled to one full step."""
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    times = {0: [], 1: []}
+    t_start = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_start < budget_s or not (times[0] and times[1]):
+        gi = i % 2
+        g = w.groups[gi]
+        j = (i // 2) % g.count
+        t0 = time.perf_counter()
+        orc.muon_step(orc.widen_f32(g.W[j]), orc.widen_f32(g.M[j]), orc.widen_bf16(g.G[j]), beta=w.beta,
+                      lr=w.lr, nesterov=w.nesterov, steps=steps_ns, eps=w.eps)
+        times[gi].append(time.perf_counter() - t0)
+        i += 1
+        if i >= 2 * min(g.count for g in w.groups):
+            break
+    t_step = sum(np.mean(times[gi]) * w.groups[gi].count for gi in (0, 1))
+    return {"value": round(1.0 / t_step, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times[0])} out_proj + {len(times[1])} in_proj matrices of the full step "
+                      f"(fp64 numpy, {steps_ns} NS steps), mean per-matrix time scaled to "
+                      f"{w.groups[0].count}+{w.groups[1].count} matrices"}
+
+
+# ----------------------------------------------------------------------------
+# exploration workloads
+# ----------------------------------------------------------------------------
+def bench_injections(args, torch, mu, wl):
+    X = wl.injections(batch=args.batch, device="cuda")
+    Y = torch.empty_like(X)
+    for _ in range(args.warmup):
+        mu.muon_ns_batched_small(X, Y, steps=args.ns_steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        mu.muon_ns_batched_small(X, Y, steps=args.ns_steps)
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = X.numel() * 2 * 2
+    gbs = nbytes / (kms * 1e-3) / 1e9
+    return {"metric": "MuonSSM batched single-step NS matrices/s", "value": round(args.batch / (ms * 1e-3), 1),
+            "unit": "matrices/s", "ms_per_step": round(ms, 4), "dtype": "bf16",
+            "config": {"workload": f"injections {args.batch}x64x128 bf16, {args.ns_steps} NS step"},
+            "roofline": {"bound": "hbm", "kernel": "ns_small_bf16_kernel<64,128>", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("ns_small_bf16_kernel", "injections", ["ns_small.hip",
+                                                                                              "common.cuh"])}}
+
+
+def bench_group(args, torch, mu, wl, which):
+    w = wl.config2() if which == "out_proj" else wl.config3() if which == "in_proj" else wl.config1()
+    groups = []
+    for g in w.groups:
+        G = (torch.from_numpy(g.G.view(np.int16)).view(torch.bfloat16) if g.grad_dtype == "bf16"
+             else torch.from_numpy(g.G)).cuda()
+        groups.append(mu.MuonGroup(W=torch.from_numpy(g.W).cuda(), M=torch.from_numpy(g.M).cuda(), G=G,
+                                   lr=w.lr, beta=w.beta))
+    prec = mu.MUON_BF16 if w.groups[0].grad_dtype == "bf16" else mu.MUON_F32
+    ws = mu.muon_step(groups, steps=args.ns_steps, precision=prec)
+    for _ in range(args.warmup):
+        mu.muon_step(groups, steps=args.ns_steps, precision=prec, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mu.muon_step(groups, steps=args.ns_steps, precision=prec, workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"metric": METRIC, "value": round(1e3 / ms, 3), "unit": "steps/s", "ms_per_step": round(ms, 4),
+            "dtype": "bf16" if prec == mu.MUON_BF16 else "f32", "config": {"workload": w.name}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="full_step",
+                    choices=["full_step", "out_proj", "in_proj", "injections", "single"])
+    ap.add_argument("--ns-steps", type=int, default=None)
+    ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
+    ap.add_argument("--batch", type=int, default=393216, help="injections batch")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the Muon step here has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.ns_steps is None:
+        args.ns_steps = 1 if args.workload == "injections" else 5
+    import torch
+    import spectral_optimizer_ssm_amd as mu
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mu.lib()
+    if args.workload == "full_step":
+        res = bench_full_step(args, torch, mu, wl)
+    elif args.workload == "injections":
+        res = bench_injections(args, torch, mu, wl)
+    else:
+        res = bench_group(args, torch, mu, wl, args.workload)
+    out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": res.pop("dtype"),
+           "data": "synthetic", "config": res.pop("config")}
+    out.update(res)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+"""ctypes binding of libmuon (include/muon.h), argument marshalling only.
+
+torch is used for device memory and streams: tensors are passed by pointer,
+the workspace is a torch byte tensor, and every call is enqueued on torch's
+current stream.  All arithmetic happens in the HIP kernels of libmuon.so; if
+that library is not built this module raises on first use (there is no CPU
+fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+MUON_F32, MUON_BF16 = 0, 1
+MUON_OK, MUON_EINVAL, MUON_EUNSUPPORTED, MUON_EWORKSPACE, MUON_EHIP = 0, -1, -2, -3, -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuon.so")
+_lib = None
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class NsCfg(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int), ("ncoef", ctypes.c_int),
+                ("coeffs", ctypes.POINTER(ctypes.c_float)), ("per_step", ctypes.c_int),
+                ("eps", ctypes.c_float), ("precision", ctypes.c_int)]
+
+
+class GroupC(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int), ("n", ctypes.c_int), ("count", ctypes.c_int),
+                ("grad_dtype", ctypes.c_int),
+                ("W", ctypes.POINTER(ctypes.c_void_p)), ("M", ctypes.POINTER(ctypes.c_void_p)),
+                ("G", ctypes.POINTER(ctypes.c_void_p)), ("O", ctypes.POINTER(ctypes.c_void_p)),
+                ("lr", ctypes.c_float), ("beta", ctypes.c_float), ("scale", ctypes.c_float),
+                ("nesterov", ctypes.c_int)]
+
+
+EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_timed", "muon_ns_workspace_size",
+           "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_status_string", "muon_version")
+
+
+def lib():
+    """Load libmuon.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmuon.so is not built ({LIB_PATH}); run "
+                           "`python -m spectral_optimizer_ssm_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.muon_step_workspace_size.argtypes = [ctypes.POINTER(GroupC), i, ctypes.POINTER(NsCfg)]
+    L.muon_step_workspace_size.restype = sz
+    L.muon_step.argtypes = [ctypes.POINTER(GroupC), i, ctypes.POINTER(NsCfg), vp, sz,
+                            ctypes.POINTER(f), vp]
+    L.muon_step.restype = i
+    L.muon_step_timed.argtypes = [ctypes.POINTER(GroupC), i, ctypes.POINTER(NsCfg), vp, sz,
+                                  ctypes.POINTER(f), vp, ctypes.POINTER(ctypes.c_void_p), i]
+    L.muon_step_timed.restype = i
+    L.muon_ns_workspace_size.argtypes = [i, i, i, i, ctypes.POINTER(NsCfg)]
+    L.muon_ns_workspace_size.restype = sz
+    L.muon_ns_orthogonalize.argtypes = [vp, vp, i, i, i, i, ctypes.POINTER(NsCfg), vp, sz, vp]
+    L.muon_ns_orthogonalize.restype = i
+    L.muon_ns_batched_small.argtypes = [vp, vp, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg), vp]
+    L.muon_ns_batched_small.restype = i
+    L.muon_status_string.argtypes = [i]
+    L.muon_status_string.restype = ctypes.c_char_p
+    L.muon_version.argtypes = []
+    L.muon_version.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().muon_status_string(int(status)).decode()
+
+
+def muon_version() -> int:
+    return int(lib().muon_version())
+
+
+def _check(rc: int, where: str):
+    if rc != MUON_OK:
+        raise MuonError(rc, where)
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    if t.dtype == torch.float32:
+        return MUON_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream) or None
+
+
+def make_cfg(steps: int = 5, coeffs=(1.5, -0.5), eps: float = 1e-7, precision: int = MUON_BF16,
+             per_step: bool = False):
+    """NsCfg plus the float array it points to (keep both alive)."""
+    flat = [float(c) for row in coeffs for c in (row if isinstance(row, (tuple, list)) else (row,))]
+    ncoef = len(coeffs[0]) if per_step else len(coeffs)
+    arr = (ctypes.c_float * max(1, len(flat)))(*flat)
+    cfg = NsCfg(int(steps), int(ncoef), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
+                int(bool(per_step)), float(eps), int(precision))
+    return cfg, arr
+
+
+def _ptrs(ts) -> ctypes.Array:
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _split(x) -> list:
+    """A [count, m, n] tensor or a sequence of [m, n] tensors -> list of matrices."""
+    if x is None:
+        return None
+    if hasattr(x, "dim") and x.dim() == 3:
+        return [x[i] for i in range(x.shape[0])]
+    return list(x)
+
+
+@dataclass
+class MuonGroup:
+    """One shape group.  W, M: float32; G: bf16 or float32; O: optional output.
+    Each is a [count, m, n] tensor or a list of [m, n] tensors, all contiguous
+    CUDA tensors."""
+    W: object
+    M: object
+    G: object
+    lr: float
+    beta: float
+    O: object = None
+    scale: float = 1.0
+    nesterov: bool = True
+
+
+def _marshal_groups(groups: Sequence[MuonGroup]):
+    keep, cgroups = [], []
+    for g in groups:
+        W, M, G, O = _split(g.W), _split(g.M), _split(g.G), _split(g.O)
+        m, n = W[0].shape
+        for t in W + M + G + (O or []):
+            if not t.is_contiguous() or tuple(t.shape) != (m, n):
+                raise ValueError("every matrix of a group must be a contiguous m x n tensor")
+        pw, pm, pg = _ptrs(W), _ptrs(M), _ptrs(G)
+        po = _ptrs(O) if O is not None else None
+        keep += [pw, pm, pg, po, W, M, G, O]
+        cgroups.append(GroupC(int(m), int(n), len(W), _dtype_code(G[0]),
+                              ctypes.cast(pw, ctypes.POINTER(ctypes.c_void_p)),
+                              ctypes.cast(pm, ctypes.POINTER(ctypes.c_void_p)),
+                              ctypes.cast(pg, ctypes.POINTER(ctypes.c_void_p)),
+                              ctypes.cast(po, ctypes.POINTER(ctypes.c_void_p)) if po is not None else None,
+                              float(g.lr), float(g.beta), float(g.scale), int(bool(g.nesterov))))
+    arr = (GroupC * len(cgroups))(*cgroups)
+    return arr, keep
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+def muon_step_workspace_size(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7,
+                             precision=MUON_BF16, per_step=False) -> int:
+    cg, keep = _marshal_groups(groups)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step)
+    return int(lib().muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
+
+
+def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7, precision=MUON_BF16,
+              per_step=False, workspace=None, norms_out=None, stream=None, events=None):
+    """One Muon step over every group (W and M updated in place).  Returns the
+    workspace tensor so that callers can reuse it.  `events`: optional list of
+    raw hipEvent_t handles (ints); when given, muon_step_timed records them at
+    the phase boundaries."""
+    import torch
+    L = lib()
+    cg, keep = _marshal_groups(groups)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step)
+    need = int(L.muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
+    if need == 0:
+        _check(MUON_EINVAL, "muon_step_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        dev = _split(groups[0].W)[0].device
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    nptr = ctypes.cast(ctypes.c_void_p(norms_out.data_ptr()), ctypes.POINTER(ctypes.c_float)) \
+        if norms_out is not None else None
+    if events is None:
+        rc = L.muon_step(cg, len(groups), ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()),
+                         workspace.numel(), nptr, _stream_handle(stream))
+        _check(rc, "muon_step")
+    else:
+        ev = (ctypes.c_void_p * len(events))(*events)
+        rc = L.muon_step_timed(cg, len(groups), ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel(), nptr, _stream_handle(stream),
+                               ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), len(events))
+        _check(rc, "muon_step_timed")
+    return workspace
+
+
+def muon_ns_workspace_size(m, n, batch, dtype, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=False) -> int:
+    cfg, arr = make_cfg(steps, coeffs, eps, dtype, per_step)
+    return int(lib().muon_ns_workspace_size(int(m), int(n), int(batch), int(dtype), ctypes.byref(cfg)))
+
+
+def muon_ns_orthogonalize(G, O, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=False, workspace=None,
+                          stream=None):
+    """O[b] = NS(G[b]) for contiguous [batch, m, n] (or [m, n]) tensors."""
+    import torch
+    L = lib()
+    G3 = G if G.dim() == 3 else G.unsqueeze(0)
+    O3 = O if O.dim() == 3 else O.unsqueeze(0)
+    if not (G3.is_contiguous() and O3.is_contiguous()) or G3.shape != O3.shape or G3.dtype != O3.dtype:
+        raise ValueError("G and O must be contiguous tensors of one shape and dtype")
+    b, m, n = G3.shape
+    dt = _dtype_code(G3)
+    cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step)
+    need = int(L.muon_ns_workspace_size(m, n, b, dt, ctypes.byref(cfg)))
+    if need == 0:
+        _check(MUON_EINVAL, "muon_ns_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=G.device)
+    rc = L.muon_ns_orthogonalize(ctypes.c_void_p(G3.data_ptr()), ctypes.c_void_p(O3.data_ptr()), dt, m, n, b,
+                                 ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 _stream_handle(stream))
+    _check(rc, "muon_ns_orthogonalize")
+    return workspace
+
+
+def muon_ns_batched_small(X, Y, steps=1, coeffs=(1.5, -0.5), eps=1e-7, per_step=False, stream=None):
+    """Y[b] = NS(X[b]) for a contiguous [batch, m, n] stack of small matrices."""
+    L = lib()
+    if X.dim() != 3 or not (X.is_contiguous() and Y.is_contiguous()) or X.shape != Y.shape or X.dtype != Y.dtype:
+        raise ValueError("X and Y must be contiguous [batch, m, n] tensors of one shape and dtype")
+    b, m, n = X.shape
+    dt = _dtype_code(X)
+    cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step)
+    rc = L.muon_ns_batched_small(ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()), dt, m, n, b,
+                                 ctypes.byref(cfg), _stream_handle(stream))
+    _check(rc, "muon_ns_batched_small")

@@ -1,0 +1,80 @@
+// Device helpers shared by the libmuon kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kMaxTable = 64;      // matrices per launch in a pointer table
+
+typedef uint16_t bf16_t;           // bfloat16 storage (raw bits)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Per-launch tables of user pointers (kernel arguments, no device copies).
+struct PtrTable {
+  const void* p[kMaxTable];
+};
+struct MutPtrTable {
+  void* p[kMaxTable];
+};
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Two floats -> two bfloat16 packed in one dword (hardware RNE convert).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float x) {
+  return static_cast<bf16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Deterministic wavefront sum (butterfly over 64 lanes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Deterministic block sum; every thread gets the result.  `red` holds at
+// least blockDim.x / 64 floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float t = 0.0f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// 1 / (||U||_F + eps) from the per-block partial sums of squares written by
+// the momentum pass; optionally returns nu = ||U||_F.
+__device__ __forceinline__ float inv_norm_from_partials(const float* part, int nparts, float eps,
+                                                        float* red, float* nu_out) {
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) s += part[i];
+  s = block_sum(s, red);
+  const float nu = sqrtf(s);
+  if (nu_out) *nu_out = nu;
+  return 1.0f / (nu + eps);
+}
+
+}  // namespace muon

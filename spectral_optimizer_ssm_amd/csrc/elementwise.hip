@@ -1,0 +1,371 @@
+// HBM-bound passes of the Muon step: the fused momentum / Nesterov /
+// Frobenius-partials pass that opens the step and the apply pass that closes
+// it.  The momentum rule is heavy-ball without dampening with the Nesterov
+// look-ahead, the plain reading taken for the optimizer momentum that
+// "Muon Meets Mamba" (abstract) leaves unstated; the descent step is the
+// "steepest descent under the spectral norm" of the same abstract.
+//
+// Both passes also move between the user's m x n layout and the oriented
+// iterate X (s x l, s = min(m, n)) that the Newton-Schulz kernels work on:
+// for a tall matrix X = U^T, transposed through an LDS tile so that global
+// reads and writes stay coalesced.  X is zero-padded to s_pad x ld.
+#include "common.cuh"
+#include "launch.h"
+
+namespace muon {
+
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+  __device__ static void load(const float* p, float* v) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  }
+  __device__ static void store(float* p, const float* v) {
+    f32x4_t a = {v[0], v[1], v[2], v[3]};
+    f32x4_t b = {v[4], v[5], v[6], v[7]};
+    *reinterpret_cast<f32x4_t*>(p) = a;
+    *reinterpret_cast<f32x4_t*>(p + 4) = b;
+  }
+};
+template <> struct Vec8<bf16_t> {
+  __device__ static void load(const bf16_t* p, float* v) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = lo_bf16(a[i]); v[2 * i + 1] = hi_bf16(a[i]); }
+  }
+  __device__ static void store(bf16_t* p, const float* v) {
+    u32x4_t a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4_t*>(p) = a;
+  }
+};
+
+template <typename T> __device__ __forceinline__ float ld1(const T* p);
+template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+template <typename T> __device__ __forceinline__ void st1(T* p, float v);
+template <> __device__ __forceinline__ void st1<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st1<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// M' = beta M + G;  U = G + beta M' (nesterov) or M';  no momentum: U = G.
+__device__ __forceinline__ float momentum1(float g, float* mp, bool has_m, float beta, bool nesterov) {
+  if (!has_m) return g;
+  const float mn = fmaf(beta, *mp, g);
+  *mp = mn;
+  return nesterov ? fmaf(beta, mn, g) : mn;
+}
+
+// ---------------------------------------------------------------------------
+// Wide matrices (m <= n): X = U, elementwise.  grid = (P, matrices).
+// ---------------------------------------------------------------------------
+template <typename GT, typename XT>
+__global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTable M, XT* X, long long xstride,
+                                                            int m, int n, int s_pad, int ld, float beta,
+                                                            int nesterov, float* partials, int P) {
+  __shared__ float red[8];
+  const int z = blockIdx.y;
+  const GT* g = static_cast<const GT*>(G.p[z]);
+  float* mm = static_cast<float*>(M.p[z]);
+  XT* x = X + z * xstride;
+  const bool has_m = mm != nullptr;
+  const bool nest = nesterov != 0;
+  const long long chunks = static_cast<long long>(s_pad) * (ld / 8);
+  const int cpr = ld / 8;
+  const bool vec = (n % 8) == 0;
+  float ss = 0.0f;
+  for (long long c = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+       c += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const int r = static_cast<int>(c / cpr);
+    const int c0 = static_cast<int>(c % cpr) * 8;
+    float u[8];
+    if (r < m && c0 < n && vec) {
+      float gv[8], mv[8];
+      const long long off = static_cast<long long>(r) * n + c0;
+      Vec8<GT>::load(g + off, gv);
+      if (has_m) Vec8<float>::load(mm + off, mv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u[j] = momentum1(gv[j], &mv[j], has_m, beta, nest);
+        ss = fmaf(u[j], u[j], ss);
+      }
+      if (has_m) Vec8<float>::store(mm + off, mv);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u[j] = 0.0f;
+        if (r < m && c0 + j < n) {
+          const long long off = static_cast<long long>(r) * n + c0 + j;
+          u[j] = momentum1(ld1<GT>(g + off), mm + off, has_m, beta, nest);
+          ss = fmaf(u[j], u[j], ss);
+        }
+      }
+    }
+    Vec8<XT>::store(x + static_cast<long long>(r) * ld + c0, u);
+  }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) partials[static_cast<long long>(z) * P + blockIdx.x] = ss;
+}
+
+// ---------------------------------------------------------------------------
+// Tall matrices (m > n): X = U^T through a 64 x 64 LDS tile.
+// grid = (tiles of X, matrices); P = tiles per matrix.
+// ---------------------------------------------------------------------------
+template <typename GT, typename XT>
+__global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTable M, XT* X, long long xstride,
+                                                            int m, int n, int s_pad, int ld, float beta,
+                                                            int nesterov, float* partials, int P) {
+  __shared__ float tile[64][65];
+  __shared__ float red[8];
+  const int z = blockIdx.y;
+  const GT* g = static_cast<const GT*>(G.p[z]);
+  float* mm = static_cast<float*>(M.p[z]);
+  XT* x = X + z * xstride;
+  const bool has_m = mm != nullptr;
+  const bool nest = nesterov != 0;
+  const int tiles_k = (ld + 63) / 64;
+  const int i0 = (blockIdx.x / tiles_k) * 64;  // X rows  = U columns (short side)
+  const int k0 = (blockIdx.x % tiles_k) * 64;  // X cols  = U rows    (long side)
+  const bool vec = (n % 8) == 0;
+  const int t = threadIdx.x;
+  float ss = 0.0f;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int kr = t / 8 + 32 * pass;
+    const int ic = (t % 8) * 8;
+    const int ur = k0 + kr, uc = i0 + ic;
+    float u[8];
+    if (ur < m && uc + 7 < n && vec) {
+      float gv[8], mv[8];
+      const long long off = static_cast<long long>(ur) * n + uc;
+      Vec8<GT>::load(g + off, gv);
+      if (has_m) Vec8<float>::load(mm + off, mv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u[j] = momentum1(gv[j], &mv[j], has_m, beta, nest);
+        ss = fmaf(u[j], u[j], ss);
+      }
+      if (has_m) Vec8<float>::store(mm + off, mv);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u[j] = 0.0f;
+        if (ur < m && uc + j < n) {
+          const long long off = static_cast<long long>(ur) * n + uc + j;
+          u[j] = momentum1(ld1<GT>(g + off), mm + off, has_m, beta, nest);
+          ss = fmaf(u[j], u[j], ss);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[kr][ic + j] = u[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int ir = t / 8 + 32 * pass;
+    const int kc = (t % 8) * 8;
+    if (i0 + ir < s_pad && k0 + kc < ld) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = tile[kc + j][ir];
+      Vec8<XT>::store(x + static_cast<long long>(i0 + ir) * ld + k0 + kc, v);
+    }
+  }
+  ss = block_sum(ss, red);
+  if (threadIdx.x == 0) partials[static_cast<long long>(z) * P + blockIdx.x] = ss;
+}
+
+// ---------------------------------------------------------------------------
+// Apply: O = X (or X^T), optionally scaled by 1/(nu+eps) when no Newton-Schulz
+// step ran; W -= lr*scale*O; optional copy of O to the user.
+// ---------------------------------------------------------------------------
+struct ApplyArgs {
+  const float* partials;  // non-null: scale X by 1/(nu+eps) (zero-step case)
+  int P;
+  float eps;
+  float neg_lr_scale;
+};
+
+__device__ __forceinline__ float apply_prologue(const ApplyArgs& a, int z, float* red) {
+  if (a.partials == nullptr) return 1.0f;
+  return inv_norm_from_partials(a.partials + static_cast<long long>(z) * a.P, a.P, a.eps, red, nullptr);
+}
+
+template <typename XT>
+__global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long xstride, int m, int n, int ld,
+                                                         MutPtrTable W, MutPtrTable O, ApplyArgs a) {
+  __shared__ float red[8];
+  const int z = blockIdx.y;
+  const XT* x = X + z * xstride;
+  float* w = static_cast<float*>(W.p[z]);
+  XT* o = static_cast<XT*>(O.p[z]);
+  const float inv = apply_prologue(a, z, red);
+  const int cpr = (n + 7) / 8;
+  const long long chunks = static_cast<long long>(m) * cpr;
+  const bool vec = (n % 8) == 0;
+  for (long long c = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+       c += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const int r = static_cast<int>(c / cpr);
+    const int c0 = static_cast<int>(c % cpr) * 8;
+    const long long off = static_cast<long long>(r) * n + c0;
+    if (vec) {
+      float ov[8], wv[8];
+      Vec8<XT>::load(x + static_cast<long long>(r) * ld + c0, ov);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ov[j] *= inv;
+      if (o) Vec8<XT>::store(o + off, ov);
+      if (w) {
+        Vec8<float>::load(w + off, wv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[j] = fmaf(a.neg_lr_scale, ov[j], wv[j]);
+        Vec8<float>::store(w + off, wv);
+      }
+    } else {
+      for (int j = 0; j < 8 && c0 + j < n; ++j) {
+        const float ov = ld1<XT>(x + static_cast<long long>(r) * ld + c0 + j) * inv;
+        if (o) st1<XT>(o + off + j, ov);
+        if (w) w[off + j] = fmaf(a.neg_lr_scale, ov, w[off + j]);
+      }
+    }
+  }
+}
+
+template <typename XT>
+__global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long xstride, int m, int n, int ld,
+                                                         MutPtrTable W, MutPtrTable O, ApplyArgs a) {
+  __shared__ float tile[64][65];
+  __shared__ float red[8];
+  const int z = blockIdx.y;
+  const XT* x = X + z * xstride;
+  float* w = static_cast<float*>(W.p[z]);
+  XT* o = static_cast<XT*>(O.p[z]);
+  const float inv = apply_prologue(a, z, red);
+  // tiles over U = X^T (m x n): rows k (long side), cols i (short side)
+  const int tiles_i = (n + 63) / 64;
+  const int k0 = (blockIdx.x / tiles_i) * 64;
+  const int i0 = (blockIdx.x % tiles_i) * 64;
+  const int t = threadIdx.x;
+  // read X rows i0.., cols k0.. (coalesced along k)
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int ir = t / 8 + 32 * pass;
+    const int kc = (t % 8) * 8;
+    float v[8];
+    if (i0 + ir < n && k0 + kc + 7 < ld) {
+      Vec8<XT>::load(x + static_cast<long long>(i0 + ir) * ld + k0 + kc, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[kc + j][ir] = v[j] * inv;
+  }
+  __syncthreads();
+  const bool vec = (n % 8) == 0;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int kr = t / 8 + 32 * pass;
+    const int ic = (t % 8) * 8;
+    const int ur = k0 + kr, uc = i0 + ic;
+    if (ur >= m) continue;
+    const long long off = static_cast<long long>(ur) * n + uc;
+    if (vec && uc + 7 < n) {
+      float ov[8], wv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ov[j] = tile[kr][ic + j];
+      if (o) Vec8<XT>::store(o + off, ov);
+      if (w) {
+        Vec8<float>::load(w + off, wv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[j] = fmaf(a.neg_lr_scale, ov[j], wv[j]);
+        Vec8<float>::store(w + off, wv);
+      }
+    } else {
+      for (int j = 0; j < 8 && uc + j < n; ++j) {
+        const float ov = tile[kr][ic + j];
+        if (o) st1<XT>(o + off + j, ov);
+        if (w) w[off + j] = fmaf(a.neg_lr_scale, ov, w[off + j]);
+      }
+    }
+  }
+}
+
+// nu per matrix from the partials (used for norms_out).
+__global__ void __launch_bounds__(256) norms_kernel(const float* partials, int P, float* out) {
+  __shared__ float red[8];
+  const int z = blockIdx.x;
+  float nu = 0.0f;
+  inv_norm_from_partials(partials + static_cast<long long>(z) * P, P, 0.0f, red, &nu);
+  if (threadIdx.x == 0) out[z] = nu;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+int momentum_blocks_per_matrix(bool tall, int s_pad, int ld) {
+  if (tall) return ((s_pad + 63) / 64) * ((ld + 63) / 64);
+  const long long chunks = static_cast<long long>(s_pad) * (ld / 8);
+  long long b = (chunks + 256 * 8 - 1) / (256 * 8);  // about 8 chunks per thread
+  if (b < 1) b = 1;
+  if (b > 1024) b = 1024;
+  return static_cast<int>(b);
+}
+
+hipError_t launch_momentum(const MomentumLaunch& L, hipStream_t st) {
+  const dim3 grid(L.P, L.count);
+  const dim3 block(256);
+#define MUON_MOM(GT, XT)                                                                            \
+  do {                                                                                              \
+    if (L.tall)                                                                                     \
+      hipLaunchKernelGGL((momentum_tall_kernel<GT, XT>), grid, block, 0, st, L.G, L.M,              \
+                         static_cast<XT*>(L.X), L.xstride, L.m, L.n, L.s_pad, L.ld, L.beta,         \
+                         L.nesterov, L.partials, L.P);                                              \
+    else                                                                                            \
+      hipLaunchKernelGGL((momentum_wide_kernel<GT, XT>), grid, block, 0, st, L.G, L.M,              \
+                         static_cast<XT*>(L.X), L.xstride, L.m, L.n, L.s_pad, L.ld, L.beta,         \
+                         L.nesterov, L.partials, L.P);                                              \
+  } while (0)
+  if (L.grad_bf16 && L.x_bf16) MUON_MOM(bf16_t, bf16_t);
+  else if (L.grad_bf16) MUON_MOM(bf16_t, float);
+  else if (L.x_bf16) MUON_MOM(float, bf16_t);
+  else MUON_MOM(float, float);
+#undef MUON_MOM
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(const ApplyLaunch& L, hipStream_t st) {
+  ApplyArgs a{L.partials, L.P, L.eps, L.neg_lr_scale};
+  const dim3 block(256);
+  if (L.tall) {
+    const dim3 grid(((L.m + 63) / 64) * ((L.n + 63) / 64), L.count);
+    if (L.x_bf16)
+      hipLaunchKernelGGL((apply_tall_kernel<bf16_t>), grid, block, 0, st, static_cast<const bf16_t*>(L.X),
+                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+    else
+      hipLaunchKernelGGL((apply_tall_kernel<float>), grid, block, 0, st, static_cast<const float*>(L.X),
+                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+  } else {
+    const long long chunks = static_cast<long long>(L.m) * ((L.n + 7) / 8);
+    long long b = (chunks + 256 * 8 - 1) / (256 * 8);
+    if (b < 1) b = 1;
+    if (b > 1024) b = 1024;
+    const dim3 grid(static_cast<unsigned>(b), L.count);
+    if (L.x_bf16)
+      hipLaunchKernelGGL((apply_wide_kernel<bf16_t>), grid, block, 0, st, static_cast<const bf16_t*>(L.X),
+                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+    else
+      hipLaunchKernelGGL((apply_wide_kernel<float>), grid, block, 0, st, static_cast<const float*>(L.X),
+                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_norms(const float* partials, int P, int count, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(norms_kernel, dim3(count), dim3(256), 0, st, partials, P, out);
+  return hipGetLastError();
+}
+
+}  // namespace muon

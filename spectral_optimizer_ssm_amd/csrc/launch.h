@@ -1,0 +1,87 @@
+// Internal interface between the C-ABI host code and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.cuh"
+
+namespace muon {
+
+// Fused momentum / Nesterov / Frobenius-partials pass (one launch covers up to
+// kMaxTable matrices of one shape group).
+struct MomentumLaunch {
+  PtrTable G;          // user gradients (m x n)
+  MutPtrTable M;       // user momentum (m x n, float), entries may be null: U = G
+  void* X;             // oriented iterate of the first matrix, s_pad x ld
+  long long xstride;   // elements between consecutive matrices of X
+  int m, n, s_pad, ld, count, P;
+  bool tall, grad_bf16, x_bf16;
+  float beta;
+  int nesterov;
+  float* partials;     // [count][P] sums of squares
+};
+
+struct ApplyLaunch {
+  const void* X;       // final iterate (oriented), s_pad x ld
+  long long xstride;
+  int m, n, ld, count;
+  bool tall, x_bf16;
+  MutPtrTable W;       // entries may be null (no apply)
+  MutPtrTable O;       // entries may be null (no copy-out); element type = X's
+  const float* partials;  // non-null: scale by 1/(nu+eps) (zero Newton-Schulz steps)
+  int P;
+  float eps;
+  float neg_lr_scale;
+};
+
+// One batched Newton-Schulz GEMM over `count` matrices of one shape, laid out
+// contiguously: X [count][s_pad][ld], A [count][s_pad][s_pad].
+struct NsGemmLaunch {
+  const void* X;       // iterate in
+  void* Y;             // iterate out (combine only)
+  void* A;             // Gram matrix (out for gram, in for combine)
+  long long xstride, astride;
+  int s_pad, ld, count;
+  // step-1 normalisation folded into the epilogues: when partials is non-null
+  // the Gram scales by inv^2 and the combine multiplies alpha, beta by inv,
+  // with inv = 1 / (sqrt(sum of partials) + eps).
+  const float* partials;
+  int P;
+  float eps;
+  float alpha, beta;   // combine coefficients (a, b)
+};
+
+int momentum_blocks_per_matrix(bool tall, int s_pad, int ld);
+hipError_t launch_momentum(const MomentumLaunch& L, hipStream_t st);
+hipError_t launch_apply(const ApplyLaunch& L, hipStream_t st);
+hipError_t launch_norms(const float* partials, int P, int count, float* out, hipStream_t st);
+
+// bf16 matrix-core path (tile multiples: s_pad % 128 == 0, ld % 128 == 0).
+constexpr int kTileS = 128;   // s_pad multiple for the bf16 tiled path
+constexpr int kTileL = 128;   // ld multiple for the bf16 tiled path
+hipError_t launch_gram_bf16(const NsGemmLaunch& L, hipStream_t st);
+hipError_t launch_combine_bf16(const NsGemmLaunch& L, hipStream_t st);
+
+// float32 path (tile multiples: s_pad % 64 == 0, ld % 64 == 0).
+constexpr int kTileF32 = 64;
+hipError_t launch_gram_f32(const NsGemmLaunch& L, hipStream_t st);
+hipError_t launch_combine_f32(const NsGemmLaunch& L, hipStream_t st);
+
+// Whole Newton-Schulz on chip for small matrices.
+struct NsSmallLaunch {
+  const void* X;       // [count] matrices, row stride ld_in
+  void* Y;             // [count] matrices, row stride ld_out
+  long long in_stride, out_stride;
+  int s, l, ld_in, ld_out;
+  long long count;
+  bool transposed;     // X stored as l x s (tall); the kernel orients it
+  int steps;
+  float a[64], b[64];  // per-step coefficients (passed by value)
+  const float* partials;  // non-null: nu from the momentum pass partials
+  int P;
+  float eps;
+};
+bool ns_small_supported(bool bf16, int s, int l);
+hipError_t launch_ns_small(const NsSmallLaunch& L, bool bf16, hipStream_t st);
+
+}  // namespace muon

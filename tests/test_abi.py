@@ -1,0 +1,122 @@
+"""The C-ABI library: it loads, exports every function include/muon.h declares,
+and rejects bad arguments before enqueueing anything (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+@pytest.fixture(scope="module")
+def mu():
+    import spectral_optimizer_ssm_amd as mu
+    if not os.path.exists(mu.binding.LIB_PATH):
+        pytest.fail("libmuon.so is not built: run python -m spectral_optimizer_ssm_amd.build")
+    mu.lib()
+    return mu
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(muon_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    for lang, comp in (("c", "gcc"), ("c++", "g++")):
+        src = tmp_path / f"t.{ 'c' if lang == 'c' else 'cpp'}"
+        src.write_text('#include "muon.h"\nint main(void){return muon_version()==MUON_VERSION?0:1;}\n')
+        r = subprocess.run([comp, "-fsyntax-only", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                            str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_exports_match_header(mu):
+    names = declared_functions()
+    assert set(names) == set(mu.binding.EXPORTS)
+    L = mu.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", mu.binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (muon_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_status(mu):
+    assert mu.muon_version() == 1
+    assert mu.status_string(0) == "ok"
+    assert "invalid" in mu.status_string(-1)
+    assert "unknown" in mu.status_string(7)
+
+
+def _cfg(mu, steps=5, coeffs=(1.5, -0.5), eps=1e-7, prec=None):
+    return mu.make_cfg(steps, coeffs, eps, mu.MUON_BF16 if prec is None else prec)
+
+
+def _group(mu, m=128, n=64, count=1, addr=0x100000, dtype=None, o=False):
+    W = (ctypes.c_void_p * count)(*[addr + 0x10000 * i for i in range(count)])
+    M = (ctypes.c_void_p * count)(*[addr + 0x1000000 + 0x10000 * i for i in range(count)])
+    G = (ctypes.c_void_p * count)(*[addr + 0x2000000 + 0x10000 * i for i in range(count)])
+    P = ctypes.POINTER(ctypes.c_void_p)
+    g = mu.binding.GroupC(m, n, count, mu.MUON_BF16 if dtype is None else dtype, ctypes.cast(W, P),
+                          ctypes.cast(M, P), ctypes.cast(G, P), None, 0.02, 0.95, 1.0, 1)
+    return g, (W, M, G)
+
+
+def test_workspace_queries(mu):
+    L = mu.lib()
+    cfg, keep = _cfg(mu)
+    g, k2 = _group(mu, 768, 1536, 24)
+    arr = (mu.binding.GroupC * 1)(g)
+    ws = L.muon_step_workspace_size(arr, 1, ctypes.byref(cfg))
+    # two bf16 iterates + Gram (768 x 768) + partials, padded
+    assert ws >= 24 * (2 * 768 * 1536 * 2 + 768 * 768 * 2)
+    assert L.muon_step_workspace_size(arr, 0, ctypes.byref(cfg)) == 0
+    assert L.muon_ns_workspace_size(768, 1536, 24, mu.MUON_BF16, ctypes.byref(cfg)) >= 24 * 2 * 768 * 1536 * 2
+    assert L.muon_ns_workspace_size(0, 1536, 24, mu.MUON_BF16, ctypes.byref(cfg)) == 0
+    assert L.muon_ns_workspace_size(8, 8, 1, 7, ctypes.byref(cfg)) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("steps_negative", -1), ("steps_too_many", -1), ("ncoef_4", -1), ("quintic_c", -2),
+    ("bad_precision", -1), ("null_groups", -1), ("misaligned", -1), ("null_matrix", -1),
+    ("no_workspace", -3), ("small_workspace", -3), ("bad_dtype", -1), ("negative_eps", -1),
+])
+def test_step_validation(mu, case, expect):
+    L = mu.lib()
+    cfg, keep = _cfg(mu, steps={"steps_negative": -1, "steps_too_many": 65}.get(case, 5),
+                     coeffs=(1.5, -0.5, 0.25) if case == "quintic_c" else (1.5, -0.5),
+                     eps=-1.0 if case == "negative_eps" else 1e-7,
+                     prec=9 if case == "bad_precision" else None)
+    if case == "ncoef_4":
+        cfg.ncoef = 4
+    g, k2 = _group(mu, dtype=5 if case == "bad_dtype" else None)
+    if case == "misaligned":
+        k2[0][0] = 0x100004
+    if case == "null_matrix":
+        k2[2][0] = None
+    arr = (mu.binding.GroupC * 1)(g)
+    ws_size = {"no_workspace": 0, "small_workspace": 64}.get(case, 1 << 40)
+    ws = None if case == "no_workspace" else ctypes.c_void_p(0x7000000)
+    grp = None if case == "null_groups" else arr
+    rc = L.muon_step(grp, 1, ctypes.byref(cfg), ws, ws_size, None, None)
+    assert rc == expect
+
+
+def test_small_and_ns_validation(mu):
+    L = mu.lib()
+    cfg, keep = _cfg(mu, steps=1)
+    x, y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)
+    assert L.muon_ns_batched_small(x, y, mu.MUON_BF16, 48, 128, 10, ctypes.byref(cfg), None) == -2
+    assert L.muon_ns_batched_small(x, y, mu.MUON_BF16, 128, 64, 10, ctypes.byref(cfg), None) == -2  # tall bf16
+    assert L.muon_ns_batched_small(x, x, mu.MUON_BF16, 64, 128, 10, ctypes.byref(cfg), None) == -1  # overlap
+    assert L.muon_ns_batched_small(x, y, mu.MUON_BF16, 64, 128, 0, ctypes.byref(cfg), None) == 0    # empty
+    cf32, k2 = _cfg(mu, steps=1, prec=mu.MUON_F32)
+    assert L.muon_ns_batched_small(x, y, mu.MUON_BF16, 64, 128, 1, ctypes.byref(cf32), None) == -2  # precision
+    assert L.muon_ns_orthogonalize(x, x, mu.MUON_BF16, 64, 128, 2, ctypes.byref(cfg), y, 1 << 30, None) == -1
+    assert L.muon_ns_orthogonalize(x, y, mu.MUON_BF16, 64, 128, 2, ctypes.byref(cfg), None, 0, None) == -3
+    assert L.muon_ns_orthogonalize(x, y, mu.MUON_BF16, 64, 128, 0, ctypes.byref(cfg), None, 0, None) == 0

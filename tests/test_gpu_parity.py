@@ -1,0 +1,294 @@
+"""GPU parity: libmuon (through its C ABI) against the fp64 oracle.
+
+Every case runs the HIP path on seeded synthetic inputs and compares it with
+oracle/muon_oracle.py on the same bits: O (the orthogonalised update) by
+relative Frobenius error (<= 1e-5 fp32, <= 2e-2 bf16 matrix cores), the
+momentum buffer (<= 1e-6) and the weight increment.  Full-size workloads are
+compared on sampled matrices (the oracle runs them one by one).
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+import workloads as wl
+from helpers import BF16_TOL, F32_TOL, compare_step, device_group, grad64, t64, to_torch_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def mu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import spectral_optimizer_ssm_amd as mu
+    mu.lib()  # raises if the HIP library is missing
+    return mu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[case] {request.node.nodeid}", flush=True)
+    yield
+
+
+def run_step(mu, w, precision=None, steps=None, want_o=True, coeffs=None, eps=None):
+    """Run one muon_step over all groups of a workload; returns (devs, outs)."""
+    devs, outs, groups = [], [], []
+    prec = precision if precision is not None else (mu.MUON_BF16 if w.groups[0].grad_dtype == "bf16" else mu.MUON_F32)
+    for g in w.groups:
+        d = device_group(g)
+        odt = torch.bfloat16 if prec == mu.MUON_BF16 else torch.float32
+        o = {"O": torch.full((g.count, g.m, g.n), float("nan"), dtype=odt, device="cuda")} if want_o else {"O": None}
+        devs.append(d)
+        outs.append(o)
+        groups.append(mu.MuonGroup(W=d["W"], M=d["M"], G=d["G"], O=o["O"], lr=w.lr, beta=w.beta,
+                                   scale=w.scale, nesterov=w.nesterov))
+    mu.muon_step(groups, steps=w.steps if steps is None else steps, coeffs=coeffs or w.coeffs,
+                 eps=w.eps if eps is None else eps, precision=prec)
+    torch.cuda.synchronize()
+    return devs, outs
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+def test_single_fp32_128x64(mu):
+    w = wl.config1()
+    devs, outs = run_step(mu, w)
+    res, _ = compare_step(w.groups[0], 0, outs[0], devs[0], w, F32_TOL)
+    print(res)
+
+
+def test_out_proj_group_full(mu):
+    w = wl.config2()
+    devs, outs = run_step(mu, w)
+    for i in (0, 13, 23):
+        res, _ = compare_step(w.groups[0], i, outs[0], devs[0], w, BF16_TOL)
+        print(i, res)
+
+
+def test_in_proj_group_full_tall(mu):
+    w = wl.config3()
+    devs, outs = run_step(mu, w)
+    for i in (0, 23):
+        res, _ = compare_step(w.groups[0], i, outs[0], devs[0], w, BF16_TOL)
+        print(i, res)
+
+
+@pytest.fixture(scope="module")
+def full_step_inputs():
+    return wl.config4()
+
+
+@pytest.mark.parametrize("steps", [1, 3, 5, 8])
+def test_full_mamba2_step(mu, full_step_inputs, steps):
+    w = full_step_inputs
+    devs, outs = run_step(mu, w, steps=steps)
+    for gi, g in enumerate(w.groups):
+        for i in (0, 17):
+            res, ref = compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL, steps=steps)
+            og = t64(outs[gi]["O"][i])
+            print(g.name, i, steps, res, "orth gpu %.4f oracle %.4f" % (orc.orthogonality_error(og),
+                                                                          orc.orthogonality_error(ref["O"])))
+
+
+def test_full_mamba2_step_zero_momentum_closed_form(mu):
+    """With M = 0, U = (1 + beta) G and G = U diag(s) V^T by construction, so
+    the oracle's update is the singular-value closed form; the GPU must match
+    the oracle, and the oracle the closed form (up to the bf16 rounding of G)."""
+    w = wl.config4(count=2, zero_momentum=True)
+    devs, outs = run_step(mu, w)
+    for gi, g in enumerate(w.groups):
+        for i in range(2):
+            compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL)
+
+
+def _injection_oracle(X, steps=1):
+    return orc.ns_batched(X.float().cpu().numpy().astype(np.float64), steps)
+
+
+def test_injections_reduced_all_matrices(mu):
+    X = wl.injections(batch=4096, device="cuda")
+    Y = torch.empty_like(X)
+    mu.muon_ns_batched_small(X, Y, steps=1)
+    torch.cuda.synchronize()
+    ref = _injection_oracle(X, 1)
+    Yd = t64(Y)
+    errs = np.array([orc.rel_frobenius(Yd[b], ref[b]) for b in range(X.shape[0])])
+    print("max rel", errs.max(), "mean", errs.mean())
+    assert errs.max() <= BF16_TOL
+
+
+def test_injections_full_size_sampled(mu):
+    X = wl.injections(device="cuda")
+    assert X.shape[0] == 393216
+    Y = torch.empty_like(X)
+    mu.muon_ns_batched_small(X, Y, steps=1)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2024)
+    idx = np.unique(np.concatenate([[0, X.shape[0] - 1], rng.integers(0, X.shape[0], 1024)]))
+    it = torch.from_numpy(idx).cuda()
+    ref = _injection_oracle(X[it], 1)
+    Yd = t64(Y[it])
+    errs = np.array([orc.rel_frobenius(Yd[k], ref[k]) for k in range(len(idx))])
+    print("sampled", len(idx), "max rel", errs.max())
+    assert errs.max() <= BF16_TOL
+    assert torch.isfinite(Y.float()).all()
+
+
+@pytest.mark.parametrize("steps", [0, 1, 3, 5])
+@pytest.mark.parametrize("shape", [(64, 128), (32, 96), (64, 64), (32, 256)])
+def test_batched_small_bf16_shapes(mu, shape, steps):
+    m, n = shape
+    g = wl.random_group(7 + m + n, 37, m, n, "bf16")
+    X = to_torch_bits(g.G).cuda()
+    Y = torch.empty_like(X)
+    mu.muon_ns_batched_small(X, Y, steps=steps)
+    torch.cuda.synchronize()
+    Yd = t64(Y)
+    for b in (0, 18, 36):
+        ref, _ = orc.newton_schulz(grad64(g, b), steps)
+        assert orc.rel_frobenius(Yd[b], ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("shape", [(128, 64), (64, 128), (40, 200), (200, 40), (7, 33)])
+def test_batched_small_fp32(mu, shape):
+    m, n = shape
+    g = wl.random_group(11 + m, 5, m, n, "f32")
+    X = torch.from_numpy(g.G).cuda()
+    Y = torch.empty_like(X)
+    mu.muon_ns_batched_small(X, Y, steps=5)
+    torch.cuda.synchronize()
+    Yd = t64(Y)
+    for b in range(5):
+        ref, _ = orc.newton_schulz(grad64(g, b), 5)
+        assert orc.rel_frobenius(Yd[b], ref) <= F32_TOL
+
+
+# ---------------------------------------------------------------------------
+# ragged shapes, both engines, both precisions
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(200, 130), (96, 300), (130, 130), (1, 70), (300, 1), (256, 512),
+                                   (64, 128), (128, 64), (513, 129)])
+def test_ragged_bf16(mu, shape):
+    m, n = shape
+    g = wl.random_group(100 + m + n, 3, m, n, "bf16")
+    w = wl.Workload(f"ragged{m}x{n}", [g])
+    devs, outs = run_step(mu, w)
+    for i in range(3):
+        compare_step(g, i, outs[0], devs[0], w, BF16_TOL)
+
+
+@pytest.mark.parametrize("shape", [(100, 150), (150, 100), (64, 64), (65, 300), (128, 64)])
+def test_ragged_fp32(mu, shape):
+    m, n = shape
+    g = wl.random_group(200 + m + n, 2, m, n, "f32")
+    w = wl.Workload(f"ragged{m}x{n}", [g])
+    devs, outs = run_step(mu, w)
+    for i in range(2):
+        compare_step(g, i, outs[0], devs[0], w, F32_TOL)
+
+
+def test_bf16_gradients_fp32_iterate(mu):
+    g = wl.random_group(5, 2, 96, 160, "bf16")
+    w = wl.Workload("mixed", [g])
+    devs, outs = run_step(mu, w, precision=mu.MUON_F32)
+    for i in range(2):
+        compare_step(g, i, outs[0], devs[0], w, F32_TOL)
+
+
+def test_many_matrices_multiple_tables(mu):
+    g = wl.random_group(9, 70, 64, 96, "bf16")  # more than one pointer table
+    w = wl.Workload("many", [g])
+    devs, outs = run_step(mu, w)
+    for i in (0, 63, 64, 69):
+        compare_step(g, i, outs[0], devs[0], w, BF16_TOL)
+
+
+# ---------------------------------------------------------------------------
+# degenerate inputs and invariants
+# ---------------------------------------------------------------------------
+def test_zero_gradient_leaves_weights(mu):
+    g = wl.random_group(1, 2, 256, 384, "bf16", zero_momentum=True)
+    g.G[:] = 0
+    w = wl.Workload("zero", [g])
+    devs, outs = run_step(mu, w)
+    assert torch.equal(devs[0]["W"].cpu(), torch.from_numpy(g.W))
+    assert (outs[0]["O"].float() == 0).all()
+
+
+def test_nan_propagates(mu):
+    g = wl.random_group(2, 1, 128, 256, "bf16")
+    g.G[0, 3, 5] = 0x7FC0
+    w = wl.Workload("nan", [g])
+    devs, outs = run_step(mu, w)
+    assert torch.isnan(devs[0]["W"]).all()
+
+
+def test_transpose_equivariance(mu):
+    g = wl.random_group(3, 2, 256, 640, "bf16", zero_momentum=True)
+    G = to_torch_bits(g.G).cuda()
+    O1 = torch.empty_like(G)
+    mu.muon_ns_orthogonalize(G, O1, steps=5)
+    Gt = G.transpose(1, 2).contiguous()
+    O2 = torch.empty_like(Gt)
+    mu.muon_ns_orthogonalize(Gt, O2, steps=5)
+    torch.cuda.synchronize()
+    for i in range(2):
+        a, b = t64(O1[i]), t64(O2[i]).T
+        assert orc.rel_frobenius(a, b) <= BF16_TOL
+        ref, _ = orc.newton_schulz(grad64(g, i), 5)
+        assert orc.rel_frobenius(a, ref) <= BF16_TOL
+
+
+def test_ns_orthogonalize_matches_oracle(mu):
+    for m, n, dt in ((768, 1536, "bf16"), (3352, 768, "bf16"), (96, 200, "f32")):
+        g = wl.random_group(m + n, 2, m, n, dt)
+        G = (to_torch_bits(g.G) if dt == "bf16" else torch.from_numpy(g.G)).cuda()
+        O = torch.empty_like(G)
+        mu.muon_ns_orthogonalize(G, O, steps=5)
+        torch.cuda.synchronize()
+        for i in range(2):
+            ref, _ = orc.newton_schulz(grad64(g, i), 5)
+            assert orc.rel_frobenius(t64(O[i]), ref) <= (BF16_TOL if dt == "bf16" else F32_TOL)
+
+
+def test_deterministic(mu):
+    w = wl.config2(count=3)
+    d1, o1 = run_step(mu, w)
+    d2, o2 = run_step(mu, w)
+    assert torch.equal(o1[0]["O"], o2[0]["O"])
+    assert torch.equal(d1[0]["W"], d2[0]["W"])
+    assert torch.equal(d1[0]["M"], d2[0]["M"])
+
+
+def test_norms_out_and_resume(mu):
+    g = wl.random_group(4, 3, 200, 300, "bf16")
+    d = device_group(g)
+    norms = torch.zeros(3, device="cuda")
+    grp = mu.MuonGroup(W=d["W"], M=d["M"], G=d["G"], lr=0.02, beta=0.95)
+    mu.muon_step([grp], steps=5, norms_out=norms)
+    torch.cuda.synchronize()
+    for i in range(3):
+        U = orc.update_direction(grad64(g, i), orc.momentum(orc.widen_f32(g.M[i]), grad64(g, i), 0.95), 0.95, True)
+        assert abs(norms[i].item() - np.linalg.norm(U)) <= 1e-5 * np.linalg.norm(U)
+    # resume: saving and restoring W, M between two steps equals running on
+    W1, M1 = d["W"].clone(), d["M"].clone()
+    mu.muon_step([grp], steps=5)
+    torch.cuda.synchronize()
+    W2a = d["W"].clone()
+    d["W"].copy_(W1)
+    d["M"].copy_(M1)
+    mu.muon_step([grp], steps=5)
+    torch.cuda.synchronize()
+    assert torch.equal(d["W"], W2a)
+
+
+def test_two_groups_one_call(mu):
+    w = wl.config4(count=3, out_shape=(128, 256), in_shape=(400, 128))
+    devs, outs = run_step(mu, w)
+    for gi, g in enumerate(w.groups):
+        for i in range(3):
+            compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL)
