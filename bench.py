@@ -83,7 +83,11 @@ def bench_full_step(args, torch, mu, wl):
         groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov))
     ws = mu.muon_step(groups, steps=steps_ns)  # allocates the workspace once
     torch.cuda.synchronize()
-    n_ev = sum(3 + 2 * steps_ns for _ in groups)
+    ng = len(groups)
+    # event order recorded by muon_step_timed for this schedule: start,
+    # after each group's momentum pass, after every grouped Gram and combine
+    # launch (one pair per NS step), after each group's apply pass
+    n_ev = 1 + ng + 2 * steps_ns + ng
 
     def make_events(k):
         evs = []
@@ -108,42 +112,33 @@ def bench_full_step(args, torch, mu, wl):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # per-kernel durations from the events
+    per_group = [(g, min(g.m, g.n), max(g.m, g.n)) for g in w.groups]
+    gram_f = sum(g.count * ns_flops(s, l)[0] for g, s, l in per_group)
+    comb_f = sum(g.count * ns_flops(s, l)[1] for g, s, l in per_group)
     dur = {"momentum": [], "gram": [], "combine": [], "apply": []}
-    per_group = []
-    for gi, g in enumerate(w.groups):
-        s, l = min(g.m, g.n), max(g.m, g.n)
-        per_group.append((g, s, l))
     for k in range(args.steps):
-        row = evs[k]
-        base = 0
-        for gi, (g, s, l) in enumerate(per_group):
-            e = row[base:base + 3 + 2 * steps_ns]
-            dur["momentum"].append((gi, e[0].elapsed_time(e[1])))
-            for j in range(steps_ns):
-                dur["gram"].append((gi, e[1 + 2 * j].elapsed_time(e[2 + 2 * j])))
-                dur["combine"].append((gi, e[2 + 2 * j].elapsed_time(e[3 + 2 * j])))
-            dur["apply"].append((gi, e[-2].elapsed_time(e[-1])))
-            base += 3 + 2 * steps_ns
-
-    def flops_of(kind, gi):
-        g, s, l = per_group[gi]
-        fg, fc = ns_flops(s, l)
-        return g.count * (fg if kind == "gram" else fc)
+        e = evs[k]
+        for gi in range(ng):
+            dur["momentum"].append((gi, e[gi].elapsed_time(e[gi + 1])))
+        for j in range(steps_ns):
+            a = ng + 2 * j
+            dur["gram"].append((-1, e[a].elapsed_time(e[a + 1])))
+            dur["combine"].append((-1, e[a + 1].elapsed_time(e[a + 2])))
+        b = ng + 2 * steps_ns
+        for gi in range(ng):
+            dur["apply"].append((gi, e[b + gi].elapsed_time(e[b + gi + 1])))
 
     def bytes_of(kind, gi):
         g, s, l = per_group[gi]
-        per = 12 if kind == "momentum" else 10
-        return g.count * g.m * g.n * per
+        return g.count * g.m * g.n * (12 if kind == "momentum" else 10)
 
     kernels = {}
-    for kind in ("gram", "combine"):
+    for kind, fl in (("gram", gram_f), ("combine", comb_f)):
         tot_ms = sum(d for _, d in dur[kind])
-        tot_f = sum(flops_of(kind, gi) for gi, _ in dur[kind])
         n = len(dur[kind])
-        kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "flops_per_launch": tot_f / n,
-                         "tflops": tot_f / (tot_ms * 1e-3) / 1e12,
-                         "frac": tot_f / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "flops_per_launch": float(fl),
+                         "tflops": fl * n / (tot_ms * 1e-3) / 1e12,
+                         "frac": fl * n / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     for kind in ("momentum", "apply"):
         tot_ms = sum(d for _, d in dur[kind])
         tot_b = sum(bytes_of(kind, gi) for gi, _ in dur[kind])

@@ -33,7 +33,9 @@
  *
  * Layout.  Every matrix is row-major, contiguous, m rows of n elements
  * (PyTorch's (out, in) layout for a Linear weight).  Device pointers must be
- * 16-byte aligned.  bfloat16 data is passed as 16-bit storage (uint16 bits).
+ * aligned to their element size (muon_ns_batched_small with bfloat16: 16
+ * bytes); 16-byte aligned matrices with n % 8 == 0 take vectorised paths.
+ * bfloat16 data is passed as 16-bit storage (uint16 bits).
  *
  * Ownership and asynchrony.  The caller owns every buffer, including the
  * workspace; the library never allocates device memory and keeps no state

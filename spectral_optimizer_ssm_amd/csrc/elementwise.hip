@@ -43,6 +43,8 @@ template <> struct Vec8<bf16_t> {
   }
 };
 
+__device__ __forceinline__ bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 template <typename T> __device__ __forceinline__ float ld1(const T* p);
 template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
@@ -74,7 +76,7 @@ __global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTa
   const bool nest = nesterov != 0;
   const long long chunks = static_cast<long long>(s_pad) * (ld / 8);
   const int cpr = ld / 8;
-  const bool vec = (n % 8) == 0;
+  const bool vec = (n % 8) == 0 && a16(g) && (!has_m || a16(mm));
   float ss = 0.0f;
   for (long long c = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
        c += static_cast<long long>(gridDim.x) * blockDim.x) {
@@ -128,7 +130,7 @@ __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTa
   const int tiles_k = (ld + 63) / 64;
   const int i0 = (blockIdx.x / tiles_k) * 64;  // X rows  = U columns (short side)
   const int k0 = (blockIdx.x % tiles_k) * 64;  // X cols  = U rows    (long side)
-  const bool vec = (n % 8) == 0;
+  const bool vec = (n % 8) == 0 && a16(g) && (!has_m || a16(mm));
   const int t = threadIdx.x;
   float ss = 0.0f;
 #pragma unroll
@@ -205,7 +207,7 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
   const float inv = apply_prologue(a, z, red);
   const int cpr = (n + 7) / 8;
   const long long chunks = static_cast<long long>(m) * cpr;
-  const bool vec = (n % 8) == 0;
+  const bool vec = (n % 8) == 0 && (!w || a16(w)) && (!o || a16(o));
   for (long long c = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
        c += static_cast<long long>(gridDim.x) * blockDim.x) {
     const int r = static_cast<int>(c / cpr);
@@ -264,7 +266,7 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
     for (int j = 0; j < 8; ++j) tile[kc + j][ir] = v[j] * inv;
   }
   __syncthreads();
-  const bool vec = (n % 8) == 0;
+  const bool vec = (n % 8) == 0 && (!w || a16(w)) && (!o || a16(o));
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int kr = t / 8 + 32 * pass;

@@ -1,305 +1,352 @@
-// Newton-Schulz matrix products on the gfx950 matrix cores, bf16 inputs and
+// Newton-Schulz matrix products on the gfx950 matrix cores: bf16 inputs,
 // fp32 accumulation (v_mfma_f32_32x32x16_bf16).
 //
 // "Muon Meets Mamba" (abstract) orthogonalises each weight update with a
 // Newton-Schulz iteration; "MuonSSM" (section on convergence and complexity)
-// notes that its matrix products are the constant-factor cost of the method.
-// One cubic step on the oriented iterate X (s x l, s <= l) is
-//     A = X X^T            (symmetric Gram, s x s)        -> gram kernel
-//     X' = a X + b A X     (polynomial combine, s x l)    -> combine kernel
-// The Gram kernel computes only tiles on or above the diagonal and writes
-// each one twice (in place and mirrored).  The combine kernel fuses the
-// a X + b (.) epilogue.  On the first step the Frobenius normalisation is
-// folded in: the Gram scales by 1/(nu+eps)^2, the combine's a and b by
-// 1/(nu+eps), nu re-reduced from the momentum pass's per-block partials.
+// notes that its matrix products are the method's constant-factor cost.  One
+// cubic step on the oriented iterate X (s x l, s <= l) is
+//     X' = a X + b (X X^T) X = A' X,   A' = a I + b X X^T   (symmetric)
+// computed as two launches:
+//   gram    : A' = alpha I + beta X X^T, only tiles on or above the diagonal,
+//             each stored in place and mirrored;
+//   combine : Y  = A' X, a plain product.
+// On the first step X holds the unnormalised U and the Frobenius
+// normalisation is folded in: alpha = a / (nu + eps), beta = b / (nu + eps)^3,
+// with nu re-reduced from the momentum pass's per-block partial sums.
 //
-// Layout: X [count][s_pad][ld] and A [count][s_pad][s_pad], bf16, row-major,
-// zero-padded so every tile is full (s_pad % 128 == 0, ld % 128 == 0); the
-// padding stays zero through every step because padded rows and columns of A
-// are zero.
+// Layout: X [count][s_pad][ld], A' [count][s_pad][s_pad], bf16 row-major,
+// s_pad % 256 == 0, ld % 256 == 0, zero padding (stays zero: padded rows and
+// columns of A' are zero).  The Gram's contraction stops at kdim, the first
+// multiple of 64 >= l.
 //
-// Main loop: 128 x 128 workgroup tile, BK = 64, four waves of 64 x 64 (2 x 2
-// MFMA blocks of 32 x 32), global -> registers -> LDS double buffering with
-// one barrier per K-tile.  LDS rows are 128 B (64 bf16); 16-byte chunks are
-// XOR-swizzled by (row >> 1) & 7 so that the fragment reads of 16 lanes cover
-// all 64 banks.
+// Tiling: 256 x 256 workgroup tile, four waves of 128 x 128 (4 x 4 MFMA blocks
+// of 32 x 32), BK = 64, two LDS stages of 64 KB filled by
+// global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane, so a
+// wave writes 1 KB of LDS per instruction; the global address each lane
+// fetches implements the swizzle).
+//  * K-contiguous operands (rows of X in the Gram, rows of A' in the combine)
+//    sit as [256 rows][64 K] with 16-byte chunks XOR-swizzled by (row>>1)&7
+//    and are read as ds_read_b128 fragments.
+//  * The combine's X operand is contracted over X's row index: it sits
+//    row-major as [64 rows j][256 columns k] (chunks swizzled by 4*(j&3)) and
+//    its fragments come from ds_read_b64_tr_b16: 16 lanes each address 4
+//    elements of a 4 x 16 block and every lane receives one column's 4
+//    consecutive rows, exactly the MFMA operand layout.
+// The MFMA's M side is X's column index in the combine, so each lane ends up
+// with 4 consecutive columns of one output row (8-byte stores).
+//
+// Work distribution: one launch covers every shape group of the step
+// (segments).  Workgroups are dealt to the 8 XCDs round-robin by hardware;
+// each segment's tiles are cut into 8 contiguous shares and XCD x runs share x
+// of every segment, heaviest segment first, so the tiles of a matrix share an
+// L2 and long tiles start early.
 #include "common.cuh"
 #include "launch.h"
 
 namespace muon {
 namespace {
 
-constexpr int BK = 64;             // K per LDS stage (64 bf16 = 128 B per row)
-constexpr int TM = 128, TN = 128;  // workgroup tile
-constexpr int WM = 64, WN = 64;    // wave tile
-constexpr int FM = WM / 32, FN = WN / 32;
-constexpr int NWAVE = (TM / WM) * (TN / WN);
-constexpr int NTHR = NWAVE * kWave;
-constexpr int STAGE_A = TM * BK;   // bf16 elements per operand tile
-constexpr int STAGE_B = TN * BK;
+constexpr int T = 256;          // workgroup tile (both dims)
+constexpr int BK = 64;          // K per LDS stage
+constexpr int WT = 128;         // wave tile
+constexpr int F = WT / 32;      // MFMA blocks per wave dimension
+constexpr int NTHR = 256;
+constexpr int OPB = T * BK * 2; // bytes of one operand tile per stage (32 KB)
+constexpr int NXCD = 8;
 
-__device__ __forceinline__ int swz(int r, int c) {  // 16-B chunk index -> byte offset in a 128-B row
-  return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
 }
 
-// Fragment (8 bf16) for a 32-row MFMA block at k-step ks (16 K) of a tile.
-__device__ __forceinline__ bf16x8_t lds_frag(const char* tile, int row0, int ks, int lane) {
+// ---- K-contiguous operand: [256 rows][64 K], 128-byte rows -------------------
+__device__ __forceinline__ int rswz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// Each of the 4 waves issues 8 instructions = 512 chunks of the 2048.
+__device__ __forceinline__ void load_rows(char* op, const bf16_t* src, long long ld, int k0) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = w * 8 + i;
+    const int P = blk * 64 + lane;
+    const int r = P >> 3, pc = P & 7;
+    const int c = pc ^ ((r >> 1) & 7);
+    dma16(src + r * ld + k0 + c * 8, op + blk * 1024);
+  }
+}
+
+__device__ __forceinline__ bf16x8_t frag_rows(const char* op, int row0, int ks, int lane) {
   const int r = row0 + (lane & 31);
-  const int c = ks * 2 + (lane >> 5);
-  return *reinterpret_cast<const bf16x8_t*>(tile + swz(r, c));
+  return *reinterpret_cast<const bf16x8_t*>(op + rswz(r, ks * 2 + (lane >> 5)));
 }
 
-// --- loaders ----------------------------------------------------------------
-// K-contiguous source: R rows of 64 bf16 starting at src (row stride ld).
-template <int R>
-struct RowLoader {
-  static constexpr int N = R * 8 / NTHR;  // 16-B chunks per thread
-  u32x4_t v[N];
-  __device__ void load(const bf16_t* src, long long ld, int k0) {
-#pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const int q = threadIdx.x + NTHR * p;
-      const int r = q >> 3, c = q & 7;
-      v[p] = *reinterpret_cast<const u32x4_t*>(src + r * ld + k0 + c * 8);
-    }
-  }
-  __device__ void store(char* tile) const {
-#pragma unroll
-    for (int p = 0; p < N; ++p) {
-      const int q = threadIdx.x + NTHR * p;
-      const int r = q >> 3, c = q & 7;
-      *reinterpret_cast<u32x4_t*>(tile + swz(r, c)) = v[p];
-    }
-  }
-};
+// ---- X operand of the combine: [64 rows j][256 cols k], 512-byte rows -------
+__device__ __forceinline__ int xswz(int j, int c) { return j * 512 + ((c ^ ((j & 3) << 2)) << 4); }
 
-// N-contiguous source transposed into a K-contiguous LDS tile: the tile row
-// is the source column (R of them, from col0), its 64 K values are source
-// rows j0..j0+63.  Each thread moves 4 source rows x 8 source columns.
-template <int R>
-struct TransLoader {
-  static constexpr int NB = (BK / 4) * (R / 8) / NTHR;  // 4x8 blocks per thread
-  u32x4_t v[NB][4];
-  __device__ void load(const bf16_t* src, long long ld, int j0, int col0) {
+__device__ __forceinline__ void load_xrows(char* op, const bf16_t* X, long long ld, int j0, int k0) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int p = 0; p < NB; ++p) {
-      const int q = threadIdx.x + NTHR * p;
-      const int cc = q % (R / 8), jq = q / (R / 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        v[p][i] = *reinterpret_cast<const u32x4_t*>(src + (j0 + jq * 4 + i) * ld + col0 + cc * 8);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int blk = w * 8 + i;
+    const int P = blk * 64 + lane;
+    const int j = P >> 5, pc = P & 31;
+    const int c = pc ^ ((j & 3) << 2);
+    dma16(X + (j0 + j) * ld + k0 + c * 8, op + blk * 1024);
   }
-  __device__ void store(char* tile) const {
-#pragma unroll
-    for (int p = 0; p < NB; ++p) {
-      const int q = threadIdx.x + NTHR * p;
-      const int cc = q % (R / 8), jq = q / (R / 8);
-      const int jchunk = jq >> 1, half = jq & 1;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int sh = 16 * h;
-          const uint32_t c0 = (v[p][0][d] >> sh) & 0xFFFFu, c1 = (v[p][1][d] >> sh) & 0xFFFFu;
-          const uint32_t c2 = (v[p][2][d] >> sh) & 0xFFFFu, c3 = (v[p][3][d] >> sh) & 0xFFFFu;
-          u32x2_t w = {c0 | (c1 << 16), c2 | (c3 << 16)};
-          const int row = cc * 8 + 2 * d + h;
-          *reinterpret_cast<u32x2_t*>(tile + swz(row, jchunk) + half * 8) = w;
-        }
-      }
-    }
-  }
-};
+}
 
-// --- main loop ----------------------------------------------------------------
+// MFMA operand with rows = columns k0..k0+31 of X and the 16 contraction
+// values j = 16 ks + 8 (lane / 32) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_xcols(const char* op, int k0, int ks, int lane) {
+  const int g = lane >> 4, jj = lane & 15;
+  const int kk = k0 + 16 * (g & 1) + 4 * (jj & 3);
+  const int c = kk >> 3, half = (kk >> 2) & 1;
+  u32x2_t part[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = ks * 16 + 8 * (g >> 1) + 4 * h + (jj >> 2);
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(op + xswz(j, c) + half * 8));
+    part[h] = __builtin_bit_cast(u32x2_t, v);
+  }
+  // whole-register repacking: 4 + 4 contraction values -> one 8-value operand
+  const u32x4_t w = {part[0][0], part[0][1], part[1][0], part[1][1]};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
 struct Acc {
-  f32x16_t c[FM][FN];
+  f32x16_t c[F][F];
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[i][j][r] = 0.0f;
+  }
 };
 
-__device__ __forceinline__ void mma_stage(const char* ta, const char* tb, int wm, int wn, Acc& acc) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    bf16x8_t fa[FM], fb[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = lds_frag(ta, wm * WM + i * 32, ks, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = lds_frag(tb, wn * WN + j * 32, ks, lane);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
+__device__ __forceinline__ void wait_dma_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0) expcnt(0): this wave's LDS fills landed
+  __syncthreads();
+}
+
+// ---- segment table ----------------------------------------------------------
+__device__ __forceinline__ bool find_tile(const GemmArgs& G, int& seg, int& tile) {
+  const int x = blockIdx.x % NXCD;
+  int local = blockIdx.x / NXCD;
+  for (int s = 0; s < G.nseg; ++s) {
+    const int tot = G.seg[s].count * G.seg[s].tiles_per_mat;
+    const int q = (tot + NXCD - 1) / NXCD;
+    const int lo = x * q;
+    const int len = lo >= tot ? 0 : (lo + q <= tot ? q : tot - lo);
+    if (local < len) {
+      seg = s;
+      tile = lo + local;
+      return true;
+    }
+    local -= len;
   }
+  return false;
 }
 
-__device__ __forceinline__ float step1_inv(const NsGemmLaunch& L, int z, float* red) {
-  if (L.partials == nullptr) return 1.0f;
-  return inv_norm_from_partials(L.partials + static_cast<long long>(z) * L.P, L.P, L.eps, red, nullptr);
+__device__ __forceinline__ float seg_inv(const GemmSeg& S, int z, float* red) {
+  if (S.partials == nullptr) return 1.0f;
+  return inv_norm_from_partials(S.partials + static_cast<long long>(z) * S.P, S.P, S.eps, red, nullptr);
 }
 
-// --- Gram: A = X X^T, tiles bi <= bj only ------------------------------------
-__global__ void __launch_bounds__(NTHR) gram_bf16_kernel(NsGemmLaunch L) {
-  __shared__ __attribute__((aligned(16))) char lds[2][(STAGE_A + STAGE_B) * 2];
-  __shared__ float red[NWAVE];
-  const int z = blockIdx.y;
-  const int nt = L.s_pad / TM;
-  // linear upper-triangle index -> (bi, bj)
-  int t = blockIdx.x, bi = 0;
+// ---- Gram: A' = alpha I + beta X X^T ------------------------------------------
+__global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
+  __shared__ float red[NTHR / 64];
+  int si, tile;
+  if (!find_tile(G, si, tile)) return;
+  const GemmSeg& S = G.seg[si];
+  const int z = tile / S.tiles_per_mat;
+  int t = tile % S.tiles_per_mat, bi = 0;
+  const int nt = S.s_pad / T;
   while (t >= nt - bi) { t -= nt - bi; ++bi; }
   const int bj = bi + t;
-  const bf16_t* X = static_cast<const bf16_t*>(L.X) + z * L.xstride;
-  bf16_t* A = static_cast<bf16_t*>(L.A) + z * L.astride;
-  const float inv = step1_inv(L, z, red);
-  const float scale = inv * inv;
+  const bool diag = bi == bj;
+  const bf16_t* X = S.X + z * S.xstride;
+  bf16_t* A = S.A + z * S.astride;
+  const float inv = seg_inv(S, z, red);
+  const float alpha = S.a * inv, beta = S.b * inv * inv * inv;
 
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wid / (TN / WN), wn = wid % (TN / WN);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
   Acc acc;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc.c[i][j][r] = 0.0f;
+  acc.zero();
+  const bf16_t* srcA = X + static_cast<long long>(bi) * T * S.ld;
+  const bf16_t* srcB = X + static_cast<long long>(bj) * T * S.ld;
+  const int nk = S.kdim / BK;
 
-  const bf16_t* srcA = X + static_cast<long long>(bi) * TM * L.ld;
-  const bf16_t* srcB = X + static_cast<long long>(bj) * TN * L.ld;
-  RowLoader<TM> la;
-  RowLoader<TN> lb;
-  const int nk = L.ld / BK;
-  la.load(srcA, L.ld, 0);
-  lb.load(srcB, L.ld, 0);
-  la.store(lds[0]);
-  lb.store(lds[0] + STAGE_A * 2);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(srcA, L.ld, (kt + 1) * BK);
-      lb.load(srcB, L.ld, (kt + 1) * BK);
+  auto stage_load = [&](char* buf, int kt) {
+    load_rows(buf, srcA, S.ld, kt * BK);
+    if (!diag) load_rows(buf + OPB, srcB, S.ld, kt * BK);
+  };
+  auto stage_mma = [&](const char* buf) {
+    const char* ta = buf;
+    const char* tb = diag ? buf : buf + OPB;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t fa[F], fb[F];
+#pragma unroll
+      for (int i = 0; i < F; ++i) fa[i] = frag_rows(ta, wm * WT + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < F; ++j) fb[j] = frag_rows(tb, wn * WT + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
     }
-    mma_stage(lds[cur], lds[cur] + STAGE_A * 2, wm, wn, acc);
-    if (kt + 1 < nk) {
-      la.store(lds[cur ^ 1]);
-      lb.store(lds[cur ^ 1] + STAGE_A * 2);
-    }
-    __syncthreads();
+  };
+
+  stage_load(lds0, 0);
+  wait_dma_and_sync();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    stage_load(lds1, kt + 1);
+    stage_mma(lds0);
+    wait_dma_and_sync();
+    if (kt + 2 < nk) stage_load(lds0, kt + 2);
+    stage_mma(lds1);
+    wait_dma_and_sync();
   }
+  if (kt < nk) stage_mma(lds0);
 
-  // D[m][n] = A[bi*TM + m][bj*TN + n]; lane holds 4 consecutive m at one n.
+  // epilogue: D[m][n] = (X X^T)[bi*T + m][bj*T + n]; lane: 4 consecutive m at one n
   const int col = lane & 31, rq = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < F; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int gn = bj * TN + wn * WN + j * 32 + col;
+    for (int j = 0; j < F; ++j) {
+      const int gn = bj * T + wn * WT + j * 32 + col;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int gm = bi * TM + wm * WM + i * 32 + g * 8 + rq;
-        const float v0 = acc.c[i][j][4 * g + 0] * scale, v1 = acc.c[i][j][4 * g + 1] * scale;
-        const float v2 = acc.c[i][j][4 * g + 2] * scale, v3 = acc.c[i][j][4 * g + 3] * scale;
-        // mirrored tile: A[gn][gm .. gm+3], contiguous
-        u32x2_t w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        *reinterpret_cast<u32x2_t*>(A + static_cast<long long>(gn) * L.s_pad + gm) = w;
-        if (bi != bj) {
-          bf16_t* p = A + static_cast<long long>(gm) * L.s_pad + gn;
+      for (int q = 0; q < 4; ++q) {
+        const int gm = bi * T + wm * WT + i * 32 + q * 8 + rq;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = beta * acc.c[i][j][4 * q + r] + ((gm + r == gn) ? alpha : 0.0f);
+        const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2_t*>(A + static_cast<long long>(gn) * S.s_pad + gm) = w;  // mirrored
+        if (!diag) {
+          bf16_t* p = A + static_cast<long long>(gm) * S.s_pad + gn;
           p[0] = static_cast<bf16_t>(w[0] & 0xFFFF);
-          p[L.s_pad] = static_cast<bf16_t>(w[0] >> 16);
-          p[2 * L.s_pad] = static_cast<bf16_t>(w[1] & 0xFFFF);
-          p[3 * L.s_pad] = static_cast<bf16_t>(w[1] >> 16);
+          p[S.s_pad] = static_cast<bf16_t>(w[0] >> 16);
+          p[2 * S.s_pad] = static_cast<bf16_t>(w[1] & 0xFFFF);
+          p[3 * S.s_pad] = static_cast<bf16_t>(w[1] >> 16);
         }
       }
     }
   }
 }
 
-// --- combine: Y = alpha X + beta A X ------------------------------------------
-// MFMA M-dim = columns k of X (the long side), N-dim = rows i; the operand
-// from X is its transpose (k rows, j contiguous), the operand from A is A's
-// rows (A symmetric).  D[k][i] = (A X)[i][k]: each lane holds 4 consecutive k
-// of one row i, so X is read and Y written 8 bytes at a time.
-__global__ void __launch_bounds__(NTHR) combine_bf16_kernel(NsGemmLaunch L) {
-  __shared__ __attribute__((aligned(16))) char lds[2][(STAGE_A + STAGE_B) * 2];
-  __shared__ float red[NWAVE];
-  const int z = blockIdx.y;
-  const int tiles_k = L.ld / TM;
-  const int tk = blockIdx.x % tiles_k;  // column block of X (M-dim)
-  const int ti = blockIdx.x / tiles_k;  // row block of X / A (N-dim)
-  const bf16_t* X = static_cast<const bf16_t*>(L.X) + z * L.xstride;
-  bf16_t* Y = static_cast<bf16_t*>(L.Y) + z * L.xstride;
-  const bf16_t* A = static_cast<const bf16_t*>(L.A) + z * L.astride;
-  const float inv = step1_inv(L, z, red);
-  const float alpha = L.alpha * inv, beta = L.beta * inv;
+// ---- combine: Y = A' X --------------------------------------------------------
+// D[k][i] = sum_j X[j][k] A'[i][j] = (A' X)[i][k]
+__global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
+  int si, tile;
+  if (!find_tile(G, si, tile)) return;
+  const GemmSeg& S = G.seg[si];
+  const int z = tile / S.tiles_per_mat;
+  const int t = tile % S.tiles_per_mat;
+  const int tiles_k = S.ld / T;
+  const int tk = t % tiles_k, ti = t / tiles_k;
+  const bf16_t* X = S.X + z * S.xstride;
+  bf16_t* Y = S.Y + z * S.xstride;
+  const bf16_t* Ap = S.A + z * S.astride + static_cast<long long>(ti) * T * S.s_pad;
 
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wid / (TN / WN), wn = wid % (TN / WN);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
   Acc acc;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc.c[i][j][r] = 0.0f;
+  acc.zero();
+  const int nk = S.s_pad / BK;
 
-  const bf16_t* srcA = A + static_cast<long long>(ti) * TN * L.s_pad;  // rows i of A
-  TransLoader<TM> lx;
-  RowLoader<TN> la;
-  const int nk = L.s_pad / BK;
-  lx.load(X, L.ld, 0, tk * TM);
-  la.load(srcA, L.s_pad, 0);
-  lx.store(lds[0]);
-  la.store(lds[0] + STAGE_A * 2);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      lx.load(X, L.ld, (kt + 1) * BK, tk * TM);
-      la.load(srcA, L.s_pad, (kt + 1) * BK);
+  auto stage_load = [&](char* buf, int kt) {
+    load_xrows(buf, X, S.ld, kt * BK, tk * T);
+    load_rows(buf + OPB, Ap, S.s_pad, kt * BK);
+  };
+  auto stage_mma = [&](const char* buf) {
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t fx[F], fa[F];
+#pragma unroll
+      for (int i = 0; i < F; ++i) fx[i] = frag_xcols(buf, wm * WT + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < F; ++j) fa[j] = frag_rows(buf + OPB, wn * WT + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[i], fa[j], acc.c[i][j], 0, 0, 0);
     }
-    mma_stage(lds[cur], lds[cur] + STAGE_A * 2, wm, wn, acc);
-    if (kt + 1 < nk) {
-      lx.store(lds[cur ^ 1]);
-      la.store(lds[cur ^ 1] + STAGE_A * 2);
-    }
-    __syncthreads();
+  };
+
+  stage_load(lds0, 0);
+  wait_dma_and_sync();
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    stage_load(lds1, kt + 1);
+    stage_mma(lds0);
+    wait_dma_and_sync();
+    if (kt + 2 < nk) stage_load(lds0, kt + 2);
+    stage_mma(lds1);
+    wait_dma_and_sync();
   }
+  if (kt < nk) stage_mma(lds0);
 
+  // lane: row i = ti*T + wn*WT + j*32 + (lane & 31); columns k = ... + 8q + 4 (lane >> 5) + 0..3
   const int col = lane & 31, rq = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < F; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int gi = ti * TN + wn * WN + j * 32 + col;  // row of X / Y
+    for (int j = 0; j < F; ++j) {
+      const int gi = ti * T + wn * WT + j * 32 + col;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int gk = tk * TM + wm * WM + i * 32 + g * 8 + rq;  // 4 consecutive columns
-        const long long off = static_cast<long long>(gi) * L.ld + gk;
-        const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(X + off);
-        const float y0 = fmaf(alpha, lo_bf16(xv[0]), beta * acc.c[i][j][4 * g + 0]);
-        const float y1 = fmaf(alpha, hi_bf16(xv[0]), beta * acc.c[i][j][4 * g + 1]);
-        const float y2 = fmaf(alpha, lo_bf16(xv[1]), beta * acc.c[i][j][4 * g + 2]);
-        const float y3 = fmaf(alpha, hi_bf16(xv[1]), beta * acc.c[i][j][4 * g + 3]);
-        u32x2_t w = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-        *reinterpret_cast<u32x2_t*>(Y + off) = w;
+      for (int q = 0; q < 4; ++q) {
+        const int gk = tk * T + wm * WT + i * 32 + q * 8 + rq;
+        const u32x2_t w = {pack_bf16x2(acc.c[i][j][4 * q + 0], acc.c[i][j][4 * q + 1]),
+                           pack_bf16x2(acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3])};
+        *reinterpret_cast<u32x2_t*>(Y + static_cast<long long>(gi) * S.ld + gk) = w;
       }
     }
   }
+}
+
+int grid_for(const GemmArgs& G) {
+  int per_xcd = 0;
+  for (int s = 0; s < G.nseg; ++s) {
+    const int tot = G.seg[s].count * G.seg[s].tiles_per_mat;
+    per_xcd += (tot + NXCD - 1) / NXCD;
+  }
+  return per_xcd * NXCD;
 }
 
 }  // namespace
 
-hipError_t launch_gram_bf16(const NsGemmLaunch& L, hipStream_t st) {
-  const int nt = L.s_pad / TM;
-  const dim3 grid(nt * (nt + 1) / 2, L.count);
-  hipLaunchKernelGGL(gram_bf16_kernel, grid, dim3(NTHR), 0, st, L);
+int gram_tiles_per_matrix(int s_pad) {
+  const int nt = s_pad / T;
+  return nt * (nt + 1) / 2;
+}
+int combine_tiles_per_matrix(int s_pad, int ld) { return (s_pad / T) * (ld / T); }
+
+hipError_t launch_gram_bf16(const GemmArgs& G, hipStream_t st) {
+  const int grid = grid_for(G);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(gram_bf16_kernel, dim3(grid), dim3(NTHR), 0, st, G);
   return hipGetLastError();
 }
 
-hipError_t launch_combine_bf16(const NsGemmLaunch& L, hipStream_t st) {
-  const dim3 grid((L.ld / TM) * (L.s_pad / TN), L.count);
-  hipLaunchKernelGGL(combine_bf16_kernel, grid, dim3(NTHR), 0, st, L);
+hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st) {
+  const int grid = grid_for(G);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid), dim3(NTHR), 0, st, G);
   return hipGetLastError();
 }
 

@@ -56,11 +56,30 @@ hipError_t launch_momentum(const MomentumLaunch& L, hipStream_t st);
 hipError_t launch_apply(const ApplyLaunch& L, hipStream_t st);
 hipError_t launch_norms(const float* partials, int P, int count, float* out, hipStream_t st);
 
-// bf16 matrix-core path (tile multiples: s_pad % 128 == 0, ld % 128 == 0).
-constexpr int kTileS = 128;   // s_pad multiple for the bf16 tiled path
-constexpr int kTileL = 128;   // ld multiple for the bf16 tiled path
-hipError_t launch_gram_bf16(const NsGemmLaunch& L, hipStream_t st);
-hipError_t launch_combine_bf16(const NsGemmLaunch& L, hipStream_t st);
+// bf16 matrix-core path.  One launch covers up to kMaxSeg shape groups
+// (segments) of one Newton-Schulz step.
+constexpr int kTileS = 256;   // s_pad multiple for the bf16 tiled path
+constexpr int kTileL = 256;   // ld multiple for the bf16 tiled path
+constexpr int kMaxSeg = 4;
+struct GemmSeg {
+  const bf16_t* X;     // iterate in  [count][s_pad][ld]
+  bf16_t* Y;           // iterate out (combine)
+  bf16_t* A;           // A' = alpha I + beta X X^T  [count][s_pad][s_pad]
+  long long xstride, astride;
+  int s_pad, ld, kdim, count, tiles_per_mat;
+  const float* partials;  // step 1: fold 1/(nu+eps) into alpha, beta
+  int P;
+  float eps;
+  float a, b;          // step coefficients
+};
+struct GemmArgs {
+  GemmSeg seg[kMaxSeg];
+  int nseg;
+};
+int gram_tiles_per_matrix(int s_pad);
+int combine_tiles_per_matrix(int s_pad, int ld);
+hipError_t launch_gram_bf16(const GemmArgs& G, hipStream_t st);
+hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st);
 
 // float32 path (tile multiples: s_pad % 64 == 0, ld % 64 == 0).
 constexpr int kTileF32 = 64;

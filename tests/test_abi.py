@@ -96,7 +96,7 @@ def test_step_validation(mu, case, expect):
         cfg.ncoef = 4
     g, k2 = _group(mu, dtype=5 if case == "bad_dtype" else None)
     if case == "misaligned":
-        k2[0][0] = 0x100004
+        k2[0][0] = 0x100002  # W is float32: 4-byte alignment required
     if case == "null_matrix":
         k2[2][0] = None
     arr = (mu.binding.GroupC * 1)(g)
