@@ -19,16 +19,21 @@
 // columns of A' are zero).  The Gram's contraction stops at kdim, the first
 // multiple of 64 >= l.
 //
-// Tiling: 256 x 256 workgroup tile, four waves of 128 x 128 (4 x 4 MFMA blocks
-// of 32 x 32), BK = 64, two LDS stages of 64 KB filled by
-// global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane, so a
-// wave writes 1 KB of LDS per instruction; the global address each lane
-// fetches implements the swizzle).
+// Tiling: 256 x 256 workgroup tile, eight waves (two per SIMD) of 128 x 64
+// (Gram) or 64 x 128 (combine) made of 32 x 32 MFMA blocks.  The contraction
+// runs in stages of BK = 32 through NSTAGE = 4 LDS buffers of 32 KB: the
+// fill of stage kt + 3 is issued while stage kt is multiplied, so three
+// stages of loads (96 KB per CU) are in flight and an L2 miss to MALL or HBM
+// does not stall the matrix pipes.  Fills use buffer_load ... lds (each
+// lane's 16 bytes land at base + 16 * lane; the per-lane source offset
+// implements the swizzle).  Stage hand-over is an explicit
+// s_waitcnt vmcnt(<loads of younger stages>) + s_barrier, because
+// __syncthreads() would drain every outstanding fill.
 //  * K-contiguous operands (rows of X in the Gram, rows of A' in the combine)
-//    sit as [256 rows][64 K] with 16-byte chunks XOR-swizzled by (row>>1)&7
-//    and are read as ds_read_b128 fragments.
+//    sit as [256 rows][32 K] (64-byte rows, 16-byte chunks XOR-swizzled by
+//    (row >> 2) & 3) and are read as ds_read_b128 fragments.
 //  * The combine's X operand is contracted over X's row index: it sits
-//    row-major as [64 rows j][256 columns k] (chunks swizzled by 4*(j&3)) and
+//    row-major as [32 rows j][256 columns k] (chunks swizzled by 4*(j&3)) and
 //    its fragments come from ds_read_b64_tr_b16: 16 lanes each address 4
 //    elements of a 4 x 16 block and every lane receives one column's 4
 //    consecutive rows, exactly the MFMA operand layout.
@@ -46,69 +51,112 @@
 namespace muon {
 namespace {
 
-constexpr int T = 256;          // workgroup tile (both dims)
-constexpr int BK = 64;          // K per LDS stage
-constexpr int WT = 128;         // wave tile
-constexpr int F = WT / 32;      // MFMA blocks per wave dimension
-constexpr int NTHR = 256;
-constexpr int OPB = T * BK * 2; // bytes of one operand tile per stage (32 KB)
+constexpr int T = 256;            // workgroup tile (both dims)
+constexpr int BK = 32;            // K per LDS stage
+constexpr int KS = BK / 16;       // MFMA k-steps per stage
+constexpr int NSTAGE = 4;         // LDS buffers (NSTAGE - 1 stages in flight)
+constexpr int NWAVE = 8;          // two waves per SIMD
+constexpr int NTHR = NWAVE * 64;
+constexpr int OPB = T * BK * 2;   // bytes of one operand tile per stage (16 KB)
 constexpr int NXCD = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+// Wave index as a scalar: everything derived from it (LDS block bases, buffer
+// soffsets) stays in SGPRs instead of being treated as divergent.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
 }
 
-// ---- K-contiguous operand: [256 rows][64 K], 128-byte rows -------------------
-__device__ __forceinline__ int rswz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// 16-byte buffer load written straight into LDS: lane l's data lands at
+// lds_wave_base + 16 * l.  The per-lane byte offset is a VGPR, everything that
+// is uniform (row block, stage) goes into the SGPR soffset.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)lds_wave_base, 16, voff, soff, 0, 0);
+}
 
-// Each of the 4 waves issues 8 instructions = 512 chunks of the 2048.
-__device__ __forceinline__ void load_rows(char* op, const bf16_t* src, long long ld, int k0) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// ---- K-contiguous operand: [256 rows][32 K], 64-byte rows ------------------
+__device__ __forceinline__ int rswz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// Per-lane byte offset of the K-contiguous fill: 1 KB block b holds rows
+// 16b + (lane >> 2); LDS chunk (lane & 3) of a row holds source chunk
+// (lane & 3) ^ ((row >> 2) & 3), and (row >> 2) & 3 = (lane >> 4) & 3 for
+// every b.
+__device__ __forceinline__ int row_voff(int ld_bytes) {
+  const int lane = threadIdx.x & 63;
+  return (lane >> 2) * ld_bytes + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+}
+
+// 16 blocks of 1 KB per operand tile, two per wave.  soff0: byte offset of
+// (first row, first K of the stage).
+__device__ __forceinline__ void load_rows(char* op, __amdgpu_buffer_rsrc_t rsrc, int voff, int ld_bytes, int soff0) {
+  const int w = wave_id();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = w * 8 + i;
-    const int P = blk * 64 + lane;
-    const int r = P >> 3, pc = P & 7;
-    const int c = pc ^ ((r >> 1) & 7);
-    dma16(src + r * ld + k0 + c * 8, op + blk * 1024);
+  for (int i = 0; i < 2; ++i) {
+    const int blk = w * 2 + i;
+    dma16(rsrc, voff, soff0 + blk * 16 * ld_bytes, op + blk * 1024);
   }
 }
 
-__device__ __forceinline__ bf16x8_t frag_rows(const char* op, int row0, int ks, int lane) {
-  const int r = row0 + (lane & 31);
-  return *reinterpret_cast<const bf16x8_t*>(op + rswz(r, ks * 2 + (lane >> 5)));
+// Lane part of a K-contiguous fragment address for k-step ks: row (lane & 31)
+// of a 32-row block, chunk 2 ks + (lane >> 5).  A block's first row is a
+// multiple of 32, which leaves the swizzle unchanged, so the full address is
+// tile + r0 * 64 + rfrag_off(ks) with r0 * 64 a constant offset.
+__device__ __forceinline__ int rfrag_off(int ks, int lane) {
+  const int r = lane & 31;
+  return r * 64 + (((ks * 2 + (lane >> 5)) ^ ((r >> 2) & 3)) << 4);
 }
 
-// ---- X operand of the combine: [64 rows j][256 cols k], 512-byte rows -------
+__device__ __forceinline__ bf16x8_t frag_at(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+
+// ---- X operand of the combine: [32 rows j][256 cols k], 512-byte rows -------
 __device__ __forceinline__ int xswz(int j, int c) { return j * 512 + ((c ^ ((j & 3) << 2)) << 4); }
 
-__device__ __forceinline__ void load_xrows(char* op, const bf16_t* X, long long ld, int j0, int k0) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// Block b holds rows 2b, 2b+1 (lane >> 5); chunk (lane & 31) of LDS row j
+// holds source chunk (lane & 31) ^ ((j & 3) << 2), which depends on b only
+// through its parity.
+struct XOffs {
+  int even, odd;
+  __device__ explicit XOffs(int ld_bytes) {
+    const int lane = threadIdx.x & 63;
+    const int base = (lane >> 5) * ld_bytes;
+    even = base + (((lane & 31) ^ ((lane >> 5) << 2)) << 4);
+    odd = base + (((lane & 31) ^ ((2 + (lane >> 5)) << 2)) << 4);
+  }
+};
+
+__device__ __forceinline__ void load_xrows(char* op, __amdgpu_buffer_rsrc_t rsrc, const XOffs& o, int ld_bytes,
+                                           int soff0) {
+  const int w = wave_id();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = w * 8 + i;
-    const int P = blk * 64 + lane;
-    const int j = P >> 5, pc = P & 31;
-    const int c = pc ^ ((j & 3) << 2);
-    dma16(X + (j0 + j) * ld + k0 + c * 8, op + blk * 1024);
+  for (int i = 0; i < 2; ++i) {
+    const int blk = w * 2 + i;
+    dma16(rsrc, (i & 1) ? o.odd : o.even, soff0 + blk * 2 * ld_bytes, op + blk * 1024);
   }
 }
 
-// MFMA operand with rows = columns k0..k0+31 of X and the 16 contraction
-// values j = 16 ks + 8 (lane / 32) + 0..7.
-__device__ __forceinline__ bf16x8_t frag_xcols(const char* op, int k0, int ks, int lane) {
+// MFMA operand with rows = columns 32 i .. 32 i + 31 of the wave's X columns
+// and the 16 contraction values j = 16 ks + 8 (lane / 32) + 0..7, from two
+// transposing reads (4 rows each).  Lane part of the address of block i:
+// the row-in-quad (lane >> 2) & 3 of the 16-lane group fixes the swizzle, so
+// ks and the half h only add constants (16 ks rows, 4 h rows).
+__device__ __forceinline__ int xfrag_off(int wcol0, int i, int lane) {
   const int g = lane >> 4, jj = lane & 15;
-  const int kk = k0 + 16 * (g & 1) + 4 * (jj & 3);
-  const int c = kk >> 3, half = (kk >> 2) & 1;
+  const int kk = wcol0 + i * 32 + 16 * (g & 1) + 4 * (jj & 3);
+  const int j = 8 * (g >> 1) + (jj >> 2);
+  return xswz(j, kk >> 3) + ((kk >> 2) & 1) * 8;
+}
+
+__device__ __forceinline__ bf16x8_t frag_xcols(const char* p) {
   u32x2_t part[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int j = ks * 16 + 8 * (g >> 1) + 4 * h + (jj >> 2);
     const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4_t*)(op + xswz(j, c) + half * 8));
+        (__attribute__((address_space(3))) s16x4_t*)(p + h * 4 * 512));
     part[h] = __builtin_bit_cast(u32x2_t, v);
   }
   // whole-register repacking: 4 + 4 contraction values -> one 8-value operand
@@ -116,21 +164,127 @@ __device__ __forceinline__ bf16x8_t frag_xcols(const char* op, int k0, int ks, i
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+template <int FM, int FN>
 struct Acc {
-  f32x16_t c[F][F];
+  f32x16_t c[FM][FN];
   __device__ void zero() {
 #pragma unroll
-    for (int i = 0; i < F; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < F; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) c[i][j][r] = 0.0f;
   }
 };
 
-__device__ __forceinline__ void wait_dma_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0) expcnt(0): this wave's LDS fills landed
-  __syncthreads();
+// The MFMAs of one stage; fragments of k-step ks+1 are read while ks runs.
+template <int FM, int FN, class FragA, class FragB>
+__device__ __forceinline__ void stage_mma(Acc<FM, FN>& acc, FragA fra, FragB frb) {
+  bf16x8_t fa[2][FM], fb[2][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa[0][i] = fra(0, i);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fb[0][j] = frb(0, j);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = ks & 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[c ^ 1][i] = fra(ks + 1, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[c ^ 1][j] = frb(ks + 1, j);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+// Stage hand-over: wait until this wave's fills of the stage about to be used
+// have landed (`younger` fills of later stages may stay in flight; fills
+// complete in issue order), finish this wave's LDS reads, then barrier so
+// every wave's part is visible and the buffer being refilled next is free.
+template <int YOUNGER>
+__device__ __forceinline__ void stage_sync() {
+  static_assert(YOUNGER >= 0 && YOUNGER < 16, "vmcnt immediate");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | YOUNGER);  // vmcnt(YOUNGER) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Loads per wave per stage are LPS (2 per operand); `ahead` = stages whose
+// fills were issued after the one needed now (0, 1 or 2).
+template <int LPS>
+__device__ __forceinline__ void stage_sync_ahead(int ahead) {
+  if (ahead >= 2) stage_sync<2 * LPS>();
+  else if (ahead == 1) stage_sync<LPS>();
+  else stage_sync<0>();
+}
+
+// The stage buffers are separate LDS arrays (so the compiler can tell a fill
+// of one from reads of another); a slab is chosen by a wave-uniform index.
+struct Bufs {
+  char* b[NSTAGE];
+  __device__ char* operator[](int p) const {
+    return p == 0 ? b[0] : p == 1 ? b[1] : p == 2 ? b[2] : b[3];
+  }
+};
+
+// The pipelined contraction: stages 0..nk-1 through NSTAGE buffers.
+// fill(buf, kt) issues this wave's fills of stage kt, mma(buf) multiplies one.
+template <int LPS, class Fill, class Mma>
+__device__ __forceinline__ void pipeline(const Bufs& bufs, int nk, Fill fill, Mma mma) {
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p)
+    if (p < nk) fill(bufs[p], p);
+  for (int kt0 = 0; kt0 < nk; kt0 += NSTAGE) {
+#pragma unroll
+    for (int b = 0; b < NSTAGE; ++b) {
+      const int kt = kt0 + b;
+      if (kt < nk) {
+        const int issued_after = (nk - 1 - kt) < (NSTAGE - 2) ? (nk - 1 - kt) : (NSTAGE - 2);
+        stage_sync_ahead<LPS>(issued_after);
+        if (kt + NSTAGE - 1 < nk) fill(bufs[(b + NSTAGE - 1) % NSTAGE], kt + NSTAGE - 1);
+        mma(bufs[b]);
+      }
+    }
+  }
+}
+
+// A copy of v the compiler cannot see through: epilogue addresses derived from
+// it are computed after the main loop instead of being hoisted above it (where
+// they would occupy registers for the whole loop).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// ---- output staging ------------------------------------------------------------
+// A 256 x 256 bf16 output tile leaves through LDS as four 64-row slabs (one
+// per stage buffer, 512-byte rows, 16-byte chunks XOR-swizzled by row & 31),
+// so that global stores are whole rows: each wave instruction writes two
+// contiguous 512-byte rows.  (Stores of 8 bytes per lane scattered over 32
+// rows were not merged into full lines and cost more than the main loop.)
+__device__ __forceinline__ int slab_off(int r, int col) {
+  return r * 512 + ((((col >> 3) ^ (r & 31))) << 4) + (col & 7) * 2;
+}
+
+// Copy the four staged slabs to dst rows (row stride ld elements), columns
+// col0 .. col0 + 255.
+__device__ __forceinline__ void slabs_to_global(const Bufs& bufs, bf16_t* dst, long long ld) {
+#pragma unroll
+  for (int p = 0; p < NSTAGE; ++p) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = threadIdx.x + NTHR * u;  // 2048 chunks of 16 B per slab
+      const int r = q >> 5, c = q & 31;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
+      *reinterpret_cast<u32x4_t*>(dst + (static_cast<long long>(p * 64 + r)) * ld + c * 8) = v;
+    }
+  }
 }
 
 // ---- segment table ----------------------------------------------------------
@@ -161,7 +315,9 @@ __device__ __forceinline__ float seg_inv(const GemmSeg& S, int z, float* red) {
 __global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
   __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
   __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
-  __shared__ float red[NTHR / 64];
+  __shared__ __attribute__((aligned(1024))) char lds2[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char lds3[2 * OPB];
+  __shared__ float red[NWAVE];
   int si, tile;
   if (!find_tile(G, si, tile)) return;
   const GemmSeg& S = G.seg[si];
@@ -176,73 +332,85 @@ __global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
   const float inv = seg_inv(S, z, red);
   const float alpha = S.a * inv, beta = S.b * inv * inv * inv;
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  Acc acc;
+  // waves: 2 along M x 4 along N, each 128 x 64 (4 x 2 MFMA blocks)
+  constexpr int GM = 128, GN = 64, FM = GM / 32, FN = GN / 32;
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int wm = wid >> 2, wn = wid & 3;
+  Acc<FM, FN> acc;
   acc.zero();
-  const bf16_t* srcA = X + static_cast<long long>(bi) * T * S.ld;
-  const bf16_t* srcB = X + static_cast<long long>(bj) * T * S.ld;
+  const int ld_bytes = S.ld * 2;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(X, static_cast<long long>(S.s_pad) * ld_bytes);
+  const int voff = row_voff(ld_bytes);
+  const int offA = bi * T * ld_bytes, offB = bj * T * ld_bytes;
   const int nk = S.kdim / BK;
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = rfrag_off(ks, lane);
+  const Bufs bufs{{lds0, lds1, lds2, lds3}};
 
-  auto stage_load = [&](char* buf, int kt) {
-    load_rows(buf, srcA, S.ld, kt * BK);
-    if (!diag) load_rows(buf + OPB, srcB, S.ld, kt * BK);
+  auto mma = [&](const char* buf, bool dg) {
+    const char* ta = buf + wm * GM * 64;
+    const char* tb = (dg ? buf : buf + OPB) + wn * GN * 64;
+    stage_mma<FM, FN>(acc, [&](int ks, int i) { return frag_at(ta + roff[ks] + i * 32 * 64); },
+                      [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); });
   };
-  auto stage_mma = [&](const char* buf) {
-    const char* ta = buf;
-    const char* tb = diag ? buf : buf + OPB;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[F], fb[F];
-#pragma unroll
-      for (int i = 0; i < F; ++i) fa[i] = frag_rows(ta, wm * WT + i * 32, ks, lane);
-#pragma unroll
-      for (int j = 0; j < F; ++j) fb[j] = frag_rows(tb, wn * WT + j * 32, ks, lane);
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
-    }
-  };
-
-  stage_load(lds0, 0);
-  wait_dma_and_sync();
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    stage_load(lds1, kt + 1);
-    stage_mma(lds0);
-    wait_dma_and_sync();
-    if (kt + 2 < nk) stage_load(lds0, kt + 2);
-    stage_mma(lds1);
-    wait_dma_and_sync();
+  if (diag) {  // both operands are the same rows: one fill per stage
+    pipeline<2>(bufs, nk, [&](char* buf, int kt) { load_rows(buf, rsrc, voff, ld_bytes, offA + kt * BK * 2); },
+                [&](const char* buf) { mma(buf, true); });
+  } else {
+    pipeline<4>(bufs, nk,
+                [&](char* buf, int kt) {
+                  load_rows(buf, rsrc, voff, ld_bytes, offA + kt * BK * 2);
+                  load_rows(buf + OPB, rsrc, voff, ld_bytes, offB + kt * BK * 2);
+                },
+                [&](const char* buf) { mma(buf, false); });
   }
-  if (kt < nk) stage_mma(lds0);
 
-  // epilogue: D[m][n] = (X X^T)[bi*T + m][bj*T + n]; lane: 4 consecutive m at one n
-  const int col = lane & 31, rq = (lane >> 5) * 4;
+  // epilogue: D[m][n] = (X X^T)[bi*T + m][bj*T + n]; lane: 4 consecutive m at one n.
+  // Pass 1 stages the mirrored tile (rows n, contiguous m) and writes it to
+  // A'[bj*T + n][bi*T + m]; pass 2 (off the diagonal) stages the tile itself.
+  stage_sync<0>();
+  const int lane_e = opaque(lane);
+  const int col = lane_e & 31, rq = (lane_e >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < F; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < F; ++j) {
-      const int gn = bj * T + wn * WT + j * 32 + col;
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * GN + j * 32 + col;  // slab wn, row j*32 + col
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int gm = bi * T + wm * WT + i * 32 + q * 8 + rq;
+        const int m = wm * GM + i * 32 + q * 8 + rq;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = beta * acc.c[i][j][4 * q + r] + ((gm + r == gn) ? alpha : 0.0f);
+        for (int r = 0; r < 4; ++r)
+          v[r] = beta * acc.c[i][j][4 * q + r] + ((bi * T + m + r == bj * T + n) ? alpha : 0.0f);
         const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2_t*>(A + static_cast<long long>(gn) * S.s_pad + gm) = w;  // mirrored
-        if (!diag) {
-          bf16_t* p = A + static_cast<long long>(gm) * S.s_pad + gn;
-          p[0] = static_cast<bf16_t>(w[0] & 0xFFFF);
-          p[S.s_pad] = static_cast<bf16_t>(w[0] >> 16);
-          p[2 * S.s_pad] = static_cast<bf16_t>(w[1] & 0xFFFF);
-          p[3 * S.s_pad] = static_cast<bf16_t>(w[1] >> 16);
+        *reinterpret_cast<u32x2_t*>(bufs[n >> 6] + slab_off(n & 63, m)) = w;
+      }
+    }
+  }
+  __syncthreads();
+  slabs_to_global(bufs, A + static_cast<long long>(bj) * T * S.s_pad + bi * T, S.s_pad);
+  if (!diag) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * GN + j * 32 + col;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = wm * GM + i * 32 + q * 8 + rq;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bf16_t b = f32_to_bf16(beta * acc.c[i][j][4 * q + r]);
+            *reinterpret_cast<bf16_t*>(bufs[(m + r) >> 6] + slab_off((m + r) & 63, n)) = b;
+          }
         }
       }
     }
+    __syncthreads();
+    slabs_to_global(bufs, A + static_cast<long long>(bi) * T * S.s_pad + bj * T, S.s_pad);
   }
 }
 
@@ -251,6 +419,8 @@ __global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
 __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
   __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
   __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char lds2[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char lds3[2 * OPB];
   int si, tile;
   if (!find_tile(G, si, tile)) return;
   const GemmSeg& S = G.seg[si];
@@ -260,63 +430,62 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
   const int tk = t % tiles_k, ti = t / tiles_k;
   const bf16_t* X = S.X + z * S.xstride;
   bf16_t* Y = S.Y + z * S.xstride;
-  const bf16_t* Ap = S.A + z * S.astride + static_cast<long long>(ti) * T * S.s_pad;
+  const bf16_t* Am = S.A + z * S.astride;
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // waves: 4 along M (columns k of X) x 2 along N (rows i), each 64 x 128
+  // (2 x 4 MFMA blocks; the transposed operand is the short side)
+  constexpr int CM = 64, CN = 128, FM = CM / 32, FN = CN / 32;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
-  Acc acc;
+  Acc<FM, FN> acc;
   acc.zero();
   const int nk = S.s_pad / BK;
+  const int ld_bytes = S.ld * 2, sp_bytes = S.s_pad * 2;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, static_cast<long long>(S.s_pad) * ld_bytes);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(Am, static_cast<long long>(S.s_pad) * sp_bytes);
+  const XOffs xo(ld_bytes);
+  const int avoff = row_voff(sp_bytes);
+  const int offA = ti * T * sp_bytes;
+  int roff[KS], xoff[FM];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = rfrag_off(ks, lane);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) xoff[i] = xfrag_off(wm * CM, i, lane);
+  const Bufs bufs{{lds0, lds1, lds2, lds3}};
 
-  auto stage_load = [&](char* buf, int kt) {
-    load_xrows(buf, X, S.ld, kt * BK, tk * T);
-    load_rows(buf + OPB, Ap, S.s_pad, kt * BK);
-  };
-  auto stage_mma = [&](const char* buf) {
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fx[F], fa[F];
-#pragma unroll
-      for (int i = 0; i < F; ++i) fx[i] = frag_xcols(buf, wm * WT + i * 32, ks, lane);
-#pragma unroll
-      for (int j = 0; j < F; ++j) fa[j] = frag_rows(buf + OPB, wn * WT + j * 32, ks, lane);
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[i], fa[j], acc.c[i][j], 0, 0, 0);
-    }
-  };
+  pipeline<4>(
+      bufs, nk,
+      [&](char* buf, int kt) {
+        load_xrows(buf, xr, xo, ld_bytes, kt * BK * ld_bytes + tk * T * 2);
+        load_rows(buf + OPB, ar, avoff, sp_bytes, offA + kt * BK * 2);
+      },
+      [&](const char* buf) {
+        const char* tb = buf + OPB + wn * CN * 64;
+        stage_mma<FM, FN>(acc, [&](int ks, int i) { return frag_xcols(buf + xoff[i] + ks * 16 * 512); },
+                          [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); });
+      });
 
-  stage_load(lds0, 0);
-  wait_dma_and_sync();
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    stage_load(lds1, kt + 1);
-    stage_mma(lds0);
-    wait_dma_and_sync();
-    if (kt + 2 < nk) stage_load(lds0, kt + 2);
-    stage_mma(lds1);
-    wait_dma_and_sync();
-  }
-  if (kt < nk) stage_mma(lds0);
-
-  // lane: row i = ti*T + wn*WT + j*32 + (lane & 31); columns k = ... + 8q + 4 (lane >> 5) + 0..3
-  const int col = lane & 31, rq = (lane >> 5) * 4;
+  // lane: row i = wn*CN + j*32 + (lane & 31) of the tile, columns
+  // k = wm*CM + i*32 + 8q + 4 (lane >> 5) + 0..3; staged in slab i >> 6.
+  stage_sync<0>();
+  const int lane_e = opaque(lane);
+  const int col = lane_e & 31, rq = (lane_e >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < F; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < F; ++j) {
-      const int gi = ti * T + wn * WT + j * 32 + col;
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * CN + j * 32 + col;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int gk = tk * T + wm * WT + i * 32 + q * 8 + rq;
+        const int k = wm * CM + i * 32 + q * 8 + rq;
         const u32x2_t w = {pack_bf16x2(acc.c[i][j][4 * q + 0], acc.c[i][j][4 * q + 1]),
                            pack_bf16x2(acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3])};
-        *reinterpret_cast<u32x2_t*>(Y + static_cast<long long>(gi) * S.ld + gk) = w;
+        *reinterpret_cast<u32x2_t*>(bufs[row >> 6] + slab_off(row & 63, k)) = w;
       }
     }
   }
+  __syncthreads();
+  slabs_to_global(bufs, Y + static_cast<long long>(ti) * T * S.ld + tk * T, S.ld);
 }
 
 int grid_for(const GemmArgs& G) {
