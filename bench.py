@@ -46,6 +46,62 @@ def kernel_source_hash(files):
     return h.hexdigest()[:16]
 
 
+COPY_CAL_BYTES = 1 << 30      # bytes read (and written) by the calibration copy
+
+
+def copy_calibration(torch):
+    """A plain streaming copy of known size (torch's elementwise negation, one
+    read and one write of every byte) so that the HBM counters of a profiled
+    run can be scaled to bytes."""
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, workload: str, kernels: dict):
+    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; both with
+    --copy-calibration) into HBM bytes per launch, scaled so that the copy
+    kernel reads and writes COPY_CAL_BYTES, and stores them with the hash of
+    the kernel sources they were taken on."""
+    import csv
+    def load(path, counter):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return per
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    def copy_factor(per):
+        vals = [v for k, vs in per.items() if "neg_kernel" in k for v in vs]
+        if not vals:
+            raise SystemExit("no calibration copy kernel in " + ", ".join(per))
+        return COPY_CAL_BYTES / float(np.median(vals))
+    fr, fw = copy_factor(fetch), copy_factor(write)
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        data = {}
+    for name, (pattern, files) in kernels.items():
+        rd = [v for k, vs in fetch.items() if pattern in k for v in vs]
+        wr = [v for k, vs in write.items() if pattern in k for v in vs]
+        if not rd or not wr:
+            log(f"[ingest] no dispatches of {pattern}")
+            continue
+        data[f"{name}@{workload}"] = {
+            "source_hash": kernel_source_hash(files), "dispatches": [len(rd), len(wr)],
+            "fetch_bytes": float(np.mean(rd)) * fr, "write_bytes": float(np.mean(wr)) * fw,
+            "bytes_per_launch": float(np.mean(rd)) * fr + float(np.mean(wr)) * fw,
+            "fetch_factor": round(fr, 4), "write_factor": round(fw, 4)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    log(f"[ingest] read factor {fr:.4f}, write factor {fw:.4f} -> {TRAFFIC_FILE}")
+
+
 def measured_traffic(kernel: str, workload: str, files):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None
     when none were taken or the kernel sources changed since."""
@@ -154,7 +210,7 @@ def bench_full_step(args, torch, mu, wl):
     kd = kernels[dom]
     roofline = {"bound": "mfma", "kernel": "combine_bf16_kernel", "achieved": round(kd["tflops"], 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kd["frac"], 4),
-                "traffic": measured_traffic("combine_bf16_kernel", "full_step", ["gemm_bf16.hip", "common.cuh"])}
+                "traffic": measured_traffic("combine_bf16_kernel", "full_step", GEMM)}
     result = {
         "metric": METRIC, "value": round(1e3 / ms_per_step, 3), "unit": "steps/s",
         "ms_per_step": round(ms_per_step, 4),
@@ -256,6 +312,19 @@ def bench_group(args, torch, mu, wl, which):
             "dtype": "bf16" if prec == mu.MUON_BF16 else "f32", "config": {"workload": w.name}}
 
 
+ELEMENTWISE = ["elementwise.hip", "common.cuh"]
+GEMM = ["gemm_bf16.hip", "common.cuh"]
+COUNTED_KERNELS = {
+    "full_step": {"combine_bf16_kernel": ("combine_bf16_kernel", GEMM),
+                  "gram_bf16_kernel": ("gram_bf16_kernel", GEMM),
+                  "momentum_wide_kernel": ("momentum_wide_kernel", ELEMENTWISE),
+                  "momentum_tall_kernel": ("momentum_tall_kernel", ELEMENTWISE),
+                  "apply_wide_kernel": ("apply_wide_kernel", ELEMENTWISE),
+                  "apply_tall_kernel": ("apply_tall_kernel", ELEMENTWISE)},
+    "injections": {"ns_small_bf16_kernel": ("ns_small_bf16_kernel", ["ns_small.hip", "common.cuh"])},
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,7 +336,14 @@ def main():
     ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
     ap.add_argument("--batch", type=int, default=393216, help="injections batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB plain copy first (reference for profiler byte counters)")
+    ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store HBM bytes per launch from two rocprofv3 counter runs of --workload")
     args = ap.parse_args()
+    if args.ingest:
+        ingest_counters(*args.ingest, args.workload, COUNTED_KERNELS[args.workload])
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the Muon step here has no "
               "multi-GPU path", file=sys.stderr)
@@ -281,6 +357,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mu.lib()
+    if args.copy_calibration:
+        copy_calibration(torch)
     if args.workload == "full_step":
         res = bench_full_step(args, torch, mu, wl)
     elif args.workload == "injections":
