@@ -139,11 +139,10 @@ def bench_full_step(args, torch, mu, wl):
         groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov))
     ws = mu.muon_step(groups, steps=steps_ns)  # allocates the workspace once
     torch.cuda.synchronize()
-    ng = len(groups)
-    # event order recorded by muon_step_timed for this schedule: start,
-    # after each group's momentum pass, after every grouped Gram and combine
-    # launch (one pair per NS step), after each group's apply pass
-    n_ev = 1 + ng + 2 * steps_ns + ng
+    # the library lists the phases muon_step_timed brackets with events
+    phases = mu.muon_step_phases(groups, steps=steps_ns)
+    n_ev = len(phases) + 1
+    log(f"[bench] schedule: {' '.join(phases)}")
 
     def make_events(k):
         evs = []
@@ -168,59 +167,89 @@ def bench_full_step(args, torch, mu, wl):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # algorithmic work of each launch of the executed schedule (every large
+    # group takes the same schedule here; per-group passes follow group order)
     per_group = [(g, min(g.m, g.n), max(g.m, g.n)) for g in w.groups]
     gram_f = sum(g.count * ns_flops(s, l)[0] for g, s, l in per_group)
     comb_f = sum(g.count * ns_flops(s, l)[1] for g, s, l in per_group)
-    dur = {"momentum": [], "gram": [], "combine": [], "apply": []}
+    sym_f = sum(g.count * s * s * (s + 1) for g, s, l in per_group)  # one symmetric s x s product
+    sym_products = []
+    if "symprod" in phases:
+        for k in range(steps_ns):
+            sym_products.append(int(k + 1 < steps_ns) + int(k >= 1))
+            if k + 1 < steps_ns:
+                sym_products.append(1)
+    assert len(sym_products) == phases.count("symprod")
+    work = []
+    gi_m = gi_a = si = 0
+    for ph in phases:
+        if ph == "momentum":
+            g, s, l = per_group[gi_m]
+            work.append(g.count * g.m * g.n * 12)
+            gi_m += 1
+        elif ph == "apply":
+            g, s, l = per_group[gi_a]
+            work.append(g.count * g.m * g.n * 10)
+            gi_a += 1
+        elif ph == "gram":
+            work.append(gram_f)
+        elif ph == "combine":
+            work.append(comb_f)
+        elif ph == "symprod":
+            work.append(sym_products[si] * sym_f)
+            si += 1
+        else:
+            raise RuntimeError(f"unexpected phase {ph}")
+    dur = {}
     for k in range(args.steps):
         e = evs[k]
-        for gi in range(ng):
-            dur["momentum"].append((gi, e[gi].elapsed_time(e[gi + 1])))
-        for j in range(steps_ns):
-            a = ng + 2 * j
-            dur["gram"].append((-1, e[a].elapsed_time(e[a + 1])))
-            dur["combine"].append((-1, e[a + 1].elapsed_time(e[a + 2])))
-        b = ng + 2 * steps_ns
-        for gi in range(ng):
-            dur["apply"].append((gi, e[b + gi].elapsed_time(e[b + gi + 1])))
-
-    def bytes_of(kind, gi):
-        g, s, l = per_group[gi]
-        return g.count * g.m * g.n * (12 if kind == "momentum" else 10)
+        for j, ph in enumerate(phases):
+            dur.setdefault(ph, []).append((e[j].elapsed_time(e[j + 1]), work[j]))
 
     kernels = {}
-    for kind, fl in (("gram", gram_f), ("combine", comb_f)):
-        tot_ms = sum(d for _, d in dur[kind])
-        n = len(dur[kind])
-        kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "flops_per_launch": float(fl),
-                         "tflops": fl * n / (tot_ms * 1e-3) / 1e12,
-                         "frac": fl * n / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    for kind in ("momentum", "apply"):
-        tot_ms = sum(d for _, d in dur[kind])
-        tot_b = sum(bytes_of(kind, gi) for gi, _ in dur[kind])
-        n = len(dur[kind])
-        kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "bytes_per_launch": tot_b / n,
-                         "gbs": tot_b / (tot_ms * 1e-3) / 1e9,
-                         "frac": tot_b / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    ns_ms = sum(d for _, d in dur["gram"]) / args.steps + sum(d for _, d in dur["combine"]) / args.steps
-    ns_flops_step = sum(sum(ns_flops(s, l)) * g.count for g, s, l in per_group) * steps_ns
+    for kind, rows in dur.items():
+        tot_ms = sum(d for d, _ in rows)
+        tot_w = sum(wk for _, wk in rows)
+        n = len(rows)
+        rate = tot_w / (tot_ms * 1e-3)
+        if kind in ("momentum", "apply"):
+            kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "bytes_per_launch": tot_w / n,
+                             "gbs": rate / 1e9, "frac": rate / 1e9 / PEAK_HBM_GBS}
+        else:
+            kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "flops_per_launch": tot_w / n,
+                             "tflops": rate / 1e12, "frac": rate / 1e12 / PEAK_BF16_TFLOPS}
+        kernels[kind]["ms_per_step"] = tot_ms / args.steps
+    ns_kinds = [k for k in ("gram", "symprod", "combine") if k in dur]
+    ns_ms = sum(sum(d for d, _ in dur[k]) for k in ns_kinds) / args.steps
+    ns_flops_step = sum(sum(wk for _, wk in dur[k]) for k in ns_kinds) / args.steps
     ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
+    # work the plain iteration (a Gram and a combine per step) would need
+    iter_flops_step = sum(sum(ns_flops(s, l)) * g.count for g, s, l in per_group) * steps_ns
 
-    dom = "combine"
+    # dominant kernel: the one with the most GPU time per step
+    dom = max(ns_kinds + ["momentum", "apply"], key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
-    roofline = {"bound": "mfma", "kernel": "combine_bf16_kernel", "achieved": round(kd["tflops"], 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kd["frac"], 4),
-                "traffic": measured_traffic("combine_bf16_kernel", "full_step", GEMM)}
+    names = {"gram": "gram_bf16_kernel", "combine": "combine_bf16_kernel", "symprod": "symprod_bf16_kernel",
+             "momentum": "momentum_*_kernel", "apply": "apply_*_kernel"}
+    if dom in ("momentum", "apply"):
+        roofline = {"bound": "hbm", "kernel": names[dom], "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(kd["frac"], 4), "traffic": None}
+    else:
+        roofline = {"bound": "mfma", "kernel": names[dom], "achieved": round(kd["tflops"], 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kd["frac"], 4),
+                    "traffic": measured_traffic(names[dom], "full_step", GEMM)}
     result = {
         "metric": METRIC, "value": round(1e3 / ms_per_step, 3), "unit": "steps/s",
         "ms_per_step": round(ms_per_step, 4),
         "ns_iters_per_s": round(steps_ns * 1e3 / ms_per_step, 2),
         "ns_tflops": round(ns_tflops, 2), "mfma_util": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
+        "ns_iteration_equivalent_tflops": round(iter_flops_step / (ns_ms * 1e-3) / 1e12, 2),
         "dtype": "bf16",
         "config": {"workload": f"mamba2-130m-full-step: {args.count}x out_proj 768x1536 + "
                                f"{args.count}x in_proj 3352x768, bf16 grads, fp32 W/M, "
                                f"{steps_ns} cubic NS steps",
-                   "matrices": 2 * args.count, "ns_steps": steps_ns, "parallelism": "none (1 GPU)"},
+                   "matrices": 2 * args.count, "ns_steps": steps_ns, "parallelism": "none (1 GPU)",
+                   "schedule": " ".join(phases)},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
@@ -317,6 +346,7 @@ GEMM = ["gemm_bf16.hip", "common.cuh"]
 COUNTED_KERNELS = {
     "full_step": {"combine_bf16_kernel": ("combine_bf16_kernel", GEMM),
                   "gram_bf16_kernel": ("gram_bf16_kernel", GEMM),
+                  "symprod_bf16_kernel": ("symprod_bf16_kernel", GEMM),
                   "momentum_wide_kernel": ("momentum_wide_kernel", ELEMENTWISE),
                   "momentum_tall_kernel": ("momentum_tall_kernel", ELEMENTWISE),
                   "apply_wide_kernel": ("apply_wide_kernel", ELEMENTWISE),

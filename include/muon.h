@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 1
+#define MUON_VERSION 2
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -72,6 +72,21 @@ typedef enum {
   MUON_EHIP = -4          /* the HIP runtime refused a launch */
 } muon_status;
 
+/* Newton-Schulz schedule of large bfloat16 matrices (the result is the same
+ * polynomial of X0 either way; rounding differs).
+ *   MUON_NS_ITERATE     per step A = X X^T, then X = (a I + b A) X: two
+ *                       products of s x l work each
+ *   MUON_NS_ACCUMULATE  every iterate is Q X0 with Q a polynomial in
+ *                       A_0 = X0 X0^T, so with B_k = a_k I + b_k A_k:
+ *                       A_{k+1} = A_k B_k^2 (= X_{k+1} X_{k+1}^T),
+ *                       Q = B_{steps-1} ... B_1 B_0, O = Q X0; one Gram, one
+ *                       final product, and 3 (steps - 1) symmetric s x s
+ *                       products; less work when l > s
+ *   MUON_NS_AUTO        per shape group, whichever needs fewer matrix-core
+ *                       operations (ACCUMULATE needs steps >= 2)
+ * float32 and small (on-chip) matrices always iterate. */
+typedef enum { MUON_NS_AUTO = 0, MUON_NS_ITERATE = 1, MUON_NS_ACCUMULATE = 2 } muon_ns_schedule;
+
 /* Newton-Schulz settings.
  *   steps     number of iterations, 0..64 (0: O is the normalised U)
  *   ncoef     2 (cubic: a, b) or 3 (quintic: a, b, c)
@@ -79,6 +94,7 @@ typedef enum {
  *   per_step  0: one (a, b[, c]) for every step; 1: one row per step
  *   eps       added to ||U||_F before dividing (>= 0)
  *   precision MUON_BF16 or MUON_F32 (see Precision above)
+ *   schedule  a muon_ns_schedule
  * A quintic c != 0 returns MUON_EUNSUPPORTED on the GPU path. */
 typedef struct {
   int steps;
@@ -87,6 +103,7 @@ typedef struct {
   int per_step;
   float eps;
   int precision;
+  int schedule;
 } muon_ns_cfg;
 
 /* One parameter group of `count` same-shape m x n matrices (the pages group
@@ -119,16 +136,30 @@ size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muo
 int muon_step(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg,
               void* workspace, size_t workspace_bytes, float* norms_out, void* stream);
 
+/* Phases of muon_step's launch schedule, for labelling measurements. */
+typedef enum {
+  MUON_PHASE_MOMENTUM = 1,    /* momentum pass of one group */
+  MUON_PHASE_NS_SMALL = 2,    /* on-chip Newton-Schulz of one group of small matrices */
+  MUON_PHASE_GRAM = 3,        /* grouped Gram launch (large bf16 matrices) */
+  MUON_PHASE_COMBINE = 4,     /* grouped combine launch (large bf16 matrices) */
+  MUON_PHASE_SYMPROD = 5,     /* grouped symmetric s x s products (accumulated schedule) */
+  MUON_PHASE_APPLY = 6,       /* apply pass of one group */
+  MUON_PHASE_F32_GRAM = 7,    /* Gram of one float32 group */
+  MUON_PHASE_F32_COMBINE = 8  /* combine of one float32 group */
+} muon_phase;
+
+/* The phases muon_step would run for these groups and cfg, in order: returns
+ * their number n (or a negative muon_status) and writes the first
+ * min(n, max_phases) of them to phases (may be NULL when max_phases is 0).
+ * Only shapes, counts, dtypes and cfg are read; no GPU work. */
+int muon_step_phases(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, int* phases,
+                     int max_phases);
+
 /* muon_step for measurement: identical work, and it records caller-created
- * hipEvent_t handles (`events`, host array) on `stream` at the boundaries of
- * the launch schedule, per group with count > 0, in order:
- *   start, after the momentum pass,
- *   then after every Gram launch and every combine launch (large matrices,
- *   2 * steps events) or after the on-chip Newton-Schulz launch (small
- *   matrices, 1 event; none when steps == 0),
- *   after the apply pass.
- * nevents must cover all groups (MUON_EINVAL otherwise).  Elapsed times
- * between consecutive events give per-kernel GPU durations. */
+ * hipEvent_t handles (`events`, host array) on `stream`: one at the start and
+ * one at the end of every phase listed by muon_step_phases, so nevents must be
+ * at least that count + 1 (MUON_EINVAL otherwise).  Elapsed times between
+ * consecutive events give each phase's GPU duration. */
 int muon_step_timed(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg,
                     void* workspace, size_t workspace_bytes, float* norms_out, void* stream,
                     void* const* events, int nevents);

@@ -15,6 +15,9 @@ from typing import Optional, Sequence
 
 MUON_F32, MUON_BF16 = 0, 1
 MUON_OK, MUON_EINVAL, MUON_EUNSUPPORTED, MUON_EWORKSPACE, MUON_EHIP = 0, -1, -2, -3, -4
+MUON_NS_AUTO, MUON_NS_ITERATE, MUON_NS_ACCUMULATE = 0, 1, 2
+PHASES = {1: "momentum", 2: "ns_small", 3: "gram", 4: "combine", 5: "symprod", 6: "apply", 7: "f32_gram",
+          8: "f32_combine"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmuon.so")
@@ -30,7 +33,7 @@ class MuonError(RuntimeError):
 class NsCfg(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int), ("ncoef", ctypes.c_int),
                 ("coeffs", ctypes.POINTER(ctypes.c_float)), ("per_step", ctypes.c_int),
-                ("eps", ctypes.c_float), ("precision", ctypes.c_int)]
+                ("eps", ctypes.c_float), ("precision", ctypes.c_int), ("schedule", ctypes.c_int)]
 
 
 class GroupC(ctypes.Structure):
@@ -42,7 +45,7 @@ class GroupC(ctypes.Structure):
                 ("nesterov", ctypes.c_int)]
 
 
-EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_timed", "muon_ns_workspace_size",
+EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
            "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_status_string", "muon_version")
 
 
@@ -61,6 +64,8 @@ def lib():
     L.muon_step.argtypes = [ctypes.POINTER(GroupC), i, ctypes.POINTER(NsCfg), vp, sz,
                             ctypes.POINTER(f), vp]
     L.muon_step.restype = i
+    L.muon_step_phases.argtypes = [ctypes.POINTER(GroupC), i, ctypes.POINTER(NsCfg), ctypes.POINTER(i), i]
+    L.muon_step_phases.restype = i
     L.muon_step_timed.argtypes = [ctypes.POINTER(GroupC), i, ctypes.POINTER(NsCfg), vp, sz,
                                   ctypes.POINTER(f), vp, ctypes.POINTER(ctypes.c_void_p), i]
     L.muon_step_timed.restype = i
@@ -110,13 +115,13 @@ def _stream_handle(stream=None) -> Optional[int]:
 
 
 def make_cfg(steps: int = 5, coeffs=(1.5, -0.5), eps: float = 1e-7, precision: int = MUON_BF16,
-             per_step: bool = False):
+             per_step: bool = False, schedule: int = MUON_NS_AUTO):
     """NsCfg plus the float array it points to (keep both alive)."""
     flat = [float(c) for row in coeffs for c in (row if isinstance(row, (tuple, list)) else (row,))]
     ncoef = len(coeffs[0]) if per_step else len(coeffs)
     arr = (ctypes.c_float * max(1, len(flat)))(*flat)
     cfg = NsCfg(int(steps), int(ncoef), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
-                int(bool(per_step)), float(eps), int(precision))
+                int(bool(per_step)), float(eps), int(precision), int(schedule))
     return cfg, arr
 
 
@@ -173,14 +178,29 @@ def _marshal_groups(groups: Sequence[MuonGroup]):
 # entry points (same names as the C ABI)
 # ----------------------------------------------------------------------------
 def muon_step_workspace_size(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7,
-                             precision=MUON_BF16, per_step=False) -> int:
+                             precision=MUON_BF16, per_step=False, schedule=MUON_NS_AUTO) -> int:
     cg, keep = _marshal_groups(groups)
-    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule)
     return int(lib().muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
 
 
+def muon_step_phases(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7, precision=MUON_BF16,
+                     per_step=False, schedule=MUON_NS_AUTO) -> list:
+    """Names of the phases muon_step runs for these groups, in order (the
+    intervals between the events muon_step_timed records)."""
+    L = lib()
+    cg, keep = _marshal_groups(groups)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule)
+    n = int(L.muon_step_phases(cg, len(groups), ctypes.byref(cfg), None, 0))
+    if n < 0:
+        _check(n, "muon_step_phases")
+    out = (ctypes.c_int * max(1, n))()
+    L.muon_step_phases(cg, len(groups), ctypes.byref(cfg), out, n)
+    return [PHASES[out[i]] for i in range(n)]
+
+
 def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7, precision=MUON_BF16,
-              per_step=False, workspace=None, norms_out=None, stream=None, events=None):
+              per_step=False, workspace=None, norms_out=None, stream=None, events=None, schedule=MUON_NS_AUTO):
     """One Muon step over every group (W and M updated in place).  Returns the
     workspace tensor so that callers can reuse it.  `events`: optional list of
     raw hipEvent_t handles (ints); when given, muon_step_timed records them at
@@ -188,7 +208,7 @@ def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7
     import torch
     L = lib()
     cg, keep = _marshal_groups(groups)
-    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule)
     need = int(L.muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
     if need == 0:
         _check(MUON_EINVAL, "muon_step_workspace_size")
@@ -210,13 +230,14 @@ def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7
     return workspace
 
 
-def muon_ns_workspace_size(m, n, batch, dtype, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=False) -> int:
-    cfg, arr = make_cfg(steps, coeffs, eps, dtype, per_step)
+def muon_ns_workspace_size(m, n, batch, dtype, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=False,
+                           schedule=MUON_NS_AUTO) -> int:
+    cfg, arr = make_cfg(steps, coeffs, eps, dtype, per_step, schedule)
     return int(lib().muon_ns_workspace_size(int(m), int(n), int(batch), int(dtype), ctypes.byref(cfg)))
 
 
 def muon_ns_orthogonalize(G, O, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=False, workspace=None,
-                          stream=None):
+                          stream=None, schedule=MUON_NS_AUTO):
     """O[b] = NS(G[b]) for contiguous [batch, m, n] (or [m, n]) tensors."""
     import torch
     L = lib()
@@ -226,7 +247,7 @@ def muon_ns_orthogonalize(G, O, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=
         raise ValueError("G and O must be contiguous tensors of one shape and dtype")
     b, m, n = G3.shape
     dt = _dtype_code(G3)
-    cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step)
+    cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step, schedule)
     need = int(L.muon_ns_workspace_size(m, n, b, dt, ctypes.byref(cfg)))
     if need == 0:
         _check(MUON_EINVAL, "muon_ns_workspace_size")

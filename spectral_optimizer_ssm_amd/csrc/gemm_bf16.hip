@@ -272,9 +272,23 @@ __device__ __forceinline__ int slab_off(int r, int col) {
   return r * 512 + ((((col >> 3) ^ (r & 31))) << 4) + (col & 7) * 2;
 }
 
+// Affine image of 8 staged bf16 values: b x, plus a for the element e == dcol
+// (the one on the matrix diagonal; dcol < 0 or > 7: none).
+__device__ __forceinline__ u32x4_t affine8(u32x4_t v, float a, float b, int dcol) {
+  u32x4_t o;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float x0 = __uint_as_float(v[h] << 16), x1 = __uint_as_float(v[h] & 0xffff0000u);
+    o[h] = pack_bf16x2(b * x0 + (dcol == 2 * h ? a : 0.0f), b * x1 + (dcol == 2 * h + 1 ? a : 0.0f));
+  }
+  return o;
+}
+
 // Copy the four staged slabs to dst rows (row stride ld elements), columns
-// col0 .. col0 + 255.
-__device__ __forceinline__ void slabs_to_global(const Bufs& bufs, bf16_t* dst, long long ld) {
+// col0 .. col0 + 255; when dst2 is non-null also dst2 = a2 I + b2 dst, taken
+// from the rounded values (the identity only on a diagonal tile, dg).
+__device__ __forceinline__ void slabs_to_global(const Bufs& bufs, bf16_t* dst, long long ld, bf16_t* dst2 = nullptr,
+                                                float a2 = 0.0f, float b2 = 0.0f, bool dg = false) {
 #pragma unroll
   for (int p = 0; p < NSTAGE; ++p) {
 #pragma unroll
@@ -282,15 +296,16 @@ __device__ __forceinline__ void slabs_to_global(const Bufs& bufs, bf16_t* dst, l
       const int q = threadIdx.x + NTHR * u;  // 2048 chunks of 16 B per slab
       const int r = q >> 5, c = q & 31;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
-      *reinterpret_cast<u32x4_t*>(dst + (static_cast<long long>(p * 64 + r)) * ld + c * 8) = v;
+      const long long o = (static_cast<long long>(p * 64 + r)) * ld + c * 8;
+      *reinterpret_cast<u32x4_t*>(dst + o) = v;
+      if (dst2 != nullptr) *reinterpret_cast<u32x4_t*>(dst2 + o) = affine8(v, a2, b2, dg ? p * 64 + r - c * 8 : -1);
     }
   }
 }
 
 // ---- segment table ----------------------------------------------------------
-__device__ __forceinline__ bool find_tile(const GemmArgs& G, int& seg, int& tile) {
-  const int x = blockIdx.x % NXCD;
-  int local = blockIdx.x / NXCD;
+template <class Args>
+__device__ __forceinline__ bool find_tile_at(const Args& G, int x, int local, int& seg, int& tile) {
   for (int s = 0; s < G.nseg; ++s) {
     const int tot = G.seg[s].count * G.seg[s].tiles_per_mat;
     const int q = (tot + NXCD - 1) / NXCD;
@@ -306,9 +321,28 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& G, int& seg, int& tile
   return false;
 }
 
-__device__ __forceinline__ float seg_inv(const GemmSeg& S, int z, float* red) {
+template <class Args>
+__device__ __forceinline__ bool find_tile(const Args& G, int& seg, int& tile) {
+  return find_tile_at(G, blockIdx.x % NXCD, blockIdx.x / NXCD, seg, tile);
+}
+
+template <class Seg>
+__device__ __forceinline__ float seg_inv(const Seg& S, int z, float* red) {
   if (S.partials == nullptr) return 1.0f;
   return inv_norm_from_partials(S.partials + static_cast<long long>(z) * S.P, S.P, S.eps, red, nullptr);
+}
+
+__device__ __forceinline__ float ipow(float x, int p) {
+  float r = 1.0f;
+  for (int i = 0; i < p; ++i) r *= x;
+  return r;
+}
+
+// Upper-triangle tile t of an nt x nt tile grid -> (bi, bj), bi <= bj.
+__device__ __forceinline__ void upper_tile(int t, int nt, int& bi, int& bj) {
+  bi = 0;
+  while (t >= nt - bi) { t -= nt - bi; ++bi; }
+  bj = bi + t;
 }
 
 // ---- Gram: A' = alpha I + beta X X^T ------------------------------------------
@@ -322,15 +356,12 @@ __global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
   if (!find_tile(G, si, tile)) return;
   const GemmSeg& S = G.seg[si];
   const int z = tile / S.tiles_per_mat;
-  int t = tile % S.tiles_per_mat, bi = 0;
-  const int nt = S.s_pad / T;
-  while (t >= nt - bi) { t -= nt - bi; ++bi; }
-  const int bj = bi + t;
+  int bi, bj;
+  upper_tile(tile % S.tiles_per_mat, S.s_pad / T, bi, bj);
   const bool diag = bi == bj;
   const bf16_t* X = S.X + z * S.xstride;
-  bf16_t* A = S.A + z * S.astride;
   const float inv = seg_inv(S, z, red);
-  const float alpha = S.a * inv, beta = S.b * inv * inv * inv;
+  const float ia = ipow(inv, S.pa), ib = ipow(inv, S.pb);
 
   // waves: 2 along M x 4 along N, each 128 x 64 (4 x 2 MFMA blocks)
   constexpr int GM = 128, GN = 64, FM = GM / 32, FN = GN / 32;
@@ -367,11 +398,15 @@ __global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
   }
 
   // epilogue: D[m][n] = (X X^T)[bi*T + m][bj*T + n]; lane: 4 consecutive m at one n.
-  // Pass 1 stages the mirrored tile (rows n, contiguous m) and writes it to
-  // A'[bj*T + n][bi*T + m]; pass 2 (off the diagonal) stages the tile itself.
+  // Per output, pass 1 stages the mirrored tile (rows n, contiguous m) and
+  // writes it to A[bj*T + n][bi*T + m]; pass 2 (off the diagonal) stages the
+  // tile itself.
   stage_sync<0>();
   const int lane_e = opaque(lane);
-  const int col = lane_e & 31, rq = (lane_e >> 5) * 4;
+  const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;  // buffers and rows below are uniform per wave
+  const float alpha = S.a * ia, beta = S.b * ib;
+  bf16_t* A = S.A + z * S.astride;
+  bf16_t* A2 = S.A2 == nullptr ? nullptr : S.A2 + z * S.astride;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -382,36 +417,38 @@ __global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
         const int m = wm * GM + i * 32 + q * 8 + rq;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          v[r] = beta * acc.c[i][j][4 * q + r] + ((bi * T + m + r == bj * T + n) ? alpha : 0.0f);
+        for (int r = 0; r < 4; ++r) v[r] = beta * acc.c[i][j][4 * q + r] + ((diag && m + r == n) ? alpha : 0.0f);
         const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2_t*>(bufs[n >> 6] + slab_off(n & 63, m)) = w;
+        *reinterpret_cast<u32x2_t*>(bufs[wn] + slab_off(j * 32 + col, m)) = w;
       }
     }
   }
   __syncthreads();
-  slabs_to_global(bufs, A + static_cast<long long>(bj) * T * S.s_pad + bi * T, S.s_pad);
-  if (!diag) {
-    __syncthreads();
+  {
+    const long long o = static_cast<long long>(bj) * T * S.s_pad + bi * T;
+    slabs_to_global(bufs, A + o, S.s_pad, A2 == nullptr ? nullptr : A2 + o, S.a2, S.b2, diag);
+  }
+  if (diag) return;
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = wn * GN + j * 32 + col;
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * GN + j * 32 + col;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = wm * GM + i * 32 + q * 8 + rq;
+      for (int q = 0; q < 4; ++q) {
+        const int m = wm * GM + i * 32 + q * 8 + rq;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bf16_t b = f32_to_bf16(beta * acc.c[i][j][4 * q + r]);
-            *reinterpret_cast<bf16_t*>(bufs[(m + r) >> 6] + slab_off((m + r) & 63, n)) = b;
-          }
+        for (int r = 0; r < 4; ++r) {
+          const bf16_t b = f32_to_bf16(beta * acc.c[i][j][4 * q + r]);
+          *reinterpret_cast<bf16_t*>(bufs[wm * 2 + (i >> 1)] + slab_off((i & 1) * 32 + q * 8 + rq + r, n)) = b;
         }
       }
     }
-    __syncthreads();
-    slabs_to_global(bufs, A + static_cast<long long>(bi) * T * S.s_pad + bj * T, S.s_pad);
   }
+  __syncthreads();
+  const long long o = static_cast<long long>(bi) * T * S.s_pad + bj * T;
+  slabs_to_global(bufs, A + o, S.s_pad, A2 == nullptr ? nullptr : A2 + o, S.a2, S.b2, false);
 }
 
 // ---- combine: Y = A' X --------------------------------------------------------
@@ -469,7 +506,7 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
   // k = wm*CM + i*32 + 8q + 4 (lane >> 5) + 0..3; staged in slab i >> 6.
   stage_sync<0>();
   const int lane_e = opaque(lane);
-  const int col = lane_e & 31, rq = (lane_e >> 5) * 4;
+  const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;  // buffers and rows below are uniform per wave
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -480,7 +517,7 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
         const int k = wm * CM + i * 32 + q * 8 + rq;
         const u32x2_t w = {pack_bf16x2(acc.c[i][j][4 * q + 0], acc.c[i][j][4 * q + 1]),
                            pack_bf16x2(acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3])};
-        *reinterpret_cast<u32x2_t*>(bufs[row >> 6] + slab_off(row & 63, k)) = w;
+        *reinterpret_cast<u32x2_t*>(bufs[wn * 2 + (j >> 1)] + slab_off((j & 1) * 32 + col, k)) = w;
       }
     }
   }
@@ -488,7 +525,141 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
   slabs_to_global(bufs, Y + static_cast<long long>(ti) * T * S.ld + tk * T, S.ld);
 }
 
-int grid_for(const GemmArgs& G) {
+// ---- symmetric products: O = alpha I + beta L R ----------------------------------
+// L and R are symmetric and commute (polynomials in one Gram matrix), so
+// tile (bi, bj) of L R is sum_k L[bi rows][k] R[bj rows][k]: both operands are
+// read row-wise (K-contiguous), exactly like the Gram.  s_pad x s_pad
+// matrices are small (768 for the Mamba-2 projections), so the tile is
+// 128 x 128 (21 upper tiles per 768 x 768 matrix instead of 6): four waves of
+// 64 x 64, two workgroups per CU.
+constexpr int T2 = kSymTile;
+constexpr int NTHR2 = 256;
+constexpr int OPB2 = T2 * BK * 2;  // 8 KB per operand per stage
+
+// 128 x 128 output tile staged as two 64-row slabs of 256-byte rows (16-byte
+// chunks XOR-swizzled by row & 15).
+__device__ __forceinline__ int slab2_off(int r, int col) {
+  return r * 256 + ((((col >> 3) ^ (r & 15))) << 4) + (col & 7) * 2;
+}
+
+__device__ __forceinline__ void slabs2_to_global(const char* b0, const char* b1, bf16_t* dst, bf16_t* dst2,
+                                                 long long off, long long ld, float a2, float b2, bool dg) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int q = threadIdx.x + NTHR2 * u;  // 2048 chunks of 16 B
+    const int r = q >> 4, c = q & 15, rr = r & 63;
+    const char* b = u < 4 ? b0 : b1;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(b + rr * 256 + ((c ^ (rr & 15)) << 4));
+    const long long o = off + static_cast<long long>(r) * ld + c * 8;
+    if (dst != nullptr) *reinterpret_cast<u32x4_t*>(dst + o) = v;
+    if (dst2 != nullptr) *reinterpret_cast<u32x4_t*>(dst2 + o) = affine8(v, a2, b2, dg ? r - c * 8 : -1);
+  }
+}
+
+__global__ void __launch_bounds__(NTHR2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+symprod_bf16_kernel(SymArgs G) {
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB2];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB2];
+  __shared__ __attribute__((aligned(1024))) char lds2[2 * OPB2];
+  __shared__ __attribute__((aligned(1024))) char lds3[2 * OPB2];
+  __shared__ float red[NTHR2 / 64];
+  const Bufs bufs{{lds0, lds1, lds2, lds3}};
+  constexpr int WM = 64, WN = 64, FM = WM / 32, FN = WN / 32;  // waves: 2 x 2 of 64 x 64
+  const int lane = threadIdx.x & 63, wid = wave_id();
+  const int wm = wid >> 1, wn = wid & 1;
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = rfrag_off(ks, lane);
+
+  // Persistent: the workgroups of XCD x walk that XCD's tile list with a
+  // stride of their number, so the stores of one tile drain while the next
+  // tile's first stages load.
+  const int x = blockIdx.x % NXCD, per_xcd = gridDim.x / NXCD;
+  for (int local = blockIdx.x / NXCD;; local += per_xcd) {
+    int si, tile;
+    if (!find_tile_at(G, x, local, si, tile)) break;
+    const SymSeg& S = G.seg[si];
+    const int z = tile / S.tiles_per_mat;
+    int bi, bj;
+    upper_tile(tile % S.tiles_per_mat, S.s_pad / T2, bi, bj);
+    const bool diag = bi == bj;
+    const bool single = diag && S.L == S.R;  // both operands are the same rows
+    const long long zoff = z * S.stride;
+    const float inv = seg_inv(S, z, red);
+    const float ia = ipow(inv, S.pa), ib = ipow(inv, S.pb);
+
+    Acc<FM, FN> acc;
+    acc.zero();
+    const int sp_bytes = S.s_pad * 2;
+    const long long mbytes = static_cast<long long>(S.s_pad) * sp_bytes;
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(S.L + zoff, mbytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(S.R + zoff, mbytes);
+    const int voff = row_voff(sp_bytes);
+    const int offL = bi * T2 * sp_bytes, offR = bj * T2 * sp_bytes;
+    const int nk = S.s_pad / BK;
+
+    auto mma = [&](const char* buf, bool one) {
+      const char* ta = buf + wm * WM * 64;
+      const char* tb = (one ? buf : buf + OPB2) + wn * WN * 64;
+      stage_mma<FM, FN>(acc, [&](int ks, int i) { return frag_at(ta + roff[ks] + i * 32 * 64); },
+                        [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); });
+    };
+    if (single) {
+      pipeline<2>(bufs, nk, [&](char* buf, int kt) { load_rows(buf, lr, voff, sp_bytes, offL + kt * BK * 2); },
+                  [&](const char* buf) { mma(buf, true); });
+    } else {
+      pipeline<4>(bufs, nk,
+                  [&](char* buf, int kt) {
+                    load_rows(buf, lr, voff, sp_bytes, offL + kt * BK * 2);
+                    load_rows(buf + OPB2, rr, voff, sp_bytes, offR + kt * BK * 2);
+                  },
+                  [&](const char* buf) { mma(buf, false); });
+    }
+
+    // epilogue: D[m][n] = (L R)[bi*T2 + m][bj*T2 + n]; lane: 4 consecutive m
+    // at one n.  The mirrored tile is staged in buffers 0-1 and (off the
+    // diagonal) the tile itself in buffers 2-3, then both leave as whole
+    // rows; O2 is the affine image of O1's rounded values.
+    stage_sync<0>();
+    const float a1 = S.a1 * ia, b1 = S.b1 * ib;
+    const int lane_e = opaque(lane);
+    const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;  // buffers and rows below are uniform per wave
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * WN + j * 32 + col;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = wm * WM + i * 32 + q * 8 + rq;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = b1 * acc.c[i][j][4 * q + r] + ((diag && m + r == n) ? a1 : 0.0f);
+          *reinterpret_cast<u32x2_t*>(bufs[wn] + slab2_off(j * 32 + col, m)) =
+              u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          if (!diag) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              *reinterpret_cast<bf16_t*>(bufs[2 + wm] + slab2_off(i * 32 + q * 8 + rq + r, n)) = f32_to_bf16(v[r]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    bf16_t* O1 = S.O1 == nullptr ? nullptr : S.O1 + zoff;
+    bf16_t* O2 = S.O2 == nullptr ? nullptr : S.O2 + zoff;
+    const long long mir = static_cast<long long>(bj) * T2 * S.s_pad + bi * T2;
+    slabs2_to_global(lds0, lds1, O1, O2, mir, S.s_pad, S.a2, S.b2, diag);
+    if (!diag) {
+      const long long dir = static_cast<long long>(bi) * T2 * S.s_pad + bj * T2;
+      slabs2_to_global(lds2, lds3, O1, O2, dir, S.s_pad, S.a2, S.b2, false);
+    }
+    __syncthreads();  // staging read out before the next tile's fills land
+  }
+}
+
+template <class Args>
+int grid_for(const Args& G) {
   int per_xcd = 0;
   for (int s = 0; s < G.nseg; ++s) {
     const int tot = G.seg[s].count * G.seg[s].tiles_per_mat;
@@ -504,6 +675,28 @@ int gram_tiles_per_matrix(int s_pad) {
   return nt * (nt + 1) / 2;
 }
 int combine_tiles_per_matrix(int s_pad, int ld) { return (s_pad / T) * (ld / T); }
+int symprod_tiles_per_matrix(int s_pad) {
+  const int nt = s_pad / T2;
+  return nt * (nt + 1) / 2;
+}
+
+hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st) {
+  // persistent: two resident workgroups per CU (LDS bound), a multiple of
+  // the XCD count
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const int slots = (2 * cus) / NXCD * NXCD;
+  const int need = grid_for(G);
+  const int grid = need < slots ? need : slots;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(symprod_bf16_kernel, dim3(grid), dim3(NTHR2), 0, st, G);
+  return hipGetLastError();
+}
 
 hipError_t launch_gram_bf16(const GemmArgs& G, hipStream_t st) {
   const int grid = grid_for(G);

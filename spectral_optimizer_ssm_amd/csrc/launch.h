@@ -64,13 +64,18 @@ constexpr int kMaxSeg = 4;
 struct GemmSeg {
   const bf16_t* X;     // iterate in  [count][s_pad][ld]
   bf16_t* Y;           // iterate out (combine)
-  bf16_t* A;           // A' = alpha I + beta X X^T  [count][s_pad][s_pad]
+  bf16_t* A;           // Gram out 1 / combine's left operand  [count][s_pad][s_pad]
+  bf16_t* A2;          // Gram out 2 (null: none)
   long long xstride, astride;
   int s_pad, ld, kdim, count, tiles_per_mat;
-  const float* partials;  // step 1: fold 1/(nu+eps) into alpha, beta
+  // Gram outputs: A = a inv^pa I + b inv^pb X X^T and A2 = a2 I + b2 A (from
+  // A's rounded values), inv = 1 / (sqrt(sum of partials) + eps), or 1 when
+  // partials is null.
+  const float* partials;
   int P;
   float eps;
-  float a, b;          // step coefficients
+  float a, b, a2, b2;
+  int pa, pb;
 };
 struct GemmArgs {
   GemmSeg seg[kMaxSeg];
@@ -80,6 +85,32 @@ int gram_tiles_per_matrix(int s_pad);
 int combine_tiles_per_matrix(int s_pad, int ld);
 hipError_t launch_gram_bf16(const GemmArgs& G, hipStream_t st);
 hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st);
+
+// Products of two symmetric, commuting s_pad x s_pad bf16 matrices (both
+// polynomials in the same Gram matrix), whose product is symmetric too:
+// O1 = a1 inv^pa I + b1 inv^pb L R and (optional) O2 = a2 I + b2 O1 from
+// O1's rounded values.  Only tiles on or above the diagonal are computed;
+// each is stored in place and mirrored.
+constexpr int kSymTile = 128;
+struct SymSeg {
+  const bf16_t* L;     // left factor   [count][s_pad][s_pad]
+  const bf16_t* R;     // right factor  (may equal L)
+  bf16_t* O1;
+  bf16_t* O2;          // null: none
+  long long stride;    // elements between consecutive matrices (all four)
+  int s_pad, count, tiles_per_mat;
+  const float* partials;
+  int P;
+  float eps;
+  float a1, b1, a2, b2;
+  int pa, pb;
+};
+struct SymArgs {
+  SymSeg seg[kMaxSeg];
+  int nseg;
+};
+int symprod_tiles_per_matrix(int s_pad);
+hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st);
 
 // float32 path (tile multiples: s_pad % 64 == 0, ld % 64 == 0).
 constexpr int kTileF32 = 64;

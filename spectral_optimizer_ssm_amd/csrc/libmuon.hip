@@ -35,6 +35,7 @@ size_t dtype_size(int dt) { return dt == MUON_BF16 ? 2 : 4; }
 
 struct NsCoefs {
   int steps;
+  int schedule;
   float a[kMaxSteps], b[kMaxSteps];
 };
 
@@ -44,8 +45,11 @@ int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out) {
   if (cfg->ncoef != 2 && cfg->ncoef != 3) return MUON_EINVAL;
   if (!(cfg->eps >= 0.0f) || !std::isfinite(cfg->eps)) return MUON_EINVAL;
   if (cfg->precision != MUON_F32 && cfg->precision != MUON_BF16) return MUON_EINVAL;
+  if (cfg->schedule != MUON_NS_AUTO && cfg->schedule != MUON_NS_ITERATE && cfg->schedule != MUON_NS_ACCUMULATE)
+    return MUON_EINVAL;
   if (cfg->steps > 0 && cfg->coeffs == nullptr) return MUON_EINVAL;
   out->steps = cfg->steps;
+  out->schedule = cfg->schedule;
   for (int k = 0; k < cfg->steps; ++k) {
     const float* row = cfg->coeffs + (cfg->per_step ? k * cfg->ncoef : 0);
     if (!std::isfinite(row[0]) || !std::isfinite(row[1])) return MUON_EINVAL;
@@ -66,12 +70,29 @@ struct GroupPlan {
   int m = 0, n = 0, s = 0, l = 0, count = 0;
   bool tall = false, bf16 = false;
   Engine engine = kSmall;
+  bool accumulate = false;  // Newton-Schulz as a polynomial in X0 X0^T (bf16 tiled only)
   int s_pad = 0, ld = 0, kdim = 0, P = 0;
   size_t esz = 0;
   size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_part = 0, end = 0;
 };
 
-int plan_group(int m, int n, int count, bool bf16, size_t base, GroupPlan* g) {
+// s_pad x s_pad buffers of the accumulated schedule, after the iterates.
+enum SqBuf { kSqA0 = 0, kSqA1, kSqB0, kSqB1, kSqE, kSqQ0, kSqQ1, kSqCount };
+
+// Matrix-core work of the two schedules (multiply-adds of the tiles actually
+// computed): per step a Gram (kdim deep) and a combine (s_pad deep), against
+// one Gram, one combine and 3 (steps - 1) symmetric s_pad^3 products.
+bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
+  if (g.engine != kTiledBf16 || C.steps < 2 || C.schedule == MUON_NS_ITERATE) return false;
+  if (C.schedule == MUON_NS_ACCUMULATE) return true;
+  const double t = kTileS, t2 = kSymTile;
+  const double gram = gram_tiles_per_matrix(g.s_pad) * t * t * g.kdim;
+  const double comb = combine_tiles_per_matrix(g.s_pad, g.ld) * t * t * g.s_pad;
+  const double prod = symprod_tiles_per_matrix(g.s_pad) * t2 * t2 * g.s_pad;
+  return gram + comb + 3.0 * (C.steps - 1) * prod < 0.85 * C.steps * (gram + comb);
+}
+
+int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base, GroupPlan* g) {
   if (m <= 0 || n <= 0 || count < 0) return MUON_EINVAL;
   if (static_cast<long long>(m) * n > (1LL << 31)) return MUON_EUNSUPPORTED;
   g->m = m;
@@ -96,6 +117,7 @@ int plan_group(int m, int n, int count, bool bf16, size_t base, GroupPlan* g) {
     g->ld = round_up(g->l, kTileF32);
   }
   g->kdim = std::min(g->ld, round_up(g->l, 64));
+  g->accumulate = choose_accumulate(*g, C);
   g->P = momentum_blocks_per_matrix(g->tall, g->s_pad, g->ld);
   const size_t xbytes = static_cast<size_t>(count) * g->s_pad * g->ld * g->esz;
   size_t off = align_up(base, kAlign);
@@ -104,7 +126,9 @@ int plan_group(int m, int n, int count, bool bf16, size_t base, GroupPlan* g) {
   g->off_x1 = off;
   off = align_up(off + xbytes, kAlign);
   g->off_a = off;
-  if (g->engine != kSmall) off = align_up(off + static_cast<size_t>(count) * g->s_pad * g->s_pad * g->esz, kAlign);
+  if (g->engine != kSmall)
+    off = align_up(off + (g->accumulate ? kSqCount : 1) * static_cast<size_t>(count) * g->s_pad * g->s_pad * g->esz,
+                   kAlign);
   g->off_part = off;
   off = align_up(off + static_cast<size_t>(count) * g->P * sizeof(float), kAlign);
   g->end = off;
@@ -141,35 +165,46 @@ struct GroupRun {
 };
 
 // Optional phase markers: caller-created events recorded on the stream after
-// launches of the schedule (profiling only; the arithmetic is unchanged).
+// each phase of the schedule (profiling only; the arithmetic is unchanged).
+// A dry run launches nothing and only lists the phases.
 struct EventRec {
   void* const* ev = nullptr;
   int n = 0, used = 0;
-  bool mark(hipStream_t st) {
+  bool dry = false;
+  std::vector<int> phases;
+  bool mark(hipStream_t st, int phase) {
+    if (dry) {
+      phases.push_back(phase);
+      return true;
+    }
     if (ev == nullptr) return true;
     if (used >= n) return false;
     return hipEventRecord(static_cast<hipEvent_t>(ev[used++]), st) == hipSuccess;
   }
+  bool live() const { return !dry; }
 };
-
-int events_needed(const std::vector<GroupRun>& runs, int steps) {
-  int n = 1, tiled_bf16 = 0;
-  for (const GroupRun& r : runs) {
-    if (r.plan.count == 0) continue;
-    n += 2;  // momentum, apply
-    if (steps > 0 && r.plan.engine == kSmall) n += 1;
-    if (steps > 0 && r.plan.engine == kTiledF32) n += 2 * steps;
-    if (r.plan.engine == kTiledBf16) tiled_bf16 = 1;
-  }
-  if (steps > 0 && tiled_bf16) n += 2 * steps;
-  return n;
-}
 
 char* x_of(const GroupPlan& p, char* ws, int which) { return ws + (which ? p.off_x1 : p.off_x0); }
 
+bf16_t* sq_of(const GroupPlan& p, char* ws, int which) {
+  return reinterpret_cast<bf16_t*>(ws + p.off_a + static_cast<size_t>(which) * p.count * p.s_pad * p.s_pad * p.esz);
+}
+
+// Grouped launches of up to kMaxSeg segments each.
+template <class Args, class Seg, class Launch>
+bool launch_segments(const std::vector<Seg>& segs, Launch launch, hipStream_t st, bool live) {
+  for (size_t c0 = 0; c0 < segs.size(); c0 += kMaxSeg) {
+    Args G{};
+    G.nseg = static_cast<int>(std::min<size_t>(kMaxSeg, segs.size() - c0));
+    for (int i = 0; i < G.nseg; ++i) G.seg[i] = segs[c0 + i];
+    if (live && launch(G, st) != hipSuccess) return false;
+  }
+  return true;
+}
+
 int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, float* norms_out, hipStream_t st,
             EventRec& E) {
-  if (!E.mark(st)) return MUON_EHIP;
+  if (!E.mark(st, 0)) return MUON_EHIP;
   // 1. momentum
   int base = 0;
   for (GroupRun& R : runs) {
@@ -177,7 +212,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     if (p.count == 0) continue;
     const long long xstride = static_cast<long long>(p.s_pad) * p.ld;
     float* part = reinterpret_cast<float*>(ws + p.off_part);
-    for (int c0 = 0; c0 < p.count; c0 += kMaxTable) {
+    for (int c0 = 0; E.live() && c0 < p.count; c0 += kMaxTable) {
       const int cn = std::min(kMaxTable, p.count - c0);
       MomentumLaunch L{};
       for (int i = 0; i < cn; ++i) {
@@ -192,10 +227,10 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       L.partials = part + static_cast<size_t>(c0) * p.P;
       if (launch_momentum(L, st) != hipSuccess) return MUON_EHIP;
     }
-    if (norms_out != nullptr && launch_norms(part, p.P, p.count, norms_out + base, st) != hipSuccess)
+    if (E.live() && norms_out != nullptr && launch_norms(part, p.P, p.count, norms_out + base, st) != hipSuccess)
       return MUON_EHIP;
     base += p.count;
-    if (!E.mark(st)) return MUON_EHIP;
+    if (!E.mark(st, MUON_PHASE_MOMENTUM)) return MUON_EHIP;
   }
 
   // 2. small matrices on chip
@@ -211,47 +246,143 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     S.count = p.count; S.transposed = false; S.steps = C.steps;
     for (int k = 0; k < C.steps; ++k) { S.a[k] = C.a[k]; S.b[k] = C.b[k]; }
     S.partials = reinterpret_cast<const float*>(ws + p.off_part); S.P = p.P; S.eps = eps;
-    if (launch_ns_small(S, p.bf16, st) != hipSuccess) return MUON_EHIP;
+    if (E.live() && launch_ns_small(S, p.bf16, st) != hipSuccess) return MUON_EHIP;
     fin[gi] = 1;
-    if (!E.mark(st)) return MUON_EHIP;
+    if (!E.mark(st, MUON_PHASE_NS_SMALL)) return MUON_EHIP;
   }
 
-  // 3. large bf16 matrices, grouped launches
-  std::vector<int> tb;
-  for (size_t gi = 0; gi < runs.size(); ++gi)
-    if (runs[gi].plan.count > 0 && runs[gi].plan.engine == kTiledBf16) tb.push_back(static_cast<int>(gi));
-  if (!tb.empty() && C.steps > 0) {
-    std::vector<int> by_k = tb, by_s = tb;  // heaviest tiles first
-    std::stable_sort(by_k.begin(), by_k.end(), [&](int x, int y) { return runs[x].plan.kdim > runs[y].plan.kdim; });
-    std::stable_sort(by_s.begin(), by_s.end(), [&](int x, int y) { return runs[x].plan.s_pad > runs[y].plan.s_pad; });
+  // 3. large bf16 matrices, grouped launches: the iterated schedule first,
+  //    then the accumulated one
+  std::vector<int> it, ac;
+  for (size_t gi = 0; gi < runs.size(); ++gi) {
+    const GroupPlan& p = runs[gi].plan;
+    if (p.count > 0 && p.engine == kTiledBf16) (p.accumulate ? ac : it).push_back(static_cast<int>(gi));
+  }
+  auto heavy_first = [&](std::vector<int> v, bool by_kdim) {
+    std::stable_sort(v.begin(), v.end(), [&](int x, int y) {
+      return by_kdim ? runs[x].plan.kdim > runs[y].plan.kdim : runs[x].plan.s_pad > runs[y].plan.s_pad;
+    });
+    return v;
+  };
+  auto gemm_seg = [&](const GroupPlan& p, bool gram) {
+    GemmSeg S{};
+    S.xstride = static_cast<long long>(p.s_pad) * p.ld;
+    S.astride = static_cast<long long>(p.s_pad) * p.s_pad;
+    S.s_pad = p.s_pad; S.ld = p.ld; S.kdim = p.kdim; S.count = p.count;
+    S.tiles_per_mat = gram ? gram_tiles_per_matrix(p.s_pad) : combine_tiles_per_matrix(p.s_pad, p.ld);
+    S.P = p.P; S.eps = eps;
+    return S;
+  };
+  if (!it.empty() && C.steps > 0) {
+    // per step: A' = a I + b X X^T (step 1 on the unnormalised U, with the
+    // normalisation folded into the coefficients), then X = A' X
+    const std::vector<int> by_k = heavy_first(it, true), by_s = heavy_first(it, false);
     for (int k = 0; k < C.steps; ++k) {
-      for (int pass = 0; pass < 2; ++pass) {
-        const std::vector<int>& order = pass == 0 ? by_k : by_s;
-        for (size_t c0 = 0; c0 < order.size(); c0 += kMaxSeg) {
-          GemmArgs G{};
-          G.nseg = static_cast<int>(std::min<size_t>(kMaxSeg, order.size() - c0));
-          for (int si = 0; si < G.nseg; ++si) {
-            const GroupPlan& p = runs[order[c0 + si]].plan;
-            GemmSeg& S = G.seg[si];
-            const int cur = k & 1;
-            S.X = reinterpret_cast<const bf16_t*>(x_of(p, ws, cur));
-            S.Y = reinterpret_cast<bf16_t*>(x_of(p, ws, cur ^ 1));
-            S.A = reinterpret_cast<bf16_t*>(ws + p.off_a);
-            S.xstride = static_cast<long long>(p.s_pad) * p.ld;
-            S.astride = static_cast<long long>(p.s_pad) * p.s_pad;
-            S.s_pad = p.s_pad; S.ld = p.ld; S.kdim = p.kdim; S.count = p.count;
-            S.tiles_per_mat = pass == 0 ? gram_tiles_per_matrix(p.s_pad) : combine_tiles_per_matrix(p.s_pad, p.ld);
-            S.partials = k == 0 ? reinterpret_cast<const float*>(ws + p.off_part) : nullptr;
-            S.P = p.P; S.eps = eps;
-            S.a = C.a[k]; S.b = C.b[k];
-          }
-          const hipError_t e = pass == 0 ? launch_gram_bf16(G, st) : launch_combine_bf16(G, st);
-          if (e != hipSuccess) return MUON_EHIP;
-        }
-        if (!E.mark(st)) return MUON_EHIP;
+      const int cur = k & 1;
+      std::vector<GemmSeg> gs, cs;
+      for (int gi : by_k) {
+        const GroupPlan& p = runs[gi].plan;
+        GemmSeg S = gemm_seg(p, true);
+        S.X = reinterpret_cast<const bf16_t*>(x_of(p, ws, cur));
+        S.A = sq_of(p, ws, 0);
+        S.partials = k == 0 ? reinterpret_cast<const float*>(ws + p.off_part) : nullptr;
+        S.a = C.a[k]; S.b = C.b[k];
+        S.pa = k == 0 ? 1 : 0; S.pb = k == 0 ? 3 : 0;
+        gs.push_back(S);
       }
+      for (int gi : by_s) {
+        const GroupPlan& p = runs[gi].plan;
+        GemmSeg S = gemm_seg(p, false);
+        S.X = reinterpret_cast<const bf16_t*>(x_of(p, ws, cur));
+        S.Y = reinterpret_cast<bf16_t*>(x_of(p, ws, cur ^ 1));
+        S.A = sq_of(p, ws, 0);
+        cs.push_back(S);
+      }
+      if (!launch_segments<GemmArgs>(gs, launch_gram_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_GRAM) ||
+          !launch_segments<GemmArgs>(cs, launch_combine_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_COMBINE))
+        return MUON_EHIP;
     }
-    for (int gi : tb) fin[gi] = C.steps & 1;
+    for (int gi : it) fin[gi] = C.steps & 1;
+  }
+  if (!ac.empty()) {
+    // Every step's factor is a polynomial in A_0 = X0 X0^T (X0 normalised), so
+    // with B_k = a_k I + b_k A_k the steps are
+    //   A_{k+1} = A_k B_k^2,   Q = B_{steps-1} ... B_1 B_0,   X = Q X0,
+    // s_pad x s_pad products instead of s_pad x ld ones.  Buffers: A_k in
+    // A[k & 1], B_k in B[k & 1], E = B_k^2, Q_1 = B_0, Q_k (k >= 2) in Q[k & 1].
+    const int n = C.steps;
+    const std::vector<int> by_k = heavy_first(ac, true), by_s = heavy_first(ac, false);
+    std::vector<GemmSeg> gs;
+    for (int gi : by_k) {
+      const GroupPlan& p = runs[gi].plan;
+      GemmSeg S = gemm_seg(p, true);
+      S.X = reinterpret_cast<const bf16_t*>(x_of(p, ws, 0));
+      S.A = sq_of(p, ws, kSqA0);
+      S.A2 = sq_of(p, ws, kSqB0);
+      S.partials = reinterpret_cast<const float*>(ws + p.off_part);
+      S.a = 0.0f; S.b = 1.0f; S.pa = 0; S.pb = 2;  // A_0 = inv^2 U U^T
+      S.a2 = C.a[0]; S.b2 = C.b[0];                // B_0
+      gs.push_back(S);
+    }
+    if (!launch_segments<GemmArgs>(gs, launch_gram_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_GRAM))
+      return MUON_EHIP;
+    auto sym_seg = [&](const GroupPlan& p) {
+      SymSeg S{};
+      S.stride = static_cast<long long>(p.s_pad) * p.s_pad;
+      S.s_pad = p.s_pad; S.count = p.count; S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);
+      S.P = p.P; S.eps = eps;
+      S.b1 = 1.0f;
+      return S;
+    };
+    for (int k = 0; k < n; ++k) {
+      std::vector<SymSeg> l1, l2;
+      for (int gi : ac) {
+        const GroupPlan& p = runs[gi].plan;
+        bf16_t* Bk = sq_of(p, ws, kSqB0 + (k & 1));
+        if (k + 1 < n) {  // E = B_k B_k
+          SymSeg S = sym_seg(p);
+          S.L = Bk; S.R = Bk; S.O1 = sq_of(p, ws, kSqE);
+          l1.push_back(S);
+        }
+        if (k >= 1) {  // Q_{k+1} = B_k Q_k; the last one carries the normalisation
+          SymSeg S = sym_seg(p);
+          S.L = Bk;
+          S.R = k == 1 ? sq_of(p, ws, kSqB0) : sq_of(p, ws, kSqQ0 + (k & 1));
+          S.O1 = sq_of(p, ws, kSqQ0 + ((k + 1) & 1));
+          if (k + 1 == n) {
+            S.partials = reinterpret_cast<const float*>(ws + p.off_part);
+            S.pb = 1;
+          }
+          l1.push_back(S);
+        }
+        if (k + 1 < n) {  // A_{k+1} = A_k E, B_{k+1} = a I + b A_{k+1}
+          SymSeg S = sym_seg(p);
+          S.L = sq_of(p, ws, kSqA0 + (k & 1));
+          S.R = sq_of(p, ws, kSqE);
+          S.O1 = k + 2 < n ? sq_of(p, ws, kSqA0 + ((k + 1) & 1)) : nullptr;  // the last A is not needed
+          S.O2 = sq_of(p, ws, kSqB0 + ((k + 1) & 1));
+          S.a2 = C.a[k + 1]; S.b2 = C.b[k + 1];
+          l2.push_back(S);
+        }
+      }
+      if (!launch_segments<SymArgs>(l1, launch_symprod_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_SYMPROD))
+        return MUON_EHIP;
+      if (!l2.empty() &&
+          (!launch_segments<SymArgs>(l2, launch_symprod_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_SYMPROD)))
+        return MUON_EHIP;
+    }
+    std::vector<GemmSeg> cs;
+    for (int gi : by_s) {
+      const GroupPlan& p = runs[gi].plan;
+      GemmSeg S = gemm_seg(p, false);
+      S.X = reinterpret_cast<const bf16_t*>(x_of(p, ws, 0));
+      S.Y = reinterpret_cast<bf16_t*>(x_of(p, ws, 1));
+      S.A = sq_of(p, ws, kSqQ0 + (n & 1));
+      cs.push_back(S);
+    }
+    if (!launch_segments<GemmArgs>(cs, launch_combine_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_COMBINE))
+      return MUON_EHIP;
+    for (int gi : ac) fin[gi] = 1;
   }
 
   // 4. large fp32 matrices
@@ -270,8 +401,9 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       L.partials = k == 0 ? reinterpret_cast<const float*>(ws + p.off_part) : nullptr;
       L.P = p.P; L.eps = eps;
       L.alpha = C.a[k]; L.beta = C.b[k];
-      if (launch_gram_f32(L, st) != hipSuccess || !E.mark(st)) return MUON_EHIP;
-      if (launch_combine_f32(L, st) != hipSuccess || !E.mark(st)) return MUON_EHIP;
+      if ((E.live() && launch_gram_f32(L, st) != hipSuccess) || !E.mark(st, MUON_PHASE_F32_GRAM)) return MUON_EHIP;
+      if ((E.live() && launch_combine_f32(L, st) != hipSuccess) || !E.mark(st, MUON_PHASE_F32_COMBINE))
+        return MUON_EHIP;
     }
     fin[gi] = C.steps & 1;
   }
@@ -281,7 +413,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     const GroupRun& R = runs[gi];
     const GroupPlan& p = R.plan;
     if (p.count == 0) continue;
-    if (R.W != nullptr || R.O != nullptr) {
+    if (E.live() && (R.W != nullptr || R.O != nullptr)) {
       const long long xstride = static_cast<long long>(p.s_pad) * p.ld;
       for (int c0 = 0; c0 < p.count; c0 += kMaxTable) {
         const int cn = std::min(kMaxTable, p.count - c0);
@@ -301,9 +433,19 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
         if (launch_apply(A, st) != hipSuccess) return MUON_EHIP;
       }
     }
-    if (!E.mark(st)) return MUON_EHIP;
+    if (!E.mark(st, MUON_PHASE_APPLY)) return MUON_EHIP;
   }
   return MUON_OK;
+}
+
+// The marks run_all makes, in order (the first is the start mark, phase 0),
+// from a dry run that launches nothing and touches no memory.
+std::vector<int> list_phases(std::vector<GroupRun>& runs, const NsCoefs& C, float eps) {
+  EventRec D;
+  D.dry = true;
+  char* fake_ws = reinterpret_cast<char*>(static_cast<uintptr_t>(kAlign));
+  run_all(runs, C, eps, fake_ws, nullptr, nullptr, D);
+  return D.phases;
 }
 
 int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, void* workspace, size_t workspace_bytes,
@@ -322,7 +464,7 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
     if (gr.O != nullptr)
       for (int j = 0; j < gr.count; ++j)
         if (!aligned_to(gr.O[j], dtype_size(cfg->precision))) return MUON_EINVAL;
-    rc = plan_group(gr.m, gr.n, gr.count, cfg->precision == MUON_BF16, off, &runs[i].plan);
+    rc = plan_group(gr.m, gr.n, gr.count, cfg->precision == MUON_BF16, C, off, &runs[i].plan);
     if (rc != MUON_OK) return rc;
     off = runs[i].plan.end;
     runs[i].grad_dtype = gr.grad_dtype;
@@ -337,7 +479,7 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < off) return MUON_EWORKSPACE;
   EventRec E;
   if (events != nullptr) {
-    const int need = events_needed(runs, C.steps);
+    const int need = static_cast<int>(list_phases(runs, C, cfg->eps).size());
     if (nevents < need) return MUON_EINVAL;
     for (int i = 0; i < need; ++i)
       if (events[i] == nullptr) return MUON_EINVAL;
@@ -370,7 +512,7 @@ size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muo
   size_t off = 0;
   for (int i = 0; i < ngroups; ++i) {
     GroupPlan g;
-    if (plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, off, &g) != MUON_OK)
+    if (plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &g) != MUON_OK)
       return 0;
     off = g.end;
   }
@@ -380,6 +522,27 @@ size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muo
 int muon_step(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, void* workspace,
               size_t workspace_bytes, float* norms_out, void* stream) {
   return step_impl(groups, ngroups, cfg, workspace, workspace_bytes, norms_out, stream, nullptr, 0);
+}
+
+int muon_step_phases(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, int* phases, int max_phases) {
+  NsCoefs C;
+  if (groups == nullptr || ngroups <= 0 || max_phases < 0 || (phases == nullptr && max_phases > 0))
+    return MUON_EINVAL;
+  int rc = parse_cfg(cfg, &C);
+  if (rc != MUON_OK) return rc;
+  std::vector<GroupRun> runs(ngroups);
+  size_t off = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    if (groups[i].grad_dtype != MUON_F32 && groups[i].grad_dtype != MUON_BF16) return MUON_EINVAL;
+    rc = plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &runs[i].plan);
+    if (rc != MUON_OK) return rc;
+    off = runs[i].plan.end;
+    runs[i].grad_dtype = groups[i].grad_dtype;
+  }
+  const std::vector<int> marks = list_phases(runs, C, cfg->eps);
+  const int n = static_cast<int>(marks.size()) - 1;
+  for (int i = 0; i < n && i < max_phases; ++i) phases[i] = marks[i + 1];
+  return n;
 }
 
 int muon_step_timed(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, void* workspace,
@@ -392,7 +555,7 @@ size_t muon_ns_workspace_size(int m, int n, int batch, int dtype, const muon_ns_
   NsCoefs C;
   if (parse_cfg(cfg, &C) != MUON_OK || (dtype != MUON_F32 && dtype != MUON_BF16)) return 0;
   GroupPlan g;
-  if (plan_group(m, n, batch, dtype == MUON_BF16, 0, &g) != MUON_OK) return 0;
+  if (plan_group(m, n, batch, dtype == MUON_BF16, C, 0, &g) != MUON_OK) return 0;
   return g.end == 0 ? kAlign : g.end;
 }
 
@@ -409,7 +572,7 @@ int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int b
     return MUON_EINVAL;
   std::vector<GroupRun> runs(1);
   GroupRun& R = runs[0];
-  rc = plan_group(m, n, batch, dtype == MUON_BF16, 0, &R.plan);
+  rc = plan_group(m, n, batch, dtype == MUON_BF16, C, 0, &R.plan);
   if (rc != MUON_OK) return rc;
   const size_t mat = static_cast<size_t>(m) * n * dtype_size(dtype);
   const char* gb = static_cast<const char*>(G);

@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 1
+    assert mu.muon_version() == 2
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -85,6 +85,7 @@ def test_workspace_queries(mu):
     ("steps_negative", -1), ("steps_too_many", -1), ("ncoef_4", -1), ("quintic_c", -2),
     ("bad_precision", -1), ("null_groups", -1), ("misaligned", -1), ("null_matrix", -1),
     ("no_workspace", -3), ("small_workspace", -3), ("bad_dtype", -1), ("negative_eps", -1),
+    ("bad_schedule", -1),
 ])
 def test_step_validation(mu, case, expect):
     L = mu.lib()
@@ -94,6 +95,8 @@ def test_step_validation(mu, case, expect):
                      prec=9 if case == "bad_precision" else None)
     if case == "ncoef_4":
         cfg.ncoef = 4
+    if case == "bad_schedule":
+        cfg.schedule = 3
     g, k2 = _group(mu, dtype=5 if case == "bad_dtype" else None)
     if case == "misaligned":
         k2[0][0] = 0x100002  # W is float32: 4-byte alignment required
@@ -120,3 +123,48 @@ def test_small_and_ns_validation(mu):
     assert L.muon_ns_orthogonalize(x, x, mu.MUON_BF16, 64, 128, 2, ctypes.byref(cfg), y, 1 << 30, None) == -1
     assert L.muon_ns_orthogonalize(x, y, mu.MUON_BF16, 64, 128, 2, ctypes.byref(cfg), None, 0, None) == -3
     assert L.muon_ns_orthogonalize(x, y, mu.MUON_BF16, 64, 128, 0, ctypes.byref(cfg), None, 0, None) == 0
+
+
+def _phases(mu, shapes, steps, schedule, prec=None):
+    L = mu.lib()
+    cfg, keep = mu.make_cfg(steps, (1.5, -0.5), 1e-7, mu.MUON_BF16 if prec is None else prec, False, schedule)
+    gs = [_group(mu, m, n, c) for m, n, c in shapes]
+    arr = (mu.binding.GroupC * len(gs))(*[g for g, _ in gs])
+    n = L.muon_step_phases(arr, len(gs), ctypes.byref(cfg), None, 0)
+    out = (ctypes.c_int * max(n, 1))()
+    assert L.muon_step_phases(arr, len(gs), ctypes.byref(cfg), out, n) == n
+    return [mu.binding.PHASES[out[i]] for i in range(n)]
+
+
+MAMBA = [(768, 1536, 24), (3352, 768, 24)]
+
+
+def test_phases_iterate_and_accumulate(mu):
+    it = _phases(mu, MAMBA, 5, mu.MUON_NS_ITERATE)
+    assert it == ["momentum"] * 2 + ["gram", "combine"] * 5 + ["apply"] * 2
+    ac = _phases(mu, MAMBA, 5, mu.MUON_NS_ACCUMULATE)
+    assert ac == ["momentum"] * 2 + ["gram"] + ["symprod"] * 9 + ["combine"] + ["apply"] * 2
+    # the Mamba-2 projections are wide enough for the accumulated schedule to
+    # need fewer matrix-core operations; a square group is not
+    assert _phases(mu, MAMBA, 5, mu.MUON_NS_AUTO) == ac
+    assert _phases(mu, [(768, 768, 4)], 5, mu.MUON_NS_AUTO) == ["momentum"] + ["gram", "combine"] * 5 + ["apply"]
+    # one step, float32 and small matrices always iterate
+    assert _phases(mu, MAMBA, 1, mu.MUON_NS_ACCUMULATE) == ["momentum"] * 2 + ["gram", "combine"] + ["apply"] * 2
+    assert _phases(mu, [(300, 700, 2)], 2, mu.MUON_NS_ACCUMULATE, mu.MUON_F32) == \
+        ["momentum", "f32_gram", "f32_combine", "f32_gram", "f32_combine", "apply"]
+    assert _phases(mu, [(64, 128, 9)], 3, mu.MUON_NS_ACCUMULATE) == ["momentum", "ns_small", "apply"]
+    assert _phases(mu, MAMBA, 0, mu.MUON_NS_AUTO) == ["momentum"] * 2 + ["apply"] * 2
+    # 2 steps: one E = B_0^2, then A_1 / B_1, then Q_2 = B_1 B_0
+    assert _phases(mu, MAMBA, 2, mu.MUON_NS_ACCUMULATE).count("symprod") == 3
+
+
+def test_accumulate_workspace_is_larger(mu):
+    L = mu.lib()
+    g, k2 = _group(mu, 768, 1536, 24)
+    arr = (mu.binding.GroupC * 1)(g)
+    sizes = {}
+    for sch in (mu.MUON_NS_ITERATE, mu.MUON_NS_ACCUMULATE):
+        cfg, keep = mu.make_cfg(5, (1.5, -0.5), 1e-7, mu.MUON_BF16, False, sch)
+        sizes[sch] = L.muon_step_workspace_size(arr, 1, ctypes.byref(cfg))
+    # seven 768 x 768 bf16 buffers per matrix instead of one
+    assert sizes[mu.MUON_NS_ACCUMULATE] - sizes[mu.MUON_NS_ITERATE] >= 24 * 6 * 768 * 768 * 2

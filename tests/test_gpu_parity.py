@@ -33,7 +33,14 @@ def _announce(request):
     yield
 
 
-def run_step(mu, w, precision=None, steps=None, want_o=True, coeffs=None, eps=None):
+SCHEDULES = ["iterate", "accumulate"]
+
+
+def sched(mu, name):
+    return {"auto": mu.MUON_NS_AUTO, "iterate": mu.MUON_NS_ITERATE, "accumulate": mu.MUON_NS_ACCUMULATE}[name]
+
+
+def run_step(mu, w, precision=None, steps=None, want_o=True, coeffs=None, eps=None, schedule="auto"):
     """Run one muon_step over all groups of a workload; returns (devs, outs)."""
     devs, outs, groups = [], [], []
     prec = precision if precision is not None else (mu.MUON_BF16 if w.groups[0].grad_dtype == "bf16" else mu.MUON_F32)
@@ -46,7 +53,7 @@ def run_step(mu, w, precision=None, steps=None, want_o=True, coeffs=None, eps=No
         groups.append(mu.MuonGroup(W=d["W"], M=d["M"], G=d["G"], O=o["O"], lr=w.lr, beta=w.beta,
                                    scale=w.scale, nesterov=w.nesterov))
     mu.muon_step(groups, steps=w.steps if steps is None else steps, coeffs=coeffs or w.coeffs,
-                 eps=w.eps if eps is None else eps, precision=prec)
+                 eps=w.eps if eps is None else eps, precision=prec, schedule=sched(mu, schedule))
     torch.cuda.synchronize()
     return devs, outs
 
@@ -61,17 +68,19 @@ def test_single_fp32_128x64(mu):
     print(res)
 
 
-def test_out_proj_group_full(mu):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_out_proj_group_full(mu, schedule):
     w = wl.config2()
-    devs, outs = run_step(mu, w)
+    devs, outs = run_step(mu, w, schedule=schedule)
     for i in (0, 13, 23):
         res, _ = compare_step(w.groups[0], i, outs[0], devs[0], w, BF16_TOL)
         print(i, res)
 
 
-def test_in_proj_group_full_tall(mu):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_in_proj_group_full_tall(mu, schedule):
     w = wl.config3()
-    devs, outs = run_step(mu, w)
+    devs, outs = run_step(mu, w, schedule=schedule)
     for i in (0, 23):
         res, _ = compare_step(w.groups[0], i, outs[0], devs[0], w, BF16_TOL)
         print(i, res)
@@ -82,15 +91,16 @@ def full_step_inputs():
     return wl.config4()
 
 
-@pytest.mark.parametrize("steps", [1, 3, 5, 8])
-def test_full_mamba2_step(mu, full_step_inputs, steps):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("steps", [1, 2, 3, 5, 8])
+def test_full_mamba2_step(mu, full_step_inputs, steps, schedule):
     w = full_step_inputs
-    devs, outs = run_step(mu, w, steps=steps)
+    devs, outs = run_step(mu, w, steps=steps, schedule=schedule)
     for gi, g in enumerate(w.groups):
         for i in (0, 17):
             res, ref = compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL, steps=steps)
             og = t64(outs[gi]["O"][i])
-            print(g.name, i, steps, res, "orth gpu %.4f oracle %.4f" % (orc.orthogonality_error(og),
+            print(g.name, i, steps, schedule, res, "orth gpu %.4f oracle %.4f" % (orc.orthogonality_error(og),
                                                                           orc.orthogonality_error(ref["O"])))
 
 
@@ -170,13 +180,14 @@ def test_batched_small_fp32(mu, shape):
 # ---------------------------------------------------------------------------
 # ragged shapes, both engines, both precisions
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("schedule", SCHEDULES)
 @pytest.mark.parametrize("shape", [(200, 130), (96, 300), (130, 130), (1, 70), (300, 1), (256, 512),
-                                   (64, 128), (128, 64), (513, 129)])
-def test_ragged_bf16(mu, shape):
+                                   (64, 128), (128, 64), (513, 129), (520, 1100)])
+def test_ragged_bf16(mu, shape, schedule):
     m, n = shape
     g = wl.random_group(100 + m + n, 3, m, n, "bf16")
     w = wl.Workload(f"ragged{m}x{n}", [g])
-    devs, outs = run_step(mu, w)
+    devs, outs = run_step(mu, w, schedule=schedule)
     for i in range(3):
         compare_step(g, i, outs[0], devs[0], w, BF16_TOL)
 
@@ -243,22 +254,24 @@ def test_transpose_equivariance(mu):
         assert orc.rel_frobenius(a, ref) <= BF16_TOL
 
 
-def test_ns_orthogonalize_matches_oracle(mu):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_ns_orthogonalize_matches_oracle(mu, schedule):
     for m, n, dt in ((768, 1536, "bf16"), (3352, 768, "bf16"), (96, 200, "f32")):
         g = wl.random_group(m + n, 2, m, n, dt)
         G = (to_torch_bits(g.G) if dt == "bf16" else torch.from_numpy(g.G)).cuda()
         O = torch.empty_like(G)
-        mu.muon_ns_orthogonalize(G, O, steps=5)
+        mu.muon_ns_orthogonalize(G, O, steps=5, schedule=sched(mu, schedule))
         torch.cuda.synchronize()
         for i in range(2):
             ref, _ = orc.newton_schulz(grad64(g, i), 5)
             assert orc.rel_frobenius(t64(O[i]), ref) <= (BF16_TOL if dt == "bf16" else F32_TOL)
 
 
-def test_deterministic(mu):
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_deterministic(mu, schedule):
     w = wl.config2(count=3)
-    d1, o1 = run_step(mu, w)
-    d2, o2 = run_step(mu, w)
+    d1, o1 = run_step(mu, w, schedule=schedule)
+    d2, o2 = run_step(mu, w, schedule=schedule)
     assert torch.equal(o1[0]["O"], o2[0]["O"])
     assert torch.equal(d1[0]["W"], d2[0]["W"])
     assert torch.equal(d1[0]["M"], d2[0]["M"])
@@ -292,3 +305,40 @@ def test_two_groups_one_call(mu):
     for gi, g in enumerate(w.groups):
         for i in range(3):
             compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL)
+
+
+def test_mixed_schedules_one_call(mu):
+    """One call whose groups take the accumulated schedule (768 x 1536), the
+    iterated one (512 x 512) and the on-chip kernel (64 x 128)."""
+    groups = [wl.random_group(31, 2, 768, 1536, "bf16"), wl.random_group(32, 2, 512, 512, "bf16"),
+              wl.random_group(33, 3, 64, 128, "bf16")]
+    w = wl.Workload("mixed-schedules", groups)
+    fake = [mu.MuonGroup(W=torch.empty(g.count, g.m, g.n), M=torch.empty(g.count, g.m, g.n),
+                         G=torch.empty(g.count, g.m, g.n, dtype=torch.bfloat16), lr=w.lr, beta=w.beta)
+            for g in groups]
+    phases = mu.muon_step_phases(fake, steps=5)
+    assert phases.count("symprod") == 9 and phases.count("gram") == 6 and phases.count("ns_small") == 1
+    devs, outs = run_step(mu, w)
+    for gi, g in enumerate(groups):
+        for i in range(g.count):
+            compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL)
+
+
+def test_timed_events_cover_phases(mu):
+    """muon_step_timed needs one event per phase plus one, and rejects fewer."""
+    w = wl.config4(count=2)
+    groups = []
+    for g in w.groups:
+        d = device_group(g)
+        groups.append(mu.MuonGroup(W=d["W"], M=d["M"], G=d["G"], lr=w.lr, beta=w.beta))
+    phases = mu.muon_step_phases(groups, steps=5)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    with pytest.raises(mu.MuonError):
+        mu.muon_step(groups, steps=5, events=[e.cuda_event for e in evs[:-1]])
+    mu.muon_step(groups, steps=5, events=[e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    times = [evs[k].elapsed_time(evs[k + 1]) for k in range(len(phases))]
+    assert all(t >= 0 for t in times)

@@ -290,3 +290,36 @@ def test_planted_momentum_slips_are_caught():
     a = GOLD["apply_rank1"]
     ascent = np.array(a["W"]) + a["lr"] * a["scale"] * np.array(a["O"])
     assert not np.allclose(ascent, np.array(a["W_new"]))
+
+
+# ---------------------------------------------------------------------------
+# The GPU path may run the iteration in accumulated form: every iterate is
+# Q X0 with Q a polynomial in A_0 = X0 X0^T, so A_k = X_k X_k^T obeys
+# A_{k+1} = A_k B_k^2 with B_k = a_k I + b_k A_k, and O = B_{n-1} ... B_0 X0.
+# That is an identity of the iteration the oracle runs; it is pinned in fp64
+# here so that the GPU's choice of schedule is a question of rounding only.
+# ---------------------------------------------------------------------------
+def _accumulated(U, steps, rows):
+    tall = U.shape[0] > U.shape[1]
+    X0 = U.T if tall else U
+    X0 = X0 / np.linalg.norm(X0)
+    A = X0 @ X0.T
+    Q = np.eye(A.shape[0])
+    for k in range(steps):
+        a, b = rows[k]
+        B = a * np.eye(A.shape[0]) + b * A
+        Q = B @ Q
+        A = A @ B @ B
+    O = Q @ X0
+    return O.T if tall else O
+
+
+@pytest.mark.parametrize("m,n,steps", [(6, 15, 2), (12, 40, 5), (30, 9, 8), (16, 16, 3)])
+def test_accumulated_schedule_is_the_iteration(m, n, steps):
+    rng = np.random.default_rng(m * 100 + n)
+    U = rng.standard_normal((m, n)) * np.exp(rng.uniform(-3, 0, (m, 1)))
+    ref, _ = orc.newton_schulz(U, steps, eps=0.0)
+    assert np.allclose(_accumulated(U, steps, [(1.5, -0.5)] * steps), ref, rtol=0, atol=1e-12)
+    rows = [(2.0 - 0.1 * k, -0.6 + 0.02 * k) for k in range(steps)]
+    ref2, _ = orc.newton_schulz(U, steps, coeffs=rows, eps=0.0, per_step=True)
+    assert np.allclose(_accumulated(U, steps, rows), ref2, rtol=0, atol=1e-12)
