@@ -177,6 +177,25 @@ struct Acc {
   }
 };
 
+// The MFMAs of one stage with one set of fragments (for accumulator tiles too
+// large to leave registers for a second set).
+template <int FM, int FN, class FragA, class FragB>
+__device__ __forceinline__ void stage_mma_single(Acc<FM, FN>& acc, FragA fra, FragB frb) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8_t fa[FM], fb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = fra(ks, i);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = frb(ks, j);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
 // The MFMAs of one stage; fragments of k-step ks+1 are read while ks runs.
 template <int FM, int FN, class FragA, class FragB>
 __device__ __forceinline__ void stage_mma(Acc<FM, FN>& acc, FragA fra, FragB frb) {
@@ -225,29 +244,34 @@ __device__ __forceinline__ void stage_sync_ahead(int ahead) {
 }
 
 // The stage buffers are separate LDS arrays (so the compiler can tell a fill
-// of one from reads of another); a slab is chosen by a wave-uniform index.
-struct Bufs {
-  char* b[NSTAGE];
+// of one from reads of another); a buffer is chosen by a wave-uniform index.
+template <int N>
+struct BufsN {
+  char* b[N];
   __device__ char* operator[](int p) const {
-    return p == 0 ? b[0] : p == 1 ? b[1] : p == 2 ? b[2] : b[3];
+    if constexpr (N == 3) return p == 0 ? b[0] : p == 1 ? b[1] : b[2];
+    else return p == 0 ? b[0] : p == 1 ? b[1] : p == 2 ? b[2] : b[3];
   }
 };
+using Bufs = BufsN<NSTAGE>;
 
-// The pipelined contraction: stages 0..nk-1 through NSTAGE buffers.
-// fill(buf, kt) issues this wave's fills of stage kt, mma(buf) multiplies one.
-template <int LPS, class Fill, class Mma>
-__device__ __forceinline__ void pipeline(const Bufs& bufs, int nk, Fill fill, Mma mma) {
+// The pipelined contraction: stages 0..nk-1 through N buffers, N - 1 fills in
+// flight.  fill(buf, kt) issues this wave's fills of stage kt, mma(buf)
+// multiplies one.
+template <int LPS, int N, class Fill, class Mma>
+__device__ __forceinline__ void pipeline(const BufsN<N>& bufs, int nk, Fill fill, Mma mma) {
+  static_assert(N == 3 || N == 4, "stage count");
 #pragma unroll
-  for (int p = 0; p < NSTAGE - 1; ++p)
+  for (int p = 0; p < N - 1; ++p)
     if (p < nk) fill(bufs[p], p);
-  for (int kt0 = 0; kt0 < nk; kt0 += NSTAGE) {
+  for (int kt0 = 0; kt0 < nk; kt0 += N) {
 #pragma unroll
-    for (int b = 0; b < NSTAGE; ++b) {
+    for (int b = 0; b < N; ++b) {
       const int kt = kt0 + b;
       if (kt < nk) {
-        const int issued_after = (nk - 1 - kt) < (NSTAGE - 2) ? (nk - 1 - kt) : (NSTAGE - 2);
+        const int issued_after = (nk - 1 - kt) < (N - 2) ? (nk - 1 - kt) : (N - 2);
         stage_sync_ahead<LPS>(issued_after);
-        if (kt + NSTAGE - 1 < nk) fill(bufs[(b + NSTAGE - 1) % NSTAGE], kt + NSTAGE - 1);
+        if (kt + N - 1 < nk) fill(bufs[(b + N - 1) % N], kt + N - 1);
         mma(bufs[b]);
       }
     }
@@ -317,6 +341,29 @@ __device__ __forceinline__ bool find_tile_at(const Args& G, int x, int local, in
       return true;
     }
     local -= len;
+  }
+  return false;
+}
+
+// Segment runs [s, e] chained by zip_next share their matrix index range:
+// each XCD takes a contiguous share of the matrices and walks them one by
+// one, all segments' tiles of a matrix together (operands they share, such
+// as a common factor, stay in that XCD's L2).
+__device__ __forceinline__ bool find_tile_zip(const SymArgs& G, int x, int local, int& seg, int& tile) {
+  for (int s = 0; s < G.nseg;) {
+    int e = s;
+    while (e + 1 < G.nseg && G.seg[e].zip_next) ++e;
+    const int cnt = G.seg[s].count, tpm = G.seg[s].tiles_per_mat, per = (e - s + 1) * tpm;
+    const int q = (cnt + NXCD - 1) / NXCD, z0 = x * q;
+    const int nz = z0 >= cnt ? 0 : (z0 + q <= cnt ? q : cnt - z0);
+    if (local < nz * per) {
+      const int z = z0 + local / per, rem = local % per;
+      seg = s + rem / tpm;
+      tile = z * tpm + rem % tpm;
+      return true;
+    }
+    local -= nz * per;
+    s = e + 1;
   }
   return false;
 }
@@ -528,43 +575,68 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
 // ---- symmetric products: O = alpha I + beta L R ----------------------------------
 // L and R are symmetric and commute (polynomials in one Gram matrix), so
 // tile (bi, bj) of L R is sum_k L[bi rows][k] R[bj rows][k]: both operands are
-// read row-wise (K-contiguous), exactly like the Gram.  s_pad x s_pad
+// read row-wise (K-contiguous), exactly like the Gram.  The s_pad x s_pad
 // matrices are small (768 for the Mamba-2 projections), so the tile is
-// 128 x 128 (21 upper tiles per 768 x 768 matrix instead of 6): four waves of
-// 64 x 64, two workgroups per CU.
-constexpr int T2 = kSymTile;
+// TT x TT with TT = 192 when it divides s_pad (10 upper tiles per 768 x 768
+// matrix: one wave of workgroups for 48 matrices, and half the operand bytes
+// per flop of TT = 128), else 128.  Four waves of TT/2 x TT/2, three LDS
+// stages; the stage buffers double as the output staging area.
+template <int TT> struct SymCfg;
+template <> struct SymCfg<128> { static constexpr int kWpe = 3; };  // 48 KB LDS: three workgroups per CU
+template <> struct SymCfg<192> { static constexpr int kWpe = 2; };  // 72 KB LDS: two workgroups per CU
 constexpr int NTHR2 = 256;
-constexpr int OPB2 = T2 * BK * 2;  // 8 KB per operand per stage
+constexpr int SYM_NSTAGE = 3;
+#ifndef SYM_SINGLE_FRAGS_ABOVE
+#define SYM_SINGLE_FRAGS_ABOVE 4  // larger wave tiles read one fragment set per k-step
+#endif
 
-// 128 x 128 output tile staged as two 64-row slabs of 256-byte rows (16-byte
-// chunks XOR-swizzled by row & 15).
-__device__ __forceinline__ int slab2_off(int r, int col) {
-  return r * 256 + ((((col >> 3) ^ (r & 15))) << 4) + (col & 7) * 2;
+int sym_tile(int s_pad) { return s_pad % 192 == 0 ? 192 : 128; }
+
+// Staging row r (0..63 within one buffer), column col (0..TT-1) of a TT-wide
+// bf16 tile: TT * 2-byte rows, 16-byte chunks swizzled by the row (XOR of the
+// low four bits for 16 chunks, of the low three within each group of eight for
+// 24 chunks).
+template <int TT>
+__device__ __forceinline__ int sym_slab_off(int r, int col) {
+  const int c = col >> 3;
+  const int cs = TT == 128 ? (c ^ (r & 15)) : ((c & ~7) | ((c ^ r) & 7));
+  return r * (TT * 2) + (cs << 4) + (col & 7) * 2;
 }
 
-__device__ __forceinline__ void slabs2_to_global(const char* b0, const char* b1, bf16_t* dst, bf16_t* dst2,
-                                                 long long off, long long ld, float a2, float b2, bool dg) {
+// Copy a staged TT x TT tile (rows 64p + r in buffer p) to dst + off (row
+// stride ld); dst2, when non-null, receives a2 I + b2 dst from the rounded
+// values (the identity only on a diagonal tile, dg).  Either may be null.
+template <int TT>
+__device__ __forceinline__ void sym_to_global(const BufsN<SYM_NSTAGE>& bufs, bf16_t* dst, bf16_t* dst2, long long off,
+                                              long long ld, float a2, float b2, bool dg) {
+  constexpr int CPR = TT / 8;              // 16-byte chunks per row
+  constexpr int PER = 64 * CPR / NTHR2;    // chunks per thread per buffer
+  const int tid = opaque(threadIdx.x);     // addresses computed here, not held across the tile loop
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int q = threadIdx.x + NTHR2 * u;  // 2048 chunks of 16 B
-    const int r = q >> 4, c = q & 15, rr = r & 63;
-    const char* b = u < 4 ? b0 : b1;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(b + rr * 256 + ((c ^ (rr & 15)) << 4));
-    const long long o = off + static_cast<long long>(r) * ld + c * 8;
-    if (dst != nullptr) *reinterpret_cast<u32x4_t*>(dst + o) = v;
-    if (dst2 != nullptr) *reinterpret_cast<u32x4_t*>(dst2 + o) = affine8(v, a2, b2, dg ? r - c * 8 : -1);
+  for (int p = 0; p < TT / 64; ++p) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + NTHR2 * u;
+      const int r = q / CPR, c = q % CPR;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bufs[p] + sym_slab_off<TT>(r, c * 8));
+      const long long o = off + static_cast<long long>(p * 64 + r) * ld + c * 8;
+      if (dst != nullptr) *reinterpret_cast<u32x4_t*>(dst + o) = v;
+      if (dst2 != nullptr) *reinterpret_cast<u32x4_t*>(dst2 + o) = affine8(v, a2, b2, dg ? p * 64 + r - c * 8 : -1);
+    }
   }
 }
 
-__global__ void __launch_bounds__(NTHR2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int TT>
+__global__ void __launch_bounds__(NTHR2) __attribute__((amdgpu_waves_per_eu(SymCfg<TT>::kWpe, SymCfg<TT>::kWpe)))
 symprod_bf16_kernel(SymArgs G) {
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB2];
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB2];
-  __shared__ __attribute__((aligned(1024))) char lds2[2 * OPB2];
-  __shared__ __attribute__((aligned(1024))) char lds3[2 * OPB2];
+  constexpr int OPBT = TT * BK * 2;  // bytes of one operand per stage
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPBT];
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPBT];
+  __shared__ __attribute__((aligned(1024))) char lds2[2 * OPBT];
   __shared__ float red[NTHR2 / 64];
-  const Bufs bufs{{lds0, lds1, lds2, lds3}};
-  constexpr int WM = 64, WN = 64, FM = WM / 32, FN = WN / 32;  // waves: 2 x 2 of 64 x 64
+  const BufsN<SYM_NSTAGE> bufs{{lds0, lds1, lds2}};
+  constexpr int WT = TT / 2, FM = WT / 32, FN = WT / 32;  // waves: 2 x 2 of WT x WT
+  constexpr int BPW = TT / 64;                             // 1 KB fill blocks per wave per operand
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int wm = wid >> 1, wn = wid & 1;
   int roff[KS];
@@ -577,11 +649,11 @@ symprod_bf16_kernel(SymArgs G) {
   const int x = blockIdx.x % NXCD, per_xcd = gridDim.x / NXCD;
   for (int local = blockIdx.x / NXCD;; local += per_xcd) {
     int si, tile;
-    if (!find_tile_at(G, x, local, si, tile)) break;
+    if (!find_tile_zip(G, x, local, si, tile)) break;
     const SymSeg& S = G.seg[si];
     const int z = tile / S.tiles_per_mat;
     int bi, bj;
-    upper_tile(tile % S.tiles_per_mat, S.s_pad / T2, bi, bj);
+    upper_tile(tile % S.tiles_per_mat, S.s_pad / TT, bi, bj);
     const bool diag = bi == bj;
     const bool single = diag && S.L == S.R;  // both operands are the same rows
     const long long zoff = z * S.stride;
@@ -595,67 +667,117 @@ symprod_bf16_kernel(SymArgs G) {
     const __amdgpu_buffer_rsrc_t lr = make_rsrc(S.L + zoff, mbytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(S.R + zoff, mbytes);
     const int voff = row_voff(sp_bytes);
-    const int offL = bi * T2 * sp_bytes, offR = bj * T2 * sp_bytes;
+    const int offL = bi * TT * sp_bytes, offR = bj * TT * sp_bytes;
     const int nk = S.s_pad / BK;
-
+    auto fill_rows = [&](char* op, __amdgpu_buffer_rsrc_t rs, int soff0) {
+#pragma unroll
+      for (int b = 0; b < BPW; ++b) {
+        const int blk = wid * BPW + b;
+        dma16(rs, voff, soff0 + blk * 16 * sp_bytes, op + blk * 1024);
+      }
+    };
     auto mma = [&](const char* buf, bool one) {
-      const char* ta = buf + wm * WM * 64;
-      const char* tb = (one ? buf : buf + OPB2) + wn * WN * 64;
-      stage_mma<FM, FN>(acc, [&](int ks, int i) { return frag_at(ta + roff[ks] + i * 32 * 64); },
-                        [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); });
+      const char* ta = buf + wm * WT * 64;
+      const char* tb = (one ? buf : buf + OPBT) + wn * WT * 64;
+      auto fa = [&](int ks, int i) { return frag_at(ta + roff[ks] + i * 32 * 64); };
+      auto fb = [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); };
+      if constexpr (FM * FN > SYM_SINGLE_FRAGS_ABOVE) stage_mma_single<FM, FN>(acc, fa, fb);
+      else stage_mma<FM, FN>(acc, fa, fb);
     };
     if (single) {
-      pipeline<2>(bufs, nk, [&](char* buf, int kt) { load_rows(buf, lr, voff, sp_bytes, offL + kt * BK * 2); },
-                  [&](const char* buf) { mma(buf, true); });
+      pipeline<BPW>(bufs, nk, [&](char* buf, int kt) { fill_rows(buf, lr, offL + kt * BK * 2); },
+                    [&](const char* buf) { mma(buf, true); });
     } else {
-      pipeline<4>(bufs, nk,
-                  [&](char* buf, int kt) {
-                    load_rows(buf, lr, voff, sp_bytes, offL + kt * BK * 2);
-                    load_rows(buf + OPB2, rr, voff, sp_bytes, offR + kt * BK * 2);
-                  },
-                  [&](const char* buf) { mma(buf, false); });
+      pipeline<2 * BPW>(bufs, nk,
+                        [&](char* buf, int kt) {
+                          fill_rows(buf, lr, offL + kt * BK * 2);
+                          fill_rows(buf + OPBT, rr, offR + kt * BK * 2);
+                        },
+                        [&](const char* buf) { mma(buf, false); });
     }
 
-    // epilogue: D[m][n] = (L R)[bi*T2 + m][bj*T2 + n]; lane: 4 consecutive m
-    // at one n.  The mirrored tile is staged in buffers 0-1 and (off the
-    // diagonal) the tile itself in buffers 2-3, then both leave as whole
-    // rows; O2 is the affine image of O1's rounded values.
+    // epilogue: D[m][n] = (L R)[bi*TT + m][bj*TT + n]; lane: 4 consecutive m
+    // at one n.  The mirrored tile is staged (rows n, contiguous m) and
+    // written out, then, off the diagonal, the tile itself; both leave as
+    // whole rows.  O2 is the affine image of O1's rounded values.  Every
+    // 32-row block lies in one 64-row buffer, so buffer choices are uniform.
     stage_sync<0>();
     const float a1 = S.a1 * ia, b1 = S.b1 * ib;
     const int lane_e = opaque(lane);
-    const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;  // buffers and rows below are uniform per wave
+    const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;
+    bf16_t* O1 = S.O1 == nullptr ? nullptr : S.O1 + zoff;
+    bf16_t* O2 = S.O2 == nullptr ? nullptr : S.O2 + zoff;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FN; ++j) {
+      const int nb = wn * WT + j * 32;  // 32-aligned block of n
+      char* buf = bufs[nb >> 6];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = wn * WN + j * 32 + col;
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m = wm * WM + i * 32 + q * 8 + rq;
+          const int m = wm * WT + i * 32 + q * 8 + rq;
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = b1 * acc.c[i][j][4 * q + r] + ((diag && m + r == n) ? a1 : 0.0f);
-          *reinterpret_cast<u32x2_t*>(bufs[wn] + slab2_off(j * 32 + col, m)) =
+          for (int r = 0; r < 4; ++r)
+            v[r] = b1 * acc.c[i][j][4 * q + r] + ((diag && m + r == nb + col) ? a1 : 0.0f);
+          *reinterpret_cast<u32x2_t*>(buf + sym_slab_off<TT>((nb & 63) + col, m)) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          if (!diag) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              *reinterpret_cast<bf16_t*>(bufs[2 + wm] + slab2_off(i * 32 + q * 8 + rq + r, n)) = f32_to_bf16(v[r]);
-          }
         }
       }
     }
     __syncthreads();
-    bf16_t* O1 = S.O1 == nullptr ? nullptr : S.O1 + zoff;
-    bf16_t* O2 = S.O2 == nullptr ? nullptr : S.O2 + zoff;
-    const long long mir = static_cast<long long>(bj) * T2 * S.s_pad + bi * T2;
-    slabs2_to_global(lds0, lds1, O1, O2, mir, S.s_pad, S.a2, S.b2, diag);
+    sym_to_global<TT>(bufs, O1, O2, static_cast<long long>(bj) * TT * S.s_pad + bi * TT, S.s_pad, S.a2, S.b2, diag);
     if (!diag) {
-      const long long dir = static_cast<long long>(bi) * T2 * S.s_pad + bj * T2;
-      slabs2_to_global(lds2, lds3, O1, O2, dir, S.s_pad, S.a2, S.b2, false);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int mb = wm * WT + i * 32;  // 32-aligned block of m
+        char* buf = bufs[mb >> 6];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              *reinterpret_cast<bf16_t*>(buf + sym_slab_off<TT>((mb & 63) + q * 8 + rq + r, wn * WT + j * 32 + col)) =
+                  f32_to_bf16(b1 * acc.c[i][j][4 * q + r]);
+      }
+      __syncthreads();
+      sym_to_global<TT>(bufs, O1, O2, static_cast<long long>(bi) * TT * S.s_pad + bj * TT, S.s_pad, S.a2, S.b2, false);
     }
     __syncthreads();  // staging read out before the next tile's fills land
   }
+}
+
+// Tiles per XCD of a segment table walked by find_tile_zip, times the XCDs.
+int grid_for_zip(const SymArgs& G) {
+  int per_xcd = 0;
+  for (int s = 0; s < G.nseg;) {
+    int e = s;
+    while (e + 1 < G.nseg && G.seg[e].zip_next) ++e;
+    per_xcd += (G.seg[s].count + NXCD - 1) / NXCD * (e - s + 1) * G.seg[s].tiles_per_mat;
+    s = e + 1;
+  }
+  return per_xcd * NXCD;
+}
+
+template <int TT>
+hipError_t launch_symprod_tt(const SymArgs& G, hipStream_t st) {
+  // persistent: kWpe resident workgroups per CU (LDS bound), a multiple of
+  // the XCD count
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const int slots = (SymCfg<TT>::kWpe * cus) / NXCD * NXCD;
+  const int need = grid_for_zip(G);
+  const int grid = need < slots ? need : slots;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(symprod_bf16_kernel<TT>, dim3(grid), dim3(NTHR2), 0, st, G);
+  return hipGetLastError();
 }
 
 template <class Args>
@@ -675,27 +797,23 @@ int gram_tiles_per_matrix(int s_pad) {
   return nt * (nt + 1) / 2;
 }
 int combine_tiles_per_matrix(int s_pad, int ld) { return (s_pad / T) * (ld / T); }
+int symprod_tile(int s_pad) { return sym_tile(s_pad); }
 int symprod_tiles_per_matrix(int s_pad) {
-  const int nt = s_pad / T2;
+  const int nt = s_pad / sym_tile(s_pad);
   return nt * (nt + 1) / 2;
 }
 
+// One launch per tile size present (zip chains never mix sizes: they share
+// s_pad).
 hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st) {
-  // persistent: two resident workgroups per CU (LDS bound), a multiple of
-  // the XCD count
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
+  SymArgs part[2] = {};
+  for (int s = 0; s < G.nseg; ++s) {
+    SymArgs& P = part[sym_tile(G.seg[s].s_pad) == 192 ? 1 : 0];
+    P.seg[P.nseg++] = G.seg[s];
   }
-  const int slots = (2 * cus) / NXCD * NXCD;
-  const int need = grid_for(G);
-  const int grid = need < slots ? need : slots;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(symprod_bf16_kernel, dim3(grid), dim3(NTHR2), 0, st, G);
-  return hipGetLastError();
+  hipError_t e = part[1].nseg ? launch_symprod_tt<192>(part[1], st) : hipSuccess;
+  if (e == hipSuccess && part[0].nseg) e = launch_symprod_tt<128>(part[0], st);
+  return e;
 }
 
 hipError_t launch_gram_bf16(const GemmArgs& G, hipStream_t st) {

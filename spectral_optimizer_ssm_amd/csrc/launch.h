@@ -91,7 +91,6 @@ hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st);
 // O1 = a1 inv^pa I + b1 inv^pb L R and (optional) O2 = a2 I + b2 O1 from
 // O1's rounded values.  Only tiles on or above the diagonal are computed;
 // each is stored in place and mirrored.
-constexpr int kSymTile = 128;
 struct SymSeg {
   const bf16_t* L;     // left factor   [count][s_pad][s_pad]
   const bf16_t* R;     // right factor  (may equal L)
@@ -104,11 +103,14 @@ struct SymSeg {
   float eps;
   float a1, b1, a2, b2;
   int pa, pb;
+  int zip_next;        // 1: the next segment has the same count and s_pad and
+                       // runs matrix by matrix together with this one
 };
 struct SymArgs {
   SymSeg seg[kMaxSeg];
   int nseg;
 };
+int symprod_tile(int s_pad);  // 192 when it divides s_pad, else 128
 int symprod_tiles_per_matrix(int s_pad);
 hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st);
 

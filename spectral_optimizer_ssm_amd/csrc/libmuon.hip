@@ -85,7 +85,7 @@ enum SqBuf { kSqA0 = 0, kSqA1, kSqB0, kSqB1, kSqE, kSqQ0, kSqQ1, kSqCount };
 bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
   if (g.engine != kTiledBf16 || C.steps < 2 || C.schedule == MUON_NS_ITERATE) return false;
   if (C.schedule == MUON_NS_ACCUMULATE) return true;
-  const double t = kTileS, t2 = kSymTile;
+  const double t = kTileS, t2 = symprod_tile(g.s_pad);
   const double gram = gram_tiles_per_matrix(g.s_pad) * t * t * g.kdim;
   const double comb = combine_tiles_per_matrix(g.s_pad, g.ld) * t * t * g.s_pad;
   const double prod = symprod_tiles_per_matrix(g.s_pad) * t2 * t2 * g.s_pad;
@@ -339,9 +339,10 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       for (int gi : ac) {
         const GroupPlan& p = runs[gi].plan;
         bf16_t* Bk = sq_of(p, ws, kSqB0 + (k & 1));
-        if (k + 1 < n) {  // E = B_k B_k
+        if (k + 1 < n) {  // E = B_k B_k (shares B_k with the Q product of the same matrix)
           SymSeg S = sym_seg(p);
           S.L = Bk; S.R = Bk; S.O1 = sq_of(p, ws, kSqE);
+          S.zip_next = k >= 1 ? 1 : 0;
           l1.push_back(S);
         }
         if (k >= 1) {  // Q_{k+1} = B_k Q_k; the last one carries the normalisation
