@@ -169,6 +169,26 @@ def muon_step_group(Ws, Ms, Gs, **kw):
 
 
 # ----------------------------------------------------------------------------
+# Factored injections: X = V K^T (MuonSSM, method section on the low-rank
+# value-key injections and their light Newton-Schulz step)
+# ----------------------------------------------------------------------------
+def factored_ns(V: np.ndarray, K: np.ndarray, steps: int, coeffs=CUBIC, eps: float = DEFAULT_EPS,
+                per_step: bool = False):
+    """Newton-Schulz of the injection X = V K^T (V m x r, K n x r), returned
+    both dense and as the r x r core C with O = V C K^T.
+
+    The dense result is the plain definition, newton_schulz(V K^T).  The core
+    is the unique C reproducing it when V and K have full column rank:
+    C = V^+ O (K^+)^T with the Moore-Penrose pseudo-inverses (LAPACK SVD
+    through numpy).  Returns (O, C, nu)."""
+    V = np.asarray(V, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    O, nu = newton_schulz(V @ K.T, steps, coeffs, eps, per_step)
+    C = np.linalg.pinv(V) @ O @ np.linalg.pinv(K).T
+    return O, C, nu
+
+
+# ----------------------------------------------------------------------------
 # Diagnostics (reported, never part of the update)
 # ----------------------------------------------------------------------------
 def orthogonality_error(O: np.ndarray) -> float:

@@ -323,3 +323,48 @@ def test_accumulated_schedule_is_the_iteration(m, n, steps):
     rows = [(2.0 - 0.1 * k, -0.6 + 0.02 * k) for k in range(steps)]
     ref2, _ = orc.newton_schulz(U, steps, coeffs=rows, eps=0.0, per_step=True)
     assert np.allclose(_accumulated(U, steps, rows), ref2, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Factored injections X = V K^T ("MuonSSM", method section on the low-rank
+# value-key injections): the oracle's core C must reproduce the dense result
+# and agree with two independent routes to it.
+# ---------------------------------------------------------------------------
+def _core_recurrence(V, K, steps, rows, eps):
+    P, S = V.T @ V, K.T @ K
+    nu = np.sqrt(np.trace(P @ S))
+    C = np.eye(V.shape[1]) / (nu + eps)
+    for a, b, c in rows:
+        N = C @ S @ C.T @ P
+        C = a * C + b * N @ C + c * N @ N @ C
+    return C
+
+
+@pytest.mark.parametrize("m,n,r,steps", [(64, 128, 8, 1), (64, 128, 8, 5), (32, 96, 4, 3), (128, 64, 8, 2),
+                                         (40, 40, 1, 4)])
+def test_factored_ns_core(m, n, r, steps):
+    rng = np.random.default_rng(m + n + r + steps)
+    V, K = rng.standard_normal((m, r)), rng.standard_normal((n, r))
+    O, C, nu = orc.factored_ns(V, K, steps)
+    np.testing.assert_allclose(V @ C @ K.T, O, rtol=0, atol=1e-12)  # the core reproduces the dense result
+    np.testing.assert_allclose(C, _core_recurrence(V, K, steps, [(1.5, -0.5, 0.0)] * steps, 1e-7), rtol=1e-10,
+                               atol=1e-12)
+    rows = [(2.0, -1.5, 0.5)] * steps
+    O5, C5, _ = orc.factored_ns(V, K, steps, coeffs=rows, per_step=True)
+    np.testing.assert_allclose(C5, _core_recurrence(V, K, steps, rows, 1e-7), rtol=1e-9, atol=1e-12)
+
+
+def test_factored_ns_orthonormal_closed_form():
+    """V = Qv diag(alpha), K = Qk with orthonormal columns: X has singular
+    values alpha, so C_ii = p^k(alpha_i / (||alpha|| + eps)) / alpha_i."""
+    rng = np.random.default_rng(7)
+    Qv, _ = np.linalg.qr(rng.standard_normal((64, 6)))
+    Qk, _ = np.linalg.qr(rng.standard_normal((128, 6)))
+    alpha = np.array([3.0, 1.0, 0.5, 0.25, 0.1, 0.01])
+    for steps in (1, 3, 6):
+        O, C, nu = orc.factored_ns(Qv * alpha, Qk, steps)
+        x = alpha / (np.linalg.norm(alpha) + 1e-7)
+        for _ in range(steps):
+            x = 1.5 * x - 0.5 * x ** 3
+        np.testing.assert_allclose(C, np.diag(x / alpha), rtol=0, atol=1e-12)
+        assert abs(nu - np.linalg.norm(alpha)) < 1e-12
