@@ -319,6 +319,39 @@ def bench_injections(args, torch, mu, wl):
                                                                                               "common.cuh"])}}
 
 
+def bench_injections_factored(args, torch, mu, wl):
+    """The same injections given by their factors V [b, 64, 8], K [b, 128, 8]:
+    muon_ns_factored writes the 8 x 8 float32 core of each (NS(V K^T) =
+    V C K^T), or also the dense result with --dense."""
+    X, V, K = wl.injections(batch=args.batch, device="cuda", return_factors=True)
+    del X
+    C = torch.empty((args.batch, 8, 8), dtype=torch.float32, device="cuda")
+    O = torch.empty((args.batch, 64, 128), dtype=torch.bfloat16, device="cuda") if args.dense else None
+    for _ in range(args.warmup):
+        mu.muon_ns_factored(V, K, C=C, O=O, steps=args.ns_steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        mu.muon_ns_factored(V, K, C=C, O=O, steps=args.ns_steps)
+        b.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    per = (64 + 128) * 8 * 2 + 8 * 8 * 4 + (64 * 128 * 2 if args.dense else 0)
+    gbs = args.batch * per / (kms * 1e-3) / 1e9
+    return {"metric": "MuonSSM factored single-step NS matrices/s", "value": round(args.batch / (ms * 1e-3), 1),
+            "unit": "matrices/s", "ms_per_step": round(ms, 4), "dtype": "bf16",
+            "config": {"workload": f"injections {args.batch} x (V 64x8, K 128x8) bf16 factors, "
+                                   f"{args.ns_steps} NS step, {'core + dense' if args.dense else '8x8 core'} out"},
+            "roofline": {"bound": "hbm", "kernel": "ns_factored_kernel", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "bytes_per_matrix": per,
+                         "traffic": measured_traffic("ns_factored_kernel", "injections_factored",
+                                                     ["ns_factored.hip", "common.cuh"])}}
+
+
 def bench_group(args, torch, mu, wl, which):
     w = wl.config2() if which == "out_proj" else wl.config3() if which == "in_proj" else wl.config1()
     groups = []
@@ -352,6 +385,7 @@ COUNTED_KERNELS = {
                   "apply_wide_kernel": ("apply_wide_kernel", ELEMENTWISE),
                   "apply_tall_kernel": ("apply_tall_kernel", ELEMENTWISE)},
     "injections": {"ns_small_bf16_kernel": ("ns_small_bf16_kernel", ["ns_small.hip", "common.cuh"])},
+    "injections_factored": {"ns_factored_kernel": ("ns_factored_kernel", ["ns_factored.hip", "common.cuh"])},
 }
 
 
@@ -361,11 +395,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_step",
-                    choices=["full_step", "out_proj", "in_proj", "injections", "single"])
+                    choices=["full_step", "out_proj", "in_proj", "injections", "injections_factored", "single"])
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
     ap.add_argument("--batch", type=int, default=393216, help="injections batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--dense", action="store_true", help="injections_factored: also write the dense result")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB plain copy first (reference for profiler byte counters)")
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -379,7 +414,7 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.ns_steps is None:
-        args.ns_steps = 1 if args.workload == "injections" else 5
+        args.ns_steps = 1 if args.workload.startswith("injections") else 5
     import torch
     import spectral_optimizer_ssm_amd as mu
     import workloads as wl
@@ -393,6 +428,8 @@ def main():
         res = bench_full_step(args, torch, mu, wl)
     elif args.workload == "injections":
         res = bench_injections(args, torch, mu, wl)
+    elif args.workload == "injections_factored":
+        res = bench_injections_factored(args, torch, mu, wl)
     else:
         res = bench_group(args, torch, mu, wl, args.workload)
     out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,

@@ -95,7 +95,7 @@ typedef enum { MUON_NS_AUTO = 0, MUON_NS_ITERATE = 1, MUON_NS_ACCUMULATE = 2 } m
  *   eps       added to ||U||_F before dividing (>= 0)
  *   precision MUON_BF16 or MUON_F32 (see Precision above)
  *   schedule  a muon_ns_schedule
- * A quintic c != 0 returns MUON_EUNSUPPORTED on the GPU path. */
+ * A quintic c != 0 returns MUON_EUNSUPPORTED except in muon_ns_factored. */
 typedef struct {
   int steps;
   int ncoef;
@@ -182,6 +182,28 @@ int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int b
  * Other shapes return MUON_EUNSUPPORTED.  Y must not overlap X. */
 int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long long batch,
                           const muon_ns_cfg* cfg, void* stream);
+
+/* Newton-Schulz of matrices given as factors, X[b] = V[b] K[b]^T ("MuonSSM",
+ * method section: each per-token, per-head injection is a sum of r
+ * value-key outer products, orthogonalised by a light Newton-Schulz step).
+ * Every step keeps the form V C K^T, so only an r x r core is computed:
+ *   P = V^T V, S = K^T K, C_0 = I / (sqrt(tr(P S)) + eps),
+ *   per step N = C S C^T P, C = a C + b N C + c N N C     (c from cfg, may be != 0)
+ * giving NS(X[b]) = V[b] C_out[b] K[b]^T exactly up to rounding (the same
+ * result as muon_ns_orthogonalize on the dense X; C is unique when V and K
+ * have full column rank).
+ *   V      [batch][m][r] bfloat16, row-major, contiguous
+ *   K      [batch][n][r] bfloat16
+ *   C_out  [batch][r][r] float32 (written)
+ *   O_out  NULL, or [batch][m][n] bfloat16 receiving the dense V C K^T
+ *          (16-byte aligned, n % 8 == 0)
+ * dtype and cfg->precision must be MUON_BF16 (P and S on the matrix cores
+ * with float32 accumulation, the core recurrence in float32).  Supported:
+ * 1 <= r <= 8, m, n <= 256 (with O_out also (m16 + n16) * 64 + m16 * 128 +
+ * 6144 <= 65536 bytes, m16 = m rounded up to 16); otherwise
+ * MUON_EUNSUPPORTED.  Outputs must not overlap inputs or each other. */
+int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int r, long long batch,
+                     const muon_ns_cfg* cfg, float* C_out, void* O_out, void* stream);
 
 /* Human-readable name of a muon_status. */
 const char* muon_status_string(int status);

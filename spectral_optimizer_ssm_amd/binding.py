@@ -46,7 +46,8 @@ class GroupC(ctypes.Structure):
 
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
-           "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_status_string", "muon_version")
+           "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_ns_factored", "muon_status_string",
+           "muon_version")
 
 
 def lib():
@@ -75,6 +76,9 @@ def lib():
     L.muon_ns_orthogonalize.restype = i
     L.muon_ns_batched_small.argtypes = [vp, vp, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg), vp]
     L.muon_ns_batched_small.restype = i
+    L.muon_ns_factored.argtypes = [vp, vp, i, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg),
+                                   ctypes.POINTER(f), vp, vp]
+    L.muon_ns_factored.restype = i
     L.muon_status_string.argtypes = [i]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_version.argtypes = []
@@ -271,3 +275,28 @@ def muon_ns_batched_small(X, Y, steps=1, coeffs=(1.5, -0.5), eps=1e-7, per_step=
     rc = L.muon_ns_batched_small(ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()), dt, m, n, b,
                                  ctypes.byref(cfg), _stream_handle(stream))
     _check(rc, "muon_ns_batched_small")
+
+
+def muon_ns_factored(V, K, C=None, O=None, steps=1, coeffs=(1.5, -0.5), eps=1e-7, per_step=False, stream=None):
+    """NS of X[b] = V[b] K[b]^T from the factors: returns the [batch, r, r]
+    float32 core C (NS(X) = V C K^T), and fills O ([batch, m, n] bf16) with the
+    dense result when given."""
+    import torch
+    L = lib()
+    if V.dim() != 3 or K.dim() != 3 or V.shape[0] != K.shape[0] or V.shape[2] != K.shape[2]:
+        raise ValueError("V, K must be [batch, m, r] and [batch, n, r]")
+    if not (V.is_contiguous() and K.is_contiguous()) or V.dtype != K.dtype:
+        raise ValueError("V and K must be contiguous tensors of one dtype")
+    b, m, r = V.shape
+    n = K.shape[1]
+    dt = _dtype_code(V)
+    if C is None:
+        C = torch.empty(b, r, r, dtype=torch.float32, device=V.device)
+    if O is not None and (not O.is_contiguous() or tuple(O.shape) != (b, m, n) or O.dtype != V.dtype):
+        raise ValueError("O must be a contiguous [batch, m, n] tensor of V's dtype")
+    cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step)
+    rc = L.muon_ns_factored(ctypes.c_void_p(V.data_ptr()), ctypes.c_void_p(K.data_ptr()), dt, m, n, r, b,
+                            ctypes.byref(cfg), ctypes.cast(ctypes.c_void_p(C.data_ptr()), ctypes.POINTER(ctypes.c_float)),
+                            ctypes.c_void_p(O.data_ptr()) if O is not None else None, _stream_handle(stream))
+    _check(rc, "muon_ns_factored")
+    return C

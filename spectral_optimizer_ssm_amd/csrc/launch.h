@@ -136,4 +136,22 @@ struct NsSmallLaunch {
 bool ns_small_supported(bool bf16, int s, int l);
 hipError_t launch_ns_small(const NsSmallLaunch& L, bool bf16, hipStream_t st);
 
+// Newton-Schulz of factored matrices X = V K^T (bf16 factors, r <= 8): the
+// r x r core and optionally the dense result.
+struct FactLaunch {
+  const bf16_t* V;     // [batch][m][r]
+  const bf16_t* K;     // [batch][n][r]
+  float* C;            // [batch][r][r]
+  bf16_t* O;           // [batch][m][n] or null
+  long long batch;
+  int m, n, r, m_pad, n_pad;  // pads: multiples of 16
+  int vec;             // r == 8 and 16-byte aligned factors: 16-byte row loads
+  int waves;           // wavefronts per workgroup
+  int steps;
+  float eps;
+  float a[64], b[64], c[64];
+};
+int factored_lds_per_wave(int m_pad, int n_pad, bool dense);
+hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st);
+
 }  // namespace muon

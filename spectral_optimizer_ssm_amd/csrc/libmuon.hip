@@ -36,10 +36,11 @@ size_t dtype_size(int dt) { return dt == MUON_BF16 ? 2 : 4; }
 struct NsCoefs {
   int steps;
   int schedule;
-  float a[kMaxSteps], b[kMaxSteps];
+  float a[kMaxSteps], b[kMaxSteps], c[kMaxSteps];
 };
 
-int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out) {
+// quintic: whether the caller supports c != 0 (else MUON_EUNSUPPORTED)
+int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out, bool quintic = false) {
   if (cfg == nullptr) return MUON_EINVAL;
   if (cfg->steps < 0 || cfg->steps > kMaxSteps) return MUON_EINVAL;
   if (cfg->ncoef != 2 && cfg->ncoef != 3) return MUON_EINVAL;
@@ -53,9 +54,11 @@ int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out) {
   for (int k = 0; k < cfg->steps; ++k) {
     const float* row = cfg->coeffs + (cfg->per_step ? k * cfg->ncoef : 0);
     if (!std::isfinite(row[0]) || !std::isfinite(row[1])) return MUON_EINVAL;
+    out->c[k] = 0.0f;
     if (cfg->ncoef == 3) {
       if (!std::isfinite(row[2])) return MUON_EINVAL;
-      if (row[2] != 0.0f) return MUON_EUNSUPPORTED;
+      if (row[2] != 0.0f && !quintic) return MUON_EUNSUPPORTED;
+      out->c[k] = row[2];
     }
     out->a[k] = row[0];
     out->b[k] = row[1];
@@ -591,6 +594,51 @@ int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int b
   R.O = R.o_own.data();
   EventRec E;
   return run_all(runs, C, cfg->eps, static_cast<char*>(workspace), nullptr, static_cast<hipStream_t>(stream), E);
+}
+
+int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int r, long long batch,
+                     const muon_ns_cfg* cfg, float* C_out, void* O_out, void* stream) {
+  NsCoefs C;
+  int rc = parse_cfg(cfg, &C, true);
+  if (rc != MUON_OK) return rc;
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_EINVAL;
+  if (m <= 0 || n <= 0 || r <= 0 || batch < 0) return MUON_EINVAL;
+  if (dtype != MUON_BF16 || cfg->precision != MUON_BF16) return MUON_EUNSUPPORTED;
+  if (r > 8 || m > 256 || n > 256) return MUON_EUNSUPPORTED;
+  if (O_out != nullptr && n % 8 != 0) return MUON_EUNSUPPORTED;
+  const int m_pad = round_up(m, 16), n_pad = round_up(n, 16);
+  const int per_wave = factored_lds_per_wave(m_pad, n_pad, O_out != nullptr);
+  if (per_wave > 65536) return MUON_EUNSUPPORTED;
+  if (batch == 0) return MUON_OK;
+  if (V == nullptr || K == nullptr || C_out == nullptr || !aligned_to(V, 2) || !aligned_to(K, 2) ||
+      !aligned_to(C_out, 4) || (O_out != nullptr && !aligned16(O_out)))
+    return MUON_EINVAL;
+  const char* vb = static_cast<const char*>(V);
+  const char* kb = static_cast<const char*>(K);
+  const char* cb = reinterpret_cast<const char*>(C_out);
+  const size_t vbytes = static_cast<size_t>(batch) * m * r * 2, kbytes = static_cast<size_t>(batch) * n * r * 2;
+  const size_t cbytes = static_cast<size_t>(batch) * r * r * 4;
+  auto overlap = [](const char* a, size_t na, const char* b, size_t nb) { return a < b + nb && b < a + na; };
+  if (overlap(cb, cbytes, vb, vbytes) || overlap(cb, cbytes, kb, kbytes)) return MUON_EINVAL;
+  if (O_out != nullptr) {
+    const char* ob = static_cast<const char*>(O_out);
+    const size_t obytes = static_cast<size_t>(batch) * m * n * 2;
+    if (overlap(ob, obytes, vb, vbytes) || overlap(ob, obytes, kb, kbytes) || overlap(ob, obytes, cb, cbytes))
+      return MUON_EINVAL;
+  }
+  FactLaunch F{};
+  F.V = static_cast<const bf16_t*>(V);
+  F.K = static_cast<const bf16_t*>(K);
+  F.C = C_out;
+  F.O = static_cast<bf16_t*>(O_out);
+  F.batch = batch;
+  F.m = m; F.n = n; F.r = r; F.m_pad = m_pad; F.n_pad = n_pad;
+  F.vec = r == 8 && aligned16(V) && aligned16(K);
+  F.waves = std::max(1, std::min(4, 65536 / per_wave));
+  F.steps = C.steps;
+  F.eps = cfg->eps;
+  for (int k = 0; k < C.steps; ++k) { F.a[k] = C.a[k]; F.b[k] = C.b[k]; F.c[k] = C.c[k]; }
+  return launch_ns_factored(F, static_cast<hipStream_t>(stream)) == hipSuccess ? MUON_OK : MUON_EHIP;
 }
 
 int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long long batch, const muon_ns_cfg* cfg,

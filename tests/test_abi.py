@@ -168,3 +168,34 @@ def test_accumulate_workspace_is_larger(mu):
         sizes[sch] = L.muon_step_workspace_size(arr, 1, ctypes.byref(cfg))
     # seven 768 x 768 bf16 buffers per matrix instead of one
     assert sizes[mu.MUON_NS_ACCUMULATE] - sizes[mu.MUON_NS_ITERATE] >= 24 * 6 * 768 * 768 * 2
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("ok_empty", 0), ("r9", -2), ("f32", -2), ("m0", -1), ("m300", -2), ("dense_n_odd", -2),
+    ("overlap_c", -1), ("overlap_o", -1), ("misaligned_o", -1), ("null_v", -1), ("quintic_ok_empty", 0),
+    ("too_big_dense", -2),
+])
+def test_factored_validation(mu, case, expect):
+    L = mu.lib()
+    cfg, keep = mu.make_cfg(1, (1.5, -0.5, 0.25) if case == "quintic_ok_empty" else (1.5, -0.5), 1e-7,
+                            mu.MUON_F32 if case == "f32" else mu.MUON_BF16)
+    m, n, r, batch = 64, 128, 8, 10
+    if case == "r9":
+        r = 9
+    if case == "m0":
+        m = 0
+    if case == "m300":
+        m = 300
+    if case == "dense_n_odd":
+        n = 127
+    if case == "too_big_dense":
+        m, n = 256, 256
+    if case in ("ok_empty", "quintic_ok_empty"):
+        batch = 0
+    V, K = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    C = ctypes.cast(ctypes.c_void_p(0x400000 if case != "overlap_c" else 0x100010), ctypes.POINTER(ctypes.c_float))
+    O = {"overlap_o": 0x200000, "misaligned_o": 0x800008}.get(case, 0x800000)
+    dense = case in ("dense_n_odd", "overlap_o", "misaligned_o", "too_big_dense")
+    rc = L.muon_ns_factored(None if case == "null_v" else V, K, mu.MUON_F32 if case == "f32" else mu.MUON_BF16,
+                            m, n, r, batch, ctypes.byref(cfg), C, ctypes.c_void_p(O) if dense else None, None)
+    assert rc == expect
