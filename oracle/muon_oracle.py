@@ -189,6 +189,57 @@ def factored_ns(V: np.ndarray, K: np.ndarray, steps: int, coeffs=CUBIC, eps: flo
 
 
 # ----------------------------------------------------------------------------
+# Spectral cap ("An Isotropy-Preserving Spectral Cap for Muon"): at each update
+# remove the direction that contributes most, to first order, to the growth of
+# the weight's top singular value; the other directions keep learning.  The
+# page gives no formula; the reading taken: with W's top singular pair (u, v)
+# and W' = W - lr * scale * O, sigma_1 moves by -lr * scale * u^T O v to first
+# order, and only the u v^T component of O contributes.  When the estimate
+# sigma of sigma_1(W) has reached the cap and u^T O v < 0 (sigma_1 would grow),
+# that component is removed: O <- O - (u^T O v) u v^T.  The pair is tracked
+# across steps by one simultaneous power step per update on the new weight.
+# ----------------------------------------------------------------------------
+def spectral_cap_update(O: np.ndarray, u: np.ndarray, v: np.ndarray, sigma: float, cap: float):
+    """The capped update for one matrix given the current estimates u (m), v
+    (n) of W's top singular vectors (unit norm) and sigma of its top singular
+    value.  Returns (O', gamma) with O' = O - gamma u v^T."""
+    O = np.asarray(O, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    c = float(u @ O @ v)
+    gamma = c if (sigma >= cap and c < 0.0) else 0.0
+    return O - gamma * np.outer(u, v), gamma
+
+
+def power_step(W: np.ndarray, u: np.ndarray, v: np.ndarray):
+    """One simultaneous power step on W: u' = W v / ||W v||, v' = W^T u /
+    ||W^T u||, sigma' = ||W v||.  A zero product leaves that vector as it was."""
+    W = np.asarray(W, dtype=np.float64)
+    y, z = W @ np.asarray(v, dtype=np.float64), W.T @ np.asarray(u, dtype=np.float64)
+    ny, nz = np.linalg.norm(y), np.linalg.norm(z)
+    u2 = y / ny if ny > 0 else np.asarray(u, dtype=np.float64)
+    v2 = z / nz if nz > 0 else np.asarray(v, dtype=np.float64)
+    return u2, v2, float(ny)
+
+
+def muon_step_capped(W, M, G, u, v, sigma, *, cap: float, beta: float, lr: float, nesterov: bool = True,
+                     steps: int = 5, coeffs=CUBIC, eps: float = DEFAULT_EPS, scale: float = 1.0,
+                     per_step: bool = False):
+    """muon_step with the spectral cap: the NS update is capped with the
+    incoming estimates, applied, and the estimates advance by one power step
+    on the new weight.  Returns muon_step's dict plus gamma, u, v, sigma."""
+    W = np.asarray(W, dtype=np.float64)
+    M_new = momentum(np.asarray(M, dtype=np.float64), np.asarray(G, dtype=np.float64), beta)
+    U = update_direction(np.asarray(G, dtype=np.float64), M_new, beta, nesterov)
+    O, nu = newton_schulz(U, steps, coeffs, eps, per_step)
+    O_cap, gamma = spectral_cap_update(O, u, v, sigma, cap)
+    W_new = W - lr * scale * O_cap
+    u2, v2, s2 = power_step(W_new, u, v)
+    return {"W": W_new, "M": M_new, "O": O_cap, "O_uncapped": O, "nu": nu, "U": U, "gamma": gamma,
+            "u": u2, "v": v2, "sigma": s2}
+
+
+# ----------------------------------------------------------------------------
 # Diagnostics (reported, never part of the update)
 # ----------------------------------------------------------------------------
 def orthogonality_error(O: np.ndarray) -> float:

@@ -368,3 +368,76 @@ def test_factored_ns_orthonormal_closed_form():
             x = 1.5 * x - 0.5 * x ** 3
         np.testing.assert_allclose(C, np.diag(x / alpha), rtol=0, atol=1e-12)
         assert abs(nu - np.linalg.norm(alpha)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Spectral cap ("An Isotropy-Preserving Spectral Cap for Muon"): pins of the
+# reading that the capped update removes exactly the first-order growth of the
+# top singular value and nothing else.
+# ---------------------------------------------------------------------------
+def _gapped(rng, m, n, top=5.0):
+    Uq, _ = np.linalg.qr(rng.standard_normal((m, min(m, n))))
+    Vq, _ = np.linalg.qr(rng.standard_normal((n, min(m, n))))
+    s = np.concatenate([[top], rng.uniform(0.1, 1.0, min(m, n) - 1)])
+    return (Uq * s) @ Vq.T, Uq[:, 0], Vq[:, 0], top
+
+
+def test_cap_removes_first_order_growth():
+    rng = np.random.default_rng(41)
+    W, u1, v1, s1 = _gapped(rng, 40, 70)
+    O = rng.standard_normal((40, 70))
+    O -= (abs(u1 @ O @ v1) + 0.5) * np.outer(u1, v1)    # make u1^T O v1 < 0: W - eps O grows sigma_1
+    c = u1 @ O @ v1
+    O2, gamma = orc.spectral_cap_update(O, u1, v1, s1, cap=1.0)
+    assert gamma == c and abs(u1 @ O2 @ v1) < 1e-12
+    # the rest of O is untouched: O - O2 is rank one along u1 v1^T
+    np.testing.assert_allclose(O - O2, c * np.outer(u1, v1), atol=1e-12)
+    for h in (1e-3, 1e-4):
+        grow = np.linalg.svd(W - h * O, compute_uv=False)[0] - s1
+        capped = np.linalg.svd(W - h * O2, compute_uv=False)[0] - s1
+        assert abs(grow + h * c) < 50 * h * h          # first order: -h u^T O v > 0
+        assert abs(capped) < 50 * h * h                # removed: second order only
+
+
+def test_cap_inactive_cases():
+    rng = np.random.default_rng(42)
+    W, u1, v1, s1 = _gapped(rng, 30, 20)
+    O = rng.standard_normal((30, 20))
+    O += (abs(u1 @ O @ v1) + 0.5) * np.outer(u1, v1)    # u1^T O v1 > 0: sigma_1 shrinks
+    O2, gamma = orc.spectral_cap_update(O, u1, v1, s1, cap=0.0)
+    assert gamma == 0.0 and np.array_equal(O2, O)
+    O3 = O - 2 * (u1 @ O @ v1) * np.outer(u1, v1)       # now it would grow, but sigma is below the cap
+    O4, gamma = orc.spectral_cap_update(O3, u1, v1, s1, cap=s1 + 1.0)
+    assert gamma == 0.0 and np.array_equal(O4, O3)
+
+
+def test_power_step_converges_to_lapack_pair():
+    rng = np.random.default_rng(43)
+    W, u1, v1, s1 = _gapped(rng, 50, 80, top=3.0)
+    u, v = rng.standard_normal(50), rng.standard_normal(80)
+    u, v = u / np.linalg.norm(u), v / np.linalg.norm(v)
+    for _ in range(60):
+        u, v, sig = orc.power_step(W, u, v)
+    assert abs(abs(u @ u1) - 1) < 1e-10 and abs(abs(v @ v1) - 1) < 1e-10
+    assert abs(sig - s1) < 1e-9
+    # rank one: exact after one step from any start not orthogonal to it
+    a, b = rng.standard_normal(12), rng.standard_normal(9)
+    u, v, sig = orc.power_step(2.5 * np.outer(a, b), rng.standard_normal(12), rng.standard_normal(9))
+    np.testing.assert_allclose(np.abs(u), np.abs(a) / np.linalg.norm(a), atol=1e-14)
+    np.testing.assert_allclose(np.abs(v), np.abs(b) / np.linalg.norm(b), atol=1e-14)
+    # zero weight: the vectors stay
+    u0, v0 = rng.standard_normal(12), rng.standard_normal(9)
+    u, v, sig = orc.power_step(np.zeros((12, 9)), u0, v0)
+    assert sig == 0.0 and np.array_equal(u, u0) and np.array_equal(v, v0)
+
+
+def test_capped_step_matches_uncapped_when_off():
+    rng = np.random.default_rng(44)
+    W, M, G = rng.standard_normal((24, 40)), rng.standard_normal((24, 40)), rng.standard_normal((24, 40))
+    u, v = rng.standard_normal(24), rng.standard_normal(40)
+    u, v = u / np.linalg.norm(u), v / np.linalg.norm(v)
+    ref = orc.muon_step(W, M, G, beta=0.95, lr=0.02, steps=3)
+    out = orc.muon_step_capped(W, M, G, u, v, 0.0, cap=1e30, beta=0.95, lr=0.02, steps=3)
+    assert out["gamma"] == 0.0
+    np.testing.assert_array_equal(out["W"], ref["W"])
+    np.testing.assert_array_equal(out["O"], ref["O"])
