@@ -131,12 +131,19 @@ def bench_full_step(args, torch, mu, wl):
     w = wl.config4(count=args.count, steps=steps_ns)
     log(f"[bench] generated in {time.time() - t0:.1f}s")
     groups, devs = [], []
+    gen = torch.Generator(device="cuda").manual_seed(5)
     for g in w.groups:
         G = torch.from_numpy(g.G.view(np.int16)).view(torch.bfloat16).cuda()
         W = torch.from_numpy(g.W).cuda()
         M = torch.from_numpy(g.M).cuda()
         devs.append((G, W, M))
-        groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov))
+        cap = {}
+        if args.cap:  # spectral cap on, estimates from random unit vectors
+            u = torch.randn((g.count, g.m), generator=gen, device="cuda")
+            v = torch.randn((g.count, g.n), generator=gen, device="cuda")
+            cap = dict(cap_u=u / u.norm(dim=1, keepdim=True), cap_v=v / v.norm(dim=1, keepdim=True),
+                       cap_sigma=torch.zeros(g.count, device="cuda"), cap=0.0)
+        groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov, **cap))
     ws = mu.muon_step(groups, steps=steps_ns)  # allocates the workspace once
     torch.cuda.synchronize()
     # the library lists the phases muon_step_timed brackets with events
@@ -198,6 +205,9 @@ def bench_full_step(args, torch, mu, wl):
         elif ph == "symprod":
             work.append(sym_products[si] * sym_f)
             si += 1
+        elif ph in ("cap", "power"):  # bytes: read X (2 B/elt) / read W (4 B/elt); power follows apply
+            g, s, l = per_group[gi_a if ph == "cap" else gi_a - 1]
+            work.append(g.count * g.m * g.n * (2 if ph == "cap" else 4))
         else:
             raise RuntimeError(f"unexpected phase {ph}")
     dur = {}
@@ -212,7 +222,7 @@ def bench_full_step(args, torch, mu, wl):
         tot_w = sum(wk for _, wk in rows)
         n = len(rows)
         rate = tot_w / (tot_ms * 1e-3)
-        if kind in ("momentum", "apply"):
+        if kind in ("momentum", "apply", "cap", "power"):
             kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "bytes_per_launch": tot_w / n,
                              "gbs": rate / 1e9, "frac": rate / 1e9 / PEAK_HBM_GBS}
         else:
@@ -249,6 +259,7 @@ def bench_full_step(args, torch, mu, wl):
                                f"{args.count}x in_proj 3352x768, bf16 grads, fp32 W/M, "
                                f"{steps_ns} cubic NS steps",
                    "matrices": 2 * args.count, "ns_steps": steps_ns, "parallelism": "none (1 GPU)",
+                   "spectral_cap": bool(args.cap),
                    "schedule": " ".join(phases)},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
@@ -401,6 +412,7 @@ def main():
     ap.add_argument("--batch", type=int, default=393216, help="injections batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense", action="store_true", help="injections_factored: also write the dense result")
+    ap.add_argument("--cap", action="store_true", help="full_step: spectral cap on (power step per update)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB plain copy first (reference for profiler byte counters)")
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 2
+#define MUON_VERSION 3
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -113,7 +113,23 @@ typedef struct {
  *              grad_dtype (MUON_BF16 or MUON_F32)
  *   O          NULL, or a host array of `count` device pointers receiving the
  *              orthogonalised update, m x n in the precision of the cfg
- *   lr, beta, scale, nesterov   as in the formulas above */
+ *              (after the spectral cap when it acts)
+ *   lr, beta, scale, nesterov   as in the formulas above
+ * Spectral cap ("An Isotropy-Preserving Spectral Cap for Muon": remove the
+ * update direction that grows the weight's top singular value, keep the
+ * rest).  cap_u NULL: off.  Otherwise, per matrix, with caller-initialised
+ * estimates u (unit, float32[m]) and v (unit, float32[n]) of W's top singular
+ * vectors and sigma of its top singular value:
+ *   c = u^T O v;  if sigma >= cap and c < 0:  O = O - c u v^T
+ *   W = W - lr * scale * O
+ *   u = W v / ||W v||,  v = W^T u / ||W^T u||,  sigma = ||W v||   (old u, v on
+ *   the right; a zero product keeps its vector)
+ * so u, v, sigma track W's top pair by one power step per update.
+ *   cap_u, cap_v  host arrays of count device pointers to float32[m], [n],
+ *                 read and updated in place
+ *   cap_sigma     device float32[count], read and updated
+ *   cap           threshold (<= 0: the cap may act at every step)
+ * Requires W.  Zero-initialised fields (cap_u NULL) leave the cap off. */
 typedef struct {
   int m, n, count;
   int grad_dtype;
@@ -123,6 +139,10 @@ typedef struct {
   void* const* O;
   float lr, beta, scale;
   int nesterov;
+  float* const* cap_u;
+  float* const* cap_v;
+  float* cap_sigma;
+  float cap;
 } muon_group;
 
 /* Bytes of device workspace muon_step needs for these groups (0 on invalid
@@ -145,7 +165,9 @@ typedef enum {
   MUON_PHASE_SYMPROD = 5,     /* grouped symmetric s x s products (accumulated schedule) */
   MUON_PHASE_APPLY = 6,       /* apply pass of one group */
   MUON_PHASE_F32_GRAM = 7,    /* Gram of one float32 group */
-  MUON_PHASE_F32_COMBINE = 8  /* combine of one float32 group */
+  MUON_PHASE_F32_COMBINE = 8, /* combine of one float32 group */
+  MUON_PHASE_CAP = 9,         /* spectral-cap coefficient u^T O v of one group */
+  MUON_PHASE_POWER = 10       /* power step on one group's updated weights */
 } muon_phase;
 
 /* The phases muon_step would run for these groups and cfg, in order: returns

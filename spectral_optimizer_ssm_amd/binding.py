@@ -17,7 +17,7 @@ MUON_F32, MUON_BF16 = 0, 1
 MUON_OK, MUON_EINVAL, MUON_EUNSUPPORTED, MUON_EWORKSPACE, MUON_EHIP = 0, -1, -2, -3, -4
 MUON_NS_AUTO, MUON_NS_ITERATE, MUON_NS_ACCUMULATE = 0, 1, 2
 PHASES = {1: "momentum", 2: "ns_small", 3: "gram", 4: "combine", 5: "symprod", 6: "apply", 7: "f32_gram",
-          8: "f32_combine"}
+          8: "f32_combine", 9: "cap", 10: "power"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmuon.so")
@@ -42,7 +42,9 @@ class GroupC(ctypes.Structure):
                 ("W", ctypes.POINTER(ctypes.c_void_p)), ("M", ctypes.POINTER(ctypes.c_void_p)),
                 ("G", ctypes.POINTER(ctypes.c_void_p)), ("O", ctypes.POINTER(ctypes.c_void_p)),
                 ("lr", ctypes.c_float), ("beta", ctypes.c_float), ("scale", ctypes.c_float),
-                ("nesterov", ctypes.c_int)]
+                ("nesterov", ctypes.c_int),
+                ("cap_u", ctypes.POINTER(ctypes.c_void_p)), ("cap_v", ctypes.POINTER(ctypes.c_void_p)),
+                ("cap_sigma", ctypes.c_void_p), ("cap", ctypes.c_float)]
 
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
@@ -155,6 +157,13 @@ class MuonGroup:
     O: object = None
     scale: float = 1.0
     nesterov: bool = True
+    # spectral cap: unit estimates of W's top singular vectors ([count, m] and
+    # [count, n] float32, updated in place), of its top singular value
+    # ([count] float32, updated), and the threshold; cap_u None: off
+    cap_u: object = None
+    cap_v: object = None
+    cap_sigma: object = None
+    cap: float = 0.0
 
 
 def _marshal_groups(groups: Sequence[MuonGroup]):
@@ -168,12 +177,27 @@ def _marshal_groups(groups: Sequence[MuonGroup]):
         pw, pm, pg = _ptrs(W), _ptrs(M), _ptrs(G)
         po = _ptrs(O) if O is not None else None
         keep += [pw, pm, pg, po, W, M, G, O]
+        cu = cv = None
+        sig = None
+        if g.cap_u is not None:
+            U1, V1 = _split(g.cap_u), _split(g.cap_v)
+            for t, size in [(t, m) for t in U1] + [(t, n) for t in V1]:
+                if not t.is_contiguous() or t.numel() != size or t.dtype != W[0].dtype:
+                    raise ValueError("cap_u / cap_v must hold contiguous float32 vectors of length m / n")
+            if not g.cap_sigma.is_contiguous() or g.cap_sigma.numel() != len(W):
+                raise ValueError("cap_sigma must be a contiguous float32 tensor with one entry per matrix")
+            cu, cv = _ptrs(U1), _ptrs(V1)
+            sig = ctypes.c_void_p(g.cap_sigma.data_ptr())
+            keep += [cu, cv, U1, V1, g.cap_sigma]
         cgroups.append(GroupC(int(m), int(n), len(W), _dtype_code(G[0]),
                               ctypes.cast(pw, ctypes.POINTER(ctypes.c_void_p)),
                               ctypes.cast(pm, ctypes.POINTER(ctypes.c_void_p)),
                               ctypes.cast(pg, ctypes.POINTER(ctypes.c_void_p)),
                               ctypes.cast(po, ctypes.POINTER(ctypes.c_void_p)) if po is not None else None,
-                              float(g.lr), float(g.beta), float(g.scale), int(bool(g.nesterov))))
+                              float(g.lr), float(g.beta), float(g.scale), int(bool(g.nesterov)),
+                              ctypes.cast(cu, ctypes.POINTER(ctypes.c_void_p)) if cu is not None else None,
+                              ctypes.cast(cv, ctypes.POINTER(ctypes.c_void_p)) if cv is not None else None,
+                              sig, float(g.cap)))
     arr = (GroupC * len(cgroups))(*cgroups)
     return arr, keep
 

@@ -189,11 +189,26 @@ struct ApplyArgs {
   int P;
   float eps;
   float neg_lr_scale;
+  const float* cap_part;  // spectral cap (see ApplyLaunch)
+  int cap_P;
+  const float* cap_sigma;
+  float cap;
+  PtrTable cu, cv;
 };
 
 __device__ __forceinline__ float apply_prologue(const ApplyArgs& a, int z, float* red) {
   if (a.partials == nullptr) return 1.0f;
   return inv_norm_from_partials(a.partials + static_cast<long long>(z) * a.P, a.P, a.eps, red, nullptr);
+}
+
+// gamma of the spectral cap for matrix z (0 when the cap is off or inactive):
+// c = u^T O v from fixed-order partial sums.
+__device__ __forceinline__ float cap_gamma(const ApplyArgs& a, int z, float* red) {
+  if (a.cap_part == nullptr) return 0.0f;
+  float c = 0.0f;
+  for (int i = threadIdx.x; i < a.cap_P; i += blockDim.x) c += a.cap_part[static_cast<long long>(z) * a.cap_P + i];
+  c = block_sum(c, red);
+  return (a.cap_sigma[z] >= a.cap && c < 0.0f) ? c : 0.0f;
 }
 
 template <typename XT>
@@ -205,6 +220,9 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
   float* w = static_cast<float*>(W.p[z]);
   XT* o = static_cast<XT*>(O.p[z]);
   const float inv = apply_prologue(a, z, red);
+  const float gamma = cap_gamma(a, z, red);
+  const float* cu = static_cast<const float*>(a.cu.p[z]);
+  const float* cv = static_cast<const float*>(a.cv.p[z]);
   const int cpr = (n + 7) / 8;
   const long long chunks = static_cast<long long>(m) * cpr;
   const bool vec = (n % 8) == 0 && (!w || a16(w)) && (!o || a16(o));
@@ -218,6 +236,11 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
       Vec8<XT>::load(x + static_cast<long long>(r) * ld + c0, ov);
 #pragma unroll
       for (int j = 0; j < 8; ++j) ov[j] *= inv;
+      if (gamma != 0.0f) {
+        const float gu = gamma * cu[r];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ov[j] = fmaf(-gu, cv[c0 + j], ov[j]);
+      }
       if (o) Vec8<XT>::store(o + off, ov);
       if (w) {
         Vec8<float>::load(w + off, wv);
@@ -227,7 +250,8 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
       }
     } else {
       for (int j = 0; j < 8 && c0 + j < n; ++j) {
-        const float ov = ld1<XT>(x + static_cast<long long>(r) * ld + c0 + j) * inv;
+        float ov = ld1<XT>(x + static_cast<long long>(r) * ld + c0 + j) * inv;
+        if (gamma != 0.0f) ov = fmaf(-gamma * cu[r], cv[c0 + j], ov);
         if (o) st1<XT>(o + off + j, ov);
         if (w) w[off + j] = fmaf(a.neg_lr_scale, ov, w[off + j]);
       }
@@ -245,6 +269,9 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
   float* w = static_cast<float*>(W.p[z]);
   XT* o = static_cast<XT*>(O.p[z]);
   const float inv = apply_prologue(a, z, red);
+  const float gamma = cap_gamma(a, z, red);
+  const float* cu = static_cast<const float*>(a.cu.p[z]);
+  const float* cv = static_cast<const float*>(a.cv.p[z]);
   // tiles over U = X^T (m x n): rows k (long side), cols i (short side)
   const int tiles_i = (n + 63) / 64;
   const int k0 = (blockIdx.x / tiles_i) * 64;
@@ -278,6 +305,11 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
       float ov[8], wv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) ov[j] = tile[kr][ic + j];
+      if (gamma != 0.0f) {
+        const float gu = gamma * cu[ur];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ov[j] = fmaf(-gu, cv[uc + j], ov[j]);
+      }
       if (o) Vec8<XT>::store(o + off, ov);
       if (w) {
         Vec8<float>::load(w + off, wv);
@@ -287,7 +319,8 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
       }
     } else {
       for (int j = 0; j < 8 && uc + j < n; ++j) {
-        const float ov = tile[kr][ic + j];
+        float ov = tile[kr][ic + j];
+        if (gamma != 0.0f) ov = fmaf(-gamma * cu[ur], cv[uc + j], ov);
         if (o) st1<XT>(o + off + j, ov);
         if (w) w[off + j] = fmaf(a.neg_lr_scale, ov, w[off + j]);
       }
@@ -339,7 +372,7 @@ hipError_t launch_momentum(const MomentumLaunch& L, hipStream_t st) {
 }
 
 hipError_t launch_apply(const ApplyLaunch& L, hipStream_t st) {
-  ApplyArgs a{L.partials, L.P, L.eps, L.neg_lr_scale};
+  ApplyArgs a{L.partials, L.P, L.eps, L.neg_lr_scale, L.cap_part, L.cap_P, L.cap_sigma, L.cap, L.cu, L.cv};
   const dim3 block(256);
   if (L.tall) {
     const dim3 grid(((L.m + 63) / 64) * ((L.n + 63) / 64), L.count);

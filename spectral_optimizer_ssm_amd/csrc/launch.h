@@ -32,7 +32,43 @@ struct ApplyLaunch {
   int P;
   float eps;
   float neg_lr_scale;
+  // spectral cap (cap_part null: none): O <- O - gamma u v^T with
+  // c = sum of the cap_P partials, gamma = c if sigma >= cap and c < 0, else 0
+  const float* cap_part;
+  int cap_P;
+  const float* cap_sigma;
+  float cap;
+  PtrTable cu, cv;     // u (m floats), v (n floats) per matrix
 };
+
+// Spectral cap: partials of u^T O v over the oriented final iterate.
+struct CapCoefLaunch {
+  const void* X;       // [count][s_pad][ld], bf16 or float
+  long long xstride;
+  int s, l, ld, count;
+  bool tall;           // X = O^T
+  PtrTable u, v;       // float[m], float[n] per matrix
+  float* part;         // [count][P]
+  int P;
+};
+int cap_coef_blocks(int s);
+hipError_t launch_cap_coef(const CapCoefLaunch& L, bool x_bf16, hipStream_t st);
+
+// One simultaneous power step on the updated weights.
+struct PowerLaunch {
+  PtrTable W;          // float m x n per matrix
+  MutPtrTable u, v;    // in: current estimates; out: the next ones
+  float* sigma;        // [count]: ||W v||
+  float* ybuf;         // [count][m]   W v
+  float* zbuf;         // [count][n]   W^T u
+  float* zpart;        // [count][nrc][n] partials of W^T u over row blocks
+  float* ynorm;        // [count][nrc] partial sums of (W v)_r^2
+  float* znorm;        // [count][ncb] partial sums of (W^T u)_j^2
+  int m, n, count, nrc, ncb;
+};
+int power_row_blocks(int m);
+int power_col_blocks(int n);
+hipError_t launch_power_step(const PowerLaunch& L, hipStream_t st);
 
 // One batched Newton-Schulz GEMM over `count` matrices of one shape, laid out
 // contiguously: X [count][s_pad][ld], A [count][s_pad][s_pad].

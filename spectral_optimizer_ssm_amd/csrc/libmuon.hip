@@ -77,6 +77,8 @@ struct GroupPlan {
   int s_pad = 0, ld = 0, kdim = 0, P = 0;
   size_t esz = 0;
   size_t off_x0 = 0, off_x1 = 0, off_a = 0, off_part = 0, end = 0;
+  bool cap = false;                 // spectral cap: partials of u^T O v and of the power step
+  size_t off_cap = 0, off_y = 0, off_z = 0, off_zp = 0, off_yn = 0, off_zn = 0;
 };
 
 // s_pad x s_pad buffers of the accumulated schedule, after the iterates.
@@ -95,7 +97,7 @@ bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
   return gram + comb + 3.0 * (C.steps - 1) * prod < 0.85 * C.steps * (gram + comb);
 }
 
-int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base, GroupPlan* g) {
+int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base, GroupPlan* g, bool cap = false) {
   if (m <= 0 || n <= 0 || count < 0) return MUON_EINVAL;
   if (static_cast<long long>(m) * n > (1LL << 31)) return MUON_EUNSUPPORTED;
   g->m = m;
@@ -134,6 +136,22 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
                    kAlign);
   g->off_part = off;
   off = align_up(off + static_cast<size_t>(count) * g->P * sizeof(float), kAlign);
+  g->cap = cap;
+  if (cap) {
+    g->off_cap = off;
+    off = align_up(off + static_cast<size_t>(count) * cap_coef_blocks(g->s) * sizeof(float), kAlign);
+    const size_t cnt = static_cast<size_t>(count), f = sizeof(float);
+    g->off_y = off;
+    off = align_up(off + cnt * m * f, kAlign);
+    g->off_z = off;
+    off = align_up(off + cnt * n * f, kAlign);
+    g->off_zp = off;
+    off = align_up(off + cnt * power_row_blocks(m) * n * f, kAlign);
+    g->off_yn = off;
+    off = align_up(off + cnt * power_row_blocks(m) * f, kAlign);
+    g->off_zn = off;
+    off = align_up(off + cnt * power_col_blocks(n) * f, kAlign);
+  }
   g->end = off;
   return MUON_OK;
 }
@@ -150,6 +168,14 @@ int validate_group(const muon_group& gr) {
       return MUON_EINVAL;
     if (gr.O != nullptr && gr.O[i] == nullptr) return MUON_EINVAL;
   }
+  if (gr.cap_u != nullptr) {
+    if (gr.cap_v == nullptr || gr.cap_sigma == nullptr || !aligned_to(gr.cap_sigma, 4) || !std::isfinite(gr.cap))
+      return MUON_EINVAL;
+    for (int i = 0; i < gr.count; ++i)
+      if (gr.cap_u[i] == nullptr || gr.cap_v[i] == nullptr || !aligned_to(gr.cap_u[i], 4) ||
+          !aligned_to(gr.cap_v[i], 4))
+        return MUON_EINVAL;
+  }
   return MUON_OK;
 }
 
@@ -165,6 +191,10 @@ struct GroupRun {
   std::vector<void*> o_own;
   float beta = 0.0f, neg_lr_scale = 0.0f;
   int nesterov = 0;
+  float* const* cap_u = nullptr;   // spectral cap state (null: off)
+  float* const* cap_v = nullptr;
+  float* cap_sigma = nullptr;
+  float cap = 0.0f;
 };
 
 // Optional phase markers: caller-created events recorded on the stream after
@@ -412,11 +442,26 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     fin[gi] = C.steps & 1;
   }
 
-  // 5. apply
+  // 5. apply (spectral cap: coefficient before, power step after)
   for (size_t gi = 0; gi < runs.size(); ++gi) {
     const GroupRun& R = runs[gi];
     const GroupPlan& p = R.plan;
     if (p.count == 0) continue;
+    const long long xs = static_cast<long long>(p.s_pad) * p.ld;
+    if (p.cap) {
+      for (int c0 = 0; E.live() && c0 < p.count; c0 += kMaxTable) {
+        const int cn = std::min(kMaxTable, p.count - c0);
+        CapCoefLaunch K{};
+        K.X = x_of(p, ws, fin[gi]) + static_cast<size_t>(c0) * xs * p.esz;
+        K.xstride = xs;
+        K.s = p.s; K.l = p.l; K.ld = p.ld; K.count = cn; K.tall = p.tall;
+        for (int i = 0; i < cn; ++i) { K.u.p[i] = R.cap_u[c0 + i]; K.v.p[i] = R.cap_v[c0 + i]; }
+        K.P = cap_coef_blocks(p.s);
+        K.part = reinterpret_cast<float*>(ws + p.off_cap) + static_cast<size_t>(c0) * K.P;
+        if (launch_cap_coef(K, p.bf16, st) != hipSuccess) return MUON_EHIP;
+      }
+      if (!E.mark(st, MUON_PHASE_CAP)) return MUON_EHIP;
+    }
     if (E.live() && (R.W != nullptr || R.O != nullptr)) {
       const long long xstride = static_cast<long long>(p.s_pad) * p.ld;
       for (int c0 = 0; c0 < p.count; c0 += kMaxTable) {
@@ -434,10 +479,36 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
                                   : nullptr;
         A.P = p.P; A.eps = eps;
         A.neg_lr_scale = R.neg_lr_scale;
+        if (p.cap) {
+          A.cap_P = cap_coef_blocks(p.s);
+          A.cap_part = reinterpret_cast<const float*>(ws + p.off_cap) + static_cast<size_t>(c0) * A.cap_P;
+          A.cap_sigma = R.cap_sigma + c0;
+          A.cap = R.cap;
+          for (int i = 0; i < cn; ++i) { A.cu.p[i] = R.cap_u[c0 + i]; A.cv.p[i] = R.cap_v[c0 + i]; }
+        }
         if (launch_apply(A, st) != hipSuccess) return MUON_EHIP;
       }
     }
     if (!E.mark(st, MUON_PHASE_APPLY)) return MUON_EHIP;
+    if (p.cap) {
+      for (int c0 = 0; E.live() && c0 < p.count; c0 += kMaxTable) {
+        const int cn = std::min(kMaxTable, p.count - c0);
+        PowerLaunch L{};
+        for (int i = 0; i < cn; ++i) {
+          L.W.p[i] = R.W[c0 + i]; L.u.p[i] = R.cap_u[c0 + i]; L.v.p[i] = R.cap_v[c0 + i];
+        }
+        L.sigma = R.cap_sigma + c0;
+        L.m = p.m; L.n = p.n; L.count = cn;
+        L.nrc = power_row_blocks(p.m); L.ncb = power_col_blocks(p.n);
+        L.ybuf = reinterpret_cast<float*>(ws + p.off_y) + static_cast<size_t>(c0) * p.m;
+        L.zbuf = reinterpret_cast<float*>(ws + p.off_z) + static_cast<size_t>(c0) * p.n;
+        L.zpart = reinterpret_cast<float*>(ws + p.off_zp) + static_cast<size_t>(c0) * L.nrc * p.n;
+        L.ynorm = reinterpret_cast<float*>(ws + p.off_yn) + static_cast<size_t>(c0) * L.nrc;
+        L.znorm = reinterpret_cast<float*>(ws + p.off_zn) + static_cast<size_t>(c0) * L.ncb;
+        if (launch_power_step(L, st) != hipSuccess) return MUON_EHIP;
+      }
+      if (!E.mark(st, MUON_PHASE_POWER)) return MUON_EHIP;
+    }
   }
   return MUON_OK;
 }
@@ -468,9 +539,14 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
     if (gr.O != nullptr)
       for (int j = 0; j < gr.count; ++j)
         if (!aligned_to(gr.O[j], dtype_size(cfg->precision))) return MUON_EINVAL;
-    rc = plan_group(gr.m, gr.n, gr.count, cfg->precision == MUON_BF16, C, off, &runs[i].plan);
+    if (gr.cap_u != nullptr && gr.W == nullptr) return MUON_EINVAL;
+    rc = plan_group(gr.m, gr.n, gr.count, cfg->precision == MUON_BF16, C, off, &runs[i].plan, gr.cap_u != nullptr);
     if (rc != MUON_OK) return rc;
     off = runs[i].plan.end;
+    runs[i].cap_u = gr.cap_u;
+    runs[i].cap_v = gr.cap_v;
+    runs[i].cap_sigma = gr.cap_sigma;
+    runs[i].cap = gr.cap;
     runs[i].grad_dtype = gr.grad_dtype;
     runs[i].G = gr.G;
     runs[i].M = gr.M;
@@ -516,7 +592,8 @@ size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muo
   size_t off = 0;
   for (int i = 0; i < ngroups; ++i) {
     GroupPlan g;
-    if (plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &g) != MUON_OK)
+    if (plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &g,
+                   groups[i].cap_u != nullptr) != MUON_OK)
       return 0;
     off = g.end;
   }
@@ -538,7 +615,8 @@ int muon_step_phases(const muon_group* groups, int ngroups, const muon_ns_cfg* c
   size_t off = 0;
   for (int i = 0; i < ngroups; ++i) {
     if (groups[i].grad_dtype != MUON_F32 && groups[i].grad_dtype != MUON_BF16) return MUON_EINVAL;
-    rc = plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &runs[i].plan);
+    rc = plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &runs[i].plan,
+                    groups[i].cap_u != nullptr);
     if (rc != MUON_OK) return rc;
     off = runs[i].plan.end;
     runs[i].grad_dtype = groups[i].grad_dtype;

@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 2
+    assert mu.muon_version() == 3
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -199,3 +199,33 @@ def test_factored_validation(mu, case, expect):
     rc = L.muon_ns_factored(None if case == "null_v" else V, K, mu.MUON_F32 if case == "f32" else mu.MUON_BF16,
                             m, n, r, batch, ctypes.byref(cfg), C, ctypes.c_void_p(O) if dense else None, None)
     assert rc == expect
+
+
+def test_cap_validation_and_phases(mu):
+    L = mu.lib()
+    cfg, keep = _cfg(mu)
+    P = ctypes.POINTER(ctypes.c_void_p)
+    g, k2 = _group(mu, 128, 256, 2)
+    cu = (ctypes.c_void_p * 2)(0x3000000, 0x3001000)
+    cv = (ctypes.c_void_p * 2)(0x3002000, 0x3003000)
+    g.cap_u = ctypes.cast(cu, P)
+    arr = (mu.binding.GroupC * 1)(g)
+    ws = ctypes.c_void_p(0x7000000)
+    assert L.muon_step(arr, 1, ctypes.byref(cfg), ws, 1 << 40, None, None) == -1  # cap_v, cap_sigma missing
+    g.cap_v = ctypes.cast(cv, P)
+    g.cap_sigma = ctypes.c_void_p(0x3004002)                                       # misaligned
+    arr = (mu.binding.GroupC * 1)(g)
+    assert L.muon_step(arr, 1, ctypes.byref(cfg), ws, 1 << 40, None, None) == -1
+    g.cap_sigma = ctypes.c_void_p(0x3004000)
+    g.W = None                                                                      # the cap needs W
+    arr = (mu.binding.GroupC * 1)(g)
+    assert L.muon_step(arr, 1, ctypes.byref(cfg), ws, 1 << 40, None, None) == -1
+    n = L.muon_step_phases(arr, 1, ctypes.byref(cfg), None, 0)
+    out = (ctypes.c_int * n)()
+    L.muon_step_phases(arr, 1, ctypes.byref(cfg), out, n)
+    names = [mu.binding.PHASES[out[i]] for i in range(n)]
+    assert names[-3:] == ["cap", "apply", "power"] and names[0] == "momentum"
+    # the cap's partial buffers enlarge the workspace
+    base, _ = _group(mu, 128, 256, 2)
+    a0 = (mu.binding.GroupC * 1)(base)
+    assert L.muon_step_workspace_size(arr, 1, ctypes.byref(cfg)) > L.muon_step_workspace_size(a0, 1, ctypes.byref(cfg))
