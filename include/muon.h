@@ -95,7 +95,10 @@ typedef enum { MUON_NS_AUTO = 0, MUON_NS_ITERATE = 1, MUON_NS_ACCUMULATE = 2 } m
  *   eps       added to ||U||_F before dividing (>= 0)
  *   precision MUON_BF16 or MUON_F32 (see Precision above)
  *   schedule  a muon_ns_schedule
- * A quintic c != 0 returns MUON_EUNSUPPORTED except in muon_ns_factored. */
+ * Quintic c != 0 runs on large bfloat16 matrices (the matrix-core path: one
+ * more s x s product per step) and in muon_ns_factored; with float32
+ * precision, on small (on-chip) matrices and in muon_ns_batched_small it
+ * returns MUON_EUNSUPPORTED. */
 typedef struct {
   int steps;
   int ncoef;

@@ -238,8 +238,9 @@ def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7
     cg, keep = _marshal_groups(groups)
     cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule)
     need = int(L.muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
-    if need == 0:
-        _check(MUON_EINVAL, "muon_step_workspace_size")
+    if need == 0:  # the size query has no status: ask the step itself, which validates first
+        rc = L.muon_step(cg, len(groups), ctypes.byref(cfg), None, 0, None, None)
+        _check(MUON_EINVAL if rc in (MUON_OK, MUON_EWORKSPACE) else rc, "muon_step")
     if workspace is None or workspace.numel() < need:
         dev = _split(groups[0].W)[0].device
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -36,6 +36,7 @@ size_t dtype_size(int dt) { return dt == MUON_BF16 ? 2 : 4; }
 struct NsCoefs {
   int steps;
   int schedule;
+  bool quintic;  // some step has c != 0
   float a[kMaxSteps], b[kMaxSteps], c[kMaxSteps];
 };
 
@@ -51,6 +52,7 @@ int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out, bool quintic = false) {
   if (cfg->steps > 0 && cfg->coeffs == nullptr) return MUON_EINVAL;
   out->steps = cfg->steps;
   out->schedule = cfg->schedule;
+  out->quintic = false;
   for (int k = 0; k < cfg->steps; ++k) {
     const float* row = cfg->coeffs + (cfg->per_step ? k * cfg->ncoef : 0);
     if (!std::isfinite(row[0]) || !std::isfinite(row[1])) return MUON_EINVAL;
@@ -59,6 +61,7 @@ int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out, bool quintic = false) {
       if (!std::isfinite(row[2])) return MUON_EINVAL;
       if (row[2] != 0.0f && !quintic) return MUON_EUNSUPPORTED;
       out->c[k] = row[2];
+      if (row[2] != 0.0f) out->quintic = true;
     }
     out->a[k] = row[0];
     out->b[k] = row[1];
@@ -81,12 +84,19 @@ struct GroupPlan {
   size_t off_cap = 0, off_y = 0, off_z = 0, off_zp = 0, off_yn = 0, off_zn = 0;
 };
 
-// s_pad x s_pad buffers of the accumulated schedule, after the iterates.
-enum SqBuf { kSqA0 = 0, kSqA1, kSqB0, kSqB1, kSqE, kSqQ0, kSqQ1, kSqCount };
+// s_pad x s_pad buffers after the iterates.  Iterated schedule: A' (cubic) or
+// A, H, P (quintic, kSqA0, kSqA1, kSqB0).  Accumulated schedule: all of
+// them, H only for quintic coefficients.
+enum SqBuf { kSqA0 = 0, kSqA1, kSqB0, kSqB1, kSqE, kSqQ0, kSqQ1, kSqH, kSqMax };
+int sq_buffers(bool accumulate, bool quintic) {
+  if (accumulate) return quintic ? kSqMax : kSqH;
+  return quintic ? 3 : 1;
+}
 
 // Matrix-core work of the two schedules (multiply-adds of the tiles actually
 // computed): per step a Gram (kdim deep) and a combine (s_pad deep), against
 // one Gram, one combine and 3 (steps - 1) symmetric s_pad^3 products.
+// (Quintic adds one s x s product per step to either schedule.)
 bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
   if (g.engine != kTiledBf16 || C.steps < 2 || C.schedule == MUON_NS_ITERATE) return false;
   if (C.schedule == MUON_NS_ACCUMULATE) return true;
@@ -94,7 +104,8 @@ bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
   const double gram = gram_tiles_per_matrix(g.s_pad) * t * t * g.kdim;
   const double comb = combine_tiles_per_matrix(g.s_pad, g.ld) * t * t * g.s_pad;
   const double prod = symprod_tiles_per_matrix(g.s_pad) * t2 * t2 * g.s_pad;
-  return gram + comb + 3.0 * (C.steps - 1) * prod < 0.85 * C.steps * (gram + comb);
+  const double q = C.quintic ? 1.0 : 0.0;
+  return gram + comb + (3.0 * (C.steps - 1) + q * C.steps) * prod < 0.85 * C.steps * (gram + comb + q * prod);
 }
 
 int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base, GroupPlan* g, bool cap = false) {
@@ -122,6 +133,7 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
     g->ld = round_up(g->l, kTileF32);
   }
   g->kdim = std::min(g->ld, round_up(g->l, 64));
+  if (C.quintic && g->engine != kTiledBf16) return MUON_EUNSUPPORTED;  // c != 0: large bf16 matrices only
   g->accumulate = choose_accumulate(*g, C);
   g->P = momentum_blocks_per_matrix(g->tall, g->s_pad, g->ld);
   const size_t xbytes = static_cast<size_t>(count) * g->s_pad * g->ld * g->esz;
@@ -132,7 +144,8 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
   off = align_up(off + xbytes, kAlign);
   g->off_a = off;
   if (g->engine != kSmall)
-    off = align_up(off + (g->accumulate ? kSqCount : 1) * static_cast<size_t>(count) * g->s_pad * g->s_pad * g->esz,
+    off = align_up(off + sq_buffers(g->accumulate, C.quintic) * static_cast<size_t>(count) * g->s_pad * g->s_pad *
+                             g->esz,
                    kAlign);
   g->off_part = off;
   off = align_up(off + static_cast<size_t>(count) * g->P * sizeof(float), kAlign);
@@ -306,21 +319,45 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     S.P = p.P; S.eps = eps;
     return S;
   };
+  auto sym_seg = [&](const GroupPlan& p) {
+    SymSeg S{};
+    S.stride = static_cast<long long>(p.s_pad) * p.s_pad;
+    S.s_pad = p.s_pad; S.count = p.count; S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);
+    S.P = p.P; S.eps = eps;
+    S.b1 = 1.0f;
+    return S;
+  };
   if (!it.empty() && C.steps > 0) {
     // per step: A' = a I + b X X^T (step 1 on the unnormalised U, with the
-    // normalisation folded into the coefficients), then X = A' X
+    // normalisation folded into the coefficients), then X = A' X.  Quintic:
+    // A = X X^T and H = b I + c A from the Gram, P = a I + A H (= a I + b A +
+    // c A^2) from one symmetric product, then X = P X.
     const std::vector<int> by_k = heavy_first(it, true), by_s = heavy_first(it, false);
     for (int k = 0; k < C.steps; ++k) {
       const int cur = k & 1;
       std::vector<GemmSeg> gs, cs;
+      std::vector<SymSeg> ps;
       for (int gi : by_k) {
         const GroupPlan& p = runs[gi].plan;
         GemmSeg S = gemm_seg(p, true);
         S.X = reinterpret_cast<const bf16_t*>(x_of(p, ws, cur));
-        S.A = sq_of(p, ws, 0);
+        S.A = sq_of(p, ws, kSqA0);
         S.partials = k == 0 ? reinterpret_cast<const float*>(ws + p.off_part) : nullptr;
-        S.a = C.a[k]; S.b = C.b[k];
-        S.pa = k == 0 ? 1 : 0; S.pb = k == 0 ? 3 : 0;
+        if (!C.quintic) {
+          S.a = C.a[k]; S.b = C.b[k];
+          S.pa = k == 0 ? 1 : 0; S.pb = k == 0 ? 3 : 0;
+        } else {
+          S.a = 0.0f; S.b = 1.0f; S.pa = 0; S.pb = k == 0 ? 2 : 0;   // A
+          S.A2 = sq_of(p, ws, kSqA1); S.a2 = C.b[k]; S.b2 = C.c[k];  // H = b I + c A
+          SymSeg Q = sym_seg(p);                                      // P = a I + A H
+          Q.L = sq_of(p, ws, kSqA0); Q.R = sq_of(p, ws, kSqA1); Q.O1 = sq_of(p, ws, kSqB0);
+          Q.a1 = C.a[k];
+          if (k == 0) {  // X0 = inv U: fold inv into P
+            Q.partials = reinterpret_cast<const float*>(ws + p.off_part);
+            Q.pa = 1; Q.pb = 1;
+          }
+          ps.push_back(Q);
+        }
         gs.push_back(S);
       }
       for (int gi : by_s) {
@@ -328,11 +365,15 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
         GemmSeg S = gemm_seg(p, false);
         S.X = reinterpret_cast<const bf16_t*>(x_of(p, ws, cur));
         S.Y = reinterpret_cast<bf16_t*>(x_of(p, ws, cur ^ 1));
-        S.A = sq_of(p, ws, 0);
+        S.A = sq_of(p, ws, C.quintic ? kSqB0 : kSqA0);
         cs.push_back(S);
       }
-      if (!launch_segments<GemmArgs>(gs, launch_gram_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_GRAM) ||
-          !launch_segments<GemmArgs>(cs, launch_combine_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_COMBINE))
+      if (!launch_segments<GemmArgs>(gs, launch_gram_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_GRAM))
+        return MUON_EHIP;
+      if (C.quintic &&
+          (!launch_segments<SymArgs>(ps, launch_symprod_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_SYMPROD)))
+        return MUON_EHIP;
+      if (!launch_segments<GemmArgs>(cs, launch_combine_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_COMBINE))
         return MUON_EHIP;
     }
     for (int gi : it) fin[gi] = C.steps & 1;
@@ -343,6 +384,8 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     //   A_{k+1} = A_k B_k^2,   Q = B_{steps-1} ... B_1 B_0,   X = Q X0,
     // s_pad x s_pad products instead of s_pad x ld ones.  Buffers: A_k in
     // A[k & 1], B_k in B[k & 1], E = B_k^2, Q_1 = B_0, Q_k (k >= 2) in Q[k & 1].
+    // Quintic: B_k = a_k I + A_k H_k with H_k = b_k I + c_k A_k (buffer H),
+    // one more product per step.
     const int n = C.steps;
     const std::vector<int> by_k = heavy_first(ac, true), by_s = heavy_first(ac, false);
     std::vector<GemmSeg> gs;
@@ -354,20 +397,29 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       S.A2 = sq_of(p, ws, kSqB0);
       S.partials = reinterpret_cast<const float*>(ws + p.off_part);
       S.a = 0.0f; S.b = 1.0f; S.pa = 0; S.pb = 2;  // A_0 = inv^2 U U^T
-      S.a2 = C.a[0]; S.b2 = C.b[0];                // B_0
+      if (!C.quintic) {
+        S.a2 = C.a[0]; S.b2 = C.b[0];              // B_0
+      } else {
+        S.A2 = sq_of(p, ws, kSqH);                 // H_0 = b_0 I + c_0 A_0
+        S.a2 = C.b[0]; S.b2 = C.c[0];
+      }
       gs.push_back(S);
     }
     if (!launch_segments<GemmArgs>(gs, launch_gram_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_GRAM))
       return MUON_EHIP;
-    auto sym_seg = [&](const GroupPlan& p) {
-      SymSeg S{};
-      S.stride = static_cast<long long>(p.s_pad) * p.s_pad;
-      S.s_pad = p.s_pad; S.count = p.count; S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);
-      S.P = p.P; S.eps = eps;
-      S.b1 = 1.0f;
-      return S;
-    };
     for (int k = 0; k < n; ++k) {
+      if (C.quintic) {  // B_k = a_k I + A_k H_k
+        std::vector<SymSeg> lb;
+        for (int gi : ac) {
+          const GroupPlan& p = runs[gi].plan;
+          SymSeg S = sym_seg(p);
+          S.L = sq_of(p, ws, kSqA0 + (k & 1)); S.R = sq_of(p, ws, kSqH); S.O1 = sq_of(p, ws, kSqB0 + (k & 1));
+          S.a1 = C.a[k];
+          lb.push_back(S);
+        }
+        if (!launch_segments<SymArgs>(lb, launch_symprod_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_SYMPROD))
+          return MUON_EHIP;
+      }
       std::vector<SymSeg> l1, l2;
       for (int gi : ac) {
         const GroupPlan& p = runs[gi].plan;
@@ -389,13 +441,19 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
           }
           l1.push_back(S);
         }
-        if (k + 1 < n) {  // A_{k+1} = A_k E, B_{k+1} = a I + b A_{k+1}
+        if (k + 1 < n) {  // A_{k+1} = A_k E, B_{k+1} = a I + b A_{k+1} (quintic: H_{k+1} = b I + c A_{k+1})
           SymSeg S = sym_seg(p);
           S.L = sq_of(p, ws, kSqA0 + (k & 1));
           S.R = sq_of(p, ws, kSqE);
-          S.O1 = k + 2 < n ? sq_of(p, ws, kSqA0 + ((k + 1) & 1)) : nullptr;  // the last A is not needed
-          S.O2 = sq_of(p, ws, kSqB0 + ((k + 1) & 1));
-          S.a2 = C.a[k + 1]; S.b2 = C.b[k + 1];
+          if (!C.quintic) {
+            S.O1 = k + 2 < n ? sq_of(p, ws, kSqA0 + ((k + 1) & 1)) : nullptr;  // the last A is not needed
+            S.O2 = sq_of(p, ws, kSqB0 + ((k + 1) & 1));
+            S.a2 = C.a[k + 1]; S.b2 = C.b[k + 1];
+          } else {
+            S.O1 = sq_of(p, ws, kSqA0 + ((k + 1) & 1));
+            S.O2 = sq_of(p, ws, kSqH);
+            S.a2 = C.b[k + 1]; S.b2 = C.c[k + 1];
+          }
           l2.push_back(S);
         }
       }
@@ -527,7 +585,7 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
               float* norms_out, void* stream, void* const* events, int nevents) {
   if (groups == nullptr || ngroups <= 0) return MUON_EINVAL;
   NsCoefs C;
-  int rc = parse_cfg(cfg, &C);
+  int rc = parse_cfg(cfg, &C, true);
   if (rc != MUON_OK) return rc;
   if (norms_out != nullptr && !aligned_to(norms_out, 4)) return MUON_EINVAL;
   std::vector<GroupRun> runs(ngroups);
@@ -588,7 +646,7 @@ int muon_version(void) { return MUON_VERSION; }
 
 size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg) {
   NsCoefs C;
-  if (groups == nullptr || ngroups <= 0 || parse_cfg(cfg, &C) != MUON_OK) return 0;
+  if (groups == nullptr || ngroups <= 0 || parse_cfg(cfg, &C, true) != MUON_OK) return 0;
   size_t off = 0;
   for (int i = 0; i < ngroups; ++i) {
     GroupPlan g;
@@ -609,7 +667,7 @@ int muon_step_phases(const muon_group* groups, int ngroups, const muon_ns_cfg* c
   NsCoefs C;
   if (groups == nullptr || ngroups <= 0 || max_phases < 0 || (phases == nullptr && max_phases > 0))
     return MUON_EINVAL;
-  int rc = parse_cfg(cfg, &C);
+  int rc = parse_cfg(cfg, &C, true);
   if (rc != MUON_OK) return rc;
   std::vector<GroupRun> runs(ngroups);
   size_t off = 0;
@@ -635,7 +693,7 @@ int muon_step_timed(const muon_group* groups, int ngroups, const muon_ns_cfg* cf
 
 size_t muon_ns_workspace_size(int m, int n, int batch, int dtype, const muon_ns_cfg* cfg) {
   NsCoefs C;
-  if (parse_cfg(cfg, &C) != MUON_OK || (dtype != MUON_F32 && dtype != MUON_BF16)) return 0;
+  if (parse_cfg(cfg, &C, true) != MUON_OK || (dtype != MUON_F32 && dtype != MUON_BF16)) return 0;
   GroupPlan g;
   if (plan_group(m, n, batch, dtype == MUON_BF16, C, 0, &g) != MUON_OK) return 0;
   return g.end == 0 ? kAlign : g.end;
@@ -644,7 +702,7 @@ size_t muon_ns_workspace_size(int m, int n, int batch, int dtype, const muon_ns_
 int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int batch, const muon_ns_cfg* cfg,
                           void* workspace, size_t workspace_bytes, void* stream) {
   NsCoefs C;
-  int rc = parse_cfg(cfg, &C);
+  int rc = parse_cfg(cfg, &C, true);
   if (rc != MUON_OK) return rc;
   if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_EINVAL;
   if (cfg->precision != dtype) return MUON_EUNSUPPORTED;
@@ -722,7 +780,7 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
 int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long long batch, const muon_ns_cfg* cfg,
                           void* stream) {
   NsCoefs C;
-  int rc = parse_cfg(cfg, &C);
+  int rc = parse_cfg(cfg, &C);  // quintic not on the on-chip kernels
   if (rc != MUON_OK) return rc;
   if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_EINVAL;
   if (cfg->precision != dtype) return MUON_EUNSUPPORTED;

@@ -35,7 +35,7 @@ def compare_step(g, i, out, dev_tensors, w, tol, steps=None, zero_eps=False):
     steps = w.steps if steps is None else steps
     ref = orc.muon_step(orc.widen_f32(g.W[i]), orc.widen_f32(g.M[i]), grad64(g, i), beta=w.beta, lr=w.lr,
                         nesterov=w.nesterov, steps=steps, coeffs=w.coeffs, eps=0.0 if zero_eps else w.eps,
-                        scale=w.scale)
+                        scale=w.scale, per_step=w.per_step)
     O = t64(out["O"][i])
     Wn = t64(dev_tensors["W"][i])
     Mn = t64(dev_tensors["M"][i])

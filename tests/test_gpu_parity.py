@@ -53,7 +53,8 @@ def run_step(mu, w, precision=None, steps=None, want_o=True, coeffs=None, eps=No
         groups.append(mu.MuonGroup(W=d["W"], M=d["M"], G=d["G"], O=o["O"], lr=w.lr, beta=w.beta,
                                    scale=w.scale, nesterov=w.nesterov))
     mu.muon_step(groups, steps=w.steps if steps is None else steps, coeffs=coeffs or w.coeffs,
-                 eps=w.eps if eps is None else eps, precision=prec, schedule=sched(mu, schedule))
+                 eps=w.eps if eps is None else eps, precision=prec, schedule=sched(mu, schedule),
+                 per_step=w.per_step)
     torch.cuda.synchronize()
     return devs, outs
 
@@ -342,3 +343,43 @@ def test_timed_events_cover_phases(mu):
     torch.cuda.synchronize()
     times = [evs[k].elapsed_time(evs[k + 1]) for k in range(len(phases))]
     assert all(t >= 0 for t in times)
+
+
+# ---------------------------------------------------------------------------
+# quintic and per-step coefficients (large bf16 matrices, both schedules)
+# ---------------------------------------------------------------------------
+QUINTIC = (2.0, -1.5, 0.5)
+ROWS = [(2.0, -1.5, 0.5), (1.875, -1.25, 0.375), (1.5, -0.5, 0.0)]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("coeffs,per_step,steps", [(QUINTIC, False, 3), (QUINTIC, False, 5), (ROWS, True, 3)])
+def test_quintic_mamba2_shapes(mu, schedule, coeffs, per_step, steps):
+    w = wl.config4(count=3)
+    w.coeffs, w.per_step, w.steps = coeffs, per_step, steps
+    devs, outs = run_step(mu, w, schedule=schedule)
+    for gi, g in enumerate(w.groups):
+        for i in (0, 2):
+            res, _ = compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL)
+            print(g.name, i, schedule, steps, res)
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+@pytest.mark.parametrize("shape", [(256, 512), (520, 1100), (300, 257)])
+def test_quintic_ragged(mu, schedule, shape):
+    m, n = shape
+    g = wl.random_group(300 + m + n, 2, m, n, "bf16")
+    w = wl.Workload(f"quintic{m}x{n}", [g], coeffs=QUINTIC, steps=4)
+    devs, outs = run_step(mu, w, schedule=schedule)
+    for i in range(2):
+        compare_step(g, i, outs[0], devs[0], w, BF16_TOL)
+
+
+def test_quintic_unsupported_paths(mu):
+    """c != 0 on the on-chip and float32 engines is refused before any work."""
+    for m, n, dt, prec in ((64, 128, "bf16", None), (96, 160, "f32", None), (300, 400, "bf16", "f32")):
+        g = wl.random_group(7, 1, m, n, dt)
+        w = wl.Workload("q", [g], coeffs=QUINTIC, steps=2)
+        with pytest.raises(mu.MuonError) as e:
+            run_step(mu, w, precision=mu.MUON_F32 if prec == "f32" else None)
+        assert e.value.status == mu.binding.MUON_EUNSUPPORTED

@@ -136,6 +136,7 @@ class Workload:
     nesterov: bool = True
     steps: int = 5
     coeffs: tuple = (1.5, -0.5)
+    per_step: bool = False
     eps: float = 1e-7
     scale: float = 1.0
     meta: dict = field(default_factory=dict)
