@@ -240,6 +240,28 @@ def muon_step_capped(W, M, G, u, v, sigma, *, cap: float, beta: float, lr: float
 
 
 # ----------------------------------------------------------------------------
+# Companion AdamW for the parameters that Muon does not take ("Muon Meets
+# Mamba": AdamW is the baseline optimizer, and the parameters outside the
+# Muon groups keep it).  The pages give no formula; the reading is AdamW with
+# decoupled weight decay and bias-corrected moments.
+# ----------------------------------------------------------------------------
+def adamw_step(p, g, m, v, *, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+               step: int):
+    """One AdamW step (step counts from 1):
+    m' = b1 m + (1 - b1) g,  v' = b2 v + (1 - b2) g^2,
+    p' = p (1 - lr wd) - lr (m' / (1 - b1^t)) / (sqrt(v' / (1 - b2^t)) + eps).
+    Returns (p', m', v')."""
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m2 = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v2 = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    mhat = m2 / (1.0 - beta1 ** step)
+    vhat = v2 / (1.0 - beta2 ** step)
+    p2 = p * (1.0 - lr * weight_decay) - lr * mhat / (np.sqrt(vhat) + eps)
+    return p2, m2, v2
+
+
+# ----------------------------------------------------------------------------
 # Diagnostics (reported, never part of the update)
 # ----------------------------------------------------------------------------
 def orthogonality_error(O: np.ndarray) -> float:

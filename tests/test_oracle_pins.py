@@ -441,3 +441,36 @@ def test_capped_step_matches_uncapped_when_off():
     assert out["gamma"] == 0.0
     np.testing.assert_array_equal(out["W"], ref["W"])
     np.testing.assert_array_equal(out["O"], ref["O"])
+
+
+# ---------------------------------------------------------------------------
+# Companion AdamW: closed forms of the bias-corrected moments.
+# ---------------------------------------------------------------------------
+def test_adamw_first_step_and_constant_gradient():
+    rng = np.random.default_rng(51)
+    p, g = rng.standard_normal(1000), rng.standard_normal(1000)
+    kw = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    # step 1 from zero moments: m_hat = g, v_hat = g^2
+    p1, m1, v1 = orc.adamw_step(p, g, np.zeros(1000), np.zeros(1000), step=1, **kw)
+    np.testing.assert_allclose(m1, 0.1 * g, rtol=1e-15)
+    np.testing.assert_allclose(v1, 0.05 * g * g, rtol=1e-15)
+    np.testing.assert_allclose(p1, p * (1 - 1e-4) - 1e-3 * g / (np.abs(g) + 1e-8), rtol=1e-12, atol=1e-15)
+    # a constant gradient keeps m_hat = g and v_hat = g^2 at every step
+    pk, mk, vk = p, np.zeros(1000), np.zeros(1000)
+    for t in range(1, 30):
+        prev = pk
+        pk, mk, vk = orc.adamw_step(pk, g, mk, vk, step=t, **kw)
+        np.testing.assert_allclose(pk, prev * (1 - 1e-4) - 1e-3 * g / (np.abs(g) + 1e-8), rtol=1e-11, atol=1e-14)
+
+
+def test_adamw_hand_example_and_zero_gradient():
+    # one scalar by hand: p=1, g=2, m=0.5, v=1, b1=0.5, b2=0.75, step 2, lr 0.1, wd 0.5, eps 0
+    p2, m2, v2 = orc.adamw_step(np.array([1.0]), np.array([2.0]), np.array([0.5]), np.array([1.0]), lr=0.1,
+                                beta1=0.5, beta2=0.75, eps=0.0, weight_decay=0.5, step=2)
+    # m' = 0.25 + 1 = 1.25, v' = 0.75 + 0.25*4 = 1.75, m_hat = 1.25/0.75, v_hat = 1.75/0.4375 = 4
+    assert m2[0] == 1.25 and v2[0] == 1.75
+    assert abs(p2[0] - (0.95 - 0.1 * (1.25 / 0.75) / 2.0)) < 1e-15
+    # zero gradient: only the moments decay and the weight decays
+    p3, m3, v3 = orc.adamw_step(np.array([3.0]), np.array([0.0]), np.array([0.0]), np.array([0.0]), lr=0.01,
+                                beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.2, step=5)
+    assert m3[0] == 0.0 and v3[0] == 0.0 and abs(p3[0] - 3.0 * (1 - 0.002)) < 1e-15
