@@ -363,6 +363,39 @@ def bench_injections_factored(args, torch, mu, wl):
                                                      ["ns_factored.hip", "common.cuh"])}}
 
 
+def bench_adamw(args, torch, mu, wl):
+    """AdamW over the Mamba-2-130M parameters outside the Muon groups (170
+    tensors, 38.9 M elements, bf16 gradients)."""
+    shapes = wl.mamba2_adamw_shapes()
+    P, G, M, V = wl.adamw_state(shapes)
+    Pd = [torch.from_numpy(p).cuda() for p in P]
+    Gd = [torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).cuda() for g in G]
+    Md = [torch.from_numpy(m).cuda() for m in M]
+    Vd = [torch.from_numpy(v).cuda() for v in V]
+    kw = dict(lr=3e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    opt = mu.AdamwTensors(Pd, Gd, Md, Vd)  # argument arrays marshalled once
+    for t in range(args.warmup):
+        opt.step(step=t + 1, **kw)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k, (a, b) in enumerate(ev):
+        a.record()
+        opt.step(step=args.warmup + k + 1, **kw)
+        b.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nel = sum(p.numel() for p in Pd)
+    gbs = nel * 26 / (kms * 1e-3) / 1e9
+    return {"metric": "AdamW companion steps/s (Mamba-2-130M non-Muon parameters)", "value": round(1e3 / ms, 2),
+            "unit": "steps/s", "ms_per_step": round(ms, 4), "dtype": "f32",
+            "config": {"workload": f"adamw: {len(Pd)} tensors, {nel} elements, bf16 grads"},
+            "roofline": {"bound": "hbm", "kernel": "adamw_kernel", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_element": 26,
+                         "traffic": None}}
+
+
 def bench_group(args, torch, mu, wl, which):
     w = wl.config2() if which == "out_proj" else wl.config3() if which == "in_proj" else wl.config1()
     groups = []
@@ -406,7 +439,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_step",
-                    choices=["full_step", "out_proj", "in_proj", "injections", "injections_factored", "single"])
+                    choices=["full_step", "out_proj", "in_proj", "injections", "injections_factored", "adamw",
+                             "single"])
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
     ap.add_argument("--batch", type=int, default=393216, help="injections batch")
@@ -442,6 +476,8 @@ def main():
         res = bench_injections(args, torch, mu, wl)
     elif args.workload == "injections_factored":
         res = bench_injections_factored(args, torch, mu, wl)
+    elif args.workload == "adamw":
+        res = bench_adamw(args, torch, mu, wl)
     else:
         res = bench_group(args, torch, mu, wl, args.workload)
     out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,

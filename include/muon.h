@@ -230,6 +230,24 @@ int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long 
 int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int r, long long batch,
                      const muon_ns_cfg* cfg, float* C_out, void* O_out, void* stream);
 
+/* AdamW for the parameters outside the Muon groups ("Muon Meets Mamba":
+ * AdamW is the baseline optimizer and keeps the non-projection parameters),
+ * with decoupled weight decay and bias-corrected moments; for each tensor i
+ * and element, with t = step (from 1):
+ *   m = beta1 m + (1 - beta1) g,   v = beta2 v + (1 - beta2) g^2
+ *   p = p (1 - lr weight_decay) - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ *   params, exp_avg, exp_avg_sq  host arrays of ntensors device pointers to
+ *                                float32 (p, m, v updated in place)
+ *   grads                         host array of device pointers (grad_dtype)
+ *   numel                         host array of element counts (0: skipped)
+ * Tensors are contiguous; 16-byte aligned tensors take vectorised loads.
+ * 0 <= beta < 1, eps >= 0, step >= 1 (MUON_EINVAL otherwise); a tensor of
+ * 2^31 or more elements returns MUON_EUNSUPPORTED.  One launch per 80 tensors;
+ * no workspace. */
+int muon_adamw(int ntensors, float* const* params, const void* const* grads, float* const* exp_avg,
+               float* const* exp_avg_sq, const long long* numel, int grad_dtype, float lr, float beta1,
+               float beta2, float eps, float weight_decay, long long step, void* stream);
+
 /* Human-readable name of a muon_status. */
 const char* muon_status_string(int status);
 

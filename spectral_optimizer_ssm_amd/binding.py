@@ -48,8 +48,8 @@ class GroupC(ctypes.Structure):
 
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
-           "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_ns_factored", "muon_status_string",
-           "muon_version")
+           "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
+           "muon_status_string", "muon_version")
 
 
 def lib():
@@ -81,6 +81,9 @@ def lib():
     L.muon_ns_factored.argtypes = [vp, vp, i, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg),
                                    ctypes.POINTER(f), vp, vp]
     L.muon_ns_factored.restype = i
+    L.muon_adamw.argtypes = [i, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                             ctypes.POINTER(ctypes.c_longlong), i, f, f, f, f, f, ctypes.c_longlong, vp]
+    L.muon_adamw.restype = i
     L.muon_status_string.argtypes = [i]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_version.argtypes = []
@@ -325,3 +328,40 @@ def muon_ns_factored(V, K, C=None, O=None, steps=1, coeffs=(1.5, -0.5), eps=1e-7
                             ctypes.c_void_p(O.data_ptr()) if O is not None else None, _stream_handle(stream))
     _check(rc, "muon_ns_factored")
     return C
+
+
+class AdamwTensors:
+    """Marshalled argument arrays of muon_adamw for fixed lists of tensors
+    (build once, call every step; the tensors must stay alive)."""
+
+    def __init__(self, params, grads, exp_avg, exp_avg_sq):
+        n = len(params)
+        if not (len(grads) == len(exp_avg) == len(exp_avg_sq) == n):
+            raise ValueError("params, grads, exp_avg, exp_avg_sq must have the same length")
+        self.n = n
+        self.gd = _dtype_code(grads[0]) if n else MUON_F32
+        for p, g, m, v in zip(params, grads, exp_avg, exp_avg_sq):
+            if not all(t.is_contiguous() for t in (p, g, m, v)) or \
+                    not (p.numel() == g.numel() == m.numel() == v.numel()):
+                raise ValueError("every tensor must be contiguous, with matching sizes")
+            if _dtype_code(g) != self.gd:
+                raise ValueError("all gradients must have one dtype")
+        cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))  # noqa: E731
+        self._keep = [params, grads, exp_avg, exp_avg_sq]
+        self._arrays = [_ptrs(params), _ptrs(grads), _ptrs(exp_avg), _ptrs(exp_avg_sq)]
+        self.ptrs = [cast(a) for a in self._arrays]
+        self.numel = (ctypes.c_longlong * max(1, n))(*[p.numel() for p in params])
+
+    def step(self, lr, step, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, stream=None):
+        if self.n == 0:
+            return
+        rc = lib().muon_adamw(self.n, *self.ptrs, self.numel, self.gd, float(lr), float(beta1), float(beta2),
+                              float(eps), float(weight_decay), int(step), _stream_handle(stream))
+        _check(rc, "muon_adamw")
+
+
+def muon_adamw(params, grads, exp_avg, exp_avg_sq, lr, step, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+               stream=None):
+    """AdamW over lists of contiguous float32 tensors (params, exp_avg,
+    exp_avg_sq updated in place); grads float32 or bf16 (one dtype)."""
+    AdamwTensors(params, grads, exp_avg, exp_avg_sq).step(lr, step, beta1, beta2, eps, weight_decay, stream)

@@ -190,4 +190,25 @@ struct FactLaunch {
 int factored_lds_per_wave(int m_pad, int n_pad, bool dense);
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st);
 
+// AdamW over a list of float32 tensors (one launch: up to kAdamwMax tensors).
+constexpr int kAdamwMax = 80;      // 40 bytes each: the table fits the kernel arguments
+constexpr int kAdamwBlock = 4096;  // elements per workgroup
+struct AdamwTensor {
+  float* p;
+  float* m;
+  float* v;
+  const void* g;       // float32 or bf16
+  int n;               // elements (< 2^31)
+  int block0;          // first workgroup of this tensor
+};
+struct AdamwLaunch {
+  AdamwTensor t[kAdamwMax];
+  int nt;
+  float beta1, beta2, one_m_b1, one_m_b2, eps;
+  float decay;         // 1 - lr * weight_decay
+  float lr_bc;         // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+};
+hipError_t launch_adamw(const AdamwLaunch& A, bool grad_bf16, int blocks, hipStream_t st);
+
 }  // namespace muon

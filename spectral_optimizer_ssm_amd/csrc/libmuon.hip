@@ -732,6 +732,60 @@ int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int b
   return run_all(runs, C, cfg->eps, static_cast<char*>(workspace), nullptr, static_cast<hipStream_t>(stream), E);
 }
 
+int muon_adamw(int ntensors, float* const* params, const void* const* grads, float* const* exp_avg,
+               float* const* exp_avg_sq, const long long* numel, int grad_dtype, float lr, float beta1, float beta2,
+               float eps, float weight_decay, long long step, void* stream) {
+  if (ntensors < 0) return MUON_EINVAL;
+  if (ntensors == 0) return MUON_OK;
+  if (params == nullptr || grads == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || numel == nullptr)
+    return MUON_EINVAL;
+  if (grad_dtype != MUON_F32 && grad_dtype != MUON_BF16) return MUON_EINVAL;
+  if (!std::isfinite(lr) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps >= 0.0f) ||
+      !std::isfinite(eps) || !std::isfinite(weight_decay) || step < 1)
+    return MUON_EINVAL;
+  for (int i = 0; i < ntensors; ++i) {
+    if (numel[i] < 0) return MUON_EINVAL;
+    if (numel[i] >= (1LL << 31)) return MUON_EUNSUPPORTED;
+    if (numel[i] == 0) continue;
+    if (params[i] == nullptr || grads[i] == nullptr || exp_avg[i] == nullptr || exp_avg_sq[i] == nullptr)
+      return MUON_EINVAL;
+    if (!aligned_to(params[i], 4) || !aligned_to(exp_avg[i], 4) || !aligned_to(exp_avg_sq[i], 4) ||
+        !aligned_to(grads[i], dtype_size(grad_dtype)))
+      return MUON_EINVAL;
+  }
+  AdamwLaunch A{};
+  const double bc1 = 1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step));
+  const double bc2 = 1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step));
+  A.beta1 = beta1; A.beta2 = beta2;
+  A.one_m_b1 = 1.0f - beta1; A.one_m_b2 = 1.0f - beta2;
+  A.eps = eps;
+  A.decay = 1.0f - lr * weight_decay;
+  A.lr_bc = static_cast<float>(lr / bc1);
+  A.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  long long blocks = 0;
+  auto flush = [&]() {
+    const hipError_t e = launch_adamw(A, grad_dtype == MUON_BF16, static_cast<int>(blocks), st);
+    A.nt = 0;
+    blocks = 0;
+    return e == hipSuccess;
+  };
+  for (int i = 0; i < ntensors; ++i) {
+    if (numel[i] == 0) continue;
+    const long long nb = (numel[i] + kAdamwBlock - 1) / kAdamwBlock;
+    if (A.nt == kAdamwMax || blocks + nb > (1LL << 30)) {  // block indices stay in int
+      if (!flush()) return MUON_EHIP;
+    }
+    AdamwTensor& T = A.t[A.nt++];
+    T.p = params[i]; T.m = exp_avg[i]; T.v = exp_avg_sq[i]; T.g = grads[i];
+    T.n = static_cast<int>(numel[i]);
+    T.block0 = static_cast<int>(blocks);
+    blocks += nb;
+  }
+  if (A.nt > 0 && !flush()) return MUON_EHIP;
+  return MUON_OK;
+}
+
 int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int r, long long batch,
                      const muon_ns_cfg* cfg, float* C_out, void* O_out, void* stream) {
   NsCoefs C;

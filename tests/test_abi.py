@@ -229,3 +229,30 @@ def test_cap_validation_and_phases(mu):
     base, _ = _group(mu, 128, 256, 2)
     a0 = (mu.binding.GroupC * 1)(base)
     assert L.muon_step_workspace_size(arr, 1, ctypes.byref(cfg)) > L.muon_step_workspace_size(a0, 1, ctypes.byref(cfg))
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("ok_empty", 0), ("beta1_one", -1), ("step0", -1), ("null_p", -1), ("misaligned", -1), ("bad_dtype", -1),
+    ("neg_numel", -1), ("zero_numel_null_ok", 0), ("neg_eps", -1),
+])
+def test_adamw_validation(mu, case, expect):
+    L = mu.lib()
+    n = 0 if case == "ok_empty" else 2
+    ptr = lambda base: (ctypes.c_void_p * 2)(base, base + 0x10000)  # noqa: E731
+    P, G, M, V = ptr(0x1000000), ptr(0x2000000), ptr(0x3000000), ptr(0x4000000)
+    N = (ctypes.c_longlong * 2)(100, 200)
+    if case == "null_p":
+        P[1] = None
+    if case == "misaligned":
+        M[0] = 0x3000002
+    if case == "neg_numel":
+        N[1] = -1
+    if case == "zero_numel_null_ok":
+        N[1] = 0
+        P[1] = None
+        # then the remaining tensor is launched: keep it off the device by making it empty too
+        N[0] = 0
+    rc = L.muon_adamw(n, P, G, M, V, N, 7 if case == "bad_dtype" else mu.MUON_BF16, 1e-3,
+                      1.0 if case == "beta1_one" else 0.9, 0.95, -1.0 if case == "neg_eps" else 1e-8, 0.1,
+                      0 if case == "step0" else 1, None)
+    assert rc == expect

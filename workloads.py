@@ -255,3 +255,40 @@ def injections(batch: int = INJ_BATCH, device="cpu", seed: int = 4,
     if return_factors:
         return out, torch.cat(Vs), torch.cat(Ks)
     return out
+
+
+# ----------------------------------------------------------------------------
+# The Mamba-2-130M parameters outside the Muon groups (AdamW companion)
+# ----------------------------------------------------------------------------
+def mamba2_adamw_shapes(layers: int = 24, d_model: int = 768, d_inner: int = 1536, d_state: int = 128,
+                        heads: int = 24, d_conv: int = 4, vocab: int = 50280):
+    """(name, shape) of the Mamba-2-130M parameters that are not in_proj or
+    out_proj: tied embedding, per layer the pre-norm, the depthwise conv1d over
+    x, B, C (weight and bias), dt_bias, A_log, D and the gated-norm weight, and
+    the final norm."""
+    conv_dim = d_inner + 2 * d_state
+    out = [("embedding", (vocab, d_model))]
+    for i in range(layers):
+        out += [(f"layers.{i}.norm", (d_model,)), (f"layers.{i}.conv1d.weight", (conv_dim, 1, d_conv)),
+                (f"layers.{i}.conv1d.bias", (conv_dim,)), (f"layers.{i}.dt_bias", (heads,)),
+                (f"layers.{i}.A_log", (heads,)), (f"layers.{i}.D", (heads,)),
+                (f"layers.{i}.mixer_norm", (d_inner,))]
+    out.append(("norm_f", (d_model,)))
+    return out
+
+
+def adamw_state(shapes, seed: int = 6, grad_dtype: str = "bf16", step: int = 3):
+    """Seeded float32 parameters (0.02 N(0,1)), gradients (N(0,1), bf16 bits
+    or float32) and moments consistent with `step - 1` earlier steps
+    (m ~ 0.1 N(0,1), v ~ 0.01 chi^2_1) for every shape."""
+    ss = np.random.SeedSequence(seed).spawn(len(shapes))
+    P, G, M, V = [], [], [], []
+    for (name, shape), child in zip(shapes, ss):
+        rng = np.random.default_rng(child)
+        n = int(np.prod(shape))
+        P.append((0.02 * rng.standard_normal(n)).astype(np.float32))
+        g = rng.standard_normal(n).astype(np.float32)
+        G.append(f32_to_bf16_bits(g) if grad_dtype == "bf16" else g)
+        M.append((0.1 * rng.standard_normal(n)).astype(np.float32))
+        V.append((0.01 * rng.standard_normal(n) ** 2).astype(np.float32))
+    return P, G, M, V
