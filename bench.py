@@ -239,7 +239,7 @@ def bench_full_step(args, torch, mu, wl):
     # dominant kernel: the one with the most GPU time per step
     dom = max(ns_kinds + ["momentum", "apply"], key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
-    names = {"gram": "gram_bf16_kernel", "combine": "combine_bf16_kernel", "symprod": "symprod_bf16_kernel",
+    names = {"gram": "symprod_bf16_kernel", "combine": "combine_bf16_kernel", "symprod": "symprod_bf16_kernel",
              "momentum": "momentum_*_kernel", "apply": "apply_*_kernel"}
     if dom in ("momentum", "apply"):
         roofline = {"bound": "hbm", "kernel": names[dom], "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
@@ -422,7 +422,6 @@ ELEMENTWISE = ["elementwise.hip", "common.cuh"]
 GEMM = ["gemm_bf16.hip", "common.cuh"]
 COUNTED_KERNELS = {
     "full_step": {"combine_bf16_kernel": ("combine_bf16_kernel", GEMM),
-                  "gram_bf16_kernel": ("gram_bf16_kernel", GEMM),
                   "symprod_bf16_kernel": ("symprod_bf16_kernel", GEMM),
                   "momentum_wide_kernel": ("momentum_wide_kernel", ELEMENTWISE),
                   "momentum_tall_kernel": ("momentum_tall_kernel", ELEMENTWISE),

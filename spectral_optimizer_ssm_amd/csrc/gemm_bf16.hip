@@ -5,40 +5,42 @@
 // Newton-Schulz iteration; "MuonSSM" (section on convergence and complexity)
 // notes that its matrix products are the method's constant-factor cost.  One
 // cubic step on the oriented iterate X (s x l, s <= l) is
-//     X' = a X + b (X X^T) X = A' X,   A' = a I + b X X^T   (symmetric)
-// computed as two launches:
-//   gram    : A' = alpha I + beta X X^T, only tiles on or above the diagonal,
-//             each stored in place and mirrored;
-//   combine : Y  = A' X, a plain product.
+//     X' = a X + b (X X^T) X = A' X,   A' = a I + b X X^T   (symmetric).
+// Two kernels:
+//   symprod_bf16_kernel : products L R^T whose result is symmetric, so only
+//       tiles on or above the diagonal are computed, each stored in place and
+//       mirrored, with O1 = a1 I + b1 L R^T and an optional affine second
+//       output O2 = a2 I + b2 O1.  It serves the Gram X X^T (L = R = X,
+//       contraction over the long side) and the products of the accumulated
+//       schedule (L, R polynomials in one Gram matrix, which commute).
+//   combine_bf16_kernel : Y = A' X, a plain product.
 // On the first step X holds the unnormalised U and the Frobenius
-// normalisation is folded in: alpha = a / (nu + eps), beta = b / (nu + eps)^3,
+// normalisation is folded into the coefficients as powers of 1/(nu + eps),
 // with nu re-reduced from the momentum pass's per-block partial sums.
 //
-// Layout: X [count][s_pad][ld], A' [count][s_pad][s_pad], bf16 row-major,
-// s_pad % 256 == 0, ld % 256 == 0, zero padding (stays zero: padded rows and
-// columns of A' are zero).  The Gram's contraction stops at kdim, the first
-// multiple of 64 >= l.
+// Layout: X [count][s_pad][ld], s x s matrices [count][s_pad][s_pad], bf16
+// row-major, s_pad % 256 == 0, ld % 256 == 0, zero padding (stays zero:
+// padded rows of X are zero).  The Gram's contraction stops at kdim, the
+// first multiple of 64 >= l.
 //
-// Tiling: 256 x 256 workgroup tile, eight waves (two per SIMD) of 128 x 64
-// (Gram) or 64 x 128 (combine) made of 32 x 32 MFMA blocks.  The contraction
-// runs in stages of BK = 32 through NSTAGE = 4 LDS buffers of 32 KB: the
-// fill of stage kt + 3 is issued while stage kt is multiplied, so three
-// stages of loads (96 KB per CU) are in flight and an L2 miss to MALL or HBM
-// does not stall the matrix pipes.  Fills use buffer_load ... lds (each
-// lane's 16 bytes land at base + 16 * lane; the per-lane source offset
-// implements the swizzle).  Stage hand-over is an explicit
-// s_waitcnt vmcnt(<loads of younger stages>) + s_barrier, because
-// __syncthreads() would drain every outstanding fill.
-//  * K-contiguous operands (rows of X in the Gram, rows of A' in the combine)
-//    sit as [256 rows][32 K] (64-byte rows, 16-byte chunks XOR-swizzled by
-//    (row >> 2) & 3) and are read as ds_read_b128 fragments.
+// Combine tiling: 256 x 256 workgroup tile, eight waves (two per SIMD) of
+// 64 x 128 made of 32 x 32 MFMA blocks.  The contraction runs in stages of
+// BK = 32 through NSTAGE = 4 LDS buffers of 32 KB: the fill of stage kt + 3
+// is issued while stage kt is multiplied, so three stages of loads are in
+// flight and an L2 miss to MALL or HBM does not stall the matrix pipes.
+// Fills use buffer_load ... lds (each lane's 16 bytes land at base + 16 *
+// lane; the per-lane source offset implements the swizzle).  Stage hand-over
+// is an explicit s_waitcnt vmcnt(<loads of younger stages>) + s_barrier,
+// because __syncthreads() would drain every outstanding fill.
+//  * K-contiguous operands (rows of A' in the combine, both operands of the
+//    symmetric products) sit as [rows][32 K] (64-byte rows, 16-byte chunks
+//    XOR-swizzled by (row >> 2) & 3) and are read as ds_read_b128 fragments.
 //  * The combine's X operand is contracted over X's row index: it sits
 //    row-major as [32 rows j][256 columns k] (chunks swizzled by 4*(j&3)) and
 //    its fragments come from ds_read_b64_tr_b16: 16 lanes each address 4
 //    elements of a 4 x 16 block and every lane receives one column's 4
 //    consecutive rows, exactly the MFMA operand layout.
-// The MFMA's M side is X's column index in the combine, so each lane ends up
-// with 4 consecutive columns of one output row (8-byte stores).
+// Outputs leave through LDS as whole rows.
 //
 // Work distribution: one launch covers every shape group of the step
 // (segments).  Workgroups are dealt to the 8 XCDs round-robin by hardware;
@@ -392,112 +394,6 @@ __device__ __forceinline__ void upper_tile(int t, int nt, int& bi, int& bj) {
   bj = bi + t;
 }
 
-// ---- Gram: A' = alpha I + beta X X^T ------------------------------------------
-__global__ void __launch_bounds__(NTHR) gram_bf16_kernel(GemmArgs G) {
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) char lds2[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) char lds3[2 * OPB];
-  __shared__ float red[NWAVE];
-  int si, tile;
-  if (!find_tile(G, si, tile)) return;
-  const GemmSeg& S = G.seg[si];
-  const int z = tile / S.tiles_per_mat;
-  int bi, bj;
-  upper_tile(tile % S.tiles_per_mat, S.s_pad / T, bi, bj);
-  const bool diag = bi == bj;
-  const bf16_t* X = S.X + z * S.xstride;
-  const float inv = seg_inv(S, z, red);
-  const float ia = ipow(inv, S.pa), ib = ipow(inv, S.pb);
-
-  // waves: 2 along M x 4 along N, each 128 x 64 (4 x 2 MFMA blocks)
-  constexpr int GM = 128, GN = 64, FM = GM / 32, FN = GN / 32;
-  const int lane = threadIdx.x & 63, wid = wave_id();
-  const int wm = wid >> 2, wn = wid & 3;
-  Acc<FM, FN> acc;
-  acc.zero();
-  const int ld_bytes = S.ld * 2;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(X, static_cast<long long>(S.s_pad) * ld_bytes);
-  const int voff = row_voff(ld_bytes);
-  const int offA = bi * T * ld_bytes, offB = bj * T * ld_bytes;
-  const int nk = S.kdim / BK;
-  int roff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) roff[ks] = rfrag_off(ks, lane);
-  const Bufs bufs{{lds0, lds1, lds2, lds3}};
-
-  auto mma = [&](const char* buf, bool dg) {
-    const char* ta = buf + wm * GM * 64;
-    const char* tb = (dg ? buf : buf + OPB) + wn * GN * 64;
-    stage_mma<FM, FN>(acc, [&](int ks, int i) { return frag_at(ta + roff[ks] + i * 32 * 64); },
-                      [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); });
-  };
-  if (diag) {  // both operands are the same rows: one fill per stage
-    pipeline<2>(bufs, nk, [&](char* buf, int kt) { load_rows(buf, rsrc, voff, ld_bytes, offA + kt * BK * 2); },
-                [&](const char* buf) { mma(buf, true); });
-  } else {
-    pipeline<4>(bufs, nk,
-                [&](char* buf, int kt) {
-                  load_rows(buf, rsrc, voff, ld_bytes, offA + kt * BK * 2);
-                  load_rows(buf + OPB, rsrc, voff, ld_bytes, offB + kt * BK * 2);
-                },
-                [&](const char* buf) { mma(buf, false); });
-  }
-
-  // epilogue: D[m][n] = (X X^T)[bi*T + m][bj*T + n]; lane: 4 consecutive m at one n.
-  // Per output, pass 1 stages the mirrored tile (rows n, contiguous m) and
-  // writes it to A[bj*T + n][bi*T + m]; pass 2 (off the diagonal) stages the
-  // tile itself.
-  stage_sync<0>();
-  const int lane_e = opaque(lane);
-  const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;  // buffers and rows below are uniform per wave
-  const float alpha = S.a * ia, beta = S.b * ib;
-  bf16_t* A = S.A + z * S.astride;
-  bf16_t* A2 = S.A2 == nullptr ? nullptr : S.A2 + z * S.astride;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = wn * GN + j * 32 + col;  // slab wn, row j*32 + col
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = wm * GM + i * 32 + q * 8 + rq;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = beta * acc.c[i][j][4 * q + r] + ((diag && m + r == n) ? alpha : 0.0f);
-        const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2_t*>(bufs[wn] + slab_off(j * 32 + col, m)) = w;
-      }
-    }
-  }
-  __syncthreads();
-  {
-    const long long o = static_cast<long long>(bj) * T * S.s_pad + bi * T;
-    slabs_to_global(bufs, A + o, S.s_pad, A2 == nullptr ? nullptr : A2 + o, S.a2, S.b2, diag);
-  }
-  if (diag) return;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = wn * GN + j * 32 + col;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = wm * GM + i * 32 + q * 8 + rq;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bf16_t b = f32_to_bf16(beta * acc.c[i][j][4 * q + r]);
-          *reinterpret_cast<bf16_t*>(bufs[wm * 2 + (i >> 1)] + slab_off((i & 1) * 32 + q * 8 + rq + r, n)) = b;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const long long o = static_cast<long long>(bi) * T * S.s_pad + bj * T;
-  slabs_to_global(bufs, A + o, S.s_pad, A2 == nullptr ? nullptr : A2 + o, S.a2, S.b2, false);
-}
-
 // ---- combine: Y = A' X --------------------------------------------------------
 // D[k][i] = sum_j X[j][k] A'[i][j] = (A' X)[i][k]
 __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
@@ -656,19 +552,20 @@ symprod_bf16_kernel(SymArgs G) {
     upper_tile(tile % S.tiles_per_mat, S.s_pad / TT, bi, bj);
     const bool diag = bi == bj;
     const bool single = diag && S.L == S.R;  // both operands are the same rows
-    const long long zoff = z * S.stride;
+    const long long zoff = z * S.stride;                 // outputs
+    const long long zin = z * S.in_stride;               // operands
     const float inv = seg_inv(S, z, red);
     const float ia = ipow(inv, S.pa), ib = ipow(inv, S.pb);
 
     Acc<FM, FN> acc;
     acc.zero();
-    const int sp_bytes = S.s_pad * 2;
+    const int sp_bytes = S.ld * 2;  // operand row stride
     const long long mbytes = static_cast<long long>(S.s_pad) * sp_bytes;
-    const __amdgpu_buffer_rsrc_t lr = make_rsrc(S.L + zoff, mbytes);
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(S.R + zoff, mbytes);
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(S.L + zin, mbytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(S.R + zin, mbytes);
     const int voff = row_voff(sp_bytes);
     const int offL = bi * TT * sp_bytes, offR = bj * TT * sp_bytes;
-    const int nk = S.s_pad / BK;
+    const int nk = S.kdim / BK;
     auto fill_rows = [&](char* op, __amdgpu_buffer_rsrc_t rs, int soff0) {
 #pragma unroll
       for (int b = 0; b < BPW; ++b) {
@@ -792,10 +689,6 @@ int grid_for(const Args& G) {
 
 }  // namespace
 
-int gram_tiles_per_matrix(int s_pad) {
-  const int nt = s_pad / T;
-  return nt * (nt + 1) / 2;
-}
 int combine_tiles_per_matrix(int s_pad, int ld) { return (s_pad / T) * (ld / T); }
 int symprod_tile(int s_pad) { return sym_tile(s_pad); }
 int symprod_tiles_per_matrix(int s_pad) {
@@ -814,13 +707,6 @@ hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st) {
   hipError_t e = part[1].nseg ? launch_symprod_tt<192>(part[1], st) : hipSuccess;
   if (e == hipSuccess && part[0].nseg) e = launch_symprod_tt<128>(part[0], st);
   return e;
-}
-
-hipError_t launch_gram_bf16(const GemmArgs& G, hipStream_t st) {
-  const int grid = grid_for(G);
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(gram_bf16_kernel, dim3(grid), dim3(NTHR), 0, st, G);
-  return hipGetLastError();
 }
 
 hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st) {

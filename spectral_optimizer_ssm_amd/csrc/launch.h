@@ -117,22 +117,23 @@ struct GemmArgs {
   GemmSeg seg[kMaxSeg];
   int nseg;
 };
-int gram_tiles_per_matrix(int s_pad);
 int combine_tiles_per_matrix(int s_pad, int ld);
-hipError_t launch_gram_bf16(const GemmArgs& G, hipStream_t st);
 hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st);
 
-// Products of two symmetric, commuting s_pad x s_pad bf16 matrices (both
-// polynomials in the same Gram matrix), whose product is symmetric too:
+// Products L R^T whose result is symmetric: the Gram X X^T (L = R = X, the
+// iterate), and products of two symmetric, commuting s_pad x s_pad bf16
+// matrices (polynomials in the same Gram matrix, where R^T = R):
 // O1 = a1 inv^pa I + b1 inv^pb L R and (optional) O2 = a2 I + b2 O1 from
 // O1's rounded values.  Only tiles on or above the diagonal are computed;
 // each is stored in place and mirrored.
 struct SymSeg {
-  const bf16_t* L;     // left factor   [count][s_pad][s_pad]
+  const bf16_t* L;     // left factor   [count][s_pad][ld], contraction over kdim columns
   const bf16_t* R;     // right factor  (may equal L)
-  bf16_t* O1;
+  bf16_t* O1;          // [count][s_pad][s_pad]
   bf16_t* O2;          // null: none
-  long long stride;    // elements between consecutive matrices (all four)
+  long long stride;    // elements between consecutive outputs
+  long long in_stride; // elements between consecutive operands
+  int ld, kdim;        // operand row stride; contraction length (multiple of 32)
   int s_pad, count, tiles_per_mat;
   const float* partials;
   int P;

@@ -101,7 +101,7 @@ bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
   if (g.engine != kTiledBf16 || C.steps < 2 || C.schedule == MUON_NS_ITERATE) return false;
   if (C.schedule == MUON_NS_ACCUMULATE) return true;
   const double t = kTileS, t2 = symprod_tile(g.s_pad);
-  const double gram = gram_tiles_per_matrix(g.s_pad) * t * t * g.kdim;
+  const double gram = symprod_tiles_per_matrix(g.s_pad) * t2 * t2 * g.kdim;
   const double comb = combine_tiles_per_matrix(g.s_pad, g.ld) * t * t * g.s_pad;
   const double prod = symprod_tiles_per_matrix(g.s_pad) * t2 * t2 * g.s_pad;
   const double q = C.quintic ? 1.0 : 0.0;
@@ -248,6 +248,26 @@ bool launch_segments(const std::vector<Seg>& segs, Launch launch, hipStream_t st
   return true;
 }
 
+// The Gram X X^T runs on the symmetric-product kernel (L = R = the iterate):
+// same outputs, coefficients and normalisation powers as the Gram segment.
+SymSeg gram_as_sym(const GemmSeg& G) {
+  SymSeg S{};
+  S.L = G.X; S.R = G.X;
+  S.O1 = G.A; S.O2 = G.A2;
+  S.stride = G.astride; S.in_stride = G.xstride;
+  S.ld = G.ld; S.kdim = G.kdim;
+  S.s_pad = G.s_pad; S.count = G.count; S.tiles_per_mat = symprod_tiles_per_matrix(G.s_pad);
+  S.partials = G.partials; S.P = G.P; S.eps = G.eps;
+  S.a1 = G.a; S.b1 = G.b; S.a2 = G.a2; S.b2 = G.b2;
+  S.pa = G.pa; S.pb = G.pb;
+  return S;
+}
+std::vector<SymSeg> grams_as_sym(const std::vector<GemmSeg>& gs) {
+  std::vector<SymSeg> out;
+  for (const GemmSeg& G : gs) out.push_back(gram_as_sym(G));
+  return out;
+}
+
 int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, float* norms_out, hipStream_t st,
             EventRec& E) {
   if (!E.mark(st, 0)) return MUON_EHIP;
@@ -315,13 +335,15 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     S.xstride = static_cast<long long>(p.s_pad) * p.ld;
     S.astride = static_cast<long long>(p.s_pad) * p.s_pad;
     S.s_pad = p.s_pad; S.ld = p.ld; S.kdim = p.kdim; S.count = p.count;
-    S.tiles_per_mat = gram ? gram_tiles_per_matrix(p.s_pad) : combine_tiles_per_matrix(p.s_pad, p.ld);
+    S.tiles_per_mat = gram ? symprod_tiles_per_matrix(p.s_pad) : combine_tiles_per_matrix(p.s_pad, p.ld);
     S.P = p.P; S.eps = eps;
     return S;
   };
   auto sym_seg = [&](const GroupPlan& p) {
     SymSeg S{};
     S.stride = static_cast<long long>(p.s_pad) * p.s_pad;
+    S.in_stride = S.stride;
+    S.ld = p.s_pad; S.kdim = p.s_pad;
     S.s_pad = p.s_pad; S.count = p.count; S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);
     S.P = p.P; S.eps = eps;
     S.b1 = 1.0f;
@@ -368,7 +390,8 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
         S.A = sq_of(p, ws, C.quintic ? kSqB0 : kSqA0);
         cs.push_back(S);
       }
-      if (!launch_segments<GemmArgs>(gs, launch_gram_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_GRAM))
+      if (!launch_segments<SymArgs>(grams_as_sym(gs), launch_symprod_bf16, st, E.live()) ||
+          !E.mark(st, MUON_PHASE_GRAM))
         return MUON_EHIP;
       if (C.quintic &&
           (!launch_segments<SymArgs>(ps, launch_symprod_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_SYMPROD)))
@@ -405,7 +428,8 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       }
       gs.push_back(S);
     }
-    if (!launch_segments<GemmArgs>(gs, launch_gram_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_GRAM))
+    if (!launch_segments<SymArgs>(grams_as_sym(gs), launch_symprod_bf16, st, E.live()) ||
+        !E.mark(st, MUON_PHASE_GRAM))
       return MUON_EHIP;
     for (int k = 0; k < n; ++k) {
       if (C.quintic) {  // B_k = a_k I + A_k H_k
