@@ -691,8 +691,8 @@ int grid_for(const Args& G) {
 
 int combine_tiles_per_matrix(int s_pad, int ld) { return (s_pad / T) * (ld / T); }
 int symprod_tile(int s_pad) { return sym_tile(s_pad); }
-int symprod_tiles_per_matrix(int s_pad) {
-  const int nt = s_pad / sym_tile(s_pad);
+int symprod_tiles_per_matrix(int s_pad, int tile) {
+  const int nt = s_pad / (tile ? tile : sym_tile(s_pad));
   return nt * (nt + 1) / 2;
 }
 
@@ -701,7 +701,8 @@ int symprod_tiles_per_matrix(int s_pad) {
 hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st) {
   SymArgs part[2] = {};
   for (int s = 0; s < G.nseg; ++s) {
-    SymArgs& P = part[sym_tile(G.seg[s].s_pad) == 192 ? 1 : 0];
+    const int tt = G.seg[s].tile ? G.seg[s].tile : sym_tile(G.seg[s].s_pad);
+    SymArgs& P = part[tt == 192 ? 1 : 0];
     P.seg[P.nseg++] = G.seg[s];
   }
   hipError_t e = part[1].nseg ? launch_symprod_tt<192>(part[1], st) : hipSuccess;

@@ -142,13 +142,14 @@ struct SymSeg {
   int pa, pb;
   int zip_next;        // 1: the next segment has the same count and s_pad and
                        // runs matrix by matrix together with this one
+  int tile;            // 0: symprod_tile(s_pad); else 128 or 192 (dividing s_pad)
 };
 struct SymArgs {
   SymSeg seg[kMaxSeg];
   int nseg;
 };
 int symprod_tile(int s_pad);  // 192 when it divides s_pad, else 128
-int symprod_tiles_per_matrix(int s_pad);
+int symprod_tiles_per_matrix(int s_pad, int tile = 0);
 hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st);
 
 // float32 path (tile multiples: s_pad % 64 == 0, ld % 64 == 0).
