@@ -9,9 +9,10 @@ beta 0.95 Nesterov, lr 0.02, 5 cubic Newton-Schulz steps.  Inputs are seeded
 and synthetic (workloads.py) and resident in HBM before timing starts.
 
 Prints one JSON line: steps/s over exactly K timed steps (wall clock between
-two device synchronisations), per-kernel durations from HIP events recorded on
-the library's stream inside those same steps, the roofline of the dominant
-kernel, and the fp64 oracle timed on a bounded sample on the host cores.
+two device synchronisations), per-kernel durations from HIP events recorded by
+muon_step_timed in K further steps (those run the phases one after another on
+one stream), the roofline of the dominant kernel, and the fp64 oracle timed on
+a bounded sample on the host cores.
 Other workloads (out_proj, in_proj, injections, single) are for exploration.
 """
 from __future__ import annotations
@@ -165,14 +166,23 @@ def bench_full_step(args, torch, mu, wl):
 
     for _ in range(args.warmup):
         mu.muon_step(groups, steps=steps_ns, workspace=ws)
-    evs = make_events(args.steps)
+    # the timed steps: plain muon_step (shape groups as two concurrent chains)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        mu.muon_step(groups, steps=steps_ns, workspace=ws, events=[e.cuda_event for e in evs[k]])
+        mu.muon_step(groups, steps=steps_ns, workspace=ws)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # per-kernel durations: the same steps again through muon_step_timed,
+    # which runs the phases one after another on one stream
+    evs = make_events(args.steps)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for k in range(args.steps):
+        mu.muon_step(groups, steps=steps_ns, workspace=ws, events=[e.cuda_event for e in evs[k]])
+    torch.cuda.synchronize()
+    ms_serial = (time.perf_counter() - t2) * 1e3 / args.steps
 
     # algorithmic work of each launch of the executed schedule (every large
     # group takes the same schedule here; per-group passes follow group order)
@@ -251,6 +261,7 @@ def bench_full_step(args, torch, mu, wl):
     result = {
         "metric": METRIC, "value": round(1e3 / ms_per_step, 3), "unit": "steps/s",
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_one_stream": round(ms_serial, 4),
         "ns_iters_per_s": round(steps_ns * 1e3 / ms_per_step, 2),
         "ns_tflops": round(ns_tflops, 2), "mfma_util": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
         "ns_iteration_equivalent_tflops": round(iter_flops_step / (ns_ms * 1e-3) / 1e12, 2),

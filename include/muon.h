@@ -38,12 +38,15 @@
  * bfloat16 data is passed as 16-bit storage (uint16 bits).
  *
  * Ownership and asynchrony.  The caller owns every buffer, including the
- * workspace; the library never allocates device memory and keeps no state
- * between calls.  All work is enqueued on `stream` (a hipStream_t; NULL is
- * the null stream) and the call returns without synchronising; a kernel fault
- * surfaces at the caller's next synchronisation.  Host pointer arrays are read
- * during the call only.  Two calls that share a workspace must be ordered on
- * one stream.
+ * workspace; the library never allocates device memory.  Its only state is,
+ * per device, one auxiliary stream and two events created on first use by
+ * muon_step (see muon_ns_cfg.streams).  All work is ordered on `stream` (a
+ * hipStream_t; NULL is the null stream): work placed on the auxiliary stream
+ * starts after everything enqueued on `stream` before the call and finishes
+ * before anything enqueued on `stream` after it.  Calls return without
+ * synchronising; a kernel fault surfaces at the caller's next
+ * synchronisation.  Host pointer arrays are read during the call only.  Two
+ * calls that share a workspace must be ordered on one stream.
  *
  * Errors.  Every entry point validates all arguments before enqueueing any
  * work and returns MUON_OK (0) or a negative muon_status; nothing has been
@@ -60,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 3
+#define MUON_VERSION 4
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -95,6 +98,11 @@ typedef enum { MUON_NS_AUTO = 0, MUON_NS_ITERATE = 1, MUON_NS_ACCUMULATE = 2 } m
  *   eps       added to ||U||_F before dividing (>= 0)
  *   precision MUON_BF16 or MUON_F32 (see Precision above)
  *   schedule  a muon_ns_schedule
+ *   streams   muon_step only: 0 runs independent shape groups as two chains,
+ *             on `stream` and on an auxiliary stream the library creates per
+ *             device on first use (joined back into `stream` before the call
+ *             returns); 1 uses `stream` alone.  muon_step_timed always uses
+ *             `stream` alone.
  * Quintic c != 0 runs on large bfloat16 matrices (the matrix-core path: one
  * more s x s product per step) and in muon_ns_factored; with float32
  * precision, on small (on-chip) matrices and in muon_ns_batched_small it
@@ -107,6 +115,7 @@ typedef struct {
   float eps;
   int precision;
   int schedule;
+  int streams;
 } muon_ns_cfg;
 
 /* One parameter group of `count` same-shape m x n matrices (the pages group

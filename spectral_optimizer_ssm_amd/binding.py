@@ -33,7 +33,8 @@ class MuonError(RuntimeError):
 class NsCfg(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int), ("ncoef", ctypes.c_int),
                 ("coeffs", ctypes.POINTER(ctypes.c_float)), ("per_step", ctypes.c_int),
-                ("eps", ctypes.c_float), ("precision", ctypes.c_int), ("schedule", ctypes.c_int)]
+                ("eps", ctypes.c_float), ("precision", ctypes.c_int), ("schedule", ctypes.c_int),
+                ("streams", ctypes.c_int)]
 
 
 class GroupC(ctypes.Structure):
@@ -124,13 +125,13 @@ def _stream_handle(stream=None) -> Optional[int]:
 
 
 def make_cfg(steps: int = 5, coeffs=(1.5, -0.5), eps: float = 1e-7, precision: int = MUON_BF16,
-             per_step: bool = False, schedule: int = MUON_NS_AUTO):
+             per_step: bool = False, schedule: int = MUON_NS_AUTO, streams: int = 0):
     """NsCfg plus the float array it points to (keep both alive)."""
     flat = [float(c) for row in coeffs for c in (row if isinstance(row, (tuple, list)) else (row,))]
     ncoef = len(coeffs[0]) if per_step else len(coeffs)
     arr = (ctypes.c_float * max(1, len(flat)))(*flat)
     cfg = NsCfg(int(steps), int(ncoef), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
-                int(bool(per_step)), float(eps), int(precision), int(schedule))
+                int(bool(per_step)), float(eps), int(precision), int(schedule), int(streams))
     return cfg, arr
 
 
@@ -231,7 +232,8 @@ def muon_step_phases(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), e
 
 
 def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7, precision=MUON_BF16,
-              per_step=False, workspace=None, norms_out=None, stream=None, events=None, schedule=MUON_NS_AUTO):
+              per_step=False, workspace=None, norms_out=None, stream=None, events=None, schedule=MUON_NS_AUTO,
+              streams=0):
     """One Muon step over every group (W and M updated in place).  Returns the
     workspace tensor so that callers can reuse it.  `events`: optional list of
     raw hipEvent_t handles (ints); when given, muon_step_timed records them at
@@ -239,7 +241,7 @@ def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7
     import torch
     L = lib()
     cg, keep = _marshal_groups(groups)
-    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule, streams)
     need = int(L.muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
     if need == 0:  # the size query has no status: ask the step itself, which validates first
         rc = L.muon_step(cg, len(groups), ctypes.byref(cfg), None, 0, None, None)

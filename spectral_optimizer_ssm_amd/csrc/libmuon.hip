@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/muon.h"
@@ -49,6 +50,7 @@ int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out, bool quintic = false) {
   if (cfg->precision != MUON_F32 && cfg->precision != MUON_BF16) return MUON_EINVAL;
   if (cfg->schedule != MUON_NS_AUTO && cfg->schedule != MUON_NS_ITERATE && cfg->schedule != MUON_NS_ACCUMULATE)
     return MUON_EINVAL;
+  if (cfg->streams != 0 && cfg->streams != 1) return MUON_EINVAL;
   if (cfg->steps > 0 && cfg->coeffs == nullptr) return MUON_EINVAL;
   out->steps = cfg->steps;
   out->schedule = cfg->schedule;
@@ -204,6 +206,7 @@ struct GroupRun {
   std::vector<void*> o_own;
   float beta = 0.0f, neg_lr_scale = 0.0f;
   int nesterov = 0;
+  int norm_base = 0;               // first slot of this group in norms_out
   float* const* cap_u = nullptr;   // spectral cap state (null: off)
   float* const* cap_v = nullptr;
   float* cap_sigma = nullptr;
@@ -272,7 +275,6 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
             EventRec& E) {
   if (!E.mark(st, 0)) return MUON_EHIP;
   // 1. momentum
-  int base = 0;
   for (GroupRun& R : runs) {
     const GroupPlan& p = R.plan;
     if (p.count == 0) continue;
@@ -293,9 +295,9 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       L.partials = part + static_cast<size_t>(c0) * p.P;
       if (launch_momentum(L, st) != hipSuccess) return MUON_EHIP;
     }
-    if (E.live() && norms_out != nullptr && launch_norms(part, p.P, p.count, norms_out + base, st) != hipSuccess)
+    if (E.live() && norms_out != nullptr &&
+        launch_norms(part, p.P, p.count, norms_out + R.norm_base, st) != hipSuccess)
       return MUON_EHIP;
-    base += p.count;
     if (!E.mark(st, MUON_PHASE_MOMENTUM)) return MUON_EHIP;
   }
 
@@ -605,6 +607,35 @@ std::vector<int> list_phases(std::vector<GroupRun>& runs, const NsCoefs& C, floa
   return D.phases;
 }
 
+// Per device, created on first use and kept until the process ends: one
+// auxiliary stream (default priority, non-blocking) and the fork / join
+// events that order it against the caller's stream.
+struct Aux {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;  // one fork / join sequence at a time
+};
+
+Aux* aux_for_current_device() {
+  static std::mutex table_mu;
+  static std::vector<Aux*> table;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(table_mu);
+  if (static_cast<int>(table.size()) <= dev) table.resize(dev + 1, nullptr);
+  if (table[dev] == nullptr) {
+    Aux* a = new Aux();
+    if (hipStreamCreateWithFlags(&a->s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&a->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&a->join, hipEventDisableTiming) != hipSuccess) {
+      delete a;  // leaves this device on one stream
+      return nullptr;
+    }
+    table[dev] = a;
+  }
+  return table[dev];
+}
+
 int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, void* workspace, size_t workspace_bytes,
               float* norms_out, void* stream, void* const* events, int nevents) {
   if (groups == nullptr || ngroups <= 0) return MUON_EINVAL;
@@ -637,9 +668,12 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
     runs[i].beta = gr.beta;
     runs[i].neg_lr_scale = -gr.lr * gr.scale;
     runs[i].nesterov = gr.nesterov;
+    runs[i].norm_base = i == 0 ? 0 : runs[i - 1].norm_base + groups[i - 1].count;
   }
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < off) return MUON_EWORKSPACE;
   EventRec E;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
   if (events != nullptr) {
     const int need = static_cast<int>(list_phases(runs, C, cfg->eps).size());
     if (nevents < need) return MUON_EINVAL;
@@ -647,8 +681,39 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
       if (events[i] == nullptr) return MUON_EINVAL;
     E.ev = events;
     E.n = nevents;
+    return run_all(runs, C, cfg->eps, ws, norms_out, st, E);  // timed: one stream, phases in order
   }
-  return run_all(runs, C, cfg->eps, static_cast<char*>(workspace), norms_out, static_cast<hipStream_t>(stream), E);
+  // Independent shape groups run as two chains on two streams (the caller's
+  // and an auxiliary one, joined back before returning), so that one chain's
+  // launch tails and bandwidth-bound passes overlap the other's matrix-core
+  // work.  Groups are dealt to the chains by estimated cost, heaviest first.
+  std::vector<int> live;
+  for (int i = 0; i < ngroups; ++i)
+    if (runs[i].plan.count > 0) live.push_back(i);
+  Aux* aux = cfg->streams == 1 || live.size() < 2 ? nullptr : aux_for_current_device();
+  if (aux == nullptr) return run_all(runs, C, cfg->eps, ws, norms_out, st, E);
+  auto cost = [&](int i) {
+    const GroupPlan& p = runs[i].plan;
+    return static_cast<double>(p.count) * p.m * p.n * (p.engine == kSmall ? 16.0 : p.s + 64.0);
+  };
+  std::stable_sort(live.begin(), live.end(), [&](int x, int y) { return cost(x) > cost(y); });
+  std::vector<GroupRun> chain[2];
+  double load[2] = {0.0, 0.0};
+  for (int i : live) {
+    const int c = load[0] <= load[1] ? 0 : 1;
+    chain[c].push_back(runs[i]);
+    load[c] += cost(i);
+  }
+  std::lock_guard<std::mutex> lock(aux->mu);
+  if (hipEventRecord(aux->fork, st) != hipSuccess || hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
+    return MUON_EHIP;
+  EventRec E1;
+  rc = run_all(chain[0], C, cfg->eps, ws, norms_out, st, E);
+  const int rc1 = run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1);
+  // join even after a failed launch, so that the caller's stream never runs ahead of the auxiliary work
+  if (hipEventRecord(aux->join, aux->s) != hipSuccess || hipStreamWaitEvent(st, aux->join, 0) != hipSuccess)
+    return MUON_EHIP;
+  return rc != MUON_OK ? rc : rc1;
 }
 
 }  // namespace

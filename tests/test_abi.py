@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 3
+    assert mu.muon_version() == 4
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -85,7 +85,7 @@ def test_workspace_queries(mu):
     ("steps_negative", -1), ("steps_too_many", -1), ("ncoef_4", -1), ("quintic_c", -2),
     ("bad_precision", -1), ("null_groups", -1), ("misaligned", -1), ("null_matrix", -1),
     ("no_workspace", -3), ("small_workspace", -3), ("bad_dtype", -1), ("negative_eps", -1),
-    ("bad_schedule", -1),
+    ("bad_schedule", -1), ("bad_streams", -1),
 ])
 def test_step_validation(mu, case, expect):
     L = mu.lib()
@@ -97,6 +97,8 @@ def test_step_validation(mu, case, expect):
         cfg.ncoef = 4
     if case == "bad_schedule":
         cfg.schedule = 3
+    if case == "bad_streams":
+        cfg.streams = 2
     g, k2 = _group(mu, dtype=5 if case == "bad_dtype" else None)
     if case == "misaligned":
         k2[0][0] = 0x100002  # W is float32: 4-byte alignment required

@@ -383,3 +383,28 @@ def test_quintic_unsupported_paths(mu):
         with pytest.raises(mu.MuonError) as e:
             run_step(mu, w, precision=mu.MUON_F32 if prec == "f32" else None)
         assert e.value.status == mu.binding.MUON_EUNSUPPORTED
+
+
+def test_two_stream_chains_match_one_stream(mu):
+    """muon_step runs independent shape groups as two chains on two streams by
+    default; the results are bitwise those of the one-stream run, and
+    norms_out keeps its order."""
+    w = wl.config4(count=3)
+    outs = []
+    for streams in (1, 0):
+        groups, devs = [], []
+        for g in w.groups:
+            d = device_group(g)
+            devs.append(d)
+            groups.append(mu.MuonGroup(W=d["W"], M=d["M"], G=d["G"], lr=w.lr, beta=w.beta))
+        norms = torch.zeros(6, device="cuda")
+        mu.muon_step(groups, steps=5, norms_out=norms, streams=streams)
+        torch.cuda.synchronize()
+        outs.append((devs, norms))
+    (d1, n1), (d2, n2) = outs
+    assert torch.equal(n1, n2)
+    for a, b in zip(d1, d2):
+        assert torch.equal(a["W"], b["W"]) and torch.equal(a["M"], b["M"])
+    for gi, g in enumerate(w.groups):
+        U = orc.update_direction(grad64(g, 1), orc.momentum(orc.widen_f32(g.M[1]), grad64(g, 1), 0.95), 0.95, True)
+        assert abs(n2[3 * gi + 1].item() - np.linalg.norm(U)) <= 1e-5 * np.linalg.norm(U)
