@@ -272,6 +272,80 @@ def orthogonality_error(O: np.ndarray) -> float:
     return float(np.linalg.norm(X @ X.T - np.eye(s)) / np.sqrt(s))
 
 
+# ----------------------------------------------------------------------------
+# Spectral diagnostics.  The first page (the "Muon Meets Mamba" practitioner
+# article, its sections on long-term engineering and on the training
+# checkpoints) asks that the largest singular value of each weight/state
+# matrix be computed every few steps and checked against a safety threshold,
+# and that singular values be logged.  It names no algorithm; the reading
+# taken here: with X the short-side orientation of A (s x l) and H = X X^T,
+# the extreme eigenvalues of H are estimated by `iters` Lanczos steps with
+# full reorthogonalisation from a fixed start vector, and sigma = sqrt(theta).
+# With iters >= s the Krylov space is the whole space and the estimates are
+# the exact extreme singular values (up to rounding).
+# ----------------------------------------------------------------------------
+WEYL_STEP = 2654435769  # floor(2^32 / golden ratio), odd
+
+
+def lanczos_start(s: int) -> np.ndarray:
+    """Unnormalised start vector: entry i is t_i / 2^24 - 1/2 with t_i the top
+    24 bits of (i * 2654435769) mod 2^32 (a Weyl sequence of the golden
+    ratio); every entry is exact in binary32 and binary64."""
+    i = np.arange(s, dtype=np.uint64)
+    h = (i * np.uint64(WEYL_STEP)) % np.uint64(1 << 32)
+    return (h >> np.uint64(8)).astype(np.float64) / float(1 << 24) - 0.5
+
+
+def lanczos_extremes(H: np.ndarray, iters: int):
+    """min(iters, order) Lanczos steps on the symmetric matrix H from the
+    normalised lanczos_start vector:
+        w = H q_j,  alpha_j = q_j^T w,  w -= alpha_j q_j + beta_j q_{j-1},
+        w -= Q (Q^T w) twice (Q = [q_0 .. q_j], classical Gram-Schmidt, two
+        passes),  beta_{j+1} = ||w||,  q_{j+1} = w / beta_{j+1};
+    the run ends early only when beta_{j+1} is exactly zero (or not finite).
+    Returns (theta_min, theta_max): the extreme eigenvalues of the tridiagonal
+    T with the alphas on its diagonal and the betas beside it."""
+    H = np.asarray(H, dtype=np.float64)
+    s = H.shape[0]
+    k = min(int(iters), s)
+    Q = np.zeros((k, s))
+    q = lanczos_start(s)
+    q = q / np.linalg.norm(q)
+    q_prev = np.zeros(s)
+    beta = 0.0
+    alphas, betas = [], []
+    for j in range(k):
+        Q[j] = q
+        w = H @ q
+        alpha = float(q @ w)
+        w = w - alpha * q - beta * q_prev
+        for _ in range(2):
+            w = w - Q[:j + 1].T @ (Q[:j + 1] @ w)
+        alphas.append(alpha)
+        beta_next = float(np.linalg.norm(w))
+        if j + 1 == k or not (beta_next > 0.0 and np.isfinite(beta_next)):
+            break
+        betas.append(beta_next)
+        q_prev, q, beta = q, w / beta_next, beta_next
+    if not np.all(np.isfinite(alphas)):
+        return float("nan"), float("nan")
+    T = np.diag(alphas) + np.diag(betas, 1) + np.diag(betas, -1)
+    ev = np.linalg.eigvalsh(T)
+    return float(ev[0]), float(ev[-1])
+
+
+def spectral_diagnostics(A: np.ndarray, iters: int) -> dict:
+    """Per matrix: the orthogonality error ||X X^T - I_s||_F / sqrt(s) and the
+    Lanczos estimates of the extreme eigenvalues of H = X X^T (theta) and of
+    the extreme singular values sqrt(max(theta, 0))."""
+    A = np.asarray(A, dtype=np.float64)
+    X = A.T if A.shape[0] > A.shape[1] else A
+    lo, hi = lanczos_extremes(X @ X.T, iters)
+    return {"orth_err": orthogonality_error(A), "theta_min": lo, "theta_max": hi,
+            "sigma_min": float(np.sqrt(max(lo, 0.0))) if np.isfinite(lo) else lo,
+            "sigma_max": float(np.sqrt(max(hi, 0.0))) if np.isfinite(hi) else hi}
+
+
 def singular_values(O: np.ndarray) -> np.ndarray:
     """Singular values, descending (LAPACK through numpy)."""
     return np.linalg.svd(np.asarray(O, dtype=np.float64), compute_uv=False)

@@ -474,3 +474,87 @@ def test_adamw_hand_example_and_zero_gradient():
     p3, m3, v3 = orc.adamw_step(np.array([3.0]), np.array([0.0]), np.array([0.0]), np.array([0.0]), lr=0.01,
                                 beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.2, step=5)
     assert m3[0] == 0.0 and v3[0] == 0.0 and abs(p3[0] - 3.0 * (1 - 0.002)) < 1e-15
+
+
+# ---- spectral diagnostics ----------------------------------------------------
+def haar(rng, n, k):
+    q, r = np.linalg.qr(rng.standard_normal((n, k)))
+    return q * np.sign(np.diag(r))
+
+
+def test_lanczos_start_hand_values():
+    # (i * 2654435769) mod 2^32 for i = 0..3, by hand: 0, 2654435769,
+    # 5308871538 - 2^32 = 1013904242, 7963307307 - 2^32 = 3668340011; top 24
+    # bits: 0, 10368889, 3960563, 14329453
+    want = np.array([0, 10368889, 3960563, 14329453]) / 2.0 ** 24 - 0.5
+    assert np.array_equal(orc.lanczos_start(4), want)
+    q = orc.lanczos_start(1000)
+    assert abs(q.mean()) < 2e-3 and q.min() >= -0.5 and q.max() < 0.5  # equidistributed
+
+
+def test_orth_error_closed_form_both_orientations():
+    rng = np.random.default_rng(31)
+    for m, n in ((40, 90), (90, 40)):
+        s = min(m, n)
+        sig = rng.uniform(0.1, 1.7, s)
+        A = haar(rng, m, s) @ np.diag(sig) @ haar(rng, n, s).T
+        want = np.sqrt(np.sum((sig ** 2 - 1.0) ** 2) / s)
+        d = orc.spectral_diagnostics(A, s)
+        assert abs(d["orth_err"] - want) <= 1e-12 * want
+        # iters = s: the Krylov space is everything, Ritz extremes = singular extremes
+        assert abs(d["sigma_max"] - sig.max()) <= 1e-10 and abs(d["sigma_min"] - sig.min()) <= 1e-10
+
+
+def test_lanczos_full_run_matches_lapack_svd():
+    rng = np.random.default_rng(5)
+    A = rng.standard_normal((60, 150))
+    sv = np.linalg.svd(A, compute_uv=False)
+    lo, hi = orc.lanczos_extremes(A @ A.T, 60)
+    assert abs(hi - sv[0] ** 2) <= 1e-10 * sv[0] ** 2 and abs(lo - sv[-1] ** 2) <= 1e-10 * sv[0] ** 2
+
+
+def test_lanczos_ritz_bounds_and_monotone():
+    """Ritz values interlace: the extreme ones lie inside the spectrum and move
+    outwards as the Krylov space grows."""
+    rng = np.random.default_rng(6)
+    s = 80
+    lam = np.sort(rng.uniform(0.05, 2.0, s))
+    Qm = haar(rng, s, s)
+    H = Qm @ np.diag(lam) @ Qm.T
+    prev_lo, prev_hi = np.inf, -np.inf
+    for k in (1, 2, 4, 8, 16, 32, 80):
+        lo, hi = orc.lanczos_extremes(H, k)
+        assert lam[0] - 1e-12 <= lo <= hi <= lam[-1] + 1e-12
+        assert lo <= prev_lo + 1e-12 and hi >= prev_hi - 1e-12
+        prev_lo, prev_hi = lo, hi
+    assert abs(prev_lo - lam[0]) < 1e-10 and abs(prev_hi - lam[-1]) < 1e-10
+
+
+def test_lanczos_two_distinct_eigenvalues_exact_after_two_steps():
+    rng = np.random.default_rng(8)
+    s = 12
+    Qm = haar(rng, s, s)
+    lam = np.array([4.0] * 5 + [0.25] * 7)
+    H = Qm @ np.diag(lam) @ Qm.T
+    lo, hi = orc.lanczos_extremes(H, 2)
+    assert abs(lo - 0.25) < 1e-12 and abs(hi - 4.0) < 1e-12
+    # continuing past the invariant subspace stays inside the spectrum
+    lo, hi = orc.lanczos_extremes(H, 12)
+    assert abs(lo - 0.25) < 1e-10 and abs(hi - 4.0) < 1e-10
+
+
+def test_lanczos_2x2_closed_form_and_degenerate_inputs():
+    A = np.array([[1.0, 2.0, 0.5], [-1.0, 0.25, 3.0]])
+    H = A @ A.T
+    a, b, c = H[0, 0], H[0, 1], H[1, 1]
+    r = np.sqrt(((a - c) / 2) ** 2 + b * b)
+    lo, hi = orc.lanczos_extremes(H, 2)
+    assert abs(lo - ((a + c) / 2 - r)) < 1e-12 and abs(hi - ((a + c) / 2 + r)) < 1e-12
+    z = orc.spectral_diagnostics(np.zeros((5, 9)), 5)
+    assert z["orth_err"] == 1.0 and z["sigma_max"] == 0.0 and z["sigma_min"] == 0.0
+    eye = orc.spectral_diagnostics(np.hstack([np.eye(6), np.zeros((6, 3))]), 6)
+    assert eye["orth_err"] == 0.0 and abs(eye["sigma_max"] - 1) < 1e-15 and abs(eye["sigma_min"] - 1) < 1e-15
+    bad = np.ones((4, 7))
+    bad[1, 2] = np.nan
+    d = orc.spectral_diagnostics(bad, 4)
+    assert np.isnan(d["orth_err"]) and np.isnan(d["sigma_max"]) and np.isnan(d["sigma_min"])
