@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 4
+#define MUON_VERSION 5
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -256,6 +256,44 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
 int muon_adamw(int ntensors, float* const* params, const void* const* grads, float* const* exp_avg,
                float* const* exp_avg_sq, const long long* numel, int grad_dtype, float lr, float beta1,
                float beta2, float eps, float weight_decay, long long step, void* stream);
+
+/* Bytes of device workspace muon_spectral_diag needs (0 for invalid or
+ * unsupported arguments).  Matrices are processed in chunks whose scratch
+ * stays within 2 GiB, so the size stops growing with batch beyond one chunk. */
+size_t muon_spectral_diag_workspace_size(int m, int n, long long batch, int dtype, int iters);
+
+/* Spectral diagnostics of a stack of matrices: the "Muon Meets Mamba"
+ * practitioner article (training checkpoints; long-term engineering) asks
+ * for the largest singular value of each weight or state matrix every few
+ * steps, checked against a threshold, and for singular values in the training
+ * log; the orthogonality error tells how far an orthogonalised update is from
+ * orthogonal.  For A[b] (m x n), X its short-side orientation (s x l, X = A
+ * or A^T) and H = X X^T:
+ *   orth_err[b]   ||H - I_s||_F / sqrt(s)
+ *   sigma_max[b]  sqrt(theta_max), sigma_min[b] = sqrt(max(theta_min, 0)),
+ *                 theta the extreme Ritz values of min(iters, s) Lanczos steps
+ *                 on H with full reorthogonalisation (two classical
+ *                 Gram-Schmidt passes) from the start vector
+ *                 q_i = t_i / 2^24 - 1/2, t_i the top 24 bits of
+ *                 (i * 2654435769) mod 2^32, normalised; the run ends early
+ *                 when the residual beta_{j+1} <= 2^-20 ||H q_j|| (an
+ *                 invariant Krylov space) or is not finite.  With
+ *                 iters >= s these are the extreme singular values; with
+ *                 fewer they lie inside [sigma_min, sigma_max] of A.
+ *   A      [batch][m][n] contiguous, dtype MUON_BF16 or MUON_F32 (finite
+ *          float32 values below 2^127 are split exactly into three bfloat16
+ *          pieces; the six products above 2^-24 relative are kept, so H has
+ *          float32 accuracy)
+ *   orth_err, sigma_max, sigma_min  device float[batch] each, or NULL (not
+ *          computed); none may overlap A.  All NULL: nothing is done.
+ * H is formed on the matrix cores (float32 accumulation), the Lanczos run is
+ * float32, the tridiagonal extremes float64.  Supported: min(m, n) <= 4096,
+ * max(m, n) <= 2^22, 1 <= iters <= 512 (larger: MUON_EUNSUPPORTED; iters < 1:
+ * MUON_EINVAL).  A NaN or Inf in A[b] gives NaN outputs for b.
+ * Deterministic; no allocation; asynchronous on `stream`. */
+int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,
+                       float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* Human-readable name of a muon_status. */
 const char* muon_status_string(int status);

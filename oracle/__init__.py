@@ -10,4 +10,4 @@ from .muon_oracle import (CUBIC, DEFAULT_EPS, widen_bf16, widen_f32, momentum,  
                           ns_iterate, newton_schulz, ns_batched, muon_step, muon_step_group,
                           orthogonality_error, singular_values, rel_frobenius, factored_ns,
                           spectral_cap_update, power_step, muon_step_capped, adamw_step,
-                          WEYL_STEP, lanczos_start, lanczos_extremes, spectral_diagnostics)
+                          WEYL_STEP, LANCZOS_BREAKDOWN, lanczos_start, lanczos_extremes, spectral_diagnostics)

@@ -285,6 +285,7 @@ def orthogonality_error(O: np.ndarray) -> float:
 # the exact extreme singular values (up to rounding).
 # ----------------------------------------------------------------------------
 WEYL_STEP = 2654435769  # floor(2^32 / golden ratio), odd
+LANCZOS_BREAKDOWN = 2.0 ** -20  # relative size of a residual taken as zero
 
 
 def lanczos_start(s: int) -> np.ndarray:
@@ -302,7 +303,10 @@ def lanczos_extremes(H: np.ndarray, iters: int):
         w = H q_j,  alpha_j = q_j^T w,  w -= alpha_j q_j + beta_j q_{j-1},
         w -= Q (Q^T w) twice (Q = [q_0 .. q_j], classical Gram-Schmidt, two
         passes),  beta_{j+1} = ||w||,  q_{j+1} = w / beta_{j+1};
-    the run ends early only when beta_{j+1} is exactly zero (or not finite).
+    the run ends early when beta_{j+1} <= 2^-20 ||H q_j|| (the Krylov space is
+    invariant to working accuracy: the residual left is rounding noise, and
+    continuing from it would build a basis that is no longer orthogonal) or
+    is not finite.
     Returns (theta_min, theta_max): the extreme eigenvalues of the tridiagonal
     T with the alphas on its diagonal and the betas beside it."""
     H = np.asarray(H, dtype=np.float64)
@@ -317,13 +321,14 @@ def lanczos_extremes(H: np.ndarray, iters: int):
     for j in range(k):
         Q[j] = q
         w = H @ q
+        hq = float(np.linalg.norm(w))
         alpha = float(q @ w)
         w = w - alpha * q - beta * q_prev
         for _ in range(2):
             w = w - Q[:j + 1].T @ (Q[:j + 1] @ w)
         alphas.append(alpha)
         beta_next = float(np.linalg.norm(w))
-        if j + 1 == k or not (beta_next > 0.0 and np.isfinite(beta_next)):
+        if j + 1 == k or not (beta_next > LANCZOS_BREAKDOWN * hq and np.isfinite(beta_next)):
             break
         betas.append(beta_next)
         q_prev, q, beta = q, w / beta_next, beta_next

@@ -50,7 +50,7 @@ class GroupC(ctypes.Structure):
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
            "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
-           "muon_status_string", "muon_version")
+           "muon_spectral_diag_workspace_size", "muon_spectral_diag", "muon_status_string", "muon_version")
 
 
 def lib():
@@ -85,6 +85,10 @@ def lib():
     L.muon_adamw.argtypes = [i, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                              ctypes.POINTER(ctypes.c_longlong), i, f, f, f, f, f, ctypes.c_longlong, vp]
     L.muon_adamw.restype = i
+    L.muon_spectral_diag_workspace_size.argtypes = [i, i, ctypes.c_longlong, i, i]
+    L.muon_spectral_diag_workspace_size.restype = sz
+    L.muon_spectral_diag.argtypes = [vp, i, i, i, ctypes.c_longlong, i, vp, vp, vp, vp, sz, vp]
+    L.muon_spectral_diag.restype = i
     L.muon_status_string.argtypes = [i]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_version.argtypes = []
@@ -367,3 +371,34 @@ def muon_adamw(params, grads, exp_avg, exp_avg_sq, lr, step, beta1=0.9, beta2=0.
     """AdamW over lists of contiguous float32 tensors (params, exp_avg,
     exp_avg_sq updated in place); grads float32 or bf16 (one dtype)."""
     AdamwTensors(params, grads, exp_avg, exp_avg_sq).step(lr, step, beta1, beta2, eps, weight_decay, stream)
+
+
+def muon_spectral_diag(A, iters=32, orth_err=True, sigma_max=True, sigma_min=True, workspace=None, stream=None):
+    """Orthogonality error and Lanczos estimates of the extreme singular values
+    of every matrix of A ([batch, m, n] or [m, n], contiguous, float32 or
+    bf16).  Returns a dict of float32 [batch] tensors for the quantities
+    asked for."""
+    import torch
+    L = lib()
+    if A.dim() == 2:
+        A = A.unsqueeze(0)
+    if A.dim() != 3 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous [batch, m, n] tensor")
+    b, m, n = A.shape
+    dt = _dtype_code(A)
+    outs = {}
+    for name, want in (("orth_err", orth_err), ("sigma_max", sigma_max), ("sigma_min", sigma_min)):
+        if want:
+            outs[name] = torch.empty(b, dtype=torch.float32, device=A.device)
+    need = L.muon_spectral_diag_workspace_size(m, n, b, dt, int(iters))
+    if need == 0:
+        rc = L.muon_spectral_diag(None, dt, m, n, b, int(iters), None, None, None, None, 0, None)
+        _check(rc if rc != MUON_OK else -1, "muon_spectral_diag")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    ptr = lambda k: ctypes.c_void_p(outs[k].data_ptr()) if k in outs else None  # noqa: E731
+    rc = L.muon_spectral_diag(ctypes.c_void_p(A.data_ptr()), dt, m, n, b, int(iters), ptr("orth_err"),
+                              ptr("sigma_max"), ptr("sigma_min"), ctypes.c_void_p(workspace.data_ptr()), need,
+                              _stream_handle(stream))
+    _check(rc, "muon_spectral_diag")
+    return outs

@@ -522,7 +522,10 @@ __device__ __forceinline__ void sym_to_global(const BufsN<SYM_NSTAGE>& bufs, bf1
   }
 }
 
-template <int TT>
+// F32: the result leaves as float32 straight from the accumulators into F
+// (the diagnostics' Gram matrix), exactly symmetric: on a diagonal tile only
+// the entries on or above the diagonal are taken and mirrored.
+template <int TT, bool F32>
 __global__ void __launch_bounds__(NTHR2) __attribute__((amdgpu_waves_per_eu(SymCfg<TT>::kWpe, SymCfg<TT>::kWpe)))
 symprod_bf16_kernel(SymArgs G) {
   constexpr int OPBT = TT * BK * 2;  // bytes of one operand per stage
@@ -602,6 +605,41 @@ symprod_bf16_kernel(SymArgs G) {
     const float a1 = S.a1 * ia, b1 = S.b1 * ib;
     const int lane_e = opaque(lane);
     const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;
+    if constexpr (F32) {
+      // lane: D[m0 + r][n], r = 0..3; the tile row-wise (32 lanes cover 32
+      // consecutive n), the mirror as one 16-byte store per lane
+      float* F = S.F + zoff;
+      const long long sp = S.s_pad;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * WT + j * 32 + col;
+        const long long gn = static_cast<long long>(bj) * TT + n;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m0 = wm * WT + i * 32 + q * 8 + rq;
+            const long long gm = static_cast<long long>(bi) * TT + m0;
+            f32x4_t v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = b1 * acc.c[i][j][4 * q + r] + ((diag && m0 + r == n) ? a1 : 0.0f);
+            if (!diag) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) F[(gm + r) * sp + gn] = v[r];
+              *reinterpret_cast<f32x4_t*>(F + gn * sp + gm) = v;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (m0 + r <= n) {
+                  F[(gm + r) * sp + gn] = v[r];
+                  F[gn * sp + gm + r] = v[r];
+                }
+            }
+          }
+        }
+      }
+      continue;  // the operands' LDS is free: every wave passed the barrier above
+    }
     bf16_t* O1 = S.O1 == nullptr ? nullptr : S.O1 + zoff;
     bf16_t* O2 = S.O2 == nullptr ? nullptr : S.O2 + zoff;
 #pragma unroll
@@ -658,7 +696,7 @@ int grid_for_zip(const SymArgs& G) {
   return per_xcd * NXCD;
 }
 
-template <int TT>
+template <int TT, bool F32>
 hipError_t launch_symprod_tt(const SymArgs& G, hipStream_t st) {
   // persistent: kWpe resident workgroups per CU (LDS bound), a multiple of
   // the XCD count
@@ -673,7 +711,7 @@ hipError_t launch_symprod_tt(const SymArgs& G, hipStream_t st) {
   const int need = grid_for_zip(G);
   const int grid = need < slots ? need : slots;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(symprod_bf16_kernel<TT>, dim3(grid), dim3(NTHR2), 0, st, G);
+  hipLaunchKernelGGL((symprod_bf16_kernel<TT, F32>), dim3(grid), dim3(NTHR2), 0, st, G);
   return hipGetLastError();
 }
 
@@ -696,17 +734,19 @@ int symprod_tiles_per_matrix(int s_pad, int tile) {
   return nt * (nt + 1) / 2;
 }
 
-// One launch per tile size present (zip chains never mix sizes: they share
-// s_pad).
+// One launch per tile size and output type present (zip chains never mix
+// them: they share s_pad and outputs).
 hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st) {
-  SymArgs part[2] = {};
+  SymArgs part[4] = {};
   for (int s = 0; s < G.nseg; ++s) {
     const int tt = G.seg[s].tile ? G.seg[s].tile : sym_tile(G.seg[s].s_pad);
-    SymArgs& P = part[tt == 192 ? 1 : 0];
+    SymArgs& P = part[(tt == 192 ? 1 : 0) + (G.seg[s].F != nullptr ? 2 : 0)];
     P.seg[P.nseg++] = G.seg[s];
   }
-  hipError_t e = part[1].nseg ? launch_symprod_tt<192>(part[1], st) : hipSuccess;
-  if (e == hipSuccess && part[0].nseg) e = launch_symprod_tt<128>(part[0], st);
+  hipError_t e = part[1].nseg ? launch_symprod_tt<192, false>(part[1], st) : hipSuccess;
+  if (e == hipSuccess && part[0].nseg) e = launch_symprod_tt<128, false>(part[0], st);
+  if (e == hipSuccess && part[3].nseg) e = launch_symprod_tt<192, true>(part[3], st);
+  if (e == hipSuccess && part[2].nseg) e = launch_symprod_tt<128, true>(part[2], st);
   return e;
 }
 

@@ -143,6 +143,8 @@ struct SymSeg {
   int zip_next;        // 1: the next segment has the same count and s_pad and
                        // runs matrix by matrix together with this one
   int tile;            // 0: symprod_tile(s_pad); else 128 or 192 (dividing s_pad)
+  float* F;            // non-null: O1 = a1 inv^pa I + b1 inv^pb L R as float32 here
+                       // [count][s_pad][s_pad] (stride), exactly symmetric; O1, O2 unused
 };
 struct SymArgs {
   SymSeg seg[kMaxSeg];
@@ -191,6 +193,33 @@ struct FactLaunch {
 };
 int factored_lds_per_wave(int m_pad, int n_pad, bool dense);
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st);
+
+// Spectral diagnostics (a chunk of `count` matrices per launch).
+struct DiagPackLaunch {
+  const void* A;       // [count][m][n], float32 or bf16 (f32)
+  long long astride;   // m * n
+  int n, s, l;         // row stride of A; short and long side
+  bool tall, f32;
+  bf16_t* L;           // [count][s_pad][ld] operand rows (X, or its pieces)
+  bf16_t* R;           // float32 inputs: the partner pieces; else null (R = L)
+  long long ostride;   // s_pad * ld
+  int s_pad, kdim, ld; // s_pad % 128 == 0, kdim % 64 == 0, ld = kdim (bf16) or 6 kdim
+  long long count;
+};
+hipError_t launch_diag_pack(const DiagPackLaunch& P, hipStream_t st);
+struct DiagLaunch {
+  const float* H;      // [count][s_pad][s_pad] Gram matrices (exactly symmetric)
+  long long hstride;
+  float* Q;            // [count][kmax][s_pad] Lanczos basis (scratch)
+  long long qstride;
+  int s, s_pad, iters, kmax;
+  float* orth;         // [count] or null
+  float* smax;         // [count] or null
+  float* smin;         // [count] or null
+  long long count;
+};
+size_t diag_lanczos_lds(int s_pad, int kmax);
+hipError_t launch_diag_lanczos(const DiagLaunch& D, hipStream_t st);
 
 // AdamW over a list of float32 tensors (one launch: up to kAdamwMax tensors).
 constexpr int kAdamwMax = 80;      // 40 bytes each: the table fits the kernel arguments

@@ -716,6 +716,47 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   return rc != MUON_OK ? rc : rc1;
 }
 
+// ---- spectral diagnostics ------------------------------------------------------
+constexpr int kDiagMaxS = 4096;
+constexpr int kDiagMaxIters = 512;
+constexpr size_t kDiagChunkBytes = size_t(1) << 31;  // workspace of one chunk of matrices
+
+struct DiagPlan {
+  int s, l, s_pad, kdim, ld, k;
+  bool tall, f32;
+  size_t op_bytes, h_bytes, q_bytes;  // per matrix
+  long long chunk;                    // matrices per pass
+  size_t off_l, off_r, off_h, off_q, end;
+};
+
+int plan_diag(int m, int n, long long batch, int dtype, int iters, DiagPlan* p) {
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_EINVAL;
+  if (m <= 0 || n <= 0 || batch < 0 || iters < 1) return MUON_EINVAL;
+  p->tall = m > n;
+  p->s = std::min(m, n);
+  p->l = std::max(m, n);
+  p->f32 = dtype == MUON_F32;
+  if (p->s > kDiagMaxS || iters > kDiagMaxIters) return MUON_EUNSUPPORTED;
+  p->s_pad = round_up(p->s, 128);
+  if (p->l > (1 << 22)) return MUON_EUNSUPPORTED;
+  p->kdim = round_up(p->l, 64);
+  p->ld = p->kdim * (p->f32 ? 6 : 1);
+  if (static_cast<long long>(p->s_pad) * p->ld * 2 >= (1LL << 31)) return MUON_EUNSUPPORTED;  // 32-bit offsets
+  p->k = std::min(iters, p->s);
+  p->op_bytes = align_up(static_cast<size_t>(p->s_pad) * p->ld * 2, kAlign);
+  p->h_bytes = align_up(static_cast<size_t>(p->s_pad) * p->s_pad * 4, kAlign);
+  p->q_bytes = align_up(static_cast<size_t>(p->k) * p->s_pad * 4, kAlign);
+  const size_t per = p->op_bytes * (p->f32 ? 2 : 1) + p->h_bytes + p->q_bytes;
+  p->chunk = std::max<long long>(1, std::min<long long>(batch, static_cast<long long>(kDiagChunkBytes / per)));
+  const size_t c = static_cast<size_t>(p->chunk);
+  p->off_l = 0;
+  p->off_r = p->off_l + c * p->op_bytes;
+  p->off_h = p->off_r + (p->f32 ? c * p->op_bytes : 0);
+  p->off_q = p->off_h + c * p->h_bytes;
+  p->end = p->off_q + c * p->q_bytes;
+  return MUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -918,6 +959,76 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
   F.eps = cfg->eps;
   for (int k = 0; k < C.steps; ++k) { F.a[k] = C.a[k]; F.b[k] = C.b[k]; F.c[k] = C.c[k]; }
   return launch_ns_factored(F, static_cast<hipStream_t>(stream)) == hipSuccess ? MUON_OK : MUON_EHIP;
+}
+
+size_t muon_spectral_diag_workspace_size(int m, int n, long long batch, int dtype, int iters) {
+  DiagPlan p;
+  if (plan_diag(m, n, batch, dtype, iters, &p) != MUON_OK) return 0;
+  return batch == 0 ? kAlign : p.end;
+}
+
+int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,
+                       float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes, void* stream) {
+  DiagPlan p;
+  const int rc = plan_diag(m, n, batch, dtype, iters, &p);
+  if (rc != MUON_OK) return rc;
+  if (batch == 0 || (orth_err == nullptr && sigma_max == nullptr && sigma_min == nullptr)) return MUON_OK;
+  const size_t es = dtype_size(dtype);
+  if (A == nullptr || !aligned_to(A, es)) return MUON_EINVAL;
+  const char* ab = static_cast<const char*>(A);
+  const size_t abytes = static_cast<size_t>(batch) * m * n * es;
+  for (float* o : {orth_err, sigma_max, sigma_min}) {
+    if (o == nullptr) continue;
+    const char* ob = reinterpret_cast<const char*>(o);
+    if (!aligned_to(o, 4) || (ob < ab + abytes && ab < ob + static_cast<size_t>(batch) * 4)) return MUON_EINVAL;
+  }
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < p.end) return MUON_EWORKSPACE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  bf16_t* L = reinterpret_cast<bf16_t*>(ws + p.off_l);
+  bf16_t* R = p.f32 ? reinterpret_cast<bf16_t*>(ws + p.off_r) : nullptr;
+  float* H = reinterpret_cast<float*>(ws + p.off_h);
+  float* Q = reinterpret_cast<float*>(ws + p.off_q);
+  for (long long c0 = 0; c0 < batch; c0 += p.chunk) {
+    const long long cnt = std::min(p.chunk, batch - c0);
+    DiagPackLaunch P{};
+    P.A = ab + static_cast<size_t>(c0) * m * n * es;
+    P.astride = static_cast<long long>(m) * n;
+    P.n = n; P.s = p.s; P.l = p.l;
+    P.tall = p.tall; P.f32 = p.f32;
+    P.L = L; P.R = R;
+    P.ostride = static_cast<long long>(p.op_bytes / 2);
+    P.s_pad = p.s_pad; P.kdim = p.kdim; P.ld = p.ld;
+    P.count = cnt;
+    if (launch_diag_pack(P, st) != hipSuccess) return MUON_EHIP;
+    SymArgs G{};
+    SymSeg& S = G.seg[0];
+    G.nseg = 1;
+    S.L = L;
+    S.R = p.f32 ? R : L;
+    S.F = H;
+    S.stride = static_cast<long long>(p.h_bytes / 4);
+    S.in_stride = P.ostride;
+    S.ld = p.ld;
+    S.kdim = p.ld;  // contraction over every piece
+    S.s_pad = p.s_pad;
+    S.count = static_cast<int>(cnt);
+    S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);
+    S.a1 = 0.0f; S.b1 = 1.0f;
+    if (launch_symprod_bf16(G, st) != hipSuccess) return MUON_EHIP;
+    DiagLaunch D{};
+    D.H = H;
+    D.hstride = S.stride;
+    D.Q = Q;
+    D.qstride = static_cast<long long>(p.q_bytes / 4);
+    D.s = p.s; D.s_pad = p.s_pad; D.iters = iters; D.kmax = p.k;
+    D.orth = orth_err ? orth_err + c0 : nullptr;
+    D.smax = sigma_max ? sigma_max + c0 : nullptr;
+    D.smin = sigma_min ? sigma_min + c0 : nullptr;
+    D.count = cnt;
+    if (launch_diag_lanczos(D, st) != hipSuccess) return MUON_EHIP;
+  }
+  return MUON_OK;
 }
 
 int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long long batch, const muon_ns_cfg* cfg,

@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 4
+    assert mu.muon_version() == 5
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -258,3 +258,53 @@ def test_adamw_validation(mu, case, expect):
                       1.0 if case == "beta1_one" else 0.9, 0.95, -1.0 if case == "neg_eps" else 1e-8, 0.1,
                       0 if case == "step0" else 1, None)
     assert rc == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("iters0", -1), ("bad_dtype", -1), ("neg_batch", -1), ("zero_m", -1), ("s_too_big", -2), ("iters_too_big", -2),
+    ("null_a", -1), ("misaligned_out", -1), ("overlap", -1), ("no_workspace", -3), ("small_workspace", -3),
+    ("empty_batch", 0), ("nothing_asked", 0),
+])
+def test_spectral_diag_validation(mu, case, expect):
+    """Every rejection happens on the host before any launch (fake device
+    addresses are never touched)."""
+    L = mu.lib()
+    m, n, b, it, dt = 96, 200, 3, 16, mu.MUON_BF16
+    if case == "iters0":
+        it = 0
+    if case == "bad_dtype":
+        dt = 9
+    if case == "neg_batch":
+        b = -1
+    if case == "zero_m":
+        m = 0
+    if case == "s_too_big":
+        m, n = 5000, 6000
+    if case == "iters_too_big":
+        it = 513
+    if case == "empty_batch":
+        b = 0
+    A = None if case == "null_a" else 0x1000000
+    out = 0x2000002 if case == "misaligned_out" else (0x1000000 + 64 if case == "overlap" else 0x2000000)
+    ws_size = L.muon_spectral_diag_workspace_size(m, n, b, dt, it)
+    if expect == 0 or case in ("no_workspace", "small_workspace", "null_a", "misaligned_out", "overlap"):
+        assert ws_size > 0
+    ws = None if case == "no_workspace" else 0x40000000
+    wsb = ws_size - 256 if case == "small_workspace" else ws_size
+    o = None if case == "nothing_asked" else out
+    rc = L.muon_spectral_diag(A, dt, m, n, b, it, o, None, None, ws, wsb, None)
+    assert rc == expect, (case, rc)
+
+
+def test_spectral_diag_workspace_sizes(mu):
+    L = mu.lib()
+    # bf16: one operand, H and the Lanczos basis per matrix
+    s_pad, kdim, k = 768, 1536, 32
+    per = s_pad * kdim * 2 + s_pad * s_pad * 4 + k * s_pad * 4
+    assert L.muon_spectral_diag_workspace_size(768, 1536, 24, mu.MUON_BF16, 32) == 24 * per
+    # float32 inputs: two operands of six pieces each; tall is oriented
+    per32 = 2 * s_pad * 6 * 3392 * 2 + s_pad * s_pad * 4 + k * s_pad * 4
+    assert L.muon_spectral_diag_workspace_size(3352, 768, 4, mu.MUON_F32, 32) == 4 * per32
+    # chunked: the size stops growing once a chunk is full
+    big = L.muon_spectral_diag_workspace_size(64, 128, 393216, mu.MUON_BF16, 64)
+    assert big <= 2 ** 31 and big == L.muon_spectral_diag_workspace_size(64, 128, 2 * 393216, mu.MUON_BF16, 64)

@@ -538,9 +538,12 @@ def test_lanczos_two_distinct_eigenvalues_exact_after_two_steps():
     H = Qm @ np.diag(lam) @ Qm.T
     lo, hi = orc.lanczos_extremes(H, 2)
     assert abs(lo - 0.25) < 1e-12 and abs(hi - 4.0) < 1e-12
-    # continuing past the invariant subspace stays inside the spectrum
+    # the Krylov space is invariant after two steps: the run stops there
     lo, hi = orc.lanczos_extremes(H, 12)
-    assert abs(lo - 0.25) < 1e-10 and abs(hi - 4.0) < 1e-10
+    assert abs(lo - 0.25) < 1e-12 and abs(hi - 4.0) < 1e-12
+    # a multiple of the identity: one step
+    lo, hi = orc.lanczos_extremes(3.0 * np.eye(9), 9)
+    assert abs(lo - 3.0) < 1e-14 and abs(hi - 3.0) < 1e-14
 
 
 def test_lanczos_2x2_closed_form_and_degenerate_inputs():
