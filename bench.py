@@ -407,6 +407,89 @@ def bench_adamw(args, torch, mu, wl):
                          "traffic": None}}
 
 
+def bench_diag(args, torch, mu, wl):
+    """Spectral diagnostics of the Mamba-2-130M projection matrices, one
+    muon_spectral_diag call per shape (24 out_proj 768 x 1536 and 24 in_proj
+    3352 x 768): by default the float32 weights (W = 0.02 N(0, 1), as in the
+    full step: the largest singular value checked every few steps), with
+    --diag-input updates their bf16 Muon updates (5 NS steps of bf16 N(0, 1)
+    gradients: the orthogonality error of the update).  Per-pass durations
+    from HIP events recorded by muon_spectral_diag_timed."""
+    stacks = []
+    for name, a in wl.projection_stacks(args.count):
+        if args.diag_input == "weights":
+            A = torch.from_numpy(0.02 * a).cuda()
+        else:
+            G = torch.from_numpy(a).cuda().to(torch.bfloat16)
+            A = torch.empty_like(G)
+            mu.muon_ns_orthogonalize(G, A, steps=5)
+            del G
+        stacks.append((name, A))
+    it = args.iters
+    wss = [torch.empty(mu.lib().muon_spectral_diag_workspace_size(A.shape[1], A.shape[2], A.shape[0],
+                                                                   mu.binding._dtype_code(A), it),
+                       dtype=torch.uint8, device="cuda") for _, A in stacks]
+    for _ in range(args.warmup):
+        for (_, A), ws in zip(stacks, wss):
+            mu.muon_spectral_diag(A, iters=it, workspace=ws)
+
+    def events(k):
+        out = []
+        for _ in range(k):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            out.append(e)
+        return out
+    evs = [[events(4) for _ in stacks] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for (_, A), ws, ev in zip(stacks, wss, evs[k]):
+            mu.muon_spectral_diag(A, iters=it, workspace=ws, events=[e.cuda_event for e in ev])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # algorithmic work per launch: pack reads A and writes the operand rows;
+    # the Gram's six (float32 input) or one (bf16) bf16 products of
+    # s (s + 1) l flops (upper triangle); Lanczos reads H once per step
+    kern = {"diag_pack_kernel": [0.0, 0.0], "symprod_bf16_kernel<F32>": [0.0, 0.0], "diag_lanczos_kernel": [0.0, 0.0]}
+    for si, (name, A) in enumerate(stacks):
+        cnt, m, n = A.shape
+        s_, l_ = min(m, n), max(m, n)
+        f32 = A.dtype == torch.float32
+        pieces = 6 if f32 else 1
+        s_pad, kdim = -(-s_ // 128) * 128, -(-l_ // 64) * 64
+        work = [cnt * (m * n * A.element_size() + (2 if f32 else 1) * s_pad * pieces * kdim * 2),
+                cnt * pieces * s_ * (s_ + 1) * l_,
+                cnt * (min(it, s_) + 1) * s_ * s_ * 4]
+        for p, key in enumerate(kern):
+            t = float(np.mean([evs[k][si][p].elapsed_time(evs[k][si][p + 1]) for k in range(args.steps)]))
+            kern[key][0] += t
+            kern[key][1] += work[p]
+    kernels = {}
+    for key, (t, work) in kern.items():
+        if key.startswith("symprod"):
+            kernels[key] = {"ms": round(t, 4), "tflops": round(work / (t * 1e-3) / 1e12, 1),
+                            "frac": round(work / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "bound": "mfma"}
+        else:
+            kernels[key] = {"ms": round(t, 4), "gbs": round(work / (t * 1e-3) / 1e9, 1),
+                            "frac": round(work / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bound": "hbm"}
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
+    if kd["bound"] == "mfma":
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": kd["tflops"], "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": kd["frac"], "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": kd["frac"], "traffic": None}
+    nmat = sum(A.shape[0] for _, A in stacks)
+    return {"metric": "Spectral diagnostics matrices/s (orthogonality error + Lanczos sigma_max/sigma_min)",
+            "value": round(nmat / (ms * 1e-3), 1), "unit": "matrices/s", "ms_per_step": round(ms, 4),
+            "dtype": "f32" if args.diag_input == "weights" else "bf16",
+            "config": {"workload": f"diag: {args.diag_input} of {args.count} out_proj 768x1536 + {args.count} "
+                                   f"in_proj 3352x768, {it} Lanczos steps"},
+            "roofline": roofline, "kernels": kernels}
+
+
 def bench_group(args, torch, mu, wl, which):
     w = wl.config2() if which == "out_proj" else wl.config3() if which == "in_proj" else wl.config1()
     groups = []
@@ -450,13 +533,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_step",
                     choices=["full_step", "out_proj", "in_proj", "injections", "injections_factored", "adamw",
-                             "single"])
+                             "diag", "single"])
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
     ap.add_argument("--batch", type=int, default=393216, help="injections batch")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense", action="store_true", help="injections_factored: also write the dense result")
     ap.add_argument("--cap", action="store_true", help="full_step: spectral cap on (power step per update)")
+    ap.add_argument("--diag-input", default="weights", choices=["weights", "updates"],
+                    help="diag: float32 weights or bf16 Muon updates")
+    ap.add_argument("--iters", type=int, default=32, help="diag: Lanczos steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB plain copy first (reference for profiler byte counters)")
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -488,6 +574,8 @@ def main():
         res = bench_injections_factored(args, torch, mu, wl)
     elif args.workload == "adamw":
         res = bench_adamw(args, torch, mu, wl)
+    elif args.workload == "diag":
+        res = bench_diag(args, torch, mu, wl)
     else:
         res = bench_group(args, torch, mu, wl, args.workload)
     out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,

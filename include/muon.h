@@ -295,6 +295,15 @@ int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, 
                        float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* muon_spectral_diag that also records HIP events on `stream`: events[0]
+ * before the first launch, then one after each of the three passes (pack,
+ * Gram, Lanczos) of every chunk; nevents must be at least 1 + 3 * chunks
+ * (chunks = 1 whenever the workspace size for `batch` is below 2 GiB), else
+ * MUON_EINVAL.  Events are created by the caller (hipEvent_t). */
+int muon_spectral_diag_timed(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,
+                             float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes,
+                             void* stream, void** events, int nevents);
+
 /* Human-readable name of a muon_status. */
 const char* muon_status_string(int status);
 

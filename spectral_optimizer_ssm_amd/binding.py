@@ -50,7 +50,8 @@ class GroupC(ctypes.Structure):
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
            "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
-           "muon_spectral_diag_workspace_size", "muon_spectral_diag", "muon_status_string", "muon_version")
+           "muon_spectral_diag_workspace_size", "muon_spectral_diag", "muon_spectral_diag_timed",
+           "muon_status_string", "muon_version")
 
 
 def lib():
@@ -89,6 +90,9 @@ def lib():
     L.muon_spectral_diag_workspace_size.restype = sz
     L.muon_spectral_diag.argtypes = [vp, i, i, i, ctypes.c_longlong, i, vp, vp, vp, vp, sz, vp]
     L.muon_spectral_diag.restype = i
+    L.muon_spectral_diag_timed.argtypes = [vp, i, i, i, ctypes.c_longlong, i, vp, vp, vp, vp, sz, vp,
+                                           ctypes.POINTER(ctypes.c_void_p), i]
+    L.muon_spectral_diag_timed.restype = i
     L.muon_status_string.argtypes = [i]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_version.argtypes = []
@@ -373,11 +377,13 @@ def muon_adamw(params, grads, exp_avg, exp_avg_sq, lr, step, beta1=0.9, beta2=0.
     AdamwTensors(params, grads, exp_avg, exp_avg_sq).step(lr, step, beta1, beta2, eps, weight_decay, stream)
 
 
-def muon_spectral_diag(A, iters=32, orth_err=True, sigma_max=True, sigma_min=True, workspace=None, stream=None):
+def muon_spectral_diag(A, iters=32, orth_err=True, sigma_max=True, sigma_min=True, workspace=None, stream=None,
+                       events=None):
     """Orthogonality error and Lanczos estimates of the extreme singular values
     of every matrix of A ([batch, m, n] or [m, n], contiguous, float32 or
     bf16).  Returns a dict of float32 [batch] tensors for the quantities
-    asked for."""
+    asked for.  events: optional list of HIP event handles (int), recorded
+    before the first pass and after each pass (muon_spectral_diag_timed)."""
     import torch
     L = lib()
     if A.dim() == 2:
@@ -397,8 +403,12 @@ def muon_spectral_diag(A, iters=32, orth_err=True, sigma_max=True, sigma_min=Tru
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ptr = lambda k: ctypes.c_void_p(outs[k].data_ptr()) if k in outs else None  # noqa: E731
-    rc = L.muon_spectral_diag(ctypes.c_void_p(A.data_ptr()), dt, m, n, b, int(iters), ptr("orth_err"),
-                              ptr("sigma_max"), ptr("sigma_min"), ctypes.c_void_p(workspace.data_ptr()), need,
-                              _stream_handle(stream))
+    args = (ctypes.c_void_p(A.data_ptr()), dt, m, n, b, int(iters), ptr("orth_err"), ptr("sigma_max"),
+            ptr("sigma_min"), ctypes.c_void_p(workspace.data_ptr()), need, _stream_handle(stream))
+    if events is None:
+        rc = L.muon_spectral_diag(*args)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        rc = L.muon_spectral_diag_timed(*args, arr, len(events))
     _check(rc, "muon_spectral_diag")
     return outs

@@ -169,7 +169,59 @@ __device__ __forceinline__ float weyl_start(int i) {
   return static_cast<float>(h >> 8) * (1.0f / 16777216.0f) - 0.5f;
 }
 
-__global__ void __launch_bounds__(512) diag_lanczos_kernel(DiagLaunch D) {
+// w = H q for symmetric H, column-parallel: w_c = sum_r H[r][c] q[r].  Work
+// items (128-column chunk, range of rows) are dealt to the waves; a lane owns
+// two adjacent columns and accumulates over its rows (rows read whole and
+// coalesced, kMvRows in flight, q[r] an LDS broadcast, no cross-lane
+// reduction); the row ranges' partials are added in a fixed order.
+constexpr int kMvRows = 16;
+__device__ void sym_matvec(const float* H, int s, int sp, const float* q, float* w, float* part) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int nchunk = sp / 128;
+  const int nsplit = (2 * nw + nchunk - 1) / nchunk;
+  const int rows_per = (s + nsplit - 1) / nsplit;
+  for (int it = wv; it < nchunk * nsplit; it += nw) {
+    const int cc = it % nchunk, rr = it / nchunk;
+    const int c = cc * 128 + lane * 2;
+    const int r0 = rr * rows_per, r1 = r0 + rows_per < s ? r0 + rows_per : s;
+    const float* hc = H + c;
+    float a0 = 0.0f, a1 = 0.0f;
+    int r = r0;
+    for (; r + kMvRows <= r1; r += kMvRows) {
+      f32x2_t h[kMvRows];
+#pragma unroll
+      for (int u = 0; u < kMvRows; ++u)
+        h[u] = *reinterpret_cast<const f32x2_t*>(hc + static_cast<long long>(r + u) * sp);
+#pragma unroll
+      for (int u = 0; u < kMvRows; ++u) {
+        const float qr = q[r + u];
+        a0 = fmaf(h[u][0], qr, a0);
+        a1 = fmaf(h[u][1], qr, a1);
+      }
+    }
+    for (; r < r1; ++r) {
+      const f32x2_t h = *reinterpret_cast<const f32x2_t*>(hc + static_cast<long long>(r) * sp);
+      a0 = fmaf(h[0], q[r], a0);
+      a1 = fmaf(h[1], q[r], a1);
+    }
+    part[rr * sp + c] = a0;
+    part[rr * sp + c + 1] = a1;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < sp; i += blockDim.x) {
+    float x = 0.0f;
+    for (int rr = 0; rr < nsplit; ++rr) x += part[rr * sp + i];
+    w[i] = x;
+  }
+  __syncthreads();
+}
+
+int sym_matvec_splits(int sp, int nw) {
+  const int nchunk = sp / 128;
+  return (2 * nw + nchunk - 1) / nchunk;
+}
+
+__global__ void __launch_bounds__(1024) diag_lanczos_kernel(DiagLaunch D) {
   extern __shared__ float sh[];
   const int sp = D.s_pad, s = D.s;
   float* q = sh;                 // [sp]
@@ -178,8 +230,9 @@ __global__ void __launch_bounds__(512) diag_lanczos_kernel(DiagLaunch D) {
   float* al = qp + sp;           // [kmax] alphas
   float* be = al + D.kmax;       // [kmax] betas (be[j] couples j-1, j)
   float* cf = be + D.kmax;       // [kmax] reorthogonalisation coefficients
-  __shared__ float red[8];
-  __shared__ double redd[8];
+  float* mvp = cf + D.kmax;      // [splits][sp] matrix-vector partials
+  __shared__ float red[16];
+  __shared__ double redd[16];
   const long long z = blockIdx.x;
   const float* H = D.H + z * D.hstride;
   float* Q = D.Q + z * D.qstride;
@@ -225,20 +278,7 @@ __global__ void __launch_bounds__(512) diag_lanczos_kernel(DiagLaunch D) {
   float beta = 0.0f;
   int kk = k;
   for (int j = 0; j < k; ++j) {
-    // w = H q
-    for (int r = wv; r < sp; r += nw) {
-      const float* row = H + static_cast<long long>(r) * sp;
-      float d = 0.0f;
-      if (r < s) {
-        for (int c = lane * 4; c < sp; c += 256) {
-          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + c);
-          d = fmaf(v[0], q[c], fmaf(v[1], q[c + 1], fmaf(v[2], q[c + 2], fmaf(v[3], q[c + 3], d))));
-        }
-        d = wave_sum(d);
-      }
-      if (lane == 0) w[r] = d;
-    }
-    __syncthreads();
+    sym_matvec(H, s, sp, q, w, mvp);
     const float hq = scaled_norm(w, sp, red);  // ||H q||: the scale of a residual taken as zero
     part = 0.0f;
     for (int i = tid; i < sp; i += nthr) part = fmaf(q[i], w[i], part);
@@ -327,12 +367,18 @@ hipError_t launch_diag_pack(const DiagPackLaunch& P, hipStream_t st) {
   return hipGetLastError();
 }
 
-size_t diag_lanczos_lds(int s_pad, int kmax) { return (3 * static_cast<size_t>(s_pad) + 3 * kmax) * sizeof(float); }
+namespace {
+int lanczos_threads(int s_pad) { return s_pad <= 256 ? 256 : 1024; }
+}  // namespace
+
+size_t diag_lanczos_lds(int s_pad, int kmax) {
+  const int splits = sym_matvec_splits(s_pad, lanczos_threads(s_pad) / 64);
+  return ((3 + static_cast<size_t>(splits)) * s_pad + 3 * static_cast<size_t>(kmax)) * sizeof(float);
+}
 
 hipError_t launch_diag_lanczos(const DiagLaunch& D, hipStream_t st) {
   if (D.count == 0) return hipSuccess;
-  const int threads = D.s_pad <= 256 ? 256 : 512;
-  hipLaunchKernelGGL(diag_lanczos_kernel, dim3(static_cast<unsigned>(D.count)), dim3(threads),
+  hipLaunchKernelGGL(diag_lanczos_kernel, dim3(static_cast<unsigned>(D.count)), dim3(lanczos_threads(D.s_pad)),
                      diag_lanczos_lds(D.s_pad, D.kmax), st, D);
   return hipGetLastError();
 }

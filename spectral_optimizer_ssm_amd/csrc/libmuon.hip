@@ -967,12 +967,15 @@ size_t muon_spectral_diag_workspace_size(int m, int n, long long batch, int dtyp
   return batch == 0 ? kAlign : p.end;
 }
 
-int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,
-                       float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes, void* stream) {
+int muon_spectral_diag_timed(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,
+                             float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes,
+                             void* stream, void** events, int nevents) {
   DiagPlan p;
   const int rc = plan_diag(m, n, batch, dtype, iters, &p);
   if (rc != MUON_OK) return rc;
   if (batch == 0 || (orth_err == nullptr && sigma_max == nullptr && sigma_min == nullptr)) return MUON_OK;
+  const long long chunks = (batch + p.chunk - 1) / p.chunk;
+  if (events != nullptr && nevents < 1 + 3 * chunks) return MUON_EINVAL;
   const size_t es = dtype_size(dtype);
   if (A == nullptr || !aligned_to(A, es)) return MUON_EINVAL;
   const char* ab = static_cast<const char*>(A);
@@ -989,6 +992,11 @@ int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, 
   bf16_t* R = p.f32 ? reinterpret_cast<bf16_t*>(ws + p.off_r) : nullptr;
   float* H = reinterpret_cast<float*>(ws + p.off_h);
   float* Q = reinterpret_cast<float*>(ws + p.off_q);
+  int ev = 0;
+  auto mark = [&]() {
+    return events == nullptr || hipEventRecord(static_cast<hipEvent_t>(events[ev++]), st) == hipSuccess;
+  };
+  if (!mark()) return MUON_EHIP;
   for (long long c0 = 0; c0 < batch; c0 += p.chunk) {
     const long long cnt = std::min(p.chunk, batch - c0);
     DiagPackLaunch P{};
@@ -1000,7 +1008,7 @@ int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, 
     P.ostride = static_cast<long long>(p.op_bytes / 2);
     P.s_pad = p.s_pad; P.kdim = p.kdim; P.ld = p.ld;
     P.count = cnt;
-    if (launch_diag_pack(P, st) != hipSuccess) return MUON_EHIP;
+    if (launch_diag_pack(P, st) != hipSuccess || !mark()) return MUON_EHIP;
     SymArgs G{};
     SymSeg& S = G.seg[0];
     G.nseg = 1;
@@ -1015,7 +1023,7 @@ int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, 
     S.count = static_cast<int>(cnt);
     S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);
     S.a1 = 0.0f; S.b1 = 1.0f;
-    if (launch_symprod_bf16(G, st) != hipSuccess) return MUON_EHIP;
+    if (launch_symprod_bf16(G, st) != hipSuccess || !mark()) return MUON_EHIP;
     DiagLaunch D{};
     D.H = H;
     D.hstride = S.stride;
@@ -1026,9 +1034,15 @@ int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, 
     D.smax = sigma_max ? sigma_max + c0 : nullptr;
     D.smin = sigma_min ? sigma_min + c0 : nullptr;
     D.count = cnt;
-    if (launch_diag_lanczos(D, st) != hipSuccess) return MUON_EHIP;
+    if (launch_diag_lanczos(D, st) != hipSuccess || !mark()) return MUON_EHIP;
   }
   return MUON_OK;
+}
+
+int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,
+                       float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes, void* stream) {
+  return muon_spectral_diag_timed(A, dtype, m, n, batch, iters, orth_err, sigma_max, sigma_min, workspace,
+                                  workspace_bytes, stream, nullptr, 0);
 }
 
 int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long long batch, const muon_ns_cfg* cfg,

@@ -308,3 +308,12 @@ def test_spectral_diag_workspace_sizes(mu):
     # chunked: the size stops growing once a chunk is full
     big = L.muon_spectral_diag_workspace_size(64, 128, 393216, mu.MUON_BF16, 64)
     assert big <= 2 ** 31 and big == L.muon_spectral_diag_workspace_size(64, 128, 2 * 393216, mu.MUON_BF16, 64)
+
+
+def test_spectral_diag_timed_needs_enough_events(mu):
+    L = mu.lib()
+    ws = L.muon_spectral_diag_workspace_size(96, 200, 3, mu.MUON_BF16, 16)
+    ev = (ctypes.c_void_p * 3)()
+    rc = L.muon_spectral_diag_timed(0x1000000, mu.MUON_BF16, 96, 200, 3, 16, 0x2000000, None, None, 0x40000000, ws,
+                                    None, ev, 3)
+    assert rc == -1  # one chunk needs 1 + 3 events

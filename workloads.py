@@ -292,3 +292,13 @@ def adamw_state(shapes, seed: int = 6, grad_dtype: str = "bf16", step: int = 3):
         M.append((0.1 * rng.standard_normal(n)).astype(np.float32))
         V.append((0.01 * rng.standard_normal(n) ** 2).astype(np.float32))
     return P, G, M, V
+
+
+def projection_stacks(count: int = N_LAYERS, seed: int = 5):
+    """The full step's two projection shapes as float32 stacks drawn N(0, 1)
+    (numpy default_rng(seed), out_proj first): [("out_proj", [count, 768,
+    1536]), ("in_proj", [count, 3352, 768])].  Scaled by 0.02 they are the
+    weights W of the full step; as bf16 they serve as gradients."""
+    rng = np.random.default_rng(seed)
+    return [(name, rng.standard_normal((count, *shape), dtype=np.float32))
+            for name, shape in (("out_proj", OUT_PROJ), ("in_proj", IN_PROJ))]
