@@ -210,7 +210,7 @@ def bench_full_step(args, torch, mu, wl):
             gi_a += 1
         elif ph == "gram":
             work.append(gram_f)
-        elif ph == "combine":
+        elif ph in ("combine", "combine_apply"):
             work.append(comb_f)
         elif ph == "symprod":
             work.append(sym_products[si] * sym_f)
@@ -239,7 +239,12 @@ def bench_full_step(args, torch, mu, wl):
             kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "flops_per_launch": tot_w / n,
                              "tflops": rate / 1e12, "frac": rate / 1e12 / PEAK_BF16_TFLOPS}
         kernels[kind]["ms_per_step"] = tot_ms / args.steps
-    ns_kinds = [k for k in ("gram", "symprod", "combine") if k in dur]
+    if "combine_apply" in kernels:  # the fused apply's bytes: X read, W read and written
+        nel = sum(g.count * g.m * g.n for g, s, l in per_group)
+        ca = kernels["combine_apply"]
+        ca["apply_bytes_per_launch"] = nel * 10
+        ca["apply_gbs"] = nel * 10 / (ca["avg_us"] * 1e-6) / 1e9
+    ns_kinds = [k for k in ("gram", "symprod", "combine", "combine_apply") if k in dur]
     ns_ms = sum(sum(d for d, _ in dur[k]) for k in ns_kinds) / args.steps
     ns_flops_step = sum(sum(wk for _, wk in dur[k]) for k in ns_kinds) / args.steps
     ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
@@ -247,10 +252,11 @@ def bench_full_step(args, torch, mu, wl):
     iter_flops_step = sum(sum(ns_flops(s, l)) * g.count for g, s, l in per_group) * steps_ns
 
     # dominant kernel: the one with the most GPU time per step
-    dom = max(ns_kinds + ["momentum", "apply"], key=lambda k: kernels[k]["ms_per_step"])
+    dom = max(ns_kinds + [k for k in ("momentum", "apply") if k in kernels], key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
     names = {"gram": "symprod_bf16_kernel", "combine": "combine_bf16_kernel", "symprod": "symprod_bf16_kernel",
-             "momentum": "momentum_*_kernel", "apply": "apply_*_kernel"}
+             "combine_apply": "combine_bf16_kernel<fused apply>", "momentum": "momentum_*_kernel",
+             "apply": "apply_*_kernel"}
     if dom in ("momentum", "apply"):
         roofline = {"bound": "hbm", "kernel": names[dom], "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(kd["frac"], 4), "traffic": None}

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 5
+#define MUON_VERSION 6
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -103,6 +103,12 @@ typedef enum { MUON_NS_AUTO = 0, MUON_NS_ITERATE = 1, MUON_NS_ACCUMULATE = 2 } m
  *             device on first use (joined back into `stream` before the call
  *             returns); 1 uses `stream` alone.  muon_step_timed always uses
  *             `stream` alone.
+ *   separate_apply  0: the final matrix product of a large bfloat16 group
+ *             also applies the update (W -= lr scale O from the bf16-rounded
+ *             product, and the copy to O) in its epilogue, so the update is
+ *             never stored and re-read; groups with the spectral cap, or
+ *             beyond 64 matrices in one launch, keep a separate pass.  1:
+ *             always a separate apply pass.  The results are bitwise equal.
  * Quintic c != 0 runs on large bfloat16 matrices (the matrix-core path: one
  * more s x s product per step) and in muon_ns_factored; with float32
  * precision, on small (on-chip) matrices and in muon_ns_batched_small it
@@ -116,6 +122,7 @@ typedef struct {
   int precision;
   int schedule;
   int streams;
+  int separate_apply;
 } muon_ns_cfg;
 
 /* One parameter group of `count` same-shape m x n matrices (the pages group
@@ -179,7 +186,8 @@ typedef enum {
   MUON_PHASE_F32_GRAM = 7,    /* Gram of one float32 group */
   MUON_PHASE_F32_COMBINE = 8, /* combine of one float32 group */
   MUON_PHASE_CAP = 9,         /* spectral-cap coefficient u^T O v of one group */
-  MUON_PHASE_POWER = 10       /* power step on one group's updated weights */
+  MUON_PHASE_POWER = 10,      /* power step on one group's updated weights */
+  MUON_PHASE_COMBINE_APPLY = 11 /* final grouped combine with the apply fused (large bf16 matrices) */
 } muon_phase;
 
 /* The phases muon_step would run for these groups and cfg, in order: returns

@@ -17,7 +17,7 @@ MUON_F32, MUON_BF16 = 0, 1
 MUON_OK, MUON_EINVAL, MUON_EUNSUPPORTED, MUON_EWORKSPACE, MUON_EHIP = 0, -1, -2, -3, -4
 MUON_NS_AUTO, MUON_NS_ITERATE, MUON_NS_ACCUMULATE = 0, 1, 2
 PHASES = {1: "momentum", 2: "ns_small", 3: "gram", 4: "combine", 5: "symprod", 6: "apply", 7: "f32_gram",
-          8: "f32_combine", 9: "cap", 10: "power"}
+          8: "f32_combine", 9: "cap", 10: "power", 11: "combine_apply"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmuon.so")
@@ -34,7 +34,7 @@ class NsCfg(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int), ("ncoef", ctypes.c_int),
                 ("coeffs", ctypes.POINTER(ctypes.c_float)), ("per_step", ctypes.c_int),
                 ("eps", ctypes.c_float), ("precision", ctypes.c_int), ("schedule", ctypes.c_int),
-                ("streams", ctypes.c_int)]
+                ("streams", ctypes.c_int), ("separate_apply", ctypes.c_int)]
 
 
 class GroupC(ctypes.Structure):
@@ -133,13 +133,14 @@ def _stream_handle(stream=None) -> Optional[int]:
 
 
 def make_cfg(steps: int = 5, coeffs=(1.5, -0.5), eps: float = 1e-7, precision: int = MUON_BF16,
-             per_step: bool = False, schedule: int = MUON_NS_AUTO, streams: int = 0):
+             per_step: bool = False, schedule: int = MUON_NS_AUTO, streams: int = 0, separate_apply: int = 0):
     """NsCfg plus the float array it points to (keep both alive)."""
     flat = [float(c) for row in coeffs for c in (row if isinstance(row, (tuple, list)) else (row,))]
     ncoef = len(coeffs[0]) if per_step else len(coeffs)
     arr = (ctypes.c_float * max(1, len(flat)))(*flat)
     cfg = NsCfg(int(steps), int(ncoef), ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)),
-                int(bool(per_step)), float(eps), int(precision), int(schedule), int(streams))
+                int(bool(per_step)), float(eps), int(precision), int(schedule), int(streams),
+                int(separate_apply))
     return cfg, arr
 
 
@@ -225,12 +226,12 @@ def muon_step_workspace_size(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, 
 
 
 def muon_step_phases(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7, precision=MUON_BF16,
-                     per_step=False, schedule=MUON_NS_AUTO) -> list:
+                     per_step=False, schedule=MUON_NS_AUTO, separate_apply=0) -> list:
     """Names of the phases muon_step runs for these groups, in order (the
     intervals between the events muon_step_timed records)."""
     L = lib()
     cg, keep = _marshal_groups(groups)
-    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule, separate_apply=separate_apply)
     n = int(L.muon_step_phases(cg, len(groups), ctypes.byref(cfg), None, 0))
     if n < 0:
         _check(n, "muon_step_phases")
@@ -241,7 +242,7 @@ def muon_step_phases(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), e
 
 def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7, precision=MUON_BF16,
               per_step=False, workspace=None, norms_out=None, stream=None, events=None, schedule=MUON_NS_AUTO,
-              streams=0):
+              streams=0, separate_apply=0):
     """One Muon step over every group (W and M updated in place).  Returns the
     workspace tensor so that callers can reuse it.  `events`: optional list of
     raw hipEvent_t handles (ints); when given, muon_step_timed records them at
@@ -249,7 +250,7 @@ def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7
     import torch
     L = lib()
     cg, keep = _marshal_groups(groups)
-    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule, streams)
+    cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule, streams, separate_apply)
     need = int(L.muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
     if need == 0:  # the size query has no status: ask the step itself, which validates first
         rc = L.muon_step(cg, len(groups), ctypes.byref(cfg), None, 0, None, None)

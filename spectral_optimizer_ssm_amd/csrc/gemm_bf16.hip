@@ -394,8 +394,68 @@ __device__ __forceinline__ void upper_tile(int t, int nt, int& bi, int& bj) {
   bj = bi + t;
 }
 
+// Fused apply of a staged bf16 tile (rows i0 + 64 p + r, columns k0 + 8 c ..
+// of the oriented iterate, a wide matrix: W and O rows are iterate rows):
+// W = fmaf(nls, o, W) and O = o, 8 elements per chunk.  Each half of the
+// thread's 16 chunks loads all its W values before the first store (W and O
+// might alias as far as the compiler knows, so it would not reorder them).
+__device__ __forceinline__ void slabs_apply(const Bufs& bufs, float* W, bf16_t* O, long long n, int i0, int k0,
+                                            int s, int l, float nls) {
+  const bool wvec = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(W) & 15u) == 0;
+  const bool ovec = (n % 8) == 0 && (reinterpret_cast<uintptr_t>(O) & 15u) == 0;
+  const bool full = k0 + 256 <= l && i0 + 256 <= s && (W == nullptr || wvec) && (O == nullptr || ovec);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4_t v[8];
+    f32x4_t w[8][2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int p = half * 2 + (t >> 2), u = t & 3;
+      const int q = threadIdx.x + NTHR * u;
+      const int r = q >> 5, c = q & 31;
+      v[t] = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
+      if (full && W != nullptr) {
+        const long long off = static_cast<long long>(i0 + p * 64 + r) * n + k0 + c * 8;
+        w[t][0] = *reinterpret_cast<const f32x4_t*>(W + off);
+        w[t][1] = *reinterpret_cast<const f32x4_t*>(W + off + 4);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int p = half * 2 + (t >> 2), u = t & 3;
+      const int q = threadIdx.x + NTHR * u;
+      const int r = q >> 5, c = q & 31;
+      const int i = i0 + p * 64 + r, k = k0 + c * 8;
+      const long long off = static_cast<long long>(i) * n + k;
+      if (full) {
+        if (O != nullptr) *reinterpret_cast<u32x4_t*>(O + off) = v[t];
+        if (W != nullptr) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            w[t][0][2 * h] = fmaf(nls, lo_bf16(v[t][h]), w[t][0][2 * h]);
+            w[t][0][2 * h + 1] = fmaf(nls, hi_bf16(v[t][h]), w[t][0][2 * h + 1]);
+            w[t][1][2 * h] = fmaf(nls, lo_bf16(v[t][2 + h]), w[t][1][2 * h]);
+            w[t][1][2 * h + 1] = fmaf(nls, hi_bf16(v[t][2 + h]), w[t][1][2 * h + 1]);
+          }
+          *reinterpret_cast<f32x4_t*>(W + off) = w[t][0];
+          *reinterpret_cast<f32x4_t*>(W + off + 4) = w[t][1];
+        }
+      } else if (i < s) {  // edge tiles: element by element within the matrix
+        for (int e = 0; e < 8 && k + e < l; ++e) {
+          const uint32_t word = v[t][e >> 1];
+          const float o = (e & 1) ? hi_bf16(word) : lo_bf16(word);
+          if (O != nullptr) O[off + e] = static_cast<bf16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
+          if (W != nullptr) W[off + e] = fmaf(nls, o, W[off + e]);
+        }
+      }
+    }
+  }
+}
+
 // ---- combine: Y = A' X --------------------------------------------------------
 // D[k][i] = sum_j X[j][k] A'[i][j] = (A' X)[i][k]
+// FUSE: the apply is fused into the epilogue (GemmSeg.fuse).
+template <bool FUSE>
 __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
   __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
   __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
@@ -450,6 +510,51 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
   stage_sync<0>();
   const int lane_e = opaque(lane);
   const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;  // buffers and rows below are uniform per wave
+  float* Wz = nullptr;
+  bf16_t* Oz = nullptr;
+  if constexpr (FUSE) {
+    Wz = static_cast<float*>(G.W.p[S.tab0 + z]);
+    Oz = static_cast<bf16_t*>(G.O.p[S.tab0 + z]);
+    if (S.tall) {
+      // W (l x s) row k holds the iterate's column k: the 32 lanes of a half
+      // wave own 32 consecutive i at each of their 4 k, so every access below
+      // covers two 128-byte row segments
+      // (per 32 x 32 block: its 16 W loads before any of its stores)
+      const float nls = S.neg_lr_scale;
+      const bool full = (ti + 1) * T <= S.s && (tk + 1) * T <= S.l;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int gi = ti * T + wn * CN + j * 32 + col;
+          const float* wcol = Wz + gi;
+          float wv[16];
+          if (full && Wz != nullptr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                wv[4 * q + r] = wcol[static_cast<long long>(tk * T + wm * CM + i * 32 + q * 8 + rq + r) * S.n];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int gk = tk * T + wm * CM + i * 32 + q * 8 + rq + r;
+              const bf16_t ob = f32_to_bf16(acc.c[i][j][4 * q + r]);
+              const long long off = static_cast<long long>(gk) * S.n + gi;
+              if (full) {
+                if (Oz != nullptr) Oz[off] = ob;
+                if (Wz != nullptr) Wz[off] = fmaf(nls, bf16_to_f32(ob), wv[4 * q + r]);
+              } else if (gi < S.s && gk < S.l) {
+                if (Oz != nullptr) Oz[off] = ob;
+                if (Wz != nullptr) Wz[off] = fmaf(nls, bf16_to_f32(ob), Wz[off]);
+              }
+            }
+        }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -465,7 +570,8 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
     }
   }
   __syncthreads();
-  slabs_to_global(bufs, Y + static_cast<long long>(ti) * T * S.ld + tk * T, S.ld);
+  if constexpr (FUSE) slabs_apply(bufs, Wz, Oz, S.n, ti * T, tk * T, S.s, S.l, S.neg_lr_scale);
+  else slabs_to_global(bufs, Y + static_cast<long long>(ti) * T * S.ld + tk * T, S.ld);
 }
 
 // ---- symmetric products: O = alpha I + beta L R ----------------------------------
@@ -750,11 +856,24 @@ hipError_t launch_symprod_bf16(const SymArgs& G, hipStream_t st) {
   return e;
 }
 
+// Segments with and without the fused apply go to separate launches.
 hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st) {
-  const int grid = grid_for(G);
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid), dim3(NTHR), 0, st, G);
-  return hipGetLastError();
+  GemmArgs part[2] = {};
+  for (int s = 0; s < G.nseg; ++s) {
+    GemmArgs& P = part[G.seg[s].fuse ? 1 : 0];
+    P.seg[P.nseg++] = G.seg[s];
+  }
+  part[1].W = G.W;
+  part[1].O = G.O;
+  for (int f = 0; f < 2; ++f) {
+    const int grid = grid_for(part[f]);
+    if (grid == 0) continue;
+    if (f) hipLaunchKernelGGL(combine_bf16_kernel<true>, dim3(grid), dim3(NTHR), 0, st, part[f]);
+    else hipLaunchKernelGGL(combine_bf16_kernel<false>, dim3(grid), dim3(NTHR), 0, st, part[f]);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace muon

@@ -112,10 +112,20 @@ struct GemmSeg {
   float eps;
   float a, b, a2, b2;
   int pa, pb;
+  // Combine with the apply fused (the final product of the iteration): Y is
+  // not written; with o the bf16 rounding of the result at (i, k) of the
+  // oriented iterate (i < s, k < l), matrix z of the segment updates
+  // W = GemmArgs.W[tab0 + z] (m x n float32, entry (i, k) wide, (k, i) tall)
+  // to fmaf(neg_lr_scale, o, W) and stores o to GemmArgs.O[tab0 + z]
+  // (m x n bf16); null table entries skip that output.
+  int fuse;
+  int tab0, m, n, s, l, tall;
+  float neg_lr_scale;
 };
 struct GemmArgs {
   GemmSeg seg[kMaxSeg];
   int nseg;
+  MutPtrTable W, O;    // fused apply: per-matrix outputs of the segments
 };
 int combine_tiles_per_matrix(int s_pad, int ld);
 hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st);

@@ -38,6 +38,7 @@ struct NsCoefs {
   int steps;
   int schedule;
   bool quintic;  // some step has c != 0
+  bool separate_apply;
   float a[kMaxSteps], b[kMaxSteps], c[kMaxSteps];
 };
 
@@ -51,9 +52,11 @@ int parse_cfg(const muon_ns_cfg* cfg, NsCoefs* out, bool quintic = false) {
   if (cfg->schedule != MUON_NS_AUTO && cfg->schedule != MUON_NS_ITERATE && cfg->schedule != MUON_NS_ACCUMULATE)
     return MUON_EINVAL;
   if (cfg->streams != 0 && cfg->streams != 1) return MUON_EINVAL;
+  if (cfg->separate_apply != 0 && cfg->separate_apply != 1) return MUON_EINVAL;
   if (cfg->steps > 0 && cfg->coeffs == nullptr) return MUON_EINVAL;
   out->steps = cfg->steps;
   out->schedule = cfg->schedule;
+  out->separate_apply = cfg->separate_apply != 0;
   out->quintic = false;
   for (int k = 0; k < cfg->steps; ++k) {
     const float* row = cfg->coeffs + (cfg->per_step ? k * cfg->ncoef : 0);
@@ -351,6 +354,51 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     S.b1 = 1.0f;
     return S;
   };
+  // The final combine of a group also applies its update when nothing else
+  // needs the final iterate (no spectral cap); the W and O tables of one
+  // launch hold at most kMaxTable matrices.
+  std::vector<char> fused(runs.size(), 0);
+  auto decide_fused = [&](const std::vector<int>& order) {
+    for (size_t c0 = 0; c0 < order.size(); c0 += kMaxSeg) {
+      int tab = 0;
+      for (size_t i = c0; i < std::min(order.size(), c0 + kMaxSeg); ++i) {
+        const GroupRun& R = runs[order[i]];
+        const bool ok = !C.separate_apply && !R.plan.cap && (R.W != nullptr || R.O != nullptr) &&
+                        tab + R.plan.count <= kMaxTable;
+        fused[order[i]] = ok;
+        if (ok) tab += R.plan.count;
+      }
+    }
+  };
+  auto final_combine = [&](std::vector<GemmSeg>& cs, const std::vector<int>& order) {
+    bool any = false;
+    for (size_t c0 = 0; c0 < cs.size(); c0 += kMaxSeg) {
+      GemmArgs G{};
+      G.nseg = static_cast<int>(std::min<size_t>(kMaxSeg, cs.size() - c0));
+      int tab = 0;
+      for (int i = 0; i < G.nseg; ++i) {
+        GemmSeg S = cs[c0 + i];
+        const GroupRun& R = runs[order[c0 + i]];
+        const GroupPlan& p = R.plan;
+        if (fused[order[c0 + i]]) {
+          any = true;
+          S.fuse = 1;
+          S.Y = nullptr;
+          S.tab0 = tab;
+          S.m = p.m; S.n = p.n; S.s = p.s; S.l = p.l; S.tall = p.tall;
+          S.neg_lr_scale = R.neg_lr_scale;
+          for (int z = 0; z < p.count; ++z) {
+            G.W.p[tab + z] = R.W ? R.W[z] : nullptr;
+            G.O.p[tab + z] = R.O ? R.O[z] : nullptr;
+          }
+          tab += p.count;
+        }
+        G.seg[i] = S;
+      }
+      if (E.live() && launch_combine_bf16(G, st) != hipSuccess) return false;
+    }
+    return E.mark(st, any ? MUON_PHASE_COMBINE_APPLY : MUON_PHASE_COMBINE);
+  };
   if (!it.empty() && C.steps > 0) {
     // per step: A' = a I + b X X^T (step 1 on the unnormalised U, with the
     // normalisation folded into the coefficients), then X = A' X.  Quintic:
@@ -398,8 +446,13 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       if (C.quintic &&
           (!launch_segments<SymArgs>(ps, launch_symprod_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_SYMPROD)))
         return MUON_EHIP;
-      if (!launch_segments<GemmArgs>(cs, launch_combine_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_COMBINE))
-        return MUON_EHIP;
+      if (k + 1 < C.steps) {
+        if (!launch_segments<GemmArgs>(cs, launch_combine_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_COMBINE))
+          return MUON_EHIP;
+      } else {
+        decide_fused(by_s);
+        if (!final_combine(cs, by_s)) return MUON_EHIP;
+      }
     }
     for (int gi : it) fin[gi] = C.steps & 1;
   }
@@ -498,8 +551,8 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       S.A = sq_of(p, ws, kSqQ0 + (n & 1));
       cs.push_back(S);
     }
-    if (!launch_segments<GemmArgs>(cs, launch_combine_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_COMBINE))
-      return MUON_EHIP;
+    decide_fused(by_s);
+    if (!final_combine(cs, by_s)) return MUON_EHIP;
     for (int gi : ac) fin[gi] = 1;
   }
 
@@ -530,7 +583,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
   for (size_t gi = 0; gi < runs.size(); ++gi) {
     const GroupRun& R = runs[gi];
     const GroupPlan& p = R.plan;
-    if (p.count == 0) continue;
+    if (p.count == 0 || fused[gi]) continue;
     const long long xs = static_cast<long long>(p.s_pad) * p.ld;
     if (p.cap) {
       for (int c0 = 0; E.live() && c0 < p.count; c0 += kMaxTable) {
@@ -808,6 +861,8 @@ int muon_step_phases(const muon_group* groups, int ngroups, const muon_ns_cfg* c
     if (rc != MUON_OK) return rc;
     off = runs[i].plan.end;
     runs[i].grad_dtype = groups[i].grad_dtype;
+    runs[i].W = groups[i].W;  // host arrays: which outputs exist decides the final passes
+    runs[i].O = groups[i].O;
   }
   const std::vector<int> marks = list_phases(runs, C, cfg->eps);
   const int n = static_cast<int>(marks.size()) - 1;

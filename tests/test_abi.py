@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 5
+    assert mu.muon_version() == 6
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -85,7 +85,7 @@ def test_workspace_queries(mu):
     ("steps_negative", -1), ("steps_too_many", -1), ("ncoef_4", -1), ("quintic_c", -2),
     ("bad_precision", -1), ("null_groups", -1), ("misaligned", -1), ("null_matrix", -1),
     ("no_workspace", -3), ("small_workspace", -3), ("bad_dtype", -1), ("negative_eps", -1),
-    ("bad_schedule", -1), ("bad_streams", -1),
+    ("bad_schedule", -1), ("bad_streams", -1), ("bad_separate_apply", -1),
 ])
 def test_step_validation(mu, case, expect):
     L = mu.lib()
@@ -99,6 +99,8 @@ def test_step_validation(mu, case, expect):
         cfg.schedule = 3
     if case == "bad_streams":
         cfg.streams = 2
+    if case == "bad_separate_apply":
+        cfg.separate_apply = 3
     g, k2 = _group(mu, dtype=5 if case == "bad_dtype" else None)
     if case == "misaligned":
         k2[0][0] = 0x100002  # W is float32: 4-byte alignment required
@@ -127,9 +129,10 @@ def test_small_and_ns_validation(mu):
     assert L.muon_ns_orthogonalize(x, y, mu.MUON_BF16, 64, 128, 0, ctypes.byref(cfg), None, 0, None) == 0
 
 
-def _phases(mu, shapes, steps, schedule, prec=None):
+def _phases(mu, shapes, steps, schedule, prec=None, separate_apply=0):
     L = mu.lib()
-    cfg, keep = mu.make_cfg(steps, (1.5, -0.5), 1e-7, mu.MUON_BF16 if prec is None else prec, False, schedule)
+    cfg, keep = mu.make_cfg(steps, (1.5, -0.5), 1e-7, mu.MUON_BF16 if prec is None else prec, False, schedule,
+                            separate_apply=separate_apply)
     gs = [_group(mu, m, n, c) for m, n, c in shapes]
     arr = (mu.binding.GroupC * len(gs))(*[g for g, _ in gs])
     n = L.muon_step_phases(arr, len(gs), ctypes.byref(cfg), None, 0)
@@ -142,16 +145,23 @@ MAMBA = [(768, 1536, 24), (3352, 768, 24)]
 
 
 def test_phases_iterate_and_accumulate(mu):
+    # the final combine applies the update of the large bf16 groups itself
     it = _phases(mu, MAMBA, 5, mu.MUON_NS_ITERATE)
-    assert it == ["momentum"] * 2 + ["gram", "combine"] * 5 + ["apply"] * 2
+    assert it == ["momentum"] * 2 + ["gram", "combine"] * 4 + ["gram", "combine_apply"]
     ac = _phases(mu, MAMBA, 5, mu.MUON_NS_ACCUMULATE)
-    assert ac == ["momentum"] * 2 + ["gram"] + ["symprod"] * 9 + ["combine"] + ["apply"] * 2
+    assert ac == ["momentum"] * 2 + ["gram"] + ["symprod"] * 9 + ["combine_apply"]
+    assert _phases(mu, MAMBA, 5, mu.MUON_NS_ACCUMULATE, separate_apply=1) == \
+        ["momentum"] * 2 + ["gram"] + ["symprod"] * 9 + ["combine"] + ["apply"] * 2
     # the Mamba-2 projections are wide enough for the accumulated schedule to
     # need fewer matrix-core operations; a square group is not
     assert _phases(mu, MAMBA, 5, mu.MUON_NS_AUTO) == ac
-    assert _phases(mu, [(768, 768, 4)], 5, mu.MUON_NS_AUTO) == ["momentum"] + ["gram", "combine"] * 5 + ["apply"]
+    assert _phases(mu, [(768, 768, 4)], 5, mu.MUON_NS_AUTO) == \
+        ["momentum"] + ["gram", "combine"] * 4 + ["gram", "combine_apply"]
+    # more than 64 matrices in one final launch: the first group fuses, the next keeps its apply pass
+    assert _phases(mu, [(768, 1536, 40), (3352, 768, 40)], 5, mu.MUON_NS_ACCUMULATE)[-2:] == \
+        ["combine_apply", "apply"]
     # one step, float32 and small matrices always iterate
-    assert _phases(mu, MAMBA, 1, mu.MUON_NS_ACCUMULATE) == ["momentum"] * 2 + ["gram", "combine"] + ["apply"] * 2
+    assert _phases(mu, MAMBA, 1, mu.MUON_NS_ACCUMULATE) == ["momentum"] * 2 + ["gram", "combine_apply"]
     assert _phases(mu, [(300, 700, 2)], 2, mu.MUON_NS_ACCUMULATE, mu.MUON_F32) == \
         ["momentum", "f32_gram", "f32_combine", "f32_gram", "f32_combine", "apply"]
     assert _phases(mu, [(64, 128, 9)], 3, mu.MUON_NS_ACCUMULATE) == ["momentum", "ns_small", "apply"]

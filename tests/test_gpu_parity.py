@@ -408,3 +408,38 @@ def test_two_stream_chains_match_one_stream(mu):
     for gi, g in enumerate(w.groups):
         U = orc.update_direction(grad64(g, 1), orc.momentum(orc.widen_f32(g.M[1]), grad64(g, 1), 0.95), 0.95, True)
         assert abs(n2[3 * gi + 1].item() - np.linalg.norm(U)) <= 1e-5 * np.linalg.norm(U)
+
+
+@pytest.mark.parametrize("shapes,schedule", [
+    ([(768, 1536, 3), (3352, 768, 3)], "accumulate"),   # the Mamba-2 projections
+    ([(768, 1536, 2), (3352, 768, 2)], "iterate"),
+    ([(200, 516, 3)], "iterate"),                        # ragged wide, n % 8 != 0: unvectorised edge
+    ([(516, 200, 3)], "accumulate"),                     # ragged tall
+    ([(260, 1000, 2), (1000, 260, 2)], "accumulate"),    # padded tiles on both sides
+])
+def test_fused_apply_matches_separate_pass(mu, shapes, schedule):
+    """The final combine applies the update in its epilogue (W, and the copy to
+    O); the separate apply pass gives bitwise the same W, M and O."""
+    sch = mu.MUON_NS_ACCUMULATE if schedule == "accumulate" else mu.MUON_NS_ITERATE
+    groups = [wl._group(70 + i, c, m, n, "gauss", f"g{i}") for i, (m, n, c) in enumerate(shapes)]
+    outs = []
+    for sep in (1, 0):
+        devs, gs = [], []
+        for g in groups:
+            d = device_group(g)
+            d["O"] = torch.full((g.count, g.m, g.n), float("nan"), dtype=torch.bfloat16, device="cuda")
+            devs.append(d)
+            gs.append(mu.MuonGroup(W=d["W"], M=d["M"], G=d["G"], O=d["O"], lr=0.02, beta=0.95))
+        assert mu.muon_step_phases(gs, steps=5, schedule=sch, separate_apply=sep)[-1] == \
+            ("apply" if sep else "combine_apply")
+        mu.muon_step(gs, steps=5, schedule=sch, separate_apply=sep)
+        torch.cuda.synchronize()
+        outs.append(devs)
+    for a, b in zip(*outs):
+        for key in ("W", "M", "O"):
+            assert torch.equal(a[key], b[key]), key
+    # and against the oracle on one matrix per group
+    for g, d in zip(groups, outs[1]):
+        ref = orc.muon_step(orc.widen_f32(g.W[0]), orc.widen_f32(g.M[0]), grad64(g, 0), beta=0.95, lr=0.02, steps=5)
+        assert orc.rel_frobenius(t64(d["O"][0]), ref["O"]) <= BF16_TOL
+        assert orc.rel_frobenius(t64(d["W"][0]) - orc.widen_f32(g.W[0]), ref["W"] - orc.widen_f32(g.W[0])) <= BF16_TOL
