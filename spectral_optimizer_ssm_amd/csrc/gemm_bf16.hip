@@ -23,15 +23,15 @@
 // padded rows of X are zero).  The Gram's contraction stops at kdim, the
 // first multiple of 64 >= l.
 //
-// Combine tiling: 256 x 256 workgroup tile, eight waves (two per SIMD) of
-// 64 x 128 made of 32 x 32 MFMA blocks.  The contraction runs in stages of
-// BK = 32 through NSTAGE = 4 LDS buffers of 32 KB: the fill of stage kt + 3
-// is issued while stage kt is multiplied, so three stages of loads are in
-// flight and an L2 miss to MALL or HBM does not stall the matrix pipes.
-// Fills use buffer_load ... lds (each lane's 16 bytes land at base + 16 *
-// lane; the per-lane source offset implements the swizzle).  Stage hand-over
-// is an explicit s_waitcnt vmcnt(<loads of younger stages>) + s_barrier,
-// because __syncthreads() would drain every outstanding fill.
+// Combine tiling: 128 (i) x 256 (k) workgroup tile, four waves of 64 x 128
+// made of 32 x 32 MFMA blocks, two workgroups per CU.  The contraction runs in
+// stages of BK = 32 through three LDS buffers of 24 KB: the fill of stage
+// kt + 2 is issued while stage kt is multiplied, so an L2 miss to MALL or HBM
+// does not stall the matrix pipes.  Fills use buffer_load ... lds (each
+// lane's 16 bytes land at base + 16 * lane; the per-lane source offset
+// implements the swizzle).  Stage hand-over is an explicit s_waitcnt
+// vmcnt(<loads of younger stages>) + s_barrier, because __syncthreads() would
+// drain every outstanding fill.
 //  * K-contiguous operands (rows of A' in the combine, both operands of the
 //    symmetric products) sit as [rows][32 K] (64-byte rows, 16-byte chunks
 //    XOR-swizzled by (row >> 2) & 3) and are read as ds_read_b128 fragments.
@@ -53,13 +53,8 @@
 namespace muon {
 namespace {
 
-constexpr int T = 256;            // workgroup tile (both dims)
 constexpr int BK = 32;            // K per LDS stage
 constexpr int KS = BK / 16;       // MFMA k-steps per stage
-constexpr int NSTAGE = 4;         // LDS buffers (NSTAGE - 1 stages in flight)
-constexpr int NWAVE = 8;          // two waves per SIMD
-constexpr int NTHR = NWAVE * 64;
-constexpr int OPB = T * BK * 2;   // bytes of one operand tile per stage (16 KB)
 constexpr int NXCD = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -93,8 +88,8 @@ __device__ __forceinline__ int row_voff(int ld_bytes) {
   return (lane >> 2) * ld_bytes + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
 }
 
-// 16 blocks of 1 KB per operand tile, two per wave.  soff0: byte offset of
-// (first row, first K of the stage).
+// Two 1 KB blocks (16 rows each) per wave: 128 rows with four waves.  soff0:
+// byte offset of (first row, first K of the stage).
 __device__ __forceinline__ void load_rows(char* op, __amdgpu_buffer_rsrc_t rsrc, int voff, int ld_bytes, int soff0) {
   const int w = wave_id();
 #pragma unroll
@@ -131,15 +126,6 @@ struct XOffs {
   }
 };
 
-__device__ __forceinline__ void load_xrows(char* op, __amdgpu_buffer_rsrc_t rsrc, const XOffs& o, int ld_bytes,
-                                           int soff0) {
-  const int w = wave_id();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = w * 2 + i;
-    dma16(rsrc, (i & 1) ? o.odd : o.even, soff0 + blk * 2 * ld_bytes, op + blk * 1024);
-  }
-}
 
 // MFMA operand with rows = columns 32 i .. 32 i + 31 of the wave's X columns
 // and the 16 contraction values j = 16 ks + 8 (lane / 32) + 0..7, from two
@@ -255,7 +241,6 @@ struct BufsN {
     else return p == 0 ? b[0] : p == 1 ? b[1] : p == 2 ? b[2] : b[3];
   }
 };
-using Bufs = BufsN<NSTAGE>;
 
 // The pipelined contraction: stages 0..nk-1 through N buffers, N - 1 fills in
 // flight.  fill(buf, kt) issues this wave's fills of stage kt, mma(buf)
@@ -289,11 +274,11 @@ __device__ __forceinline__ int opaque(int v) {
 }
 
 // ---- output staging ------------------------------------------------------------
-// A 256 x 256 bf16 output tile leaves through LDS as four 64-row slabs (one
-// per stage buffer, 512-byte rows, 16-byte chunks XOR-swizzled by row & 31),
-// so that global stores are whole rows: each wave instruction writes two
-// contiguous 512-byte rows.  (Stores of 8 bytes per lane scattered over 32
-// rows were not merged into full lines and cost more than the main loop.)
+// The combine's bf16 output tile leaves through LDS as 32-row slabs (512-byte
+// rows, 16-byte chunks XOR-swizzled by row & 31), so that global stores are
+// whole rows: each wave instruction writes two contiguous 512-byte rows.
+// (Stores of 8 bytes per lane scattered over 32 rows were not merged into
+// full lines and cost more than the main loop.)
 __device__ __forceinline__ int slab_off(int r, int col) {
   return r * 512 + ((((col >> 3) ^ (r & 31))) << 4) + (col & 7) * 2;
 }
@@ -308,25 +293,6 @@ __device__ __forceinline__ u32x4_t affine8(u32x4_t v, float a, float b, int dcol
     o[h] = pack_bf16x2(b * x0 + (dcol == 2 * h ? a : 0.0f), b * x1 + (dcol == 2 * h + 1 ? a : 0.0f));
   }
   return o;
-}
-
-// Copy the four staged slabs to dst rows (row stride ld elements), columns
-// col0 .. col0 + 255; when dst2 is non-null also dst2 = a2 I + b2 dst, taken
-// from the rounded values (the identity only on a diagonal tile, dg).
-__device__ __forceinline__ void slabs_to_global(const Bufs& bufs, bf16_t* dst, long long ld, bf16_t* dst2 = nullptr,
-                                                float a2 = 0.0f, float b2 = 0.0f, bool dg = false) {
-#pragma unroll
-  for (int p = 0; p < NSTAGE; ++p) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = threadIdx.x + NTHR * u;  // 2048 chunks of 16 B per slab
-      const int r = q >> 5, c = q & 31;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
-      const long long o = (static_cast<long long>(p * 64 + r)) * ld + c * 8;
-      *reinterpret_cast<u32x4_t*>(dst + o) = v;
-      if (dst2 != nullptr) *reinterpret_cast<u32x4_t*>(dst2 + o) = affine8(v, a2, b2, dg ? p * 64 + r - c * 8 : -1);
-    }
-  }
 }
 
 // ---- segment table ----------------------------------------------------------
@@ -394,89 +360,104 @@ __device__ __forceinline__ void upper_tile(int t, int nt, int& bi, int& bj) {
   bj = bi + t;
 }
 
-// Fused apply of a staged bf16 tile (rows i0 + 64 p + r, columns k0 + 8 c ..
-// of the oriented iterate, a wide matrix: W and O rows are iterate rows):
-// W = fmaf(nls, o, W) and O = o, 8 elements per chunk.  Each half of the
-// thread's 16 chunks loads all its W values before the first store (W and O
-// might alias as far as the compiler knows, so it would not reorder them).
-__device__ __forceinline__ void slabs_apply(const Bufs& bufs, float* W, bf16_t* O, long long n, int i0, int k0,
-                                            int s, int l, float nls) {
-  const bool wvec = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(W) & 15u) == 0;
-  const bool ovec = (n % 8) == 0 && (reinterpret_cast<uintptr_t>(O) & 15u) == 0;
-  const bool full = k0 + 256 <= l && i0 + 256 <= s && (W == nullptr || wvec) && (O == nullptr || ovec);
+// ---- combine: Y = A' X, 128 x 256 tiles ----------------------------------------
+// D[k][i] = sum_j X[j][k] A'[i][j] = (A' X)[i][k].  Four waves of 64 (k) x
+// 128 (i), three LDS stages of 24 KB (X rows j x 256 k and A' rows i x 32 K):
+// two workgroups share a CU.  The output leaves through 32-row slabs in two
+// rounds (rows 0..95 through the three buffers, then rows 96..127).
+// FUSE: the apply is fused into the epilogue (GemmSeg.fuse).
+constexpr int C2_TI = 128, C2_TK = 256, C2_NTHR = 256;
+constexpr int C2_OPX = BK * C2_TK * 2;      // 16 KB
+constexpr int C2_OPA = C2_TI * BK * 2;      // 8 KB
+constexpr int C2_STAGE = C2_OPX + C2_OPA;   // 24 KB
+
+// Copy NS staged 32-row slabs (bufs[p] holds tile rows 32 (j0 + p) + r) out:
+// to Y (row stride ldy) or, fused, into W and O of a wide matrix.
+template <int NS, bool FUSE>
+__device__ __forceinline__ void slabs32_out(const BufsN<3>& bufs, int j0, bf16_t* Y, long long ldy, float* W,
+                                            bf16_t* O, long long n, int i0, int k0, int s, int l, float nls) {
+  constexpr int PER = 32 * 32 / C2_NTHR;  // 16-byte chunks per thread per slab
+  const int tid = opaque(threadIdx.x);
+  if constexpr (!FUSE) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    u32x4_t v[8];
-    f32x4_t w[8][2];
+    for (int p = 0; p < NS; ++p)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int p = half * 2 + (t >> 2), u = t & 3;
-      const int q = threadIdx.x + NTHR * u;
-      const int r = q >> 5, c = q & 31;
-      v[t] = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
-      if (full && W != nullptr) {
-        const long long off = static_cast<long long>(i0 + p * 64 + r) * n + k0 + c * 8;
-        w[t][0] = *reinterpret_cast<const f32x4_t*>(W + off);
-        w[t][1] = *reinterpret_cast<const f32x4_t*>(W + off + 4);
+      for (int u = 0; u < PER; ++u) {
+        const int q = tid + C2_NTHR * u, r = q >> 5, c = q & 31;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
+        *reinterpret_cast<u32x4_t*>(Y + static_cast<long long>(i0 + (j0 + p) * 32 + r) * ldy + k0 + c * 8) = v;
       }
-    }
+  } else {
+    const bool full = i0 + (j0 + NS) * 32 <= s && k0 + C2_TK <= l && (W == nullptr || ((n % 4) == 0 &&
+                      (reinterpret_cast<uintptr_t>(W) & 15u) == 0)) &&
+                      (O == nullptr || ((n % 8) == 0 && (reinterpret_cast<uintptr_t>(O) & 15u) == 0));
+    u32x4_t v[NS][PER];
+    f32x4_t w[NS][PER][2];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int p = half * 2 + (t >> 2), u = t & 3;
-      const int q = threadIdx.x + NTHR * u;
-      const int r = q >> 5, c = q & 31;
-      const int i = i0 + p * 64 + r, k = k0 + c * 8;
-      const long long off = static_cast<long long>(i) * n + k;
-      if (full) {
-        if (O != nullptr) *reinterpret_cast<u32x4_t*>(O + off) = v[t];
-        if (W != nullptr) {
+    for (int p = 0; p < NS; ++p)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            w[t][0][2 * h] = fmaf(nls, lo_bf16(v[t][h]), w[t][0][2 * h]);
-            w[t][0][2 * h + 1] = fmaf(nls, hi_bf16(v[t][h]), w[t][0][2 * h + 1]);
-            w[t][1][2 * h] = fmaf(nls, lo_bf16(v[t][2 + h]), w[t][1][2 * h]);
-            w[t][1][2 * h + 1] = fmaf(nls, hi_bf16(v[t][2 + h]), w[t][1][2 * h + 1]);
+      for (int u = 0; u < PER; ++u) {  // every W load of this thread before its first store
+        const int q = tid + C2_NTHR * u, r = q >> 5, c = q & 31;
+        v[p][u] = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
+        if (full && W != nullptr) {
+          const long long off = static_cast<long long>(i0 + (j0 + p) * 32 + r) * n + k0 + c * 8;
+          w[p][u][0] = *reinterpret_cast<const f32x4_t*>(W + off);
+          w[p][u][1] = *reinterpret_cast<const f32x4_t*>(W + off + 4);
+        }
+      }
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int q = tid + C2_NTHR * u, r = q >> 5, c = q & 31;
+        const int i = i0 + (j0 + p) * 32 + r, k = k0 + c * 8;
+        const long long off = static_cast<long long>(i) * n + k;
+        const u32x4_t vv = v[p][u];
+        if (full) {
+          if (O != nullptr) *reinterpret_cast<u32x4_t*>(O + off) = vv;
+          if (W != nullptr) {
+            f32x4_t w0 = w[p][u][0], w1 = w[p][u][1];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              w0[2 * h] = fmaf(nls, lo_bf16(vv[h]), w0[2 * h]);
+              w0[2 * h + 1] = fmaf(nls, hi_bf16(vv[h]), w0[2 * h + 1]);
+              w1[2 * h] = fmaf(nls, lo_bf16(vv[2 + h]), w1[2 * h]);
+              w1[2 * h + 1] = fmaf(nls, hi_bf16(vv[2 + h]), w1[2 * h + 1]);
+            }
+            *reinterpret_cast<f32x4_t*>(W + off) = w0;
+            *reinterpret_cast<f32x4_t*>(W + off + 4) = w1;
           }
-          *reinterpret_cast<f32x4_t*>(W + off) = w[t][0];
-          *reinterpret_cast<f32x4_t*>(W + off + 4) = w[t][1];
-        }
-      } else if (i < s) {  // edge tiles: element by element within the matrix
-        for (int e = 0; e < 8 && k + e < l; ++e) {
-          const uint32_t word = v[t][e >> 1];
-          const float o = (e & 1) ? hi_bf16(word) : lo_bf16(word);
-          if (O != nullptr) O[off + e] = static_cast<bf16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
-          if (W != nullptr) W[off + e] = fmaf(nls, o, W[off + e]);
+        } else if (i < s) {  // edge tiles: element by element within the matrix
+          for (int e = 0; e < 8 && k + e < l; ++e) {
+            const uint32_t word = vv[e >> 1];
+            const float o = (e & 1) ? hi_bf16(word) : lo_bf16(word);
+            if (O != nullptr) O[off + e] = static_cast<bf16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
+            if (W != nullptr) W[off + e] = fmaf(nls, o, W[off + e]);
+          }
         }
       }
-    }
   }
 }
 
-// ---- combine: Y = A' X --------------------------------------------------------
-// D[k][i] = sum_j X[j][k] A'[i][j] = (A' X)[i][k]
-// FUSE: the apply is fused into the epilogue (GemmSeg.fuse).
 template <bool FUSE>
-__global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) char lds2[2 * OPB];
-  __shared__ __attribute__((aligned(1024))) char lds3[2 * OPB];
+__global__ void __launch_bounds__(C2_NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
+combine_bf16_kernel(GemmArgs G) {
+  __shared__ __attribute__((aligned(1024))) char lds0[C2_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1[C2_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds2[C2_STAGE];
   int si, tile;
   if (!find_tile(G, si, tile)) return;
   const GemmSeg& S = G.seg[si];
   const int z = tile / S.tiles_per_mat;
   const int t = tile % S.tiles_per_mat;
-  const int tiles_k = S.ld / T;
+  const int tiles_k = S.ld / C2_TK;
   const int tk = t % tiles_k, ti = t / tiles_k;
   const bf16_t* X = S.X + z * S.xstride;
-  bf16_t* Y = S.Y + z * S.xstride;
   const bf16_t* Am = S.A + z * S.astride;
 
-  // waves: 4 along M (columns k of X) x 2 along N (rows i), each 64 x 128
-  // (2 x 4 MFMA blocks; the transposed operand is the short side)
-  constexpr int CM = 64, CN = 128, FM = CM / 32, FN = CN / 32;
-  const int lane = threadIdx.x & 63, wid = wave_id();
-  const int wm = wid >> 1, wn = wid & 1;
+  // waves: 4 along k (columns of X), each 64 (k) x 128 (i): 2 x 4 MFMA blocks
+  constexpr int CM = 64, FM = 2, FN = 4;
+  const int lane = threadIdx.x & 63, wm = wave_id();
   Acc<FM, FN> acc;
   acc.zero();
   const int nk = S.s_pad / BK;
@@ -485,31 +466,38 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(Am, static_cast<long long>(S.s_pad) * sp_bytes);
   const XOffs xo(ld_bytes);
   const int avoff = row_voff(sp_bytes);
-  const int offA = ti * T * sp_bytes;
+  const int offA = ti * C2_TI * sp_bytes;
   int roff[KS], xoff[FM];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) roff[ks] = rfrag_off(ks, lane);
 #pragma unroll
   for (int i = 0; i < FM; ++i) xoff[i] = xfrag_off(wm * CM, i, lane);
-  const Bufs bufs{{lds0, lds1, lds2, lds3}};
+  const BufsN<3> bufs{{lds0, lds1, lds2}};
 
-  pipeline<4>(
+  pipeline<6>(
       bufs, nk,
       [&](char* buf, int kt) {
-        load_xrows(buf, xr, xo, ld_bytes, kt * BK * ld_bytes + tk * T * 2);
-        load_rows(buf + OPB, ar, avoff, sp_bytes, offA + kt * BK * 2);
+        // X: 16 blocks of two 512-byte rows, 4 per wave; A': 8 blocks of 16
+        // 64-byte rows, 2 per wave
+        const int soffx = kt * BK * ld_bytes + tk * C2_TK * 2;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int blk = wm * 4 + b;
+          dma16(xr, (b & 1) ? xo.odd : xo.even, soffx + blk * 2 * ld_bytes, buf + blk * 1024);
+        }
+        load_rows(buf + C2_OPX, ar, avoff, sp_bytes, offA + kt * BK * 2);
       },
       [&](const char* buf) {
-        const char* tb = buf + OPB + wn * CN * 64;
+        const char* tb = buf + C2_OPX;
         stage_mma<FM, FN>(acc, [&](int ks, int i) { return frag_xcols(buf + xoff[i] + ks * 16 * 512); },
                           [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); });
       });
 
-  // lane: row i = wn*CN + j*32 + (lane & 31) of the tile, columns
-  // k = wm*CM + i*32 + 8q + 4 (lane >> 5) + 0..3; staged in slab i >> 6.
+  // lane: row i = j*32 + (lane & 31) of the tile, columns
+  // k = wm*CM + i*32 + 8q + 4 (lane >> 5) + 0..3
   stage_sync<0>();
   const int lane_e = opaque(lane);
-  const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;  // buffers and rows below are uniform per wave
+  const int col = lane_e & 31, rq = ((lane_e >> 5) & 1) * 4;
   float* Wz = nullptr;
   bf16_t* Oz = nullptr;
   if constexpr (FUSE) {
@@ -517,16 +505,15 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
     Oz = static_cast<bf16_t*>(G.O.p[S.tab0 + z]);
     if (S.tall) {
       // W (l x s) row k holds the iterate's column k: the 32 lanes of a half
-      // wave own 32 consecutive i at each of their 4 k, so every access below
-      // covers two 128-byte row segments
-      // (per 32 x 32 block: its 16 W loads before any of its stores)
+      // wave own 32 consecutive i at each of their 4 k (two 128-byte row
+      // segments per access); per 32 x 32 block, its 16 W loads first
       const float nls = S.neg_lr_scale;
-      const bool full = (ti + 1) * T <= S.s && (tk + 1) * T <= S.l;
+      const bool full = (ti + 1) * C2_TI <= S.s && (tk + 1) * C2_TK <= S.l;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int gi = ti * T + wn * CN + j * 32 + col;
+          const int gi = ti * C2_TI + j * 32 + col;
           const float* wcol = Wz + gi;
           float wv[16];
           if (full && Wz != nullptr) {
@@ -534,13 +521,13 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
             for (int q = 0; q < 4; ++q)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                wv[4 * q + r] = wcol[static_cast<long long>(tk * T + wm * CM + i * 32 + q * 8 + rq + r) * S.n];
+                wv[4 * q + r] = wcol[static_cast<long long>(tk * C2_TK + wm * CM + i * 32 + q * 8 + rq + r) * S.n];
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int gk = tk * T + wm * CM + i * 32 + q * 8 + rq + r;
+              const int gk = tk * C2_TK + wm * CM + i * 32 + q * 8 + rq + r;
               const bf16_t ob = f32_to_bf16(acc.c[i][j][4 * q + r]);
               const long long off = static_cast<long long>(gk) * S.n + gi;
               if (full) {
@@ -555,23 +542,28 @@ __global__ void __launch_bounds__(NTHR) combine_bf16_kernel(GemmArgs G) {
       return;
     }
   }
+  // staged: 32-row slabs, rows 0..95 then 96..127
+  bf16_t* Y = FUSE ? nullptr : S.Y + z * S.xstride;
+  auto stage_block = [&](int j, char* buf) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = wn * CN + j * 32 + col;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int k = wm * CM + i * 32 + q * 8 + rq;
         const u32x2_t w = {pack_bf16x2(acc.c[i][j][4 * q + 0], acc.c[i][j][4 * q + 1]),
                            pack_bf16x2(acc.c[i][j][4 * q + 2], acc.c[i][j][4 * q + 3])};
-        *reinterpret_cast<u32x2_t*>(bufs[wn * 2 + (j >> 1)] + slab_off((j & 1) * 32 + col, k)) = w;
+        *reinterpret_cast<u32x2_t*>(buf + slab_off(col, k)) = w;
       }
-    }
-  }
+  };
+  stage_block(0, lds0);
+  stage_block(1, lds1);
+  stage_block(2, lds2);
   __syncthreads();
-  if constexpr (FUSE) slabs_apply(bufs, Wz, Oz, S.n, ti * T, tk * T, S.s, S.l, S.neg_lr_scale);
-  else slabs_to_global(bufs, Y + static_cast<long long>(ti) * T * S.ld + tk * T, S.ld);
+  slabs32_out<3, FUSE>(bufs, 0, Y, S.ld, Wz, Oz, S.n, ti * C2_TI, tk * C2_TK, S.s, S.l, S.neg_lr_scale);
+  __syncthreads();
+  stage_block(3, lds0);
+  __syncthreads();
+  slabs32_out<1, FUSE>(bufs, 3, Y, S.ld, Wz, Oz, S.n, ti * C2_TI, tk * C2_TK, S.s, S.l, S.neg_lr_scale);
 }
 
 // ---- symmetric products: O = alpha I + beta L R ----------------------------------
@@ -833,7 +825,7 @@ int grid_for(const Args& G) {
 
 }  // namespace
 
-int combine_tiles_per_matrix(int s_pad, int ld) { return (s_pad / T) * (ld / T); }
+int combine_tiles_per_matrix(int s_pad, int ld) { return (s_pad / C2_TI) * (ld / C2_TK); }
 int symprod_tile(int s_pad) { return sym_tile(s_pad); }
 int symprod_tiles_per_matrix(int s_pad, int tile) {
   const int nt = s_pad / (tile ? tile : sym_tile(s_pad));
@@ -868,8 +860,8 @@ hipError_t launch_combine_bf16(const GemmArgs& G, hipStream_t st) {
   for (int f = 0; f < 2; ++f) {
     const int grid = grid_for(part[f]);
     if (grid == 0) continue;
-    if (f) hipLaunchKernelGGL(combine_bf16_kernel<true>, dim3(grid), dim3(NTHR), 0, st, part[f]);
-    else hipLaunchKernelGGL(combine_bf16_kernel<false>, dim3(grid), dim3(NTHR), 0, st, part[f]);
+    if (f) hipLaunchKernelGGL(combine_bf16_kernel<true>, dim3(grid), dim3(C2_NTHR), 0, st, part[f]);
+    else hipLaunchKernelGGL(combine_bf16_kernel<false>, dim3(grid), dim3(C2_NTHR), 0, st, part[f]);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -105,9 +105,9 @@ int sq_buffers(bool accumulate, bool quintic) {
 bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
   if (g.engine != kTiledBf16 || C.steps < 2 || C.schedule == MUON_NS_ITERATE) return false;
   if (C.schedule == MUON_NS_ACCUMULATE) return true;
-  const double t = kTileS, t2 = symprod_tile(g.s_pad);
+  const double t2 = symprod_tile(g.s_pad);
   const double gram = symprod_tiles_per_matrix(g.s_pad) * t2 * t2 * g.kdim;
-  const double comb = combine_tiles_per_matrix(g.s_pad, g.ld) * t * t * g.s_pad;
+  const double comb = static_cast<double>(g.s_pad) * g.ld * g.s_pad;  // whatever the combine's tile shape
   const double prod = symprod_tiles_per_matrix(g.s_pad) * t2 * t2 * g.s_pad;
   const double q = C.quintic ? 1.0 : 0.0;
   return gram + comb + (3.0 * (C.steps - 1) + q * C.steps) * prod < 0.85 * C.steps * (gram + comb + q * prod);
