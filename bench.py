@@ -69,10 +69,18 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, kernels: dict
     the kernel sources they were taken on."""
     import csv
     def load(path, counter):
+        rows = sorted((r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter),
+                      key=lambda r: (r["Queue_Id"], int(r["Dispatch_Id"])))
         per = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] == counter:
-                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        after_momentum = {}  # per queue: a momentum pass ran since the last symmetric product
+        for r in rows:
+            name, q = r["Kernel_Name"], r["Queue_Id"]
+            if "momentum_" in name:
+                after_momentum[q] = True
+            elif "symprod_bf16_kernel" in name and after_momentum.get(q):
+                name = "gram:" + name  # the first symmetric product of a chain is its Gram
+                after_momentum[q] = False
+            per.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)
         return per
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
     def copy_factor(per):
@@ -86,8 +94,10 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, kernels: dict
     except (OSError, ValueError):
         data = {}
     for name, (pattern, files) in kernels.items():
-        rd = [v for k, vs in fetch.items() if pattern in k for v in vs]
-        wr = [v for k, vs in write.items() if pattern in k for v in vs]
+        base = pattern[len("gram:"):] if pattern.startswith("gram:") else pattern
+        keep = lambda k: base in k and (k.startswith("gram:") == pattern.startswith("gram:"))  # noqa: E731
+        rd = [v for k, vs in fetch.items() if keep(k) for v in vs]
+        wr = [v for k, vs in write.items() if keep(k) for v in vs]
         if not rd or not wr:
             log(f"[ingest] no dispatches of {pattern}")
             continue
@@ -145,7 +155,8 @@ def bench_full_step(args, torch, mu, wl):
             cap = dict(cap_u=u / u.norm(dim=1, keepdim=True), cap_v=v / v.norm(dim=1, keepdim=True),
                        cap_sigma=torch.zeros(g.count, device="cuda"), cap=0.0)
         groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov, **cap))
-    ws = mu.muon_step(groups, steps=steps_ns)  # allocates the workspace once
+    streams = 1 if args.one_stream else 0
+    ws = mu.muon_step(groups, steps=steps_ns, streams=streams)  # allocates the workspace once
     torch.cuda.synchronize()
     # the library lists the phases muon_step_timed brackets with events
     phases = mu.muon_step_phases(groups, steps=steps_ns)
@@ -165,12 +176,12 @@ def bench_full_step(args, torch, mu, wl):
         return evs
 
     for _ in range(args.warmup):
-        mu.muon_step(groups, steps=steps_ns, workspace=ws)
+        mu.muon_step(groups, steps=steps_ns, workspace=ws, streams=streams)
     # the timed steps: plain muon_step (shape groups as two concurrent chains)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        mu.muon_step(groups, steps=steps_ns, workspace=ws)
+        mu.muon_step(groups, steps=steps_ns, workspace=ws, streams=streams)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -523,6 +534,7 @@ GEMM = ["gemm_bf16.hip", "common.cuh"]
 COUNTED_KERNELS = {
     "full_step": {"combine_bf16_kernel": ("combine_bf16_kernel", GEMM),
                   "symprod_bf16_kernel": ("symprod_bf16_kernel", GEMM),
+                  "gram": ("gram:symprod_bf16_kernel", GEMM),
                   "momentum_wide_kernel": ("momentum_wide_kernel", ELEMENTWISE),
                   "momentum_tall_kernel": ("momentum_tall_kernel", ELEMENTWISE),
                   "apply_wide_kernel": ("apply_wide_kernel", ELEMENTWISE),
@@ -549,6 +561,9 @@ def main():
     ap.add_argument("--diag-input", default="weights", choices=["weights", "updates"],
                     help="diag: float32 weights or bf16 Muon updates")
     ap.add_argument("--iters", type=int, default=32, help="diag: Lanczos steps")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="full_step: every step on one stream (the launch configuration of the per-kernel "
+                         "timing; used for the counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB plain copy first (reference for profiler byte counters)")
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

@@ -450,8 +450,10 @@ combine_bf16_kernel(GemmArgs G) {
   const GemmSeg& S = G.seg[si];
   const int z = tile / S.tiles_per_mat;
   const int t = tile % S.tiles_per_mat;
-  const int tiles_k = S.ld / C2_TK;
-  const int tk = t % tiles_k, ti = t / tiles_k;
+  // row tiles innermost: the tiles that share an X column panel run together
+  // (on one XCD) and read it once from HBM
+  const int tiles_i = S.s_pad / C2_TI;
+  const int ti = t % tiles_i, tk = t / tiles_i;
   const bf16_t* X = S.X + z * S.xstride;
   const bf16_t* Am = S.A + z * S.astride;
 
