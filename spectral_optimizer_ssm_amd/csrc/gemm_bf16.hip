@@ -152,6 +152,21 @@ __device__ __forceinline__ bf16x8_t frag_xcols(const char* p) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// The same transposing read for a K-major tile of RS-byte rows (the
+// symmetric products' transposed operand blocks, rows = contraction index).
+template <int RS>
+__device__ __forceinline__ bf16x8_t frag_tr(const char* p) {
+  u32x2_t part[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(p + h * 4 * RS));
+    part[h] = __builtin_bit_cast(u32x2_t, v);
+  }
+  const u32x4_t w = {part[0][0], part[0][1], part[1][0], part[1][1]};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
 template <int FM, int FN>
 struct Acc {
   f32x16_t c[FM][FN];
@@ -243,8 +258,8 @@ struct BufsN {
 };
 
 // The pipelined contraction: stages 0..nk-1 through N buffers, N - 1 fills in
-// flight.  fill(buf, kt) issues this wave's fills of stage kt, mma(buf)
-// multiplies one.
+// flight.  fill(buf, kt) issues this wave's fills of stage kt, mma(buf, kt)
+// multiplies it.
 template <int LPS, int N, class Fill, class Mma>
 __device__ __forceinline__ void pipeline(const BufsN<N>& bufs, int nk, Fill fill, Mma mma) {
   static_assert(N == 3 || N == 4, "stage count");
@@ -259,7 +274,7 @@ __device__ __forceinline__ void pipeline(const BufsN<N>& bufs, int nk, Fill fill
         const int issued_after = (nk - 1 - kt) < (N - 2) ? (nk - 1 - kt) : (N - 2);
         stage_sync_ahead<LPS>(issued_after);
         if (kt + N - 1 < nk) fill(bufs[(b + N - 1) % N], kt + N - 1);
-        mma(bufs[b]);
+        mma(bufs[b], kt);
       }
     }
   }
@@ -489,7 +504,7 @@ combine_bf16_kernel(GemmArgs G) {
         }
         load_rows(buf + C2_OPX, ar, avoff, sp_bytes, offA + kt * BK * 2);
       },
-      [&](const char* buf) {
+      [&](const char* buf, int) {
         const char* tb = buf + C2_OPX;
         stage_mma<FM, FN>(acc, [&](int ks, int i) { return frag_xcols(buf + xoff[i] + ks * 16 * 512); },
                           [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); });
@@ -588,6 +603,37 @@ constexpr int SYM_NSTAGE = 3;
 
 int sym_tile(int s_pad) { return s_pad % 192 == 0 ? 192 : 128; }
 
+// Operands stored as their upper block triangle (SymSeg.tri_in): block
+// (kb, b) with kb < b is read as the transpose of the stored block (kb, b) into
+// a K-major tile [32 k rows][TT columns] (TT * 2-byte rows).  The 16-byte
+// chunk in position p of row j holds source chunk p ^ sym_tswz(j), which keeps
+// the four rows of a transposing read on distinct banks (row strides of 96 or
+// 64 banks).
+template <int TT>
+__device__ __forceinline__ int sym_tswz(int j) {
+  return TT == 192 ? (((j >> 1) & 1) << 2) : ((j & 3) << 2);
+}
+
+// Lane part of the DMA source offset of fill block blk of a K-major tile:
+// LDS chunk position blk * 64 + lane = (row j, position p).
+template <int TT>
+__device__ __forceinline__ int sym_tvoff(int blk, int lane, int ld_bytes) {
+  constexpr int CPR = TT / 8;
+  const int idx = blk * 64 + lane, j = idx / CPR, p = idx % CPR;
+  return j * ld_bytes + ((p ^ sym_tswz<TT>(j)) << 4);
+}
+
+// Lane part of the address of the transposed operand fragment whose rows are
+// tile columns col0 .. col0 + 31 (k-step 0; a k-step adds 16 rows, which
+// leaves the swizzle unchanged).
+template <int TT>
+__device__ __forceinline__ int sym_tfrag_off(int col0, int lane) {
+  const int g = lane >> 4, jj = lane & 15;
+  const int c = col0 + 16 * (g & 1) + 4 * (jj & 3);
+  const int j = 8 * (g >> 1) + (jj >> 2);
+  return j * (TT * 2) + (((c >> 3) ^ sym_tswz<TT>(j)) << 4) + ((c >> 2) & 1) * 8;
+}
+
 // Staging row r (0..63 within one buffer), column col (0..TT-1) of a TT-wide
 // bf16 tile: TT * 2-byte rows, 16-byte chunks swizzled by the row (XOR of the
 // low four bits for 16 chunks, of the low three within each group of eight for
@@ -641,6 +687,11 @@ symprod_bf16_kernel(SymArgs G) {
   int roff[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) roff[ks] = rfrag_off(ks, lane);
+  int tfa[FM], tfb[FN];  // transposed-fragment offsets (upper-triangle operands)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) tfa[i] = sym_tfrag_off<TT>(wm * WT + i * 32, lane);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) tfb[j] = sym_tfrag_off<TT>(wn * WT + j * 32, lane);
 
   // Persistent: the workgroups of XCD x walk that XCD's tile list with a
   // stride of their number, so the stores of one tile drain while the next
@@ -676,24 +727,48 @@ symprod_bf16_kernel(SymArgs G) {
         dma16(rs, voff, soff0 + blk * 16 * sp_bytes, op + blk * 1024);
       }
     };
-    auto mma = [&](const char* buf, bool one) {
-      const char* ta = buf + wm * WT * 64;
-      const char* tb = (one ? buf : buf + OPBT) + wn * WT * 64;
-      auto fa = [&](int ks, int i) { return frag_at(ta + roff[ks] + i * 32 * 64); };
-      auto fb = [&](int ks, int j) { return frag_at(tb + roff[ks] + j * 32 * 64); };
+    // upper-triangle operands: stage kt reads block (kt / kb_stages) of the
+    // row panels bi and bj; below the diagonal it is a transposed block
+    // (bi <= bj, so a transposed L block implies a transposed R block)
+    const int tri = S.tri_in;
+    const int kbs = TT / BK;  // stages per k block
+    auto fill_t = [&](char* op, __amdgpu_buffer_rsrc_t rs, int soff) {
+#pragma unroll
+      for (int b = 0; b < BPW; ++b) {
+        const int blk = wid * BPW + b;
+        dma16(rs, sym_tvoff<TT>(blk, lane, sp_bytes), soff, op + blk * 1024);
+      }
+    };
+    auto fill_op = [&](char* op, __amdgpu_buffer_rsrc_t rs, int b, int off, int kt) {
+      if (tri && kt / kbs < b) fill_t(op, rs, kt * BK * sp_bytes + b * TT * 2);
+      else fill_rows(op, rs, off + kt * BK * 2);
+    };
+    auto mma = [&](const char* buf, int kt, bool one) {
+      const int kb = kt / kbs;
+      const bool lt = tri && kb < bi, rt = tri && kb < bj;  // uniform per stage
+      const char* ab = buf;
+      const char* bb = one ? buf : buf + OPBT;
+      auto fa = [&](int ks, int i) {
+        return lt ? frag_tr<TT * 2>(ab + tfa[i] + ks * 16 * TT * 2)
+                  : frag_at(ab + wm * WT * 64 + roff[ks] + i * 32 * 64);
+      };
+      auto fb = [&](int ks, int j) {
+        return rt ? frag_tr<TT * 2>(bb + tfb[j] + ks * 16 * TT * 2)
+                  : frag_at(bb + wn * WT * 64 + roff[ks] + j * 32 * 64);
+      };
       if constexpr (FM * FN > SYM_SINGLE_FRAGS_ABOVE) stage_mma_single<FM, FN>(acc, fa, fb);
       else stage_mma<FM, FN>(acc, fa, fb);
     };
     if (single) {
-      pipeline<BPW>(bufs, nk, [&](char* buf, int kt) { fill_rows(buf, lr, offL + kt * BK * 2); },
-                    [&](const char* buf) { mma(buf, true); });
+      pipeline<BPW>(bufs, nk, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt); },
+                    [&](const char* buf, int kt) { mma(buf, kt, true); });
     } else {
       pipeline<2 * BPW>(bufs, nk,
                         [&](char* buf, int kt) {
-                          fill_rows(buf, lr, offL + kt * BK * 2);
-                          fill_rows(buf + OPBT, rr, offR + kt * BK * 2);
+                          fill_op(buf, lr, bi, offL, kt);
+                          fill_op(buf + OPBT, rr, bj, offR, kt);
                         },
-                        [&](const char* buf) { mma(buf, false); });
+                        [&](const char* buf, int kt) { mma(buf, kt, false); });
     }
 
     // epilogue: D[m][n] = (L R)[bi*TT + m][bj*TT + n]; lane: 4 consecutive m
@@ -742,6 +817,10 @@ symprod_bf16_kernel(SymArgs G) {
     }
     bf16_t* O1 = S.O1 == nullptr ? nullptr : S.O1 + zoff;
     bf16_t* O2 = S.O2 == nullptr ? nullptr : S.O2 + zoff;
+    // the mirrored block (bj, bi) is skipped when the output keeps only its
+    // upper block triangle (a diagonal block is always whole)
+    const bool mirror = diag || !S.tri_out;
+    if (mirror) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int nb = wn * WT + j * 32;  // 32-aligned block of n
@@ -762,8 +841,9 @@ symprod_bf16_kernel(SymArgs G) {
     }
     __syncthreads();
     sym_to_global<TT>(bufs, O1, O2, static_cast<long long>(bj) * TT * S.s_pad + bi * TT, S.s_pad, S.a2, S.b2, diag);
+    }
     if (!diag) {
-      __syncthreads();
+      if (mirror) __syncthreads();
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int mb = wm * WT + i * 32;  // 32-aligned block of m

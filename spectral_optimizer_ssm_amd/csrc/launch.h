@@ -155,6 +155,9 @@ struct SymSeg {
   int tile;            // 0: symprod_tile(s_pad); else 128 or 192 (dividing s_pad)
   float* F;            // non-null: O1 = a1 inv^pa I + b1 inv^pb L R as float32 here
                        // [count][s_pad][s_pad] (stride), exactly symmetric; O1, O2 unused
+  int tri_in;          // 1: L and R hold only their upper block triangle (tile-sized
+                       // blocks on and above the diagonal); the others are read transposed
+  int tri_out;         // 1: O1 and O2 get only their upper block triangle
 };
 struct SymArgs {
   SymSeg seg[kMaxSeg];

@@ -268,9 +268,14 @@ SymSeg gram_as_sym(const GemmSeg& G) {
   S.pa = G.pa; S.pb = G.pb;
   return S;
 }
-std::vector<SymSeg> grams_as_sym(const std::vector<GemmSeg>& gs) {
+// tri_out: the outputs keep only their upper block triangle (they feed
+// symmetric products only).
+std::vector<SymSeg> grams_as_sym(const std::vector<GemmSeg>& gs, bool tri_out = false) {
   std::vector<SymSeg> out;
-  for (const GemmSeg& G : gs) out.push_back(gram_as_sym(G));
+  for (const GemmSeg& G : gs) {
+    out.push_back(gram_as_sym(G));
+    out.back().tri_out = tri_out ? 1 : 0;
+  }
   return out;
 }
 
@@ -483,9 +488,12 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       }
       gs.push_back(S);
     }
-    if (!launch_segments<SymArgs>(grams_as_sym(gs), launch_symprod_bf16, st, E.live()) ||
+    if (!launch_segments<SymArgs>(grams_as_sym(gs, true), launch_symprod_bf16, st, E.live()) ||
         !E.mark(st, MUON_PHASE_GRAM))
       return MUON_EHIP;
+    // every s x s matrix of the chain keeps only its upper block triangle
+    // (the products read the rest transposed), except the final Q, which the
+    // combine reads whole
     for (int k = 0; k < n; ++k) {
       if (C.quintic) {  // B_k = a_k I + A_k H_k
         std::vector<SymSeg> lb;
@@ -494,6 +502,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
           SymSeg S = sym_seg(p);
           S.L = sq_of(p, ws, kSqA0 + (k & 1)); S.R = sq_of(p, ws, kSqH); S.O1 = sq_of(p, ws, kSqB0 + (k & 1));
           S.a1 = C.a[k];
+          S.tri_in = 1; S.tri_out = 1;
           lb.push_back(S);
         }
         if (!launch_segments<SymArgs>(lb, launch_symprod_bf16, st, E.live()) || !E.mark(st, MUON_PHASE_SYMPROD))
@@ -507,6 +516,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
           SymSeg S = sym_seg(p);
           S.L = Bk; S.R = Bk; S.O1 = sq_of(p, ws, kSqE);
           S.zip_next = k >= 1 ? 1 : 0;
+          S.tri_in = 1; S.tri_out = 1;
           l1.push_back(S);
         }
         if (k >= 1) {  // Q_{k+1} = B_k Q_k; the last one carries the normalisation
@@ -514,6 +524,8 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
           S.L = Bk;
           S.R = k == 1 ? sq_of(p, ws, kSqB0) : sq_of(p, ws, kSqQ0 + (k & 1));
           S.O1 = sq_of(p, ws, kSqQ0 + ((k + 1) & 1));
+          S.tri_in = 1;
+          S.tri_out = k + 1 < n ? 1 : 0;
           if (k + 1 == n) {
             S.partials = reinterpret_cast<const float*>(ws + p.off_part);
             S.pb = 1;
@@ -524,6 +536,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
           SymSeg S = sym_seg(p);
           S.L = sq_of(p, ws, kSqA0 + (k & 1));
           S.R = sq_of(p, ws, kSqE);
+          S.tri_in = 1; S.tri_out = 1;
           if (!C.quintic) {
             S.O1 = k + 2 < n ? sq_of(p, ws, kSqA0 + ((k + 1) & 1)) : nullptr;  // the last A is not needed
             S.O2 = sq_of(p, ws, kSqB0 + ((k + 1) & 1));
