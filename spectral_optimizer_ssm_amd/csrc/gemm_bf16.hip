@@ -523,23 +523,28 @@ combine_bf16_kernel(GemmArgs G) {
     if (S.tall) {
       // W (l x s) row k holds the iterate's column k: the 32 lanes of a half
       // wave own 32 consecutive i at each of their 4 k (two 128-byte row
-      // segments per access); per 32 x 32 block, its 16 W loads first
+      // segments per access); per 32-column block i, all 64 of its W loads
+      // before any of its stores (memory-level parallelism: the epilogue is
+      // bound by the latency of these loads, not by bandwidth)
       const float nls = S.neg_lr_scale;
       const bool full = (ti + 1) * C2_TI <= S.s && (tk + 1) * C2_TK <= S.l;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        float wv[FN][16];
+        if (full && Wz != nullptr) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int gi = ti * C2_TI + j * 32 + col;
-          const float* wcol = Wz + gi;
-          float wv[16];
-          if (full && Wz != nullptr) {
+          for (int j = 0; j < FN; ++j) {
+            const float* wcol = Wz + ti * C2_TI + j * 32 + col;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                wv[4 * q + r] = wcol[static_cast<long long>(tk * C2_TK + wm * CM + i * 32 + q * 8 + rq + r) * S.n];
+                wv[j][4 * q + r] = wcol[static_cast<long long>(tk * C2_TK + wm * CM + i * 32 + q * 8 + rq + r) * S.n];
           }
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int gi = ti * C2_TI + j * 32 + col;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -549,13 +554,14 @@ combine_bf16_kernel(GemmArgs G) {
               const long long off = static_cast<long long>(gk) * S.n + gi;
               if (full) {
                 if (Oz != nullptr) Oz[off] = ob;
-                if (Wz != nullptr) Wz[off] = fmaf(nls, bf16_to_f32(ob), wv[4 * q + r]);
+                if (Wz != nullptr) Wz[off] = fmaf(nls, bf16_to_f32(ob), wv[j][4 * q + r]);
               } else if (gi < S.s && gk < S.l) {
                 if (Oz != nullptr) Oz[off] = ob;
                 if (Wz != nullptr) Wz[off] = fmaf(nls, bf16_to_f32(ob), Wz[off]);
               }
             }
         }
+      }
       return;
     }
   }
