@@ -279,8 +279,10 @@ std::vector<SymSeg> grams_as_sym(const std::vector<GemmSeg>& gs, bool tri_out = 
   return out;
 }
 
+// after_momentum: when non-null, recorded on st once the momentum passes of
+// these groups have been enqueued.
 int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, float* norms_out, hipStream_t st,
-            EventRec& E) {
+            EventRec& E, hipEvent_t after_momentum = nullptr) {
   if (!E.mark(st, 0)) return MUON_EHIP;
   // 1. momentum
   for (GroupRun& R : runs) {
@@ -308,6 +310,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       return MUON_EHIP;
     if (!E.mark(st, MUON_PHASE_MOMENTUM)) return MUON_EHIP;
   }
+  if (after_momentum != nullptr && E.live() && hipEventRecord(after_momentum, st) != hipSuccess) return MUON_EHIP;
 
   // 2. small matrices on chip
   std::vector<int> fin(runs.size(), 0);  // which buffer holds the final iterate
@@ -752,7 +755,10 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   // Independent shape groups run as two chains on two streams (the caller's
   // and an auxiliary one, joined back before returning), so that one chain's
   // launch tails and bandwidth-bound passes overlap the other's matrix-core
-  // work.  Groups are dealt to the chains by estimated cost, heaviest first.
+  // work.  Groups are dealt to the chains by estimated cost, heaviest first;
+  // the lighter chain starts once the heavier one's momentum pass is done, so
+  // that the critical chain's first, bandwidth-bound pass runs alone (measured
+  // faster than starting both together).
   std::vector<int> live;
   for (int i = 0; i < ngroups; ++i)
     if (runs[i].plan.count > 0) live.push_back(i);
@@ -771,11 +777,10 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
     load[c] += cost(i);
   }
   std::lock_guard<std::mutex> lock(aux->mu);
-  if (hipEventRecord(aux->fork, st) != hipSuccess || hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
-    return MUON_EHIP;
   EventRec E1;
-  rc = run_all(chain[0], C, cfg->eps, ws, norms_out, st, E);
-  const int rc1 = run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1);
+  rc = run_all(chain[0], C, cfg->eps, ws, norms_out, st, E, aux->fork);  // fork: after chain 0's momentum
+  if (hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess) return MUON_EHIP;
+  const int rc1 = rc == MUON_OK ? run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1) : MUON_OK;
   // join even after a failed launch, so that the caller's stream never runs ahead of the auxiliary work
   if (hipEventRecord(aux->join, aux->s) != hipSuccess || hipStreamWaitEvent(st, aux->join, 0) != hipSuccess)
     return MUON_EHIP;
