@@ -13,7 +13,10 @@ two device synchronisations), per-kernel durations from HIP events recorded by
 muon_step_timed in K further steps (those run the phases one after another on
 one stream), the roofline of the dominant kernel, and the fp64 oracle timed on
 a bounded sample on the host cores.
-Other workloads (out_proj, in_proj, injections, single) are for exploration.
+Other workloads: injections, injections_factored, adamw, diag, sweep (1/3/5/8
+NS steps with the orthogonality error of each update); out_proj, in_proj,
+single are for exploration.  --schedule, --separate-apply, --one-stream and
+--per-matrix switch single design choices of the full step for A/B runs.
 """
 from __future__ import annotations
 
@@ -156,10 +159,14 @@ def bench_full_step(args, torch, mu, wl):
                        cap_sigma=torch.zeros(g.count, device="cuda"), cap=0.0)
         groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov, **cap))
     streams = 1 if args.one_stream else 0
-    ws = mu.muon_step(groups, steps=steps_ns, streams=streams)  # allocates the workspace once
+    sched = {"auto": mu.MUON_NS_AUTO, "iterate": mu.MUON_NS_ITERATE, "accumulate": mu.MUON_NS_ACCUMULATE}[args.schedule]
+    opts = dict(steps=steps_ns, streams=streams, schedule=sched, separate_apply=int(args.separate_apply))
+    if args.per_matrix:  # one muon_step call per matrix (the ungrouped launch pattern)
+        return bench_per_matrix(args, torch, mu, w, groups, opts)
+    ws = mu.muon_step(groups, **opts)  # allocates the workspace once
     torch.cuda.synchronize()
     # the library lists the phases muon_step_timed brackets with events
-    phases = mu.muon_step_phases(groups, steps=steps_ns)
+    phases = mu.muon_step_phases(groups, steps=steps_ns, schedule=sched, separate_apply=int(args.separate_apply))
     n_ev = len(phases) + 1
     log(f"[bench] schedule: {' '.join(phases)}")
 
@@ -176,22 +183,24 @@ def bench_full_step(args, torch, mu, wl):
         return evs
 
     for _ in range(args.warmup):
-        mu.muon_step(groups, steps=steps_ns, workspace=ws, streams=streams)
+        mu.muon_step(groups, workspace=ws, **opts)
     # the timed steps: plain muon_step (shape groups as two concurrent chains)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        mu.muon_step(groups, steps=steps_ns, workspace=ws, streams=streams)
+        mu.muon_step(groups, workspace=ws, **opts)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    cold = cold_cache_steps(torch, lambda: mu.muon_step(groups, workspace=ws, **opts), args.steps)
     # per-kernel durations: the same steps again through muon_step_timed,
     # which runs the phases one after another on one stream
     evs = make_events(args.steps)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for k in range(args.steps):
-        mu.muon_step(groups, steps=steps_ns, workspace=ws, events=[e.cuda_event for e in evs[k]])
+        mu.muon_step(groups, steps=steps_ns, workspace=ws, events=[e.cuda_event for e in evs[k]], schedule=sched,
+                     separate_apply=int(args.separate_apply))
     torch.cuda.synchronize()
     ms_serial = (time.perf_counter() - t2) * 1e3 / args.steps
 
@@ -202,7 +211,7 @@ def bench_full_step(args, torch, mu, wl):
     comb_f = sum(g.count * ns_flops(s, l)[1] for g, s, l in per_group)
     sym_f = sum(g.count * s * s * (s + 1) for g, s, l in per_group)  # one symmetric s x s product
     sym_products = []
-    if "symprod" in phases:
+    if "symprod" in phases:  # the accumulated schedule's products per launch
         for k in range(steps_ns):
             sym_products.append(int(k + 1 < steps_ns) + int(k >= 1))
             if k + 1 < steps_ns:
@@ -279,6 +288,7 @@ def bench_full_step(args, torch, mu, wl):
         "metric": METRIC, "value": round(1e3 / ms_per_step, 3), "unit": "steps/s",
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_one_stream": round(ms_serial, 4),
+        "cold_cache": cold,
         "ns_iters_per_s": round(steps_ns * 1e3 / ms_per_step, 2),
         "ns_tflops": round(ns_tflops, 2), "mfma_util": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
         "ns_iteration_equivalent_tflops": round(iter_flops_step / (ns_ms * 1e-3) / 1e12, 2),
@@ -287,7 +297,8 @@ def bench_full_step(args, torch, mu, wl):
                                f"{args.count}x in_proj 3352x768, bf16 grads, fp32 W/M, "
                                f"{steps_ns} cubic NS steps",
                    "matrices": 2 * args.count, "ns_steps": steps_ns, "parallelism": "none (1 GPU)",
-                   "spectral_cap": bool(args.cap),
+                   "spectral_cap": bool(args.cap), "ns_schedule": args.schedule,
+                   "separate_apply": bool(args.separate_apply), "chains": 1 if args.one_stream else "auto",
                    "schedule": " ".join(phases)},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
@@ -296,6 +307,96 @@ def bench_full_step(args, torch, mu, wl):
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline_full_step(w, steps_ns)
     return result
+
+
+def cold_cache_steps(torch, step, k):
+    """Per-step durations with L2 and the 256 MB last-level cache flushed
+    before each step (a 512 MB fill, outside the events): median, p10, p90."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    for a, b in ev:
+        flush.zero_()
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    del flush
+    return {"ms_median": round(float(np.median(ms)), 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
+            "ms_p90": round(float(np.percentile(ms, 90)), 4), "steps": k}
+
+
+def bench_per_matrix(args, torch, mu, w, groups, opts):
+    """The full step as one muon_step call per matrix (48 calls of one
+    matrix each, every kernel launched per matrix): the ungrouped pattern the
+    grouped launches replace."""
+    single = [mu.MuonGroup(W=g.W[i:i + 1], M=g.M[i:i + 1], G=g.G[i:i + 1], lr=g.lr, beta=g.beta,
+                           nesterov=g.nesterov) for g in groups for i in range(g.W.shape[0])]
+    ws = None
+    for g in single:  # grows the workspace to the largest matrix's need
+        ws = mu.muon_step([g], workspace=ws, **opts)
+    for _ in range(args.warmup):
+        for g in single:
+            mu.muon_step([g], workspace=ws, **opts)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for g in single:
+            mu.muon_step([g], workspace=ws, **opts)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"metric": METRIC, "value": round(1e3 / ms, 3), "unit": "steps/s", "ms_per_step": round(ms, 4),
+            "dtype": "bf16",
+            "config": {"workload": f"mamba2-130m-full-step, one call per matrix: {args.count}x out_proj 768x1536 + "
+                                   f"{args.count}x in_proj 3352x768, {opts['steps']} cubic NS steps",
+                       "matrices": 2 * args.count, "calls_per_step": len(single), "ns_schedule": args.schedule,
+                       "separate_apply": bool(args.separate_apply)}}
+
+
+def bench_sweep(args, torch, mu, wl):
+    """Steps sweep of the full step (1, 3, 5, 8 NS steps) on the zero-momentum
+    variant of the inputs (U = (1 + beta) G): optimizer steps/s at each step
+    count, and the orthogonality error ||O O^T - I||_F / sqrt(s) and extreme
+    singular value of every update O, measured on the GPU by
+    muon_spectral_diag (32 Lanczos steps)."""
+    log(f"[bench] generating zero-momentum full-step inputs ({args.count}+{args.count} matrices)")
+    w = wl.config4(count=args.count, zero_momentum=True)
+    host = [(g.G.view(np.int16), g.W, g.M) for g in w.groups]
+    dev = [(torch.from_numpy(G).view(torch.bfloat16).cuda(), torch.from_numpy(W).cuda(), torch.from_numpy(M).cuda())
+           for G, W, M in host]
+    outs = [torch.empty(G.shape, dtype=torch.bfloat16, device="cuda") for G, _, _ in dev]
+    rows = []
+    for steps in (1, 3, 5, 8):
+        for (G, W, M), (_, W0, M0) in zip(dev, host):
+            W.copy_(torch.from_numpy(W0))
+            M.copy_(torch.from_numpy(M0))
+        groups = [mu.MuonGroup(W=W, M=M, G=G, O=O, lr=w.lr, beta=w.beta, nesterov=w.nesterov)
+                  for (G, W, M), O in zip(dev, outs)]
+        ws = mu.muon_step(groups, steps=steps)  # the first step from M = 0: its O is the one measured
+        diag = [mu.muon_spectral_diag(O, iters=32, sigma_min=False) for O in outs]
+        timed = [mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov) for G, W, M in dev]
+        for _ in range(args.warmup):
+            mu.muon_step(timed, steps=steps, workspace=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            mu.muon_step(timed, steps=steps, workspace=ws)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        row = {"ns_steps": steps, "steps_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
+               "ns_iters_per_s": round(steps * 1e3 / ms, 1)}
+        for g, d in zip(w.groups, diag):
+            e = d["orth_err"].cpu().numpy()
+            row[g.name] = {"orth_err_mean": round(float(e.mean()), 5), "orth_err_max": round(float(e.max()), 5),
+                           "sigma_max": round(float(d["sigma_max"].max()), 5)}
+        log(f"[bench] sweep {row}")
+        rows.append(row)
+    five = next(r for r in rows if r["ns_steps"] == 5)
+    return {"metric": METRIC, "value": five["steps_per_s"], "unit": "steps/s", "ms_per_step": five["ms_per_step"],
+            "dtype": "bf16",
+            "config": {"workload": f"mamba2-130m-full-step steps sweep (M = 0): {args.count}x out_proj 768x1536 + "
+                                   f"{args.count}x in_proj 3352x768, bf16 grads, 1/3/5/8 cubic NS steps; value at 5"},
+            "sweep": rows}
 
 
 def cpu_baseline_full_step(w, steps_ns, budget_s=15.0):
@@ -551,7 +652,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_step",
                     choices=["full_step", "out_proj", "in_proj", "injections", "injections_factored", "adamw",
-                             "diag", "single"])
+                             "diag", "single", "sweep"])
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
     ap.add_argument("--batch", type=int, default=393216, help="injections batch")
@@ -564,6 +665,12 @@ def main():
     ap.add_argument("--one-stream", action="store_true",
                     help="full_step: every step on one stream (the launch configuration of the per-kernel "
                          "timing; used for the counter runs)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "iterate", "accumulate"],
+                    help="full_step: Newton-Schulz schedule of the large groups")
+    ap.add_argument("--separate-apply", action="store_true",
+                    help="full_step: apply the update in its own pass instead of the final product's epilogue")
+    ap.add_argument("--per-matrix", action="store_true",
+                    help="full_step: one muon_step call per matrix instead of one grouped call")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB plain copy first (reference for profiler byte counters)")
     ap.add_argument("--ingest", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -597,6 +704,8 @@ def main():
         res = bench_adamw(args, torch, mu, wl)
     elif args.workload == "diag":
         res = bench_diag(args, torch, mu, wl)
+    elif args.workload == "sweep":
+        res = bench_sweep(args, torch, mu, wl)
     else:
         res = bench_group(args, torch, mu, wl, args.workload)
     out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,

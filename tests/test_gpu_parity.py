@@ -116,6 +116,39 @@ def test_full_mamba2_step_zero_momentum_closed_form(mu):
             compare_step(g, i, outs[gi], devs[gi], w, BF16_TOL)
 
 
+def test_orthogonality_error_vs_steps_closed_form(mu):
+    """Orthogonality error ||O O^T - I||_F / sqrt(s) of the update after 1, 3,
+    5 and 8 steps with M = 0: the GPU's (muon_spectral_diag of the bf16 O),
+    the oracle's (its fp64 O), and the closed form from the singular values
+    of the rounded gradient (U = (1 + beta) G, X0 = U / (||U||_F + eps),
+    every singular value x through p^k).  Oracle and closed form agree to
+    rounding; the GPU follows within the bf16 update tolerance; the error
+    falls with the step count."""
+    w = wl.config4(count=2, zero_momentum=True)
+    a, b = w.coeffs
+    prev = {}
+    for steps in (1, 3, 5, 8):
+        devs, outs = run_step(mu, w, steps=steps)
+        for gi, g in enumerate(w.groups):
+            d = mu.muon_spectral_diag(outs[gi]["O"], iters=16, sigma_max=False, sigma_min=False)
+            torch.cuda.synchronize()
+            e_gpu = float(d["orth_err"][0].cpu())
+            G = grad64(g, 0)
+            ref = orc.muon_step(orc.widen_f32(g.W[0]), np.zeros_like(G), G, beta=w.beta, lr=w.lr,
+                                nesterov=w.nesterov, steps=steps, coeffs=w.coeffs, eps=w.eps)
+            e_orc = orc.orthogonality_error(ref["O"])
+            sig = (1 + w.beta) * np.linalg.svd(G, compute_uv=False)
+            x = sig / (np.sqrt(np.sum(sig * sig)) + w.eps)
+            for _ in range(steps):
+                x = a * x + b * x ** 3
+            e_cf = float(np.sqrt(np.sum((x * x - 1.0) ** 2) / x.size))
+            print(g.name, steps, "orth gpu %.5f oracle %.5f closed form %.5f" % (e_gpu, e_orc, e_cf))
+            assert abs(e_orc - e_cf) <= 1e-9 * max(1.0, e_cf)
+            assert abs(e_gpu - e_orc) <= 2e-2 * e_orc
+            assert e_gpu < prev.get(g.name, np.inf)
+            prev[g.name] = e_gpu
+
+
 def _injection_oracle(X, steps=1):
     return orc.ns_batched(X.float().cpu().numpy().astype(np.float64), steps)
 
