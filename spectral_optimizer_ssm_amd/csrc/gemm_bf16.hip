@@ -72,8 +72,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 // 16-byte buffer load written straight into LDS: lane l's data lands at
 // lds_wave_base + 16 * l.  The per-lane byte offset is a VGPR, everything that
 // is uniform (row block, stage) goes into the SGPR soffset.
+//
+// The LDS destination goes through an empty asm, so the compiler cannot tie
+// the fill to a stage buffer: otherwise its own wait insertion, which merges
+// the pending fills imprecisely at control-flow joins, makes some stages wait
+// for every fill in flight (vmcnt(0)) before reading LDS.  Every read of a
+// stage is ordered after its fills by the explicit vmcnt + barrier hand-over.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff, char* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)lds_wave_base, 16, voff, soff, 0, 0);
+  unsigned a = static_cast<unsigned>(reinterpret_cast<unsigned long long>((lds_ptr_t)lds_wave_base));
+  asm volatile("" : "+s"(a));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)static_cast<unsigned long long>(a), 16, voff, soff, 0, 0);
 }
 
 // ---- K-contiguous operand: [256 rows][32 K], 64-byte rows ------------------
@@ -280,6 +288,36 @@ __device__ __forceinline__ void pipeline(const BufsN<N>& bufs, int nk, Fill fill
   }
 }
 
+// The same pipeline over three consecutive stage ranges [0, k2), [k2, k1),
+// [k1, nk), each multiplied by its own straight-line body (mma0, mma1, mma2
+// in range order).  k2 and k1 must be multiples of N, so that stage kt sits in
+// buffer kt % N with a static choice in every range.
+template <int LPS, int N, class Fill, class MmaA, class MmaB, class MmaC>
+__device__ __forceinline__ void pipeline3(const BufsN<N>& bufs, int nk, int k2, int k1, Fill fill, MmaA mma0,
+                                          MmaB mma1, MmaC mma2) {
+  static_assert(N == 3 || N == 4, "stage count");
+#pragma unroll
+  for (int p = 0; p < N - 1; ++p)
+    if (p < nk) fill(bufs[p], p);
+  auto range = [&](int kbeg, int kend, auto mma) {
+    for (int kt0 = kbeg; kt0 < kend; kt0 += N) {
+#pragma unroll
+      for (int b = 0; b < N; ++b) {
+        const int kt = kt0 + b;
+        if (kt < kend) {
+          const int issued_after = (nk - 1 - kt) < (N - 2) ? (nk - 1 - kt) : (N - 2);
+          stage_sync_ahead<LPS>(issued_after);
+          if (kt + N - 1 < nk) fill(bufs[(b + N - 1) % N], kt + N - 1);
+          mma(bufs[b], kt);
+        }
+      }
+    }
+  };
+  range(0, k2, mma0);
+  range(k2, k1, mma1);
+  range(k1, nk, mma2);
+}
+
 // A copy of v the compiler cannot see through: epilogue addresses derived from
 // it are computed after the main loop instead of being hoisted above it (where
 // they would occupy registers for the whole loop).
@@ -463,12 +501,15 @@ combine_bf16_kernel(GemmArgs G) {
   int si, tile;
   if (!find_tile(G, si, tile)) return;
   const GemmSeg& S = G.seg[si];
-  const int z = tile / S.tiles_per_mat;
-  const int t = tile % S.tiles_per_mat;
+  // the integer divisions run on the vector unit: their results are moved
+  // back to scalars, so that everything derived from them (matrix bases,
+  // buffer descriptors) is provably uniform
+  const int z = __builtin_amdgcn_readfirstlane(tile / S.tiles_per_mat);
+  const int t = __builtin_amdgcn_readfirstlane(tile % S.tiles_per_mat);
   // row tiles innermost: the tiles that share an X column panel run together
   // (on one XCD) and read it once from HBM
   const int tiles_i = S.s_pad / C2_TI;
-  const int ti = t % tiles_i, tk = t / tiles_i;
+  const int ti = __builtin_amdgcn_readfirstlane(t % tiles_i), tk = __builtin_amdgcn_readfirstlane(t / tiles_i);
   const bf16_t* X = S.X + z * S.xstride;
   const bf16_t* Am = S.A + z * S.astride;
 
@@ -598,6 +639,7 @@ combine_bf16_kernel(GemmArgs G) {
 // matrix: one wave of workgroups for 48 matrices, and half the operand bytes
 // per flop of TT = 128), else 128.  Four waves of TT/2 x TT/2, three LDS
 // stages; the stage buffers double as the output staging area.
+template <int V> struct IntC { static constexpr int value = V; };
 template <int TT> struct SymCfg;
 template <> struct SymCfg<128> { static constexpr int kWpe = 3; };  // 48 KB LDS: three workgroups per CU
 template <> struct SymCfg<192> { static constexpr int kWpe = 2; };  // 72 KB LDS: two workgroups per CU
@@ -765,7 +807,39 @@ symprod_bf16_kernel(SymArgs G) {
       if constexpr (FM * FN > SYM_SINGLE_FRAGS_ABOVE) stage_mma_single<FM, FN>(acc, fa, fb);
       else stage_mma<FM, FN>(acc, fa, fb);
     };
-    if (single) {
+    if constexpr (TT == 192) {
+      // the operand modes change only at k-block boundaries (multiples of 6
+      // stages): stages below block bi read both operands transposed, those
+      // below bj only R; each range runs a straight-line body
+      const int k2 = tri ? bi * kbs : 0, k1 = tri ? bj * kbs : 0;
+      auto body = [&](const char* buf, bool one, auto lt_rt) {
+        constexpr int MODE = decltype(lt_rt)::value;
+        const char* ab = buf;
+        const char* bb = one ? buf : buf + OPBT;
+        auto fa_r = [&](int ks, int i) { return frag_at(ab + wm * WT * 64 + roff[ks] + i * 32 * 64); };
+        auto fa_t = [&](int ks, int i) { return frag_tr<TT * 2>(ab + tfa[i] + ks * 16 * TT * 2); };
+        auto fb_r = [&](int ks, int j) { return frag_at(bb + wn * WT * 64 + roff[ks] + j * 32 * 64); };
+        auto fb_t = [&](int ks, int j) { return frag_tr<TT * 2>(bb + tfb[j] + ks * 16 * TT * 2); };
+        if constexpr (MODE == 2) stage_mma_single<FM, FN>(acc, fa_t, fb_t);
+        else if constexpr (MODE == 1) stage_mma_single<FM, FN>(acc, fa_r, fb_t);
+        else stage_mma_single<FM, FN>(acc, fa_r, fb_r);
+      };
+      if (single) {
+        pipeline3<BPW>(bufs, nk, k2, k1, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt); },
+                       [&](const char* buf, int) { body(buf, true, IntC<2>{}); },
+                       [&](const char* buf, int) { body(buf, true, IntC<1>{}); },
+                       [&](const char* buf, int) { body(buf, true, IntC<0>{}); });
+      } else {
+        pipeline3<2 * BPW>(bufs, nk, k2, k1,
+                           [&](char* buf, int kt) {
+                             fill_op(buf, lr, bi, offL, kt);
+                             fill_op(buf + OPBT, rr, bj, offR, kt);
+                           },
+                           [&](const char* buf, int) { body(buf, false, IntC<2>{}); },
+                           [&](const char* buf, int) { body(buf, false, IntC<1>{}); },
+                           [&](const char* buf, int) { body(buf, false, IntC<0>{}); });
+      }
+    } else if (single) {
       pipeline<BPW>(bufs, nk, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt); },
                     [&](const char* buf, int kt) { mma(buf, kt, true); });
     } else {
