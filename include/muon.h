@@ -164,6 +164,13 @@ typedef struct {
   float cap;
 } muon_group;
 
+/* Sizes.  m * n <= 2^31 per matrix; on the matrix-core path (bfloat16, not
+ * small) also s_pad * ld * 2 < 2^31 bytes, where s_pad is min(m, n) and ld is
+ * max(m, n), each rounded up to a multiple of 256 (one padded iterate below
+ * 2 GiB: e.g. 16384 x 65280 is accepted, 16384 x 65536 is not); beyond either
+ * bound muon_step, its size queries and muon_step_phases return
+ * MUON_EUNSUPPORTED (muon_step_workspace_size: 0). */
+
 /* Bytes of device workspace muon_step needs for these groups (0 on invalid
  * arguments). */
 size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg);

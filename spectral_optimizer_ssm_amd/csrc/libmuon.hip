@@ -138,6 +138,10 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
     g->ld = round_up(g->l, kTileF32);
   }
   g->kdim = std::min(g->ld, round_up(g->l, 64));
+  // the matrix-core kernels address one padded iterate with 32-bit buffer
+  // offsets: below 2 GiB per matrix
+  if (g->engine == kTiledBf16 && static_cast<long long>(g->s_pad) * g->ld * 2 >= (1LL << 31))
+    return MUON_EUNSUPPORTED;
   if (C.quintic && g->engine != kTiledBf16) return MUON_EUNSUPPORTED;  // c != 0: large bf16 matrices only
   g->accumulate = choose_accumulate(*g, C);
   g->P = momentum_blocks_per_matrix(g->tall, g->s_pad, g->ld);

@@ -114,6 +114,29 @@ def test_step_validation(mu, case, expect):
     assert rc == expect
 
 
+@pytest.mark.parametrize("m,n,ok", [
+    (16384, 65280, True),     # padded iterate 16384 x 65280 bf16: just under 2 GiB
+    (65280, 16384, True),     # the same, tall
+    (16384, 65536, False),    # exactly 2 GiB: beyond the 32-bit buffer offsets
+    (32768, 32768, False),
+    (46341, 46341, False),    # m * n > 2^31
+])
+def test_size_limits(mu, m, n, ok):
+    """Shapes at the documented size bounds: accepted by the planner (phases
+    listed, workspace sized) or rejected with MUON_EUNSUPPORTED, no GPU work."""
+    L = mu.lib()
+    cfg, keep = _cfg(mu)
+    g, k2 = _group(mu, m, n, 1)
+    arr = (mu.binding.GroupC * 1)(g)
+    n_ph = L.muon_step_phases(arr, 1, ctypes.byref(cfg), None, 0)
+    ws = L.muon_step_workspace_size(arr, 1, ctypes.byref(cfg))
+    if ok:
+        assert n_ph > 0 and ws >= 2 * min(m, n) * max(m, n) * 2
+    else:
+        assert n_ph == -2 and ws == 0
+        assert L.muon_step(arr, 1, ctypes.byref(cfg), ctypes.c_void_p(0x7000000), 1 << 40, None, None) == -2
+
+
 def test_small_and_ns_validation(mu):
     L = mu.lib()
     cfg, keep = _cfg(mu, steps=1)
