@@ -149,6 +149,54 @@ def test_orthogonality_error_vs_steps_closed_form(mu):
             prev[g.name] = e_gpu
 
 
+@pytest.mark.parametrize("tall", [False, True])
+def test_max_size_block_diagonal(mu, tall):
+    """The largest accepted matrix-core shape, 16384 x 65280 (the padded bf16
+    iterate just under 2 GiB), one matrix, M = W = 0, a gradient of 256 blocks
+    of 64 x 255 on the diagonal.  The Frobenius normalisation is global and
+    every Gram X X^T is block diagonal, so the update is block diagonal, each
+    block the Newton-Schulz iterate of its own block scaled by the norm of
+    the whole matrix: the oracle iterates each block; entries outside the
+    blocks must be exactly zero, and the weight increment is exactly
+    -lr * O (float32 product of the bf16 update)."""
+    s, l, nb = 16384, 65280, 256
+    bs, bl = s // nb, l // nb
+    rng = np.random.default_rng(11)
+    bits = wl.f64_to_bf16_bits(rng.standard_normal((nb, bs, bl)) / np.sqrt(bl))
+    exact = orc.widen_bf16(bits)
+    beta, lr = 0.95, 0.02
+    nu = (1 + beta) * np.sqrt(np.sum(exact * exact))
+    ref = np.stack([orc.ns_iterate((1 + beta) * exact[b] / (nu + 1e-7), 5) for b in range(nb)])
+    idx = torch.arange(nb, device="cuda")
+    Gw = torch.zeros((s, l), dtype=torch.bfloat16, device="cuda")
+    Gw.view(nb, bs, nb, bl)[idx, :, idx, :] = to_torch_bits(bits).cuda()
+    G = (Gw.t().contiguous() if tall else Gw).unsqueeze(0)
+    del Gw
+    m, n = G.shape[1:]
+    W = torch.zeros((1, m, n), dtype=torch.float32, device="cuda")
+    M = torch.zeros_like(W)
+    O = torch.full((1, m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mu.muon_step([mu.MuonGroup(W=W, M=M, G=G, O=O, lr=lr, beta=beta, nesterov=True)], steps=5)
+    torch.cuda.synchronize()
+    Ow = O[0].t() if tall else O[0]
+    blocks = Ow.reshape(nb, bs, nb, bl)[idx, :, idx, :] if not tall else \
+        torch.stack([Ow[b * bs:(b + 1) * bs, b * bl:(b + 1) * bl] for b in range(nb)])
+    err = orc.rel_frobenius(t64(blocks), ref)
+    print("max size", "tall" if tall else "wide", "rel_F", err, flush=True)
+    assert err <= BF16_TOL
+    O2 = O.clone()
+    O2v = (O2[0].t() if tall else O2[0])
+    if tall:
+        for b in range(nb):
+            O2v[b * bs:(b + 1) * bs, b * bl:(b + 1) * bl] = 0
+    else:
+        O2v.view(nb, bs, nb, bl)[idx, :, idx, :] = 0
+    assert int(torch.count_nonzero(O2)) == 0
+    del O2
+    assert torch.equal(W, O.float() * torch.tensor(-lr, dtype=torch.float32, device="cuda"))
+    assert torch.equal(M, G.float())
+
+
 def _injection_oracle(X, steps=1):
     return orc.ns_batched(X.float().cpu().numpy().astype(np.float64), steps)
 
