@@ -16,8 +16,8 @@
 //  * Combine D[k][i] = sum_j X[j][k] A[i][j] with the X operand gathered from
 //    LDS in the same contraction order; each lane then holds 4 consecutive
 //    columns of one row of Y = a X + b A X.
-//  * Y overwrites X in LDS (same wave, in order) and leaves through coalesced
-//    16-byte stores.
+//  * Y overwrites X in LDS one 32-column block at a time (same wave, in
+//    order) and leaves through coalesced 16-byte stores.
 // fp32 kernel: one workgroup per matrix, plain FMA dot products in LDS.
 #include "common.cuh"
 #include "launch.h"
@@ -49,8 +49,13 @@ struct SmallGeo {
   __device__ static int elem_off(int r, int k) { return chunk_off(r, k >> 3) + ((k & 7) << 1); }
 };
 
+// Two waves per SIMD where the registers allow it without spilling (up to
+// 64 x 128; larger shapes hold more accumulators).
+template <int S, int L> struct SmallWpe { static constexpr int v = S * L <= 64 * 128 ? 2 : 1; };
+
 template <int S, int L>
-__global__ void __launch_bounds__(WPB * 64) ns_small_bf16_kernel(NsSmallLaunch P) {
+__global__ void __launch_bounds__(WPB * 64) __attribute__((amdgpu_waves_per_eu(SmallWpe<S, L>::v)))
+ns_small_bf16_kernel(NsSmallLaunch P) {
   using Geo = SmallGeo<S, L>;
   constexpr int NB = S / 32;      // 32-row blocks of X (and of A)
   constexpr int NJ = S / 16;      // contraction steps over j in the combine
@@ -130,10 +135,14 @@ __global__ void __launch_bounds__(WPB * 64) ns_small_bf16_kernel(NsSmallLaunch P
           }
         }
       // ---- combine, one 32-column block of X at a time ----------------------
+      // Column block kb of X is read only by block kb of the combine, so Y's
+      // block kb replaces it in LDS right away (this wave's region; LDS
+      // operations of a wave execute in order) and only one block of Y is
+      // held in registers: two waves per SIMD instead of one.
       const float alpha = P.a[step] * sc, beta = P.b[step] * sc;
-      u32x2_t ypk[NK][NB][4];
-#pragma unroll
+#pragma unroll 1
       for (int kb = 0; kb < NK; ++kb) {
+        u32x2_t ypk[NB][4];
         f32x16_t c[NB];
 #pragma unroll
         for (int ib = 0; ib < NB; ++ib)
@@ -163,21 +172,18 @@ __global__ void __launch_bounds__(WPB * 64) ns_small_bf16_kernel(NsSmallLaunch P
             const float y1 = fmaf(alpha, hi_bf16(xv[0]), beta * c[ib][4 * q + 1]);
             const float y2 = fmaf(alpha, lo_bf16(xv[1]), beta * c[ib][4 * q + 2]);
             const float y3 = fmaf(alpha, hi_bf16(xv[1]), beta * c[ib][4 * q + 3]);
-            ypk[kb][ib][q] = u32x2_t{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+            ypk[ib][q] = u32x2_t{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
           }
-      }
-      // ---- Y replaces X in LDS (this wave's region only; LDS ops in order) --
-      wave_lds_sync();
-#pragma unroll
-      for (int kb = 0; kb < NK; ++kb)
+        wave_lds_sync();
 #pragma unroll
         for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int i = ib * 32 + l32, k = kb * 32 + 8 * q + 4 * G;
-            *reinterpret_cast<u32x2_t*>(lds + Geo::elem_off(i, k)) = ypk[kb][ib][q];
+            *reinterpret_cast<u32x2_t*>(lds + Geo::elem_off(i, k)) = ypk[ib][q];
           }
-      wave_lds_sync();
+        wave_lds_sync();
+      }
     }
 
     // ---- store (zero steps: the normalised input) ---------------------------
