@@ -200,11 +200,12 @@ struct FactLaunch {
   int m, n, r, m_pad, n_pad;  // pads: multiples of 16
   int vec;             // r == 8 and 16-byte aligned factors: 16-byte row loads
   int waves;           // wavefronts per workgroup
+  int per_wave, f_off; // LDS bytes per wavefront; offset of the r x r work matrices in it
   int steps;
   float eps;
   float a[64], b[64], c[64];
 };
-int factored_lds_per_wave(int m_pad, int n_pad, bool dense);
+int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off = nullptr);
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st);
 
 // Spectral diagnostics (a chunk of `count` matrices per launch).

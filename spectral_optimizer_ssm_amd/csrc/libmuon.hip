@@ -1004,7 +1004,8 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
   if (r > 8 || m > 256 || n > 256) return MUON_EUNSUPPORTED;
   if (O_out != nullptr && n % 8 != 0) return MUON_EUNSUPPORTED;
   const int m_pad = round_up(m, 16), n_pad = round_up(n, 16);
-  const int per_wave = factored_lds_per_wave(m_pad, n_pad, O_out != nullptr);
+  int f_off = 0;
+  const int per_wave = factored_lds_per_wave(m_pad, n_pad, O_out != nullptr, &f_off);
   if (per_wave > 65536) return MUON_EUNSUPPORTED;
   if (batch == 0) return MUON_OK;
   if (V == nullptr || K == nullptr || C_out == nullptr || !aligned_to(V, 2) || !aligned_to(K, 2) ||
@@ -1032,6 +1033,8 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
   F.m = m; F.n = n; F.r = r; F.m_pad = m_pad; F.n_pad = n_pad;
   F.vec = r == 8 && aligned16(V) && aligned16(K);
   F.waves = std::max(1, std::min(4, 65536 / per_wave));
+  F.per_wave = per_wave;
+  F.f_off = f_off;
   F.steps = C.steps;
   F.eps = cfg->eps;
   for (int k = 0; k < C.steps; ++k) { F.a[k] = C.a[k]; F.b[k] = C.b[k]; F.c[k] = C.c[k]; }

@@ -19,6 +19,12 @@
 // the MFMA operand (one column of 8 consecutive rows per lane) comes from
 // two ds_read_b64_tr_b16.  The r x r recurrence then runs on 16 lanes per
 // matrix, each lane owning 4 entries of one row, through LDS.
+//
+// Waves are persistent and walk the groups of four with a stride of the grid.
+// For 64 x 128 rank-8 injections with aligned factors (the MuonSSM shape) a
+// wave loads the next group's factors into registers (12 x 16 bytes per lane)
+// while it computes the current one, so the load latency overlaps the
+// recurrence; other shapes stage each group from memory in turn.
 #include "common.cuh"
 #include "launch.h"
 
@@ -27,6 +33,9 @@ namespace {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMats = 4;          // matrices per wavefront
+#ifndef FACT_WG_PER_CU
+#define FACT_WG_PER_CU 4
+#endif
 constexpr int kRow = 64;          // bytes per staged row (32 bf16 columns)
 
 __device__ __forceinline__ void wave_sync() {
@@ -104,21 +113,77 @@ __device__ void mm8(const WaveLds& L, int x, int y, int z, int lane) {
   wave_sync();
 }
 
+// Steps 2-6 for the four matrices b0 .. b0 + nm - 1 staged in L.vk.
+__device__ __forceinline__ void factored_compute(const FactLaunch& F, const WaveLds& L, long long b0, int nm,
+                                                 int lane);
+
+// Factors of one full group (four 64 x 128 rank-8 injections) in registers:
+// lane l holds V rows l + 64 e (e < 4) and K rows l + 64 e (e < 8) of the
+// group's concatenated rows, 16 bytes each.
+constexpr int kFastM = 64, kFastN = 128, kFastV = kMats * kFastM / 64, kFastK = kMats * kFastN / 64;
+struct FastRegs {
+  u32x4_t v[kFastV], k[kFastK];
+};
+__device__ __forceinline__ void fast_load(const FactLaunch& F, long long b0, int lane, FastRegs& R) {
+  const u32x4_t* Vg = reinterpret_cast<const u32x4_t*>(F.V + b0 * kFastM * 8);
+  const u32x4_t* Kg = reinterpret_cast<const u32x4_t*>(F.K + b0 * kFastN * 8);
+#pragma unroll
+  for (int e = 0; e < kFastV; ++e) R.v[e] = Vg[lane + 64 * e];
+#pragma unroll
+  for (int e = 0; e < kFastK; ++e) R.k[e] = Kg[lane + 64 * e];
+}
+// Row t of matrix q (t = e % m, q = e / m for concatenated row e) goes to
+// staged row t, bytes 16 q: with four full matrices every staged byte is
+// written, so no zero padding is needed.
+__device__ __forceinline__ void fast_stage(const WaveLds& L, int lane, const FastRegs& R) {
+#pragma unroll
+  for (int e = 0; e < kFastV; ++e) {
+    const int c = lane + 64 * e, q = c / kFastM, t = c % kFastM;
+    *reinterpret_cast<u32x4_t*>(L.vk + t * kRow + 16 * q) = R.v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < kFastK; ++e) {
+    const int c = lane + 64 * e, q = c / kFastN, u = c % kFastN;
+    *reinterpret_cast<u32x4_t*>(L.vk + (kFastM + u) * kRow + 16 * q) = R.k[e];
+  }
+}
+
 __global__ void __launch_bounds__(256) ns_factored_kernel(FactLaunch F) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = F.m_pad + F.n_pad;
-  const int per_wave = rows * kRow + kMats * 6 * 64 * 4 + (F.O != nullptr ? F.m_pad * 32 * 4 : 0);
-  char* base = lds + wave * per_wave;
+  char* base = lds + wave * F.per_wave;
   WaveLds L;
   L.vk = base;
-  L.f = reinterpret_cast<float*>(base + rows * kRow);
+  L.f = reinterpret_cast<float*>(base + F.f_off);
   L.t = reinterpret_cast<float*>(base + rows * kRow + kMats * 6 * 64 * 4);
-  const long long b0 = (static_cast<long long>(blockIdx.x) * F.waves + wave) * kMats;
-  if (b0 >= F.batch) return;
-  const int nm = F.batch - b0 < kMats ? static_cast<int>(F.batch - b0) : kMats;
   const int m = F.m, n = F.n, r = F.r;
+  // groups of four matrices, walked by every wave of the grid in turn
+  const long long groups = (F.batch + kMats - 1) / kMats;
+  const long long gstride = static_cast<long long>(gridDim.x) * F.waves;
+  long long gi = static_cast<long long>(blockIdx.x) * F.waves + wave;
+
+  // fast path (64 x 128, rank 8, aligned factors, full groups): the next
+  // group's factors are loaded into registers while this group is computed
+  if (F.vec && m == kFastM && n == kFastN && r == 8 && F.m_pad == kFastM && F.n_pad == kFastN) {
+    const long long full = F.batch / kMats;
+    if (gi < full) {
+      FastRegs R;
+      fast_load(F, gi * kMats, lane, R);
+      for (; gi < full; gi += gstride) {
+        fast_stage(L, lane, R);
+        wave_sync();
+        if (gi + gstride < full) fast_load(F, (gi + gstride) * kMats, lane, R);
+        factored_compute(F, L, gi * kMats, kMats, lane);
+      }
+    }
+    // the remaining partial group (at most one) takes the general path
+    if (gi != full || full * kMats == F.batch) return;
+  }
+  for (; gi < groups; gi += gstride) {
+  const long long b0 = gi * kMats;
+  const int nm = F.batch - b0 < kMats ? static_cast<int>(F.batch - b0) : kMats;
 
   // 1. stage V and K (zero padded) as [rows][32 bf16]
   for (int o = lane * 16; o < rows * kRow; o += 64 * 16)
@@ -148,10 +213,20 @@ __global__ void __launch_bounds__(256) ns_factored_kernel(FactLaunch F) {
     }
   }
   wave_sync();
+  factored_compute(F, L, b0, nm, lane);
+  }
+}
 
-  // 2. P = V^T V and S = K^T K on the matrix cores
-  store_blocks(gram32(L.vk, 0, F.m_pad, lane), L, kP, lane);
-  store_blocks(gram32(L.vk, F.m_pad, F.n_pad, lane), L, kS, lane);
+__device__ __forceinline__ void factored_compute(const FactLaunch& F, const WaveLds& L, long long b0, int nm,
+                                                 int lane) {
+  const int m = F.m, n = F.n, r = F.r;
+  // 2. P = V^T V and S = K^T K on the matrix cores; both are read before
+  // either is stored (the work matrices may share the staging area)
+  const f32x16_t gp = gram32(L.vk, 0, F.m_pad, lane);
+  const f32x16_t gq = gram32(L.vk, F.m_pad, F.n_pad, lane);
+  wave_sync();
+  store_blocks(gp, L, kP, lane);
+  store_blocks(gq, L, kS, lane);
   wave_sync();
 
   // 3. nu^2 = tr(P S) per matrix (16 lanes each), C_0 = I_r / (nu + eps)
@@ -251,14 +326,34 @@ __global__ void __launch_bounds__(256) ns_factored_kernel(FactLaunch F) {
 
 }  // namespace
 
-int factored_lds_per_wave(int m_pad, int n_pad, bool dense) {
-  return (m_pad + n_pad) * kRow + kMats * 6 * 64 * 4 + (dense ? m_pad * 32 * 4 : 0);
+// Without the dense output the r x r work matrices share the staging area:
+// the Gram has read the staged factors before the recurrence writes them, and
+// the next group is staged only after the core has been stored (one wave, LDS
+// operations in order).
+int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off) {
+  const int stage = (m_pad + n_pad) * kRow, work = kMats * 6 * 64 * 4;
+  if (!dense) {
+    if (f_off) *f_off = 0;
+    return stage > work ? stage : work;
+  }
+  if (f_off) *f_off = stage;
+  return stage + work + m_pad * 32 * 4;
 }
 
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st) {
   const long long groups = (F.batch + kMats - 1) / kMats;
-  const long long blocks = (groups + F.waves - 1) / F.waves;
-  const size_t lds = static_cast<size_t>(F.waves) * factored_lds_per_wave(F.m_pad, F.n_pad, F.O != nullptr);
+  // persistent waves: a few resident workgroups per CU walk the groups
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const long long need = (groups + F.waves - 1) / F.waves;
+  const long long cap = static_cast<long long>(cus) * FACT_WG_PER_CU;
+  const long long blocks = need < cap ? need : cap;
+  const size_t lds = static_cast<size_t>(F.waves) * F.per_wave;
   hipLaunchKernelGGL(ns_factored_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64 * F.waves), lds, st, F);
   return hipGetLastError();
 }
