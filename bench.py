@@ -532,7 +532,10 @@ def bench_diag(args, torch, mu, wl):
     full step: the largest singular value checked every few steps), with
     --diag-input updates their bf16 Muon updates (5 NS steps of bf16 N(0, 1)
     gradients: the orthogonality error of the update).  Per-pass durations
-    from HIP events recorded by muon_spectral_diag_timed."""
+    from HIP events recorded by muon_spectral_diag_timed.  With 24 matrices
+    per call the Lanczos pass runs as the split kernel (six co-resident
+    workgroups per matrix); its algorithmic bytes count the whole of H per
+    step, although the kernel reads only the upper block triangle."""
     stacks = []
     for name, a in wl.projection_stacks(args.count):
         if args.diag_input == "weights":
@@ -569,7 +572,7 @@ def bench_diag(args, torch, mu, wl):
     # algorithmic work per launch: pack reads A and writes the operand rows;
     # the Gram's six (float32 input) or one (bf16) bf16 products of
     # s (s + 1) l flops (upper triangle); Lanczos reads H once per step
-    kern = {"diag_pack_kernel": [0.0, 0.0], "symprod_bf16_kernel<F32>": [0.0, 0.0], "diag_lanczos_kernel": [0.0, 0.0]}
+    kern = {"diag_pack_kernel": [0.0, 0.0], "symprod_bf16_kernel<F32>": [0.0, 0.0], "diag_lanczos_split_kernel": [0.0, 0.0]}
     for si, (name, A) in enumerate(stacks):
         cnt, m, n = A.shape
         s_, l_ = min(m, n), max(m, n)

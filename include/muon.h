@@ -305,7 +305,14 @@ size_t muon_spectral_diag_workspace_size(int m, int n, long long batch, int dtyp
  * float32, the tridiagonal extremes float64.  Supported: min(m, n) <= 4096,
  * max(m, n) <= 2^22, 1 <= iters <= 512 (larger: MUON_EUNSUPPORTED; iters < 1:
  * MUON_EINVAL).  A NaN or Inf in A[b] gives NaN outputs for b.
- * Deterministic; no allocation; asynchronous on `stream`. */
+ * When one workgroup per matrix would leave most compute units idle, the
+ * Lanczos pass runs as one cooperative launch with several workgroups per
+ * matrix that exchange partial products through the workspace (their waits
+ * are bounded: a matrix whose workgroups ever gave up waiting gets NaN
+ * outputs); if the device refuses that launch, one workgroup per matrix is
+ * used.  Deterministic for a given device (the split depends on its compute
+ * unit count); no allocation; asynchronous on `stream`; calls that share a
+ * workspace must not overlap. */
 int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,
                        float* sigma_max, float* sigma_min, void* workspace, size_t workspace_bytes,
                        void* stream);

@@ -219,20 +219,27 @@ struct DiagPackLaunch {
   long long ostride;   // s_pad * ld
   int s_pad, kdim, ld; // s_pad % 128 == 0, kdim % 64 == 0, ld = kdim (bf16) or 6 kdim
   long long count;
+  unsigned* clr;       // split run: the first clr_words words of each matrix's scratch
+  long long cstride;   //   (stride cstride) are zeroed; or null
+  long long clr_words;
 };
 hipError_t launch_diag_pack(const DiagPackLaunch& P, hipStream_t st);
 struct DiagLaunch {
   const float* H;      // [count][s_pad][s_pad] Gram matrices (exactly symmetric)
   long long hstride;
-  float* Q;            // [count][kmax][s_pad] Lanczos basis (scratch)
+  float* Q;            // [count][kmax][s_pad] Lanczos basis, or the split run's scratch
   long long qstride;
   int s, s_pad, iters, kmax;
+  int split_p, split_r, split_nb;  // split run (set by the planner): blocks per side, row ranges, workgroups
   float* orth;         // [count] or null
   float* smax;         // [count] or null
   float* smin;         // [count] or null
   long long count;
 };
 size_t diag_lanczos_lds(int s_pad, int kmax);
+// Plans the launch (split run or one workgroup per matrix); returns the
+// 32-bit words of each matrix's scratch to zero beforehand (0: none).
+long long diag_split_clear_words(DiagLaunch& D);
 hipError_t launch_diag_lanczos(const DiagLaunch& D, hipStream_t st);
 
 // AdamW over a list of float32 tensors (one launch: up to kAdamwMax tensors).

@@ -1088,6 +1088,19 @@ int muon_spectral_diag_timed(const void* A, int dtype, int m, int n, long long b
     P.ostride = static_cast<long long>(p.op_bytes / 2);
     P.s_pad = p.s_pad; P.kdim = p.kdim; P.ld = p.ld;
     P.count = cnt;
+    DiagLaunch D{};
+    D.H = H;
+    D.hstride = static_cast<long long>(p.h_bytes / 4);
+    D.Q = Q;
+    D.qstride = static_cast<long long>(p.q_bytes / 4);
+    D.s = p.s; D.s_pad = p.s_pad; D.iters = iters; D.kmax = p.k;
+    D.orth = orth_err ? orth_err + c0 : nullptr;
+    D.smax = sigma_max ? sigma_max + c0 : nullptr;
+    D.smin = sigma_min ? sigma_min + c0 : nullptr;
+    D.count = cnt;
+    P.clr_words = diag_split_clear_words(D);
+    P.clr = P.clr_words > 0 ? reinterpret_cast<unsigned*>(Q) : nullptr;
+    P.cstride = D.qstride;
     if (launch_diag_pack(P, st) != hipSuccess || !mark()) return MUON_EHIP;
     SymArgs G{};
     SymSeg& S = G.seg[0];
@@ -1104,16 +1117,6 @@ int muon_spectral_diag_timed(const void* A, int dtype, int m, int n, long long b
     S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);
     S.a1 = 0.0f; S.b1 = 1.0f;
     if (launch_symprod_bf16(G, st) != hipSuccess || !mark()) return MUON_EHIP;
-    DiagLaunch D{};
-    D.H = H;
-    D.hstride = S.stride;
-    D.Q = Q;
-    D.qstride = static_cast<long long>(p.q_bytes / 4);
-    D.s = p.s; D.s_pad = p.s_pad; D.iters = iters; D.kmax = p.k;
-    D.orth = orth_err ? orth_err + c0 : nullptr;
-    D.smax = sigma_max ? sigma_max + c0 : nullptr;
-    D.smin = sigma_min ? sigma_min + c0 : nullptr;
-    D.count = cnt;
     if (launch_diag_lanczos(D, st) != hipSuccess || !mark()) return MUON_EHIP;
   }
   return MUON_OK;

@@ -187,3 +187,16 @@ def test_diag_of_newton_schulz_output(mu):
         assert np.all(np.abs(e - ref) <= ORTH_ABS + ORTH_REL * np.array(ref))
         errs.append(e.mean())
     assert errs[0] > errs[1] > errs[2]
+
+
+def test_diag_workspace_reuse_across_calls(mu):
+    """Three calls on one workspace, with different matrices and step counts
+    (the split run's tagged partials of an earlier call must never be taken
+    for this call's): every call matches the oracle."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for seed, (m, n, it) in enumerate(((300, 300, 24), (300, 300, 12), (256, 640, 20))):
+        A, exact = to_device(stack(100 + seed, 5, m, n, "spread"), "bf16")
+        out = mu.muon_spectral_diag(A, iters=it, workspace=ws)
+        torch.cuda.synchronize()
+        out = {k: v.cpu().numpy() for k, v in out.items()}
+        check(out, exact, it, range(5))
