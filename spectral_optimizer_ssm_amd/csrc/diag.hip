@@ -268,7 +268,7 @@ int sym_matvec_splits(int sp, int nw) {
 }
 
 __global__ void __launch_bounds__(1024) diag_lanczos_kernel(DiagLaunch D) {
-  extern __shared__ float sh[];
+  extern __shared__ __attribute__((aligned(16))) float sh[];  // 16-byte LDS accesses need the base aligned
   const int sp = D.s_pad, s = D.s;
   float* q = sh;                 // [sp]
   float* w = q + sp;             // [sp]
@@ -627,7 +627,7 @@ __device__ double tri_matvec(const float* H, int s, int sp, int ra0, int rb0, in
 }
 
 __global__ void __launch_bounds__(kSplitThreads) diag_lanczos_split_kernel(DiagLaunch D) {
-  extern __shared__ float sh[];
+  extern __shared__ __attribute__((aligned(16))) float sh[];  // 16-byte LDS accesses need the base aligned
   const int sp = D.s_pad, s = D.s, P = D.split_p, R = D.split_r, nb = D.split_nb;
   float* Qs = sh;                          // [kmax][sp] basis
   float* w = Qs + static_cast<long long>(D.kmax) * sp;  // [sp]
