@@ -569,7 +569,8 @@ def bench_diag(args, torch, mu, wl):
             mu.muon_spectral_diag(A, iters=it, workspace=ws, events=[e.cuda_event for e in ev])
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    # algorithmic work per launch: pack reads A and writes the operand rows;
+    # algorithmic work per launch: pack reads A and writes the operand rows
+    # (three bf16 pieces per float32 element);
     # the Gram's six (float32 input) or one (bf16) bf16 products of
     # s (s + 1) l flops (upper triangle); Lanczos reads H once per step
     kern = {"diag_pack_kernel": [0.0, 0.0], "symprod_bf16_kernel<F32>": [0.0, 0.0], "diag_lanczos_split_kernel": [0.0, 0.0]}
@@ -577,9 +578,10 @@ def bench_diag(args, torch, mu, wl):
         cnt, m, n = A.shape
         s_, l_ = min(m, n), max(m, n)
         f32 = A.dtype == torch.float32
-        pieces = 6 if f32 else 1
+        pieces = 6 if f32 else 1  # products summed by the Gram
+        stored = 3 if f32 else 1  # bf16 pieces the pack writes per element
         s_pad, kdim = -(-s_ // 128) * 128, -(-l_ // 64) * 64
-        work = [cnt * (m * n * A.element_size() + (2 if f32 else 1) * s_pad * pieces * kdim * 2),
+        work = [cnt * (m * n * A.element_size() + s_pad * stored * kdim * 2),
                 cnt * pieces * s_ * (s_ + 1) * l_,
                 cnt * (min(it, s_) + 1) * s_ * s_ * 4]
         for p, key in enumerate(kern):

@@ -12,9 +12,10 @@
 //   diag_pack_kernel     orient X (transposing tall inputs through LDS) into
 //                        bf16 operand rows for the symmetric-product kernel;
 //                        float32 inputs are split exactly into three bf16
-//                        pieces x = h + d + e and the operand rows carry the six
-//                        products that matter, h h + h d + d h + d d + h e + e h,
-//                        as L = [h h d d h e], R = [h d h d e h]
+//                        pieces x = h + d + e, stored once side by side; the
+//                        Gram contracts over six segments that pair them as the
+//                        six products that matter, hh + hd + dh + dd + he + eh
+//                        (L segments h h d d h e, R segments h d h d e h)
 //   symprod (float32 output) H = L R^T on the matrix cores
 //   diag_lanczos_kernel  one workgroup per matrix: ||H - I|| in float64, then
 //                        the Lanczos run in float32 with its vectors in LDS and
@@ -77,12 +78,9 @@ __global__ void __launch_bounds__(256) diag_pack_kernel(DiagPackLaunch P) {
       const bf16_t d = f32_to_bf16(xd);
       const bf16_t e = f32_to_bf16(xd - bf16_to_f32(d));
       const long long K = P.kdim;
-      P.L[o] = h;         P.R[o] = h;
-      P.L[o + K] = h;     P.R[o + K] = d;
-      P.L[o + 2 * K] = d; P.R[o + 2 * K] = h;
-      P.L[o + 3 * K] = d; P.R[o + 3 * K] = d;
-      P.L[o + 4 * K] = h; P.R[o + 4 * K] = e;
-      P.L[o + 5 * K] = e; P.R[o + 5 * K] = h;
+      P.L[o] = h;
+      P.L[o + K] = d;
+      P.L[o + 2 * K] = e;
     }
   }
 }

@@ -753,7 +753,7 @@ symprod_bf16_kernel(SymArgs G) {
     int bi, bj;
     upper_tile(tile % S.tiles_per_mat, S.s_pad / TT, bi, bj);
     const bool diag = bi == bj;
-    const bool single = diag && S.L == S.R;  // both operands are the same rows
+    const bool single = diag && S.L == S.R && (!F32 || S.lmap == S.rmap);  // both operands are the same rows
     const long long zoff = z * S.stride;                 // outputs
     const long long zin = z * S.in_stride;               // operands
     const float inv = seg_inv(S, z, red);
@@ -787,9 +787,21 @@ symprod_bf16_kernel(SymArgs G) {
         dma16(rs, sym_tvoff<TT>(blk, lane, sp_bytes), soff, op + blk * 1024);
       }
     };
-    auto fill_op = [&](char* op, __amdgpu_buffer_rsrc_t rs, int b, int off, int kt) {
+    // column offset (bytes) of stage kt in the rows of L (map = lmap) or R
+    auto kcol = [&](int kt, unsigned map) {
+      if constexpr (F32) {
+        if (S.kseg > 0) {
+          const int per = S.kseg / BK;
+          int g = 0;
+          while (kt >= (g + 1) * per) ++g;  // at most 7 segments
+          return (static_cast<int>((map >> (4 * g)) & 0xfu) * S.kseg + (kt - g * per) * BK) * 2;
+        }
+      }
+      return kt * BK * 2;
+    };
+    auto fill_op = [&](char* op, __amdgpu_buffer_rsrc_t rs, int b, int off, int kt, unsigned map = 0u) {
       if (tri && kt / kbs < b) fill_t(op, rs, kt * BK * sp_bytes + b * TT * 2);
-      else fill_rows(op, rs, off + kt * BK * 2);
+      else fill_rows(op, rs, off + kcol(kt, map));
     };
     auto mma = [&](const char* buf, int kt, bool one) {
       const int kb = kt / kbs;
@@ -825,28 +837,28 @@ symprod_bf16_kernel(SymArgs G) {
         else stage_mma_single<FM, FN>(acc, fa_r, fb_r);
       };
       if (single) {
-        pipeline3<BPW>(bufs, nk, k2, k1, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt); },
+        pipeline3<BPW>(bufs, nk, k2, k1, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt, S.lmap); },
                        [&](const char* buf, int) { body(buf, true, IntC<2>{}); },
                        [&](const char* buf, int) { body(buf, true, IntC<1>{}); },
                        [&](const char* buf, int) { body(buf, true, IntC<0>{}); });
       } else {
         pipeline3<2 * BPW>(bufs, nk, k2, k1,
                            [&](char* buf, int kt) {
-                             fill_op(buf, lr, bi, offL, kt);
-                             fill_op(buf + OPBT, rr, bj, offR, kt);
+                             fill_op(buf, lr, bi, offL, kt, S.lmap);
+                             fill_op(buf + OPBT, rr, bj, offR, kt, S.rmap);
                            },
                            [&](const char* buf, int) { body(buf, false, IntC<2>{}); },
                            [&](const char* buf, int) { body(buf, false, IntC<1>{}); },
                            [&](const char* buf, int) { body(buf, false, IntC<0>{}); });
       }
     } else if (single) {
-      pipeline<BPW>(bufs, nk, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt); },
+      pipeline<BPW>(bufs, nk, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt, S.lmap); },
                     [&](const char* buf, int kt) { mma(buf, kt, true); });
     } else {
       pipeline<2 * BPW>(bufs, nk,
                         [&](char* buf, int kt) {
-                          fill_op(buf, lr, bi, offL, kt);
-                          fill_op(buf + OPBT, rr, bj, offR, kt);
+                          fill_op(buf, lr, bi, offL, kt, S.lmap);
+                          fill_op(buf + OPBT, rr, bj, offR, kt, S.rmap);
                         },
                         [&](const char* buf, int kt) { mma(buf, kt, false); });
     }

@@ -158,6 +158,11 @@ struct SymSeg {
   int tri_in;          // 1: L and R hold only their upper block triangle (tile-sized
                        // blocks on and above the diagonal); the others are read transposed
   int tri_out;         // 1: O1 and O2 get only their upper block triangle
+  int kseg;            // float32-output runs: > 0 splits the contraction into kdim / kseg
+                       // segments of kseg columns; segment g of L reads columns
+                       // [lmap_g kseg, (lmap_g + 1) kseg) of the rows, of R those of
+                       // rmap_g (4 bits per segment); 0: the columns in order
+  unsigned lmap, rmap;
 };
 struct SymArgs {
   SymSeg seg[kMaxSeg];
@@ -214,10 +219,10 @@ struct DiagPackLaunch {
   long long astride;   // m * n
   int n, s, l;         // row stride of A; short and long side
   bool tall, f32;
-  bf16_t* L;           // [count][s_pad][ld] operand rows (X, or its pieces)
-  bf16_t* R;           // float32 inputs: the partner pieces; else null (R = L)
+  bf16_t* L;           // [count][s_pad][ld] operand rows: X, or for float32 inputs its
+                       // three bf16 pieces side by side [h | d | e]
   long long ostride;   // s_pad * ld
-  int s_pad, kdim, ld; // s_pad % 128 == 0, kdim % 64 == 0, ld = kdim (bf16) or 6 kdim
+  int s_pad, kdim, ld; // s_pad % 128 == 0, kdim % 64 == 0, ld = kdim (bf16) or 3 kdim
   long long count;
   unsigned* clr;       // split run: the first clr_words words of each matrix's scratch
   long long cstride;   //   (stride cstride) are zeroed; or null

@@ -801,7 +801,7 @@ struct DiagPlan {
   bool tall, f32;
   size_t op_bytes, h_bytes, q_bytes;  // per matrix
   long long chunk;                    // matrices per pass
-  size_t off_l, off_r, off_h, off_q, end;
+  size_t off_l, off_h, off_q, end;
 };
 
 int plan_diag(int m, int n, long long batch, int dtype, int iters, DiagPlan* p) {
@@ -815,18 +815,17 @@ int plan_diag(int m, int n, long long batch, int dtype, int iters, DiagPlan* p) 
   p->s_pad = round_up(p->s, 128);
   if (p->l > (1 << 22)) return MUON_EUNSUPPORTED;
   p->kdim = round_up(p->l, 64);
-  p->ld = p->kdim * (p->f32 ? 6 : 1);
+  p->ld = p->kdim * (p->f32 ? 3 : 1);
   if (static_cast<long long>(p->s_pad) * p->ld * 2 >= (1LL << 31)) return MUON_EUNSUPPORTED;  // 32-bit offsets
   p->k = std::min(iters, p->s);
   p->op_bytes = align_up(static_cast<size_t>(p->s_pad) * p->ld * 2, kAlign);
   p->h_bytes = align_up(static_cast<size_t>(p->s_pad) * p->s_pad * 4, kAlign);
   p->q_bytes = align_up(static_cast<size_t>(p->k) * p->s_pad * 4, kAlign);
-  const size_t per = p->op_bytes * (p->f32 ? 2 : 1) + p->h_bytes + p->q_bytes;
+  const size_t per = p->op_bytes + p->h_bytes + p->q_bytes;
   p->chunk = std::max<long long>(1, std::min<long long>(batch, static_cast<long long>(kDiagChunkBytes / per)));
   const size_t c = static_cast<size_t>(p->chunk);
   p->off_l = 0;
-  p->off_r = p->off_l + c * p->op_bytes;
-  p->off_h = p->off_r + (p->f32 ? c * p->op_bytes : 0);
+  p->off_h = p->off_l + c * p->op_bytes;
   p->off_q = p->off_h + c * p->h_bytes;
   p->end = p->off_q + c * p->q_bytes;
   return MUON_OK;
@@ -1069,7 +1068,6 @@ int muon_spectral_diag_timed(const void* A, int dtype, int m, int n, long long b
   const hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   bf16_t* L = reinterpret_cast<bf16_t*>(ws + p.off_l);
-  bf16_t* R = p.f32 ? reinterpret_cast<bf16_t*>(ws + p.off_r) : nullptr;
   float* H = reinterpret_cast<float*>(ws + p.off_h);
   float* Q = reinterpret_cast<float*>(ws + p.off_q);
   int ev = 0;
@@ -1084,7 +1082,7 @@ int muon_spectral_diag_timed(const void* A, int dtype, int m, int n, long long b
     P.astride = static_cast<long long>(m) * n;
     P.n = n; P.s = p.s; P.l = p.l;
     P.tall = p.tall; P.f32 = p.f32;
-    P.L = L; P.R = R;
+    P.L = L;
     P.ostride = static_cast<long long>(p.op_bytes / 2);
     P.s_pad = p.s_pad; P.kdim = p.kdim; P.ld = p.ld;
     P.count = cnt;
@@ -1106,12 +1104,19 @@ int muon_spectral_diag_timed(const void* A, int dtype, int m, int n, long long b
     SymSeg& S = G.seg[0];
     G.nseg = 1;
     S.L = L;
-    S.R = p.f32 ? R : L;
+    S.R = L;
     S.F = H;
     S.stride = static_cast<long long>(p.h_bytes / 4);
     S.in_stride = P.ostride;
     S.ld = p.ld;
-    S.kdim = p.ld;  // contraction over every piece
+    if (p.f32) {  // six segments over the pieces [h | d | e]: hh + hd + dh + dd + he + eh
+      S.kdim = 6 * p.kdim;
+      S.kseg = p.kdim;
+      S.lmap = 0x201100u;  // segments 0..5 of L: h h d d h e
+      S.rmap = 0x021010u;  // segments 0..5 of R: h d h d e h
+    } else {
+      S.kdim = p.kdim;
+    }
     S.s_pad = p.s_pad;
     S.count = static_cast<int>(cnt);
     S.tiles_per_mat = symprod_tiles_per_matrix(p.s_pad);

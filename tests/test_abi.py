@@ -335,8 +335,9 @@ def test_spectral_diag_workspace_sizes(mu):
     s_pad, kdim, k = 768, 1536, 32
     per = s_pad * kdim * 2 + s_pad * s_pad * 4 + k * s_pad * 4
     assert L.muon_spectral_diag_workspace_size(768, 1536, 24, mu.MUON_BF16, 32) == 24 * per
-    # float32 inputs: two operands of six pieces each; tall is oriented
-    per32 = 2 * s_pad * 6 * 3392 * 2 + s_pad * s_pad * 4 + k * s_pad * 4
+    # float32 inputs: one operand array holding the three bf16 pieces side by
+    # side; tall is oriented
+    per32 = s_pad * 3 * 3392 * 2 + s_pad * s_pad * 4 + k * s_pad * 4
     assert L.muon_spectral_diag_workspace_size(3352, 768, 4, mu.MUON_F32, 32) == 4 * per32
     # chunked: the size stops growing once a chunk is full
     big = L.muon_spectral_diag_workspace_size(64, 128, 393216, mu.MUON_BF16, 64)
