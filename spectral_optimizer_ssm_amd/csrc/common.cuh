@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace muon {
 
 constexpr int kWave = 64;          // CDNA wavefront width
@@ -75,6 +77,20 @@ __device__ __forceinline__ float inv_norm_from_partials(const float* part, int n
   const float nu = sqrtf(s);
   if (nu_out) *nu_out = nu;
   return 1.0f / (nu + eps);
+}
+
+// Compute units of the current device, cached per device (relaxed atomics:
+// concurrent first calls store the same value); 256 if the query fails.
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 }  // namespace muon

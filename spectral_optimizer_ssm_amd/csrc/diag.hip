@@ -30,6 +30,8 @@
 //                        the vector work on its own copy of the basis in LDS
 //                        (identical arithmetic, so the copies stay equal).
 // Every reduction runs in a fixed order: results are deterministic.
+#include <mutex>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -904,16 +906,22 @@ struct SplitDevice {
 // matrix's basis region.
 int plan_split(DiagLaunch& D, size_t* lds) {
   static SplitDevice devs[64];
+  static std::mutex devs_mu;
   D.split_p = D.split_r = D.split_nb = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  SplitDevice& sd = devs[dev];
-  if (!sd.ok) {
-    if (hipDeviceGetAttribute(&sd.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&sd.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&sd.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      return 0;
-    sd.ok = true;
+  SplitDevice sd;
+  {
+    std::lock_guard<std::mutex> lock(devs_mu);
+    SplitDevice& cached = devs[dev];
+    if (!cached.ok) {
+      if (hipDeviceGetAttribute(&cached.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cached.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cached.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return 0;
+      cached.ok = true;
+    }
+    sd = cached;
   }
   const int k = D.iters < D.s ? D.iters : D.s;
   if (D.count <= 0 || !sd.coop || sd.cus <= 0 || k < 2) return 0;

@@ -972,13 +972,7 @@ template <int TT, bool F32>
 hipError_t launch_symprod_tt(const SymArgs& G, hipStream_t st) {
   // persistent: kWpe resident workgroups per CU (LDS bound), a multiple of
   // the XCD count
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
+  const int cus = device_cus();
   const int slots = (SymCfg<TT>::kWpe * cus) / NXCD * NXCD;
   const int need = grid_for_zip(G);
   const int grid = need < slots ? need : slots;

@@ -343,13 +343,7 @@ int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off) {
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st) {
   const long long groups = (F.batch + kMats - 1) / kMats;
   // persistent waves: a few resident workgroups per CU walk the groups
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
+  const int cus = device_cus();
   const long long need = (groups + F.waves - 1) / F.waves;
   const long long cap = static_cast<long long>(cus) * FACT_WG_PER_CU;
   const long long blocks = need < cap ? need : cap;
