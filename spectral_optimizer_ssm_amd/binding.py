@@ -157,6 +157,26 @@ def _split(x) -> list:
     return list(x)
 
 
+def _table(x, shape, what):
+    """(device pointer array, count, a tensor of the group) for x: a
+    contiguous [count, *shape] tensor, whose pointers are computed from its
+    base address (no per-matrix views: this runs on every step), or a
+    sequence of contiguous tensors of `shape`."""
+    if hasattr(x, "dim") and x.dim() == len(shape) + 1:
+        if not x.is_contiguous() or tuple(x.shape[1:]) != tuple(shape):
+            raise ValueError(f"{what} must be a contiguous [count, {', '.join(map(str, shape))}] tensor")
+        count, step = x.shape[0], x.element_size()
+        for d in shape:
+            step *= d
+        base = x.data_ptr()
+        return (ctypes.c_void_p * count)(*range(base, base + count * step, step)), count, x
+    ts = list(x)
+    for t in ts:
+        if not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"every entry of {what} must be a contiguous {' x '.join(map(str, shape))} tensor")
+    return _ptrs(ts), len(ts), (ts[0] if ts else None)
+
+
 @dataclass
 class MuonGroup:
     """One shape group.  W, M: float32; G: bf16 or float32; O: optional output.
@@ -182,27 +202,28 @@ class MuonGroup:
 def _marshal_groups(groups: Sequence[MuonGroup]):
     keep, cgroups = [], []
     for g in groups:
-        W, M, G, O = _split(g.W), _split(g.M), _split(g.G), _split(g.O)
-        m, n = W[0].shape
-        for t in W + M + G + (O or []):
-            if not t.is_contiguous() or tuple(t.shape) != (m, n):
-                raise ValueError("every matrix of a group must be a contiguous m x n tensor")
-        pw, pm, pg = _ptrs(W), _ptrs(M), _ptrs(G)
-        po = _ptrs(O) if O is not None else None
-        keep += [pw, pm, pg, po, W, M, G, O]
+        w0 = g.W if hasattr(g.W, "dim") and g.W.dim() == 3 else list(g.W)[0]
+        m, n = (g.W.shape[1:] if w0 is g.W else w0.shape)
+        m, n = int(m), int(n)
+        pw, count, wt = _table(g.W, (m, n), "W")
+        pm, cm, _ = _table(g.M, (m, n), "M")
+        pg, cgr, gt = _table(g.G, (m, n), "G")
+        po, co = (None, count) if g.O is None else _table(g.O, (m, n), "O")[:2]
+        if not count == cm == cgr == co:
+            raise ValueError("W, M, G (and O) must hold the same number of matrices")
+        keep += [pw, pm, pg, po, g.W, g.M, g.G, g.O]
         cu = cv = None
         sig = None
         if g.cap_u is not None:
-            U1, V1 = _split(g.cap_u), _split(g.cap_v)
-            for t, size in [(t, m) for t in U1] + [(t, n) for t in V1]:
-                if not t.is_contiguous() or t.numel() != size or t.dtype != W[0].dtype:
-                    raise ValueError("cap_u / cap_v must hold contiguous float32 vectors of length m / n")
-            if not g.cap_sigma.is_contiguous() or g.cap_sigma.numel() != len(W):
+            cu, cnu, ut = _table(g.cap_u, (m,), "cap_u")
+            cv, cnv, vt = _table(g.cap_v, (n,), "cap_v")
+            if cnu != count or cnv != count or ut.dtype != wt.dtype or vt.dtype != wt.dtype:
+                raise ValueError("cap_u / cap_v must hold one float32 vector of length m / n per matrix")
+            if not g.cap_sigma.is_contiguous() or g.cap_sigma.numel() != count:
                 raise ValueError("cap_sigma must be a contiguous float32 tensor with one entry per matrix")
-            cu, cv = _ptrs(U1), _ptrs(V1)
             sig = ctypes.c_void_p(g.cap_sigma.data_ptr())
-            keep += [cu, cv, U1, V1, g.cap_sigma]
-        cgroups.append(GroupC(int(m), int(n), len(W), _dtype_code(G[0]),
+            keep += [cu, cv, g.cap_u, g.cap_v, g.cap_sigma]
+        cgroups.append(GroupC(m, n, count, _dtype_code(gt),
                               ctypes.cast(pw, ctypes.POINTER(ctypes.c_void_p)),
                               ctypes.cast(pm, ctypes.POINTER(ctypes.c_void_p)),
                               ctypes.cast(pg, ctypes.POINTER(ctypes.c_void_p)),
@@ -256,7 +277,8 @@ def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7
         rc = L.muon_step(cg, len(groups), ctypes.byref(cfg), None, 0, None, None)
         _check(MUON_EINVAL if rc in (MUON_OK, MUON_EWORKSPACE) else rc, "muon_step")
     if workspace is None or workspace.numel() < need:
-        dev = _split(groups[0].W)[0].device
+        w = groups[0].W
+        dev = (w if hasattr(w, "device") else list(w)[0]).device
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     nptr = ctypes.cast(ctypes.c_void_p(norms_out.data_ptr()), ctypes.POINTER(ctypes.c_float)) \
         if norms_out is not None else None

@@ -11,8 +11,10 @@
 // All passes are deterministic (fixed-order partial sums, no atomics):
 //   cap_coef_kernel         per-block partials of u^T O v over the oriented
 //                           final iterate X (O = X, or X^T for tall matrices);
-//   power_partials_kernel   one read of W': W' v complete per 32-row block,
-//                           partials of W'^T u over those rows, norm partials;
+//   power_partials_kernel   one read of W': W' v complete per 32-row block
+//                           (lane shares kept in registers, one wave sum per
+//                           row), partials of W'^T u over those rows, norm
+//                           partials;
 //   power_zsum_kernel       W'^T u from its partials;
 //   power_normalize_kernel  writes u, v, sigma.
 #include "common.cuh"
@@ -73,9 +75,11 @@ __global__ void __launch_bounds__(256) cap_coef_kernel(CapCoefLaunch L) {
 }
 
 // One read of W (m x n fp32) for both products of the power step.  A block
-// owns 32 full rows: y_r = (W v)_r is complete within it (lane partials, wave
-// butterflies, the four waves summed in order), written with its square to
-// the per-block norm partial; (W^T u)_j gets a partial over the 32 rows.
+// owns 32 full rows: each lane keeps its share of y_r = (W v)_r for the 32
+// rows in registers across the columns it reads, and each row is summed over
+// the wave once at the end (DPP), the four waves in order; y_r is written with
+// its square to the per-block norm partial.  (W^T u)_j gets a partial over the
+// 32 rows.
 constexpr int kPowRows = 32;
 __global__ void __launch_bounds__(256) power_partials_kernel(PowerLaunch L) {
   __shared__ float yw[4][kPowRows];
@@ -84,88 +88,91 @@ __global__ void __launch_bounds__(256) power_partials_kernel(PowerLaunch L) {
   const float* u = static_cast<const float*>(L.u.p[z]);
   const float* v = static_cast<const float*>(L.v.p[z]);
   const int r0 = blockIdx.x * kPowRows;
+  const int rows = L.m - r0 < kPowRows ? L.m - r0 : kPowRows;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool vec = (L.n % 4) == 0 && ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(v)) & 15u) == 0;
   float* zp = L.zpart + (static_cast<long long>(z) * L.nrc + blockIdx.x) * L.n;
+  float yacc[kPowRows];
+#pragma unroll
+  for (int i = 0; i < kPowRows; ++i) yacc[i] = 0.0f;
   if (vec) {
     const int groups = L.n / 4;
-    // column groups of this thread: g = threadIdx.x + 256 k (at most 8: n <= 8192)
-    for (int g0 = 0; g0 < groups; g0 += 256 * 2) {
-      const int ga = g0 + threadIdx.x, gb = ga + 256;
-      const bool ina = ga < groups, inb = gb < groups;
-      const f32x4_t va = ina ? *reinterpret_cast<const f32x4_t*>(v + 4 * ga) : f32x4_t{0, 0, 0, 0};
-      const f32x4_t vb = inb ? *reinterpret_cast<const f32x4_t*>(v + 4 * gb) : f32x4_t{0, 0, 0, 0};
-      f32x4_t za = {0, 0, 0, 0}, zb = {0, 0, 0, 0};
+    for (int g = threadIdx.x; g < groups; g += 256) {  // four columns per thread and pass
+      const f32x4_t vg = *reinterpret_cast<const f32x4_t*>(v + 4 * g);
+      f32x4_t zg = {0, 0, 0, 0};
+#pragma unroll 8
       for (int i = 0; i < kPowRows; ++i) {
-        const int r = r0 + i;
-        float yp = 0.0f;
-        if (r < L.m) {
-          const float ur = u[r];
-          const float* row = w + static_cast<long long>(r) * L.n;
-          if (ina) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(row + 4 * ga);
+        if (i < rows) {
+          const float ur = u[r0 + i];
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(w + static_cast<long long>(r0 + i) * L.n + 4 * g);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { za[e] = fmaf(x[e], ur, za[e]); yp = fmaf(x[e], va[e], yp); }
-          }
-          if (inb) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(row + 4 * gb);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { zb[e] = fmaf(x[e], ur, zb[e]); yp = fmaf(x[e], vb[e], yp); }
+          for (int e = 0; e < 4; ++e) {
+            zg[e] = fmaf(x[e], ur, zg[e]);
+            yacc[i] = fmaf(x[e], vg[e], yacc[i]);
           }
         }
-        yp = wave_sum(yp);
-        if (lane == 0) yw[wave][i] = (g0 == 0 ? 0.0f : yw[wave][i]) + yp;
       }
-      if (ina) *reinterpret_cast<f32x4_t*>(zp + 4 * ga) = za;
-      if (inb) *reinterpret_cast<f32x4_t*>(zp + 4 * gb) = zb;
+      *reinterpret_cast<f32x4_t*>(zp + 4 * g) = zg;
     }
   } else {
-    for (int c0 = 0; c0 < L.n; c0 += 256) {
-      const int c = c0 + threadIdx.x;
-      const bool in = c < L.n;
-      const float vc = in ? v[c] : 0.0f;
+    for (int c = threadIdx.x; c < L.n; c += 256) {
+      const float vc = v[c];
       float zc = 0.0f;
+#pragma unroll 8
       for (int i = 0; i < kPowRows; ++i) {
-        const int r = r0 + i;
-        float yp = 0.0f;
-        if (r < L.m && in) {
-          const float x = w[static_cast<long long>(r) * L.n + c];
-          zc = fmaf(x, u[r], zc);
-          yp = x * vc;
+        if (i < rows) {
+          const float x = w[static_cast<long long>(r0 + i) * L.n + c];
+          zc = fmaf(x, u[r0 + i], zc);
+          yacc[i] = fmaf(x, vc, yacc[i]);
         }
-        yp = wave_sum(yp);
-        if (lane == 0) yw[wave][i] = (c0 == 0 ? 0.0f : yw[wave][i]) + yp;
       }
-      if (in) zp[c] = zc;
+      zp[c] = zc;
     }
+  }
+#pragma unroll
+  for (int i = 0; i < kPowRows; ++i) {
+    const float y = wave_total(yacc[i]);
+    if (lane == 0) yw[wave][i] = y;
   }
   __syncthreads();
   if (threadIdx.x < 64) {
     const int i = threadIdx.x;
     float y = 0.0f;
-    if (i < kPowRows) {
+    if (i < rows) {
       y = ((yw[0][i] + yw[1][i]) + yw[2][i]) + yw[3][i];
-      if (r0 + i < L.m) L.ybuf[static_cast<long long>(z) * L.m + r0 + i] = y;
-      else y = 0.0f;
+      L.ybuf[static_cast<long long>(z) * L.m + r0 + i] = y;
     }
     const float yy = wave_sum(y * y);
     if (threadIdx.x == 0) L.ynorm[static_cast<long long>(z) * L.nrc + blockIdx.x] = yy;
   }
 }
 
-// z_j = sum over the row blocks of the partials (fixed order), and per-block
-// partial sums of z_j^2.
+// z_j = sum over the row blocks of the partials: each of the four waves adds
+// a quarter of the row blocks for the block's 64 columns, and the quarters
+// are added in order (fixed order throughout); per-block partial sums of z_j^2.
+constexpr int kZCols = 64;
 __global__ void __launch_bounds__(256) power_zsum_kernel(PowerLaunch L) {
+  __shared__ float part[4][kZCols];
   __shared__ float red[8];
   const int z = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int cl = threadIdx.x & (kZCols - 1), q = threadIdx.x >> 6;
+  const int j = blockIdx.x * kZCols + cl;
+  const int per = (L.nrc + 3) / 4;
+  const int k0 = q * per, k1 = k0 + per < L.nrc ? k0 + per : L.nrc;
   float t = 0.0f;
   if (j < L.n) {
     const float* zp = L.zpart + static_cast<long long>(z) * L.nrc * L.n + j;
-    for (int k = 0; k < L.nrc; ++k) t += zp[static_cast<long long>(k) * L.n];
-    L.zbuf[static_cast<long long>(z) * L.n + j] = t;
+    for (int k = k0; k < k1; ++k) t += zp[static_cast<long long>(k) * L.n];
   }
-  const float tt = block_sum(t * t, red);
+  part[q][cl] = t;
+  __syncthreads();
+  float tt = 0.0f;
+  if (q == 0 && j < L.n) {
+    const float zj = ((part[0][cl] + part[1][cl]) + part[2][cl]) + part[3][cl];
+    L.zbuf[static_cast<long long>(z) * L.n + j] = zj;
+    tt = zj * zj;
+  }
+  tt = block_sum(tt, red);
   if (threadIdx.x == 0) L.znorm[static_cast<long long>(z) * L.ncb + blockIdx.x] = tt;
 }
 
@@ -191,7 +198,7 @@ __global__ void __launch_bounds__(256) power_normalize_kernel(PowerLaunch L) {
 
 int cap_coef_blocks(int s) { return (s + 15) / 16; }
 int power_row_blocks(int m) { return (m + kPowRows - 1) / kPowRows; }
-int power_col_blocks(int n) { return (n + 255) / 256; }
+int power_col_blocks(int n) { return (n + kZCols - 1) / kZCols; }
 
 hipError_t launch_cap_coef(const CapCoefLaunch& L, bool x_bf16, hipStream_t st) {
   const dim3 grid(cap_coef_blocks(L.s), L.count);

@@ -449,33 +449,6 @@ __device__ __noinline__ float wait_tagged(unsigned long long* a, unsigned tag, i
   }
 }
 
-// Cross-lane moves on the DPP path (no LDS round trip).  Lanes whose source
-// falls outside the row read 0.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp_d(double v) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xf, 0xf, false);
-  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
-}
-constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118, kDppShl4 = 0x104;
-constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143, kDppRor8 = 0x128, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
-
-// Wave totals: inclusive scans within each 16-lane row, then the rows are
-// carried into lane 63, whose value every lane reads (fixed order).
-__device__ __forceinline__ float wave_total(float v) {
-  v += dpp_f<kDppShr1>(v);
-  v += dpp_f<kDppShr2>(v);
-  v += dpp_f<kDppShr4>(v);
-  v += dpp_f<kDppShr8>(v);
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppBcast15, 0xa, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppBcast31, 0xc, 0xf, false));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
 __device__ __forceinline__ double wave_total_d(double v) {
   v += dpp_d<kDppShr1>(v);
   v += dpp_d<kDppShr2>(v);
