@@ -1,0 +1,76 @@
+"""Host-side marshalling of muon_step's groups (no GPU needed: pointer tables
+are built from CPU tensors' addresses and never dereferenced here)."""
+import ctypes
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from spectral_optimizer_ssm_amd import binding as B  # noqa: E402
+
+
+def table(ptr_array, count):
+    return [ptr_array[i] for i in range(count)]
+
+
+def group(count=3, m=5, n=7, cap=False, **kw):
+    W = torch.zeros(count, m, n)
+    M = torch.zeros(count, m, n)
+    G = torch.zeros(count, m, n, dtype=torch.bfloat16)
+    extra = dict(cap_u=torch.zeros(count, m), cap_v=torch.zeros(count, n), cap_sigma=torch.zeros(count), cap=1.0) \
+        if cap else {}
+    extra.update(kw)
+    return B.MuonGroup(W=W, M=M, G=G, lr=0.01, beta=0.9, **extra)
+
+
+def test_tables_of_stacked_tensors_match_each_matrix():
+    g = group(cap=True)
+    arr, keep = B._marshal_groups([g])
+    c = arr[0]
+    assert (c.m, c.n, c.count, c.grad_dtype) == (5, 7, 3, B.MUON_BF16)
+    for name, t in (("W", g.W), ("M", g.M), ("G", g.G), ("cap_u", g.cap_u), ("cap_v", g.cap_v)):
+        assert table(getattr(c, name), 3) == [t[i].data_ptr() for i in range(3)], name
+    assert c.cap_sigma == g.cap_sigma.data_ptr()
+    assert not c.O
+
+
+def test_lists_and_stacks_give_the_same_tables():
+    g = group()
+    lst = B.MuonGroup(W=list(g.W), M=list(g.M), G=[g.G[i] for i in range(3)], lr=0.01, beta=0.9)
+    a, _ = B._marshal_groups([g])
+    b, _ = B._marshal_groups([lst])
+    for name in ("W", "M", "G"):
+        assert table(getattr(a[0], name), 3) == table(getattr(b[0], name), 3)
+
+
+def test_optional_output_table():
+    O = torch.zeros(3, 5, 7, dtype=torch.bfloat16)
+    arr, _ = B._marshal_groups([group(O=O)])
+    assert table(arr[0].O, 3) == [O[i].data_ptr() for i in range(3)]
+
+
+@pytest.mark.parametrize("bad", ["noncontiguous", "shape", "count", "cap_len", "cap_count", "sigma"])
+def test_invalid_groups_are_rejected(bad):
+    g = group(cap=True)
+    if bad == "noncontiguous":
+        g.W = torch.zeros(3, 7, 5).transpose(1, 2)
+    elif bad == "shape":
+        g.M = torch.zeros(3, 5, 8)
+    elif bad == "count":
+        g.G = torch.zeros(2, 5, 7, dtype=torch.bfloat16)
+    elif bad == "cap_len":
+        g.cap_v = torch.zeros(3, 6)
+    elif bad == "cap_count":
+        g.cap_u = torch.zeros(2, 5)
+    else:
+        g.cap_sigma = torch.zeros(4)
+    with pytest.raises(ValueError):
+        B._marshal_groups([g])
+
+
+def test_float32_gradients_are_marked():
+    g = group()
+    g.G = torch.zeros(3, 5, 7)
+    arr, _ = B._marshal_groups([g])
+    assert arr[0].grad_dtype == B.MUON_F32
+    assert isinstance(arr[0].W, ctypes.POINTER(ctypes.c_void_p))
