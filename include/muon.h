@@ -40,7 +40,7 @@
  * Ownership and asynchrony.  The caller owns every buffer, including the
  * workspace; the library never allocates device memory.  Its only state is,
  * per device, one auxiliary stream and two events created on first use by
- * muon_step (see muon_ns_cfg.streams).  All work is ordered on `stream` (a
+ * muon_step (see muon_ns_cfg.streams) or muon_adamw.  All work is ordered on `stream` (a
  * hipStream_t; NULL is the null stream): work placed on the auxiliary stream
  * starts after everything enqueued on `stream` before the call and finishes
  * before anything enqueued on `stream` after it.  Calls return without
@@ -266,8 +266,10 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
  *   numel                         host array of element counts (0: skipped)
  * Tensors are contiguous; 16-byte aligned tensors take vectorised loads.
  * 0 <= beta < 1, eps >= 0, step >= 1 (MUON_EINVAL otherwise); a tensor of
- * 2^31 or more elements returns MUON_EUNSUPPORTED.  One launch per 80 tensors;
- * no workspace. */
+ * 2^31 or more elements returns MUON_EUNSUPPORTED.  One launch per 80 tensors
+ * (the tensor table travels in the kernel arguments); with more than one, the
+ * launch with the most work runs on `stream` and the others beside it on the
+ * auxiliary stream.  No workspace. */
 int muon_adamw(int ntensors, float* const* params, const void* const* grads, float* const* exp_avg,
                float* const* exp_avg_sq, const long long* numel, int grad_dtype, float lr, float beta1,
                float beta2, float eps, float weight_decay, long long step, void* stream);

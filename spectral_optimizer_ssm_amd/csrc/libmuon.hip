@@ -969,18 +969,19 @@ int muon_adamw(int ntensors, float* const* params, const void* const* grads, flo
   A.lr_bc = static_cast<float>(lr / bc1);
   A.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = grad_dtype == MUON_BF16;
+  // launches of up to kAdamwMax tensors (the table travels in the kernel arguments)
+  std::vector<AdamwLaunch> chunks;
+  std::vector<long long> chunk_blocks;
   long long blocks = 0;
-  auto flush = [&]() {
-    const hipError_t e = launch_adamw(A, grad_dtype == MUON_BF16, static_cast<int>(blocks), st);
-    A.nt = 0;
-    blocks = 0;
-    return e == hipSuccess;
-  };
   for (int i = 0; i < ntensors; ++i) {
     if (numel[i] == 0) continue;
     const long long nb = (numel[i] + kAdamwBlock - 1) / kAdamwBlock;
     if (A.nt == kAdamwMax || blocks + nb > (1LL << 30)) {  // block indices stay in int
-      if (!flush()) return MUON_EHIP;
+      chunks.push_back(A);
+      chunk_blocks.push_back(blocks);
+      A.nt = 0;
+      blocks = 0;
     }
     AdamwTensor& T = A.t[A.nt++];
     T.p = params[i]; T.m = exp_avg[i]; T.v = exp_avg_sq[i]; T.g = grads[i];
@@ -988,8 +989,36 @@ int muon_adamw(int ntensors, float* const* params, const void* const* grads, flo
     T.block0 = static_cast<int>(blocks);
     blocks += nb;
   }
-  if (A.nt > 0 && !flush()) return MUON_EHIP;
-  return MUON_OK;
+  if (A.nt > 0) {
+    chunks.push_back(A);
+    chunk_blocks.push_back(blocks);
+  }
+  auto run = [&](size_t c, hipStream_t s) {
+    return launch_adamw(chunks[c], bf16, static_cast<int>(chunk_blocks[c]), s) == hipSuccess;
+  };
+  Aux* aux = chunks.size() > 1 ? aux_for_current_device() : nullptr;
+  if (aux == nullptr) {
+    for (size_t c = 0; c < chunks.size(); ++c)
+      if (!run(c, st)) return MUON_EHIP;
+    return MUON_OK;
+  }
+  // The tensors are independent: the chunk with the most work runs on the
+  // caller's stream while the others (typically the many small tensors, which
+  // alone would leave most of the chip idle) run beside it on the auxiliary
+  // stream, joined back before returning.
+  size_t big = 0;
+  for (size_t c = 1; c < chunks.size(); ++c)
+    if (chunk_blocks[c] > chunk_blocks[big]) big = c;
+  std::lock_guard<std::mutex> lock(aux->mu);
+  if (hipEventRecord(aux->fork, st) != hipSuccess || hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
+    return MUON_EHIP;
+  bool ok = run(big, st);
+  for (size_t c = 0; ok && c < chunks.size(); ++c)
+    if (c != big) ok = run(c, aux->s);
+  // join even after a failed launch, so that the caller's stream never runs ahead of the auxiliary work
+  if (hipEventRecord(aux->join, aux->s) != hipSuccess || hipStreamWaitEvent(st, aux->join, 0) != hipSuccess)
+    return MUON_EHIP;
+  return ok ? MUON_OK : MUON_EHIP;
 }
 
 int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int r, long long batch,
