@@ -23,12 +23,14 @@
 //                        of the tridiagonal matrix by float64 multisection.
 //   diag_lanczos_split_kernel  the same run when few matrices would leave most
 //                        CUs idle: P co-resident workgroups per matrix (one
-//                        cooperative launch) each own a slice of H (256
-//                        columns x a range of rows) and compute that slice of
-//                        H q; the slices meet through global memory behind one
-//                        barrier per step, and every workgroup then repeats
-//                        the vector work on its own copy of the basis in LDS
-//                        (identical arithmetic, so the copies stay equal).
+//                        cooperative launch) each own a 256 x 256 block of the
+//                        upper block triangle of H (or a range of its rows)
+//                        and contribute its column sums and, off the diagonal,
+//                        its row sums to H q; the contributions meet through
+//                        global memory as tagged words that the readers wait
+//                        on, and every workgroup then repeats the vector work
+//                        on its own copy of the basis in LDS (identical
+//                        arithmetic, so the copies stay equal).
 // Every reduction runs in a fixed order: results are deterministic.
 #include <mutex>
 
