@@ -200,3 +200,35 @@ def test_diag_workspace_reuse_across_calls(mu):
         torch.cuda.synchronize()
         out = {k: v.cpu().numpy() for k, v in out.items()}
         check(out, exact, it, range(5))
+
+
+@pytest.mark.parametrize("m,n,dtype", [(600, 1000, "bf16"), (1000, 600, "f32")])
+def test_diag_three_blocks_ragged(mu, m, n, dtype):
+    """s = 600 pads to 640: blocks of 256, 256 and a 128-wide last block with
+    88 live rows, whose off-diagonal blocks form row sums with half the lanes
+    idle (a few matrices: the split run)."""
+    A, exact = to_device(stack(m + 7 * n, 3, m, n, "spread"), dtype)
+    out = mu.muon_spectral_diag(A, iters=40)
+    torch.cuda.synchronize()
+    check({k: v.cpu().numpy() for k, v in out.items()}, exact, 40, range(3))
+
+
+def test_diag_split_run_agrees_with_one_workgroup_per_matrix(mu):
+    """The same matrices as a batch of 4 (several workgroups per matrix) and
+    inside a batch of 300 (one workgroup per matrix): both match the oracle
+    and each other."""
+    A, exact = to_device(stack(41, 4, 384, 704, "spread"), "bf16")
+    filler = torch.zeros((296, 384, 704), dtype=A.dtype, device=A.device)
+    few = mu.muon_spectral_diag(A, iters=24)
+    many = mu.muon_spectral_diag(torch.cat([A, filler]), iters=24)
+    torch.cuda.synchronize()
+    few = {k: v.cpu().numpy() for k, v in few.items()}
+    many = {k: v[:4].cpu().numpy() for k, v in many.items()}
+    check(few, exact, 24, range(4))
+    check(many, exact, 24, range(4))
+    for k in few:
+        top = float(np.max(few["sigma_max"])) ** 2
+        if k == "orth_err":
+            assert np.all(np.abs(few[k] - many[k]) <= ORTH_ABS + ORTH_REL * np.abs(many[k]))
+        else:
+            assert np.all(np.abs(few[k] ** 2 - many[k] ** 2) <= 2 * THETA_REL * top)
