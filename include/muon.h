@@ -311,7 +311,8 @@ size_t muon_spectral_diag_workspace_size(int m, int n, long long batch, int dtyp
  * Lanczos pass runs as one cooperative launch with several workgroups per
  * matrix that exchange partial products through the workspace (their waits
  * are bounded: a matrix whose workgroups ever gave up waiting gets NaN
- * outputs); if the device refuses that launch, one workgroup per matrix is
+ * outputs; the environment variable MUON_DIAG_SPIN_LIMIT, a test hook read
+ * at each launch, shortens the bound); if the device refuses that launch, one workgroup per matrix is
  * used.  Deterministic for a given device (the split depends on its compute
  * unit count); no allocation; asynchronous on `stream`; calls that share a
  * workspace must not overlap. */

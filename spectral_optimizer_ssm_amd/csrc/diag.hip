@@ -32,6 +32,7 @@
 //                        on its own copy of the basis in LDS (identical
 //                        arithmetic, so the copies stay equal).
 // Every reduction runs in a fixed order: results are deterministic.
+#include <cstdlib>
 #include <mutex>
 
 #include "common.cuh"
@@ -393,7 +394,7 @@ constexpr int kSplitThreads = 512;
 constexpr int kSplitWaves = kSplitThreads / 64;
 constexpr int kSplitBlock = 256;           // H is cut into 256 x 256 blocks (4 columns per lane)
 constexpr int kSplitMaxR = 16;             // row ranges per block
-constexpr unsigned kSpinLimit = 1u << 20;  // polls before a wait is given up
+constexpr unsigned kSpinLimit = 1u << 20;  // polls before a wait is given up (unless a test shortens it)
 
 // A matrix's split scratch, in floats from the start of its basis region
 // (unused by this kernel: the basis lives in LDS): [0] a barrier counter,
@@ -411,12 +412,12 @@ __host__ __device__ constexpr long long split_scratch_floats(int p, int r, int n
 // at agent scope with its arrival, waits for `target` arrivals and
 // acquires; the workgroup barrier then orders every wave's later loads.
 // The wait is bounded: a workgroup that gives up marks itself dead.
-__device__ bool split_barrier(unsigned* cnt, unsigned target, int* dead) {
+__device__ bool split_barrier(unsigned* cnt, unsigned target, int* dead, unsigned limit) {
   if (threadIdx.x == 0 && *dead == 0) {
     __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     unsigned polls = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (++polls > kSpinLimit) {
+      if (++polls > limit) {
         *dead = 1;
         break;
       }
@@ -439,11 +440,11 @@ __device__ __forceinline__ void put_tagged(unsigned long long* a, float v, unsig
 // Bounded wait for a tagged word (out of line: the common case finds the
 // word ready on the first read); after a timeout, or once another wave of
 // the workgroup has timed out, returns NaN and leaves *dead set.
-__device__ __noinline__ float wait_tagged(unsigned long long* a, unsigned tag, int* dead) {
+__device__ __noinline__ float wait_tagged(unsigned long long* a, unsigned tag, int* dead, unsigned limit) {
   for (unsigned polls = 0;; ++polls) {
     const unsigned long long x = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (static_cast<unsigned>(x >> 32) == tag) return __uint_as_float(static_cast<unsigned>(x));
-    if (polls > kSpinLimit || __hip_atomic_load(dead, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+    if (polls > limit || __hip_atomic_load(dead, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
       __hip_atomic_store(dead, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       return NAN;
     }
@@ -681,7 +682,7 @@ __global__ void __launch_bounds__(kSplitThreads) diag_lanczos_split_kernel(DiagL
       for (int e = 0; e < 4; ++e) put_tagged(cs + e, x[e], tag);
     }
     if (j == 0) {
-      const bool alive = split_barrier(cnt, static_cast<unsigned>(P), &dead);
+      const bool alive = split_barrier(cnt, static_cast<unsigned>(P), &dead, D.spin_limit);
       if (alive && p == 0 && tid == 0 && D.orth != nullptr) {
         double tot = 0.0;
         for (int i = 0; i < P; ++i) tot += gorth[i];
@@ -728,7 +729,7 @@ __global__ void __launch_bounds__(kSplitThreads) diag_lanczos_split_kernel(DiagL
         for (int t = 0; t < 8; ++t) {
           if (at[t] >= 0)
             gat[at[t]] = static_cast<unsigned>(v[t] >> 32) == tag ? __uint_as_float(static_cast<unsigned>(v[t]))
-                                                                  : wait_tagged(base + at[t], tag, &dead);
+                                                                  : wait_tagged(base + at[t], tag, &dead, D.spin_limit);
         }
       }
       __syncthreads();
@@ -941,6 +942,14 @@ long long diag_split_clear_words(DiagLaunch& D) {
 hipError_t launch_diag_lanczos(const DiagLaunch& D0, hipStream_t st) {
   if (D0.count == 0) return hipSuccess;
   DiagLaunch D = D0;
+  // test hook: MUON_DIAG_SPIN_LIMIT shortens the split run's bounded waits so
+  // that their give-up path (NaN outputs, every wave ends) can be exercised
+  D.spin_limit = kSpinLimit;
+  if (const char* e = std::getenv("MUON_DIAG_SPIN_LIMIT")) {
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    if (end != e && v < kSpinLimit) D.spin_limit = static_cast<unsigned>(v);
+  }
   size_t lds = 0;
   if (plan_split(D, &lds) > 0) {
     void* args[] = {&D};

@@ -236,6 +236,7 @@ struct DiagLaunch {
   long long qstride;
   int s, s_pad, iters, kmax;
   int split_p, split_r, split_nb;  // split run (set by the planner): blocks per side, row ranges, workgroups
+  unsigned spin_limit;             // split run: polls before a wait is given up (set by the launcher)
   float* orth;         // [count] or null
   float* smax;         // [count] or null
   float* smin;         // [count] or null
