@@ -163,11 +163,6 @@ def muon_step(W, M, G, *, beta: float, lr: float, nesterov: bool = True, steps: 
     return {"W": W_new, "M": M_new, "O": O, "nu": nu, "U": U}
 
 
-def muon_step_group(Ws, Ms, Gs, **kw):
-    """muon_step over a list of same-shape matrices (one parameter group)."""
-    return [muon_step(W, M, G, **kw) for W, M, G in zip(Ws, Ms, Gs)]
-
-
 # ----------------------------------------------------------------------------
 # Factored injections: X = V K^T (MuonSSM, method section on the low-rank
 # value-key injections and their light Newton-Schulz step)

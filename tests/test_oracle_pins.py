@@ -561,3 +561,96 @@ def test_lanczos_2x2_closed_form_and_degenerate_inputs():
     bad[1, 2] = np.nan
     d = orc.spectral_diagnostics(bad, 4)
     assert np.isnan(d["orth_err"]) and np.isnan(d["sigma_max"]) and np.isnan(d["sigma_min"])
+
+
+# ---------------------------------------------------------------------------
+# Batched Newton-Schulz and the capped step's outputs, pinned independently of
+# the oracle's own code paths.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n", [(6, 10), (10, 6)])
+@pytest.mark.parametrize("steps", [0, 1, 5])
+def test_ns_batched_closed_form_per_matrix(m, n, steps):
+    """Every matrix of the stack is normalised by its own Frobenius norm and
+    iterated the given number of steps: built as U_i diag(s_i) V_i^T with
+    scales that differ by orders of magnitude, each must equal the singular
+    value closed form of its own factors (a wrong step count, a norm taken
+    over the whole stack or coefficients not passed through all fail)."""
+    rng = np.random.default_rng(300 + steps)
+    k = min(m, n)
+    mats, want = [], []
+    for i, scale in enumerate((1e-3, 1.0, 40.0, 0.5)):
+        U, V = haar(rng, m, k), haar(rng, n, k)
+        s = scale * rng.uniform(0.05, 1.0, k)
+        mats.append((U * s) @ V.T)
+        want.append(spectral_expected(U, s, V, steps, (1.5, -0.5), 1e-7))
+    out = orc.ns_batched(np.stack(mats), steps)
+    for i in range(len(mats)):
+        np.testing.assert_allclose(out[i], want[i], atol=1e-12)
+    # per-step coefficients reach every matrix of the stack
+    rows = [(3.4445, -4.7750, 2.0315)] * steps
+    if steps:
+        outq = orc.ns_batched(np.stack(mats), steps, coeffs=[c for r in rows for c in r], per_step=True)
+        for i, M in enumerate(mats):
+            Uu, s, Vt = np.linalg.svd(M, full_matrices=False)
+            np.testing.assert_allclose(outq[i], spectral_expected(Uu, s, Vt.T, steps, rows, 1e-7), atol=1e-11)
+
+
+def test_capped_step_active_increment_and_tracked_pair():
+    """Cap active: with W built from its SVD and (u, v) = W's exact top pair,
+    a gradient dominated by -u v^T makes u^T O v < 0.  The weight increment
+    must be -lr (O - gamma u v^T) with O the singular-value closed form of
+    the direction U = (1 + beta) G (M = 0) and gamma = u^T O v; the tracked
+    triple must come from one power step on the new weight, started from the
+    old (u, v): computed here from W' through its own SVD factors, and
+    different from the same step taken on the old weight."""
+    rng = np.random.default_rng(310)
+    m, n, beta, lr, steps = 24, 40, 0.95, 0.02, 5
+    Uw, Vw = haar(rng, m, m), haar(rng, n, m)
+    sw = np.concatenate([[3.0], rng.uniform(0.2, 1.0, m - 1)])
+    W = (Uw * sw) @ Vw.T
+    u, v, sigma = Uw[:, 0], Vw[:, 0], 3.0
+    G = -5.0 * np.outer(u, v) + 0.1 * rng.standard_normal((m, n))
+    out = orc.muon_step_capped(W, np.zeros((m, n)), G, u, v, sigma, cap=2.0, beta=beta, lr=lr, steps=steps)
+    Ug, sg, Vgt = np.linalg.svd((1 + beta) * G, full_matrices=False)
+    O_cf = spectral_expected(Ug, sg, Vgt.T, steps, (1.5, -0.5), 1e-7)
+    c = float(u @ O_cf @ v)
+    assert c < 0 and abs(out["gamma"] - c) < 1e-12
+    np.testing.assert_allclose(out["O_uncapped"], O_cf, atol=1e-12)
+    np.testing.assert_allclose(out["W"] - W, -lr * (O_cf - c * np.outer(u, v)), atol=1e-13)
+    assert abs(u @ out["O"] @ v) < 1e-12
+    # the new triple: W' v / ||W' v|| etc. through the SVD factors of W'
+    Up, sp, Vpt = np.linalg.svd(out["W"], full_matrices=False)
+    y = Up @ (sp * (Vpt @ v))
+    z = Vpt.T @ (sp * (Up.T @ u))
+    np.testing.assert_allclose(out["u"], y / np.linalg.norm(y), atol=1e-12)
+    np.testing.assert_allclose(out["v"], z / np.linalg.norm(z), atol=1e-12)
+    assert abs(out["sigma"] - np.linalg.norm(y)) < 1e-12
+    u_old, v_old, s_old = orc.power_step(W, u, v)
+    assert np.abs(out["u"] - u_old).max() > 1e-6 or abs(out["sigma"] - s_old) > 1e-6
+    # cap not reached (sigma below it): the update is the plain one
+    off = orc.muon_step_capped(W, np.zeros((m, n)), G, u, v, sigma, cap=3.5, beta=beta, lr=lr, steps=steps)
+    assert off["gamma"] == 0.0
+    np.testing.assert_allclose(off["W"] - W, -lr * O_cf, atol=1e-13)
+
+
+@pytest.mark.parametrize("k", [2, 3, 5])
+def test_lanczos_ritz_values_are_the_krylov_projection(k):
+    """For k < s the Lanczos estimates are the extreme eigenvalues of H
+    projected onto the Krylov space span{q, Hq, ..., H^(k-1) q} of the start
+    vector (Rayleigh-Ritz): here that space is orthonormalised by a QR of the
+    Krylov matrix itself, not by the Lanczos recurrence."""
+    rng = np.random.default_rng(320 + k)
+    s = 40
+    lam = np.sort(rng.uniform(0.1, 2.0, s))
+    Qm = haar(rng, s, s)
+    H = Qm @ np.diag(lam) @ Qm.T
+    q = orc.lanczos_start(s)
+    K = np.empty((s, k))
+    K[:, 0] = q / np.linalg.norm(q)
+    for j in range(1, k):
+        w = H @ K[:, j - 1]
+        K[:, j] = w / np.linalg.norm(w)
+    B, _ = np.linalg.qr(K)
+    ev = np.linalg.eigvalsh(B.T @ H @ B)
+    lo, hi = orc.lanczos_extremes(H, k)
+    assert abs(lo - ev[0]) < 1e-10 and abs(hi - ev[-1]) < 1e-10
