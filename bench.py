@@ -235,6 +235,8 @@ def bench_full_step(args, torch, mu, wl):
         elif ph == "symprod":
             work.append(sym_products[si] * sym_f)
             si += 1
+        elif ph == "flags":  # the non-finite flag: one small read of the partial sums
+            work.append(0)
         elif ph in ("cap", "power"):  # bytes: read X (2 B/elt) / read W (4 B/elt); power follows apply
             g, s, l = per_group[gi_a if ph == "cap" else gi_a - 1]
             work.append(g.count * g.m * g.n * (2 if ph == "cap" else 4))
@@ -252,7 +254,9 @@ def bench_full_step(args, torch, mu, wl):
         tot_w = sum(wk for _, wk in rows)
         n = len(rows)
         rate = tot_w / (tot_ms * 1e-3)
-        if kind in ("momentum", "apply", "cap", "power"):
+        if kind == "flags":
+            kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n}
+        elif kind in ("momentum", "apply", "cap", "power"):
             kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "bytes_per_launch": tot_w / n,
                              "gbs": rate / 1e9, "frac": rate / 1e9 / PEAK_HBM_GBS}
         else:

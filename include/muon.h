@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 6
+#define MUON_VERSION 7
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -178,7 +178,9 @@ size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muo
 /* One Muon step over every matrix of every group: momentum (M in place),
  * Newton-Schulz orthogonalisation, and W -= lr * scale * O (W in place).
  * norms_out: NULL, or a device float array with one slot per matrix (groups in
- * order, matrices in order) receiving ||U||_F. */
+ * order, matrices in order) receiving ||U||_F.  The workspace (at least the
+ * size query's bytes, 16-byte aligned) holds the iterates and, in its first
+ * bytes, the non-finite flag of the step (muon_query_flags). */
 int muon_step(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg,
               void* workspace, size_t workspace_bytes, float* norms_out, void* stream);
 
@@ -194,7 +196,8 @@ typedef enum {
   MUON_PHASE_F32_COMBINE = 8, /* combine of one float32 group */
   MUON_PHASE_CAP = 9,         /* spectral-cap coefficient u^T O v of one group */
   MUON_PHASE_POWER = 10,      /* power step on one group's updated weights */
-  MUON_PHASE_COMBINE_APPLY = 11 /* final grouped combine with the apply fused (large bf16 matrices) */
+  MUON_PHASE_COMBINE_APPLY = 11, /* final grouped combine with the apply fused (large bf16 matrices) */
+  MUON_PHASE_FLAGS = 12       /* the call's non-finite flag (see muon_query_flags) */
 } muon_phase;
 
 /* The phases muon_step would run for these groups and cfg, in order: returns
@@ -213,15 +216,40 @@ int muon_step_timed(const muon_group* groups, int ngroups, const muon_ns_cfg* cf
                     void* workspace, size_t workspace_bytes, float* norms_out, void* stream,
                     void* const* events, int nevents);
 
-/* Bytes of device workspace muon_ns_orthogonalize needs. */
+/* Bytes of device workspace muon_ns_orthogonalize needs (independent of ld
+ * and stride). */
 size_t muon_ns_workspace_size(int m, int n, int batch, int dtype, const muon_ns_cfg* cfg);
 
-/* Newton-Schulz only: O[b] = NS(G[b]) for a contiguous [batch][m][n] stack.
- * G and O have element type `dtype`; the iteration runs in cfg->precision,
- * which must equal dtype.  O must not overlap G. */
-int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int batch,
-                          const muon_ns_cfg* cfg, void* workspace, size_t workspace_bytes,
-                          void* stream);
+/* Newton-Schulz only ("Muon Meets Mamba", abstract: the orthogonalisation of
+ * one weight update), without momentum or apply: O[b] = NS(G[b]) for b <
+ * batch.  Matrix b of G starts at element b * stride of G, its rows are ld
+ * elements apart (ld >= n; stride >= (m - 1) * ld + n when batch > 1); O uses
+ * the same ld and stride.  G and O have element type `dtype`; the iteration
+ * runs in cfg->precision, which must equal dtype (MUON_EUNSUPPORTED
+ * otherwise).  O may be G itself (in place: every element of G is read before
+ * any element of O is written); otherwise the two must not overlap
+ * (MUON_EINVAL).  Rows with ld % 8 == 0 and 16-byte aligned matrices take
+ * vectorised paths.  Also sets the workspace's non-finite flag (see
+ * muon_query_flags). */
+int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int ld, int batch,
+                          long long stride, const muon_ns_cfg* cfg, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* The non-finite flag of the last muon_step or muon_ns_orthogonalize call that
+ * used this workspace ("Muon Meets Mamba" practitioner article, long-term
+ * engineering and the training checkpoints: stop and alert on abnormal
+ * gradient norms, check for NaN).  The call computes ||U||_F^2 of every
+ * matrix's update direction U from per-block partial sums; the flag is 1 when
+ * any of those sums is not finite (a NaN or Inf in G or M, or an overflow),
+ * else 0.  The flag lives in the first bytes of the workspace and is written
+ * by the call's last kernel on `stream`, so read it only after that stream
+ * has been synchronised (this function copies 4 bytes device -> host with
+ * hipMemcpy).  A call with no matrices leaves it unchanged.
+ *   workspace     the workspace passed to that call (16-byte aligned)
+ *   nonfinite_out host int receiving 0 or 1
+ * Returns MUON_EINVAL on null or misaligned pointers, MUON_EHIP if the copy
+ * fails. */
+int muon_query_flags(const void* workspace, int* nonfinite_out);
 
 /* Newton-Schulz on a large batch of small matrices (MuonSSM's per-token,
  * per-head injections), each held on chip for the whole iteration:
@@ -311,9 +339,10 @@ size_t muon_spectral_diag_workspace_size(int m, int n, long long batch, int dtyp
  * Lanczos pass runs as one cooperative launch with several workgroups per
  * matrix that exchange partial products through the workspace (their waits
  * are bounded: a matrix whose workgroups ever gave up waiting gets NaN
- * outputs; the environment variable MUON_DIAG_SPIN_LIMIT, a test hook read
- * at each launch, shortens the bound); if the device refuses that launch, one workgroup per matrix is
- * used.  Deterministic for a given device (the split depends on its compute
+ * outputs); if the device refuses that launch, one workgroup per matrix is
+ * used.  Debug only, for tests of that give-up path: the environment
+ * variable MUON_DEBUG_DIAG_SPIN_LIMIT (read at each launch; it can only lower
+ * the bound) cuts the number of polls of those waits.  Deterministic for a given device (the split depends on its compute
  * unit count); no allocation; asynchronous on `stream`; calls that share a
  * workspace must not overlap. */
 int muon_spectral_diag(const void* A, int dtype, int m, int n, long long batch, int iters, float* orth_err,

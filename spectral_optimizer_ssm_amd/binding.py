@@ -17,7 +17,7 @@ MUON_F32, MUON_BF16 = 0, 1
 MUON_OK, MUON_EINVAL, MUON_EUNSUPPORTED, MUON_EWORKSPACE, MUON_EHIP = 0, -1, -2, -3, -4
 MUON_NS_AUTO, MUON_NS_ITERATE, MUON_NS_ACCUMULATE = 0, 1, 2
 PHASES = {1: "momentum", 2: "ns_small", 3: "gram", 4: "combine", 5: "symprod", 6: "apply", 7: "f32_gram",
-          8: "f32_combine", 9: "cap", 10: "power", 11: "combine_apply"}
+          8: "f32_combine", 9: "cap", 10: "power", 11: "combine_apply", 12: "flags"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmuon.so")
@@ -49,7 +49,7 @@ class GroupC(ctypes.Structure):
 
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
-           "muon_ns_orthogonalize", "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
+           "muon_ns_orthogonalize", "muon_query_flags", "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
            "muon_spectral_diag_workspace_size", "muon_spectral_diag", "muon_spectral_diag_timed",
            "muon_status_string", "muon_version")
 
@@ -76,8 +76,10 @@ def lib():
     L.muon_step_timed.restype = i
     L.muon_ns_workspace_size.argtypes = [i, i, i, i, ctypes.POINTER(NsCfg)]
     L.muon_ns_workspace_size.restype = sz
-    L.muon_ns_orthogonalize.argtypes = [vp, vp, i, i, i, i, ctypes.POINTER(NsCfg), vp, sz, vp]
+    L.muon_ns_orthogonalize.argtypes = [vp, vp, i, i, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg), vp, sz, vp]
     L.muon_ns_orthogonalize.restype = i
+    L.muon_query_flags.argtypes = [vp, ctypes.POINTER(i)]
+    L.muon_query_flags.restype = i
     L.muon_ns_batched_small.argtypes = [vp, vp, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg), vp]
     L.muon_ns_batched_small.restype = i
     L.muon_ns_factored.argtypes = [vp, vp, i, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg),
@@ -157,14 +159,38 @@ def _split(x) -> list:
     return list(x)
 
 
-def _table(x, shape, what):
+def _current_device():
+    """The CUDA device the library's kernels will run on (torch's current one)."""
+    import torch
+    return torch.device("cuda", torch.cuda.current_device())
+
+
+def _check_tensors(ts, what, dtypes, device):
+    """Every tensor of ts has one of `dtypes` (all the same one) and, when
+    `device` is given, lives on it; raises TypeError / ValueError otherwise."""
+    names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+    first = None
+    for t in ts:
+        if t.dtype not in dtypes:
+            raise TypeError(f"{what} must be {names} (got {t.dtype})")
+        if first is None:
+            first = t.dtype
+        elif t.dtype != first:
+            raise TypeError(f"every entry of {what} must have one dtype ({first} and {t.dtype} found)")
+        if device is not None and t.device != device:
+            raise ValueError(f"{what} must be on {device} (got {t.device})")
+
+
+def _table(x, shape, what, dtypes, device):
     """(device pointer array, count, a tensor of the group) for x: a
     contiguous [count, *shape] tensor, whose pointers are computed from its
     base address (no per-matrix views: this runs on every step), or a
-    sequence of contiguous tensors of `shape`."""
+    sequence of contiguous tensors of `shape`.  dtypes / device as in
+    _check_tensors."""
     if hasattr(x, "dim") and x.dim() == len(shape) + 1:
         if not x.is_contiguous() or tuple(x.shape[1:]) != tuple(shape):
             raise ValueError(f"{what} must be a contiguous [count, {', '.join(map(str, shape))}] tensor")
+        _check_tensors([x], what, dtypes, device)
         count, step = x.shape[0], x.element_size()
         for d in shape:
             step *= d
@@ -174,6 +200,7 @@ def _table(x, shape, what):
     for t in ts:
         if not t.is_contiguous() or tuple(t.shape) != tuple(shape):
             raise ValueError(f"every entry of {what} must be a contiguous {' x '.join(map(str, shape))} tensor")
+    _check_tensors(ts, what, dtypes, device)
     return _ptrs(ts), len(ts), (ts[0] if ts else None)
 
 
@@ -199,31 +226,40 @@ class MuonGroup:
     cap: float = 0.0
 
 
-def _marshal_groups(groups: Sequence[MuonGroup]):
+def _marshal_groups(groups: Sequence[MuonGroup], precision: int = MUON_BF16, device=None):
+    """C group records for the groups.  W, M, cap_u, cap_v and cap_sigma must
+    be float32, G bf16 or float32 (one dtype per group), O the precision's
+    dtype; with `device` (calls that launch work) every tensor must be on it."""
+    import torch
+    f32 = (torch.float32,)
+    gdt = (torch.bfloat16, torch.float32)
+    odt = (torch.bfloat16,) if precision == MUON_BF16 else f32
     keep, cgroups = [], []
     for g in groups:
         w0 = g.W if hasattr(g.W, "dim") and g.W.dim() == 3 else list(g.W)[0]
         m, n = (g.W.shape[1:] if w0 is g.W else w0.shape)
         m, n = int(m), int(n)
-        pw, count, wt = _table(g.W, (m, n), "W")
-        pm, cm, _ = _table(g.M, (m, n), "M")
-        pg, cgr, gt = _table(g.G, (m, n), "G")
-        po, co = (None, count) if g.O is None else _table(g.O, (m, n), "O")[:2]
+        pw, count, wt = _table(g.W, (m, n), "W", f32, device)
+        pm, cm, _ = _table(g.M, (m, n), "M", f32, device)
+        pg, cgr, gt = _table(g.G, (m, n), "G", gdt, device)
+        po, co = (None, count) if g.O is None else _table(g.O, (m, n), "O", odt, device)[:2]
         if not count == cm == cgr == co:
             raise ValueError("W, M, G (and O) must hold the same number of matrices")
         keep += [pw, pm, pg, po, g.W, g.M, g.G, g.O]
         cu = cv = None
         sig = None
         if g.cap_u is not None:
-            cu, cnu, ut = _table(g.cap_u, (m,), "cap_u")
-            cv, cnv, vt = _table(g.cap_v, (n,), "cap_v")
-            if cnu != count or cnv != count or ut.dtype != wt.dtype or vt.dtype != wt.dtype:
+            cu, cnu, ut = _table(g.cap_u, (m,), "cap_u", f32, device)
+            cv, cnv, vt = _table(g.cap_v, (n,), "cap_v", f32, device)
+            if cnu != count or cnv != count:
                 raise ValueError("cap_u / cap_v must hold one float32 vector of length m / n per matrix")
-            if not g.cap_sigma.is_contiguous() or g.cap_sigma.numel() != count:
+            if not hasattr(g.cap_sigma, "is_contiguous") or not g.cap_sigma.is_contiguous() or \
+                    g.cap_sigma.numel() != count:
                 raise ValueError("cap_sigma must be a contiguous float32 tensor with one entry per matrix")
+            _check_tensors([g.cap_sigma], "cap_sigma", f32, device)
             sig = ctypes.c_void_p(g.cap_sigma.data_ptr())
             keep += [cu, cv, g.cap_u, g.cap_v, g.cap_sigma]
-        cgroups.append(GroupC(m, n, count, _dtype_code(gt),
+        cgroups.append(GroupC(m, n, count, _dtype_code(gt) if gt is not None else MUON_BF16,
                               ctypes.cast(pw, ctypes.POINTER(ctypes.c_void_p)),
                               ctypes.cast(pm, ctypes.POINTER(ctypes.c_void_p)),
                               ctypes.cast(pg, ctypes.POINTER(ctypes.c_void_p)),
@@ -236,12 +272,26 @@ def _marshal_groups(groups: Sequence[MuonGroup]):
     return arr, keep
 
 
+def _workspace(workspace, need, device):
+    """The caller's workspace when it is a large enough uint8 tensor on the
+    device, else a new one."""
+    import torch
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous uint8 tensor")
+        if workspace.device != device:
+            raise ValueError(f"workspace must be on {device} (got {workspace.device})")
+        if workspace.numel() >= need:
+            return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
 # ----------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ----------------------------------------------------------------------------
 def muon_step_workspace_size(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7,
                              precision=MUON_BF16, per_step=False, schedule=MUON_NS_AUTO) -> int:
-    cg, keep = _marshal_groups(groups)
+    cg, keep = _marshal_groups(groups, precision)
     cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule)
     return int(lib().muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
 
@@ -251,7 +301,7 @@ def muon_step_phases(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), e
     """Names of the phases muon_step runs for these groups, in order (the
     intervals between the events muon_step_timed records)."""
     L = lib()
-    cg, keep = _marshal_groups(groups)
+    cg, keep = _marshal_groups(groups, precision)
     cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule, separate_apply=separate_apply)
     n = int(L.muon_step_phases(cg, len(groups), ctypes.byref(cfg), None, 0))
     if n < 0:
@@ -270,16 +320,19 @@ def muon_step(groups: Sequence[MuonGroup], steps=5, coeffs=(1.5, -0.5), eps=1e-7
     the phase boundaries."""
     import torch
     L = lib()
-    cg, keep = _marshal_groups(groups)
+    dev = _current_device()
+    cg, keep = _marshal_groups(groups, precision, dev)
     cfg, arr = make_cfg(steps, coeffs, eps, precision, per_step, schedule, streams, separate_apply)
     need = int(L.muon_step_workspace_size(cg, len(groups), ctypes.byref(cfg)))
     if need == 0:  # the size query has no status: ask the step itself, which validates first
         rc = L.muon_step(cg, len(groups), ctypes.byref(cfg), None, 0, None, None)
         _check(MUON_EINVAL if rc in (MUON_OK, MUON_EWORKSPACE) else rc, "muon_step")
-    if workspace is None or workspace.numel() < need:
-        w = groups[0].W
-        dev = (w if hasattr(w, "device") else list(w)[0]).device
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, need, dev)
+    if norms_out is not None:
+        total = sum(int(c.count) for c in cg)
+        if not norms_out.is_contiguous() or norms_out.numel() < total:
+            raise ValueError("norms_out must be a contiguous float32 tensor with one entry per matrix")
+        _check_tensors([norms_out], "norms_out", (torch.float32,), dev)
     nptr = ctypes.cast(ctypes.c_void_p(norms_out.data_ptr()), ctypes.POINTER(ctypes.c_float)) \
         if norms_out is not None else None
     if events is None:
@@ -301,35 +354,62 @@ def muon_ns_workspace_size(m, n, batch, dtype, steps=5, coeffs=(1.5, -0.5), eps=
     return int(lib().muon_ns_workspace_size(int(m), int(n), int(batch), int(dtype), ctypes.byref(cfg)))
 
 
+def _strided_stack(t):
+    """(batch, m, n, ld, stride) of a [batch, m, n] (or [m, n]) tensor whose
+    rows are contiguous (unit column stride)."""
+    t3 = t if t.dim() == 3 else t.unsqueeze(0)
+    if t3.dim() != 3 or t3.stride(2) != 1:
+        raise ValueError("the matrices must have contiguous rows (unit column stride)")
+    b, m, n = t3.shape
+    ld = t3.stride(1) if m > 1 else n
+    stride = t3.stride(0) if b > 1 else m * ld
+    return t3, int(b), int(m), int(n), int(ld), int(stride)
+
+
 def muon_ns_orthogonalize(G, O, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=False, workspace=None,
                           stream=None, schedule=MUON_NS_AUTO):
-    """O[b] = NS(G[b]) for contiguous [batch, m, n] (or [m, n]) tensors."""
+    """O[b] = NS(G[b]) for [batch, m, n] (or [m, n]) tensors whose rows are
+    contiguous: row and matrix strides (ld, stride) are taken from G, and O
+    must have the same strides (O may be G itself: in place)."""
     import torch
     L = lib()
-    G3 = G if G.dim() == 3 else G.unsqueeze(0)
-    O3 = O if O.dim() == 3 else O.unsqueeze(0)
-    if not (G3.is_contiguous() and O3.is_contiguous()) or G3.shape != O3.shape or G3.dtype != O3.dtype:
-        raise ValueError("G and O must be contiguous tensors of one shape and dtype")
-    b, m, n = G3.shape
+    dev = _current_device()
+    G3, b, m, n, ld, stride = _strided_stack(G)
+    O3, bo, mo, no, ldo, so = _strided_stack(O)
+    if (b, m, n) != (bo, mo, no) or (ld, stride) != (ldo, so) or G3.dtype != O3.dtype:
+        raise ValueError("G and O must have one shape, dtype and stride layout")
+    _check_tensors([G3, O3], "G and O", (torch.bfloat16, torch.float32), dev)
     dt = _dtype_code(G3)
     cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step, schedule)
     need = int(L.muon_ns_workspace_size(m, n, b, dt, ctypes.byref(cfg)))
     if need == 0:
         _check(MUON_EINVAL, "muon_ns_workspace_size")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=G.device)
-    rc = L.muon_ns_orthogonalize(ctypes.c_void_p(G3.data_ptr()), ctypes.c_void_p(O3.data_ptr()), dt, m, n, b,
-                                 ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+    workspace = _workspace(workspace, need, dev)
+    rc = L.muon_ns_orthogonalize(ctypes.c_void_p(G3.data_ptr()), ctypes.c_void_p(O3.data_ptr()), dt, m, n, ld, b,
+                                 stride, ctypes.byref(cfg), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                  _stream_handle(stream))
     _check(rc, "muon_ns_orthogonalize")
     return workspace
 
 
+def muon_query_flags(workspace) -> int:
+    """The non-finite flag (0 or 1) of the last muon_step / muon_ns_orthogonalize
+    call that used this workspace; synchronise its stream first."""
+    import torch
+    if workspace is None or workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be the uint8 device tensor returned by muon_step")
+    out = ctypes.c_int(-1)
+    _check(lib().muon_query_flags(ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(out)), "muon_query_flags")
+    return int(out.value)
+
+
 def muon_ns_batched_small(X, Y, steps=1, coeffs=(1.5, -0.5), eps=1e-7, per_step=False, stream=None):
     """Y[b] = NS(X[b]) for a contiguous [batch, m, n] stack of small matrices."""
+    import torch
     L = lib()
     if X.dim() != 3 or not (X.is_contiguous() and Y.is_contiguous()) or X.shape != Y.shape or X.dtype != Y.dtype:
         raise ValueError("X and Y must be contiguous [batch, m, n] tensors of one shape and dtype")
+    _check_tensors([X, Y], "X and Y", (torch.bfloat16, torch.float32), _current_device())
     b, m, n = X.shape
     dt = _dtype_code(X)
     cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step)
@@ -350,11 +430,18 @@ def muon_ns_factored(V, K, C=None, O=None, steps=1, coeffs=(1.5, -0.5), eps=1e-7
         raise ValueError("V and K must be contiguous tensors of one dtype")
     b, m, r = V.shape
     n = K.shape[1]
+    dev = _current_device()
+    _check_tensors([V, K], "V and K", (torch.bfloat16, torch.float32), dev)
     dt = _dtype_code(V)
     if C is None:
-        C = torch.empty(b, r, r, dtype=torch.float32, device=V.device)
+        C = torch.empty(b, r, r, dtype=torch.float32, device=dev)
+    if not C.is_contiguous() or tuple(C.shape) != (b, r, r):
+        raise ValueError(f"C must be a contiguous [{b}, {r}, {r}] float32 tensor")
+    _check_tensors([C], "C", (torch.float32,), dev)
     if O is not None and (not O.is_contiguous() or tuple(O.shape) != (b, m, n) or O.dtype != V.dtype):
         raise ValueError("O must be a contiguous [batch, m, n] tensor of V's dtype")
+    if O is not None:
+        _check_tensors([O], "O", (V.dtype,), dev)
     cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step)
     rc = L.muon_ns_factored(ctypes.c_void_p(V.data_ptr()), ctypes.c_void_p(K.data_ptr()), dt, m, n, r, b,
                             ctypes.byref(cfg), ctypes.cast(ctypes.c_void_p(C.data_ptr()), ctypes.POINTER(ctypes.c_float)),
@@ -371,14 +458,20 @@ class AdamwTensors:
         n = len(params)
         if not (len(grads) == len(exp_avg) == len(exp_avg_sq) == n):
             raise ValueError("params, grads, exp_avg, exp_avg_sq must have the same length")
+        import torch
         self.n = n
         self.gd = _dtype_code(grads[0]) if n else MUON_F32
         for p, g, m, v in zip(params, grads, exp_avg, exp_avg_sq):
             if not all(t.is_contiguous() for t in (p, g, m, v)) or \
                     not (p.numel() == g.numel() == m.numel() == v.numel()):
                 raise ValueError("every tensor must be contiguous, with matching sizes")
-            if _dtype_code(g) != self.gd:
-                raise ValueError("all gradients must have one dtype")
+        self.device = params[0].device if n else None
+        if n and self.device.type != "cuda":
+            raise ValueError(f"params must be CUDA tensors (got {self.device})")
+        _check_tensors(list(params), "params", (torch.float32,), self.device)
+        _check_tensors(list(exp_avg), "exp_avg", (torch.float32,), self.device)
+        _check_tensors(list(exp_avg_sq), "exp_avg_sq", (torch.float32,), self.device)
+        _check_tensors(list(grads), "grads", (torch.bfloat16, torch.float32), self.device)
         cast = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p))  # noqa: E731
         self._keep = [params, grads, exp_avg, exp_avg_sq]
         self._arrays = [_ptrs(params), _ptrs(grads), _ptrs(exp_avg), _ptrs(exp_avg_sq)]
@@ -388,6 +481,8 @@ class AdamwTensors:
     def step(self, lr, step, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, stream=None):
         if self.n == 0:
             return
+        if self.device != _current_device():
+            raise ValueError(f"the tensors are on {self.device}, the current device is {_current_device()}")
         rc = lib().muon_adamw(self.n, *self.ptrs, self.numel, self.gd, float(lr), float(beta1), float(beta2),
                               float(eps), float(weight_decay), int(step), _stream_handle(stream))
         _check(rc, "muon_adamw")
@@ -413,18 +508,19 @@ def muon_spectral_diag(A, iters=32, orth_err=True, sigma_max=True, sigma_min=Tru
         A = A.unsqueeze(0)
     if A.dim() != 3 or not A.is_contiguous():
         raise ValueError("A must be a contiguous [batch, m, n] tensor")
+    dev = _current_device()
+    _check_tensors([A], "A", (torch.bfloat16, torch.float32), dev)
     b, m, n = A.shape
     dt = _dtype_code(A)
     outs = {}
     for name, want in (("orth_err", orth_err), ("sigma_max", sigma_max), ("sigma_min", sigma_min)):
         if want:
-            outs[name] = torch.empty(b, dtype=torch.float32, device=A.device)
+            outs[name] = torch.empty(b, dtype=torch.float32, device=dev)
     need = L.muon_spectral_diag_workspace_size(m, n, b, dt, int(iters))
     if need == 0:
         rc = L.muon_spectral_diag(None, dt, m, n, b, int(iters), None, None, None, None, 0, None)
         _check(rc if rc != MUON_OK else -1, "muon_spectral_diag")
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    workspace = _workspace(workspace, max(int(need), 1), dev)
     ptr = lambda k: ctypes.c_void_p(outs[k].data_ptr()) if k in outs else None  # noqa: E731
     args = (ctypes.c_void_p(A.data_ptr()), dt, m, n, b, int(iters), ptr("orth_err"), ptr("sigma_max"),
             ptr("sigma_min"), ctypes.c_void_p(workspace.data_ptr()), need, _stream_handle(stream))

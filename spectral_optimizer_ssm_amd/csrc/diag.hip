@@ -942,10 +942,11 @@ long long diag_split_clear_words(DiagLaunch& D) {
 hipError_t launch_diag_lanczos(const DiagLaunch& D0, hipStream_t st) {
   if (D0.count == 0) return hipSuccess;
   DiagLaunch D = D0;
-  // test hook: MUON_DIAG_SPIN_LIMIT shortens the split run's bounded waits so
-  // that their give-up path (NaN outputs, every wave ends) can be exercised
+  // debug hook for tests only: MUON_DEBUG_DIAG_SPIN_LIMIT shortens the split
+  // run's bounded waits so that their give-up path (NaN outputs, every wave
+  // ends) can be exercised; it can only lower the bound
   D.spin_limit = kSpinLimit;
-  if (const char* e = std::getenv("MUON_DIAG_SPIN_LIMIT")) {
+  if (const char* e = std::getenv("MUON_DEBUG_DIAG_SPIN_LIMIT")) {
     char* end = nullptr;
     const unsigned long v = std::strtoul(e, &end, 10);
     if (end != e && v < kSpinLimit) D.spin_limit = static_cast<unsigned>(v);

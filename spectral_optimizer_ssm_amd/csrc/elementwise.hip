@@ -65,7 +65,7 @@ __device__ __forceinline__ float momentum1(float g, float* mp, bool has_m, float
 // ---------------------------------------------------------------------------
 template <typename GT, typename XT>
 __global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTable M, XT* X, long long xstride,
-                                                            int m, int n, int s_pad, int ld, float beta,
+                                                            int m, int n, int ldg, int s_pad, int ld, float beta,
                                                             int nesterov, float* partials, int P) {
   __shared__ float red[8];
   const int z = blockIdx.y;
@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTa
   const bool nest = nesterov != 0;
   const long long chunks = static_cast<long long>(s_pad) * (ld / 8);
   const int cpr = ld / 8;
-  const bool vec = (n % 8) == 0 && a16(g) && (!has_m || a16(mm));
+  const bool vec = (n % 8) == 0 && (ldg % 8) == 0 && a16(g) && (!has_m || a16(mm));
   float ss = 0.0f;
   for (long long c = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
        c += static_cast<long long>(gridDim.x) * blockDim.x) {
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTa
     if (r < m && c0 < n && vec) {
       float gv[8], mv[8];
       const long long off = static_cast<long long>(r) * n + c0;
-      Vec8<GT>::load(g + off, gv);
+      Vec8<GT>::load(g + static_cast<long long>(r) * ldg + c0, gv);
       if (has_m) Vec8<float>::load(mm + off, mv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTa
         u[j] = 0.0f;
         if (r < m && c0 + j < n) {
           const long long off = static_cast<long long>(r) * n + c0 + j;
-          u[j] = momentum1(ld1<GT>(g + off), mm + off, has_m, beta, nest);
+          u[j] = momentum1(ld1<GT>(g + static_cast<long long>(r) * ldg + c0 + j), mm + off, has_m, beta, nest);
           ss = fmaf(u[j], u[j], ss);
         }
       }
@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTa
 // ---------------------------------------------------------------------------
 template <typename GT, typename XT>
 __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTable M, XT* X, long long xstride,
-                                                            int m, int n, int s_pad, int ld, float beta,
+                                                            int m, int n, int ldg, int s_pad, int ld, float beta,
                                                             int nesterov, float* partials, int P) {
   __shared__ float tile[64][65];
   __shared__ float red[8];
@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTa
   const int tiles_k = (ld + 63) / 64;
   const int i0 = (blockIdx.x / tiles_k) * 64;  // X rows  = U columns (short side)
   const int k0 = (blockIdx.x % tiles_k) * 64;  // X cols  = U rows    (long side)
-  const bool vec = (n % 8) == 0 && a16(g) && (!has_m || a16(mm));
+  const bool vec = (n % 8) == 0 && (ldg % 8) == 0 && a16(g) && (!has_m || a16(mm));
   const int t = threadIdx.x;
   float ss = 0.0f;
 #pragma unroll
@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTa
     if (ur < m && uc + 7 < n && vec) {
       float gv[8], mv[8];
       const long long off = static_cast<long long>(ur) * n + uc;
-      Vec8<GT>::load(g + off, gv);
+      Vec8<GT>::load(g + static_cast<long long>(ur) * ldg + uc, gv);
       if (has_m) Vec8<float>::load(mm + off, mv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -156,7 +156,7 @@ __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTa
         u[j] = 0.0f;
         if (ur < m && uc + j < n) {
           const long long off = static_cast<long long>(ur) * n + uc + j;
-          u[j] = momentum1(ld1<GT>(g + off), mm + off, has_m, beta, nest);
+          u[j] = momentum1(ld1<GT>(g + static_cast<long long>(ur) * ldg + uc + j), mm + off, has_m, beta, nest);
           ss = fmaf(u[j], u[j], ss);
         }
       }
@@ -213,7 +213,7 @@ __device__ __forceinline__ float cap_gamma(const ApplyArgs& a, int z, float* red
 
 template <typename XT>
 __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long xstride, int m, int n, int ld,
-                                                         MutPtrTable W, MutPtrTable O, ApplyArgs a) {
+                                                         int ldo, MutPtrTable W, MutPtrTable O, ApplyArgs a) {
   __shared__ float red[8];
   const int z = blockIdx.y;
   const XT* x = X + z * xstride;
@@ -225,12 +225,13 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
   const float* cv = static_cast<const float*>(a.cv.p[z]);
   const int cpr = (n + 7) / 8;
   const long long chunks = static_cast<long long>(m) * cpr;
-  const bool vec = (n % 8) == 0 && (!w || a16(w)) && (!o || a16(o));
+  const bool vec = (n % 8) == 0 && (ldo % 8) == 0 && (!w || a16(w)) && (!o || a16(o));
   for (long long c = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
        c += static_cast<long long>(gridDim.x) * blockDim.x) {
     const int r = static_cast<int>(c / cpr);
     const int c0 = static_cast<int>(c % cpr) * 8;
     const long long off = static_cast<long long>(r) * n + c0;
+    const long long ooff = static_cast<long long>(r) * ldo + c0;
     if (vec) {
       float ov[8], wv[8];
       Vec8<XT>::load(x + static_cast<long long>(r) * ld + c0, ov);
@@ -241,7 +242,7 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
 #pragma unroll
         for (int j = 0; j < 8; ++j) ov[j] = fmaf(-gu, cv[c0 + j], ov[j]);
       }
-      if (o) Vec8<XT>::store(o + off, ov);
+      if (o) Vec8<XT>::store(o + ooff, ov);
       if (w) {
         Vec8<float>::load(w + off, wv);
 #pragma unroll
@@ -252,7 +253,7 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
       for (int j = 0; j < 8 && c0 + j < n; ++j) {
         float ov = ld1<XT>(x + static_cast<long long>(r) * ld + c0 + j) * inv;
         if (gamma != 0.0f) ov = fmaf(-gamma * cu[r], cv[c0 + j], ov);
-        if (o) st1<XT>(o + off + j, ov);
+        if (o) st1<XT>(o + ooff + j, ov);
         if (w) w[off + j] = fmaf(a.neg_lr_scale, ov, w[off + j]);
       }
     }
@@ -261,7 +262,7 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
 
 template <typename XT>
 __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long xstride, int m, int n, int ld,
-                                                         MutPtrTable W, MutPtrTable O, ApplyArgs a) {
+                                                         int ldo, MutPtrTable W, MutPtrTable O, ApplyArgs a) {
   __shared__ float tile[64][65];
   __shared__ float red[8];
   const int z = blockIdx.y;
@@ -293,7 +294,7 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
     for (int j = 0; j < 8; ++j) tile[kc + j][ir] = v[j] * inv;
   }
   __syncthreads();
-  const bool vec = (n % 8) == 0 && (!w || a16(w)) && (!o || a16(o));
+  const bool vec = (n % 8) == 0 && (ldo % 8) == 0 && (!w || a16(w)) && (!o || a16(o));
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int kr = t / 8 + 32 * pass;
@@ -301,6 +302,7 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
     const int ur = k0 + kr, uc = i0 + ic;
     if (ur >= m) continue;
     const long long off = static_cast<long long>(ur) * n + uc;
+    const long long ooff = static_cast<long long>(ur) * ldo + uc;
     if (vec && uc + 7 < n) {
       float ov[8], wv[8];
 #pragma unroll
@@ -310,7 +312,7 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
 #pragma unroll
         for (int j = 0; j < 8; ++j) ov[j] = fmaf(-gu, cv[uc + j], ov[j]);
       }
-      if (o) Vec8<XT>::store(o + off, ov);
+      if (o) Vec8<XT>::store(o + ooff, ov);
       if (w) {
         Vec8<float>::load(w + off, wv);
 #pragma unroll
@@ -321,7 +323,7 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
       for (int j = 0; j < 8 && uc + j < n; ++j) {
         float ov = tile[kr][ic + j];
         if (gamma != 0.0f) ov = fmaf(-gamma * cu[ur], cv[uc + j], ov);
-        if (o) st1<XT>(o + off + j, ov);
+        if (o) st1<XT>(o + ooff + j, ov);
         if (w) w[off + j] = fmaf(a.neg_lr_scale, ov, w[off + j]);
       }
     }
@@ -335,6 +337,31 @@ __global__ void __launch_bounds__(256) norms_kernel(const float* partials, int P
   float nu = 0.0f;
   inv_norm_from_partials(partials + static_cast<long long>(z) * P, P, 0.0f, red, &nu);
   if (threadIdx.x == 0) out[z] = nu;
+}
+
+// Non-finite flag of a call: any partial sum of squares of the update
+// direction that is not finite (a NaN or Inf in G or M, or an overflow of
+// ||U||^2).  One workgroup; every thread issues all of its loads before it
+// tests them; the flag is written with a plain store.
+__global__ void __launch_bounds__(1024) flags_kernel(const float* partials, long long n, unsigned* flag) {
+  __shared__ int any;
+  if (threadIdx.x == 0) any = 0;
+  __syncthreads();
+  constexpr int U = 16;
+  int bad = 0;
+  for (long long i0 = 0; i0 < n; i0 += static_cast<long long>(U) * blockDim.x) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long i = i0 + static_cast<long long>(u) * blockDim.x + threadIdx.x;
+      v[u] = i < n ? partials[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) bad |= !__builtin_isfinite(v[u]);
+  }
+  if (bad) any = 1;
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = static_cast<unsigned>(any);
 }
 
 // ---------------------------------------------------------------------------
@@ -356,11 +383,11 @@ hipError_t launch_momentum(const MomentumLaunch& L, hipStream_t st) {
   do {                                                                                              \
     if (L.tall)                                                                                     \
       hipLaunchKernelGGL((momentum_tall_kernel<GT, XT>), grid, block, 0, st, L.G, L.M,              \
-                         static_cast<XT*>(L.X), L.xstride, L.m, L.n, L.s_pad, L.ld, L.beta,         \
+                         static_cast<XT*>(L.X), L.xstride, L.m, L.n, L.ldg, L.s_pad, L.ld, L.beta,  \
                          L.nesterov, L.partials, L.P);                                              \
     else                                                                                            \
       hipLaunchKernelGGL((momentum_wide_kernel<GT, XT>), grid, block, 0, st, L.G, L.M,              \
-                         static_cast<XT*>(L.X), L.xstride, L.m, L.n, L.s_pad, L.ld, L.beta,         \
+                         static_cast<XT*>(L.X), L.xstride, L.m, L.n, L.ldg, L.s_pad, L.ld, L.beta,  \
                          L.nesterov, L.partials, L.P);                                              \
   } while (0)
   if (L.grad_bf16 && L.x_bf16) MUON_MOM(bf16_t, bf16_t);
@@ -378,10 +405,10 @@ hipError_t launch_apply(const ApplyLaunch& L, hipStream_t st) {
     const dim3 grid(((L.m + 63) / 64) * ((L.n + 63) / 64), L.count);
     if (L.x_bf16)
       hipLaunchKernelGGL((apply_tall_kernel<bf16_t>), grid, block, 0, st, static_cast<const bf16_t*>(L.X),
-                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+                         L.xstride, L.m, L.n, L.ld, L.ldo, L.W, L.O, a);
     else
       hipLaunchKernelGGL((apply_tall_kernel<float>), grid, block, 0, st, static_cast<const float*>(L.X),
-                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+                         L.xstride, L.m, L.n, L.ld, L.ldo, L.W, L.O, a);
   } else {
     const long long chunks = static_cast<long long>(L.m) * ((L.n + 7) / 8);
     long long b = (chunks + 256 * 8 - 1) / (256 * 8);
@@ -390,16 +417,21 @@ hipError_t launch_apply(const ApplyLaunch& L, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(b), L.count);
     if (L.x_bf16)
       hipLaunchKernelGGL((apply_wide_kernel<bf16_t>), grid, block, 0, st, static_cast<const bf16_t*>(L.X),
-                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+                         L.xstride, L.m, L.n, L.ld, L.ldo, L.W, L.O, a);
     else
       hipLaunchKernelGGL((apply_wide_kernel<float>), grid, block, 0, st, static_cast<const float*>(L.X),
-                         L.xstride, L.m, L.n, L.ld, L.W, L.O, a);
+                         L.xstride, L.m, L.n, L.ld, L.ldo, L.W, L.O, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_norms(const float* partials, int P, int count, float* out, hipStream_t st) {
   hipLaunchKernelGGL(norms_kernel, dim3(count), dim3(256), 0, st, partials, P, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_flags(const float* partials, long long n, unsigned* flag, hipStream_t st) {
+  hipLaunchKernelGGL(flags_kernel, dim3(1), dim3(1024), 0, st, partials, n, flag);
   return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ struct MomentumLaunch {
   void* X;             // oriented iterate of the first matrix, s_pad x ld
   long long xstride;   // elements between consecutive matrices of X
   int m, n, s_pad, ld, count, P;
+  int ldg;             // row stride of G (elements, >= n); M is contiguous (n)
   bool tall, grad_bf16, x_bf16;
   float beta;
   int nesterov;
@@ -25,6 +26,7 @@ struct ApplyLaunch {
   const void* X;       // final iterate (oriented), s_pad x ld
   long long xstride;
   int m, n, ld, count;
+  int ldo;             // row stride of O (elements, >= n); W is contiguous (n)
   bool tall, x_bf16;
   MutPtrTable W;       // entries may be null (no apply)
   MutPtrTable O;       // entries may be null (no copy-out); element type = X's
@@ -91,6 +93,9 @@ int momentum_blocks_per_matrix(bool tall, int s_pad, int ld);
 hipError_t launch_momentum(const MomentumLaunch& L, hipStream_t st);
 hipError_t launch_apply(const ApplyLaunch& L, hipStream_t st);
 hipError_t launch_norms(const float* partials, int P, int count, float* out, hipStream_t st);
+// flag = 1 if any of the n partial sums of squares is not finite, else 0
+// (one workgroup; a plain store)
+hipError_t launch_flags(const float* partials, long long n, unsigned* flag, hipStream_t st);
 
 // bf16 matrix-core path.  One launch covers up to kMaxSeg shape groups
 // (segments) of one Newton-Schulz step.

@@ -27,6 +27,10 @@ namespace {
 
 constexpr int kMaxSteps = 64;
 constexpr size_t kAlign = 256;
+// Every muon_step / muon_ns_orthogonalize workspace opens with this header:
+// word 0 is the non-finite flag of the last call (muon_query_flags); the
+// per-block partial sums of squares of all groups follow it, contiguous.
+constexpr size_t kHeader = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int round_up(int x, int a) { return (x + a - 1) / a * a; }
@@ -113,7 +117,11 @@ bool choose_accumulate(const GroupPlan& g, const NsCoefs& C) {
   return gram + comb + (3.0 * (C.steps - 1) + q * C.steps) * prod < 0.85 * C.steps * (gram + comb + q * prod);
 }
 
-int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base, GroupPlan* g, bool cap = false) {
+// Shapes, engine, schedule and the group's own buffers from `base` on; its
+// partial sums go to `part_off` (all groups' partials sit together after the
+// workspace header, see plan_groups).
+int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base, GroupPlan* g, bool cap = false,
+               size_t part_off = kHeader) {
   if (m <= 0 || n <= 0 || count < 0) return MUON_EINVAL;
   if (static_cast<long long>(m) * n > (1LL << 31)) return MUON_EUNSUPPORTED;
   g->m = m;
@@ -145,6 +153,7 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
   if (C.quintic && g->engine != kTiledBf16) return MUON_EUNSUPPORTED;  // c != 0: large bf16 matrices only
   g->accumulate = choose_accumulate(*g, C);
   g->P = momentum_blocks_per_matrix(g->tall, g->s_pad, g->ld);
+  g->off_part = part_off;
   const size_t xbytes = static_cast<size_t>(count) * g->s_pad * g->ld * g->esz;
   size_t off = align_up(base, kAlign);
   g->off_x0 = off;
@@ -156,8 +165,6 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
     off = align_up(off + sq_buffers(g->accumulate, C.quintic) * static_cast<size_t>(count) * g->s_pad * g->s_pad *
                              g->esz,
                    kAlign);
-  g->off_part = off;
-  off = align_up(off + static_cast<size_t>(count) * g->P * sizeof(float), kAlign);
   g->cap = cap;
   if (cap) {
     g->off_cap = off;
@@ -201,6 +208,35 @@ int validate_group(const muon_group& gr) {
   return MUON_OK;
 }
 
+// Workspace plan of a list of groups: the header, then the partial sums of
+// every group (contiguous, so that one pass can scan them), then each group's
+// buffers.  Returns MUON_OK and the total size in *end, the number of partial
+// sums in *nparts.
+struct GroupShape {
+  int m, n, count;
+  bool cap;
+};
+int plan_groups(const std::vector<GroupShape>& shapes, bool bf16, const NsCoefs& C, std::vector<GroupPlan>& plans,
+                size_t* end, long long* nparts) {
+  plans.assign(shapes.size(), GroupPlan{});
+  long long parts = 0;
+  for (size_t i = 0; i < shapes.size(); ++i) {
+    const int rc = plan_group(shapes[i].m, shapes[i].n, shapes[i].count, bf16, C, 0, &plans[i], shapes[i].cap);
+    if (rc != MUON_OK) return rc;
+    parts += static_cast<long long>(plans[i].count) * plans[i].P;
+  }
+  size_t off = align_up(kHeader + static_cast<size_t>(parts) * sizeof(float), kAlign);
+  size_t part = kHeader;
+  for (size_t i = 0; i < shapes.size(); ++i) {
+    plan_group(shapes[i].m, shapes[i].n, shapes[i].count, bf16, C, off, &plans[i], shapes[i].cap, part);
+    part += static_cast<size_t>(plans[i].count) * plans[i].P * sizeof(float);
+    off = plans[i].end;
+  }
+  *end = off;
+  *nparts = parts;
+  return MUON_OK;
+}
+
 // Everything the launch schedule needs for one group of matrices.
 struct GroupRun {
   GroupPlan plan;
@@ -213,6 +249,7 @@ struct GroupRun {
   std::vector<void*> o_own;
   float beta = 0.0f, neg_lr_scale = 0.0f;
   int nesterov = 0;
+  int ldg = 0, ldo = 0;            // row strides of G and O (elements; 0: n)
   int norm_base = 0;               // first slot of this group in norms_out
   float* const* cap_u = nullptr;   // spectral cap state (null: off)
   float* const* cap_v = nullptr;
@@ -283,10 +320,15 @@ std::vector<SymSeg> grams_as_sym(const std::vector<GemmSeg>& gs, bool tri_out = 
   return out;
 }
 
+int flags_pass(long long nparts, char* ws, hipStream_t st, EventRec& E);
+
 // after_momentum: when non-null, recorded on st once the momentum passes of
-// these groups have been enqueued.
+// these groups have been enqueued.  flags_nparts >= 0: after those passes,
+// the call's non-finite flag from the first flags_nparts partial sums (every
+// group's partials are complete by then: this run's momentum passes are the
+// call's last ones).
 int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, float* norms_out, hipStream_t st,
-            EventRec& E, hipEvent_t after_momentum = nullptr) {
+            EventRec& E, hipEvent_t after_momentum = nullptr, long long flags_nparts = -1) {
   if (!E.mark(st, 0)) return MUON_EHIP;
   // 1. momentum
   for (GroupRun& R : runs) {
@@ -304,6 +346,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       L.X = ws + p.off_x0 + static_cast<size_t>(c0) * xstride * p.esz;
       L.xstride = xstride;
       L.m = p.m; L.n = p.n; L.s_pad = p.s_pad; L.ld = p.ld; L.count = cn; L.P = p.P;
+      L.ldg = R.ldg > 0 ? R.ldg : p.n;
       L.tall = p.tall; L.grad_bf16 = R.grad_dtype == MUON_BF16; L.x_bf16 = p.bf16;
       L.beta = R.beta; L.nesterov = R.nesterov;
       L.partials = part + static_cast<size_t>(c0) * p.P;
@@ -315,6 +358,10 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     if (!E.mark(st, MUON_PHASE_MOMENTUM)) return MUON_EHIP;
   }
   if (after_momentum != nullptr && E.live() && hipEventRecord(after_momentum, st) != hipSuccess) return MUON_EHIP;
+  if (flags_nparts >= 0) {
+    const int rc = flags_pass(flags_nparts, ws, st, E);
+    if (rc != MUON_OK) return rc;
+  }
 
   // 2. small matrices on chip
   std::vector<int> fin(runs.size(), 0);  // which buffer holds the final iterate
@@ -375,8 +422,9 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       int tab = 0;
       for (size_t i = c0; i < std::min(order.size(), c0 + kMaxSeg); ++i) {
         const GroupRun& R = runs[order[i]];
+        // (the fused epilogue writes O with rows n apart: a strided O keeps the apply pass)
         const bool ok = !C.separate_apply && !R.plan.cap && (R.W != nullptr || R.O != nullptr) &&
-                        tab + R.plan.count <= kMaxTable;
+                        (R.ldo == 0 || R.ldo == R.plan.n) && tab + R.plan.count <= kMaxTable;
         fused[order[i]] = ok;
         if (ok) tab += R.plan.count;
       }
@@ -631,6 +679,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
         A.X = x_of(p, ws, fin[gi]) + static_cast<size_t>(c0) * xstride * p.esz;
         A.xstride = xstride;
         A.m = p.m; A.n = p.n; A.ld = p.ld; A.count = cn;
+        A.ldo = R.ldo > 0 ? R.ldo : p.n;
         A.tall = p.tall; A.x_bf16 = p.bf16;
         A.partials = C.steps == 0 ? reinterpret_cast<const float*>(ws + p.off_part) + static_cast<size_t>(c0) * p.P
                                   : nullptr;
@@ -670,13 +719,23 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
   return MUON_OK;
 }
 
+// The non-finite flag of the header from the partial sums of all groups,
+// enqueued once every momentum pass of the call is.
+int flags_pass(long long nparts, char* ws, hipStream_t st, EventRec& E) {
+  if (nparts == 0) return MUON_OK;  // no matrix: nothing ran, the flag is left as it was
+  if (E.live() && launch_flags(reinterpret_cast<const float*>(ws + kHeader), nparts, reinterpret_cast<unsigned*>(ws),
+                               st) != hipSuccess)
+    return MUON_EHIP;
+  return E.mark(st, MUON_PHASE_FLAGS) ? MUON_OK : MUON_EHIP;
+}
+
 // The marks run_all makes, in order (the first is the start mark, phase 0),
 // from a dry run that launches nothing and touches no memory.
-std::vector<int> list_phases(std::vector<GroupRun>& runs, const NsCoefs& C, float eps) {
+std::vector<int> list_phases(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, long long nparts) {
   EventRec D;
   D.dry = true;
   char* fake_ws = reinterpret_cast<char*>(static_cast<uintptr_t>(kAlign));
-  run_all(runs, C, eps, fake_ws, nullptr, nullptr, D);
+  run_all(runs, C, eps, fake_ws, nullptr, nullptr, D, nullptr, nparts);
   return D.phases;
 }
 
@@ -709,26 +768,34 @@ Aux* aux_for_current_device() {
   return table[dev];
 }
 
-int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, void* workspace, size_t workspace_bytes,
-              float* norms_out, void* stream, void* const* events, int nevents) {
+// Validates every group, plans the workspace and fills the launch records.
+int prepare_step(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, NsCoefs* C,
+                 std::vector<GroupRun>& runs, size_t* end, long long* nparts, bool validate_ptrs) {
   if (groups == nullptr || ngroups <= 0) return MUON_EINVAL;
-  NsCoefs C;
-  int rc = parse_cfg(cfg, &C, true);
+  int rc = parse_cfg(cfg, C, true);
   if (rc != MUON_OK) return rc;
-  if (norms_out != nullptr && !aligned_to(norms_out, 4)) return MUON_EINVAL;
-  std::vector<GroupRun> runs(ngroups);
-  size_t off = 0;
+  std::vector<GroupShape> shapes(ngroups);
   for (int i = 0; i < ngroups; ++i) {
     const muon_group& gr = groups[i];
-    rc = validate_group(gr);
-    if (rc != MUON_OK) return rc;
-    if (gr.O != nullptr)
-      for (int j = 0; j < gr.count; ++j)
-        if (!aligned_to(gr.O[j], dtype_size(cfg->precision))) return MUON_EINVAL;
-    if (gr.cap_u != nullptr && gr.W == nullptr) return MUON_EINVAL;
-    rc = plan_group(gr.m, gr.n, gr.count, cfg->precision == MUON_BF16, C, off, &runs[i].plan, gr.cap_u != nullptr);
-    if (rc != MUON_OK) return rc;
-    off = runs[i].plan.end;
+    if (validate_ptrs) {
+      rc = validate_group(gr);
+      if (rc != MUON_OK) return rc;
+      if (gr.O != nullptr)
+        for (int j = 0; j < gr.count; ++j)
+          if (!aligned_to(gr.O[j], dtype_size(cfg->precision))) return MUON_EINVAL;
+      if (gr.cap_u != nullptr && gr.W == nullptr) return MUON_EINVAL;
+    } else if (gr.grad_dtype != MUON_F32 && gr.grad_dtype != MUON_BF16) {
+      return MUON_EINVAL;
+    }
+    shapes[i] = GroupShape{gr.m, gr.n, gr.count, gr.cap_u != nullptr};
+  }
+  std::vector<GroupPlan> plans;
+  rc = plan_groups(shapes, cfg->precision == MUON_BF16, *C, plans, end, nparts);
+  if (rc != MUON_OK) return rc;
+  runs.assign(ngroups, GroupRun{});
+  for (int i = 0; i < ngroups; ++i) {
+    const muon_group& gr = groups[i];
+    runs[i].plan = plans[i];
     runs[i].cap_u = gr.cap_u;
     runs[i].cap_v = gr.cap_v;
     runs[i].cap_sigma = gr.cap_sigma;
@@ -743,18 +810,30 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
     runs[i].nesterov = gr.nesterov;
     runs[i].norm_base = i == 0 ? 0 : runs[i - 1].norm_base + groups[i - 1].count;
   }
-  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < off) return MUON_EWORKSPACE;
+  return MUON_OK;
+}
+
+int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, void* workspace, size_t workspace_bytes,
+              float* norms_out, void* stream, void* const* events, int nevents) {
+  NsCoefs C;
+  std::vector<GroupRun> runs;
+  size_t need = 0;
+  long long nparts = 0;
+  int rc = prepare_step(groups, ngroups, cfg, &C, runs, &need, &nparts, true);
+  if (rc != MUON_OK) return rc;
+  if (norms_out != nullptr && !aligned_to(norms_out, 4)) return MUON_EINVAL;
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return MUON_EWORKSPACE;
   EventRec E;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (events != nullptr) {
-    const int need = static_cast<int>(list_phases(runs, C, cfg->eps).size());
-    if (nevents < need) return MUON_EINVAL;
-    for (int i = 0; i < need; ++i)
+    const int need_ev = static_cast<int>(list_phases(runs, C, cfg->eps, nparts).size());
+    if (nevents < need_ev) return MUON_EINVAL;
+    for (int i = 0; i < need_ev; ++i)
       if (events[i] == nullptr) return MUON_EINVAL;
     E.ev = events;
     E.n = nevents;
-    return run_all(runs, C, cfg->eps, ws, norms_out, st, E);  // timed: one stream, phases in order
+    return run_all(runs, C, cfg->eps, ws, norms_out, st, E, nullptr, nparts);  // timed: one stream, phases in order
   }
   // Independent shape groups run as two chains on two streams (the caller's
   // and an auxiliary one, joined back before returning), so that one chain's
@@ -767,7 +846,7 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   for (int i = 0; i < ngroups; ++i)
     if (runs[i].plan.count > 0) live.push_back(i);
   Aux* aux = cfg->streams == 1 || live.size() < 2 ? nullptr : aux_for_current_device();
-  if (aux == nullptr) return run_all(runs, C, cfg->eps, ws, norms_out, st, E);
+  if (aux == nullptr) return run_all(runs, C, cfg->eps, ws, norms_out, st, E, nullptr, nparts);
   auto cost = [&](int i) {
     const GroupPlan& p = runs[i].plan;
     return static_cast<double>(p.count) * p.m * p.n * (p.engine == kSmall ? 16.0 : p.s + 64.0);
@@ -784,7 +863,9 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   EventRec E1;
   rc = run_all(chain[0], C, cfg->eps, ws, norms_out, st, E, aux->fork);  // fork: after chain 0's momentum
   if (hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess) return MUON_EHIP;
-  const int rc1 = rc == MUON_OK ? run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1) : MUON_OK;
+  // the second chain's momentum passes are the call's last: the flag follows them on that stream
+  const int rc1 = rc == MUON_OK ? run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1, nullptr, nparts)
+                                : MUON_OK;
   // join even after a failed launch, so that the caller's stream never runs ahead of the auxiliary work
   if (hipEventRecord(aux->join, aux->s) != hipSuccess || hipStreamWaitEvent(st, aux->join, 0) != hipSuccess)
     return MUON_EHIP;
@@ -850,16 +931,11 @@ int muon_version(void) { return MUON_VERSION; }
 
 size_t muon_step_workspace_size(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg) {
   NsCoefs C;
-  if (groups == nullptr || ngroups <= 0 || parse_cfg(cfg, &C, true) != MUON_OK) return 0;
-  size_t off = 0;
-  for (int i = 0; i < ngroups; ++i) {
-    GroupPlan g;
-    if (plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &g,
-                   groups[i].cap_u != nullptr) != MUON_OK)
-      return 0;
-    off = g.end;
-  }
-  return off == 0 ? kAlign : off;
+  std::vector<GroupRun> runs;
+  size_t need = 0;
+  long long nparts = 0;
+  if (prepare_step(groups, ngroups, cfg, &C, runs, &need, &nparts, false) != MUON_OK) return 0;
+  return need;
 }
 
 int muon_step(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, void* workspace,
@@ -868,24 +944,15 @@ int muon_step(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
 }
 
 int muon_step_phases(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, int* phases, int max_phases) {
-  NsCoefs C;
   if (groups == nullptr || ngroups <= 0 || max_phases < 0 || (phases == nullptr && max_phases > 0))
     return MUON_EINVAL;
-  int rc = parse_cfg(cfg, &C, true);
+  NsCoefs C;
+  std::vector<GroupRun> runs;
+  size_t need = 0;
+  long long nparts = 0;
+  const int rc = prepare_step(groups, ngroups, cfg, &C, runs, &need, &nparts, false);
   if (rc != MUON_OK) return rc;
-  std::vector<GroupRun> runs(ngroups);
-  size_t off = 0;
-  for (int i = 0; i < ngroups; ++i) {
-    if (groups[i].grad_dtype != MUON_F32 && groups[i].grad_dtype != MUON_BF16) return MUON_EINVAL;
-    rc = plan_group(groups[i].m, groups[i].n, groups[i].count, cfg->precision == MUON_BF16, C, off, &runs[i].plan,
-                    groups[i].cap_u != nullptr);
-    if (rc != MUON_OK) return rc;
-    off = runs[i].plan.end;
-    runs[i].grad_dtype = groups[i].grad_dtype;
-    runs[i].W = groups[i].W;  // host arrays: which outputs exist decides the final passes
-    runs[i].O = groups[i].O;
-  }
-  const std::vector<int> marks = list_phases(runs, C, cfg->eps);
+  const std::vector<int> marks = list_phases(runs, C, cfg->eps, nparts);
   const int n = static_cast<int>(marks.size()) - 1;
   for (int i = 0; i < n && i < max_phases; ++i) phases[i] = marks[i + 1];
   return n;
@@ -900,42 +967,65 @@ int muon_step_timed(const muon_group* groups, int ngroups, const muon_ns_cfg* cf
 size_t muon_ns_workspace_size(int m, int n, int batch, int dtype, const muon_ns_cfg* cfg) {
   NsCoefs C;
   if (parse_cfg(cfg, &C, true) != MUON_OK || (dtype != MUON_F32 && dtype != MUON_BF16)) return 0;
-  GroupPlan g;
-  if (plan_group(m, n, batch, dtype == MUON_BF16, C, 0, &g) != MUON_OK) return 0;
-  return g.end == 0 ? kAlign : g.end;
+  if (batch < 0) return 0;
+  std::vector<GroupPlan> plans;
+  size_t need = 0;
+  long long nparts = 0;
+  if (plan_groups({GroupShape{m, n, batch, false}}, dtype == MUON_BF16, C, plans, &need, &nparts) != MUON_OK)
+    return 0;
+  return need;
 }
 
-int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int batch, const muon_ns_cfg* cfg,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int ld, int batch, long long stride,
+                          const muon_ns_cfg* cfg, void* workspace, size_t workspace_bytes, void* stream) {
   NsCoefs C;
   int rc = parse_cfg(cfg, &C, true);
   if (rc != MUON_OK) return rc;
   if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_EINVAL;
   if (cfg->precision != dtype) return MUON_EUNSUPPORTED;
-  if (m <= 0 || n <= 0 || batch < 0) return MUON_EINVAL;
-  if (batch == 0) return MUON_OK;
-  if (G == nullptr || O == nullptr || !aligned_to(G, dtype_size(dtype)) || !aligned_to(O, dtype_size(dtype)))
-    return MUON_EINVAL;
+  if (m <= 0 || n <= 0 || batch < 0 || ld < n) return MUON_EINVAL;
+  const long long span = static_cast<long long>(m - 1) * ld + n;  // elements of one matrix's rows
+  if (batch > 1 && stride < span) return MUON_EINVAL;
   std::vector<GroupRun> runs(1);
   GroupRun& R = runs[0];
-  rc = plan_group(m, n, batch, dtype == MUON_BF16, C, 0, &R.plan);
+  std::vector<GroupPlan> plans;
+  size_t need = 0;
+  long long nparts = 0;
+  rc = plan_groups({GroupShape{m, n, batch, false}}, dtype == MUON_BF16, C, plans, &need, &nparts);
   if (rc != MUON_OK) return rc;
-  const size_t mat = static_cast<size_t>(m) * n * dtype_size(dtype);
+  if (batch == 0) return MUON_OK;
+  const size_t es = dtype_size(dtype);
+  if (G == nullptr || O == nullptr || !aligned_to(G, es) || !aligned_to(O, es)) return MUON_EINVAL;
+  const size_t bytes = (static_cast<size_t>(batch - 1) * (batch > 1 ? stride : 0) + span) * es;
   const char* gb = static_cast<const char*>(G);
   char* ob = static_cast<char*>(O);
-  if (ob < gb + mat * batch && gb < ob + mat * batch) return MUON_EINVAL;  // overlap
-  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < R.plan.end) return MUON_EWORKSPACE;
+  // in place (O == G) is allowed: every element of G is read by the first pass, before any write of O
+  if (ob != gb && ob < gb + bytes && gb < ob + bytes) return MUON_EINVAL;
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return MUON_EWORKSPACE;
+  R.plan = plans[0];
   R.g_own.resize(batch);
   R.o_own.resize(batch);
   for (int b = 0; b < batch; ++b) {
-    R.g_own[b] = gb + mat * b;
-    R.o_own[b] = ob + mat * b;
+    R.g_own[b] = gb + static_cast<size_t>(b) * stride * es;
+    R.o_own[b] = ob + static_cast<size_t>(b) * stride * es;
   }
   R.grad_dtype = dtype;
   R.G = R.g_own.data();
   R.O = R.o_own.data();
+  R.ldg = ld;
+  R.ldo = ld;
   EventRec E;
-  return run_all(runs, C, cfg->eps, static_cast<char*>(workspace), nullptr, static_cast<hipStream_t>(stream), E);
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return run_all(runs, C, cfg->eps, ws, nullptr, st, E, nullptr, nparts);
+}
+
+int muon_query_flags(const void* workspace, int* nonfinite_out) {
+  if (workspace == nullptr || nonfinite_out == nullptr || !aligned16(workspace)) return MUON_EINVAL;
+  unsigned f = 0;
+  if (hipMemcpy(&f, workspace, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return MUON_EHIP;
+  *nonfinite_out = f != 0u ? 1 : 0;
+  return MUON_OK;
 }
 
 int muon_adamw(int ntensors, float* const* params, const void* const* grads, float* const* exp_avg,

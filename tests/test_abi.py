@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 6
+    assert mu.muon_version() == 7
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -147,9 +147,23 @@ def test_small_and_ns_validation(mu):
     assert L.muon_ns_batched_small(x, y, mu.MUON_BF16, 64, 128, 0, ctypes.byref(cfg), None) == 0    # empty
     cf32, k2 = _cfg(mu, steps=1, prec=mu.MUON_F32)
     assert L.muon_ns_batched_small(x, y, mu.MUON_BF16, 64, 128, 1, ctypes.byref(cf32), None) == -2  # precision
-    assert L.muon_ns_orthogonalize(x, x, mu.MUON_BF16, 64, 128, 2, ctypes.byref(cfg), y, 1 << 30, None) == -1
-    assert L.muon_ns_orthogonalize(x, y, mu.MUON_BF16, 64, 128, 2, ctypes.byref(cfg), None, 0, None) == -3
-    assert L.muon_ns_orthogonalize(x, y, mu.MUON_BF16, 64, 128, 0, ctypes.byref(cfg), None, 0, None) == 0
+    ws = ctypes.c_void_p(0x7000000)
+    x64 = ctypes.c_void_p(0x100000 + 64)
+    ns = L.muon_ns_orthogonalize
+    # partial overlap of G and O (in place, O == G, is allowed)
+    assert ns(x, x64, mu.MUON_BF16, 64, 128, 128, 2, 64 * 128, ctypes.byref(cfg), ws, 1 << 30, None) == -1
+    assert ns(x, y, mu.MUON_BF16, 64, 128, 127, 2, 64 * 128, ctypes.byref(cfg), ws, 1 << 30, None) == -1  # ld < n
+    assert ns(x, y, mu.MUON_BF16, 64, 128, 160, 2, 63 * 160 + 127, ctypes.byref(cfg), ws, 1 << 30,
+              None) == -1                                                                           # stride < span
+    assert ns(x, y, mu.MUON_BF16, 64, 128, 128, 2, 64 * 128, ctypes.byref(cfg), None, 0, None) == -3
+    assert ns(x, y, mu.MUON_BF16, 64, 128, 128, 0, 0, ctypes.byref(cfg), None, 0, None) == 0
+    assert ns(x, y, mu.MUON_BF16, 64, 128, 128, 2, 64 * 128, ctypes.byref(cf32), ws, 1 << 30, None) == -2
+    assert ns(None, y, mu.MUON_BF16, 64, 128, 128, 2, 64 * 128, ctypes.byref(cfg), ws, 1 << 30, None) == -1
+    # the flag query validates its pointers before any copy
+    out = ctypes.c_int(-1)
+    assert L.muon_query_flags(None, ctypes.byref(out)) == -1
+    assert L.muon_query_flags(ctypes.c_void_p(0x7000008), ctypes.byref(out)) == -1
+    assert L.muon_query_flags(ws, None) == -1 and out.value == -1
 
 
 def _phases(mu, shapes, steps, schedule, prec=None, separate_apply=0):
@@ -161,7 +175,12 @@ def _phases(mu, shapes, steps, schedule, prec=None, separate_apply=0):
     n = L.muon_step_phases(arr, len(gs), ctypes.byref(cfg), None, 0)
     out = (ctypes.c_int * max(n, 1))()
     assert L.muon_step_phases(arr, len(gs), ctypes.byref(cfg), out, n) == n
-    return [mu.binding.PHASES[out[i]] for i in range(n)]
+    names = [mu.binding.PHASES[out[i]] for i in range(n)]
+    # every call takes its non-finite flag once all momentum passes are done
+    assert names.count("flags") == 1
+    k = names.index("flags")
+    assert names[k - 1] == "momentum" and "momentum" not in names[k:]
+    return names[:k] + names[k + 1:]
 
 
 MAMBA = [(768, 1536, 24), (3352, 768, 24)]
@@ -259,7 +278,7 @@ def test_cap_validation_and_phases(mu):
     out = (ctypes.c_int * n)()
     L.muon_step_phases(arr, 1, ctypes.byref(cfg), out, n)
     names = [mu.binding.PHASES[out[i]] for i in range(n)]
-    assert names[-3:] == ["cap", "apply", "power"] and names[0] == "momentum"
+    assert names[-3:] == ["cap", "apply", "power"] and names[:2] == ["momentum", "flags"]
     # the cap's partial buffers enlarge the workspace
     base, _ = _group(mu, 128, 256, 2)
     a0 = (mu.binding.GroupC * 1)(base)

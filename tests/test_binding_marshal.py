@@ -74,3 +74,76 @@ def test_float32_gradients_are_marked():
     arr, _ = B._marshal_groups([g])
     assert arr[0].grad_dtype == B.MUON_F32
     assert isinstance(arr[0].W, ctypes.POINTER(ctypes.c_void_p))
+
+
+# ---------------------------------------------------------------------------
+# dtype and device checks: a wrong element type or a host tensor must never
+# reach the kernels as a device pointer of another type
+# ---------------------------------------------------------------------------
+CPU = torch.device("cpu")
+FAKE_GPU = torch.device("cuda", 0)
+
+
+@pytest.mark.parametrize("bad", ["W_bf16", "M_f64", "G_f16", "O_f32", "cap_u_bf16", "cap_sigma_f64",
+                                 "G_mixed_list", "O_bf16_for_f32"])
+def test_wrong_dtypes_are_rejected(bad):
+    g = group(cap=True, O=torch.zeros(3, 5, 7, dtype=torch.bfloat16))
+    prec = B.MUON_BF16
+    if bad == "W_bf16":
+        g.W = torch.zeros(3, 5, 7, dtype=torch.bfloat16)
+    elif bad == "M_f64":
+        g.M = torch.zeros(3, 5, 7, dtype=torch.float64)
+    elif bad == "G_f16":
+        g.G = torch.zeros(3, 5, 7, dtype=torch.float16)
+    elif bad == "O_f32":
+        g.O = torch.zeros(3, 5, 7)
+    elif bad == "cap_u_bf16":
+        g.cap_u = torch.zeros(3, 5, dtype=torch.bfloat16)
+    elif bad == "cap_sigma_f64":
+        g.cap_sigma = torch.zeros(3, dtype=torch.float64)
+    elif bad == "G_mixed_list":
+        g.G = [torch.zeros(5, 7, dtype=torch.bfloat16), torch.zeros(5, 7), torch.zeros(5, 7, dtype=torch.bfloat16)]
+    else:
+        prec = B.MUON_F32  # O must then be float32
+    with pytest.raises(TypeError):
+        B._marshal_groups([g], prec)
+
+
+@pytest.mark.parametrize("which", ["W", "M", "G", "O", "cap_u", "cap_v", "cap_sigma"])
+def test_tensors_off_the_device_are_rejected_for_launches(which):
+    """Calls that launch work pass the device the kernels run on: every
+    tensor of the group lives on it (the meta device stands in for the GPU
+    here) except one host tensor, which must be refused by name."""
+    meta = torch.device("meta")
+    g = group(cap=True, O=torch.zeros(3, 5, 7, dtype=torch.bfloat16))
+    for name in ("W", "M", "G", "O", "cap_u", "cap_v", "cap_sigma"):
+        if name != which:
+            setattr(g, name, getattr(g, name).to(meta))
+    with pytest.raises(ValueError, match=which):
+        B._marshal_groups([g], B.MUON_BF16, meta)
+    setattr(g, which, getattr(g, which).to(meta))
+    arr, _ = B._marshal_groups([g], B.MUON_BF16, meta)
+    assert arr[0].count == 3
+
+
+def test_queries_accept_host_tensors_without_a_device():
+    arr, _ = B._marshal_groups([group(cap=True)], B.MUON_BF16, None)
+    assert arr[0].count == 3
+
+
+def test_workspace_checks():
+    with pytest.raises(TypeError):
+        B._workspace(torch.zeros(16), 8, CPU)
+    with pytest.raises(ValueError):
+        B._workspace(torch.zeros(16, dtype=torch.uint8), 8, FAKE_GPU)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    assert B._workspace(ws, 8, CPU) is ws
+
+
+def test_strided_stack_layout():
+    base = torch.zeros(4, 6, 10)
+    b, m, n, ld, stride = B._strided_stack(base[:, :, :8])[1:]
+    assert (b, m, n, ld, stride) == (4, 6, 8, 10, 60)
+    with pytest.raises(ValueError):
+        B._strided_stack(base.transpose(1, 2))
+    assert B._strided_stack(torch.zeros(6, 8))[1:] == (1, 6, 8, 8, 48)

@@ -236,22 +236,25 @@ def test_diag_split_run_agrees_with_one_workgroup_per_matrix(mu):
 
 def test_diag_split_run_bounded_waits_give_up_cleanly(mu, monkeypatch):
     """The split run's waits on other workgroups are bounded.  With the bound
-    cut to nothing (MUON_DIAG_SPIN_LIMIT, a test hook read at each launch)
-    workgroups give up on words that are not there yet: the call still ends,
-    a matrix whose run gave up reports NaN and any other matches the oracle,
-    and the next call on the same workspace is exact again."""
+    cut to nothing (MUON_DEBUG_DIAG_SPIN_LIMIT, a debug hook read at each
+    launch) workgroups give up on words that are not there yet: the call
+    still ends, a matrix whose run gave up reports NaN and any other matches
+    the oracle, and the next call on the same workspace is exact again.  Only
+    the split run waits on other workgroups, so at least one NaN shows that
+    the split plan was taken and its give-up path ran."""
     A, exact = to_device(stack(5, 6, 384, 704, "spread"), "bf16")
     ws = torch.zeros(mu.lib().muon_spectral_diag_workspace_size(384, 704, 6, mu.MUON_BF16, 24),
                      dtype=torch.uint8, device="cuda")
-    monkeypatch.setenv("MUON_DIAG_SPIN_LIMIT", "0")
+    monkeypatch.setenv("MUON_DEBUG_DIAG_SPIN_LIMIT", "0")
     out = mu.muon_spectral_diag(A, iters=24, workspace=ws)
     torch.cuda.synchronize()
     o = {k: v.cpu().numpy() for k, v in out.items()}
     gave_up = [b for b in range(6) if not (np.isfinite(o["sigma_max"][b]) and np.isfinite(o["sigma_min"][b]))]
     print("matrices whose run gave up:", gave_up)
+    assert len(gave_up) >= 1
     done = [b for b in range(6) if b not in gave_up]
     check({k: v[done] for k, v in o.items()}, exact, 24, done)
-    monkeypatch.delenv("MUON_DIAG_SPIN_LIMIT")
+    monkeypatch.delenv("MUON_DEBUG_DIAG_SPIN_LIMIT")
     again = mu.muon_spectral_diag(A, iters=24, workspace=ws)
     torch.cuda.synchronize()
     check({k: v.cpu().numpy() for k, v in again.items()}, exact, 24, range(6))
