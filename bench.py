@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Muon NS steps/s + TFLOP/s, MFMA util (Mamba-2-130M-shaped grads), 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak (published)
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -138,16 +139,33 @@ def ns_flops(s, l):
     return s * (s + 1) * l, 2 * s * s * l
 
 
+def workload_for(args, wl):
+    """The seeded inputs of a step workload: the full step (both projection
+    groups, the headline), one projection group, or the single fp32 matrix."""
+    if args.workload == "out_proj":
+        return wl.config2(), "mamba2-130m out_proj group: 24x 768x1536, bf16 grads (singular values log-uniform in " \
+                             "[1e-3, 1]), fp32 W/M"
+    if args.workload == "in_proj":
+        return wl.config3(), "mamba2-130m in_proj group: 24x 3352x768 (tall), bf16 Gaussian grads with a rank-8 " \
+                             "spike 10x the bulk, fp32 W/M"
+    if args.workload == "single":
+        return wl.config1(), "single fp32 gradient 128x64 (fp32 path), W N(0,0.02), M = 0"
+    return wl.config4(count=args.count, steps=args.ns_steps), \
+        f"mamba2-130m-full-step: {args.count}x out_proj 768x1536 + {args.count}x in_proj 3352x768, bf16 grads, fp32 W/M"
+
+
 def bench_full_step(args, torch, mu, wl):
     steps_ns = args.ns_steps
-    log(f"[bench] generating full-step inputs ({args.count}+{args.count} matrices)")
+    log(f"[bench] generating {args.workload} inputs")
     t0 = time.time()
-    w = wl.config4(count=args.count, steps=steps_ns)
+    w, desc = workload_for(args, wl)
     log(f"[bench] generated in {time.time() - t0:.1f}s")
+    fp32 = w.groups[0].grad_dtype != "bf16"
+    prec = mu.MUON_F32 if fp32 else mu.MUON_BF16
     groups, devs = [], []
     gen = torch.Generator(device="cuda").manual_seed(5)
     for g in w.groups:
-        G = torch.from_numpy(g.G.view(np.int16)).view(torch.bfloat16).cuda()
+        G = (torch.from_numpy(g.G) if fp32 else torch.from_numpy(g.G.view(np.int16)).view(torch.bfloat16)).cuda()
         W = torch.from_numpy(g.W).cuda()
         M = torch.from_numpy(g.M).cuda()
         devs.append((G, W, M))
@@ -160,13 +178,15 @@ def bench_full_step(args, torch, mu, wl):
         groups.append(mu.MuonGroup(W=W, M=M, G=G, lr=w.lr, beta=w.beta, nesterov=w.nesterov, **cap))
     streams = 1 if args.one_stream else 0
     sched = {"auto": mu.MUON_NS_AUTO, "iterate": mu.MUON_NS_ITERATE, "accumulate": mu.MUON_NS_ACCUMULATE}[args.schedule]
-    opts = dict(steps=steps_ns, streams=streams, schedule=sched, separate_apply=int(args.separate_apply))
+    opts = dict(steps=steps_ns, streams=streams, schedule=sched, separate_apply=int(args.separate_apply),
+                precision=prec)
     if args.per_matrix:  # one muon_step call per matrix (the ungrouped launch pattern)
         return bench_per_matrix(args, torch, mu, w, groups, opts)
     ws = mu.muon_step(groups, **opts)  # allocates the workspace once
     torch.cuda.synchronize()
     # the library lists the phases muon_step_timed brackets with events
-    phases = mu.muon_step_phases(groups, steps=steps_ns, schedule=sched, separate_apply=int(args.separate_apply))
+    phases = mu.muon_step_phases(groups, steps=steps_ns, schedule=sched, separate_apply=int(args.separate_apply),
+                                 precision=prec)
     n_ev = len(phases) + 1
     log(f"[bench] schedule: {' '.join(phases)}")
 
@@ -200,13 +220,14 @@ def bench_full_step(args, torch, mu, wl):
     t2 = time.perf_counter()
     for k in range(args.steps):
         mu.muon_step(groups, steps=steps_ns, workspace=ws, events=[e.cuda_event for e in evs[k]], schedule=sched,
-                     separate_apply=int(args.separate_apply))
+                     separate_apply=int(args.separate_apply), precision=prec)
     torch.cuda.synchronize()
     ms_serial = (time.perf_counter() - t2) * 1e3 / args.steps
 
     # algorithmic work of each launch of the executed schedule (every large
     # group takes the same schedule here; per-group passes follow group order)
     per_group = [(g, min(g.m, g.n), max(g.m, g.n)) for g in w.groups]
+    gsz, xsz = (4, 4) if fp32 else (2, 2)  # bytes of a gradient / iterate element
     gram_f = sum(g.count * ns_flops(s, l)[0] for g, s, l in per_group)
     comb_f = sum(g.count * ns_flops(s, l)[1] for g, s, l in per_group)
     sym_f = sum(g.count * s * s * (s + 1) for g, s, l in per_group)  # one symmetric s x s product
@@ -218,15 +239,15 @@ def bench_full_step(args, torch, mu, wl):
                 sym_products.append(1)
     assert len(sym_products) == phases.count("symprod")
     work = []
-    gi_m = gi_a = si = 0
+    gi_m = gi_a = si = gi_n = 0
     for ph in phases:
-        if ph == "momentum":
+        if ph == "momentum":  # G in, M in and out, the iterate out
             g, s, l = per_group[gi_m]
-            work.append(g.count * g.m * g.n * 12)
+            work.append(g.count * g.m * g.n * (gsz + 8 + xsz))
             gi_m += 1
-        elif ph == "apply":
+        elif ph == "apply":  # the iterate in, W in and out
             g, s, l = per_group[gi_a]
-            work.append(g.count * g.m * g.n * 10)
+            work.append(g.count * g.m * g.n * (xsz + 8))
             gi_a += 1
         elif ph == "gram":
             work.append(gram_f)
@@ -237,6 +258,10 @@ def bench_full_step(args, torch, mu, wl):
             si += 1
         elif ph == "flags":  # the non-finite flag: one small read of the partial sums
             work.append(0)
+        elif ph == "ns_small":  # the whole iteration on chip: per step a Gram and a combine
+            g, s, l = per_group[gi_n]
+            work.append(g.count * sum(ns_flops(s, l)) * steps_ns)
+            gi_n += 1
         elif ph in ("cap", "power"):  # bytes: read X (2 B/elt) / read W (4 B/elt); power follows apply
             g, s, l = per_group[gi_a if ph == "cap" else gi_a - 1]
             work.append(g.count * g.m * g.n * (2 if ph == "cap" else 4))
@@ -260,15 +285,16 @@ def bench_full_step(args, torch, mu, wl):
             kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "bytes_per_launch": tot_w / n,
                              "gbs": rate / 1e9, "frac": rate / 1e9 / PEAK_HBM_GBS}
         else:
+            peak = PEAK_F32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
             kernels[kind] = {"avg_us": tot_ms / n * 1e3, "launches": n, "flops_per_launch": tot_w / n,
-                             "tflops": rate / 1e12, "frac": rate / 1e12 / PEAK_BF16_TFLOPS}
+                             "tflops": rate / 1e12, "frac": rate / 1e12 / peak}
         kernels[kind]["ms_per_step"] = tot_ms / args.steps
     if "combine_apply" in kernels:  # the fused apply's bytes: X read, W read and written
         nel = sum(g.count * g.m * g.n for g, s, l in per_group)
         ca = kernels["combine_apply"]
         ca["apply_bytes_per_launch"] = nel * 10
         ca["apply_gbs"] = nel * 10 / (ca["avg_us"] * 1e-6) / 1e9
-    ns_kinds = [k for k in ("gram", "symprod", "combine", "combine_apply") if k in dur]
+    ns_kinds = [k for k in ("gram", "symprod", "combine", "combine_apply", "ns_small") if k in dur]
     ns_ms = sum(sum(d for d, _ in dur[k]) for k in ns_kinds) / args.steps
     ns_flops_step = sum(sum(wk for _, wk in dur[k]) for k in ns_kinds) / args.steps
     ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
@@ -280,14 +306,21 @@ def bench_full_step(args, torch, mu, wl):
     kd = kernels[dom]
     names = {"gram": "symprod_bf16_kernel", "combine": "combine_bf16_kernel", "symprod": "symprod_bf16_kernel",
              "combine_apply": "combine_bf16_kernel<fused apply>", "momentum": "momentum_*_kernel",
-             "apply": "apply_*_kernel"}
+             "apply": "apply_*_kernel", "ns_small": "ns_small_f32_kernel" if fp32 else "ns_small_bf16_kernel"}
     if dom in ("momentum", "apply"):
         roofline = {"bound": "hbm", "kernel": names[dom], "achieved": round(kd["gbs"], 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(kd["frac"], 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(kd["frac"], 4),
+                    "traffic": measured_traffic(names[dom].replace("*", "wide" if dom == "momentum" else "tall"),
+                                                args.workload, ELEMENTWISE)}
+    elif fp32:
+        # float32 iteration on the vector ALUs (no matrix cores): fp32 vector peak
+        tf = kd["tflops"]
+        roofline = {"bound": "alu", "kernel": names[dom], "achieved": round(tf, 4), "peak": PEAK_F32_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / PEAK_F32_TFLOPS, 6), "traffic": None}
     else:
         roofline = {"bound": "mfma", "kernel": names[dom], "achieved": round(kd["tflops"], 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(kd["frac"], 4),
-                    "traffic": measured_traffic(names[dom], "full_step", GEMM)}
+                    "traffic": measured_traffic(names[dom], args.workload, GEMM)}
     result = {
         "metric": METRIC, "value": round(1e3 / ms_per_step, 3), "unit": "steps/s",
         "ms_per_step": round(ms_per_step, 4),
@@ -296,11 +329,9 @@ def bench_full_step(args, torch, mu, wl):
         "ns_iters_per_s": round(steps_ns * 1e3 / ms_per_step, 2),
         "ns_tflops": round(ns_tflops, 2), "mfma_util": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
         "ns_iteration_equivalent_tflops": round(iter_flops_step / (ns_ms * 1e-3) / 1e12, 2),
-        "dtype": "bf16",
-        "config": {"workload": f"mamba2-130m-full-step: {args.count}x out_proj 768x1536 + "
-                               f"{args.count}x in_proj 3352x768, bf16 grads, fp32 W/M, "
-                               f"{steps_ns} cubic NS steps",
-                   "matrices": 2 * args.count, "ns_steps": steps_ns, "parallelism": "none (1 GPU)",
+        "dtype": "f32" if fp32 else "bf16",
+        "config": {"workload": f"{desc}, {steps_ns} cubic NS steps",
+                   "matrices": sum(g.count for g in w.groups), "ns_steps": steps_ns, "parallelism": "none (1 GPU)",
                    "spectral_cap": bool(args.cap), "ns_schedule": args.schedule,
                    "separate_apply": bool(args.separate_apply), "chains": 1 if args.one_stream else "auto",
                    "schedule": " ".join(phases)},
@@ -309,7 +340,7 @@ def bench_full_step(args, torch, mu, wl):
                     for k, v in kernels.items()},
     }
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline_full_step(w, steps_ns)
+        result["cpu_baseline"] = cpu_baseline_step(w, steps_ns, one_core=args.workload in ("single", "out_proj"))
     return result
 
 
@@ -403,34 +434,83 @@ def bench_sweep(args, torch, mu, wl):
             "sweep": rows}
 
 
-def cpu_baseline_full_step(w, steps_ns, budget_s=15.0):
-    """The fp64 oracle as it stands on a bounded sample: matrices alternately
-    from each group until ~budget_s of CPU work, scaled to one full step."""
-    import oracle as orc
+def host_cores():
+    """CPU cores this process may run on (the box's share, not the machine's)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count()
-    times = {0: [], 1: []}
+        return host_cores()
+
+
+def _oracle_step_time(w, steps_ns, budget_s):
+    """Mean oracle time per matrix of each group over a bounded sample
+    (matrices taken alternately from each group until budget_s of CPU work,
+    at least one per group)."""
+    import oracle as orc
+    times = {gi: [] for gi in range(len(w.groups))}
     t_start = time.perf_counter()
     i = 0
-    while time.perf_counter() - t_start < budget_s or not (times[0] and times[1]):
-        gi = i % 2
+    while True:
+        gi = i % len(w.groups)
         g = w.groups[gi]
-        j = (i // 2) % g.count
+        j = (i // len(w.groups)) % g.count
+        G = orc.widen_bf16(g.G[j]) if g.grad_dtype == "bf16" else orc.widen_f32(g.G[j])
         t0 = time.perf_counter()
-        orc.muon_step(orc.widen_f32(g.W[j]), orc.widen_f32(g.M[j]), orc.widen_bf16(g.G[j]), beta=w.beta,
-                      lr=w.lr, nesterov=w.nesterov, steps=steps_ns, eps=w.eps)
+        orc.muon_step(orc.widen_f32(g.W[j]), orc.widen_f32(g.M[j]), G, beta=w.beta, lr=w.lr, nesterov=w.nesterov,
+                      steps=steps_ns, eps=w.eps)
         times[gi].append(time.perf_counter() - t0)
         i += 1
-        if i >= 2 * min(g.count for g in w.groups):
+        done = all(times.values()) and time.perf_counter() - t_start >= budget_s
+        if done or i >= max(4 * sum(g.count for g in w.groups), 256):
             break
-    t_step = sum(np.mean(times[gi]) * w.groups[gi].count for gi in (0, 1))
-    return {"value": round(1.0 / t_step, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times[0])} out_proj + {len(times[1])} in_proj matrices of the full step "
-                      f"(fp64 numpy, {steps_ns} NS steps), mean per-matrix time scaled to "
-                      f"{w.groups[0].count}+{w.groups[1].count} matrices"}
+    t_step = sum(np.mean(times[gi]) * w.groups[gi].count for gi in times)
+    return t_step, {gi: len(v) for gi, v in times.items()}
+
+
+def cpu_baseline_step(w, steps_ns, budget_s=15.0, one_core=False):
+    """The fp64 oracle as it stands on a bounded sample of the workload's
+    matrices, scaled to one whole step, on every host core this process may
+    use (BLAS threads); with one_core, also on one thread."""
+    t_step, n = _oracle_step_time(w, steps_ns, budget_s)
+    sample = " + ".join(f"{n[gi]} oracle runs over the {g.count} {g.name} matrices" for gi, g in enumerate(w.groups))
+    out = {"value": round(1.0 / t_step, 5), "unit": "steps/s", "cores": int(blas_threads()), "kind": "oracle",
+           "sample": f"{sample} (fp64 numpy, {steps_ns} NS steps), mean per-matrix time scaled to the whole step",
+           "host_cores": host_cores()}
+    if one_core:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(1):
+                t1, n1 = _oracle_step_time(w, steps_ns, budget_s / 3)
+            out["one_core"] = {"value": round(1.0 / t1, 5), "unit": "steps/s", "cores": 1,
+                               "sample": " + ".join(f"{n1[gi]} oracle runs" for gi in n1)}
+        except ImportError:
+            pass
+    return out
+
+
+def cpu_baseline_injections(X, steps_ns, budget_s=15.0):
+    """The oracle's batched NS on a contiguous slice of the injections (chunks
+    of 512 matrices from the start until budget_s), extrapolated linearly to
+    the whole batch: the matrices are independent."""
+    import oracle as orc
+    done, t = 0, 0.0
+    while t < budget_s and done < X.shape[0]:
+        chunk = X[done:done + 512].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        orc.ns_batched(chunk, steps_ns)
+        t += time.perf_counter() - t0
+        done += chunk.shape[0]
+    how = "all" if done >= X.shape[0] else f"the first {done} of {X.shape[0]}, rate extrapolated to all"
+    return {"value": round(done / t, 1), "unit": "matrices/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{how} matrices (fp64 numpy, {steps_ns} NS step, chunks of 512)", "host_cores": host_cores()}
 
 
 # ----------------------------------------------------------------------------
@@ -454,7 +534,8 @@ def bench_injections(args, torch, mu, wl):
     kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nbytes = X.numel() * 2 * 2
     gbs = nbytes / (kms * 1e-3) / 1e9
-    return {"metric": "MuonSSM batched single-step NS matrices/s", "value": round(args.batch / (ms * 1e-3), 1),
+    extra = {} if args.no_cpu else {"cpu_baseline": cpu_baseline_injections(X, args.ns_steps)}
+    return {**extra, "metric": "MuonSSM batched single-step NS matrices/s", "value": round(args.batch / (ms * 1e-3), 1),
             "unit": "matrices/s", "ms_per_step": round(ms, 4), "dtype": "bf16",
             "config": {"workload": f"injections {args.batch}x64x128 bf16, {args.ns_steps} NS step"},
             "roofline": {"bound": "hbm", "kernel": "ns_small_bf16_kernel<64,128>", "achieved": round(gbs, 1),
@@ -617,28 +698,6 @@ def bench_diag(args, torch, mu, wl):
             "roofline": roofline, "kernels": kernels}
 
 
-def bench_group(args, torch, mu, wl, which):
-    w = wl.config2() if which == "out_proj" else wl.config3() if which == "in_proj" else wl.config1()
-    groups = []
-    for g in w.groups:
-        G = (torch.from_numpy(g.G.view(np.int16)).view(torch.bfloat16) if g.grad_dtype == "bf16"
-             else torch.from_numpy(g.G)).cuda()
-        groups.append(mu.MuonGroup(W=torch.from_numpy(g.W).cuda(), M=torch.from_numpy(g.M).cuda(), G=G,
-                                   lr=w.lr, beta=w.beta))
-    prec = mu.MUON_BF16 if w.groups[0].grad_dtype == "bf16" else mu.MUON_F32
-    ws = mu.muon_step(groups, steps=args.ns_steps, precision=prec)
-    for _ in range(args.warmup):
-        mu.muon_step(groups, steps=args.ns_steps, precision=prec, workspace=ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        mu.muon_step(groups, steps=args.ns_steps, precision=prec, workspace=ws)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    return {"metric": METRIC, "value": round(1e3 / ms, 3), "unit": "steps/s", "ms_per_step": round(ms, 4),
-            "dtype": "bf16" if prec == mu.MUON_BF16 else "f32", "config": {"workload": w.name}}
-
-
 ELEMENTWISE = ["elementwise.hip", "common.cuh"]
 GEMM = ["gemm_bf16.hip", "common.cuh"]
 COUNTED_KERNELS = {
@@ -703,7 +762,7 @@ def main():
     mu.lib()
     if args.copy_calibration:
         copy_calibration(torch)
-    if args.workload == "full_step":
+    if args.workload in ("full_step", "out_proj", "in_proj", "single"):
         res = bench_full_step(args, torch, mu, wl)
     elif args.workload == "injections":
         res = bench_injections(args, torch, mu, wl)
@@ -715,8 +774,6 @@ def main():
         res = bench_diag(args, torch, mu, wl)
     elif args.workload == "sweep":
         res = bench_sweep(args, torch, mu, wl)
-    else:
-        res = bench_group(args, torch, mu, wl, args.workload)
     out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": res.pop("dtype"),

@@ -14,32 +14,52 @@
 
 namespace muon {
 
+// 16-byte vector loads and stores; NT marks data touched once in the step
+// (read once, or written and not read again by this step) as non-temporal.
+// A contiguous momentum-shaped stream reached 6.1 TB/s with it against 5.3
+// plain, but the momentum passes themselves measured slower with it (their
+// 32-byte-per-lane M accesses), so only the apply passes use it.
+template <bool NT, typename V>
+__device__ __forceinline__ V ld16(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void st16(void* p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  else *reinterpret_cast<V*>(p) = v;
+}
+
 template <typename T> struct Vec8;
 template <> struct Vec8<float> {
+  template <bool NT = false>
   __device__ static void load(const float* p, float* v) {
-    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+    const f32x4_t a = ld16<NT, f32x4_t>(p);
+    const f32x4_t b = ld16<NT, f32x4_t>(p + 4);
     v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
     v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
   }
+  template <bool NT = false>
   __device__ static void store(float* p, const float* v) {
     f32x4_t a = {v[0], v[1], v[2], v[3]};
     f32x4_t b = {v[4], v[5], v[6], v[7]};
-    *reinterpret_cast<f32x4_t*>(p) = a;
-    *reinterpret_cast<f32x4_t*>(p + 4) = b;
+    st16<NT>(p, a);
+    st16<NT>(p + 4, b);
   }
 };
 template <> struct Vec8<bf16_t> {
+  template <bool NT = false>
   __device__ static void load(const bf16_t* p, float* v) {
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t a = ld16<NT, u32x4_t>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { v[2 * i] = lo_bf16(a[i]); v[2 * i + 1] = hi_bf16(a[i]); }
   }
+  template <bool NT = false>
   __device__ static void store(bf16_t* p, const float* v) {
     u32x4_t a;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4_t*>(p) = a;
+    st16<NT>(p, a);
   }
 };
 
@@ -234,7 +254,7 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
     const long long ooff = static_cast<long long>(r) * ldo + c0;
     if (vec) {
       float ov[8], wv[8];
-      Vec8<XT>::load(x + static_cast<long long>(r) * ld + c0, ov);
+      Vec8<XT>::template load<true>(x + static_cast<long long>(r) * ld + c0, ov);
 #pragma unroll
       for (int j = 0; j < 8; ++j) ov[j] *= inv;
       if (gamma != 0.0f) {
@@ -242,12 +262,12 @@ __global__ void __launch_bounds__(256) apply_wide_kernel(const XT* X, long long 
 #pragma unroll
         for (int j = 0; j < 8; ++j) ov[j] = fmaf(-gu, cv[c0 + j], ov[j]);
       }
-      if (o) Vec8<XT>::store(o + ooff, ov);
+      if (o) Vec8<XT>::template store<true>(o + ooff, ov);
       if (w) {
-        Vec8<float>::load(w + off, wv);
+        Vec8<float>::template load<true>(w + off, wv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) wv[j] = fmaf(a.neg_lr_scale, ov[j], wv[j]);
-        Vec8<float>::store(w + off, wv);
+        Vec8<float>::template store<true>(w + off, wv);
       }
     } else {
       for (int j = 0; j < 8 && c0 + j < n; ++j) {
@@ -285,7 +305,7 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
     const int kc = (t % 8) * 8;
     float v[8];
     if (i0 + ir < n && k0 + kc + 7 < ld) {
-      Vec8<XT>::load(x + static_cast<long long>(i0 + ir) * ld + k0 + kc, v);
+      Vec8<XT>::template load<true>(x + static_cast<long long>(i0 + ir) * ld + k0 + kc, v);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0.0f;
@@ -312,12 +332,12 @@ __global__ void __launch_bounds__(256) apply_tall_kernel(const XT* X, long long 
 #pragma unroll
         for (int j = 0; j < 8; ++j) ov[j] = fmaf(-gu, cv[uc + j], ov[j]);
       }
-      if (o) Vec8<XT>::store(o + ooff, ov);
+      if (o) Vec8<XT>::template store<true>(o + ooff, ov);
       if (w) {
-        Vec8<float>::load(w + off, wv);
+        Vec8<float>::template load<true>(w + off, wv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) wv[j] = fmaf(a.neg_lr_scale, ov[j], wv[j]);
-        Vec8<float>::store(w + off, wv);
+        Vec8<float>::template store<true>(w + off, wv);
       }
     } else {
       for (int j = 0; j < 8 && uc + j < n; ++j) {

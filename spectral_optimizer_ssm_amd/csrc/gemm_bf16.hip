@@ -452,10 +452,10 @@ __device__ __forceinline__ void slabs32_out(const BufsN<3>& bufs, int j0, bf16_t
       for (int u = 0; u < PER; ++u) {  // every W load of this thread before its first store
         const int q = tid + C2_NTHR * u, r = q >> 5, c = q & 31;
         v[p][u] = *reinterpret_cast<const u32x4_t*>(bufs[p] + r * 512 + ((c ^ (r & 31)) << 4));
-        if (full && W != nullptr) {
+        if (full && W != nullptr) {  // W is read once and written once: non-temporal
           const long long off = static_cast<long long>(i0 + (j0 + p) * 32 + r) * n + k0 + c * 8;
-          w[p][u][0] = *reinterpret_cast<const f32x4_t*>(W + off);
-          w[p][u][1] = *reinterpret_cast<const f32x4_t*>(W + off + 4);
+          w[p][u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(W + off));
+          w[p][u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(W + off + 4));
         }
       }
 #pragma unroll
@@ -467,7 +467,7 @@ __device__ __forceinline__ void slabs32_out(const BufsN<3>& bufs, int j0, bf16_t
         const long long off = static_cast<long long>(i) * n + k;
         const u32x4_t vv = v[p][u];
         if (full) {
-          if (O != nullptr) *reinterpret_cast<u32x4_t*>(O + off) = vv;
+          if (O != nullptr) __builtin_nontemporal_store(vv, reinterpret_cast<u32x4_t*>(O + off));
           if (W != nullptr) {
             f32x4_t w0 = w[p][u][0], w1 = w[p][u][1];
 #pragma unroll
@@ -477,8 +477,8 @@ __device__ __forceinline__ void slabs32_out(const BufsN<3>& bufs, int j0, bf16_t
               w1[2 * h] = fmaf(nls, lo_bf16(vv[2 + h]), w1[2 * h]);
               w1[2 * h + 1] = fmaf(nls, hi_bf16(vv[2 + h]), w1[2 * h + 1]);
             }
-            *reinterpret_cast<f32x4_t*>(W + off) = w0;
-            *reinterpret_cast<f32x4_t*>(W + off + 4) = w1;
+            __builtin_nontemporal_store(w0, reinterpret_cast<f32x4_t*>(W + off));
+            __builtin_nontemporal_store(w1, reinterpret_cast<f32x4_t*>(W + off + 4));
           }
         } else if (i < s) {  // edge tiles: element by element within the matrix
           for (int e = 0; e < 8 && k + e < l; ++e) {
@@ -580,7 +580,8 @@ combine_bf16_kernel(GemmArgs G) {
             for (int q = 0; q < 4; ++q)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                wv[j][4 * q + r] = wcol[static_cast<long long>(tk * C2_TK + wm * CM + i * 32 + q * 8 + rq + r) * S.n];
+                wv[j][4 * q + r] = __builtin_nontemporal_load(
+                    &wcol[static_cast<long long>(tk * C2_TK + wm * CM + i * 32 + q * 8 + rq + r) * S.n]);
           }
         }
 #pragma unroll
@@ -594,8 +595,8 @@ combine_bf16_kernel(GemmArgs G) {
               const bf16_t ob = f32_to_bf16(acc.c[i][j][4 * q + r]);
               const long long off = static_cast<long long>(gk) * S.n + gi;
               if (full) {
-                if (Oz != nullptr) Oz[off] = ob;
-                if (Wz != nullptr) Wz[off] = fmaf(nls, bf16_to_f32(ob), wv[j][4 * q + r]);
+                if (Oz != nullptr) __builtin_nontemporal_store(ob, &Oz[off]);
+                if (Wz != nullptr) __builtin_nontemporal_store(fmaf(nls, bf16_to_f32(ob), wv[j][4 * q + r]), &Wz[off]);
               } else if (gi < S.s && gk < S.l) {
                 if (Oz != nullptr) Oz[off] = ob;
                 if (Wz != nullptr) Wz[off] = fmaf(nls, bf16_to_f32(ob), Wz[off]);

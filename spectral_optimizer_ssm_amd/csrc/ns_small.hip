@@ -241,20 +241,58 @@ __global__ void __launch_bounds__(256) ns_small_f32_kernel(NsSmallLaunch P) {
     __syncthreads();
     float (*cur)[LMAX + 1] = xa;
     float (*nxt)[LMAX + 1] = xb;
+    // register blocks: thread (ti, tj) of a 16 x 16 grid owns rows 4 ti .. 4 ti + 3
+    // and, in the Gram, columns 4 tj .. 4 tj + 3, in the combine, columns
+    // tj + 16 c (c < LMAX / 16); independent accumulators, every LDS value
+    // read once per k is used four or more times
+    constexpr int CPT = LMAX / 16;
+    const int ti = tid >> 4, tj = tid & 15;
+    const int i0 = 4 * ti, j0 = 4 * tj;
     for (int step = 0; step < P.steps; ++step) {
-      for (int e = tid; e < S * S; e += 256) {
-        const int i = e / S, j = e % S;
-        float acc = 0.0f;
-        for (int k = 0; k < Lw; ++k) acc = fmaf(cur[i][k], cur[j][k], acc);
-        am[i][j] = acc;
+      if (i0 < S && j0 < S) {
+        float g[4][4] = {};
+#pragma unroll 8
+        for (int k = 0; k < Lw; ++k) {
+          float xi[4], xj[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            xi[r] = i0 + r < S ? cur[i0 + r][k] : 0.0f;
+            xj[r] = j0 + r < S ? cur[j0 + r][k] : 0.0f;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) g[r][c] = fmaf(xi[r], xj[c], g[r][c]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (i0 + r < S && j0 + c < S) am[i0 + r][j0 + c] = g[r][c];
       }
       __syncthreads();
       const float a = P.a[step], b = P.b[step];
-      for (int e = tid; e < S * Lw; e += 256) {
-        const int i = e / Lw, k = e % Lw;
-        float acc = 0.0f;
-        for (int j = 0; j < S; ++j) acc = fmaf(am[i][j], cur[j][k], acc);
-        nxt[i][k] = fmaf(a, cur[i][k], b * acc);
+      if (i0 < S) {
+        float y[4][CPT] = {};
+#pragma unroll 4
+        for (int j = 0; j < S; ++j) {
+          float ar[4], xr[CPT];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ar[r] = i0 + r < S ? am[i0 + r][j] : 0.0f;
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) xr[c] = tj + 16 * c < Lw ? cur[j][tj + 16 * c] : 0.0f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) y[r][c] = fmaf(ar[r], xr[c], y[r][c]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) {
+            const int i = i0 + r, k = tj + 16 * c;
+            if (i < S && k < Lw) nxt[i][k] = fmaf(a, cur[i][k], b * y[r][c]);
+          }
       }
       __syncthreads();
       float (*t)[LMAX + 1] = cur;
