@@ -235,6 +235,23 @@ int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int l
                           long long stride, const muon_ns_cfg* cfg, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * muon_ns_orthogonalize without a workspace argument.  Its workspace is a
+ * library-owned device array of muon_ns_noalloc_max_bytes() bytes (32 MiB),
+ * one per GPU, part of the loaded library and held until the process ends;
+ * the call allocates nothing (no hipMalloc or hipFree; the array's device
+ * address is looked up once per device).  Arguments, results and errors as in
+ * muon_ns_orthogonalize, plus MUON_EWORKSPACE when muon_ns_workspace_size for
+ * these arguments exceeds the array.  Nothing in the array needs to start at
+ * zero; the last call's contents stay in it (its non-finite flag among them,
+ * which muon_query_flags cannot reach).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (concurrent streams,
+ * other threads) race and must be ordered by the caller. */
+size_t muon_ns_noalloc_max_bytes(void);
+int muon_ns_orthogonalize_noalloc(const void* G, void* O, int dtype, int m, int n, int ld, int batch,
+                                  long long stride, const muon_ns_cfg* cfg, void* stream);
+
 /* The non-finite flag of the last muon_step or muon_ns_orthogonalize call that
  * used this workspace ("Muon Meets Mamba" practitioner article, long-term
  * engineering and the training checkpoints: stop and alert on abnormal

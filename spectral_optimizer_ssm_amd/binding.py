@@ -49,7 +49,8 @@ class GroupC(ctypes.Structure):
 
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
-           "muon_ns_orthogonalize", "muon_query_flags", "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
+           "muon_ns_orthogonalize", "muon_ns_noalloc_max_bytes", "muon_ns_orthogonalize_noalloc", "muon_query_flags",
+           "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
            "muon_spectral_diag_workspace_size", "muon_spectral_diag", "muon_spectral_diag_timed",
            "muon_status_string", "muon_version")
 
@@ -78,6 +79,10 @@ def lib():
     L.muon_ns_workspace_size.restype = sz
     L.muon_ns_orthogonalize.argtypes = [vp, vp, i, i, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg), vp, sz, vp]
     L.muon_ns_orthogonalize.restype = i
+    L.muon_ns_noalloc_max_bytes.argtypes = []
+    L.muon_ns_noalloc_max_bytes.restype = sz
+    L.muon_ns_orthogonalize_noalloc.argtypes = [vp, vp, i, i, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg), vp]
+    L.muon_ns_orthogonalize_noalloc.restype = i
     L.muon_query_flags.argtypes = [vp, ctypes.POINTER(i)]
     L.muon_query_flags.restype = i
     L.muon_ns_batched_small.argtypes = [vp, vp, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg), vp]
@@ -390,6 +395,26 @@ def muon_ns_orthogonalize(G, O, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=
                                  _stream_handle(stream))
     _check(rc, "muon_ns_orthogonalize")
     return workspace
+
+
+def muon_ns_orthogonalize_noalloc(G, O, steps=5, coeffs=(1.5, -0.5), eps=1e-7, per_step=False, stream=None,
+                                  schedule=MUON_NS_AUTO):
+    """muon_ns_orthogonalize on the library's own device array instead of a
+    workspace (nothing is allocated; at most muon_ns_noalloc_max_bytes() of
+    workspace need; calls that overlap on one GPU race)."""
+    import torch
+    L = lib()
+    dev = _current_device()
+    G3, b, m, n, ld, stride = _strided_stack(G)
+    O3, bo, mo, no, ldo, so = _strided_stack(O)
+    if (b, m, n) != (bo, mo, no) or (ld, stride) != (ldo, so) or G3.dtype != O3.dtype:
+        raise ValueError("G and O must have one shape, dtype and stride layout")
+    _check_tensors([G3, O3], "G and O", (torch.bfloat16, torch.float32), dev)
+    dt = _dtype_code(G3)
+    cfg, arr = make_cfg(steps, coeffs, eps, dt, per_step, schedule)
+    rc = L.muon_ns_orthogonalize_noalloc(ctypes.c_void_p(G3.data_ptr()), ctypes.c_void_p(O3.data_ptr()), dt, m, n,
+                                         ld, b, stride, ctypes.byref(cfg), _stream_handle(stream))
+    _check(rc, "muon_ns_orthogonalize_noalloc")
 
 
 def muon_query_flags(workspace) -> int:

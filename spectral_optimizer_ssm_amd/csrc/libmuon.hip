@@ -1020,6 +1020,57 @@ int muon_ns_orthogonalize(const void* G, void* O, int dtype, int m, int n, int l
   return run_all(runs, C, cfg->eps, ws, nullptr, st, E, nullptr, nparts);
 }
 
+}  // extern "C"
+
+namespace {
+// Workspace of muon_ns_orthogonalize_noalloc: one array per GPU, held by the
+// loaded code object until the process ends.  Host code never uses its name
+// as an address (that is a host-side stand-in): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+
+char* scratch_for_current_device(int* status) {
+  static std::mutex mu;
+  static char* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *status = MUON_EHIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      *status = MUON_EHIP;
+      return nullptr;
+    }
+    ptrs[dev] = static_cast<char*>(p);
+  }
+  *status = MUON_OK;
+  return ptrs[dev];
+}
+}  // namespace
+
+extern "C" {
+
+size_t muon_ns_noalloc_max_bytes(void) { return kNoAllocBytes; }
+
+int muon_ns_orthogonalize_noalloc(const void* G, void* O, int dtype, int m, int n, int ld, int batch,
+                                  long long stride, const muon_ns_cfg* cfg, void* stream) {
+  // every argument check of muon_ns_orthogonalize first (without a workspace
+  // it validates, then stops at MUON_EWORKSPACE before any launch), so that
+  // errors do not depend on the scratch array
+  const int rc = muon_ns_orthogonalize(G, O, dtype, m, n, ld, batch, stride, cfg, nullptr, 0, stream);
+  if (rc != MUON_EWORKSPACE) return rc;  // a validation error, or nothing to do
+  if (muon_ns_workspace_size(m, n, batch, dtype, cfg) > kNoAllocBytes) return MUON_EWORKSPACE;
+  int st = MUON_OK;
+  char* ws = scratch_for_current_device(&st);
+  if (ws == nullptr) return st;
+  return muon_ns_orthogonalize(G, O, dtype, m, n, ld, batch, stride, cfg, ws, kNoAllocBytes, stream);
+}
+
 int muon_query_flags(const void* workspace, int* nonfinite_out) {
   if (workspace == nullptr || nonfinite_out == nullptr || !aligned16(workspace)) return MUON_EINVAL;
   unsigned f = 0;

@@ -159,6 +159,14 @@ def test_small_and_ns_validation(mu):
     assert ns(x, y, mu.MUON_BF16, 64, 128, 128, 0, 0, ctypes.byref(cfg), None, 0, None) == 0
     assert ns(x, y, mu.MUON_BF16, 64, 128, 128, 2, 64 * 128, ctypes.byref(cf32), ws, 1 << 30, None) == -2
     assert ns(None, y, mu.MUON_BF16, 64, 128, 128, 2, 64 * 128, ctypes.byref(cfg), ws, 1 << 30, None) == -1
+    # the workspace-free variant: the same validation, and workspaces beyond its array refused
+    na = L.muon_ns_orthogonalize_noalloc
+    assert L.muon_ns_noalloc_max_bytes() == 32 << 20
+    assert na(x, x64, mu.MUON_BF16, 64, 128, 128, 2, 64 * 128, ctypes.byref(cfg), None) == -1
+    assert na(x, y, mu.MUON_BF16, 64, 128, 127, 2, 64 * 128, ctypes.byref(cfg), None) == -1
+    assert na(x, y, mu.MUON_BF16, 64, 128, 128, 0, 0, ctypes.byref(cfg), None) == 0
+    big = ctypes.c_void_p(0x10000000)
+    assert na(x, big, mu.MUON_BF16, 768, 1536, 1536, 24, 768 * 1536, ctypes.byref(cfg), None) == -3
     # the flag query validates its pointers before any copy
     out = ctypes.c_int(-1)
     assert L.muon_query_flags(None, ctypes.byref(out)) == -1
