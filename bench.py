@@ -516,8 +516,19 @@ def cpu_baseline_injections(X, steps_ns, budget_s=15.0):
 # ----------------------------------------------------------------------------
 # exploration workloads
 # ----------------------------------------------------------------------------
+def small_bf16_kernel(m, n):
+    """The on-chip kernel muon_ns_batched_small launches for a bf16 m x n
+    stack (m <= n): one wave per matrix for s = 32 with l <= 256 and s = 64
+    with l <= 128, else one workgroup per matrix."""
+    if (m == 32 and n <= 256) or (m == 64 and n <= 128):
+        return f"ns_small_bf16_kernel<{m},{n}>"
+    return f"ns_small_bf16_wg_kernel<{m}>"
+
+
 def bench_injections(args, torch, mu, wl):
-    X = wl.injections(batch=args.batch, device="cuda")
+    m, n = args.inj_shape
+    batch = args.batch if args.batch is not None else 393216 * 64 * 128 // (m * n)
+    X = wl.injections(batch=batch, device="cuda", shape=(m, n))
     Y = torch.empty_like(X)
     for _ in range(args.warmup):
         mu.muon_ns_batched_small(X, Y, steps=args.ns_steps)
@@ -533,25 +544,41 @@ def bench_injections(args, torch, mu, wl):
     ms = (t1 - t0) * 1e3 / args.steps
     kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nbytes = X.numel() * 2 * 2
+    gram, comb = ns_flops(m, n)
+    flops = batch * args.ns_steps * (gram + comb)
     gbs = nbytes / (kms * 1e-3) / 1e9
+    tflops = flops / (kms * 1e-3) / 1e12
+    kernel = small_bf16_kernel(m, n)
+    default = (m, n) == (64, 128)
+    wname = "injections" if default else f"injections_{m}x{n}"
+    traffic = measured_traffic(kernel.split("<")[0], wname, ["ns_small.hip", "common.cuh"])
+    # the bound whose peak the kernel's algorithmic work would take longer to reach
+    if nbytes / PEAK_HBM_GBS >= flops / 1e3 / PEAK_BF16_TFLOPS:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
     extra = {} if args.no_cpu else {"cpu_baseline": cpu_baseline_injections(X, args.ns_steps)}
-    return {**extra, "metric": "MuonSSM batched single-step NS matrices/s", "value": round(args.batch / (ms * 1e-3), 1),
+    return {**extra, "metric": "MuonSSM batched single-step NS matrices/s" if default and args.ns_steps == 1
+            else "batched on-chip NS matrices/s", "value": round(batch / (ms * 1e-3), 1),
             "unit": "matrices/s", "ms_per_step": round(ms, 4), "dtype": "bf16",
-            "config": {"workload": f"injections {args.batch}x64x128 bf16, {args.ns_steps} NS step"},
-            "roofline": {"bound": "hbm", "kernel": "ns_small_bf16_kernel<64,128>", "achieved": round(gbs, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("ns_small_bf16_kernel", "injections", ["ns_small.hip",
-                                                                                              "common.cuh"])}}
+            "config": {"workload": f"injections {batch}x{m}x{n} bf16 (rank-8 V K^T), {args.ns_steps} NS step"
+                       + ("" if args.ns_steps == 1 else "s")},
+            "roofline": {**roof, "kernel": kernel, "traffic": traffic,
+                         "algorithmic": {"bytes": nbytes, "flops": flops, "achieved_hbm_gbs": round(gbs, 1),
+                                         "achieved_tflops": round(tflops, 1)}}}
 
 
 def bench_injections_factored(args, torch, mu, wl):
     """The same injections given by their factors V [b, 64, 8], K [b, 128, 8]:
     muon_ns_factored writes the 8 x 8 float32 core of each (NS(V K^T) =
     V C K^T), or also the dense result with --dense."""
-    X, V, K = wl.injections(batch=args.batch, device="cuda", return_factors=True)
+    batch = args.batch if args.batch is not None else 393216
+    X, V, K = wl.injections(batch=batch, device="cuda", return_factors=True)
     del X
-    C = torch.empty((args.batch, 8, 8), dtype=torch.float32, device="cuda")
-    O = torch.empty((args.batch, 64, 128), dtype=torch.bfloat16, device="cuda") if args.dense else None
+    C = torch.empty((batch, 8, 8), dtype=torch.float32, device="cuda")
+    O = torch.empty((batch, 64, 128), dtype=torch.bfloat16, device="cuda") if args.dense else None
     for _ in range(args.warmup):
         mu.muon_ns_factored(V, K, C=C, O=O, steps=args.ns_steps)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -565,10 +592,10 @@ def bench_injections_factored(args, torch, mu, wl):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     per = (64 + 128) * 8 * 2 + 8 * 8 * 4 + (64 * 128 * 2 if args.dense else 0)
-    gbs = args.batch * per / (kms * 1e-3) / 1e9
-    return {"metric": "MuonSSM factored single-step NS matrices/s", "value": round(args.batch / (ms * 1e-3), 1),
+    gbs = batch * per / (kms * 1e-3) / 1e9
+    return {"metric": "MuonSSM factored single-step NS matrices/s", "value": round(batch / (ms * 1e-3), 1),
             "unit": "matrices/s", "ms_per_step": round(ms, 4), "dtype": "bf16",
-            "config": {"workload": f"injections {args.batch} x (V 64x8, K 128x8) bf16 factors, "
+            "config": {"workload": f"injections {batch} x (V 64x8, K 128x8) bf16 factors, "
                                    f"{args.ns_steps} NS step, {'core + dense' if args.dense else '8x8 core'} out"},
             "roofline": {"bound": "hbm", "kernel": "ns_factored_kernel", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -723,7 +750,10 @@ def main():
                              "diag", "single", "sweep"])
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
-    ap.add_argument("--batch", type=int, default=393216, help="injections batch")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="injections batch (default 393216 64 x 128 matrices, or the same bytes at --inj-shape)")
+    ap.add_argument("--inj-shape", type=lambda v: tuple(int(x) for x in v.split("x")), default=(64, 128),
+                    help="injections: m x n of the stacked matrices (m <= n), e.g. 128x256")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense", action="store_true", help="injections_factored: also write the dense result")
     ap.add_argument("--cap", action="store_true", help="full_step: spectral cap on (power step per update)")

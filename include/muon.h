@@ -109,10 +109,11 @@ typedef enum { MUON_NS_AUTO = 0, MUON_NS_ITERATE = 1, MUON_NS_ACCUMULATE = 2 } m
  *             never stored and re-read; groups with the spectral cap, or
  *             beyond 64 matrices in one launch, keep a separate pass.  1:
  *             always a separate apply pass.  The results are bitwise equal.
- * Quintic c != 0 runs on large bfloat16 matrices (the matrix-core path: one
- * more s x s product per step) and in muon_ns_factored; with float32
- * precision, on small (on-chip) matrices and in muon_ns_batched_small it
- * returns MUON_EUNSUPPORTED. */
+ * Quintic c != 0 runs on bfloat16 matrices of every shape (on the
+ * matrix-core path, one more s x s product per step; small matrices then take
+ * that path instead of the on-chip kernel) and in muon_ns_factored; with
+ * float32 precision and in muon_ns_batched_small it returns
+ * MUON_EUNSUPPORTED. */
 typedef struct {
   int steps;
   int ncoef;
@@ -271,9 +272,11 @@ int muon_query_flags(const void* workspace, int* nonfinite_out);
 /* Newton-Schulz on a large batch of small matrices (MuonSSM's per-token,
  * per-head injections), each held on chip for the whole iteration:
  * Y[b] = NS(X[b]) for a contiguous [batch][m][n] stack, no workspace.
- * Supported: MUON_BF16 with min(m, n) in {32, 64}, max(m, n) a multiple of 32
- * up to 256, m <= n; MUON_F32 with min(m, n) <= 64 and max(m, n) <= 256.
- * Other shapes return MUON_EUNSUPPORTED.  Y must not overlap X. */
+ * Supported: MUON_BF16 with min(m, n) in {32, 64, 96, 128}, max(m, n) a
+ * multiple of 32 up to 512, m <= n; MUON_F32 with min(m, n) <= 64 and
+ * max(m, n) <= 256.  Other shapes return MUON_EUNSUPPORTED.  Y must not
+ * overlap X.  (muon_step and muon_ns_orthogonalize send bfloat16 groups with
+ * these short sides and any long side up to 512 to the same kernels.) */
 int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long long batch,
                           const muon_ns_cfg* cfg, void* stream);
 

@@ -58,7 +58,6 @@ constexpr int KS = BK / 16;       // MFMA k-steps per stage
 constexpr int NXCD = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // Wave index as a scalar: everything derived from it (LDS block bases, buffer
 // soffsets) stays in SGPRs instead of being treated as divergent.

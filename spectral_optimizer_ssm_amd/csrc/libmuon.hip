@@ -132,10 +132,13 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
   g->l = g->tall ? m : n;
   g->bf16 = bf16;
   g->esz = bf16 ? 2 : 4;
-  if (ns_small_supported(bf16, g->s, g->l)) {
+  // quintic steps (c != 0) run on the matrix-core path at every shape
+  if (ns_small_supported(bf16, g->s, g->l) && !(bf16 && C.quintic)) {
     g->engine = kSmall;
-    g->s_pad = g->s;
-    g->ld = round_up(g->l, 8);
+    // the bf16 kernels take both sides in multiples of 32 (the zero rows and
+    // columns the momentum pass appends stay zero through every product)
+    g->s_pad = bf16 ? round_up(g->s, 32) : g->s;
+    g->ld = round_up(g->l, bf16 ? 32 : 8);
   } else if (bf16) {
     g->engine = kTiledBf16;
     g->s_pad = round_up(g->s, kTileS);
@@ -150,7 +153,7 @@ int plan_group(int m, int n, int count, bool bf16, const NsCoefs& C, size_t base
   // offsets: below 2 GiB per matrix
   if (g->engine == kTiledBf16 && static_cast<long long>(g->s_pad) * g->ld * 2 >= (1LL << 31))
     return MUON_EUNSUPPORTED;
-  if (C.quintic && g->engine != kTiledBf16) return MUON_EUNSUPPORTED;  // c != 0: large bf16 matrices only
+  if (C.quintic && g->engine != kTiledBf16) return MUON_EUNSUPPORTED;  // c != 0: bf16 matrix-core path only
   g->accumulate = choose_accumulate(*g, C);
   g->P = momentum_blocks_per_matrix(g->tall, g->s_pad, g->ld);
   g->off_part = part_off;
@@ -372,7 +375,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     NsSmallLaunch S{};
     S.X = ws + p.off_x0; S.Y = ws + p.off_x1;
     S.in_stride = xstride; S.out_stride = xstride;
-    S.s = p.s; S.l = p.l; S.ld_in = p.ld; S.ld_out = p.ld;
+    S.s = p.bf16 ? p.s_pad : p.s; S.l = p.bf16 ? p.ld : p.l; S.ld_in = p.ld; S.ld_out = p.ld;
     S.count = p.count; S.transposed = false; S.steps = C.steps;
     for (int k = 0; k < C.steps; ++k) { S.a[k] = C.a[k]; S.b[k] = C.b[k]; }
     S.partials = reinterpret_cast<const float*>(ws + p.off_part); S.P = p.P; S.eps = eps;
@@ -1314,7 +1317,7 @@ int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long 
   const bool bf16 = dtype == MUON_BF16;
   const bool tall = m > n;
   const int s = tall ? n : m, l = tall ? m : n;
-  if (bf16 && tall) return MUON_EUNSUPPORTED;
+  if (bf16 && (tall || s % 32 != 0 || l % 32 != 0)) return MUON_EUNSUPPORTED;
   if (!ns_small_supported(bf16, s, l)) return MUON_EUNSUPPORTED;
   if (batch == 0) return MUON_OK;
   // the bf16 kernel moves 16-byte chunks (every matrix is a multiple of 2 KB)

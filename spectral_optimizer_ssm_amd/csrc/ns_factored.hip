@@ -31,7 +31,6 @@
 namespace muon {
 namespace {
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kMats = 4;          // matrices per wavefront
 #ifndef FACT_WG_PER_CU
 #define FACT_WG_PER_CU 4

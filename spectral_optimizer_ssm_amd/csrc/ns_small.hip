@@ -3,22 +3,26 @@
 // "MuonSSM" (method section on light Newton-Schulz orthogonalisation) runs a
 // single Newton-Schulz step, with no explicit SVD, on the low-rank injection of
 // every token and head; its ablation on the number of Newton-Schulz steps
-// compares one step with five.  Each matrix (s x l, s <= 64) is loaded once,
+// compares one step with five.  Each matrix (s x l, s <= 128) is loaded once,
 // normalised by its Frobenius norm, iterated in LDS and registers, and stored
 // once, so the pass streams HBM exactly once each way.
 //
-// bf16 kernel: one wavefront per matrix, several matrices per workgroup.
+// bf16 kernel (s = 32 with l <= 256, s = 64 with l <= 128): one wavefront per
+// matrix, several matrices per workgroup.
 //  * X lives in LDS (row-major, 16-byte chunks XOR-swizzled per row).
 //  * Gram A = X X^T on v_mfma_f32_32x32x16_bf16 from ds_read_b128 fragments.
 //  * A never touches memory: by symmetry the Gram accumulators already hold,
 //    lane by lane, the operand fragments of A that the combine needs, after a
 //    permutation of the contraction index (a sum is invariant under one).
-//  * Combine D[k][i] = sum_j X[j][k] A[i][j] with the X operand gathered from
-//    LDS in the same contraction order; each lane then holds 4 consecutive
-//    columns of one row of Y = a X + b A X.
+//  * Combine D[k][i] = sum_j X[j][k] A[i][j] with the X operand read from
+//    LDS in the same contraction order by transposing reads
+//    (ds_read_b64_tr_b16); each lane then holds 4 consecutive columns of one
+//    row of Y = a X + b A X.
 //  * Y overwrites X in LDS one 32-column block at a time (same wave, in
 //    order) and leaves through coalesced 16-byte stores.
-// fp32 kernel: one workgroup per matrix, plain FMA dot products in LDS.
+// Larger bf16 shapes (s up to 128, l up to 512): one matrix per workgroup of
+// s / 32 waves (ns_small_bf16_wg_kernel).
+// fp32 kernel: one workgroup per matrix, register-blocked FMA products in LDS.
 #include "common.cuh"
 #include "launch.h"
 
@@ -36,6 +40,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// ds_read_b64_tr_b16: in each 16-lane group the lanes address a 4 x 16 block
+// of 16-bit values (lane 4 r + u: row r, elements 4 u .. 4 u + 3) and lane p
+// receives column p's 4 values, rows 0..3 in order.
+__device__ __forceinline__ u32x2_t tr_read(const char* p) {
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p));
+}
+
 template <int S, int L>
 struct SmallGeo {
   static constexpr int CPR = L / 8;                       // 16-B chunks per row
@@ -49,12 +61,11 @@ struct SmallGeo {
   __device__ static int elem_off(int r, int k) { return chunk_off(r, k >> 3) + ((k & 7) << 1); }
 };
 
-// Two waves per SIMD where the registers allow it without spilling (up to
-// 64 x 128; larger shapes hold more accumulators).
-template <int S, int L> struct SmallWpe { static constexpr int v = S * L <= 64 * 128 ? 2 : 1; };
 
 template <int S, int L>
-__global__ void __launch_bounds__(WPB * 64) __attribute__((amdgpu_waves_per_eu(SmallWpe<S, L>::v)))
+// Two waves per SIMD: the shapes taken here (up to 32 x 256 and 64 x 128)
+// hold few enough accumulators and fragments.
+__global__ void __launch_bounds__(WPB * 64) __attribute__((amdgpu_waves_per_eu(2)))
 ns_small_bf16_kernel(NsSmallLaunch P) {
   using Geo = SmallGeo<S, L>;
   constexpr int NB = S / 32;      // 32-row blocks of X (and of A)
@@ -148,15 +159,18 @@ ns_small_bf16_kernel(NsSmallLaunch P) {
         for (int ib = 0; ib < NB; ++ib)
 #pragma unroll
           for (int r = 0; r < 16; ++r) c[ib][r] = 0.0f;
-        const int kcol = kb * 32 + l32;
+        // X operand xf[t] = X[16 js + 8 (t / 4) + 4 G + t % 4][32 kb + l32] from
+        // two transposing reads: lane 16 g4 + 4 rr + u addresses row
+        // 16 js + 8 h + 4 (g4 / 2) + rr, columns 32 kb + 16 (g4 & 1) + 4 u .. + 3
+        const int g4 = lane >> 4, rr = (lane >> 2) & 3, u = lane & 3;
+        const int tcol = kb * 32 + 16 * (g4 & 1) + 4 * u;
 #pragma unroll
         for (int js = 0; js < NJ; ++js) {
-          bf16x8_t xf;
+          u32x2_t part[2];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int j = 16 * js + 8 * (t >> 2) + 4 * G + (t & 3);
-            xf[t] = *reinterpret_cast<const __bf16*>(lds + Geo::elem_off(j, kcol));
-          }
+          for (int h = 0; h < 2; ++h)
+            part[h] = tr_read(lds + Geo::elem_off(16 * js + 8 * h + 4 * (g4 >> 1) + rr, tcol));
+          const bf16x8_t xf = __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
 #pragma unroll
           for (int ib = 0; ib < NB; ++ib)
             c[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, __builtin_bit_cast(bf16x8_t, af[ib][js]), c[ib], 0, 0, 0);
@@ -201,6 +215,231 @@ ns_small_bf16_kernel(NsSmallLaunch P) {
     wave_lds_sync();  // the next matrix overwrites this region
   }
 }
+
+// ---- bf16, one matrix per workgroup: short sides to 128, long sides to 512 ----
+// The same arithmetic as ns_small_bf16_kernel, shared by S / 32 waves (one per
+// 32-row block) so that a large matrix is not left to one wave's latency:
+//  * X (s x l, l a runtime multiple of 32) sits in LDS, 16-byte chunks
+//    XOR-swizzled per row; A = X X^T (s x s bf16) after it.
+//  * Gram: wave w accumulates column block w of A over the whole long side and
+//    writes it, by symmetry, as rows 32 w .. 32 w + 31 of A (8-byte row
+//    segments, chunks swizzled per row).
+//  * Combine: wave w takes the 32-column blocks kb = w, w + S/32, ... of
+//    Y = a X + b A X.  Its A operand fragments come from A's rows (two 8-byte
+//    reads each), its X operand, contracted over X's row index, from two
+//    ds_read_b64_tr_b16 per 16 rows: in each 16-lane group the lanes address
+//    a 4 x 16 block and every lane receives one column's 4 consecutive rows.
+//    Only wave w reads and writes its column blocks, so Y overwrites X in
+//    place; two workgroup barriers per step separate the Gram, the combine
+//    and the next Gram.
+// Zero rows and columns (muon_step's padding of both sides to multiples of
+// 32) stay zero through every product.
+struct RtGeo {
+  int row, cpr, swm1;
+  __device__ explicit RtGeo(int l) : row(2 * l), cpr(l / 8) {
+    // long sides >= 96 here: one row covers a 256-byte bank sweep, and the
+    // XOR key r mod swm (swm = 4, 8 or 16 chunks, dividing 16) is shared by
+    // rows 16 apart
+    swm1 = ((cpr % 16 == 0) ? 16 : (cpr % 8 == 0) ? 8 : 4) - 1;
+  }
+  __device__ int chunk_off(int r, int c) const { return r * row + ((c ^ (r & swm1)) << 4); }
+};
+
+template <int S>
+struct WgGeoA {  // A: S rows of S bf16, 16-byte chunks XOR-swizzled per row
+  static constexpr int ROW = 2 * S, CPR = S / 8;
+  static constexpr int SW1 = ((CPR % 16 == 0) ? 16 : (CPR % 8 == 0) ? 8 : 4) - 1;
+  __device__ static int off(int r, int c) { return r * ROW + ((c ^ (r & SW1)) << 4); }
+};
+
+template <int S>
+__global__ void __launch_bounds__(256) ns_small_bf16_wg_kernel(NsSmallLaunch P) {
+  extern __shared__ __attribute__((aligned(16))) char lds_dyn[];
+  constexpr int NB = S / 32, NJ = S / 16, NT = NB * 64;
+  using GA = WgGeoA<S>;
+  const int L = P.l;
+  const RtGeo geo(L);
+  const int nk = L / 32, chunks = S * geo.cpr;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  char* xs = lds_dyn;
+  char* as = lds_dyn + static_cast<size_t>(S) * L * 2;
+  float* red = reinterpret_cast<float*>(as);  // the norm's reduction, before A exists
+  const int G = lane >> 5, l32 = lane & 31;
+  // Gram operand rows l32 + 32 b and the update's rows share one key
+  const int key32 = l32 & geo.swm1, base32 = l32 * geo.row;
+  // transposing reads: lane 16 g4 + 4 rr + u addresses row 8 h + 4 (g4 / 2)
+  // + rr (+ 16 js), columns 16 (g4 & 1) + 4 u .. + 3 of the block
+  const int g4 = lane >> 4, rr = (lane >> 2) & 3, u = lane & 3;
+  int trow[2], tkey[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * h + 4 * (g4 >> 1) + rr;
+    trow[h] = r * geo.row + 8 * (u & 1);
+    tkey[h] = r & geo.swm1;
+  }
+  const int tchunk = 2 * (g4 & 1) + (u >> 1);
+
+  for (long long mat = blockIdx.x; mat < P.count; mat += gridDim.x) {
+    const bf16_t* src = static_cast<const bf16_t*>(P.X) + mat * P.in_stride;
+    bf16_t* dst = static_cast<bf16_t*>(P.Y) + mat * P.out_stride;
+    // stage X: eight 16-byte loads in flight per thread
+    float ss = 0.0f;
+    for (int q0 = threadIdx.x; q0 < chunks; q0 += 8 * NT) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+          v[e] = *reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float x0 = lo_bf16(v[e][t]), x1 = hi_bf16(v[e][t]);
+            ss = fmaf(x0, x0, ss);
+            ss = fmaf(x1, x1, ss);
+          }
+          *reinterpret_cast<u32x4_t*>(xs + geo.chunk_off(r, c)) = v[e];
+        }
+      }
+    }
+    float tot;
+    if (P.partials != nullptr) {
+      float s2 = 0.0f;
+      for (int i = threadIdx.x; i < P.P; i += NT) s2 += P.partials[mat * P.P + i];
+      tot = block_sum(s2, red);
+    } else {
+      tot = block_sum(ss, red);
+    }
+    const float inv = 1.0f / (sqrtf(tot) + P.eps);
+    __syncthreads();  // red is read by every thread before A overwrites it
+
+    for (int step = 0; step < P.steps; ++step) {
+      const float sc = step == 0 ? inv : 1.0f;
+      // Gram column block w
+      f32x16_t g[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) g[b][r] = 0.0f;
+#pragma unroll 2
+      for (int ks = 0; ks < L / 16; ++ks) {
+        const int co = ((ks * 2 + G) ^ key32) << 4;
+        bf16x8_t f[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) f[b] = *reinterpret_cast<const bf16x8_t*>(xs + base32 + b * 32 * geo.row + co);
+        bf16x8_t fw = f[0];
+#pragma unroll
+        for (int b = 1; b < NB; ++b)
+          if (b == w) fw = f[b];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) g[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[b], fw, g[b], 0, 0, 0);
+      }
+      // g[b] lane (G, l32), register 4 q + e = A[32 b + 8 q + 4 G + e][32 w + l32]
+      // = A[32 w + l32][32 b + 8 q + 4 G + e]: one 8-byte row segment per q
+      const float gs = sc * sc;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2_t v = {pack_bf16x2(g[b][4 * q] * gs, g[b][4 * q + 1] * gs),
+                             pack_bf16x2(g[b][4 * q + 2] * gs, g[b][4 * q + 3] * gs)};
+          *reinterpret_cast<u32x2_t*>(as + GA::off(32 * w + l32, 4 * b + q) + 8 * G) = v;
+        }
+      __syncthreads();  // A complete; every Gram read of X done
+
+      // the combine's A operand: af[ib][js] = A[32 ib + l32][16 js + 8 h + 4 G + 0..3], h = 0, 1
+      u32x4_t af[NB][NJ];
+#pragma unroll
+      for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+        for (int js = 0; js < NJ; ++js) {
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(as + GA::off(32 * ib + l32, 2 * js) + 8 * G);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(as + GA::off(32 * ib + l32, 2 * js + 1) + 8 * G);
+          af[ib][js] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+      const float alpha = P.a[step] * sc, beta = P.b[step] * sc;
+#pragma unroll 1
+      for (int kb = w; kb < nk; kb += NB) {
+        f32x16_t c[NB];
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[ib][r] = 0.0f;
+        int xo[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xo[h] = trow[h] + (((kb * 4 + tchunk) ^ tkey[h]) << 4);
+#pragma unroll
+        for (int js = 0; js < NJ; ++js) {
+          const u32x2_t p0 = tr_read(xs + xo[0] + js * 16 * geo.row);
+          const u32x2_t p1 = tr_read(xs + xo[1] + js * 16 * geo.row);
+          const bf16x8_t xf = __builtin_bit_cast(bf16x8_t, u32x4_t{p0[0], p0[1], p1[0], p1[1]});
+#pragma unroll
+          for (int ib = 0; ib < NB; ++ib)
+            c[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, __builtin_bit_cast(bf16x8_t, af[ib][js]), c[ib], 0,
+                                                            0, 0);
+        }
+        // c[ib] lane (G, l32), register 4 q + e = (A X)[32 ib + l32][32 kb + 8 q + 4 G + e]
+        int yo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yo[q] = base32 + (((kb * 4 + q) ^ key32) << 4) + 8 * G;
+        u32x2_t ypk[NB][4];
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(xs + yo[q] + ib * 32 * geo.row);
+            const float y0 = fmaf(alpha, lo_bf16(xv[0]), beta * c[ib][4 * q + 0]);
+            const float y1 = fmaf(alpha, hi_bf16(xv[0]), beta * c[ib][4 * q + 1]);
+            const float y2 = fmaf(alpha, lo_bf16(xv[1]), beta * c[ib][4 * q + 2]);
+            const float y3 = fmaf(alpha, hi_bf16(xv[1]), beta * c[ib][4 * q + 3]);
+            ypk[ib][q] = u32x2_t{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+          }
+        wave_lds_sync();  // this wave's reads of block kb before its writes
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x2_t*>(xs + yo[q] + ib * 32 * geo.row) = ypk[ib][q];
+      }
+      __syncthreads();  // Y complete before the next Gram or the store
+    }
+
+    for (int q0 = threadIdx.x; q0 < chunks; q0 += 4 * NT) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+          v[e] = *reinterpret_cast<const u32x4_t*>(xs + geo.chunk_off(r, c));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+          u32x4_t o = v[e];
+          if (P.steps == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o[t] = pack_bf16x2(lo_bf16(o[t]) * inv, hi_bf16(o[t]) * inv);
+          }
+          *reinterpret_cast<u32x4_t*>(dst + static_cast<long long>(r) * P.ld_out + c * 8) = o;
+        }
+      }
+    }
+    __syncthreads();  // the next matrix overwrites X and the reduction slots
+  }
+}
+
+constexpr int kRtMaxL = 512;
+constexpr int kMaxLds = 160 * 1024;
 
 // ---- float32: one workgroup per matrix --------------------------------------
 template <int LMAX>
@@ -317,11 +556,36 @@ long long small_grid(long long units, long long cap) { return units < cap ? (uni
 }  // namespace
 
 bool ns_small_supported(bool bf16, int s, int l) {
-  if (bf16) return (s == 32 || s == 64) && l % 32 == 0 && l >= s && l <= 256;
+  // bf16: the kernels take s in {32, 64, 96, 128} and l a multiple of 32;
+  // muon_step pads other sides with zeros up to those
+  if (bf16) return s >= 1 && s <= 128 && l >= s && l <= kRtMaxL;
   return s >= 1 && s <= 64 && l >= s && l <= 256;
 }
 
 hipError_t launch_ns_small(const NsSmallLaunch& P, bool bf16, hipStream_t st) {
+  if (bf16 && (P.s % 32 != 0 || P.l % 32 != 0 || P.s > 128 || P.l < P.s || P.l > kRtMaxL))
+    return hipErrorInvalidValue;
+  // one matrix per workgroup of s / 32 waves, X and A in dynamic LDS: short
+  // sides above 64, long sides above 256, and 64 x 160 .. 64 x 256, where one
+  // wave per matrix holds too many accumulators for two waves per SIMD
+  if (bf16 && (P.s > 64 || P.l > 256 || (P.s == 64 && P.l >= 160))) {
+    const size_t lds = static_cast<size_t>(P.s) * P.l * 2 + static_cast<size_t>(P.s) * P.s * 2;
+    if (lds > static_cast<size_t>(kMaxLds)) return hipErrorInvalidValue;
+    const long long blocks = small_grid(P.count, 1LL << 16);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(P.s * 2);
+#define MUON_SMALL_WG(SS)                                                                                \
+  if (P.s == SS) {                                                                                       \
+    const void* fn = reinterpret_cast<const void*>(ns_small_bf16_wg_kernel<SS>);                         \
+    if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,             \
+                                           static_cast<int>(lds)) != hipSuccess)                         \
+      return hipErrorInvalidValue;                                                                       \
+    hipLaunchKernelGGL((ns_small_bf16_wg_kernel<SS>), grid, block, lds, st, P);                          \
+    return hipGetLastError();                                                                            \
+  }
+    MUON_SMALL_WG(32) MUON_SMALL_WG(64) MUON_SMALL_WG(96) MUON_SMALL_WG(128)
+#undef MUON_SMALL_WG
+    return hipErrorInvalidValue;
+  }
   if (bf16) {
     const long long blocks = small_grid((P.count + WPB - 1) / WPB, 1LL << 16);
     const dim3 grid(static_cast<unsigned>(blocks)), block(WPB * 64);
@@ -332,8 +596,7 @@ hipError_t launch_ns_small(const NsSmallLaunch& P, bool bf16, hipStream_t st) {
   }
     MUON_SMALL(32, 32) MUON_SMALL(32, 64) MUON_SMALL(32, 96) MUON_SMALL(32, 128)
     MUON_SMALL(32, 160) MUON_SMALL(32, 192) MUON_SMALL(32, 224) MUON_SMALL(32, 256)
-    MUON_SMALL(64, 64) MUON_SMALL(64, 96) MUON_SMALL(64, 128) MUON_SMALL(64, 160)
-    MUON_SMALL(64, 192) MUON_SMALL(64, 224) MUON_SMALL(64, 256)
+    MUON_SMALL(64, 64) MUON_SMALL(64, 96) MUON_SMALL(64, 128)
 #undef MUON_SMALL
     return hipErrorInvalidValue;
   }

@@ -92,7 +92,7 @@ def test_step_validation(mu, case, expect):
     cfg, keep = _cfg(mu, steps={"steps_negative": -1, "steps_too_many": 65}.get(case, 5),
                      coeffs=(1.5, -0.5, 0.25) if case == "quintic_c" else (1.5, -0.5),
                      eps=-1.0 if case == "negative_eps" else 1e-7,
-                     prec=9 if case == "bad_precision" else None)
+                     prec={"bad_precision": 9, "quintic_c": mu.MUON_F32}.get(case))
     if case == "ncoef_4":
         cfg.ncoef = 4
     if case == "bad_schedule":
@@ -174,9 +174,9 @@ def test_small_and_ns_validation(mu):
     assert L.muon_query_flags(ws, None) == -1 and out.value == -1
 
 
-def _phases(mu, shapes, steps, schedule, prec=None, separate_apply=0):
+def _phases(mu, shapes, steps, schedule, prec=None, separate_apply=0, coeffs=(1.5, -0.5)):
     L = mu.lib()
-    cfg, keep = mu.make_cfg(steps, (1.5, -0.5), 1e-7, mu.MUON_BF16 if prec is None else prec, False, schedule,
+    cfg, keep = mu.make_cfg(steps, coeffs, 1e-7, mu.MUON_BF16 if prec is None else prec, False, schedule,
                             separate_apply=separate_apply)
     gs = [_group(mu, m, n, c) for m, n, c in shapes]
     arr = (mu.binding.GroupC * len(gs))(*[g for g, _ in gs])
@@ -215,6 +215,14 @@ def test_phases_iterate_and_accumulate(mu):
     assert _phases(mu, [(300, 700, 2)], 2, mu.MUON_NS_ACCUMULATE, mu.MUON_F32) == \
         ["momentum", "f32_gram", "f32_combine", "f32_gram", "f32_combine", "apply"]
     assert _phases(mu, [(64, 128, 9)], 3, mu.MUON_NS_ACCUMULATE) == ["momentum", "ns_small", "apply"]
+    # bf16 short sides up to 128 and long sides up to 512 stay on chip (both
+    # padded to multiples of 32); beyond either, the matrix-core path
+    for shape in ((128, 512), (96, 300), (300, 96), (1, 70), (33, 500), (512, 128)):
+        assert _phases(mu, [shape + (3,)], 5, mu.MUON_NS_ITERATE) == ["momentum", "ns_small", "apply"], shape
+    for shape in ((129, 512), (128, 513), (600, 100)):
+        assert "ns_small" not in _phases(mu, [shape + (3,)], 5, mu.MUON_NS_ITERATE), shape
+    # quintic steps take the matrix-core path whatever the shape
+    assert "ns_small" not in _phases(mu, [(64, 128, 3)], 3, mu.MUON_NS_ITERATE, coeffs=(2.0, -1.5, 0.5))
     assert _phases(mu, MAMBA, 0, mu.MUON_NS_AUTO) == ["momentum"] * 2 + ["apply"] * 2
     # 2 steps: one E = B_0^2, then A_1 / B_1, then Q_2 = B_1 B_0
     assert _phases(mu, MAMBA, 2, mu.MUON_NS_ACCUMULATE).count("symprod") == 3

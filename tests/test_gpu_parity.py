@@ -280,6 +280,42 @@ def test_batched_small_bf16_shapes(mu, shape, steps):
         assert orc.rel_frobenius(Yd[b], ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("steps", [1, 5])
+@pytest.mark.parametrize("shape", [(96, 192), (128, 256), (128, 512), (96, 96), (32, 512), (64, 320), (64, 192)])
+def test_batched_small_bf16_wide_shapes(mu, shape, steps):
+    """Short sides 96 and 128, and long sides beyond 256, on the on-chip
+    kernel with a runtime long side: every matrix against the oracle."""
+    m, n = shape
+    g = wl.random_group(17 + m + n, 9, m, n, "bf16")
+    X = to_torch_bits(g.G).cuda()
+    Y = torch.empty_like(X)
+    mu.muon_ns_batched_small(X, Y, steps=steps)
+    torch.cuda.synchronize()
+    Yd = t64(Y)
+    worst = sdev = 0.0
+    for b in range(9):
+        ref, _ = orc.newton_schulz(grad64(g, b), steps)
+        worst = max(worst, orc.rel_frobenius(Yd[b], ref))
+        sdev = max(sdev, sigma_deviation(Yd[b], ref))
+    print(f"[parity] batched_small {m}x{n} steps {steps}: max_O {worst:.3e} max_sigma_dev {sdev:.3e}", flush=True)
+    assert worst <= BF16_TOL
+
+
+@pytest.mark.parametrize("steps", [0, 1, 5])
+@pytest.mark.parametrize("shape", [(128, 512), (96, 300), (300, 96), (128, 128), (100, 100), (1, 70), (33, 500),
+                                   (512, 128), (64, 320), (70, 20)])
+def test_small_bf16_groups_on_chip(mu, shape, steps):
+    """bf16 groups with short side up to 128 and long side up to 512 run on
+    chip, both sides padded with zeros to multiples of 32: W, M and O of
+    every matrix against the oracle."""
+    m, n = shape
+    g = wl.random_group(400 + m + n, 5, m, n, "bf16")
+    w = wl.Workload(f"small{m}x{n}", [g], steps=steps)
+    devs, outs = run_step(mu, w)
+    for i in range(5):
+        compare_step(g, i, outs[0], devs[0], w, BF16_TOL)
+
+
 @pytest.mark.parametrize("shape", [(128, 64), (64, 128), (40, 200), (200, 40), (7, 33)])
 def test_batched_small_fp32(mu, shape):
     m, n = shape
@@ -481,7 +517,7 @@ def test_quintic_mamba2_shapes(mu, schedule, coeffs, per_step, steps):
 
 
 @pytest.mark.parametrize("schedule", SCHEDULES)
-@pytest.mark.parametrize("shape", [(256, 512), (520, 1100), (300, 257)])
+@pytest.mark.parametrize("shape", [(256, 512), (520, 1100), (300, 257), (64, 128), (96, 300)])
 def test_quintic_ragged(mu, schedule, shape):
     m, n = shape
     g = wl.random_group(300 + m + n, 2, m, n, "bf16")
@@ -492,8 +528,8 @@ def test_quintic_ragged(mu, schedule, shape):
 
 
 def test_quintic_unsupported_paths(mu):
-    """c != 0 on the on-chip and float32 engines is refused before any work."""
-    for m, n, dt, prec in ((64, 128, "bf16", None), (96, 160, "f32", None), (300, 400, "bf16", "f32")):
+    """c != 0 with float32 precision is refused before any work."""
+    for m, n, dt, prec in ((96, 160, "f32", None), (300, 400, "bf16", "f32")):
         g = wl.random_group(7, 1, m, n, dt)
         w = wl.Workload("q", [g], coeffs=QUINTIC, steps=2)
         with pytest.raises(mu.MuonError) as e:
