@@ -184,6 +184,43 @@ def factored_ns(V: np.ndarray, K: np.ndarray, steps: int, coeffs=CUBIC, eps: flo
 
 
 # ----------------------------------------------------------------------------
+# Momentum pathway (MuonSSM, method section on the momentum-augmented state
+# update, and the parallelism paragraph of its theory section): a momentum
+# state M_t, beside the memory state S_t, accumulates the conditioned
+# injections, and the pair follows a block-affine recurrence.  The pages give
+# no equation; the reading taken is heavy-ball momentum on the memory:
+#   U_t = NS(V_t K_t^T)                 (the light Newton-Schulz step above)
+#   M_t = beta M_{t-1} + U_t
+#   S_t = a_t S_{t-1} + M_t             (a_t the backbone's per-token decay)
+# i.e. [S_t; M_t] = [[a_t, beta], [0, beta]] [S_{t-1}; M_{t-1}] + [U_t; U_t].
+# ----------------------------------------------------------------------------
+def momentum_recurrence(U, a, beta: float, M0: np.ndarray, S0=None):
+    """Run the pair recurrence over the updates U[t] (t = 0..T-1, each m x n)
+    from (S0, M0); a[t] is the decay of token t (unused when S0 is None).
+    Returns (M_T, S_T) (S_T None when S0 is None)."""
+    M = np.array(M0, dtype=np.float64)
+    S = None if S0 is None else np.array(S0, dtype=np.float64)
+    for t in range(len(U)):
+        M = beta * M + np.asarray(U[t], dtype=np.float64)
+        if S is not None:
+            S = float(a[t]) * S + M
+    return M, S
+
+
+def ssm_momentum(V, K, a, beta: float, M0, S0=None, steps: int = 1, coeffs=CUBIC, eps: float = DEFAULT_EPS,
+                 per_step: bool = False):
+    """The momentum pathway over one sequence of factored injections:
+    V [T, m, r], K [T, n, r] (token t's injection X_t = V[t] K[t]^T), decays
+    a [T].  Each U_t is the dense Newton-Schulz result of X_t (newton_schulz
+    above, the plain definition); then momentum_recurrence.  Returns
+    (M_T, S_T)."""
+    V = np.asarray(V, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    U = [newton_schulz(V[t] @ K[t].T, steps, coeffs, eps, per_step)[0] for t in range(V.shape[0])]
+    return momentum_recurrence(U, a, beta, M0, S0)
+
+
+# ----------------------------------------------------------------------------
 # Spectral cap ("An Isotropy-Preserving Spectral Cap for Muon"): at each update
 # remove the direction that contributes most, to first order, to the growth of
 # the weight's top singular value; the other directions keep learning.  The

@@ -654,3 +654,135 @@ def test_lanczos_ritz_values_are_the_krylov_projection(k):
     ev = np.linalg.eigvalsh(B.T @ H @ B)
     lo, hi = orc.lanczos_extremes(H, k)
     assert abs(lo - ev[0]) < 1e-10 and abs(hi - ev[-1]) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# Momentum pathway of MuonSSM (momentum-augmented state update): M_t and S_t
+# ---------------------------------------------------------------------------
+def test_momentum_recurrence_three_tokens_written_out():
+    """Three tokens expanded by hand from M_t = b M_{t-1} + U_t and
+    S_t = a_t S_{t-1} + M_t:
+      M_3 = b^3 M0 + b^2 U1 + b U2 + U3
+      S_3 = a3 a2 a1 S0 + (a3 a2 b + a3 b^2 + b^3) M0 + (a3 a2 + a3 b + b^2) U1
+            + (a3 + b) U2 + U3
+    An off-by-one in either recurrence (S fed M_{t-1}, M fed before S, the
+    decay applied to M) changes these coefficients."""
+    rng = np.random.default_rng(71)
+    M0, S0 = rng.standard_normal((2, 3, 5))
+    U1, U2, U3 = rng.standard_normal((3, 3, 5))
+    a1, a2, a3 = 0.91, 0.63, 0.77
+    b = 0.85
+    M, S = orc.momentum_recurrence([U1, U2, U3], [a1, a2, a3], b, M0, S0)
+    M_ref = b ** 3 * M0 + b ** 2 * U1 + b * U2 + U3
+    S_ref = (a3 * a2 * a1 * S0 + (a3 * a2 * b + a3 * b ** 2 + b ** 3) * M0 + (a3 * a2 + a3 * b + b ** 2) * U1
+             + (a3 + b) * U2 + U3)
+    np.testing.assert_allclose(M, M_ref, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-14, atol=1e-14)
+    M_only, S_none = orc.momentum_recurrence([U1, U2, U3], None, b, M0)
+    assert S_none is None
+    np.testing.assert_allclose(M_only, M_ref, rtol=1e-14, atol=1e-14)
+
+
+def test_momentum_recurrence_is_block_affine_in_any_bracketing():
+    """The pages state that the memory and momentum states together follow a
+    block-affine recurrence, so a parallel scan may compose the per-token maps
+    in any bracketing.  Each token is the map (S, M) -> (a S + b M + U,
+    b M + U); composing them as a balanced tree of (2 x 2 coefficient matrix,
+    offset pair) maps must give the sequential result."""
+    rng = np.random.default_rng(72)
+    T, b = 13, 0.9
+    U = rng.standard_normal((T, 4, 6))
+    a = rng.uniform(0.5, 1.0, T)
+    M0, S0 = rng.standard_normal((2, 4, 6))
+
+    def token_map(t):
+        return np.array([[a[t], b], [0.0, b]]), (U[t], U[t])
+
+    def compose(f, g):  # g after f
+        Af, (bs_f, bm_f) = f
+        Ag, (bs_g, bm_g) = g
+        return Ag @ Af, (Ag[0, 0] * bs_f + Ag[0, 1] * bm_f + bs_g, Ag[1, 0] * bs_f + Ag[1, 1] * bm_f + bm_g)
+
+    def tree(lo, hi):
+        if hi - lo == 1:
+            return token_map(lo)
+        mid = (lo + hi) // 2
+        return compose(tree(lo, mid), tree(mid, hi))
+
+    A, (bs, bm) = tree(0, T)
+    S_scan = A[0, 0] * S0 + A[0, 1] * M0 + bs
+    M_scan = A[1, 0] * S0 + A[1, 1] * M0 + bm
+    M, S = orc.momentum_recurrence(U, a, b, M0, S0)
+    np.testing.assert_allclose(M, M_scan, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, S_scan, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("steps", [1, 5])
+def test_ssm_momentum_rank_one_closed_form(steps):
+    """Rank-1 injections X_t = v_t k_t^T have one singular value, so the
+    Frobenius-normalised matrix has sigma = 1 (up to eps), a fixed point of
+    the cubic (1.5 - 0.5 = 1): U_t = v_t k_t^T / (|v_t| |k_t|).  The final
+    states are then weighted sums with weights written as explicit products
+    and sums (no recurrence):
+      M_T = b^T M0 + sum_u b^(T-u) U_u
+      S_T = (prod_t a_t) S0 + sum_t g_t b^t M0 + sum_u (sum_{t>=u} g_t b^(t-u)) U_u,
+    g_t = prod_{s>t} a_s (tokens numbered 1..T)."""
+    rng = np.random.default_rng(73)
+    T, m, n, b = 6, 5, 7, 0.8
+    V = rng.standard_normal((T, m, 1))
+    K = rng.standard_normal((T, n, 1))
+    a = rng.uniform(0.6, 1.0, T)
+    M0, S0 = rng.standard_normal((2, m, n))
+    Uc = [np.outer(V[t, :, 0], K[t, :, 0]) / (np.linalg.norm(V[t]) * np.linalg.norm(K[t])) for t in range(T)]
+    g = [np.prod(a[t + 1:]) for t in range(T)]  # token t + 1 in 1-based numbering
+    M_ref = b ** T * M0 + sum(b ** (T - 1 - u) * Uc[u] for u in range(T))
+    S_ref = (np.prod(a) * S0 + sum(g[t] * b ** (t + 1) for t in range(T)) * M0
+             + sum(sum(g[t] * b ** (t - u) for t in range(u, T)) * Uc[u] for u in range(T)))
+    M, S = orc.ssm_momentum(V, K, a, b, M0, S0, steps=steps, eps=0.0)
+    np.testing.assert_allclose(M, M_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_ssm_momentum_single_token_is_the_ns_step():
+    """With b = 0 and a = 0 both states equal the newest token's Newton-Schulz
+    result, whatever M0 and S0 held."""
+    rng = np.random.default_rng(74)
+    V = rng.standard_normal((3, 16, 8))
+    K = rng.standard_normal((3, 24, 8))
+    M0, S0 = rng.standard_normal((2, 16, 24))
+    M, S = orc.ssm_momentum(V, K, np.zeros(3), 0.0, M0, S0, steps=1)
+    O, _ = orc.newton_schulz(V[2] @ K[2].T, 1)
+    np.testing.assert_allclose(M, O, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(S, O, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("slip", ["s_uses_old_m", "decay_on_m", "ema_momentum", "s_skips_momentum"])
+def test_planted_recurrence_slips_are_caught(slip):
+    """Plausible misreadings of the momentum pathway, planted in a copy of the
+    recurrence, each break the written-out three-token pin."""
+    rng = np.random.default_rng(75)
+    M0, S0 = rng.standard_normal((2, 3, 4))
+    U = rng.standard_normal((3, 3, 4))
+    a, b = [0.91, 0.63, 0.77], 0.85
+
+    def slipped():
+        M, S = M0.copy(), S0.copy()
+        for t in range(3):
+            M_old = M
+            if slip == "decay_on_m":
+                M = a[t] * M + U[t]
+            elif slip == "ema_momentum":
+                M = b * M + (1 - b) * U[t]
+            else:
+                M = b * M + U[t]
+            if slip == "s_uses_old_m":
+                S = a[t] * S + M_old
+            elif slip == "s_skips_momentum":
+                S = a[t] * S + U[t]
+            else:
+                S = a[t] * S + M
+        return M, S
+
+    M_ref, S_ref = orc.momentum_recurrence(U, a, b, M0, S0)
+    M, S = slipped()
+    assert not (np.allclose(M, M_ref, rtol=1e-6) and np.allclose(S, S_ref, rtol=1e-6))
