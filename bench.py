@@ -13,7 +13,7 @@ two device synchronisations), per-kernel durations from HIP events recorded by
 muon_step_timed in K further steps (those run the phases one after another on
 one stream), the roofline of the dominant kernel, and the fp64 oracle timed on
 a bounded sample on the host cores.
-Other workloads: injections, injections_factored, adamw, diag, sweep (1/3/5/8
+Other workloads: injections, injections_factored, ssm_momentum, adamw, diag, sweep (1/3/5/8
 NS steps with the orthogonality error of each update); out_proj, in_proj,
 single are for exploration.  --schedule, --separate-apply, --one-stream and
 --per-matrix switch single design choices of the full step for A/B runs.
@@ -604,6 +604,84 @@ def bench_injections_factored(args, torch, mu, wl):
                                                      ["ns_factored.hip", "common.cuh"])}}
 
 
+def cpu_baseline_ssm_momentum(V, K, a, M0, S0, beta, steps_ns, budget_s=15.0):
+    """The oracle's momentum pathway (dense fp64 NS of every token, then the
+    recurrence) on the first tokens of sequence 0 until budget_s, as a token
+    rate; every token costs the same, so the rate scales to the workload."""
+    import oracle as orc
+    Vs = V[0].float().cpu().numpy().astype(np.float64)
+    Ks = K[0].float().cpu().numpy().astype(np.float64)
+    As = a[0].cpu().numpy().astype(np.float64)
+    M = M0[0].cpu().numpy().astype(np.float64)
+    S = S0[0].cpu().numpy().astype(np.float64)
+    done, t = 0, 0.0
+    while t < budget_s and done < Vs.shape[0]:
+        c = slice(done, done + 64)
+        t0 = time.perf_counter()
+        M, S = orc.ssm_momentum(Vs[c], Ks[c], As[c], beta, M, S, steps=steps_ns)
+        t += time.perf_counter() - t0
+        done += Vs[c].shape[0]
+    return {"value": round(done / t, 1), "unit": "injections/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"the first {done} tokens of sequence 0 (fp64 numpy: dense NS of each 64x128 injection, "
+                      f"{steps_ns} step, then the state recurrence), rate per token", "host_cores": host_cores()}
+
+
+def bench_ssm_momentum(args, torch, mu, wl):
+    """MuonSSM's momentum pathway over the injection workload as sequences:
+    192 sequences (batch 8 x 24 heads) x 2048 tokens of 64 x 128 rank-8
+    injections; per token NS(V K^T) in factored form, M_t = beta M_{t-1} + U_t,
+    S_t = a_t S_{t-1} + M_t."""
+    V, K, a, M0, S0 = wl.ssm_sequences(device="cuda")
+    nseq, T, m, r = V.shape
+    n = K.shape[2]
+    M, S = M0.clone(), S0.clone()
+    beta = wl.SSM_BETA
+    ws = mu.muon_ssm_momentum(V, K, M, S, a, beta=beta, steps=args.ns_steps)
+    for _ in range(args.warmup):
+        mu.muon_ssm_momentum(V, K, M, S, a, beta=beta, steps=args.ns_steps, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mu.muon_ssm_momentum(V, K, M, S, a, beta=beta, steps=args.ns_steps, workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-kernel durations from the events muon_ssm_momentum_timed records
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in row:
+            e.record()
+        evs.append(row)
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        mu.muon_ssm_momentum(V, K, M, S, a, beta=beta, steps=args.ns_steps, workspace=ws,
+                             events=[e.cuda_event for e in evs[k]])
+    torch.cuda.synchronize()
+    names = ["ns_factored_kernel", "ssm_momentum_accum_kernel", "ssm_momentum_combine_kernel"]
+    dur = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+           for i, nm in enumerate(names)}
+    tokens = nseq * T
+    chunks = -(-T // 256)
+    fb = (m + n) * r * 2                      # the factors of one token
+    alg = {"ns_factored_kernel": tokens * (fb + r * r * 4),
+           "ssm_momentum_accum_kernel": tokens * (fb + r * r * 4 + 4) + nseq * chunks * 2 * 64 * 128 * 4,
+           "ssm_momentum_combine_kernel": nseq * (4 * m * n * 4 + chunks * 2 * 64 * 128 * 4)}
+    dom = max(names, key=lambda nm: dur[nm])
+    gbs = alg[dom] / (dur[dom] * 1e-3) / 1e9
+    kernels = {nm: {"ms": round(dur[nm], 4), "alg_bytes": alg[nm],
+                    "gbs": round(alg[nm] / (dur[nm] * 1e-3) / 1e9, 1)} for nm in names}
+    extra = {} if args.no_cpu else {"cpu_baseline": cpu_baseline_ssm_momentum(V, K, a, M0, S0, beta, args.ns_steps)}
+    return {**extra, "metric": "MuonSSM momentum pathway injections/s", "value": round(tokens / (ms * 1e-3), 1),
+            "unit": "injections/s", "ms_per_step": round(ms, 4), "dtype": "bf16",
+            "config": {"workload": f"ssm_momentum {nseq} sequences x {T} tokens of {m}x{n} rank-{r} bf16 injections,"
+                                   f" {args.ns_steps} NS step, beta {beta}, fp32 M and S"},
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(dom, "ssm_momentum", ["ssm_momentum.hip", "ns_factored.hip",
+                                                                           "common.cuh"])},
+            "kernels": kernels}
+
+
 def bench_adamw(args, torch, mu, wl):
     """AdamW over the Mamba-2-130M parameters outside the Muon groups (170
     tensors, 38.9 M elements, bf16 gradients)."""
@@ -746,7 +824,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_step",
-                    choices=["full_step", "out_proj", "in_proj", "injections", "injections_factored", "adamw",
+                    choices=["full_step", "out_proj", "in_proj", "injections", "injections_factored", "ssm_momentum",
+                             "adamw",
                              "diag", "single", "sweep"])
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--count", type=int, default=24, help="matrices per group (full_step)")
@@ -782,7 +861,7 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.ns_steps is None:
-        args.ns_steps = 1 if args.workload.startswith("injections") else 5
+        args.ns_steps = 1 if args.workload.startswith("injections") or args.workload == "ssm_momentum" else 5
     import torch
     import spectral_optimizer_ssm_amd as mu
     import workloads as wl
@@ -798,6 +877,8 @@ def main():
         res = bench_injections(args, torch, mu, wl)
     elif args.workload == "injections_factored":
         res = bench_injections_factored(args, torch, mu, wl)
+    elif args.workload == "ssm_momentum":
+        res = bench_ssm_momentum(args, torch, mu, wl)
     elif args.workload == "adamw":
         res = bench_adamw(args, torch, mu, wl)
     elif args.workload == "diag":

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 7
+#define MUON_VERSION 8
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -301,6 +301,44 @@ int muon_ns_batched_small(const void* X, void* Y, int dtype, int m, int n, long 
  * MUON_EUNSUPPORTED.  Outputs must not overlap inputs or each other. */
 int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int r, long long batch,
                      const muon_ns_cfg* cfg, float* C_out, void* O_out, void* stream);
+
+/* The momentum pathway of MuonSSM over sequences of factored injections
+ * ("MuonSSM", method section on the momentum-augmented state update, and the
+ * theory section's parallelism paragraph: a momentum state M_t beside the
+ * memory state S_t accumulates the conditioned injections; the pair follows
+ * a block-affine recurrence).  The pages give no equation; the reading
+ * implemented is heavy-ball momentum on the memory.  For every sequence and
+ * token t = 1..T, with X_t = V_t K_t^T:
+ *   U_t = NS(X_t)                      (cfg: steps, coefficients, eps)
+ *   M_t = beta M_{t-1} + U_t
+ *   S_t = a_t S_{t-1} + M_t            (only when S is given)
+ * and (M, S) are replaced by (M_T, S_T).  U_t is formed in factored form,
+ * V_t C_t K_t^T with an r x r core (as muon_ns_factored), and never stored
+ * densely; a long sequence may be processed in consecutive calls (the states
+ * carry over exactly up to rounding).
+ *   V      [nseq][T][m][r] bfloat16, contiguous, 16-byte aligned
+ *   K      [nseq][T][n][r] bfloat16, contiguous, 16-byte aligned
+ *   beta   momentum coefficient (finite)
+ *   decay  [nseq][T] float32 per-token decays a_t; read only when S != NULL
+ *   M      [nseq][m][n] float32, in/out
+ *   S      NULL, or [nseq][m][n] float32, in/out
+ * dtype and cfg->precision must be MUON_BF16 (cores as in muon_ns_factored;
+ * the rank-r products accumulate in float32 from bf16 operands scaled by each
+ * token's weight).  Supported: r == 8, m <= 64, n <= 128; otherwise
+ * MUON_EUNSUPPORTED.  M, S, decay, the factors and the workspace must not
+ * overlap.  nseq == 0 or T == 0 leaves the states unchanged.  The workspace
+ * (muon_ssm_momentum_workspace_size bytes, 16-byte aligned) holds the cores
+ * and per-chunk partial sums; muon_query_flags does not apply to it. */
+size_t muon_ssm_momentum_workspace_size(int m, int n, int r, long long nseq, int T);
+int muon_ssm_momentum(const void* V, const void* K, int dtype, int m, int n, int r, long long nseq, int T,
+                      float beta, const float* decay, float* M, float* S, const muon_ns_cfg* cfg,
+                      void* workspace, size_t workspace_bytes, void* stream);
+/* muon_ssm_momentum for measurement: records four caller-created hipEvent_t
+ * handles on `stream` (nevents >= 4): before the core pass, after it, after
+ * the per-chunk accumulation and after the in-order combine. */
+int muon_ssm_momentum_timed(const void* V, const void* K, int dtype, int m, int n, int r, long long nseq, int T,
+                            float beta, const float* decay, float* M, float* S, const muon_ns_cfg* cfg,
+                            void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents);
 
 /* AdamW for the parameters outside the Muon groups ("Muon Meets Mamba":
  * AdamW is the baseline optimizer and keeps the non-projection parameters),

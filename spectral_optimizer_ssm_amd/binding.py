@@ -50,7 +50,8 @@ class GroupC(ctypes.Structure):
 
 EXPORTS = ("muon_step_workspace_size", "muon_step", "muon_step_phases", "muon_step_timed", "muon_ns_workspace_size",
            "muon_ns_orthogonalize", "muon_ns_noalloc_max_bytes", "muon_ns_orthogonalize_noalloc", "muon_query_flags",
-           "muon_ns_batched_small", "muon_ns_factored", "muon_adamw",
+           "muon_ns_batched_small", "muon_ns_factored", "muon_ssm_momentum_workspace_size", "muon_ssm_momentum",
+           "muon_ssm_momentum_timed", "muon_adamw",
            "muon_spectral_diag_workspace_size", "muon_spectral_diag", "muon_spectral_diag_timed",
            "muon_status_string", "muon_version")
 
@@ -90,6 +91,15 @@ def lib():
     L.muon_ns_factored.argtypes = [vp, vp, i, i, i, i, ctypes.c_longlong, ctypes.POINTER(NsCfg),
                                    ctypes.POINTER(f), vp, vp]
     L.muon_ns_factored.restype = i
+    L.muon_ssm_momentum_workspace_size.argtypes = [i, i, i, ctypes.c_longlong, i]
+    L.muon_ssm_momentum_workspace_size.restype = sz
+    L.muon_ssm_momentum.argtypes = [vp, vp, i, i, i, i, ctypes.c_longlong, i, f, ctypes.POINTER(f), ctypes.POINTER(f),
+                                    ctypes.POINTER(f), ctypes.POINTER(NsCfg), vp, sz, vp]
+    L.muon_ssm_momentum.restype = i
+    L.muon_ssm_momentum_timed.argtypes = [vp, vp, i, i, i, i, ctypes.c_longlong, i, f, ctypes.POINTER(f),
+                                          ctypes.POINTER(f), ctypes.POINTER(f), ctypes.POINTER(NsCfg), vp, sz, vp,
+                                          ctypes.POINTER(ctypes.c_void_p), i]
+    L.muon_ssm_momentum_timed.restype = i
     L.muon_adamw.argtypes = [i, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                              ctypes.POINTER(ctypes.c_longlong), i, f, f, f, f, f, ctypes.c_longlong, vp]
     L.muon_adamw.restype = i
@@ -473,6 +483,54 @@ def muon_ns_factored(V, K, C=None, O=None, steps=1, coeffs=(1.5, -0.5), eps=1e-7
                             ctypes.c_void_p(O.data_ptr()) if O is not None else None, _stream_handle(stream))
     _check(rc, "muon_ns_factored")
     return C
+
+
+def _fptr(t):
+    return None if t is None else ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float))
+
+
+def muon_ssm_momentum(V, K, M, S=None, decay=None, beta=0.9, steps=1, coeffs=(1.5, -0.5), eps=1e-7, per_step=False,
+                      workspace=None, stream=None, events=None):
+    """The momentum pathway over nseq sequences of T factored injections:
+    V [nseq, T, m, r] and K [nseq, T, n, r] bf16, M (and S) [nseq, m, n]
+    float32 updated in place to the states after the T tokens
+    (M_t = beta M_{t-1} + NS(V_t K_t^T); S_t = decay_t S_{t-1} + M_t with
+    decay [nseq, T] float32).  Returns the workspace tensor for reuse.
+    `events`: optional list of 4 raw hipEvent_t handles (ints) recorded by
+    muon_ssm_momentum_timed at its phase boundaries."""
+    import torch
+    L = lib()
+    if V.dim() != 4 or K.dim() != 4 or V.shape[:2] != K.shape[:2] or V.shape[3] != K.shape[3]:
+        raise ValueError("V, K must be [nseq, T, m, r] and [nseq, T, n, r]")
+    nseq, T, m, r = V.shape
+    n = K.shape[2]
+    dev = _current_device()
+    if not (V.is_contiguous() and K.is_contiguous()):
+        raise ValueError("V and K must be contiguous")
+    _check_tensors([V, K], "V and K", (torch.bfloat16,), dev)
+    for name, t in (("M", M), ("S", S)):
+        if t is not None and (not t.is_contiguous() or tuple(t.shape) != (nseq, m, n)):
+            raise ValueError(f"{name} must be a contiguous [{nseq}, {m}, {n}] float32 tensor")
+    _check_tensors([M] + ([S] if S is not None else []), "M and S", (torch.float32,), dev)
+    if S is not None:
+        if decay is None or not decay.is_contiguous() or tuple(decay.shape) != (nseq, T):
+            raise ValueError(f"with S, decay must be a contiguous [{nseq}, {T}] float32 tensor")
+        _check_tensors([decay], "decay", (torch.float32,), dev)
+    need = int(L.muon_ssm_momentum_workspace_size(m, n, r, nseq, T))
+    if need == 0:
+        raise MuonError(MUON_EUNSUPPORTED, "muon_ssm_momentum_workspace_size")
+    ws = _workspace(workspace, need, dev)
+    cfg, arr = make_cfg(steps, coeffs, eps, MUON_BF16, per_step)
+    args = (ctypes.c_void_p(V.data_ptr()), ctypes.c_void_p(K.data_ptr()), MUON_BF16, m, n, r, nseq, T, float(beta),
+            _fptr(decay if S is not None else None), _fptr(M), _fptr(S), ctypes.byref(cfg),
+            ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream_handle(stream))
+    if events is None:
+        rc = L.muon_ssm_momentum(*args)
+    else:
+        ev = (ctypes.c_void_p * len(events))(*events)
+        rc = L.muon_ssm_momentum_timed(*args, ev, len(events))
+    _check(rc, "muon_ssm_momentum")
+    return ws
 
 
 class AdamwTensors:

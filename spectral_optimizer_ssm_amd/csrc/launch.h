@@ -218,6 +218,26 @@ struct FactLaunch {
 int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off = nullptr);
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st);
 
+// Momentum pathway over sequences of factored injections (ssm_momentum.hip):
+// per (sequence, chunk of kSsmMomQ tokens) float32 partial sums, then the
+// chunk maps applied in token order to the caller's states.
+constexpr int kSsmMomQ = 256;
+struct SsmMomLaunch {
+  const bf16_t* V;     // [nseq][T][m][8]
+  const bf16_t* K;     // [nseq][T][n][8]
+  const float* C;      // [nseq][T][8][8] Newton-Schulz cores
+  const float* a;      // [nseq][T] decays (with S)
+  float beta;
+  int m, n, T, Q, nchunks;  // m <= 64, n <= 128, Q tokens per chunk
+  long long nseq;
+  float* part;         // [nseq][nchunks][1 or 2][64][128] partial sums
+  float* coef;         // [nseq][nchunks][4]: beta^L, prod a, B, 0
+  float* M;            // [nseq][m][n] in/out
+  float* S;            // null, or [nseq][m][n] in/out
+};
+// phase 0: partial sums; phase 1: combine into M (and S)
+hipError_t launch_ssm_momentum(const SsmMomLaunch& P, hipStream_t st, int phase);
+
 // Spectral diagnostics (a chunk of `count` matrices per launch).
 struct DiagPackLaunch {
   const void* A;       // [count][m][n], float32 or bf16 (f32)

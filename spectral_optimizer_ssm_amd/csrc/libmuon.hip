@@ -917,6 +917,56 @@ int plan_diag(int m, int n, long long batch, int dtype, int iters, DiagPlan* p) 
 
 }  // namespace
 
+namespace {
+
+// Shapes, padding, LDS split and coefficients of a factored Newton-Schulz
+// launch (pointers and the vector-load flag are the caller's).
+int factored_launch(int m, int n, int r, long long batch, const NsCoefs& C, float eps, bool dense, FactLaunch* F) {
+  if (m <= 0 || n <= 0 || r <= 0 || batch < 0) return MUON_EINVAL;
+  if (r > 8 || m > 256 || n > 256) return MUON_EUNSUPPORTED;
+  if (dense && n % 8 != 0) return MUON_EUNSUPPORTED;
+  const int m_pad = round_up(m, 16), n_pad = round_up(n, 16);
+  int f_off = 0;
+  const int per_wave = factored_lds_per_wave(m_pad, n_pad, dense, &f_off);
+  if (per_wave > 65536) return MUON_EUNSUPPORTED;
+  F->batch = batch;
+  F->m = m; F->n = n; F->r = r; F->m_pad = m_pad; F->n_pad = n_pad;
+  F->waves = std::max(1, std::min(4, 65536 / per_wave));
+  F->per_wave = per_wave;
+  F->f_off = f_off;
+  F->steps = C.steps;
+  F->eps = eps;
+  for (int k = 0; k < C.steps; ++k) { F->a[k] = C.a[k]; F->b[k] = C.b[k]; F->c[k] = C.c[k]; }
+  return MUON_OK;
+}
+
+bool overlaps(const char* a, size_t na, const char* b, size_t nb) { return a < b + nb && b < a + na; }
+
+// Workspace of the momentum pathway: the cores, the per-chunk partial sums
+// (two 64 x 128 float32 tiles each) and the chunk coefficients.
+struct SsmMomPlan {
+  int nchunks = 0;
+  size_t off_c = 0, off_part = 0, off_coef = 0, end = 0;
+};
+int plan_ssm_momentum(int m, int n, int r, long long nseq, int T, SsmMomPlan* p) {
+  if (m <= 0 || n <= 0 || r <= 0 || nseq < 0 || T < 0) return MUON_EINVAL;
+  if (r != 8 || m > 64 || n > 128) return MUON_EUNSUPPORTED;
+  p->nchunks = (T + kSsmMomQ - 1) / kSsmMomQ;
+  const long long wgs = nseq * p->nchunks;
+  if (wgs > (1LL << 31) - 1 || nseq * m * n / 256 > (1LL << 31) - 1) return MUON_EUNSUPPORTED;
+  size_t off = 0;
+  p->off_c = off;
+  off = align_up(off + static_cast<size_t>(nseq) * T * 64 * sizeof(float), kAlign);
+  p->off_part = off;
+  off = align_up(off + static_cast<size_t>(wgs) * 2 * 64 * 128 * sizeof(float), kAlign);
+  p->off_coef = off;
+  off = align_up(off + static_cast<size_t>(wgs) * 4 * sizeof(float), kAlign);
+  p->end = std::max<size_t>(off, kAlign);
+  return MUON_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* muon_status_string(int status) {
@@ -1173,12 +1223,9 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
   if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_EINVAL;
   if (m <= 0 || n <= 0 || r <= 0 || batch < 0) return MUON_EINVAL;
   if (dtype != MUON_BF16 || cfg->precision != MUON_BF16) return MUON_EUNSUPPORTED;
-  if (r > 8 || m > 256 || n > 256) return MUON_EUNSUPPORTED;
-  if (O_out != nullptr && n % 8 != 0) return MUON_EUNSUPPORTED;
-  const int m_pad = round_up(m, 16), n_pad = round_up(n, 16);
-  int f_off = 0;
-  const int per_wave = factored_lds_per_wave(m_pad, n_pad, O_out != nullptr, &f_off);
-  if (per_wave > 65536) return MUON_EUNSUPPORTED;
+  FactLaunch F{};
+  rc = factored_launch(m, n, r, batch, C, cfg->eps, O_out != nullptr, &F);
+  if (rc != MUON_OK) return rc;
   if (batch == 0) return MUON_OK;
   if (V == nullptr || K == nullptr || C_out == nullptr || !aligned_to(V, 2) || !aligned_to(K, 2) ||
       !aligned_to(C_out, 4) || (O_out != nullptr && !aligned16(O_out)))
@@ -1188,29 +1235,102 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
   const char* cb = reinterpret_cast<const char*>(C_out);
   const size_t vbytes = static_cast<size_t>(batch) * m * r * 2, kbytes = static_cast<size_t>(batch) * n * r * 2;
   const size_t cbytes = static_cast<size_t>(batch) * r * r * 4;
-  auto overlap = [](const char* a, size_t na, const char* b, size_t nb) { return a < b + nb && b < a + na; };
-  if (overlap(cb, cbytes, vb, vbytes) || overlap(cb, cbytes, kb, kbytes)) return MUON_EINVAL;
+  if (overlaps(cb, cbytes, vb, vbytes) || overlaps(cb, cbytes, kb, kbytes)) return MUON_EINVAL;
   if (O_out != nullptr) {
     const char* ob = static_cast<const char*>(O_out);
     const size_t obytes = static_cast<size_t>(batch) * m * n * 2;
-    if (overlap(ob, obytes, vb, vbytes) || overlap(ob, obytes, kb, kbytes) || overlap(ob, obytes, cb, cbytes))
+    if (overlaps(ob, obytes, vb, vbytes) || overlaps(ob, obytes, kb, kbytes) || overlaps(ob, obytes, cb, cbytes))
       return MUON_EINVAL;
   }
-  FactLaunch F{};
   F.V = static_cast<const bf16_t*>(V);
   F.K = static_cast<const bf16_t*>(K);
   F.C = C_out;
   F.O = static_cast<bf16_t*>(O_out);
-  F.batch = batch;
-  F.m = m; F.n = n; F.r = r; F.m_pad = m_pad; F.n_pad = n_pad;
   F.vec = r == 8 && aligned16(V) && aligned16(K);
-  F.waves = std::max(1, std::min(4, 65536 / per_wave));
-  F.per_wave = per_wave;
-  F.f_off = f_off;
-  F.steps = C.steps;
-  F.eps = cfg->eps;
-  for (int k = 0; k < C.steps; ++k) { F.a[k] = C.a[k]; F.b[k] = C.b[k]; F.c[k] = C.c[k]; }
   return launch_ns_factored(F, static_cast<hipStream_t>(stream)) == hipSuccess ? MUON_OK : MUON_EHIP;
+}
+
+size_t muon_ssm_momentum_workspace_size(int m, int n, int r, long long nseq, int T) {
+  SsmMomPlan p;
+  return plan_ssm_momentum(m, n, r, nseq, T, &p) == MUON_OK ? p.end : 0;
+}
+
+int muon_ssm_momentum_timed(const void* V, const void* K, int dtype, int m, int n, int r, long long nseq, int T,
+                            float beta, const float* decay, float* M, float* S, const muon_ns_cfg* cfg,
+                            void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents) {
+  NsCoefs C;
+  int rc = parse_cfg(cfg, &C, true);
+  if (rc != MUON_OK) return rc;
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_EINVAL;
+  if (dtype != MUON_BF16 || cfg->precision != MUON_BF16) return MUON_EUNSUPPORTED;
+  SsmMomPlan p;
+  rc = plan_ssm_momentum(m, n, r, nseq, T, &p);
+  if (rc != MUON_OK) return rc;
+  if (!std::isfinite(beta)) return MUON_EINVAL;
+  FactLaunch F{};
+  rc = factored_launch(m, n, r, nseq * T, C, cfg->eps, false, &F);
+  if (rc != MUON_OK) return rc;
+  if (events != nullptr && nevents < 4) return MUON_EINVAL;
+  if (nseq == 0 || T == 0) return MUON_OK;
+  if (V == nullptr || K == nullptr || M == nullptr || !aligned16(V) || !aligned16(K) || !aligned_to(M, 4) ||
+      (S != nullptr && (decay == nullptr || !aligned_to(S, 4) || !aligned_to(decay, 4))))
+    return MUON_EINVAL;
+  const size_t tokens = static_cast<size_t>(nseq) * T;
+  const size_t sbytes = static_cast<size_t>(nseq) * m * n * 4;
+  const char* vb = static_cast<const char*>(V);
+  const char* kb = static_cast<const char*>(K);
+  const char* mb = reinterpret_cast<const char*>(M);
+  const size_t vbytes = tokens * m * r * 2, kbytes = tokens * n * r * 2;
+  if (overlaps(mb, sbytes, vb, vbytes) || overlaps(mb, sbytes, kb, kbytes)) return MUON_EINVAL;
+  if (S != nullptr) {
+    const char* sb = reinterpret_cast<const char*>(S);
+    const char* db = reinterpret_cast<const char*>(decay);
+    if (overlaps(sb, sbytes, vb, vbytes) || overlaps(sb, sbytes, kb, kbytes) || overlaps(sb, sbytes, mb, sbytes) ||
+        overlaps(sb, sbytes, db, tokens * 4) || overlaps(mb, sbytes, db, tokens * 4))
+      return MUON_EINVAL;
+  }
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < p.end) return MUON_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  for (const auto& b : {std::make_pair(vb, vbytes), std::make_pair(kb, kbytes), std::make_pair(mb, sbytes)})
+    if (overlaps(ws, p.end, b.first, b.second)) return MUON_EINVAL;
+  if (S != nullptr && (overlaps(ws, p.end, reinterpret_cast<const char*>(S), sbytes) ||
+                       overlaps(ws, p.end, reinterpret_cast<const char*>(decay), tokens * 4)))
+    return MUON_EINVAL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  EventRec E;
+  E.ev = events;
+  E.n = nevents;
+  if (!E.mark(st, 0)) return MUON_EHIP;
+  // 1. the Newton-Schulz core of every token's injection
+  F.V = static_cast<const bf16_t*>(V);
+  F.K = static_cast<const bf16_t*>(K);
+  F.C = reinterpret_cast<float*>(ws + p.off_c);
+  F.O = nullptr;
+  F.vec = 1;
+  if (launch_ns_factored(F, st) != hipSuccess || !E.mark(st, 0)) return MUON_EHIP;
+  // 2. per-chunk partial sums, 3. chunk maps applied in token order
+  SsmMomLaunch L{};
+  L.V = static_cast<const bf16_t*>(V);
+  L.K = static_cast<const bf16_t*>(K);
+  L.C = F.C;
+  L.a = S != nullptr ? decay : nullptr;
+  L.beta = beta;
+  L.m = m; L.n = n; L.T = T; L.Q = kSsmMomQ; L.nchunks = p.nchunks;
+  L.nseq = nseq;
+  L.part = reinterpret_cast<float*>(ws + p.off_part);
+  L.coef = reinterpret_cast<float*>(ws + p.off_coef);
+  L.M = M;
+  L.S = S;
+  if (launch_ssm_momentum(L, st, 0) != hipSuccess || !E.mark(st, 0)) return MUON_EHIP;
+  if (launch_ssm_momentum(L, st, 1) != hipSuccess || !E.mark(st, 0)) return MUON_EHIP;
+  return MUON_OK;
+}
+
+int muon_ssm_momentum(const void* V, const void* K, int dtype, int m, int n, int r, long long nseq, int T, float beta,
+                      const float* decay, float* M, float* S, const muon_ns_cfg* cfg, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return muon_ssm_momentum_timed(V, K, dtype, m, n, r, nseq, T, beta, decay, M, S, cfg, workspace,
+                                 workspace_bytes, stream, nullptr, 0);
 }
 
 size_t muon_spectral_diag_workspace_size(int m, int n, long long batch, int dtype, int iters) {

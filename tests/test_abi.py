@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 7
+    assert mu.muon_version() == 8
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -386,3 +386,59 @@ def test_spectral_diag_timed_needs_enough_events(mu):
     rc = L.muon_spectral_diag_timed(0x1000000, mu.MUON_BF16, 96, 200, 3, 16, 0x2000000, None, None, 0x40000000, ws,
                                     None, ev, 3)
     assert rc == -1  # one chunk needs 1 + 3 events
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("ok_empty_seq", 0), ("ok_empty_T", 0), ("r4", -2), ("m65", -2), ("n129", -2), ("m0", -1), ("f32", -2),
+    ("s_without_decay", -1), ("misaligned_v", -1), ("null_m", -1), ("overlap_ms", -1), ("overlap_ws_m", -1),
+    ("no_workspace", -3), ("small_workspace", -3), ("beta_nan", -1), ("few_events", -1), ("null_k", -1),
+])
+def test_ssm_momentum_validation(mu, case, expect):
+    """muon_ssm_momentum rejects bad arguments before any GPU work."""
+    L = mu.lib()
+    m, n, r, nseq, T = 64, 128, 8, 2, 300
+    if case == "r4":
+        r = 4
+    if case == "m65":
+        m = 65
+    if case == "n129":
+        n = 129
+    if case == "m0":
+        m = 0
+    if case == "ok_empty_seq":
+        nseq = 0
+    if case == "ok_empty_T":
+        T = 0
+    cfg, keep = _cfg(mu, steps=1, prec=mu.MUON_F32 if case == "f32" else None)
+    dt = mu.MUON_F32 if case == "f32" else mu.MUON_BF16
+    fp = ctypes.POINTER(ctypes.c_float)
+    V = ctypes.c_void_p(0x1000000 + (8 if case == "misaligned_v" else 0))
+    K = None if case == "null_k" else ctypes.c_void_p(0x3000000)
+    M = None if case == "null_m" else ctypes.cast(ctypes.c_void_p(0x5000000), fp)
+    S = ctypes.cast(ctypes.c_void_p(0x5000000 + (1024 if case == "overlap_ms" else 0x100000)), fp)
+    dec = None if case == "s_without_decay" else ctypes.cast(ctypes.c_void_p(0x5800000), fp)
+    need = L.muon_ssm_momentum_workspace_size(max(m, 1), n, r, nseq, T) if case not in ("m0",) else 0
+    ws = None if case == "no_workspace" else ctypes.c_void_p(0x5000000 if case == "overlap_ws_m" else 0x10000000)
+    wsz = 64 if case == "small_workspace" else (1 << 30)
+    beta = float("nan") if case == "beta_nan" else 0.9
+    args = (V, K, dt, m, n, r, nseq, T, beta, dec, M, S, ctypes.byref(cfg), ws, wsz, None)
+    if case == "few_events":
+        ev = (ctypes.c_void_p * 3)()
+        rc = L.muon_ssm_momentum_timed(*args, ev, 3)
+    else:
+        rc = L.muon_ssm_momentum(*args)
+    assert rc == expect, (case, rc, need)
+
+
+def test_ssm_momentum_workspace_size(mu):
+    L = mu.lib()
+    # cores 256 B per token, two 64 x 128 float32 partials and 4 coefficients per 256-token chunk
+    nseq, T = 3, 600
+    chunks = 3
+    expect = 0
+    for b in (nseq * T * 256, nseq * chunks * 2 * 64 * 128 * 4, nseq * chunks * 16):
+        expect += -(-b // 256) * 256
+    assert L.muon_ssm_momentum_workspace_size(64, 128, 8, nseq, T) == expect
+    assert L.muon_ssm_momentum_workspace_size(64, 128, 4, nseq, T) == 0
+    assert L.muon_ssm_momentum_workspace_size(64, 129, 8, nseq, T) == 0
+    assert L.muon_ssm_momentum_workspace_size(64, 128, 8, 0, 0) > 0

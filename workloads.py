@@ -258,6 +258,34 @@ def injections(batch: int = INJ_BATCH, device="cpu", seed: int = 4,
 
 
 # ----------------------------------------------------------------------------
+# Sequences for the momentum pathway (MuonSSM, momentum-augmented state update)
+# ----------------------------------------------------------------------------
+SSM_SEQS = 8 * 24                   # batch 8 x 24 heads
+SSM_T = 2048                        # tokens per sequence (8 x 2048 x 24 injections, as above)
+SSM_BETA = 0.875                    # momentum coefficient (exact in float32; the pages give none)
+
+
+def ssm_sequences(nseq: int = SSM_SEQS, T: int = SSM_T, m: int = INJ_SHAPE[0], n: int = INJ_SHAPE[1],
+                  r: int = INJ_RANK, seed: int = 8, device="cpu"):
+    """Inputs of the momentum pathway: V [nseq, T, m, r] and K [nseq, T, n, r]
+    bf16 (N(0,1) in float32 -> bf16), per-token decays a [nseq, T] float32
+    uniform in [0.85, 1) (the range of a selective SSM's per-token decay
+    exp(-dt A) for small steps), and initial states M0, S0 [nseq, m, n]
+    float32 N(0, 0.1).  A torch.Generator(device).manual_seed(seed) draws V,
+    K, a, M0, S0 in that order; as for the injections, CPU and GPU streams
+    differ."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    V = torch.randn((nseq, T, m, r), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    K = torch.randn((nseq, T, n, r), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    a = 0.85 + 0.15 * torch.rand((nseq, T), generator=g, device=device, dtype=torch.float32)
+    M0 = 0.1 * torch.randn((nseq, m, n), generator=g, device=device, dtype=torch.float32)
+    S0 = 0.1 * torch.randn((nseq, m, n), generator=g, device=device, dtype=torch.float32)
+    return V, K, a, M0, S0
+
+
+# ----------------------------------------------------------------------------
 # The Mamba-2-130M parameters outside the Muon groups (AdamW companion)
 # ----------------------------------------------------------------------------
 def mamba2_adamw_shapes(layers: int = 24, d_model: int = 768, d_inner: int = 1536, d_state: int = 128,
