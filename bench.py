@@ -516,6 +516,14 @@ def cpu_baseline_injections(X, steps_ns, budget_s=15.0):
 # ----------------------------------------------------------------------------
 # exploration workloads
 # ----------------------------------------------------------------------------
+def traffic_key(args):
+    """The workload name under which counter runs are stored: the injections
+    carry their shape when it is not the default 64 x 128."""
+    if args.workload == "injections" and tuple(args.inj_shape) != (64, 128):
+        return f"injections_{args.inj_shape[0]}x{args.inj_shape[1]}"
+    return args.workload
+
+
 def small_bf16_kernel(m, n):
     """The on-chip kernel muon_ns_batched_small launches for a bf16 m x n
     stack (m <= n): one wave per matrix for s = 32 with l <= 256 and s = 64
@@ -550,7 +558,7 @@ def bench_injections(args, torch, mu, wl):
     tflops = flops / (kms * 1e-3) / 1e12
     kernel = small_bf16_kernel(m, n)
     default = (m, n) == (64, 128)
-    wname = "injections" if default else f"injections_{m}x{n}"
+    wname = traffic_key(args)
     traffic = measured_traffic(kernel.split("<")[0], wname, ["ns_small.hip", "common.cuh"])
     # the bound whose peak the kernel's algorithmic work would take longer to reach
     if nbytes / PEAK_HBM_GBS >= flops / 1e3 / PEAK_BF16_TFLOPS:
@@ -663,8 +671,9 @@ def bench_ssm_momentum(args, torch, mu, wl):
     tokens = nseq * T
     chunks = -(-T // 256)
     fb = (m + n) * r * 2                      # the factors of one token
-    alg = {"ns_factored_kernel": tokens * (fb + r * r * 4),
-           "ssm_momentum_accum_kernel": tokens * (fb + r * r * 4 + 4) + nseq * chunks * 2 * 64 * 128 * 4,
+    wb = m * r * 2                            # its W = V C (bf16), written by the core pass
+    alg = {"ns_factored_kernel": tokens * (fb + wb),
+           "ssm_momentum_accum_kernel": tokens * (wb + n * r * 2 + 4) + nseq * chunks * 2 * 64 * 128 * 4,
            "ssm_momentum_combine_kernel": nseq * (4 * m * n * 4 + chunks * 2 * 64 * 128 * 4)}
     dom = max(names, key=lambda nm: dur[nm])
     gbs = alg[dom] / (dur[dom] * 1e-3) / 1e9
@@ -677,8 +686,7 @@ def bench_ssm_momentum(args, torch, mu, wl):
                                    f" {args.ns_steps} NS step, beta {beta}, fp32 M and S"},
             "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic(dom, "ssm_momentum", ["ssm_momentum.hip", "ns_factored.hip",
-                                                                           "common.cuh"])},
+                         "traffic": measured_traffic(dom, "ssm_momentum", COUNTED_KERNELS["ssm_momentum"][dom][1])},
             "kernels": kernels}
 
 
@@ -813,7 +821,12 @@ COUNTED_KERNELS = {
                   "momentum_tall_kernel": ("momentum_tall_kernel", ELEMENTWISE),
                   "apply_wide_kernel": ("apply_wide_kernel", ELEMENTWISE),
                   "apply_tall_kernel": ("apply_tall_kernel", ELEMENTWISE)},
-    "injections": {"ns_small_bf16_kernel": ("ns_small_bf16_kernel", ["ns_small.hip", "common.cuh"])},
+    "injections": {"ns_small_bf16_kernel": ("ns_small_bf16_kernel", ["ns_small.hip", "common.cuh"]),
+                   "ns_small_bf16_wg_kernel": ("ns_small_bf16_wg_kernel", ["ns_small.hip", "common.cuh"])},
+    "ssm_momentum": {"ns_factored_kernel": ("ns_factored_kernel", ["ns_factored.hip", "common.cuh"]),
+                     "ssm_momentum_accum_kernel": ("ssm_momentum_accum_kernel", ["ssm_momentum.hip", "common.cuh"]),
+                     "ssm_momentum_combine_kernel": ("ssm_momentum_combine_kernel",
+                                                     ["ssm_momentum.hip", "common.cuh"])},
     "injections_factored": {"ns_factored_kernel": ("ns_factored_kernel", ["ns_factored.hip", "common.cuh"])},
 }
 
@@ -854,7 +867,7 @@ def main():
                     help="store HBM bytes per launch from two rocprofv3 counter runs of --workload")
     args = ap.parse_args()
     if args.ingest:
-        ingest_counters(*args.ingest, args.workload, COUNTED_KERNELS[args.workload])
+        ingest_counters(*args.ingest, traffic_key(args), COUNTED_KERNELS[args.workload])
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the Muon step here has no "

@@ -204,8 +204,9 @@ hipError_t launch_ns_small(const NsSmallLaunch& L, bool bf16, hipStream_t st);
 struct FactLaunch {
   const bf16_t* V;     // [batch][m][r]
   const bf16_t* K;     // [batch][n][r]
-  float* C;            // [batch][r][r]
+  float* C;            // [batch][r][r], or null
   bf16_t* O;           // [batch][m][n] or null
+  bf16_t* W;           // [batch][m][8] = V C (r == 8), or null
   long long batch;
   int m, n, r, m_pad, n_pad;  // pads: multiples of 16
   int vec;             // r == 8 and 16-byte aligned factors: 16-byte row loads
@@ -215,7 +216,8 @@ struct FactLaunch {
   float eps;
   float a[64], b[64], c[64];
 };
-int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off = nullptr);
+// keep_v: the staged V rows stay intact for the W output
+int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off = nullptr, bool keep_v = false);
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st);
 
 // Momentum pathway over sequences of factored injections (ssm_momentum.hip):
@@ -225,7 +227,7 @@ constexpr int kSsmMomQ = 256;
 struct SsmMomLaunch {
   const bf16_t* V;     // [nseq][T][m][8]
   const bf16_t* K;     // [nseq][T][n][8]
-  const float* C;      // [nseq][T][8][8] Newton-Schulz cores
+  const bf16_t* W;     // [nseq][T][m][8] V C, the factor of each token's NS result
   const float* a;      // [nseq][T] decays (with S)
   float beta;
   int m, n, T, Q, nchunks;  // m <= 64, n <= 128, Q tokens per chunk

@@ -267,12 +267,42 @@ __device__ __forceinline__ void factored_compute(const FactLaunch& F, const Wave
   }
 
   // 5. the core, r x r float32 per matrix
-  if (q < nm && i < r) {
+  if (F.C != nullptr && q < nm && i < r) {
     const float* C = L.mat(q, kC);
     float* dst = F.C + (b0 + q) * r * r + i * r;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (j0 + e < r) dst[j0 + e] = C[i * 8 + j0 + e];
+  }
+  // 5'. W = V C (bf16, m x 8) for the momentum pathway: lane p of matrix q
+  // forms rows p, p + 16, ... from the staged V rows (kept: the work
+  // matrices sit over the staged K rows in this mode)
+  if (F.W != nullptr) {
+    const float* C = L.mat(q, kC);
+    const int p = lane & 15;
+    if (q < nm) {
+      for (int t = p; t < m; t += 16) {
+        const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(L.vk + t * kRow + 16 * q);
+        float v[8];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          v[2 * h] = lo_bf16(vv[h]);
+          v[2 * h + 1] = hi_bf16(vv[h]);
+        }
+        float o[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[c] = fmaf(v[d], C[d * 8 + c], o[c]);
+        u32x4_t w;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) w[h] = pack_bf16x2(o[2 * h], o[2 * h + 1]);
+        *reinterpret_cast<u32x4_t*>(F.W + ((b0 + q) * m + t) * 8) = w;
+      }
+    }
+    wave_sync();  // V read before the next group is staged
   }
   if (F.O == nullptr) return;
 
@@ -329,8 +359,16 @@ __device__ __forceinline__ void factored_compute(const FactLaunch& F, const Wave
 // the Gram has read the staged factors before the recurrence writes them, and
 // the next group is staged only after the core has been stored (one wave, LDS
 // operations in order).
-int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off) {
+int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off, bool keep_v) {
   const int stage = (m_pad + n_pad) * kRow, work = kMats * 6 * 64 * 4;
+  if (keep_v && !dense && n_pad * kRow >= work) {  // work matrices over the staged K rows
+    if (f_off) *f_off = m_pad * kRow;
+    return stage;
+  }
+  if (keep_v && !dense) {
+    if (f_off) *f_off = stage;
+    return stage + work;
+  }
   if (!dense) {
     if (f_off) *f_off = 0;
     return stage > work ? stage : work;

@@ -5,11 +5,11 @@
 // memory state S_t a momentum state M_t accumulates the Newton-Schulz
 // conditioned injections, and the pair follows a block-affine recurrence.
 // Read as heavy-ball momentum on the memory:
-//   U_t = NS(V_t K_t^T) = V_t C_t K_t^T   (r x r core C_t, ns_factored.hip)
+//   U_t = NS(V_t K_t^T) = V_t C_t K_t^T = W_t K_t^T   (r x r core C_t, ns_factored.hip)
 //   M_t = beta M_{t-1} + U_t,   S_t = a_t S_{t-1} + M_t.
 // The dense U_t (16 KB for a 64 x 128 injection) never reaches memory: the
-// cores come from the factored kernel (256 B per token) and this file turns
-// the recurrence into weighted sums of rank-r products.
+// factored kernel writes W_t = V_t C_t (1 KB per token) and this file turns
+// the recurrence into weighted sums of rank-r products W_t K_t^T.
 //
 // Chunks.  Over a chunk of L tokens u = 0..L-1 entered with (S, M):
 //   M' = beta^L M + sum_u beta^(L-1-u) U_u
@@ -22,26 +22,23 @@
 //
 // Accumulation kernel: one workgroup of 4 waves per (sequence, chunk), the
 // 64 x 128 state tile (zero padded) split into four 32-column blocks, one per
-// wave.  Per sub-batch of 16 tokens the workgroup forms W_u = V_u C_u (64 x 8,
-// float32 FMAs, every row once) scaled by the token's two weights, rounds it
-// to bf16 in LDS, and each wave accumulates
-//   P[i][j] += sum_{u, r} (w_u W_u)[i][r] K_u[j][r]
-// on v_mfma_f32_32x32x16_bf16: the contraction index is (token pair, rank),
-// its A operand a 16-byte LDS row of W, its B operand a 16-byte row of K
-// straight from memory.
+// wave.  The factored kernel has written W_u = V_u C_u (m x 8 bf16) for every
+// token, so
+//   P[i][j] += sum_{u, r} W_u[i][r] (w_u K_u[j][r])
+// runs on v_mfma_f32_32x32x16_bf16 with the contraction index (token pair,
+// rank): each lane loads its two 16-byte rows of W and its 16-byte row of K
+// straight from memory, scales the K row by the token's weight (one per
+// partial sum) and rounds it to bf16.  No LDS staging and no barriers in the
+// token loop; the four waves read the same W rows (L2 serves three of them).
 #include "common.cuh"
 #include "launch.h"
 
 namespace muon {
 namespace {
 
-constexpr int kSub = 16;        // tokens per sub-batch
 constexpr int kTileM = 64, kTileN = 128, kTile = kTileM * kTileN;
 
 __global__ void __launch_bounds__(256) ssm_momentum_accum_kernel(SsmMomLaunch P) {
-  __shared__ __attribute__((aligned(16))) float cs[kSub][64];
-  __shared__ __attribute__((aligned(16))) bf16_t wm[kSub][kTileM][8];
-  __shared__ __attribute__((aligned(16))) bf16_t wsh[kSub][kTileM][8];
   __shared__ float wgt[2][kSsmMomQ];
   __shared__ float dec[kSsmMomQ];
   const int tid = threadIdx.x;
@@ -70,92 +67,47 @@ __global__ void __launch_bounds__(256) ssm_momentum_accum_kernel(SsmMomLaunch P)
       }
     }
     float* cf = P.coef + (seq * P.nchunks + ch) * 4;
-    cf[0] = wmv;                        // beta^L
-    cf[1] = with_s ? g : 0.0f;          // A = prod a
+    cf[0] = wmv;                          // beta^L
+    cf[1] = with_s ? g : 0.0f;            // A = prod a
     cf[2] = with_s ? P.beta * ws : 0.0f;  // B = beta w_0
     cf[3] = 0.0f;
   }
+  __syncthreads();
 
-  const bf16_t* Vs = P.V + tok0 * P.m * 8;
+  const bf16_t* Ws = P.W + tok0 * P.m * 8;
   const bf16_t* Ks = P.K + tok0 * P.n * 8;
-  const float* Cs = P.C + tok0 * 64;
   f32x16_t accM[2], accS[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) accM[rb][r] = accS[rb][r] = 0.0f;
   const int col = 32 * w + l32;
-  const int tt = tid >> 4, rsub = tid & 15;  // W rows: token tt, rows rsub + 16 e
-
-  for (int tb = 0; tb < len; tb += kSub) {
-    const int nt = len - tb < kSub ? len - tb : kSub;
-    // loads: the core (16 B per thread), this thread's 4 rows of V, and the
-    // wave's K rows for the 8 token pairs (token tb + 2 p + G, row col)
-    f32x4_t cv = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (tt < nt) cv = *reinterpret_cast<const f32x4_t*>(Cs + static_cast<long long>(tb + tt) * 64 + 4 * rsub);
-    u32x4_t vr[4];
+  const bool row0 = l32 < P.m, row1 = l32 + 32 < P.m, colok = col < P.n;
+  auto scaled = [](const u32x4_t& k, float s) {
+    u32x4_t o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = rsub + 16 * e;
-      vr[e] = u32x4_t{0u, 0u, 0u, 0u};
-      if (tt < nt && row < P.m)
-        vr[e] = *reinterpret_cast<const u32x4_t*>(Vs + (static_cast<long long>(tb + tt) * P.m + row) * 8);
+    for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(lo_bf16(k[h]) * s, hi_bf16(k[h]) * s);
+    return __builtin_bit_cast(bf16x8_t, o);
+  };
+#pragma unroll 4
+  for (int tp = 0; tp < len; tp += 2) {
+    const int t = tp + G;
+    const bool ok = t < len;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const long long wt = static_cast<long long>(t) * P.m, kt = static_cast<long long>(t) * P.n;
+    const u32x4_t a0 = (ok && row0) ? *reinterpret_cast<const u32x4_t*>(Ws + (wt + l32) * 8) : z;
+    const u32x4_t a1 = (ok && row1) ? *reinterpret_cast<const u32x4_t*>(Ws + (wt + l32 + 32) * 8) : z;
+    const u32x4_t kv = (ok && colok) ? *reinterpret_cast<const u32x4_t*>(Ks + (kt + col) * 8) : z;
+    const float sm = ok ? wgt[0][t] : 0.0f;
+    const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, a0), A1 = __builtin_bit_cast(bf16x8_t, a1);
+    const bf16x8_t km = scaled(kv, sm);
+    accM[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, km, accM[0], 0, 0, 0);
+    accM[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, km, accM[1], 0, 0, 0);
+    if (with_s) {
+      const bf16x8_t ks = scaled(kv, ok ? wgt[1][t] : 0.0f);
+      accS[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, ks, accS[0], 0, 0, 0);
+      accS[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, ks, accS[1], 0, 0, 0);
     }
-    u32x4_t kf[kSub / 2];
-#pragma unroll
-    for (int p = 0; p < kSub / 2; ++p) {
-      const int t = 2 * p + G;
-      kf[p] = u32x4_t{0u, 0u, 0u, 0u};
-      if (t < nt && col < P.n)
-        kf[p] = *reinterpret_cast<const u32x4_t*>(Ks + (static_cast<long long>(tb + t) * P.n + col) * 8);
-    }
-    *reinterpret_cast<f32x4_t*>(&cs[tt][4 * rsub]) = cv;
-    __syncthreads();  // cores staged (and the weights, on the first pass)
-
-    // W = V C for 4 rows of token tt, scaled by the token's two weights
-    const float sm = tt < nt ? wgt[0][tb + tt] : 0.0f;
-    const float ss = (with_s && tt < nt) ? wgt[1][tb + tt] : 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v[8];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        v[2 * h] = lo_bf16(vr[e][h]);
-        v[2 * h + 1] = hi_bf16(vr[e][h]);
-      }
-      float o[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = fmaf(v[r], cs[tt][r * 8 + c], o[c]);
-      const int row = rsub + 16 * e;
-      u32x4_t pm, ps;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        pm[h] = pack_bf16x2(o[2 * h] * sm, o[2 * h + 1] * sm);
-        ps[h] = pack_bf16x2(o[2 * h] * ss, o[2 * h + 1] * ss);
-      }
-      *reinterpret_cast<u32x4_t*>(&wm[tt][row][0]) = pm;
-      if (with_s) *reinterpret_cast<u32x4_t*>(&wsh[tt][row][0]) = ps;
-    }
-    __syncthreads();  // W of the sub-batch staged
-
-#pragma unroll
-    for (int p = 0; p < kSub / 2; ++p) {
-      const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kf[p]);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const bf16x8_t am = *reinterpret_cast<const bf16x8_t*>(&wm[2 * p + G][32 * rb + l32][0]);
-        accM[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, kb, accM[rb], 0, 0, 0);
-        if (with_s) {
-          const bf16x8_t as = *reinterpret_cast<const bf16x8_t*>(&wsh[2 * p + G][32 * rb + l32][0]);
-          accS[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as, kb, accS[rb], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();  // every wave has read the sub-batch before it is replaced
   }
 
   // partials: lane (G, l32), register 4 q + e holds row 32 rb + 8 q + 4 G + e,

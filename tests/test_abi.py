@@ -432,11 +432,11 @@ def test_ssm_momentum_validation(mu, case, expect):
 
 def test_ssm_momentum_workspace_size(mu):
     L = mu.lib()
-    # cores 256 B per token, two 64 x 128 float32 partials and 4 coefficients per 256-token chunk
+    # V C per token (64 x 8 bf16), two 64 x 128 float32 partials and 4 coefficients per 256-token chunk
     nseq, T = 3, 600
     chunks = 3
     expect = 0
-    for b in (nseq * T * 256, nseq * chunks * 2 * 64 * 128 * 4, nseq * chunks * 16):
+    for b in (nseq * T * 64 * 8 * 2, nseq * chunks * 2 * 64 * 128 * 4, nseq * chunks * 16):
         expect += -(-b // 256) * 256
     assert L.muon_ssm_momentum_workspace_size(64, 128, 8, nseq, T) == expect
     assert L.muon_ssm_momentum_workspace_size(64, 128, 4, nseq, T) == 0
