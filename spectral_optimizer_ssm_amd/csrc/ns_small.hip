@@ -5,7 +5,8 @@
 // every token and head; its ablation on the number of Newton-Schulz steps
 // compares one step with five.  Each matrix (s x l, s <= 128) is loaded once,
 // normalised by its Frobenius norm, iterated in LDS and registers, and stored
-// once, so the pass streams HBM exactly once each way.
+// once, so the pass streams HBM exactly once each way (non-temporal loads and
+// stores: the matrices are touched once).
 //
 // bf16 kernel (s = 32 with l <= 256, s = 64 with l <= 128): one wavefront per
 // matrix, several matrices per workgroup.
@@ -22,7 +23,7 @@
 //    order) and leaves through coalesced 16-byte stores.
 // Larger bf16 shapes (s up to 128, l up to 512): one matrix per workgroup of
 // s / 32 waves (ns_small_bf16_wg_kernel).
-// fp32 kernel: one workgroup per matrix, register-blocked FMA products in LDS.
+// fp32 kernel: one workgroup per matrix, products on the fp32 matrix cores.
 #include "common.cuh"
 #include "launch.h"
 
@@ -87,7 +88,7 @@ ns_small_bf16_kernel(NsSmallLaunch P) {
     for (int p = 0; p < Geo::CHUNKS / 64; ++p) {
       const int q = lane + 64 * p;
       const int r = q / Geo::CPR, c = q % Geo::CPR;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8);
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float a = lo_bf16(v[e]), b = hi_bf16(v[e]);
@@ -210,7 +211,7 @@ ns_small_bf16_kernel(NsSmallLaunch P) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(lo_bf16(v[e]) * inv, hi_bf16(v[e]) * inv);
       }
-      *reinterpret_cast<u32x4_t*>(dst + static_cast<long long>(r) * P.ld_out + c * 8) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + static_cast<long long>(r) * P.ld_out + c * 8));
     }
     wave_lds_sync();  // the next matrix overwrites this region
   }
@@ -291,7 +292,7 @@ __global__ void __launch_bounds__(256) ns_small_bf16_wg_kernel(NsSmallLaunch P) 
         const int q = q0 + e * NT;
         if (q < chunks) {
           const int r = q / geo.cpr, c = q - r * geo.cpr;
-          v[e] = *reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8);
+          v[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8));
         }
       }
 #pragma unroll
@@ -430,7 +431,7 @@ __global__ void __launch_bounds__(256) ns_small_bf16_wg_kernel(NsSmallLaunch P) 
 #pragma unroll
             for (int t = 0; t < 4; ++t) o[t] = pack_bf16x2(lo_bf16(o[t]) * inv, hi_bf16(o[t]) * inv);
           }
-          *reinterpret_cast<u32x4_t*>(dst + static_cast<long long>(r) * P.ld_out + c * 8) = o;
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(dst + static_cast<long long>(r) * P.ld_out + c * 8));
         }
       }
     }
@@ -442,28 +443,41 @@ constexpr int kRtMaxL = 512;
 constexpr int kMaxLds = 160 * 1024;
 
 // ---- float32: one workgroup per matrix --------------------------------------
+// fp32: one workgroup of four waves per matrix on the fp32 matrix cores
+// (v_mfma_f32_32x32x2f32: fp32 products, fp32 accumulation).  X (s x l, s <=
+// 64, l <= LMAX) sits in LDS zero-padded to multiples of 32 on both sides; the
+// Gram's 32 x 32 blocks go to the four waves (block (w / 2, w % 2)), then the
+// combine's blocks (row block, column block w, w + 4, ...).  Operands are one
+// float per lane per MFMA: A[i][k] from lane (k % 2) * 32 + i, B[k][j] from
+// lane (k % 2) * 32 + j; the result's lane l holds column l % 32, rows
+// 8 q + 4 (l / 32) + e in register 4 q + e.
 template <int LMAX>
 __global__ void __launch_bounds__(256) ns_small_f32_kernel(NsSmallLaunch P) {
-  constexpr int SMAX = 64;
-  __shared__ float xa[SMAX][LMAX + 1];
-  __shared__ float xb[SMAX][LMAX + 1];
-  __shared__ float am[SMAX][SMAX + 1];
+  // odd row strides: the operands are read down columns (32 lanes, 32 rows)
+  constexpr int SMAX = 64, XS = LMAX + 1, AS = SMAX + 1;
+  __shared__ float xa[SMAX][XS];
+  __shared__ float xb[SMAX][XS];
+  __shared__ float am[SMAX][AS];
   __shared__ float red[4];
   const int S = P.s, Lw = P.l, tid = threadIdx.x;
+  const int Sp = (S + 31) & ~31, Lp = (Lw + 31) & ~31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int G = lane >> 5, l32 = lane & 31;
   for (long long mat = blockIdx.x; mat < P.count; mat += gridDim.x) {
     const float* src = static_cast<const float*>(P.X) + mat * P.in_stride;
     float* dst = static_cast<float*>(P.Y) + mat * P.out_stride;
+    // stage X, zero padded to Sp x Lp (the padding stays zero through every step)
     float ss = 0.0f;
-    for (int e = tid; e < S * Lw; e += 256) {
+    for (int e = tid; e < Sp * Lp; e += 256) {
       int i, k;
-      float v;
       if (P.transposed) {  // stored as l x s: consecutive threads read consecutive i
-        i = e % S; k = e / S;
-        v = src[static_cast<long long>(k) * P.ld_in + i];
+        i = e % Sp; k = e / Sp;
       } else {
-        i = e / Lw; k = e % Lw;
-        v = src[static_cast<long long>(i) * P.ld_in + k];
+        i = e / Lp; k = e % Lp;
       }
+      float v = 0.0f;
+      if (i < S && k < Lw)
+        v = P.transposed ? src[static_cast<long long>(k) * P.ld_in + i] : src[static_cast<long long>(i) * P.ld_in + k];
       xa[i][k] = v;
       ss = fmaf(v, v, ss);
     }
@@ -476,65 +490,53 @@ __global__ void __launch_bounds__(256) ns_small_f32_kernel(NsSmallLaunch P) {
       inv = 1.0f / (sqrtf(block_sum(ss, red)) + P.eps);
     }
     __syncthreads();
-    for (int e = tid; e < S * Lw; e += 256) xa[e / Lw][e % Lw] *= inv;
+    for (int e = tid; e < Sp * Lp; e += 256) xa[e / Lp][e % Lp] *= inv;
     __syncthreads();
-    float (*cur)[LMAX + 1] = xa;
-    float (*nxt)[LMAX + 1] = xb;
-    // register blocks: thread (ti, tj) of a 16 x 16 grid owns rows 4 ti .. 4 ti + 3
-    // and, in the Gram, columns 4 tj .. 4 tj + 3, in the combine, columns
-    // tj + 16 c (c < LMAX / 16); independent accumulators, every LDS value
-    // read once per k is used four or more times
-    constexpr int CPT = LMAX / 16;
-    const int ti = tid >> 4, tj = tid & 15;
-    const int i0 = 4 * ti, j0 = 4 * tj;
+    float (*cur)[XS] = xa;
+    float (*nxt)[XS] = xb;
+    const int nbs = Sp / 32, nbl = Lp / 32;
     for (int step = 0; step < P.steps; ++step) {
-      if (i0 < S && j0 < S) {
-        float g[4][4] = {};
-#pragma unroll 8
-        for (int k = 0; k < Lw; ++k) {
-          float xi[4], xj[4];
+      // Gram A = X X^T: block (bi, bj) per wave
+      const int bi = w >> 1, bj = w & 1;
+      if (bi < nbs && bj < nbs) {
+        f32x16_t g;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            xi[r] = i0 + r < S ? cur[i0 + r][k] : 0.0f;
-            xj[r] = j0 + r < S ? cur[j0 + r][k] : 0.0f;
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) g[r][c] = fmaf(xi[r], xj[c], g[r][c]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (i0 + r < S && j0 + c < S) am[i0 + r][j0 + c] = g[r][c];
-      }
-      __syncthreads();
-      const float a = P.a[step], b = P.b[step];
-      if (i0 < S) {
-        float y[4][CPT] = {};
+        for (int r = 0; r < 16; ++r) g[r] = 0.0f;
 #pragma unroll 4
-        for (int j = 0; j < S; ++j) {
-          float ar[4], xr[CPT];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ar[r] = i0 + r < S ? am[i0 + r][j] : 0.0f;
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) xr[c] = tj + 16 * c < Lw ? cur[j][tj + 16 * c] : 0.0f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) y[r][c] = fmaf(ar[r], xr[c], y[r][c]);
+        for (int k = 0; k < Lp; k += 2) {
+          const float av = cur[bi * 32 + l32][k + G];
+          const float bv = cur[bj * 32 + l32][k + G];
+          g = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, g, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int c = 0; c < CPT; ++c) {
-            const int i = i0 + r, k = tj + 16 * c;
-            if (i < S && k < Lw) nxt[i][k] = fmaf(a, cur[i][k], b * y[r][c]);
-          }
+          for (int e = 0; e < 4; ++e) am[bi * 32 + 8 * q + 4 * G + e][bj * 32 + l32] = g[4 * q + e];
       }
       __syncthreads();
-      float (*t)[LMAX + 1] = cur;
+      // combine Y = a X + b A X: blocks (bi, bk), bk = w, w + 4, ...
+      const float a = P.a[step], b = P.b[step];
+      for (int bk = w; bk < nbl; bk += 4)
+        for (int bi2 = 0; bi2 < nbs; ++bi2) {
+          f32x16_t y;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) y[r] = 0.0f;
+#pragma unroll 4
+          for (int j = 0; j < Sp; j += 2) {
+            const float av = am[bi2 * 32 + l32][j + G];
+            const float bv = cur[j + G][bk * 32 + l32];
+            y = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, y, 0, 0, 0);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = bi2 * 32 + 8 * q + 4 * G + e, k = bk * 32 + l32;
+              nxt[i][k] = fmaf(a, cur[i][k], b * y[4 * q + e]);
+            }
+        }
+      __syncthreads();
+      float (*t)[XS] = cur;
       cur = nxt;
       nxt = t;
     }
