@@ -527,9 +527,12 @@ def traffic_key(args):
 def small_bf16_kernel(m, n):
     """The on-chip kernel muon_ns_batched_small launches for a bf16 m x n
     stack (m <= n): one wave per matrix for s = 32 with l <= 256 and s = 64
-    with l <= 128, else one workgroup per matrix."""
+    with l <= 128, else one workgroup per matrix, its rows split over the
+    waves where X fits the 160 KB of LDS twice, its columns otherwise."""
     if (m == 32 and n <= 256) or (m == 64 and n <= 128):
         return f"ns_small_bf16_kernel<{m},{n}>"
+    if 160 * 1024 // (m * n * 2) >= 2:
+        return f"ns_small_bf16_wgr_kernel<{m}>"
     return f"ns_small_bf16_wg_kernel<{m}>"
 
 
@@ -822,7 +825,8 @@ COUNTED_KERNELS = {
                   "apply_wide_kernel": ("apply_wide_kernel", ELEMENTWISE),
                   "apply_tall_kernel": ("apply_tall_kernel", ELEMENTWISE)},
     "injections": {"ns_small_bf16_kernel": ("ns_small_bf16_kernel", ["ns_small.hip", "common.cuh"]),
-                   "ns_small_bf16_wg_kernel": ("ns_small_bf16_wg_kernel", ["ns_small.hip", "common.cuh"])},
+                   "ns_small_bf16_wg_kernel": ("ns_small_bf16_wg_kernel", ["ns_small.hip", "common.cuh"]),
+                   "ns_small_bf16_wgr_kernel": ("ns_small_bf16_wgr_kernel", ["ns_small.hip", "common.cuh"])},
     "ssm_momentum": {"ns_factored_kernel": ("ns_factored_kernel", ["ns_factored.hip", "common.cuh"]),
                      "ssm_momentum_accum_kernel": ("ssm_momentum_accum_kernel", ["ssm_momentum.hip", "common.cuh"]),
                      "ssm_momentum_combine_kernel": ("ssm_momentum_combine_kernel",

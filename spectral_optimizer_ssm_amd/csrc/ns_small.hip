@@ -22,7 +22,9 @@
 //  * Y overwrites X in LDS one 32-column block at a time (same wave, in
 //    order) and leaves through coalesced 16-byte stores.
 // Larger bf16 shapes (s up to 128, l up to 512): one matrix per workgroup of
-// s / 32 waves (ns_small_bf16_wg_kernel).
+// s / 32 waves, rows of the result split over the waves
+// (ns_small_bf16_wgr_kernel) or, for the largest, columns
+// (ns_small_bf16_wg_kernel).
 // fp32 kernel: one workgroup per matrix, products on the fp32 matrix cores.
 #include "common.cuh"
 #include "launch.h"
@@ -439,6 +441,180 @@ __global__ void __launch_bounds__(256) ns_small_bf16_wg_kernel(NsSmallLaunch P) 
   }
 }
 
+// ---- bf16, one matrix per workgroup, rows split over the waves ----
+// The variant of ns_small_bf16_wg_kernel that keeps only X in LDS, so that two
+// workgroups share a CU where X alone fits twice (128 x 256: 64 KB).  Wave w
+// accumulates column block w of the Gram, A[32 b + ..][32 w + ..], which by
+// symmetry holds, lane by lane, the combine's operand fragments for output
+// rows 32 w .. 32 w + 31 (as in ns_small_bf16_kernel, with one row block per
+// wave instead of all of them); the wave then forms those rows of Y for every
+// 32-column block, reading X's operand for the block with transposing reads.
+// A workgroup barrier per column block separates every wave's reads of the
+// block from the writes of Y into it.
+template <int S>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+ns_small_bf16_wgr_kernel(NsSmallLaunch P) {
+  extern __shared__ __attribute__((aligned(16))) char lds_dyn[];
+  __shared__ float red[8];
+  constexpr int NB = S / 32, NJ = S / 16, NT = NB * 64;
+  const int L = P.l;
+  const RtGeo geo(L);
+  const int nk = L / 32, chunks = S * geo.cpr;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  char* xs = lds_dyn;
+  const int G = lane >> 5, l32 = lane & 31;
+  const int key32 = l32 & geo.swm1, base32 = l32 * geo.row;
+  const int g4 = lane >> 4, rr = (lane >> 2) & 3, u = lane & 3;
+  int trow[2], tkey[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * h + 4 * (g4 >> 1) + rr;
+    trow[h] = r * geo.row + 8 * (u & 1);
+    tkey[h] = r & geo.swm1;
+  }
+  const int tchunk = 2 * (g4 & 1) + (u >> 1);
+  const int ybase = base32 + w * 32 * geo.row;  // this wave's output rows
+
+  for (long long mat = blockIdx.x; mat < P.count; mat += gridDim.x) {
+    const bf16_t* src = static_cast<const bf16_t*>(P.X) + mat * P.in_stride;
+    bf16_t* dst = static_cast<bf16_t*>(P.Y) + mat * P.out_stride;
+    float ss = 0.0f;
+    for (int q0 = threadIdx.x; q0 < chunks; q0 += 8 * NT) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+          v[e] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float x0 = lo_bf16(v[e][t]), x1 = hi_bf16(v[e][t]);
+            ss = fmaf(x0, x0, ss);
+            ss = fmaf(x1, x1, ss);
+          }
+          *reinterpret_cast<u32x4_t*>(xs + geo.chunk_off(r, c)) = v[e];
+        }
+      }
+    }
+    float tot;
+    if (P.partials != nullptr) {
+      float s2 = 0.0f;
+      for (int i = threadIdx.x; i < P.P; i += NT) s2 += P.partials[mat * P.P + i];
+      tot = block_sum(s2, red);
+    } else {
+      tot = block_sum(ss, red);
+    }
+    const float inv = 1.0f / (sqrtf(tot) + P.eps);
+
+    for (int step = 0; step < P.steps; ++step) {
+      const float sc = step == 0 ? inv : 1.0f;
+      f32x16_t g[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) g[b][r] = 0.0f;
+#pragma unroll 2
+      for (int ks = 0; ks < L / 16; ++ks) {
+        const int co = ((ks * 2 + G) ^ key32) << 4;
+        bf16x8_t f[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) f[b] = *reinterpret_cast<const bf16x8_t*>(xs + base32 + b * 32 * geo.row + co);
+        bf16x8_t fw = f[0];
+#pragma unroll
+        for (int b = 1; b < NB; ++b)
+          if (b == w) fw = f[b];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) g[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[b], fw, g[b], 0, 0, 0);
+      }
+      // g[bm] lane (G, l32), register 4 q + e = A[32 bm + 8 q + 4 G + e][32 w + l32]:
+      // the B operand of the combine for output row 32 w + l32 and contraction
+      // j = 16 js + 8 h + 4 G + e (js = 2 bm + kap, q = 2 kap + h)
+      const float gs = sc * sc;
+      u32x4_t af[NJ];
+#pragma unroll
+      for (int js = 0; js < NJ; ++js) {
+        const int bm = js >> 1, kap = js & 1;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int gp = 2 * kap + h;
+          af[js][2 * h] = pack_bf16x2(g[bm][4 * gp + 0] * gs, g[bm][4 * gp + 1] * gs);
+          af[js][2 * h + 1] = pack_bf16x2(g[bm][4 * gp + 2] * gs, g[bm][4 * gp + 3] * gs);
+        }
+      }
+      const float alpha = P.a[step] * sc, beta = P.b[step] * sc;
+#pragma unroll 1
+      for (int kb = 0; kb < nk; ++kb) {
+        f32x16_t c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = 0.0f;
+        int xo[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xo[h] = trow[h] + (((kb * 4 + tchunk) ^ tkey[h]) << 4);
+#pragma unroll
+        for (int js = 0; js < NJ; ++js) {
+          const u32x2_t p0 = tr_read(xs + xo[0] + js * 16 * geo.row);
+          const u32x2_t p1 = tr_read(xs + xo[1] + js * 16 * geo.row);
+          const bf16x8_t xf = __builtin_bit_cast(bf16x8_t, u32x4_t{p0[0], p0[1], p1[0], p1[1]});
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, __builtin_bit_cast(bf16x8_t, af[js]), c, 0, 0, 0);
+        }
+        // c lane (G, l32), register 4 q + e = (A X)[32 w + l32][32 kb + 8 q + 4 G + e]
+        int yo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yo[q] = ybase + (((kb * 4 + q) ^ key32) << 4) + 8 * G;
+        u32x2_t ypk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(xs + yo[q]);
+          const float y0 = fmaf(alpha, lo_bf16(xv[0]), beta * c[4 * q + 0]);
+          const float y1 = fmaf(alpha, hi_bf16(xv[0]), beta * c[4 * q + 1]);
+          const float y2 = fmaf(alpha, lo_bf16(xv[1]), beta * c[4 * q + 2]);
+          const float y3 = fmaf(alpha, hi_bf16(xv[1]), beta * c[4 * q + 3]);
+          ypk[q] = u32x2_t{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        }
+        __syncthreads();  // every wave has read column block kb
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x2_t*>(xs + yo[q]) = ypk[q];
+      }
+      __syncthreads();  // Y complete before the next Gram or the store
+    }
+
+    for (int q0 = threadIdx.x; q0 < chunks; q0 += 4 * NT) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+          v[e] = *reinterpret_cast<const u32x4_t*>(xs + geo.chunk_off(r, c));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = q0 + e * NT;
+        if (q < chunks) {
+          const int r = q / geo.cpr, c = q - r * geo.cpr;
+          u32x4_t o = v[e];
+          if (P.steps == 0) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o[t] = pack_bf16x2(lo_bf16(o[t]) * inv, hi_bf16(o[t]) * inv);
+          }
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(dst + static_cast<long long>(r) * P.ld_out + c * 8));
+        }
+      }
+    }
+    __syncthreads();  // the next matrix overwrites X
+  }
+}
+
 constexpr int kRtMaxL = 512;
 constexpr int kMaxLds = 160 * 1024;
 
@@ -569,12 +745,32 @@ hipError_t launch_ns_small(const NsSmallLaunch& P, bool bf16, hipStream_t st) {
     return hipErrorInvalidValue;
   // one matrix per workgroup of s / 32 waves, X and A in dynamic LDS: short
   // sides above 64, long sides above 256, and 64 x 160 .. 64 x 256, where one
-  // wave per matrix holds too many accumulators for two waves per SIMD
+  // wave per matrix holds too many accumulators for two waves per SIMD.  Rows
+  // split over the waves (X alone in LDS) wherever X fits a CU twice: the
+  // same results bit for bit, 1.1-2x faster (more workgroups per CU, no A
+  // round trip); columns split (X and A) for the larger shapes, where one
+  // workgroup per CU is all either can have and the row split reads more LDS.
   if (bf16 && (P.s > 64 || P.l > 256 || (P.s == 64 && P.l >= 160))) {
-    const size_t lds = static_cast<size_t>(P.s) * P.l * 2 + static_cast<size_t>(P.s) * P.s * 2;
+    const size_t xbytes = static_cast<size_t>(P.s) * P.l * 2;
+    const size_t lds = xbytes + static_cast<size_t>(P.s) * P.s * 2;
     if (lds > static_cast<size_t>(kMaxLds)) return hipErrorInvalidValue;
     const long long blocks = small_grid(P.count, 1LL << 16);
     const dim3 grid(static_cast<unsigned>(blocks)), block(P.s * 2);
+    const bool rows = kMaxLds / xbytes >= 2;
+#define MUON_SMALL_WGR(SS)                                                                               \
+  if (P.s == SS) {                                                                                       \
+    const void* fn = reinterpret_cast<const void*>(ns_small_bf16_wgr_kernel<SS>);                        \
+    if (xbytes > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,          \
+                                              static_cast<int>(xbytes)) != hipSuccess)                   \
+      return hipErrorInvalidValue;                                                                       \
+    hipLaunchKernelGGL((ns_small_bf16_wgr_kernel<SS>), grid, block, xbytes, st, P);                      \
+    return hipGetLastError();                                                                            \
+  }
+    if (rows) {
+      MUON_SMALL_WGR(32) MUON_SMALL_WGR(64) MUON_SMALL_WGR(96) MUON_SMALL_WGR(128)
+      return hipErrorInvalidValue;
+    }
+#undef MUON_SMALL_WGR
 #define MUON_SMALL_WG(SS)                                                                                \
   if (P.s == SS) {                                                                                       \
     const void* fn = reinterpret_cast<const void*>(ns_small_bf16_wg_kernel<SS>);                         \
