@@ -117,6 +117,9 @@ def compare(W, M, Gb, U1, V1, sigma, cap, grad, out, tol, steps=5, lr=0.02):
     (64, 128, "bf16", "bf16", False),     # on-chip small kernel
     (96, 160, "f32", "f32", True),        # float32 path
     (130, 70, "bf16", "f32", False),      # bf16 gradients, float32 iterate, ragged
+    (50, 70, "bf16", "bf16", True),       # on-chip, both sides zero-padded to 64 x 96
+    (300, 96, "bf16", "bf16", False),     # on-chip, tall, rows split over the waves
+    (128, 512, "bf16", "bf16", True),     # on-chip, columns split over the waves
 ])
 def test_cap_matches_oracle(mu, m, n, grad, prec, exact):
     count = 4

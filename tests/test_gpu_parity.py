@@ -374,8 +374,9 @@ def test_many_matrices_multiple_tables(mu):
 # ---------------------------------------------------------------------------
 # degenerate inputs and invariants
 # ---------------------------------------------------------------------------
-def test_zero_gradient_leaves_weights(mu):
-    g = wl.random_group(1, 2, 256, 384, "bf16", zero_momentum=True)
+@pytest.mark.parametrize("shape", [(256, 384), (50, 70), (100, 100)])  # matrix cores; on chip, one wave / rows split
+def test_zero_gradient_leaves_weights(mu, shape):
+    g = wl.random_group(1, 2, *shape, "bf16", zero_momentum=True)
     g.G[:] = 0
     w = wl.Workload("zero", [g])
     devs, outs = run_step(mu, w)
@@ -383,8 +384,9 @@ def test_zero_gradient_leaves_weights(mu):
     assert (outs[0]["O"].float() == 0).all()
 
 
-def test_nan_propagates(mu):
-    g = wl.random_group(2, 1, 128, 256, "bf16")
+@pytest.mark.parametrize("shape", [(128, 256), (50, 70), (100, 100), (128, 512)])
+def test_nan_propagates(mu, shape):
+    g = wl.random_group(2, 1, *shape, "bf16")
     g.G[0, 3, 5] = 0x7FC0
     w = wl.Workload("nan", [g])
     devs, outs = run_step(mu, w)
