@@ -139,6 +139,24 @@ def ns_flops(s, l):
     return s * (s + 1) * l, 2 * s * s * l
 
 
+def graph_steps(torch, step, k):
+    """The step captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed k times: no host work or launch gaps between the kernels."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(k):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / k
+    return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3), "steps": k}
+
+
 def workload_for(args, wl):
     """The seeded inputs of a step workload: the full step (both projection
     groups, the headline), one projection group, or the single fp32 matrix."""
@@ -213,6 +231,7 @@ def bench_full_step(args, torch, mu, wl):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     cold = cold_cache_steps(torch, lambda: mu.muon_step(groups, workspace=ws, **opts), args.steps)
+    graph = graph_steps(torch, lambda: mu.muon_step(groups, workspace=ws, **opts), args.steps) if args.graph else None
     # per-kernel durations: the same steps again through muon_step_timed,
     # which runs the phases one after another on one stream
     evs = make_events(args.steps)
@@ -326,6 +345,7 @@ def bench_full_step(args, torch, mu, wl):
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_one_stream": round(ms_serial, 4),
         "cold_cache": cold,
+        **({"graph": graph} if graph is not None else {}),
         "ns_iters_per_s": round(steps_ns * 1e3 / ms_per_step, 2),
         "ns_tflops": round(ns_tflops, 2), "mfma_util": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
         "ns_iteration_equivalent_tflops": round(iter_flops_step / (ns_ms * 1e-3) / 1e12, 2),
@@ -863,6 +883,8 @@ def main():
                     help="full_step: Newton-Schulz schedule of the large groups")
     ap.add_argument("--separate-apply", action="store_true",
                     help="full_step: apply the update in its own pass instead of the final product's epilogue")
+    ap.add_argument("--graph", action="store_true",
+                    help="full_step: also time the step captured in a HIP graph and replayed (reported beside value)")
     ap.add_argument("--per-matrix", action="store_true",
                     help="full_step: one muon_step call per matrix instead of one grouped call")
     ap.add_argument("--copy-calibration", action="store_true",
