@@ -645,9 +645,7 @@ template <> struct SymCfg<128> { static constexpr int kWpe = 3; };  // 48 KB LDS
 template <> struct SymCfg<192> { static constexpr int kWpe = 2; };  // 72 KB LDS: two workgroups per CU
 constexpr int NTHR2 = 256;
 constexpr int SYM_NSTAGE = 3;
-#ifndef SYM_SINGLE_FRAGS_ABOVE
-#define SYM_SINGLE_FRAGS_ABOVE 4  // larger wave tiles read one fragment set per k-step
-#endif
+constexpr int kSymSingleFragsAbove = 4;  // larger wave tiles read one fragment set per k-step
 
 int sym_tile(int s_pad) { return s_pad % 192 == 0 ? 192 : 128; }
 
@@ -816,7 +814,7 @@ symprod_bf16_kernel(SymArgs G) {
         return rt ? frag_tr<TT * 2>(bb + tfb[j] + ks * 16 * TT * 2)
                   : frag_at(bb + wn * WT * 64 + roff[ks] + j * 32 * 64);
       };
-      if constexpr (FM * FN > SYM_SINGLE_FRAGS_ABOVE) stage_mma_single<FM, FN>(acc, fa, fb);
+      if constexpr (FM * FN > kSymSingleFragsAbove) stage_mma_single<FM, FN>(acc, fa, fb);
       else stage_mma<FM, FN>(acc, fa, fb);
     };
     if constexpr (TT == 192) {

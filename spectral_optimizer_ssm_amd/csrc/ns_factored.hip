@@ -32,9 +32,10 @@ namespace muon {
 namespace {
 
 constexpr int kMats = 4;          // matrices per wavefront
-#ifndef FACT_WG_PER_CU
-#define FACT_WG_PER_CU 4
-#endif
+// Persistent grid: four workgroups of four waves per CU, each walking an equal
+// share of the groups (two are resident at a time at 204 registers per lane; a
+// grid of three per CU at three waves per SIMD measured no faster).
+constexpr int kFactWgPerCu = 4;
 constexpr int kRow = 64;          // bytes per staged row (32 bf16 columns)
 
 __device__ __forceinline__ void wave_sync() {
@@ -382,7 +383,7 @@ hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st) {
   // persistent waves: a few resident workgroups per CU walk the groups
   const int cus = device_cus();
   const long long need = (groups + F.waves - 1) / F.waves;
-  const long long cap = static_cast<long long>(cus) * FACT_WG_PER_CU;
+  const long long cap = static_cast<long long>(cus) * kFactWgPerCu;
   const long long blocks = need < cap ? need : cap;
   const size_t lds = static_cast<size_t>(F.waves) * F.per_wave;
   hipLaunchKernelGGL(ns_factored_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64 * F.waves), lds, st, F);
