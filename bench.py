@@ -631,8 +631,9 @@ def bench_injections_factored(args, torch, mu, wl):
             "roofline": {"bound": "hbm", "kernel": "ns_factored_kernel", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "bytes_per_matrix": per,
-                         "traffic": measured_traffic("ns_factored_kernel", "injections_factored",
-                                                     ["ns_factored.hip", "common.cuh"])}}
+                         "traffic": measured_traffic(
+                             "ns_factored_kernel", "injections_factored",
+                             COUNTED_KERNELS["injections_factored"]["ns_factored_kernel"][1])}}
 
 
 def cpu_baseline_ssm_momentum(V, K, a, M0, S0, beta, steps_ns, budget_s=15.0):
@@ -679,7 +680,7 @@ def bench_ssm_momentum(args, torch, mu, wl):
     # per-kernel durations from the events muon_ssm_momentum_timed records
     evs = []
     for _ in range(args.steps):
-        row = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         for e in row:
             e.record()
         evs.append(row)
@@ -688,16 +689,15 @@ def bench_ssm_momentum(args, torch, mu, wl):
         mu.muon_ssm_momentum(V, K, M, S, a, beta=beta, steps=args.ns_steps, workspace=ws,
                              events=[e.cuda_event for e in evs[k]])
     torch.cuda.synchronize()
-    names = ["ns_factored_kernel", "ssm_momentum_accum_kernel", "ssm_momentum_combine_kernel"]
+    names = ["ssm_momentum_fused_kernel", "ssm_momentum_combine_kernel"]
     dur = {nm: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
            for i, nm in enumerate(names)}
     tokens = nseq * T
     chunks = -(-T // 256)
     fb = (m + n) * r * 2                      # the factors of one token
-    wb = m * r * 2                            # its W = V C (bf16), written by the core pass
-    alg = {"ns_factored_kernel": tokens * (fb + wb),
-           "ssm_momentum_accum_kernel": tokens * (wb + n * r * 2 + 4) + nseq * chunks * 2 * 64 * 128 * 4,
-           "ssm_momentum_combine_kernel": nseq * (4 * m * n * 4 + chunks * 2 * 64 * 128 * 4)}
+    part = nseq * chunks * (2 * 64 * 128 * 4 + 16)   # partial sums and map of every chunk
+    alg = {"ssm_momentum_fused_kernel": tokens * (fb + 4) + part,
+           "ssm_momentum_combine_kernel": nseq * 4 * m * n * 4 + part}
     dom = max(names, key=lambda nm: dur[nm])
     gbs = alg[dom] / (dur[dom] * 1e-3) / 1e9
     kernels = {nm: {"ms": round(dur[nm], 4), "alg_bytes": alg[nm],
@@ -836,6 +836,7 @@ def bench_diag(args, torch, mu, wl):
 
 ELEMENTWISE = ["elementwise.hip", "common.cuh"]
 GEMM = ["gemm_bf16.hip", "common.cuh"]
+FACTORED_MOM = ["ssm_momentum.hip", "factored_core.cuh", "common.cuh"]
 COUNTED_KERNELS = {
     "full_step": {"combine_bf16_kernel": ("combine_bf16_kernel", GEMM),
                   "symprod_bf16_kernel": ("symprod_bf16_kernel", GEMM),
@@ -847,11 +848,10 @@ COUNTED_KERNELS = {
     "injections": {"ns_small_bf16_kernel": ("ns_small_bf16_kernel", ["ns_small.hip", "common.cuh"]),
                    "ns_small_bf16_wg_kernel": ("ns_small_bf16_wg_kernel", ["ns_small.hip", "common.cuh"]),
                    "ns_small_bf16_wgr_kernel": ("ns_small_bf16_wgr_kernel", ["ns_small.hip", "common.cuh"])},
-    "ssm_momentum": {"ns_factored_kernel": ("ns_factored_kernel", ["ns_factored.hip", "common.cuh"]),
-                     "ssm_momentum_accum_kernel": ("ssm_momentum_accum_kernel", ["ssm_momentum.hip", "common.cuh"]),
-                     "ssm_momentum_combine_kernel": ("ssm_momentum_combine_kernel",
-                                                     ["ssm_momentum.hip", "common.cuh"])},
-    "injections_factored": {"ns_factored_kernel": ("ns_factored_kernel", ["ns_factored.hip", "common.cuh"])},
+    "ssm_momentum": {"ssm_momentum_fused_kernel": ("ssm_momentum_fused_kernel", FACTORED_MOM),
+                     "ssm_momentum_combine_kernel": ("ssm_momentum_combine_kernel", FACTORED_MOM)},
+    "injections_factored": {"ns_factored_kernel": ("ns_factored_kernel",
+                                                   ["ns_factored.hip", "factored_core.cuh", "common.cuh"])},
 }
 
 

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MUON_VERSION 8
+#define MUON_VERSION 9
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
@@ -327,17 +327,17 @@ int muon_ns_factored(const void* V, const void* K, int dtype, int m, int n, int 
  * token's weight).  Supported: r == 8, m <= 64, n <= 128; otherwise
  * MUON_EUNSUPPORTED.  M, S, decay, the factors and the workspace must not
  * overlap.  nseq == 0 or T == 0 leaves the states unchanged.  The workspace
- * (muon_ssm_momentum_workspace_size bytes, 16-byte aligned) holds each
- * token's V C (m x r bf16) and per-chunk partial sums; muon_query_flags does
- * not apply to it. */
+ * (muon_ssm_momentum_workspace_size bytes, 16-byte aligned) holds the
+ * per-chunk partial sums (two 64 x 128 float32 tiles per 256 tokens of a
+ * sequence); muon_query_flags does not apply to it. */
 size_t muon_ssm_momentum_workspace_size(int m, int n, int r, long long nseq, int T);
 int muon_ssm_momentum(const void* V, const void* K, int dtype, int m, int n, int r, long long nseq, int T,
                       float beta, const float* decay, float* M, float* S, const muon_ns_cfg* cfg,
                       void* workspace, size_t workspace_bytes, void* stream);
-/* muon_ssm_momentum for measurement: records four caller-created hipEvent_t
- * handles on `stream` (nevents >= 4): before the core pass (which writes each
- * token's V C), after it, after the per-chunk accumulation and after the
- * in-order combine. */
+/* muon_ssm_momentum for measurement: records three caller-created hipEvent_t
+ * handles on `stream` (nevents >= 3): before the fused pass (every token's
+ * core and the per-chunk partial sums), after it and after the in-order
+ * combine. */
 int muon_ssm_momentum_timed(const void* V, const void* K, int dtype, int m, int n, int r, long long nseq, int T,
                             float beta, const float* decay, float* M, float* S, const muon_ns_cfg* cfg,
                             void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents);

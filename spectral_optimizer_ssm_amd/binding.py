@@ -496,7 +496,7 @@ def muon_ssm_momentum(V, K, M, S=None, decay=None, beta=0.9, steps=1, coeffs=(1.
     float32 updated in place to the states after the T tokens
     (M_t = beta M_{t-1} + NS(V_t K_t^T); S_t = decay_t S_{t-1} + M_t with
     decay [nseq, T] float32).  Returns the workspace tensor for reuse.
-    `events`: optional list of 4 raw hipEvent_t handles (ints) recorded by
+    `events`: optional list of 3 raw hipEvent_t handles (ints) recorded by
     muon_ssm_momentum_timed at its phase boundaries."""
     import torch
     L = lib()

@@ -1,0 +1,166 @@
+// The r x r Newton-Schulz core of four factored injections on one wavefront,
+// shared by the factored kernel (ns_factored.hip) and the fused momentum
+// pathway (ssm_momentum.hip).
+//
+// "MuonSSM: Orthogonalizing State Space Models" (method section on the
+// value-key injections and their light Newton-Schulz step): for X = V K^T
+// with V m x r and K n x r every NS step keeps the form X_k = V C_k K^T,
+//   P = V^T V,  S = K^T K,  nu = ||X||_F = sqrt(tr(P S)),  C_0 = I / (nu + eps),
+//   N = C S C^T P   (so that X X^T X = V (N C) K^T),
+//   C <- a C + b N C + c N N C.
+//
+// LDS of a wavefront: the four matrices' V and K side by side as 64-byte rows
+// of four 16-byte slots (matrix q's r = 8 bf16 in slot q, zero padded), V
+// rows first, so one v_mfma_f32_32x32x16_bf16 per 16 rows gives the four
+// Gram matrices at once on its diagonal 8 x 8 blocks (operands from two
+// ds_read_b64_tr_b16 per lane); the 8 x 8 recurrence then runs on 16 lanes
+// per matrix, each lane owning 4 entries of one row, through LDS.  Slot q of
+// row t sits at position q ^ ((t / 4) % 4) of the row, so sixteen
+// consecutive rows accessed at one slot fall on distinct LDS banks.
+#pragma once
+
+#include "common.cuh"
+
+namespace muon {
+namespace fact {
+
+constexpr int kMats = 4;   // matrices per wavefront
+constexpr int kRow = 64;   // bytes per staged row (32 bf16 columns)
+
+// Byte offset of slot q (matrix q's 16 bytes) of staged row t.
+__device__ __forceinline__ int slot(int t, int q) { return t * kRow + 16 * (q ^ ((t >> 2) & 3)); }
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// LDS of one wavefront.
+struct WaveLds {
+  char* vk;      // (m_pad + n_pad) x kRow: V rows, then K rows
+  float* f;      // kMats x 6 x 64: P, S, C, T1, N, T2
+  float* t;      // m_pad x 32 floats: V C of the four matrices (dense output only)
+  __device__ float* mat(int q, int which) const { return f + (q * 6 + which) * 64; }
+};
+enum { kP = 0, kS, kC, kT1, kN, kT2 };
+constexpr int kWorkBytes = kMats * 6 * 64 * 4;
+
+// Gram of the 32 staged columns over rows [row0, row0 + rows): lane l holds
+// column l % 32, rows 8 (g / 4) + 4 (l / 32) + g % 4 of the 32 x 32 result.
+__device__ __forceinline__ f32x16_t gram32(const char* vk, int row0, int rows, int lane) {
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  const int g = lane >> 4;
+  const int colbase = 16 * (g & 1);
+  const int rr = (lane & 15) >> 2, u = lane & 3;
+  for (int k0 = 0; k0 < rows; k0 += 16) {
+    // A operand: row (= staged column) lane % 32, contraction index
+    // k0 + 8 (lane / 32) + 0..7; lane 16g + 4rr + u addresses staged row
+    // k0 + 8 (g >> 1) + 4h + rr, columns colbase + 4u .. + 3 (slot
+    // colbase / 8 + u / 2, bytes 8 (u % 2) ..).
+    u32x2_t part[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = row0 + k0 + 8 * (g >> 1) + 4 * h + rr;
+      const char* p = vk + slot(row, (colbase >> 3) + (u >> 1)) + 8 * (u & 1);
+      const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+      part[h] = __builtin_bit_cast(u32x2_t, v);
+    }
+    const u32x4_t w = {part[0][0], part[0][1], part[1][0], part[1][1]};
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, w);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Keep the diagonal 8 x 8 blocks of a gram32 result: lane l writes rows
+// 4 (l / 32) + 0..3, column l % 8 of matrix (l % 32) / 8.
+__device__ __forceinline__ void store_blocks(const f32x16_t& acc, const WaveLds& L, int which, int lane) {
+  const int q = (lane & 31) >> 3, j = lane & 7, i0 = 4 * (lane >> 5);
+  float* dst = L.mat(q, which);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = q == 0 ? acc[e] : q == 1 ? acc[4 + e] : q == 2 ? acc[8 + e] : acc[12 + e];
+    dst[(i0 + e) * 8 + j] = v;
+  }
+}
+
+// Z = X Y (or X Y^T) for the wave's four 8 x 8 matrices; lane l handles
+// matrix l / 16, row i = (l % 16) / 2, columns j0 .. j0 + 3 with j0 = 4 (l % 2).
+template <bool TRANS_Y>
+__device__ __forceinline__ void mm8(const WaveLds& L, int x, int y, int z, int lane) {
+  const int q = lane >> 4, i = (lane & 15) >> 1, j0 = 4 * (lane & 1);
+  const float* X = L.mat(q, x);
+  const float* Y = L.mat(q, y);
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float xv = X[i * 8 + c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(xv, TRANS_Y ? Y[(j0 + e) * 8 + c] : Y[c * 8 + j0 + e], acc[e]);
+  }
+  wave_sync();  // every lane has read X and Y before Z (which may alias neither) is written
+  float* Z = L.mat(q, z);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Z[i * 8 + j0 + e] = acc[e];
+  wave_sync();
+}
+
+// The cores C of the four matrices staged in L.vk (V rows 0 .. m_pad - 1, K
+// rows m_pad .. m_pad + n_pad - 1), left in L.mat(q, kC).  Args supplies
+// m_pad, n_pad (multiples of 16), r, eps, steps and the per-step
+// coefficients a[], b[], c[].  Both Grams are read before either is stored,
+// so the work matrices may lie over the staged rows.
+template <class Args>
+__device__ __forceinline__ void core(const Args& F, const WaveLds& L, int lane) {
+  const int r = F.r;
+  // P = V^T V and S = K^T K on the matrix cores
+  const f32x16_t gp = gram32(L.vk, 0, F.m_pad, lane);
+  const f32x16_t gq = gram32(L.vk, F.m_pad, F.n_pad, lane);
+  wave_sync();
+  store_blocks(gp, L, kP, lane);
+  store_blocks(gq, L, kS, lane);
+  wave_sync();
+
+  // nu^2 = tr(P S) per matrix (16 lanes each), C_0 = I_r / (nu + eps)
+  const int q = lane >> 4, i = (lane & 15) >> 1, j0 = 4 * (lane & 1);
+  {
+    const float* P = L.mat(q, kP);
+    const float* S = L.mat(q, kS);
+    float t2 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t2 = fmaf(P[i * 8 + j0 + e], S[(j0 + e) * 8 + i], t2);
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) t2 += __shfl_xor(t2, d, 64);
+    const float inv = 1.0f / (sqrtf(t2) + F.eps);
+    float* C = L.mat(q, kC);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) C[i * 8 + j0 + e] = (i == j0 + e && i < r) ? inv : 0.0f;
+  }
+  wave_sync();
+
+  // the r x r recurrence (zero padding stays zero)
+  for (int k = 0; k < F.steps; ++k) {
+    mm8<false>(L, kC, kS, kT1, lane);   // C S
+    mm8<true>(L, kT1, kC, kT2, lane);   // C S C^T
+    mm8<false>(L, kT2, kP, kN, lane);   // N = C S C^T P
+    mm8<false>(L, kN, kC, kT1, lane);   // N C
+    const bool quintic = F.c[k] != 0.0f;
+    if (quintic) mm8<false>(L, kN, kT1, kT2, lane);  // N N C
+    float* C = L.mat(q, kC);
+    const float* NC = L.mat(q, kT1);
+    const float* NNC = L.mat(q, kT2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int o = i * 8 + j0 + e;
+      float v = fmaf(F.a[k], C[o], F.b[k] * NC[o]);
+      if (quintic) v = fmaf(F.c[k], NNC[o], v);
+      C[o] = v;
+    }
+    wave_sync();
+  }
+}
+
+}  // namespace fact
+}  // namespace muon

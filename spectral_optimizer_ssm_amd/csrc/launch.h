@@ -206,7 +206,6 @@ struct FactLaunch {
   const bf16_t* K;     // [batch][n][r]
   float* C;            // [batch][r][r], or null
   bf16_t* O;           // [batch][m][n] or null
-  bf16_t* W;           // [batch][m][8] = V C (r == 8), or null
   long long batch;
   int m, n, r, m_pad, n_pad;  // pads: multiples of 16
   int vec;             // r == 8 and 16-byte aligned factors: 16-byte row loads
@@ -216,19 +215,25 @@ struct FactLaunch {
   float eps;
   float a[64], b[64], c[64];
 };
-// keep_v: the staged V rows stay intact for the W output
-int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off = nullptr, bool keep_v = false);
+int factored_lds_per_wave(int m_pad, int n_pad, bool dense, int* f_off = nullptr);
 hipError_t launch_ns_factored(const FactLaunch& F, hipStream_t st);
 
+// Padded sides, rank and Newton-Schulz coefficients of a factored core.
+struct FactCoreArgs {
+  int m_pad, n_pad, r, steps;
+  float eps;
+  float a[64], b[64], c[64];
+};
+
 // Momentum pathway over sequences of factored injections (ssm_momentum.hip):
-// per (sequence, chunk of kSsmMomQ tokens) float32 partial sums, then the
-// chunk maps applied in token order to the caller's states.
+// one workgroup per (sequence, chunk of kSsmMomQ tokens) forms the NS cores
+// of the chunk's tokens and the chunk's float32 partial sums; then the chunk
+// maps are applied in token order to the caller's states.
 constexpr int kSsmMomQ = 256;
 struct SsmMomLaunch {
   const bf16_t* V;     // [nseq][T][m][8]
   const bf16_t* K;     // [nseq][T][n][8]
-  const bf16_t* W;     // [nseq][T][m][8] V C, the factor of each token's NS result
-  const float* a;      // [nseq][T] decays (with S)
+  const float* a;      // [nseq][T] decays (with S), else null
   float beta;
   int m, n, T, Q, nchunks;  // m <= 64, n <= 128, Q tokens per chunk
   long long nseq;
@@ -236,8 +241,9 @@ struct SsmMomLaunch {
   float* coef;         // [nseq][nchunks][4]: beta^L, prod a, B, 0
   float* M;            // [nseq][m][n] in/out
   float* S;            // null, or [nseq][m][n] in/out
+  FactCoreArgs ns;     // m_pad 64, n_pad 128, r 8
 };
-// phase 0: partial sums; phase 1: combine into M (and S)
+// phase 0: cores and partial sums; phase 1: combine into M (and S)
 hipError_t launch_ssm_momentum(const SsmMomLaunch& P, hipStream_t st, int phase);
 
 // Spectral diagnostics (a chunk of `count` matrices per launch).

@@ -921,14 +921,13 @@ namespace {
 
 // Shapes, padding, LDS split and coefficients of a factored Newton-Schulz
 // launch (pointers and the vector-load flag are the caller's).
-int factored_launch(int m, int n, int r, long long batch, const NsCoefs& C, float eps, bool dense, FactLaunch* F,
-                    bool keep_v = false) {
+int factored_launch(int m, int n, int r, long long batch, const NsCoefs& C, float eps, bool dense, FactLaunch* F) {
   if (m <= 0 || n <= 0 || r <= 0 || batch < 0) return MUON_EINVAL;
   if (r > 8 || m > 256 || n > 256) return MUON_EUNSUPPORTED;
   if (dense && n % 8 != 0) return MUON_EUNSUPPORTED;
   const int m_pad = round_up(m, 16), n_pad = round_up(n, 16);
   int f_off = 0;
-  const int per_wave = factored_lds_per_wave(m_pad, n_pad, dense, &f_off, keep_v);
+  const int per_wave = factored_lds_per_wave(m_pad, n_pad, dense, &f_off);
   if (per_wave > 65536) return MUON_EUNSUPPORTED;
   F->batch = batch;
   F->m = m; F->n = n; F->r = r; F->m_pad = m_pad; F->n_pad = n_pad;
@@ -943,12 +942,11 @@ int factored_launch(int m, int n, int r, long long batch, const NsCoefs& C, floa
 
 bool overlaps(const char* a, size_t na, const char* b, size_t nb) { return a < b + nb && b < a + na; }
 
-// Workspace of the momentum pathway: W = V C of every token (m x 8 bf16), the
-// per-chunk partial sums (two 64 x 128 float32 tiles each) and the chunk
-// coefficients.
+// Workspace of the momentum pathway: the per-chunk partial sums (two 64 x 128
+// float32 tiles each) and the chunk coefficients.
 struct SsmMomPlan {
   int nchunks = 0;
-  size_t off_w = 0, off_part = 0, off_coef = 0, end = 0;
+  size_t off_part = 0, off_coef = 0, end = 0;
 };
 int plan_ssm_momentum(int m, int n, int r, long long nseq, int T, SsmMomPlan* p) {
   if (m <= 0 || n <= 0 || r <= 0 || nseq < 0 || T < 0) return MUON_EINVAL;
@@ -957,8 +955,6 @@ int plan_ssm_momentum(int m, int n, int r, long long nseq, int T, SsmMomPlan* p)
   const long long wgs = nseq * p->nchunks;
   if (wgs > (1LL << 31) - 1 || nseq * m * n / 256 > (1LL << 31) - 1) return MUON_EUNSUPPORTED;
   size_t off = 0;
-  p->off_w = off;
-  off = align_up(off + static_cast<size_t>(nseq) * T * m * 8 * sizeof(bf16_t), kAlign);
   p->off_part = off;
   off = align_up(off + static_cast<size_t>(wgs) * 2 * 64 * 128 * sizeof(float), kAlign);
   p->off_coef = off;
@@ -1269,10 +1265,7 @@ int muon_ssm_momentum_timed(const void* V, const void* K, int dtype, int m, int 
   rc = plan_ssm_momentum(m, n, r, nseq, T, &p);
   if (rc != MUON_OK) return rc;
   if (!std::isfinite(beta)) return MUON_EINVAL;
-  FactLaunch F{};
-  rc = factored_launch(m, n, r, nseq * T, C, cfg->eps, false, &F, true);
-  if (rc != MUON_OK) return rc;
-  if (events != nullptr && nevents < 4) return MUON_EINVAL;
+  if (events != nullptr && nevents < 3) return MUON_EINVAL;
   if (nseq == 0 || T == 0) return MUON_OK;
   if (V == nullptr || K == nullptr || M == nullptr || !aligned16(V) || !aligned16(K) || !aligned_to(M, 4) ||
       (S != nullptr && (decay == nullptr || !aligned_to(S, 4) || !aligned_to(decay, 4))))
@@ -1303,19 +1296,11 @@ int muon_ssm_momentum_timed(const void* V, const void* K, int dtype, int m, int 
   E.ev = events;
   E.n = nevents;
   if (!E.mark(st, 0)) return MUON_EHIP;
-  // 1. the Newton-Schulz core of every token's injection, applied to V: W = V C
-  F.V = static_cast<const bf16_t*>(V);
-  F.K = static_cast<const bf16_t*>(K);
-  F.C = nullptr;
-  F.W = reinterpret_cast<bf16_t*>(ws + p.off_w);
-  F.O = nullptr;
-  F.vec = 1;
-  if (launch_ns_factored(F, st) != hipSuccess || !E.mark(st, 0)) return MUON_EHIP;
-  // 2. per-chunk partial sums, 3. chunk maps applied in token order
+  // 1. every token's Newton-Schulz core and the per-chunk partial sums,
+  // 2. the chunk maps applied in token order
   SsmMomLaunch L{};
   L.V = static_cast<const bf16_t*>(V);
   L.K = static_cast<const bf16_t*>(K);
-  L.W = F.W;
   L.a = S != nullptr ? decay : nullptr;
   L.beta = beta;
   L.m = m; L.n = n; L.T = T; L.Q = kSsmMomQ; L.nchunks = p.nchunks;
@@ -1324,6 +1309,10 @@ int muon_ssm_momentum_timed(const void* V, const void* K, int dtype, int m, int 
   L.coef = reinterpret_cast<float*>(ws + p.off_coef);
   L.M = M;
   L.S = S;
+  L.ns.m_pad = 64; L.ns.n_pad = 128; L.ns.r = r;
+  L.ns.steps = C.steps;
+  L.ns.eps = cfg->eps;
+  for (int k = 0; k < C.steps; ++k) { L.ns.a[k] = C.a[k]; L.ns.b[k] = C.b[k]; L.ns.c[k] = C.c[k]; }
   if (launch_ssm_momentum(L, st, 0) != hipSuccess || !E.mark(st, 0)) return MUON_EHIP;
   if (launch_ssm_momentum(L, st, 1) != hipSuccess || !E.mark(st, 0)) return MUON_EHIP;
   return MUON_OK;

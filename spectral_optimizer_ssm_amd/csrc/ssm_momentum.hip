@@ -5,124 +5,301 @@
 // memory state S_t a momentum state M_t accumulates the Newton-Schulz
 // conditioned injections, and the pair follows a block-affine recurrence.
 // Read as heavy-ball momentum on the memory:
-//   U_t = NS(V_t K_t^T) = V_t C_t K_t^T = W_t K_t^T   (r x r core C_t, ns_factored.hip)
+//   U_t = NS(V_t K_t^T) = V_t C_t K_t^T = W_t K_t^T   (r x r core C_t, factored_core.cuh)
 //   M_t = beta M_{t-1} + U_t,   S_t = a_t S_{t-1} + M_t.
-// The dense U_t (16 KB for a 64 x 128 injection) never reaches memory: the
-// factored kernel writes W_t = V_t C_t (1 KB per token) and this file turns
-// the recurrence into weighted sums of rank-r products W_t K_t^T.
+// Neither U_t (16 KB dense for a 64 x 128 injection) nor W_t = V_t C_t ever
+// reaches memory: one kernel forms every token's core from its factors and
+// folds W_t K_t^T into float32 partial sums on the matrix cores.
 //
-// Chunks.  Over a chunk of L tokens u = 0..L-1 entered with (S, M):
+// Regrouping.  Over L tokens u = 0..L-1 entered with (S, M):
 //   M' = beta^L M + sum_u beta^(L-1-u) U_u
 //   S' = A S + B M + sum_u w_u U_u,   A = prod_u a_u,   B = beta w_0,
 //   w_u = g_u + beta w_{u+1} (w_L = 0),   g_u = prod_{s>u} a_s.
-// ssm_momentum_accum_kernel forms the two sums of one (sequence, chunk) as
-// float32 partials; ssm_momentum_combine_kernel applies the chunk maps in
-// token order to the caller's (S, M).  Sums and maps are the same
-// recurrence regrouped (the block-affine structure the pages point to).
+// The fused kernel takes a chunk of 256 tokens in rounds of 32: per round it
+// applies the round's map to its running sums and adds the round's weighted
+// products, which yields the chunk's sums; the chunk's map is the rounds'
+// maps composed.  The combine kernel applies the chunk maps in token order to
+// the caller's (S, M).  Maps and sums are the recurrence regrouped (the
+// block-affine structure the pages point to).
 //
-// Accumulation kernel: one workgroup of 4 waves per (sequence, chunk), the
-// 64 x 128 state tile (zero padded) split into four 32-column blocks, one per
-// wave.  The factored kernel has written W_u = V_u C_u (m x 8 bf16) for every
-// token, so
-//   P[i][j] += sum_{u, r} W_u[i][r] (w_u K_u[j][r])
-// runs on v_mfma_f32_32x32x16_bf16 with the contraction index (token pair,
-// rank): each lane loads its two 16-byte rows of W and its 16-byte row of K
-// straight from memory, scales the K row by the token's weight (one per
-// partial sum) and rounds it to bf16.  No LDS staging and no barriers in the
-// token loop; the four waves read the same W rows (L2 serves three of them).
+// Fused kernel: one workgroup of eight waves per (sequence, chunk), persistent
+// over chunks.  In a round each wave stages four tokens' V and K in its own
+// LDS area (factored_core.cuh layout), loads the next round's factors into
+// registers, runs the core and overwrites its V rows with W = V C (bf16).
+// After a barrier wave w accumulates block (rows 32 (w % 2), columns
+// 32 (w / 2)) of the zero-padded 64 x 128 state tile over the round's 32
+// tokens on v_mfma_f32_32x32x16_bf16, the contraction index being (token
+// pair, rank): W rows are the A operand, the K row scaled by the token's
+// weight (one per partial sum) and rounded to bf16 the B operand.  The next
+// round's barrier keeps the areas until every wave has read them.
 #include "common.cuh"
+#include "factored_core.cuh"
 #include "launch.h"
 
 namespace muon {
 namespace {
 
+using fact::kRow;
+using fact::slot;
+using fact::wave_sync;
+
 constexpr int kTileM = 64, kTileN = 128, kTile = kTileM * kTileN;
+constexpr int kWaves = 8;                          // waves per workgroup
+constexpr int kRound = kWaves * fact::kMats;       // tokens per round
+constexpr int kStage = (kTileM + kTileN) * kRow;   // staged V and K rows of a wave
+constexpr int kArea = kStage + fact::kWorkBytes;   // LDS of a wave
+constexpr int kFusedLds = kWaves * kArea;          // 144 KB: one workgroup per CU
+static_assert(kSsmMomQ % kRound == 0, "chunks are whole rounds");
 
-__global__ void __launch_bounds__(256) ssm_momentum_accum_kernel(SsmMomLaunch P) {
-  __shared__ float wgt[2][kSsmMomQ];
-  __shared__ float dec[kSsmMomQ];
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int G = lane >> 5, l32 = lane & 31;
-  const long long seq = blockIdx.x / P.nchunks;
-  const int ch = static_cast<int>(blockIdx.x - seq * P.nchunks);
-  const int t0 = ch * P.Q;
-  const int len = P.T - t0 < P.Q ? P.T - t0 : P.Q;
-  const bool with_s = P.S != nullptr;
-  const long long tok0 = seq * P.T + t0;
+// Factors of a wave's four tokens: lane l holds rows l + 64 e of their
+// concatenated V rows (e < 4) and K rows (e < 8), zero past the valid tokens;
+// and the decay of token l % 32 of the round (1 past the valid tokens).
+struct RoundRegs {
+  u32x4_t v[4], k[8];
+  float a;
+};
 
-  // per-token weights by the backward recurrence (one thread, decays staged)
-  if (with_s)
-    for (int u = tid; u < len; u += 256) dec[u] = P.a[tok0 + u];
-  __syncthreads();
-  if (tid == 0) {
-    float wmv = 1.0f, g = 1.0f, ws = 0.0f;
-    for (int u = len - 1; u >= 0; --u) {
-      wgt[0][u] = wmv;
-      wmv *= P.beta;
-      if (with_s) {
-        ws = g + P.beta * ws;
-        wgt[1][u] = ws;
-        g *= dec[u];
+// tokr: first token of the round (index into [nseq * T]); nvr: its valid tokens.
+template <bool FIXED>
+__device__ __forceinline__ void load_round(const SsmMomLaunch& P, long long tokr, int nvr, int w, int lane,
+                                           RoundRegs& R) {
+  const int m = FIXED ? kTileM : P.m, n = FIXED ? kTileN : P.n;
+  int nv = nvr - fact::kMats * w;
+  nv = nv < 0 ? 0 : nv > fact::kMats ? fact::kMats : nv;
+  const long long tok = tokr + fact::kMats * w;
+  const u32x4_t* Vg = reinterpret_cast<const u32x4_t*>(P.V) + tok * m;   // one 16-byte row per rank-8 row
+  const u32x4_t* Kg = reinterpret_cast<const u32x4_t*>(P.K) + tok * n;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = lane + 64 * e;
+    R.v[e] = c < nv * m ? Vg[c] : z;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = lane + 64 * e;
+    R.k[e] = c < nv * n ? Kg[c] : z;
+  }
+  const int j = lane & 31;
+  R.a = (P.a != nullptr && j < nvr) ? P.a[tokr + j] : 1.0f;
+}
+
+// Row t of token q goes to staged row t, slot q; K rows after the 64 V rows.
+// Rows past m and n are never written (zero from the start).
+template <bool FIXED>
+__device__ __forceinline__ void stage_round(const SsmMomLaunch& P, char* vk, const RoundRegs& R, int lane) {
+  const int m = FIXED ? kTileM : P.m, n = FIXED ? kTileN : P.n;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = lane + 64 * e;
+    if (c < fact::kMats * m) {
+      const int q = c / m, t = c - q * m;
+      *reinterpret_cast<u32x4_t*>(vk + slot(t, q)) = R.v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = lane + 64 * e;
+    if (c < fact::kMats * n) {
+      const int q = c / n, u = c - q * n;
+      *reinterpret_cast<u32x4_t*>(vk + slot(kTileM + u, q)) = R.k[e];
+    }
+  }
+}
+
+// W = V C over the staged V rows of the wave's nv valid tokens: lane p of
+// token q = lane / 16 rewrites rows p, p + 16, ... (each row read, then
+// written, by the same lane).
+template <bool FIXED>
+__device__ __forceinline__ void write_w(const SsmMomLaunch& P, const fact::WaveLds& L, int nv, int lane) {
+  const int m = FIXED ? kTileM : P.m;
+  const int q = lane >> 4, p = lane & 15;
+  if (q >= nv) return;
+  const float* C = L.mat(q, fact::kC);
+  for (int t = p; t < m; t += 16) {
+    u32x4_t* row = reinterpret_cast<u32x4_t*>(L.vk + slot(t, q));
+    const u32x4_t vv = *row;
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[2 * h] = lo_bf16(vv[h]);
+      v[2 * h + 1] = hi_bf16(vv[h]);
+    }
+    float o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[c] = fmaf(v[d], C[d * 8 + c], o[c]);
+    u32x4_t wv;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) wv[h] = pack_bf16x2(o[2 * h], o[2 * h + 1]);
+    *row = wv;
+  }
+}
+
+// Weights and map of a round of nvr tokens, on lane j = lane % 32 (both
+// halves of the wave alike):
+//   wm_j = beta^(nvr-1-j),  ws_j = w_j = sum_{v=j}^{nvr-1} beta^(v-j) g_v,
+//   g_v = prod_{s>v} a_s;  map: bl = beta^nvr, A = prod a, B = beta w_0.
+// Suffix scans over the 32 lanes; tokens past nvr act as the identity
+// (a = 1, no beta factor, no term).
+struct RoundMap {
+  float wm, ws, bl, A, B;
+};
+__device__ __forceinline__ RoundMap round_map(float beta, float a, bool with_s, int nvr, int lane) {
+  const int j = lane & 31;
+  const bool valid = j < nvr;
+  const float fb = valid ? beta : 1.0f;
+  float pf = fb, pa = a;   // inclusive suffix products of beta and of a
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) {
+    const float of = __shfl_down(pf, d, 32), oa = __shfl_down(pa, d, 32);
+    if (j + d < 32) {
+      pf *= of;
+      pa *= oa;
+    }
+  }
+  float wm = __shfl_down(pf, 1, 32), g = __shfl_down(pa, 1, 32);
+  if (j == 31) wm = g = 1.0f;
+  RoundMap R;
+  R.wm = wm;
+  R.bl = __shfl(pf, 0, 32);
+  R.ws = 0.0f;
+  R.A = R.B = 0.0f;
+  if (with_s) {
+    // segments (s, f) = (sum of beta^(v-j) g_v over the segment, beta^(its valid tokens)),
+    // joined as (s1 + f1 s2, f1 f2)
+    float s = valid ? g : 0.0f, f = fb;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const float os = __shfl_down(s, d, 32), of = __shfl_down(f, d, 32);
+      if (j + d < 32) {
+        s = fmaf(f, os, s);
+        f *= of;
       }
     }
-    float* cf = P.coef + (seq * P.nchunks + ch) * 4;
-    cf[0] = wmv;                          // beta^L
-    cf[1] = with_s ? g : 0.0f;            // A = prod a
-    cf[2] = with_s ? P.beta * ws : 0.0f;  // B = beta w_0
-    cf[3] = 0.0f;
+    R.ws = s;
+    R.A = __shfl(pa, 0, 32);
+    R.B = beta * __shfl(s, 0, 32);
   }
-  __syncthreads();
+  return R;
+}
 
-  const bf16_t* Ws = P.W + tok0 * P.m * 8;
-  const bf16_t* Ks = P.K + tok0 * P.n * 8;
-  f32x16_t accM[2], accS[2];
+__device__ __forceinline__ bf16x8_t scaled(const u32x4_t& k, float s) {
+  u32x4_t o;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) accM[rb][r] = accS[rb][r] = 0.0f;
-  const int col = 32 * w + l32;
-  const bool row0 = l32 < P.m, row1 = l32 + 32 < P.m, colok = col < P.n;
-  auto scaled = [](const u32x4_t& k, float s) {
-    u32x4_t o;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(lo_bf16(k[h]) * s, hi_bf16(k[h]) * s);
-    return __builtin_bit_cast(bf16x8_t, o);
+  for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(lo_bf16(k[h]) * s, hi_bf16(k[h]) * s);
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+template <bool FIXED>
+__global__ void __launch_bounds__(kWaves * 64) ssm_momentum_fused_kernel(SsmMomLaunch P) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long nitems = P.nseq * P.nchunks;
+  long long it = blockIdx.x;
+  if (it >= nitems) return;  // (the grid holds no more workgroups than items)
+  const bool with_s = P.S != nullptr;
+  char* area = lds + w * kArea;
+  fact::WaveLds L;
+  L.vk = area;
+  L.f = reinterpret_cast<float*>(area + kStage);
+  L.t = nullptr;
+  for (int o = lane * 16; o < kStage; o += 64 * 16) *reinterpret_cast<u32x4_t*>(area + o) = u32x4_t{0u, 0u, 0u, 0u};
+
+  // chunk `it` of sequence it / nchunks: its first token and length
+  auto chunk = [&](long long i, long long& tok0, int& len) {
+    const long long seq = i / P.nchunks;
+    const int t0 = static_cast<int>(i - seq * P.nchunks) * P.Q;
+    len = P.T - t0 < P.Q ? P.T - t0 : P.Q;
+    tok0 = seq * P.T + t0;
   };
-#pragma unroll 4
-  for (int tp = 0; tp < len; tp += 2) {
-    const int t = tp + G;
-    const bool ok = t < len;
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    const long long wt = static_cast<long long>(t) * P.m, kt = static_cast<long long>(t) * P.n;
-    const u32x4_t a0 = (ok && row0) ? *reinterpret_cast<const u32x4_t*>(Ws + (wt + l32) * 8) : z;
-    const u32x4_t a1 = (ok && row1) ? *reinterpret_cast<const u32x4_t*>(Ws + (wt + l32 + 32) * 8) : z;
-    const u32x4_t kv = (ok && colok) ? *reinterpret_cast<const u32x4_t*>(Ks + (kt + col) * 8) : z;
-    const float sm = ok ? wgt[0][t] : 0.0f;
-    const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, a0), A1 = __builtin_bit_cast(bf16x8_t, a1);
-    const bf16x8_t km = scaled(kv, sm);
-    accM[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, km, accM[0], 0, 0, 0);
-    accM[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, km, accM[1], 0, 0, 0);
-    if (with_s) {
-      const bf16x8_t ks = scaled(kv, ok ? wgt[1][t] : 0.0f);
-      accS[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, ks, accS[0], 0, 0, 0);
-      accS[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, ks, accS[1], 0, 0, 0);
-    }
-  }
+  long long tok0;
+  int len;
+  chunk(it, tok0, len);
+  RoundRegs R;
+  load_round<FIXED>(P, tok0, len < kRound ? len : kRound, w, lane, R);
 
-  // partials: lane (G, l32), register 4 q + e holds row 32 rb + 8 q + 4 G + e,
-  // column 32 w + l32 of the padded 64 x 128 tile
-  float* pm = P.part + (seq * P.nchunks + ch) * (with_s ? 2 : 1) * static_cast<long long>(kTile);
+  const int G = lane >> 5, l32 = lane & 31;
+  const int rb = w & 1, cb = w >> 1;
+  const int arow = 32 * rb + l32, krow = kTileM + 32 * cb + l32;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  for (;;) {
+    const int nr = (len + kRound - 1) / kRound;
+    f32x16_t accM, accS;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int r = 0; r < 16; ++r) accM[r] = accS[r] = 0.0f;
+    float cbl = 1.0f, ca = 1.0f, cB = 0.0f;   // the chunk's map so far
+    for (int rd = 0; rd < nr; ++rd) {
+      const int nvr = len - kRound * rd < kRound ? len - kRound * rd : kRound;
+      __syncthreads();  // every wave is done with the previous round's areas
+      stage_round<FIXED>(P, area, R, lane);
+      const float a_cur = R.a;
+      wave_sync();
+      // the next round's factors load while this round is computed
+      if (rd + 1 < nr) {
+        const int nv2 = len - kRound * (rd + 1);
+        load_round<FIXED>(P, tok0 + kRound * (rd + 1), nv2 < kRound ? nv2 : kRound, w, lane, R);
+      } else if (it + gridDim.x < nitems) {
+        long long tok2;
+        int len2;
+        chunk(it + gridDim.x, tok2, len2);
+        load_round<FIXED>(P, tok2, len2 < kRound ? len2 : kRound, w, lane, R);
+      }
+      fact::core(P.ns, L, lane);
+      int nv = nvr - fact::kMats * w;
+      nv = nv < 0 ? 0 : nv;
+      write_w<FIXED>(P, L, nv, lane);
+      const RoundMap map = round_map(P.beta, a_cur, with_s, nvr, lane);
+      __syncthreads();  // every wave's W and K rows are staged
+
+      // the round's map on the running sums (S uses the old M), then its products
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float mv = accM[r];
+        accM[r] = map.bl * mv;
+        if (with_s) accS[r] = fmaf(map.A, accS[r], map.B * mv);
+      }
+      cB = fmaf(map.A, cB, map.B * cbl);
+      ca *= map.A;
+      cbl *= map.bl;
+      for (int tp = 0; 2 * tp < nvr; ++tp) {
+        const int j = 2 * tp + G, q = 2 * (tp & 1) + G;
+        const char* src = lds + (tp >> 1) * kArea;   // token j lives in wave j / 4's area, slot j % 4
+        u32x4_t wv = *reinterpret_cast<const u32x4_t*>(src + slot(arow, q));
+        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(src + slot(krow, q));
+        if (j >= nvr) wv = z;
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, wv);
+        accM = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, scaled(kv, __shfl(map.wm, j)), accM, 0, 0, 0);
+        if (with_s) accS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, scaled(kv, __shfl(map.ws, j)), accS, 0, 0, 0);
+      }
+    }
+
+    // partials: lane (G, l32), register 4 q + e holds row 32 rb + 8 q + 4 G + e,
+    // column 32 cb + l32 of the padded 64 x 128 tile
+    float* pm = P.part + it * (with_s ? 2 : 1) * static_cast<long long>(kTile);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 32 * rb + 8 * q + 4 * G + e;
-        pm[row * kTileN + col] = accM[rb][4 * q + e];
-        if (with_s) pm[kTile + row * kTileN + col] = accS[rb][4 * q + e];
+        const int o = (32 * rb + 8 * q + 4 * G + e) * kTileN + 32 * cb + l32;
+        pm[o] = accM[4 * q + e];
+        if (with_s) pm[kTile + o] = accS[4 * q + e];
       }
+    if (tid == 0) {
+      float* cf = P.coef + it * 4;
+      cf[0] = cbl;
+      cf[1] = with_s ? ca : 0.0f;
+      cf[2] = with_s ? cB : 0.0f;
+      cf[3] = 0.0f;
+    }
+    it += gridDim.x;
+    if (it >= nitems) break;
+    chunk(it, tok0, len);
+  }
 }
 
 // (S, M) <- chunk maps in token order; one thread per state element.
@@ -150,9 +327,22 @@ __global__ void __launch_bounds__(256) ssm_momentum_combine_kernel(SsmMomLaunch 
 }  // namespace
 
 hipError_t launch_ssm_momentum(const SsmMomLaunch& P, hipStream_t st, int phase) {
+  if (P.m > kTileM || P.n > kTileN || P.ns.r != 8 || P.ns.m_pad != kTileM || P.ns.n_pad != kTileN ||
+      P.Q % kRound != 0)
+    return hipErrorInvalidValue;
   if (phase == 0) {
-    const long long blocks = P.nseq * P.nchunks;
-    hipLaunchKernelGGL(ssm_momentum_accum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, P);
+    const long long items = P.nseq * P.nchunks;
+    const long long cus = device_cus();  // 144 KB of LDS: one workgroup per CU
+    const unsigned blocks = static_cast<unsigned>(items < cus ? items : cus);
+    const bool fixed = P.m == kTileM && P.n == kTileN;
+    const void* fn = fixed ? reinterpret_cast<const void*>(ssm_momentum_fused_kernel<true>)
+                           : reinterpret_cast<const void*>(ssm_momentum_fused_kernel<false>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds) != hipSuccess)
+      return hipErrorInvalidValue;
+    if (fixed)
+      hipLaunchKernelGGL(ssm_momentum_fused_kernel<true>, dim3(blocks), dim3(kWaves * 64), kFusedLds, st, P);
+    else
+      hipLaunchKernelGGL(ssm_momentum_fused_kernel<false>, dim3(blocks), dim3(kWaves * 64), kFusedLds, st, P);
   } else {
     const long long blocks = (P.nseq * P.m * P.n + 255) / 256;
     hipLaunchKernelGGL(ssm_momentum_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, P);

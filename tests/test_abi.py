@@ -47,7 +47,7 @@ def test_exports_match_header(mu):
 
 
 def test_version_and_status(mu):
-    assert mu.muon_version() == 8
+    assert mu.muon_version() == 9
     assert mu.status_string(0) == "ok"
     assert "invalid" in mu.status_string(-1)
     assert "unknown" in mu.status_string(7)
@@ -423,8 +423,8 @@ def test_ssm_momentum_validation(mu, case, expect):
     beta = float("nan") if case == "beta_nan" else 0.9
     args = (V, K, dt, m, n, r, nseq, T, beta, dec, M, S, ctypes.byref(cfg), ws, wsz, None)
     if case == "few_events":
-        ev = (ctypes.c_void_p * 3)()
-        rc = L.muon_ssm_momentum_timed(*args, ev, 3)
+        ev = (ctypes.c_void_p * 2)()
+        rc = L.muon_ssm_momentum_timed(*args, ev, 2)
     else:
         rc = L.muon_ssm_momentum(*args)
     assert rc == expect, (case, rc, need)
@@ -432,11 +432,11 @@ def test_ssm_momentum_validation(mu, case, expect):
 
 def test_ssm_momentum_workspace_size(mu):
     L = mu.lib()
-    # V C per token (64 x 8 bf16), two 64 x 128 float32 partials and 4 coefficients per 256-token chunk
+    # two 64 x 128 float32 partials and 4 coefficients per 256-token chunk
     nseq, T = 3, 600
     chunks = 3
     expect = 0
-    for b in (nseq * T * 64 * 8 * 2, nseq * chunks * 2 * 64 * 128 * 4, nseq * chunks * 16):
+    for b in (nseq * chunks * 2 * 64 * 128 * 4, nseq * chunks * 16):
         expect += -(-b // 256) * 256
     assert L.muon_ssm_momentum_workspace_size(64, 128, 8, nseq, T) == expect
     assert L.muon_ssm_momentum_workspace_size(64, 128, 4, nseq, T) == 0
