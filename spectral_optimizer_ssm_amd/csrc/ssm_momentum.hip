@@ -44,11 +44,11 @@ using fact::slot;
 using fact::wave_sync;
 
 constexpr int kTileM = 64, kTileN = 128, kTile = kTileM * kTileN;
-constexpr int kWaves = 8;                          // waves per workgroup
+constexpr int kWaves = 4;                          // waves per workgroup
 constexpr int kRound = kWaves * fact::kMats;       // tokens per round
 constexpr int kStage = (kTileM + kTileN) * kRow;   // staged V and K rows of a wave
 constexpr int kArea = kStage + fact::kWorkBytes;   // LDS of a wave
-constexpr int kFusedLds = kWaves * kArea;          // 144 KB: one workgroup per CU
+constexpr int kFusedLds = kWaves * kArea;          // 72 KB: two workgroups per CU
 static_assert(kSsmMomQ % kRound == 0, "chunks are whole rounds");
 
 // Factors of a wave's four tokens: lane l holds rows l + 64 e of their
@@ -107,35 +107,76 @@ __device__ __forceinline__ void stage_round(const SsmMomLaunch& P, char* vk, con
   }
 }
 
-// W = V C over the staged V rows of the wave's nv valid tokens: lane p of
-// token q = lane / 16 rewrites rows p, p + 16, ... (each row read, then
-// written, by the same lane).
-template <bool FIXED>
-__device__ __forceinline__ void write_w(const SsmMomLaunch& P, const fact::WaveLds& L, int nv, int lane) {
-  const int m = FIXED ? kTileM : P.m;
-  const int q = lane >> 4, p = lane & 15;
-  if (q >= nv) return;
-  const float* C = L.mat(q, fact::kC);
-  for (int t = p; t < m; t += 16) {
-    u32x4_t* row = reinterpret_cast<u32x4_t*>(L.vk + slot(t, q));
-    const u32x4_t vv = *row;
-    float v[8];
+// The round's weighted factors of the wave's nv valid tokens q (token
+// 4 w + q of the round), on the matrix cores:
+//   W_M = V (wm C) over the staged V rows (in place),
+//   W_S = V (ws C) into the wave's work area (same row and slot layout),
+// so that token q adds W_M K^T to the momentum sum and W_S K^T to the memory
+// sum.  Per 32-row block, W^T (rows (token q, rank c), columns the block's V
+// rows) = BD^T V^T with BD the block-diagonal of the four weighted cores, the
+// contraction (token, rank d) taken 16 at a time (two tokens).  The weighted
+// core enters as two bf16 terms (hi + lo, to about 2^-17 relative), so with
+// the exact bf16 V the float32 products and sums match a float32 V (w C) to
+// about 2^-16 before the one rounding of W to bf16.  Every V row and core is
+// read before any W row is written; rows past m stay zero.
+__device__ __forceinline__ void write_w(const fact::WaveLds& L, int nv, int w, float wm, float ws, bool with_s,
+                                        int lane) {
+  const int i = lane & 31, kg = lane >> 5;
+  const int qc = i >> 3, c = i & 7;        // A operand row: core qc, column c
+  const bool live = qc < nv;
+  const float* C = L.mat(qc, fact::kC);
+  float col[8];                            // column c of core qc (rows d), or zeros
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      v[2 * h] = lo_bf16(vv[h]);
-      v[2 * h + 1] = hi_bf16(vv[h]);
+  for (int d = 0; d < 8; ++d) col[d] = live ? C[d * 8 + c] : 0.0f;
+  const float sw[2] = {__shfl(wm, fact::kMats * w + qc), __shfl(ws, fact::kMats * w + qc)};
+  // A operands for the token pairs (0, 1) and (2, 3): lane (i, kg) holds the
+  // weighted column when core qc is the pair's token kg
+  bf16x8_t ahi[2][2], alo[2][2];   // [sum][pair]
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool mine = qc == 2 * h + kg;
+      u32x4_t hv, lv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = mine ? col[2 * e] * sw[u] : 0.0f, x1 = mine ? col[2 * e + 1] * sw[u] : 0.0f;
+        hv[e] = pack_bf16x2(x0, x1);
+        lv[e] = pack_bf16x2(x0 - lo_bf16(hv[e]), x1 - hi_bf16(hv[e]));
+      }
+      ahi[u][h] = __builtin_bit_cast(bf16x8_t, hv);
+      alo[u][h] = __builtin_bit_cast(bf16x8_t, lv);
     }
-    float o[8];
+  // B operands: lane (j, kg) holds V row 32 rb + j of token 2 h + kg (one slot)
+  u32x4_t bv[2][2];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[c] = 0.0f;
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
+    for (int h = 0; h < 2; ++h)
+      bv[rb][h] = *reinterpret_cast<const u32x4_t*>(L.vk + slot(32 * rb + i, 2 * h + kg));
+  wave_sync();  // every V row and core read before W overwrites them
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] = fmaf(v[d], C[d * 8 + c], o[c]);
-    u32x4_t wv;
+  for (int u = 0; u < 2; ++u) {
+    if (u == 1 && !with_s) break;
+    char* dst = u == 0 ? L.vk : reinterpret_cast<char*>(L.f);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) wv[h] = pack_bf16x2(o[2 * h], o[2 * h + 1]);
-    *row = wv;
+    for (int rb = 0; rb < 2; ++rb) {
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv[rb][h]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[u][h], b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[u][h], b, acc, 0, 0, 0);
+      }
+      // lane (j, kg), registers 4 q + e: row 32 rb + j, token q, ranks 4 kg + e
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2_t wv = {pack_bf16x2(acc[4 * q], acc[4 * q + 1]), pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3])};
+        *reinterpret_cast<u32x2_t*>(dst + slot(32 * rb + i, q) + 8 * kg) = wv;
+      }
+    }
   }
 }
 
@@ -187,15 +228,8 @@ __device__ __forceinline__ RoundMap round_map(float beta, float a, bool with_s, 
   return R;
 }
 
-__device__ __forceinline__ bf16x8_t scaled(const u32x4_t& k, float s) {
-  u32x4_t o;
-#pragma unroll
-  for (int h = 0; h < 4; ++h) o[h] = pack_bf16x2(lo_bf16(k[h]) * s, hi_bf16(k[h]) * s);
-  return __builtin_bit_cast(bf16x8_t, o);
-}
-
 template <bool FIXED>
-__global__ void __launch_bounds__(kWaves * 64) ssm_momentum_fused_kernel(SsmMomLaunch P) {
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) ssm_momentum_fused_kernel(SsmMomLaunch P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -224,14 +258,14 @@ __global__ void __launch_bounds__(kWaves * 64) ssm_momentum_fused_kernel(SsmMomL
   load_round<FIXED>(P, tok0, len < kRound ? len : kRound, w, lane, R);
 
   const int G = lane >> 5, l32 = lane & 31;
-  const int rb = w & 1, cb = w >> 1;
-  const int arow = 32 * rb + l32, krow = kTileM + 32 * cb + l32;
-  const u32x4_t z = {0u, 0u, 0u, 0u};
+  const int krow = kTileM + 32 * w + l32;   // wave w: tile columns 32 w .. 32 w + 31
   for (;;) {
     const int nr = (len + kRound - 1) / kRound;
-    f32x16_t accM, accS;
+    f32x16_t accM[2], accS[2];   // row blocks 0 and 1
 #pragma unroll
-    for (int r = 0; r < 16; ++r) accM[r] = accS[r] = 0.0f;
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accM[rb][r] = accS[rb][r] = 0.0f;
     float cbl = 1.0f, ca = 1.0f, cB = 0.0f;   // the chunk's map so far
     for (int rd = 0; rd < nr; ++rd) {
       const int nvr = len - kRound * rd < kRound ? len - kRound * rd : kRound;
@@ -249,46 +283,67 @@ __global__ void __launch_bounds__(kWaves * 64) ssm_momentum_fused_kernel(SsmMomL
         chunk(it + gridDim.x, tok2, len2);
         load_round<FIXED>(P, tok2, len2 < kRound ? len2 : kRound, w, lane, R);
       }
+      const RoundMap map = round_map(P.beta, a_cur, with_s, nvr, lane);
       fact::core(P.ns, L, lane);
       int nv = nvr - fact::kMats * w;
       nv = nv < 0 ? 0 : nv;
-      write_w<FIXED>(P, L, nv, lane);
-      const RoundMap map = round_map(P.beta, a_cur, with_s, nvr, lane);
-      __syncthreads();  // every wave's W and K rows are staged
+      write_w(L, nv, w, map.wm, map.ws, with_s, lane);
+      __syncthreads();  // every wave's weighted factors and K rows are staged
 
       // the round's map on the running sums (S uses the old M), then its products
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float mv = accM[r];
-        accM[r] = map.bl * mv;
-        if (with_s) accS[r] = fmaf(map.A, accS[r], map.B * mv);
-      }
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float mv = accM[rb][r];
+          accM[rb][r] = map.bl * mv;
+          if (with_s) accS[rb][r] = fmaf(map.A, accS[rb][r], map.B * mv);
+        }
       cB = fmaf(map.A, cB, map.B * cbl);
       ca *= map.A;
       cbl *= map.bl;
       for (int tp = 0; 2 * tp < nvr; ++tp) {
-        const int j = 2 * tp + G, q = 2 * (tp & 1) + G;
-        const char* src = lds + (tp >> 1) * kArea;   // token j lives in wave j / 4's area, slot j % 4
-        u32x4_t wv = *reinterpret_cast<const u32x4_t*>(src + slot(arow, q));
-        const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(src + slot(krow, q));
-        if (j >= nvr) wv = z;
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, wv);
-        accM = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, scaled(kv, __shfl(map.wm, j)), accM, 0, 0, 0);
-        if (with_s) accS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, scaled(kv, __shfl(map.ws, j)), accS, 0, 0, 0);
+        // token 2 tp + G lives in wave tp / 2's area, slot q; tokens past nvr
+        // have zero factors
+        const int q = 2 * (tp & 1) + G;
+        const char* src = lds + (tp >> 1) * kArea;
+        const bf16x8_t km = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(src + slot(krow, q)));
+        const bf16x8_t m0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(src + slot(l32, q)));
+        const bf16x8_t m1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(src + slot(32 + l32, q)));
+        accM[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m0, km, accM[0], 0, 0, 0);
+        accM[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m1, km, accM[1], 0, 0, 0);
+        if (with_s) {
+          const char* ss = src + kStage;   // W_S rows in the work area
+          const bf16x8_t s0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ss + slot(l32, q)));
+          const bf16x8_t s1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ss + slot(32 + l32, q)));
+          accS[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0, km, accS[0], 0, 0, 0);
+          accS[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1, km, accS[1], 0, 0, 0);
+        }
       }
     }
 
-    // partials: lane (G, l32), register 4 q + e holds row 32 rb + 8 q + 4 G + e,
-    // column 32 cb + l32 of the padded 64 x 128 tile
-    float* pm = P.part + it * (with_s ? 2 : 1) * static_cast<long long>(kTile);
+    // partials: lane (G, l32), register 4 q + e of row block rb holds row
+    // 32 rb + 8 q + 4 G + e, column 32 w + l32 of the padded 64 x 128 tile;
+    // stored through a buffer resource (one per-lane offset, the row offsets
+    // scalar)
+    {
+      const int nout = with_s ? 2 : 1;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          P.part + it * nout * static_cast<long long>(kTile), static_cast<short>(0), nout * kTile * 4, 0x00020000);
+      const int voff = ((4 * G) * kTileN + 32 * w + l32) * 4;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int o = (32 * rb + 8 * q + 4 * G + e) * kTileN + 32 * cb + l32;
-        pm[o] = accM[4 * q + e];
-        if (with_s) pm[kTile + o] = accS[4 * q + e];
-      }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int soff = (32 * rb + 8 * q + e) * kTileN * 4;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(accM[rb][4 * q + e]), rs, voff, soff, 0);
+            if (with_s)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(accS[rb][4 * q + e]), rs, voff, soff + kTile * 4,
+                                                    0);
+          }
+    }
     if (tid == 0) {
       float* cf = P.coef + it * 4;
       cf[0] = cbl;
@@ -332,8 +387,8 @@ hipError_t launch_ssm_momentum(const SsmMomLaunch& P, hipStream_t st, int phase)
     return hipErrorInvalidValue;
   if (phase == 0) {
     const long long items = P.nseq * P.nchunks;
-    const long long cus = device_cus();  // 144 KB of LDS: one workgroup per CU
-    const unsigned blocks = static_cast<unsigned>(items < cus ? items : cus);
+    const long long slots = 2LL * device_cus();  // 72 KB of LDS: two workgroups per CU
+    const unsigned blocks = static_cast<unsigned>(items < slots ? items : slots);
     const bool fixed = P.m == kTileM && P.n == kTileN;
     const void* fn = fixed ? reinterpret_cast<const void*>(ssm_momentum_fused_kernel<true>)
                            : reinterpret_cast<const void*>(ssm_momentum_fused_kernel<false>);
