@@ -35,15 +35,21 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// The 8 x 8 float32 work matrices: rows kLd = 9 floats apart and each
+// matrix's six in a block of 432 floats, so the column reads of one matrix
+// (rows i = 0..7) and the same reads of its neighbour fall on distinct banks.
+constexpr int kLd = 9;
+constexpr int kMatF = 8 * kLd, kGroupF = 6 * kMatF;
+
 // LDS of one wavefront.
 struct WaveLds {
   char* vk;      // (m_pad + n_pad) x kRow: V rows, then K rows
-  float* f;      // kMats x 6 x 64: P, S, C, T1, N, T2
+  float* f;      // kMats x 6 matrices: P, S, C, T1, N, T2
   float* t;      // m_pad x 32 floats: V C of the four matrices (dense output only)
-  __device__ float* mat(int q, int which) const { return f + (q * 6 + which) * 64; }
+  __device__ float* mat(int q, int which) const { return f + q * kGroupF + which * kMatF; }
 };
 enum { kP = 0, kS, kC, kT1, kN, kT2 };
-constexpr int kWorkBytes = kMats * 6 * 64 * 4;
+constexpr int kWorkBytes = kMats * kGroupF * 4;
 
 // Gram of the 32 staged columns over rows [row0, row0 + rows): lane l holds
 // column l % 32, rows 8 (g / 4) + 4 (l / 32) + g % 4 of the 32 x 32 result.
@@ -82,7 +88,7 @@ __device__ __forceinline__ void store_blocks(const f32x16_t& acc, const WaveLds&
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float v = q == 0 ? acc[e] : q == 1 ? acc[4 + e] : q == 2 ? acc[8 + e] : acc[12 + e];
-    dst[(i0 + e) * 8 + j] = v;
+    dst[(i0 + e) * kLd + j] = v;
   }
 }
 
@@ -96,14 +102,14 @@ __device__ __forceinline__ void mm8(const WaveLds& L, int x, int y, int z, int l
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const float xv = X[i * 8 + c];
+    const float xv = X[i * kLd + c];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(xv, TRANS_Y ? Y[(j0 + e) * 8 + c] : Y[c * 8 + j0 + e], acc[e]);
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(xv, TRANS_Y ? Y[(j0 + e) * kLd + c] : Y[c * kLd + j0 + e], acc[e]);
   }
   wave_sync();  // every lane has read X and Y before Z (which may alias neither) is written
   float* Z = L.mat(q, z);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) Z[i * 8 + j0 + e] = acc[e];
+  for (int e = 0; e < 4; ++e) Z[i * kLd + j0 + e] = acc[e];
   wave_sync();
 }
 
@@ -125,23 +131,51 @@ __device__ __forceinline__ void core(const Args& F, const WaveLds& L, int lane) 
 
   // nu^2 = tr(P S) per matrix (16 lanes each), C_0 = I_r / (nu + eps)
   const int q = lane >> 4, i = (lane & 15) >> 1, j0 = 4 * (lane & 1);
+  float inv;
   {
     const float* P = L.mat(q, kP);
     const float* S = L.mat(q, kS);
     float t2 = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t2 = fmaf(P[i * 8 + j0 + e], S[(j0 + e) * 8 + i], t2);
+    for (int e = 0; e < 4; ++e) t2 = fmaf(P[i * kLd + j0 + e], S[(j0 + e) * kLd + i], t2);
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) t2 += __shfl_xor(t2, d, 64);
-    const float inv = 1.0f / (sqrtf(t2) + F.eps);
+    inv = 1.0f / (sqrtf(t2) + F.eps);
+  }
+  if (F.steps == 0) {
     float* C = L.mat(q, kC);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) C[i * 8 + j0 + e] = (i == j0 + e && i < r) ? inv : 0.0f;
+    for (int e = 0; e < 4; ++e) C[i * kLd + j0 + e] = (i == j0 + e && i < r) ? inv : 0.0f;
+    wave_sync();
+    return;
   }
-  wave_sync();
 
-  // the r x r recurrence (zero padding stays zero)
-  for (int k = 0; k < F.steps; ++k) {
+  // The first step from C_0 = inv I_r (P and S vanish outside the leading
+  // r x r block): C S C^T = inv^2 S, so N = inv^2 S P, N C = inv^3 S P and
+  // N N C = inv^5 (S P)^2 -- one product (two for a quintic step) instead of
+  // four (five).  The powers of inv are applied one factor at a time, so a
+  // zero product stays zero however large 1 / eps is.
+  {
+    const bool quintic = F.c[0] != 0.0f;
+    mm8<false>(L, kS, kP, kT1, lane);                 // S P
+    if (quintic) mm8<false>(L, kT1, kT1, kT2, lane);  // (S P)^2
+    float* C = L.mat(q, kC);
+    const float* SP = L.mat(q, kT1);
+    const float* SP2 = L.mat(q, kT2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int o = i * kLd + j0 + e;
+      const float c0 = (i == j0 + e && i < r) ? inv : 0.0f;
+      const float nc = ((SP[o] * inv) * inv) * inv;
+      float v = fmaf(F.a[0], c0, F.b[0] * nc);
+      if (quintic) v = fmaf(F.c[0], ((((SP2[o] * inv) * inv) * inv) * inv) * inv, v);
+      C[o] = v;
+    }
+    wave_sync();
+  }
+
+  // later steps: the r x r recurrence in full (zero padding stays zero)
+  for (int k = 1; k < F.steps; ++k) {
     mm8<false>(L, kC, kS, kT1, lane);   // C S
     mm8<true>(L, kT1, kC, kT2, lane);   // C S C^T
     mm8<false>(L, kT2, kP, kN, lane);   // N = C S C^T P
@@ -153,7 +187,7 @@ __device__ __forceinline__ void core(const Args& F, const WaveLds& L, int lane) 
     const float* NNC = L.mat(q, kT2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int o = i * 8 + j0 + e;
+      const int o = i * kLd + j0 + e;
       float v = fmaf(F.a[k], C[o], F.b[k] * NC[o]);
       if (quintic) v = fmaf(F.c[k], NNC[o], v);
       C[o] = v;

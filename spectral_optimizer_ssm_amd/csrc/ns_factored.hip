@@ -154,7 +154,7 @@ __device__ __forceinline__ void factored_compute(const FactLaunch& F, const Wave
     float* dst = F.C + (b0 + q) * r * r + i * r;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (j0 + e < r) dst[j0 + e] = C[i * 8 + j0 + e];
+      if (j0 + e < r) dst[j0 + e] = C[i * fact::kLd + j0 + e];
   }
   if (F.O == nullptr) return;
 
@@ -171,7 +171,7 @@ __device__ __forceinline__ void factored_compute(const FactLaunch& F, const Wave
       for (int d = 0; d < 8; ++d) {
         const float v = bf16_to_f32(*reinterpret_cast<const bf16_t*>(L.vk + fact::slot(t, q) + 2 * d));
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = fmaf(v, C[d * 8 + c], acc[c]);
+        for (int c = 0; c < 8; ++c) acc[c] = fmaf(v, C[d * fact::kLd + c], acc[c]);
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) L.t[t * 32 + 8 * q + c] = acc[c];

@@ -48,8 +48,10 @@ constexpr int kWaves = 4;                          // waves per workgroup
 constexpr int kRound = kWaves * fact::kMats;       // tokens per round
 constexpr int kStage = (kTileM + kTileN) * kRow;   // staged V and K rows of a wave
 constexpr int kArea = kStage + fact::kWorkBytes;   // LDS of a wave
-constexpr int kFusedLds = kWaves * kArea;          // 72 KB: two workgroups per CU
+constexpr int kFusedLds = kWaves * kArea;          // 75 KB: two workgroups per CU
 static_assert(kSsmMomQ % kRound == 0, "chunks are whole rounds");
+static_assert(kTileM * kRow <= fact::kWorkBytes, "the work area holds the 64 rows of W_S");
+static_assert(2 * kFusedLds <= 160 * 1024, "two workgroups fit a CU");
 
 // Factors of a wave's four tokens: lane l holds rows l + 64 e of their
 // concatenated V rows (e < 4) and K rows (e < 8), zero past the valid tokens;
@@ -127,7 +129,7 @@ __device__ __forceinline__ void write_w(const fact::WaveLds& L, int nv, int w, f
   const float* C = L.mat(qc, fact::kC);
   float col[8];                            // column c of core qc (rows d), or zeros
 #pragma unroll
-  for (int d = 0; d < 8; ++d) col[d] = live ? C[d * 8 + c] : 0.0f;
+  for (int d = 0; d < 8; ++d) col[d] = live ? C[d * fact::kLd + c] : 0.0f;
   const float sw[2] = {__shfl(wm, fact::kMats * w + qc), __shfl(ws, fact::kMats * w + qc)};
   // A operands for the token pairs (0, 1) and (2, 3): lane (i, kg) holds the
   // weighted column when core qc is the pair's token kg
