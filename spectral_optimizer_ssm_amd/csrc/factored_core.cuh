@@ -82,14 +82,17 @@ __device__ __forceinline__ f32x16_t gram32(const char* vk, int row0, int rows, i
 
 // Keep the diagonal 8 x 8 blocks of a gram32 result: lane l writes rows
 // 4 (l / 32) + 0..3, column l % 8 of matrix (l % 32) / 8.
+// (Each lane stores under its own matrix's branch: a select of the register
+// group by lane compiles to a 16-way select chain per value.)
 __device__ __forceinline__ void store_blocks(const f32x16_t& acc, const WaveLds& L, int which, int lane) {
   const int q = (lane & 31) >> 3, j = lane & 7, i0 = 4 * (lane >> 5);
-  float* dst = L.mat(q, which);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float v = q == 0 ? acc[e] : q == 1 ? acc[4 + e] : q == 2 ? acc[8 + e] : acc[12 + e];
-    dst[(i0 + e) * kLd + j] = v;
-  }
+  for (int qq = 0; qq < kMats; ++qq)
+    if (q == qq) {
+      float* dst = L.mat(qq, which);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(i0 + e) * kLd + j] = acc[4 * qq + e];
+    }
 }
 
 // Z = X Y (or X Y^T) for the wave's four 8 x 8 matrices; lane l handles

@@ -61,7 +61,9 @@ struct RoundRegs {
   float a;
 };
 
-// tokr: first token of the round (index into [nseq * T]); nvr: its valid tokens.
+// tokr: first token of the round (index into [nseq * T]); nvr: its valid
+// tokens.  Buffer loads through resources that end with the wave's valid
+// tokens: rows past them read as zero without a select.
 template <bool FIXED>
 __device__ __forceinline__ void load_round(const SsmMomLaunch& P, long long tokr, int nvr, int w, int lane,
                                            RoundRegs& R) {
@@ -69,19 +71,17 @@ __device__ __forceinline__ void load_round(const SsmMomLaunch& P, long long tokr
   int nv = nvr - fact::kMats * w;
   nv = nv < 0 ? 0 : nv > fact::kMats ? fact::kMats : nv;
   const long long tok = tokr + fact::kMats * w;
-  const u32x4_t* Vg = reinterpret_cast<const u32x4_t*>(P.V) + tok * m;   // one 16-byte row per rank-8 row
-  const u32x4_t* Kg = reinterpret_cast<const u32x4_t*>(P.K) + tok * n;
-  const u32x4_t z = {0u, 0u, 0u, 0u};
+  // one 16-byte row per rank-8 row
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(P.V) + tok * m * 8, static_cast<short>(0), nv * m * 16, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(P.K) + tok * n * 8, static_cast<short>(0), nv * n * 16, 0x00020000);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int c = lane + 64 * e;
-    R.v[e] = c < nv * m ? Vg[c] : z;
-  }
+  for (int e = 0; e < 4; ++e)
+    R.v[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (lane + 64 * e) * 16, 0, 0));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = lane + 64 * e;
-    R.k[e] = c < nv * n ? Kg[c] : z;
-  }
+  for (int e = 0; e < 8; ++e)
+    R.k[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (lane + 64 * e) * 16, 0, 0));
   const int j = lane & 31;
   R.a = (P.a != nullptr && j < nvr) ? P.a[tokr + j] : 1.0f;
 }
@@ -230,15 +230,17 @@ __device__ __forceinline__ RoundMap round_map(float beta, float a, bool with_s, 
   return R;
 }
 
-template <bool FIXED>
-__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) ssm_momentum_fused_kernel(SsmMomLaunch P) {
+// FIXED: the 64 x 128 shape; WITH_S: the memory state is carried (P.S given).
+template <bool FIXED, bool WITH_S>
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+ssm_momentum_fused_kernel(SsmMomLaunch P) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long nitems = P.nseq * P.nchunks;
   long long it = blockIdx.x;
   if (it >= nitems) return;  // (the grid holds no more workgroups than items)
-  const bool with_s = P.S != nullptr;
+  constexpr bool with_s = WITH_S;
   char* area = lds + w * kArea;
   fact::WaveLds L;
   L.vk = area;
@@ -389,17 +391,24 @@ hipError_t launch_ssm_momentum(const SsmMomLaunch& P, hipStream_t st, int phase)
     return hipErrorInvalidValue;
   if (phase == 0) {
     const long long items = P.nseq * P.nchunks;
-    const long long slots = 2LL * device_cus();  // 72 KB of LDS: two workgroups per CU
+    const long long slots = 2LL * device_cus();  // 75 KB of LDS: two workgroups per CU
     const unsigned blocks = static_cast<unsigned>(items < slots ? items : slots);
-    const bool fixed = P.m == kTileM && P.n == kTileN;
-    const void* fn = fixed ? reinterpret_cast<const void*>(ssm_momentum_fused_kernel<true>)
-                           : reinterpret_cast<const void*>(ssm_momentum_fused_kernel<false>);
+    const bool fixed = P.m == kTileM && P.n == kTileN, with_s = P.S != nullptr;
+    const void* fn = fixed ? (with_s ? reinterpret_cast<const void*>(ssm_momentum_fused_kernel<true, true>)
+                                     : reinterpret_cast<const void*>(ssm_momentum_fused_kernel<true, false>))
+                           : (with_s ? reinterpret_cast<const void*>(ssm_momentum_fused_kernel<false, true>)
+                                     : reinterpret_cast<const void*>(ssm_momentum_fused_kernel<false, false>));
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds) != hipSuccess)
       return hipErrorInvalidValue;
-    if (fixed)
-      hipLaunchKernelGGL(ssm_momentum_fused_kernel<true>, dim3(blocks), dim3(kWaves * 64), kFusedLds, st, P);
+    const dim3 grid(blocks), block(kWaves * 64);
+    if (fixed && with_s)
+      hipLaunchKernelGGL((ssm_momentum_fused_kernel<true, true>), grid, block, kFusedLds, st, P);
+    else if (fixed)
+      hipLaunchKernelGGL((ssm_momentum_fused_kernel<true, false>), grid, block, kFusedLds, st, P);
+    else if (with_s)
+      hipLaunchKernelGGL((ssm_momentum_fused_kernel<false, true>), grid, block, kFusedLds, st, P);
     else
-      hipLaunchKernelGGL(ssm_momentum_fused_kernel<false>, dim3(blocks), dim3(kWaves * 64), kFusedLds, st, P);
+      hipLaunchKernelGGL((ssm_momentum_fused_kernel<false, false>), grid, block, kFusedLds, st, P);
   } else {
     const long long blocks = (P.nseq * P.m * P.n + 255) / 256;
     hipLaunchKernelGGL(ssm_momentum_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, P);
