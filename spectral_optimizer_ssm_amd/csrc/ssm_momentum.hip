@@ -15,22 +15,23 @@
 //   M' = beta^L M + sum_u beta^(L-1-u) U_u
 //   S' = A S + B M + sum_u w_u U_u,   A = prod_u a_u,   B = beta w_0,
 //   w_u = g_u + beta w_{u+1} (w_L = 0),   g_u = prod_{s>u} a_s.
-// The fused kernel takes a chunk of 256 tokens in rounds of 32: per round it
-// applies the round's map to its running sums and adds the round's weighted
-// products, which yields the chunk's sums; the chunk's map is the rounds'
-// maps composed.  The combine kernel applies the chunk maps in token order to
-// the caller's (S, M).  Maps and sums are the recurrence regrouped (the
+// The fused kernel forms the two sums of a chunk of 256 tokens with the
+// weights taken relative to the chunk's end, and the chunk's map (beta^L, A,
+// B); the combine kernel applies the chunk maps in token order to the
+// caller's (S, M).  Maps and sums are the recurrence regrouped (the
 // block-affine structure the pages point to).
 //
-// Fused kernel: one workgroup of eight waves per (sequence, chunk), persistent
-// over chunks.  In a round each wave stages four tokens' V and K in its own
-// LDS area (factored_core.cuh layout), loads the next round's factors into
-// registers, runs the core and overwrites its V rows with W = V C (bf16).
-// After a barrier wave w accumulates block (rows 32 (w % 2), columns
-// 32 (w / 2)) of the zero-padded 64 x 128 state tile over the round's 32
-// tokens on v_mfma_f32_32x32x16_bf16, the contraction index being (token
-// pair, rank): W rows are the A operand, the K row scaled by the token's
-// weight (one per partial sum) and rounded to bf16 the B operand.  The next
+// Fused kernel: one workgroup of four waves per (sequence, chunk), persistent
+// over chunks, two workgroups per CU.  At a chunk's start every wave computes
+// its weights by suffix scans over the chunk's decays.  In a round of 16
+// tokens each wave stages four tokens' V and K in its own LDS area
+// (factored_core.cuh layout), loads the next round's factors into registers,
+// runs the core and forms the weighted factors W_M = V (wm C) over its V rows
+// and W_S = V (ws C) in its work area on the matrix cores.  After a barrier
+// wave w accumulates the column block 32 w .. 32 w + 31 (both 32-row blocks)
+// of the zero-padded 64 x 128 tiles of both sums over the round's tokens on
+// v_mfma_f32_32x32x16_bf16, the contraction index being (token pair, rank):
+// weighted-factor rows are the A operand, K rows the B operand.  The next
 // round's barrier keeps the areas until every wave has read them.
 #include "common.cuh"
 #include "factored_core.cuh"
@@ -54,11 +55,9 @@ static_assert(kTileM * kRow <= fact::kWorkBytes, "the work area holds the 64 row
 static_assert(2 * kFusedLds <= 160 * 1024, "two workgroups fit a CU");
 
 // Factors of a wave's four tokens: lane l holds rows l + 64 e of their
-// concatenated V rows (e < 4) and K rows (e < 8), zero past the valid tokens;
-// and the decay of token l % 32 of the round (1 past the valid tokens).
+// concatenated V rows (e < 4) and K rows (e < 8), zero past the valid tokens.
 struct RoundRegs {
   u32x4_t v[4], k[8];
-  float a;
 };
 
 // tokr: first token of the round (index into [nseq * T]); nvr: its valid
@@ -82,8 +81,6 @@ __device__ __forceinline__ void load_round(const SsmMomLaunch& P, long long tokr
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     R.k[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (lane + 64 * e) * 16, 0, 0));
-  const int j = lane & 31;
-  R.a = (P.a != nullptr && j < nvr) ? P.a[tokr + j] : 1.0f;
 }
 
 // Row t of token q goes to staged row t, slot q; K rows after the 64 V rows.
@@ -121,7 +118,7 @@ __device__ __forceinline__ void stage_round(const SsmMomLaunch& P, char* vk, con
 // the exact bf16 V the float32 products and sums match a float32 V (w C) to
 // about 2^-16 before the one rounding of W to bf16.  Every V row and core is
 // read before any W row is written; rows past m stay zero.
-__device__ __forceinline__ void write_w(const fact::WaveLds& L, int nv, int w, float wm, float ws, bool with_s,
+__device__ __forceinline__ void write_w(const fact::WaveLds& L, int nv, float wmq, float wsq, bool with_s,
                                         int lane) {
   const int i = lane & 31, kg = lane >> 5;
   const int qc = i >> 3, c = i & 7;        // A operand row: core qc, column c
@@ -130,7 +127,7 @@ __device__ __forceinline__ void write_w(const fact::WaveLds& L, int nv, int w, f
   float col[8];                            // column c of core qc (rows d), or zeros
 #pragma unroll
   for (int d = 0; d < 8; ++d) col[d] = live ? C[d * fact::kLd + c] : 0.0f;
-  const float sw[2] = {__shfl(wm, fact::kMats * w + qc), __shfl(ws, fact::kMats * w + qc)};
+  const float sw[2] = {wmq, wsq};   // the two weights of core qc
   // A operands for the token pairs (0, 1) and (2, 3): lane (i, kg) holds the
   // weighted column when core qc is the pair's token kg
   bf16x8_t ahi[2][2], alo[2][2];   // [sum][pair]
@@ -182,52 +179,69 @@ __device__ __forceinline__ void write_w(const fact::WaveLds& L, int nv, int w, f
   }
 }
 
-// Weights and map of a round of nvr tokens, on lane j = lane % 32 (both
-// halves of the wave alike):
-//   wm_j = beta^(nvr-1-j),  ws_j = w_j = sum_{v=j}^{nvr-1} beta^(v-j) g_v,
-//   g_v = prod_{s>v} a_s;  map: bl = beta^nvr, A = prod a, B = beta w_0.
-// Suffix scans over the 32 lanes; tokens past nvr act as the identity
-// (a = 1, no beta factor, no term).
-struct RoundMap {
-  float wm, ws, bl, A, B;
+// Weights of a chunk's len tokens relative to its end, token t = 4 l + i on
+// lane l (i < 4), and the chunk's map:
+//   wm_t = beta^(len-1-t),  ws_t = w_t = sum_{v=t}^{len-1} beta^(v-t) g_v,
+//   g_v = prod_{s>v} a_s;  map: bl = beta^len, A = prod a, B = beta w_0.
+// Each lane summarises its four tokens as (pa, pf, s) = (prod a, beta^(its
+// tokens), w of its first token counting only its own tokens); a suffix scan
+// over the lanes joins a segment L with the one after it, R, as
+// (pa_L pa_R, pf_L pf_R, pa_R s_L + pf_L s_R); each lane then walks its four
+// tokens backwards from the summary of the lanes after it.  Every wave of the
+// workgroup computes the same values.
+struct ChunkW {
+  float wm[4], ws[4];
+  float bl, A, B;
 };
-__device__ __forceinline__ RoundMap round_map(float beta, float a, bool with_s, int nvr, int lane) {
-  const int j = lane & 31;
-  const bool valid = j < nvr;
-  const float fb = valid ? beta : 1.0f;
-  float pf = fb, pa = a;   // inclusive suffix products of beta and of a
+template <bool WITH_S>
+__device__ __forceinline__ ChunkW chunk_weights(const SsmMomLaunch& P, long long tok0, int len, int lane) {
+  const float beta = P.beta;
+  float a[4];
 #pragma unroll
-  for (int d = 1; d < 32; d <<= 1) {
-    const float of = __shfl_down(pf, d, 32), oa = __shfl_down(pa, d, 32);
-    if (j + d < 32) {
-      pf *= of;
+  for (int i = 0; i < 4; ++i) {
+    const int t = 4 * lane + i;
+    a[i] = (WITH_S && t < len) ? P.a[tok0 + t] : 1.0f;
+  }
+  float pa = 1.0f, pf = 1.0f, sv = 0.0f;
+#pragma unroll
+  for (int i = 3; i >= 0; --i)
+    if (4 * lane + i < len) {
+      sv = fmaf(beta, sv, pa);
+      pa *= a[i];
+      pf *= beta;
+    }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float oa = __shfl_down(pa, d, 64), of = __shfl_down(pf, d, 64), os = __shfl_down(sv, d, 64);
+    if (lane + d < 64) {
+      sv = fmaf(pf, os, sv * oa);
       pa *= oa;
+      pf *= of;
     }
   }
-  float wm = __shfl_down(pf, 1, 32), g = __shfl_down(pa, 1, 32);
-  if (j == 31) wm = g = 1.0f;
-  RoundMap R;
-  R.wm = wm;
-  R.bl = __shfl(pf, 0, 32);
-  R.ws = 0.0f;
-  R.A = R.B = 0.0f;
-  if (with_s) {
-    // segments (s, f) = (sum of beta^(v-j) g_v over the segment, beta^(its valid tokens)),
-    // joined as (s1 + f1 s2, f1 f2)
-    float s = valid ? g : 0.0f, f = fb;
+  // the lanes after this one: exclusive values
+  float ga = __shfl_down(pa, 1, 64), gf = __shfl_down(pf, 1, 64), w = __shfl_down(sv, 1, 64);
+  if (lane == 63) {
+    ga = 1.0f;
+    gf = 1.0f;
+    w = 0.0f;
+  }
+  ChunkW C;
 #pragma unroll
-    for (int d = 1; d < 32; d <<= 1) {
-      const float os = __shfl_down(s, d, 32), of = __shfl_down(f, d, 32);
-      if (j + d < 32) {
-        s = fmaf(f, os, s);
-        f *= of;
-      }
+  for (int i = 3; i >= 0; --i) {
+    const bool valid = 4 * lane + i < len;   // tokens past len: no term, no factor
+    if (valid) w = fmaf(beta, w, ga);
+    C.wm[i] = valid ? gf : 0.0f;
+    C.ws[i] = valid ? w : 0.0f;
+    if (valid) {
+      ga *= a[i];
+      gf *= beta;
     }
-    R.ws = s;
-    R.A = __shfl(pa, 0, 32);
-    R.B = beta * __shfl(s, 0, 32);
   }
-  return R;
+  C.bl = __shfl(pf, 0, 64);
+  C.A = WITH_S ? __shfl(pa, 0, 64) : 0.0f;
+  C.B = WITH_S ? beta * __shfl(C.ws[0], 0, 64) : 0.0f;
+  return C;
 }
 
 // FIXED: the 64 x 128 shape; WITH_S: the memory state is carried (P.S given).
@@ -263,19 +277,19 @@ ssm_momentum_fused_kernel(SsmMomLaunch P) {
 
   const int G = lane >> 5, l32 = lane & 31;
   const int krow = kTileM + 32 * w + l32;   // wave w: tile columns 32 w .. 32 w + 31
+  const int qc = l32 >> 3;                  // the core whose weights this lane applies
   for (;;) {
     const int nr = (len + kRound - 1) / kRound;
+    const ChunkW cw = chunk_weights<WITH_S>(P, tok0, len, lane);
     f32x16_t accM[2], accS[2];   // row blocks 0 and 1
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) accM[rb][r] = accS[rb][r] = 0.0f;
-    float cbl = 1.0f, ca = 1.0f, cB = 0.0f;   // the chunk's map so far
     for (int rd = 0; rd < nr; ++rd) {
       const int nvr = len - kRound * rd < kRound ? len - kRound * rd : kRound;
       __syncthreads();  // every wave is done with the previous round's areas
       stage_round<FIXED>(P, area, R, lane);
-      const float a_cur = R.a;
       wave_sync();
       // the next round's factors load while this round is computed
       if (rd + 1 < nr) {
@@ -287,25 +301,23 @@ ssm_momentum_fused_kernel(SsmMomLaunch P) {
         chunk(it + gridDim.x, tok2, len2);
         load_round<FIXED>(P, tok2, len2 < kRound ? len2 : kRound, w, lane, R);
       }
-      const RoundMap map = round_map(P.beta, a_cur, with_s, nvr, lane);
+      // weights of the wave's tokens 16 rd + 4 w + i (i < 4), held by lane
+      // 4 rd + w; this lane applies those of its core qc
+      const int src_lane = fact::kMats * rd + w;
+      float wm_r[4], ws_r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wm_r[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cw.wm[i]), src_lane));
+        ws_r[i] = WITH_S ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cw.ws[i]), src_lane)) : 0.0f;
+      }
+      const float wmq = qc == 0 ? wm_r[0] : qc == 1 ? wm_r[1] : qc == 2 ? wm_r[2] : wm_r[3];
+      const float wsq = qc == 0 ? ws_r[0] : qc == 1 ? ws_r[1] : qc == 2 ? ws_r[2] : ws_r[3];
       fact::core(P.ns, L, lane);
       int nv = nvr - fact::kMats * w;
       nv = nv < 0 ? 0 : nv;
-      write_w(L, nv, w, map.wm, map.ws, with_s, lane);
+      write_w(L, nv, wmq, wsq, with_s, lane);
       __syncthreads();  // every wave's weighted factors and K rows are staged
 
-      // the round's map on the running sums (S uses the old M), then its products
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float mv = accM[rb][r];
-          accM[rb][r] = map.bl * mv;
-          if (with_s) accS[rb][r] = fmaf(map.A, accS[rb][r], map.B * mv);
-        }
-      cB = fmaf(map.A, cB, map.B * cbl);
-      ca *= map.A;
-      cbl *= map.bl;
       for (int tp = 0; 2 * tp < nvr; ++tp) {
         // token 2 tp + G lives in wave tp / 2's area, slot q; tokens past nvr
         // have zero factors
@@ -350,9 +362,9 @@ ssm_momentum_fused_kernel(SsmMomLaunch P) {
     }
     if (tid == 0) {
       float* cf = P.coef + it * 4;
-      cf[0] = cbl;
-      cf[1] = with_s ? ca : 0.0f;
-      cf[2] = with_s ? cB : 0.0f;
+      cf[0] = cw.bl;
+      cf[1] = cw.A;
+      cf[2] = cw.B;
       cf[3] = 0.0f;
     }
     it += gridDim.x;

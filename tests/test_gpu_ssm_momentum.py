@@ -98,15 +98,15 @@ def test_ssm_momentum_zero_beta_and_decay_is_last_token(mu):
 
 def test_ssm_momentum_consecutive_calls_carry_the_states(mu):
     """Two calls over parts of a sequence give the one-call result: the
-    states carry over.  Each token's factor enters the sums weighted and
-    rounded once to bf16 (2^-9 relative, about 1.1e-3 RMS per element), and
-    its weight depends on where the token's round of 16 starts, which the
-    split moves; M and S are dominated by the last few tokens (beta = 0.875),
-    so the two results differ by about one such rounding: 1.4e-3 (M) and
-    1.9e-3 (S) in an fp64 emulation of this arithmetic, hence the bound of
-    4e-3.  A state dropped or misapplied at the split changes them by O(1);
-    the two-call result also stays within the parity tolerance of the
-    oracle."""
+    states carry over.  Each token's factor enters the sums weighted relative
+    to the end of its 256-token chunk and rounded once to bf16 (2^-9
+    relative), so tokens whose chunk ends differently in the two runs are
+    rounded differently.  The last chunk ends with the sequence in both runs
+    and its tokens dominate M (beta = 0.875); S keeps older tokens longer.
+    An fp64 emulation of this arithmetic gives 1.7e-6 (M) and 1.2e-4 (S) for
+    this split, hence the bound of 1e-3.  A state dropped or misapplied at
+    the split changes them by O(1); the two-call result also stays within
+    the parity tolerance of the oracle."""
     V, K, a, M0, S0 = wl.ssm_sequences(2, 500, 64, 128, seed=10)
     M1, S1 = run(mu, V, K, a, M0, S0, wl.SSM_BETA, 1)
     h = 190
@@ -114,7 +114,7 @@ def test_ssm_momentum_consecutive_calls_carry_the_states(mu):
     M2, S2 = run(mu, V[:, h:].contiguous(), K[:, h:].contiguous(), a[:, h:].contiguous(), Mh, Sh, wl.SSM_BETA, 1)
     dm, ds = orc.rel_frobenius(f64(M2), f64(M1)), orc.rel_frobenius(f64(S2), f64(S1))
     print(f"[parity] ssm_momentum split at {h}: M {dm:.3e} S {ds:.3e}", flush=True)
-    assert dm <= 4e-3 and ds <= 4e-3
+    assert dm <= 1e-3 and ds <= 1e-3
     Mr, Sr = oracle_states(V, K, a, M0, S0, 0, wl.SSM_BETA, 1)
     assert orc.rel_frobenius(f64(M2[0]), Mr) <= BF16_TOL
     assert orc.rel_frobenius(f64(S2[0]), Sr) <= BF16_TOL
