@@ -373,7 +373,8 @@ ssm_momentum_fused_kernel(SsmMomLaunch P) {
   }
 }
 
-// (S, M) <- chunk maps in token order; one thread per state element.
+// (S, M) <- chunk maps in token order; one thread per state element, the
+// partials of four chunks loaded before they are applied.
 __global__ void __launch_bounds__(256) ssm_momentum_combine_kernel(SsmMomLaunch P) {
   const long long mn = static_cast<long long>(P.m) * P.n;
   const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
@@ -382,14 +383,31 @@ __global__ void __launch_bounds__(256) ssm_momentum_combine_kernel(SsmMomLaunch 
   const int e = static_cast<int>(idx - seq * mn);
   const int i = e / P.n, j = e - i * P.n;
   const bool with_s = P.S != nullptr;
-  const int nout = with_s ? 2 : 1;
+  const long long stride = (with_s ? 2 : 1) * static_cast<long long>(kTile);   // floats per chunk
+  const float* pb = P.part + seq * P.nchunks * stride + i * kTileN + j;
+  const float4* cf = reinterpret_cast<const float4*>(P.coef) + seq * P.nchunks;
   float M = P.M[idx];
   float S = with_s ? P.S[idx] : 0.0f;
-  for (int c = 0; c < P.nchunks; ++c) {
-    const float* cf = P.coef + (seq * P.nchunks + c) * 4;
-    const float* pb = P.part + (seq * P.nchunks + c) * nout * static_cast<long long>(kTile) + i * kTileN + j;
-    if (with_s) S = fmaf(cf[1], S, fmaf(cf[2], M, pb[kTile]));
-    M = fmaf(cf[0], M, pb[0]);
+  int c = 0;
+  for (; c + 4 <= P.nchunks; c += 4) {
+    float pm[4], ps[4];
+    float4 k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      pm[u] = pb[(c + u) * stride];
+      ps[u] = with_s ? pb[(c + u) * stride + kTile] : 0.0f;
+      k[u] = cf[c + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (with_s) S = fmaf(k[u].y, S, fmaf(k[u].z, M, ps[u]));
+      M = fmaf(k[u].x, M, pm[u]);
+    }
+  }
+  for (; c < P.nchunks; ++c) {
+    const float4 k = cf[c];
+    if (with_s) S = fmaf(k.y, S, fmaf(k.z, M, pb[c * stride + kTile]));
+    M = fmaf(k.x, M, pb[c * stride]);
   }
   P.M[idx] = M;
   if (with_s) P.S[idx] = S;
