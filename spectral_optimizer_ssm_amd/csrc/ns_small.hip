@@ -619,32 +619,40 @@ constexpr int kRtMaxL = 512;
 constexpr int kMaxLds = 160 * 1024;
 
 // ---- float32: one workgroup per matrix --------------------------------------
-// fp32: one workgroup of four waves per matrix on the fp32 matrix cores
-// (v_mfma_f32_32x32x2f32: fp32 products, fp32 accumulation).  X (s x l, s <=
-// 64, l <= LMAX) sits in LDS zero-padded to multiples of 32 on both sides; the
-// Gram's 32 x 32 blocks go to the four waves (block (w / 2, w % 2)), then the
-// combine's blocks (row block, column block w, w + 4, ...).  Operands are one
-// float per lane per MFMA: A[i][k] from lane (k % 2) * 32 + i, B[k][j] from
-// lane (k % 2) * 32 + j; the result's lane l holds column l % 32, rows
-// 8 q + 4 (l / 32) + e in register 4 q + e.
+// fp32: one workgroup of eight waves per matrix on the fp32 matrix cores
+// (fp32 products, fp32 accumulation).  X (s x l, s <= 64, l <= LMAX) sits in
+// LDS zero-padded to multiples of 32 on both sides.  Per step:
+//  * the Gram A = X X^T on its upper 16 x 16 blocks (ti <= tj; ten for s = 64),
+//    dealt to the waves, v_mfma_f32_16x16x4f32: A[i][k] from lane
+//    16 (k % 4) + i, B[k][j] from lane 16 (k % 4) + j, the result's lane l
+//    holding column l % 16, rows 4 (l / 16) + e; each block is stored with
+//    its mirror, so A is exactly symmetric;
+//  * the combine Y = a X + b A X on 32 x 32 blocks (row block, column block),
+//    dealt to the waves, v_mfma_f32_32x32x2f32: A[i][k] from lane
+//    (k % 2) * 32 + i, B[k][j] from lane (k % 2) * 32 + j, the result's lane l
+//    holding column l % 32, rows 8 q + 4 (l / 32) + e in register 4 q + e.
+// A single matrix runs on one CU, so its step time is the dependent chain of
+// each wave's products: eight waves and the Gram's symmetry halve it against
+// four waves taking the four 32 x 32 Gram blocks and two combine blocks each.
 template <int LMAX>
-__global__ void __launch_bounds__(256) ns_small_f32_kernel(NsSmallLaunch P) {
-  // odd row strides: the operands are read down columns (32 lanes, 32 rows)
-  constexpr int SMAX = 64, XS = LMAX + 1, AS = SMAX + 1;
+__global__ void __launch_bounds__(512) ns_small_f32_kernel(NsSmallLaunch P) {
+  // odd row strides: the operands are read down columns
+  constexpr int SMAX = 64, XS = LMAX + 1, AS = SMAX + 1, NT = 512, NW = NT / 64;
   __shared__ float xa[SMAX][XS];
   __shared__ float xb[SMAX][XS];
   __shared__ float am[SMAX][AS];
-  __shared__ float red[4];
+  __shared__ float red[NW];
   const int S = P.s, Lw = P.l, tid = threadIdx.x;
   const int Sp = (S + 31) & ~31, Lp = (Lw + 31) & ~31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int G = lane >> 5, l32 = lane & 31;
+  const int r16 = lane & 15, kq = lane >> 4;
   for (long long mat = blockIdx.x; mat < P.count; mat += gridDim.x) {
     const float* src = static_cast<const float*>(P.X) + mat * P.in_stride;
     float* dst = static_cast<float*>(P.Y) + mat * P.out_stride;
     // stage X, zero padded to Sp x Lp (the padding stays zero through every step)
     float ss = 0.0f;
-    for (int e = tid; e < Sp * Lp; e += 256) {
+    for (int e = tid; e < Sp * Lp; e += NT) {
       int i, k;
       if (P.transposed) {  // stored as l x s: consecutive threads read consecutive i
         i = e % Sp; k = e / Sp;
@@ -660,63 +668,68 @@ __global__ void __launch_bounds__(256) ns_small_f32_kernel(NsSmallLaunch P) {
     float inv;
     if (P.partials != nullptr) {
       float s2 = 0.0f;
-      for (int i = tid; i < P.P; i += 256) s2 += P.partials[mat * P.P + i];
+      for (int i = tid; i < P.P; i += NT) s2 += P.partials[mat * P.P + i];
       inv = 1.0f / (sqrtf(block_sum(s2, red)) + P.eps);
     } else {
       inv = 1.0f / (sqrtf(block_sum(ss, red)) + P.eps);
     }
     __syncthreads();
-    for (int e = tid; e < Sp * Lp; e += 256) xa[e / Lp][e % Lp] *= inv;
+    for (int e = tid; e < Sp * Lp; e += NT) xa[e / Lp][e % Lp] *= inv;
     __syncthreads();
     float (*cur)[XS] = xa;
     float (*nxt)[XS] = xb;
-    const int nbs = Sp / 32, nbl = Lp / 32;
+    const int nbs = Sp / 32, nbl = Lp / 32, n16 = Sp / 16, nu = n16 * (n16 + 1) / 2;
     for (int step = 0; step < P.steps; ++step) {
-      // Gram A = X X^T: block (bi, bj) per wave
-      const int bi = w >> 1, bj = w & 1;
-      if (bi < nbs && bj < nbs) {
-        f32x16_t g;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) g[r] = 0.0f;
+      // Gram: upper 16 x 16 block u (row-major over ti <= tj) per wave
+      for (int u = w; u < nu; u += NW) {
+        int ti = 0, rem = u;
+        while (rem >= n16 - ti) {
+          rem -= n16 - ti;
+          ++ti;
+        }
+        const int tj = ti + rem;
+        f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
-        for (int k = 0; k < Lp; k += 2) {
-          const float av = cur[bi * 32 + l32][k + G];
-          const float bv = cur[bj * 32 + l32][k + G];
-          g = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, g, 0, 0, 0);
+        for (int k = 0; k < Lp; k += 4) {
+          const float av = cur[ti * 16 + r16][k + kq];
+          const float bv = cur[tj * 16 + r16][k + kq];
+          g = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, g, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = ti * 16 + 4 * kq + e, j = tj * 16 + r16;
+          am[i][j] = g[e];
+          if (ti != tj) am[j][i] = g[e];
+        }
+      }
+      __syncthreads();
+      // combine Y = a X + b A X: 32 x 32 block (bi2, bk) per wave
+      const float a = P.a[step], b = P.b[step];
+      for (int blk = w; blk < nbs * nbl; blk += NW) {
+        const int bi2 = blk % nbs, bk = blk / nbs;
+        f32x16_t y;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[r] = 0.0f;
+#pragma unroll 4
+        for (int j = 0; j < Sp; j += 2) {
+          const float av = am[bi2 * 32 + l32][j + G];
+          const float bv = cur[j + G][bk * 32 + l32];
+          y = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, y, 0, 0, 0);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) am[bi * 32 + 8 * q + 4 * G + e][bj * 32 + l32] = g[4 * q + e];
-      }
-      __syncthreads();
-      // combine Y = a X + b A X: blocks (bi, bk), bk = w, w + 4, ...
-      const float a = P.a[step], b = P.b[step];
-      for (int bk = w; bk < nbl; bk += 4)
-        for (int bi2 = 0; bi2 < nbs; ++bi2) {
-          f32x16_t y;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) y[r] = 0.0f;
-#pragma unroll 4
-          for (int j = 0; j < Sp; j += 2) {
-            const float av = am[bi2 * 32 + l32][j + G];
-            const float bv = cur[j + G][bk * 32 + l32];
-            y = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, y, 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const int i = bi2 * 32 + 8 * q + 4 * G + e, k = bk * 32 + l32;
+            nxt[i][k] = fmaf(a, cur[i][k], b * y[4 * q + e]);
           }
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = bi2 * 32 + 8 * q + 4 * G + e, k = bk * 32 + l32;
-              nxt[i][k] = fmaf(a, cur[i][k], b * y[4 * q + e]);
-            }
-        }
+      }
       __syncthreads();
       float (*t)[XS] = cur;
       cur = nxt;
       nxt = t;
     }
-    for (int e = tid; e < S * Lw; e += 256) {
+    for (int e = tid; e < S * Lw; e += NT) {
       if (P.transposed) {
         const int i = e % S, k = e / S;
         dst[static_cast<long long>(k) * P.ld_out + i] = cur[i][k];
@@ -800,9 +813,9 @@ hipError_t launch_ns_small(const NsSmallLaunch& P, bool bf16, hipStream_t st) {
   }
   const long long blocks = small_grid(P.count, 1LL << 16);
   if (P.l <= 128)
-    hipLaunchKernelGGL((ns_small_f32_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, P);
+    hipLaunchKernelGGL((ns_small_f32_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, P);
   else
-    hipLaunchKernelGGL((ns_small_f32_kernel<256>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, P);
+    hipLaunchKernelGGL((ns_small_f32_kernel<256>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, P);
   return hipGetLastError();
 }
 
