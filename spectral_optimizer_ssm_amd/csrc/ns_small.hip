@@ -619,25 +619,23 @@ constexpr int kRtMaxL = 512;
 constexpr int kMaxLds = 160 * 1024;
 
 // ---- float32: one workgroup per matrix --------------------------------------
-// fp32: one workgroup of eight waves per matrix on the fp32 matrix cores
-// (fp32 products, fp32 accumulation).  X (s x l, s <= 64, l <= LMAX) sits in
-// LDS zero-padded to multiples of 32 on both sides.  Per step:
+// fp32: one workgroup of sixteen waves per matrix on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32: fp32 products, fp32 accumulation).  X (s x l,
+// s <= 64, l <= LMAX) sits in LDS zero-padded to multiples of 32 on both
+// sides.  Operands are one float per lane per MFMA: A[i][k] from lane
+// 16 (k % 4) + i, B[k][j] from lane 16 (k % 4) + j; the result's lane l holds
+// column l % 16, rows 4 (l / 16) + e.  Per step:
 //  * the Gram A = X X^T on its upper 16 x 16 blocks (ti <= tj; ten for s = 64),
-//    dealt to the waves, v_mfma_f32_16x16x4f32: A[i][k] from lane
-//    16 (k % 4) + i, B[k][j] from lane 16 (k % 4) + j, the result's lane l
-//    holding column l % 16, rows 4 (l / 16) + e; each block is stored with
-//    its mirror, so A is exactly symmetric;
-//  * the combine Y = a X + b A X on 32 x 32 blocks (row block, column block),
-//    dealt to the waves, v_mfma_f32_32x32x2f32: A[i][k] from lane
-//    (k % 2) * 32 + i, B[k][j] from lane (k % 2) * 32 + j, the result's lane l
-//    holding column l % 32, rows 8 q + 4 (l / 32) + e in register 4 q + e.
+//    dealt to the waves, each stored with its mirror (A exactly symmetric);
+//  * the combine Y = a X + b A X on 16 x 16 blocks (32 for 64 x 128), dealt
+//    to the waves.
 // A single matrix runs on one CU, so its step time is the dependent chain of
-// each wave's products: eight waves and the Gram's symmetry halve it against
-// four waves taking the four 32 x 32 Gram blocks and two combine blocks each.
+// each wave's products: sixteen waves on 16 x 16 blocks and the Gram's
+// symmetry cut it to a quarter of four waves on 32 x 32 blocks.
 template <int LMAX>
-__global__ void __launch_bounds__(512) ns_small_f32_kernel(NsSmallLaunch P) {
+__global__ void __launch_bounds__(1024) ns_small_f32_kernel(NsSmallLaunch P) {
   // odd row strides: the operands are read down columns
-  constexpr int SMAX = 64, XS = LMAX + 1, AS = SMAX + 1, NT = 512, NW = NT / 64;
+  constexpr int SMAX = 64, XS = LMAX + 1, AS = SMAX + 1, NT = 1024, NW = NT / 64;
   __shared__ float xa[SMAX][XS];
   __shared__ float xb[SMAX][XS];
   __shared__ float am[SMAX][AS];
@@ -645,7 +643,6 @@ __global__ void __launch_bounds__(512) ns_small_f32_kernel(NsSmallLaunch P) {
   const int S = P.s, Lw = P.l, tid = threadIdx.x;
   const int Sp = (S + 31) & ~31, Lp = (Lw + 31) & ~31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int G = lane >> 5, l32 = lane & 31;
   const int r16 = lane & 15, kq = lane >> 4;
   for (long long mat = blockIdx.x; mat < P.count; mat += gridDim.x) {
     const float* src = static_cast<const float*>(P.X) + mat * P.in_stride;
@@ -678,7 +675,7 @@ __global__ void __launch_bounds__(512) ns_small_f32_kernel(NsSmallLaunch P) {
     __syncthreads();
     float (*cur)[XS] = xa;
     float (*nxt)[XS] = xb;
-    const int nbs = Sp / 32, nbl = Lp / 32, n16 = Sp / 16, nu = n16 * (n16 + 1) / 2;
+    const int n16 = Sp / 16, nu = n16 * (n16 + 1) / 2;
     for (int step = 0; step < P.steps; ++step) {
       // Gram: upper 16 x 16 block u (row-major over ti <= tj) per wave
       for (int u = w; u < nu; u += NW) {
@@ -703,26 +700,23 @@ __global__ void __launch_bounds__(512) ns_small_f32_kernel(NsSmallLaunch P) {
         }
       }
       __syncthreads();
-      // combine Y = a X + b A X: 32 x 32 block (bi2, bk) per wave
+      // combine Y = a X + b A X: 16 x 16 block (ti, tk) per wave
       const float a = P.a[step], b = P.b[step];
-      for (int blk = w; blk < nbs * nbl; blk += NW) {
-        const int bi2 = blk % nbs, bk = blk / nbs;
-        f32x16_t y;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) y[r] = 0.0f;
+      const int n16l = Lp / 16;
+      for (int blk = w; blk < n16 * n16l; blk += NW) {
+        const int ti = blk % n16, tk = blk / n16;
+        f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
-        for (int j = 0; j < Sp; j += 2) {
-          const float av = am[bi2 * 32 + l32][j + G];
-          const float bv = cur[j + G][bk * 32 + l32];
-          y = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, y, 0, 0, 0);
+        for (int j = 0; j < Sp; j += 4) {
+          const float av = am[ti * 16 + r16][j + kq];
+          const float bv = cur[j + kq][tk * 16 + r16];
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, y, 0, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = bi2 * 32 + 8 * q + 4 * G + e, k = bk * 32 + l32;
-            nxt[i][k] = fmaf(a, cur[i][k], b * y[4 * q + e]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int i = ti * 16 + 4 * kq + e, k = tk * 16 + r16;
+          nxt[i][k] = fmaf(a, cur[i][k], b * y[e]);
+        }
       }
       __syncthreads();
       float (*t)[XS] = cur;
@@ -813,9 +807,9 @@ hipError_t launch_ns_small(const NsSmallLaunch& P, bool bf16, hipStream_t st) {
   }
   const long long blocks = small_grid(P.count, 1LL << 16);
   if (P.l <= 128)
-    hipLaunchKernelGGL((ns_small_f32_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, P);
+    hipLaunchKernelGGL((ns_small_f32_kernel<128>), dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, st, P);
   else
-    hipLaunchKernelGGL((ns_small_f32_kernel<256>), dim3(static_cast<unsigned>(blocks)), dim3(512), 0, st, P);
+    hipLaunchKernelGGL((ns_small_f32_kernel<256>), dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, st, P);
   return hipGetLastError();
 }
 
