@@ -533,6 +533,68 @@ def cpu_baseline_injections(X, steps_ns, budget_s=15.0):
             "sample": f"{how} matrices (fp64 numpy, {steps_ns} NS step, chunks of 512)", "host_cores": host_cores()}
 
 
+def cpu_baseline_factored(V, K, steps_ns, budget_s=10.0):
+    """The oracle's factored NS (dense fp64 NS of V K^T, then the core through
+    pseudo-inverses) on the first injections until budget_s, as a rate per
+    matrix; the matrices are independent."""
+    import oracle as orc
+    done, t = 0, 0.0
+    while t < budget_s and done < V.shape[0]:
+        n = min(256, V.shape[0] - done)
+        Vc = V[done:done + n].float().cpu().numpy().astype(np.float64)
+        Kc = K[done:done + n].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        for i in range(n):
+            orc.factored_ns(Vc[i], Kc[i], steps_ns)
+        t += time.perf_counter() - t0
+        done += n
+    how = f"all {done}" if done >= V.shape[0] else f"the first {done} of {V.shape[0]}"
+    return {"value": round(done / t, 1), "unit": "matrices/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{how} injections (fp64 numpy: dense NS of V K^T, {steps_ns} step, core by pseudo-inverses), "
+                      f"rate per matrix", "host_cores": host_cores()}
+
+
+def cpu_baseline_adamw(P, G, M, V, kw, budget_s=15.0):
+    """The oracle's AdamW step (fp64 numpy) over the tensors in turn until
+    budget_s, its time scaled to the whole parameter set by element count."""
+    import oracle as orc
+    total = sum(p.size for p in P)
+    done, t, k = 0, 0.0, 0
+    while t < budget_s and k < len(P):
+        g = orc.widen_bf16(G[k])
+        t0 = time.perf_counter()
+        orc.adamw_step(P[k], g, M[k], V[k], step=1, **kw)
+        t += time.perf_counter() - t0
+        done += P[k].size
+        k += 1
+    how = "all" if k == len(P) else f"the first {k} of {len(P)}"
+    return {"value": round(done / (t * total), 4), "unit": "steps/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{how} tensors ({done} of {total} elements, fp64 numpy), time scaled by element count",
+            "host_cores": host_cores()}
+
+
+def cpu_baseline_diag(stacks, iters, budget_s=15.0):
+    """The oracle's diagnostics (fp64: orthogonality error, Lanczos on the
+    Gram) over the matrices, alternating the stacks, until budget_s, as a rate
+    per matrix."""
+    import oracle as orc
+    done, t, i = 0, 0.0, 0
+    nmax = max(A.shape[0] for _, A in stacks)
+    while t < budget_s and i < nmax:
+        for _, A in stacks:
+            if i < A.shape[0] and t < budget_s:
+                a = A[i].float().cpu().numpy().astype(np.float64)
+                t0 = time.perf_counter()
+                orc.spectral_diagnostics(a, iters)
+                t += time.perf_counter() - t0
+                done += 1
+        i += 1
+    total = sum(A.shape[0] for _, A in stacks)
+    return {"value": round(done / t, 3), "unit": "matrices/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{done} of the {total} matrices, alternating the shapes (fp64 numpy, {iters} Lanczos steps)",
+            "host_cores": host_cores()}
+
+
 # ----------------------------------------------------------------------------
 # exploration workloads
 # ----------------------------------------------------------------------------
@@ -624,7 +686,8 @@ def bench_injections_factored(args, torch, mu, wl):
     kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     per = (64 + 128) * 8 * 2 + 8 * 8 * 4 + (64 * 128 * 2 if args.dense else 0)
     gbs = batch * per / (kms * 1e-3) / 1e9
-    return {"metric": "MuonSSM factored single-step NS matrices/s", "value": round(batch / (ms * 1e-3), 1),
+    extra = {} if args.no_cpu else {"cpu_baseline": cpu_baseline_factored(V, K, args.ns_steps)}
+    return {**extra, "metric": "MuonSSM factored single-step NS matrices/s", "value": round(batch / (ms * 1e-3), 1),
             "unit": "matrices/s", "ms_per_step": round(ms, 4), "dtype": "bf16",
             "config": {"workload": f"injections {batch} x (V 64x8, K 128x8) bf16 factors, "
                                    f"{args.ns_steps} NS step, {'core + dense' if args.dense else '8x8 core'} out"},
@@ -738,7 +801,8 @@ def bench_adamw(args, torch, mu, wl):
     kms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nel = sum(p.numel() for p in Pd)
     gbs = nel * 26 / (kms * 1e-3) / 1e9
-    return {"metric": "AdamW companion steps/s (Mamba-2-130M non-Muon parameters)", "value": round(1e3 / ms, 2),
+    extra = {} if args.no_cpu else {"cpu_baseline": cpu_baseline_adamw(P, G, M, V, kw)}
+    return {**extra, "metric": "AdamW companion steps/s (Mamba-2-130M non-Muon parameters)", "value": round(1e3 / ms, 2),
             "unit": "steps/s", "ms_per_step": round(ms, 4), "dtype": "f32",
             "config": {"workload": f"adamw: {len(Pd)} tensors, {nel} elements, bf16 grads"},
             "roofline": {"bound": "hbm", "kernel": "adamw_kernel", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -826,7 +890,8 @@ def bench_diag(args, torch, mu, wl):
         roofline = {"bound": "hbm", "kernel": dom, "achieved": kd["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": kd["frac"], "traffic": None}
     nmat = sum(A.shape[0] for _, A in stacks)
-    return {"metric": "Spectral diagnostics matrices/s (orthogonality error + Lanczos sigma_max/sigma_min)",
+    extra = {} if args.no_cpu else {"cpu_baseline": cpu_baseline_diag(stacks, it)}
+    return {**extra, "metric": "Spectral diagnostics matrices/s (orthogonality error + Lanczos sigma_max/sigma_min)",
             "value": round(nmat / (ms * 1e-3), 1), "unit": "matrices/s", "ms_per_step": round(ms, 4),
             "dtype": "f32" if args.diag_input == "weights" else "bf16",
             "config": {"workload": f"diag: {args.diag_input} of {args.count} out_proj 768x1536 + {args.count} "
