@@ -142,3 +142,32 @@ def test_ssm_momentum_full_size_sampled(mu):
         em, es = orc.rel_frobenius(f64(M[q]), Mr), orc.rel_frobenius(f64(S[q]), Sr)
         print(f"[parity] ssm_momentum full size, sequence {q}: M {em:.3e} S {es:.3e}", flush=True)
         assert em <= BF16_TOL and es <= BF16_TOL
+
+
+def _random_case(seed):
+    """Shape, length, beta, decay range, S on or off and NS steps drawn from a
+    seeded generator: m in 1..64, n in 1..128, T in 1..700 (chunk and round
+    boundaries anywhere), beta in [0, 0.99], decays in [lo, 1) with lo in
+    [0, 0.95]."""
+    rng = np.random.default_rng(1000 + seed)
+    return dict(nseq=int(rng.integers(1, 4)), T=int(rng.integers(1, 701)), m=int(rng.integers(1, 65)),
+                n=int(rng.integers(1, 129)), beta=float(rng.uniform(0.0, 0.99)), lo=float(rng.uniform(0.0, 0.95)),
+                with_s=bool(rng.integers(0, 2)), steps=int(rng.integers(1, 3)))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_ssm_momentum_random_cases(mu, seed):
+    """Seeded random shapes, lengths, momenta, decay ranges, S on or off and
+    NS step counts against the oracle, every sequence whole."""
+    c = _random_case(seed)
+    V, K, a, M0, S0 = wl.ssm_sequences(c["nseq"], c["T"], c["m"], c["n"], seed=seed)
+    a = c["lo"] + (1.0 - c["lo"]) * (a - 0.85) / 0.15   # the drawn decays mapped onto [lo, 1)
+    M, S = run(mu, V, K, a, M0, S0, c["beta"], c["steps"], c["with_s"])
+    worst = 0.0
+    for q in range(c["nseq"]):
+        Mr, Sr = oracle_states(V, K, a, M0, S0, q, c["beta"], c["steps"], with_s=c["with_s"])
+        worst = max(worst, orc.rel_frobenius(f64(M[q]), Mr))
+        if c["with_s"]:
+            worst = max(worst, orc.rel_frobenius(f64(S[q]), Sr))
+    print(f"[parity] ssm_momentum random {c}: max rel {worst:.3e}", flush=True)
+    assert worst <= BF16_TOL
