@@ -244,6 +244,17 @@ __device__ __forceinline__ ChunkW chunk_weights(const SsmMomLaunch& P, long long
   return C;
 }
 
+// Workgroup barrier for the hand-over of LDS areas: this wave's LDS accesses
+// complete (lgkmcnt(0)) and the barrier; the next round's factor loads stay in
+// flight (vmcnt not waited for), where __syncthreads() would drain them.  The
+// registers they fill are waited for where they are used.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // FIXED: the 64 x 128 shape; WITH_S: the memory state is carried (P.S given).
 template <bool FIXED, bool WITH_S>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -288,7 +299,7 @@ ssm_momentum_fused_kernel(SsmMomLaunch P) {
       for (int r = 0; r < 16; ++r) accM[rb][r] = accS[rb][r] = 0.0f;
     for (int rd = 0; rd < nr; ++rd) {
       const int nvr = len - kRound * rd < kRound ? len - kRound * rd : kRound;
-      __syncthreads();  // every wave is done with the previous round's areas
+      lds_barrier();  // every wave is done with the previous round's areas
       stage_round<FIXED>(P, area, R, lane);
       wave_sync();
       // the next round's factors load while this round is computed
@@ -316,7 +327,7 @@ ssm_momentum_fused_kernel(SsmMomLaunch P) {
       int nv = nvr - fact::kMats * w;
       nv = nv < 0 ? 0 : nv;
       write_w(L, nv, wmq, wsq, with_s, lane);
-      __syncthreads();  // every wave's weighted factors and K rows are staged
+      lds_barrier();  // every wave's weighted factors and K rows are staged
 
       for (int tp = 0; 2 * tp < nvr; ++tp) {
         // token 2 tp + G lives in wave tp / 2's area, slot q; tokens past nvr
