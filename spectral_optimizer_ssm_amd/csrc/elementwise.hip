@@ -132,9 +132,12 @@ __global__ void __launch_bounds__(256) momentum_wide_kernel(PtrTable G, MutPtrTa
 }
 
 // ---------------------------------------------------------------------------
-// Tall matrices (m > n): X = U^T through a 64 x 64 LDS tile.
-// grid = (tiles of X, matrices); P = tiles per matrix.
+// Tall matrices (m > n): X = U^T through a 64 x 64 LDS tile.  A workgroup
+// takes kTallTiles consecutive tiles along X's long side and writes one
+// partial; grid = (row blocks x tile groups, matrices), P = workgroups per
+// matrix.
 // ---------------------------------------------------------------------------
+constexpr int kTallTiles = 2;
 template <typename GT, typename XT>
 __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTable M, XT* X, long long xstride,
                                                             int m, int n, int ldg, int s_pad, int ld, float beta,
@@ -148,11 +151,16 @@ __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTa
   const bool has_m = mm != nullptr;
   const bool nest = nesterov != 0;
   const int tiles_k = (ld + 63) / 64;
-  const int i0 = (blockIdx.x / tiles_k) * 64;  // X rows  = U columns (short side)
-  const int k0 = (blockIdx.x % tiles_k) * 64;  // X cols  = U rows    (long side)
+  const int groups_k = (tiles_k + kTallTiles - 1) / kTallTiles;
+  const int i0 = (blockIdx.x / groups_k) * 64;  // X rows  = U columns (short side)
+  const int kt0 = (blockIdx.x % groups_k) * kTallTiles;
+  const int kt1 = kt0 + kTallTiles < tiles_k ? kt0 + kTallTiles : tiles_k;
   const bool vec = (n % 8) == 0 && (ldg % 8) == 0 && a16(g) && (!has_m || a16(mm));
   const int t = threadIdx.x;
   float ss = 0.0f;
+  for (int kt = kt0; kt < kt1; ++kt) {
+  const int k0 = kt * 64;                          // X cols  = U rows    (long side)
+  if (kt != kt0) __syncthreads();                  // the previous tile's transposed reads are done
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int kr = t / 8 + 32 * pass;
@@ -195,6 +203,7 @@ __global__ void __launch_bounds__(256) momentum_tall_kernel(PtrTable G, MutPtrTa
       for (int j = 0; j < 8; ++j) v[j] = tile[kc + j][ir];
       Vec8<XT>::store(x + static_cast<long long>(i0 + ir) * ld + k0 + kc, v);
     }
+  }
   }
   ss = block_sum(ss, red);
   if (threadIdx.x == 0) partials[static_cast<long long>(z) * P + blockIdx.x] = ss;
@@ -388,7 +397,7 @@ __global__ void __launch_bounds__(1024) flags_kernel(const float* partials, long
 // Host launchers
 // ---------------------------------------------------------------------------
 int momentum_blocks_per_matrix(bool tall, int s_pad, int ld) {
-  if (tall) return ((s_pad + 63) / 64) * ((ld + 63) / 64);
+  if (tall) return ((s_pad + 63) / 64) * (((ld + 63) / 64 + kTallTiles - 1) / kTallTiles);
   const long long chunks = static_cast<long long>(s_pad) * (ld / 8);
   long long b = (chunks + 256 * 8 - 1) / (256 * 8);  // about 8 chunks per thread
   if (b < 1) b = 1;
