@@ -59,7 +59,9 @@ def check(V, K, C, O, steps, coeffs, per_step, idx):
 
 
 @pytest.mark.parametrize("m,n,r,steps,coeffs,per_step", [
+    (64, 128, 8, 0, (1.5, -0.5), False),                          # normalisation only
     (64, 128, 8, 1, (1.5, -0.5), False),
+    (64, 128, 8, 1, (2.0, -1.5, 0.5), False),                     # quintic first step alone
     (64, 128, 8, 5, (1.5, -0.5), False),
     (64, 128, 8, 3, (2.0, -1.5, 0.5), False),                     # quintic
     (64, 128, 8, 2, [(1.6, -0.6), (1.4, -0.4)], True),            # per-step rows

@@ -80,7 +80,8 @@ def test_ssm_momentum_without_memory_state(mu):
     check(mu, 2, 300, 64, 128, with_s=False)
 
 
-@pytest.mark.parametrize("steps,coeffs", [(5, (1.5, -0.5)), (2, (2.0, -1.5, 0.5))])
+@pytest.mark.parametrize("steps,coeffs", [(0, (1.5, -0.5)), (1, (2.0, -1.5, 0.5)), (5, (1.5, -0.5)),
+                                          (2, (2.0, -1.5, 0.5))])
 def test_ssm_momentum_more_steps_and_quintic(mu, steps, coeffs):
     check(mu, 2, 40, 64, 128, steps=steps, coeffs=coeffs)
 
