@@ -188,8 +188,9 @@ struct Acc {
 };
 
 // The MFMAs of one stage with one set of fragments (for accumulator tiles too
-// large to leave registers for a second set).
-template <int FM, int FN, class FragA, class FragB>
+// large to leave registers for a second set).  SWAP: the B fragment is the
+// MFMA's first operand, so acc.c[i][j] holds the transpose of block (i, j).
+template <int FM, int FN, bool SWAP = false, class FragA, class FragB>
 __device__ __forceinline__ void stage_mma_single(Acc<FM, FN>& acc, FragA fra, FragB frb) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -202,12 +203,14 @@ __device__ __forceinline__ void stage_mma_single(Acc<FM, FN>& acc, FragA fra, Fr
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
+        acc.c[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc.c[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
   }
 }
 
 // The MFMAs of one stage; fragments of k-step ks+1 are read while ks runs.
-template <int FM, int FN, class FragA, class FragB>
+// SWAP as in stage_mma_single.
+template <int FM, int FN, bool SWAP = false, class FragA, class FragB>
 __device__ __forceinline__ void stage_mma(Acc<FM, FN>& acc, FragA fra, FragB frb) {
   bf16x8_t fa[2][FM], fb[2][FN];
 #pragma unroll
@@ -227,7 +230,8 @@ __device__ __forceinline__ void stage_mma(Acc<FM, FN>& acc, FragA fra, FragB frb
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc.c[i][j], 0, 0, 0);
+        acc.c[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc.c[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc.c[i][j], 0, 0, 0);
   }
 }
 
@@ -752,6 +756,12 @@ symprod_bf16_kernel(SymArgs G) {
     upper_tile(tile % S.tiles_per_mat, S.s_pad / TT, bi, bj);
     const bool diag = bi == bj;
     const bool single = diag && S.L == S.R && (!F32 || S.lmap == S.rmap);  // both operands are the same rows
+    // An off-diagonal tile of an upper-triangle output is computed transposed
+    // (the B fragment as the MFMA's first operand): lanes then hold four
+    // consecutive columns of the tile, which leave in 8-byte stores.  The
+    // product of commuting symmetric factors is symmetric and each element is
+    // the same products summed in the same k order.
+    const bool swap = !F32 && !diag && S.tri_out;
     const long long zoff = z * S.stride;                 // outputs
     const long long zin = z * S.in_stride;               // operands
     const float inv = seg_inv(S, z, red);
@@ -801,7 +811,8 @@ symprod_bf16_kernel(SymArgs G) {
       if (tri && kt / kbs < b) fill_t(op, rs, kt * BK * sp_bytes + b * TT * 2);
       else fill_rows(op, rs, off + kcol(kt, map));
     };
-    auto mma = [&](const char* buf, int kt, bool one) {
+    auto mma = [&](const char* buf, int kt, bool one, auto sw) {
+      constexpr bool SW = decltype(sw)::value != 0;
       const int kb = kt / kbs;
       const bool lt = tri && kb < bi, rt = tri && kb < bj;  // uniform per stage
       const char* ab = buf;
@@ -814,51 +825,59 @@ symprod_bf16_kernel(SymArgs G) {
         return rt ? frag_tr<TT * 2>(bb + tfb[j] + ks * 16 * TT * 2)
                   : frag_at(bb + wn * WT * 64 + roff[ks] + j * 32 * 64);
       };
-      if constexpr (FM * FN > kSymSingleFragsAbove) stage_mma_single<FM, FN>(acc, fa, fb);
-      else stage_mma<FM, FN>(acc, fa, fb);
+      if constexpr (FM * FN > kSymSingleFragsAbove) stage_mma_single<FM, FN, SW>(acc, fa, fb);
+      else stage_mma<FM, FN, SW>(acc, fa, fb);
     };
     if constexpr (TT == 192) {
       // the operand modes change only at k-block boundaries (multiples of 6
       // stages): stages below block bi read both operands transposed, those
       // below bj only R; each range runs a straight-line body
       const int k2 = tri ? bi * kbs : 0, k1 = tri ? bj * kbs : 0;
-      auto body = [&](const char* buf, bool one, auto lt_rt) {
+      auto body = [&](const char* buf, bool one, auto lt_rt, auto sw) {
         constexpr int MODE = decltype(lt_rt)::value;
+        constexpr bool SW = decltype(sw)::value != 0;
         const char* ab = buf;
         const char* bb = one ? buf : buf + OPBT;
         auto fa_r = [&](int ks, int i) { return frag_at(ab + wm * WT * 64 + roff[ks] + i * 32 * 64); };
         auto fa_t = [&](int ks, int i) { return frag_tr<TT * 2>(ab + tfa[i] + ks * 16 * TT * 2); };
         auto fb_r = [&](int ks, int j) { return frag_at(bb + wn * WT * 64 + roff[ks] + j * 32 * 64); };
         auto fb_t = [&](int ks, int j) { return frag_tr<TT * 2>(bb + tfb[j] + ks * 16 * TT * 2); };
-        if constexpr (MODE == 2) stage_mma_single<FM, FN>(acc, fa_t, fb_t);
-        else if constexpr (MODE == 1) stage_mma_single<FM, FN>(acc, fa_r, fb_t);
-        else stage_mma_single<FM, FN>(acc, fa_r, fb_r);
+        if constexpr (MODE == 2) stage_mma_single<FM, FN, SW>(acc, fa_t, fb_t);
+        else if constexpr (MODE == 1) stage_mma_single<FM, FN, SW>(acc, fa_r, fb_t);
+        else stage_mma_single<FM, FN, SW>(acc, fa_r, fb_r);
+      };
+      auto fill2 = [&](char* buf, int kt) {
+        fill_op(buf, lr, bi, offL, kt, S.lmap);
+        fill_op(buf + OPBT, rr, bj, offR, kt, S.rmap);
       };
       if (single) {
         pipeline3<BPW>(bufs, nk, k2, k1, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt, S.lmap); },
-                       [&](const char* buf, int) { body(buf, true, IntC<2>{}); },
-                       [&](const char* buf, int) { body(buf, true, IntC<1>{}); },
-                       [&](const char* buf, int) { body(buf, true, IntC<0>{}); });
+                       [&](const char* buf, int) { body(buf, true, IntC<2>{}, IntC<0>{}); },
+                       [&](const char* buf, int) { body(buf, true, IntC<1>{}, IntC<0>{}); },
+                       [&](const char* buf, int) { body(buf, true, IntC<0>{}, IntC<0>{}); });
+      } else if (swap) {
+        pipeline3<2 * BPW>(bufs, nk, k2, k1, fill2,
+                           [&](const char* buf, int) { body(buf, false, IntC<2>{}, IntC<1>{}); },
+                           [&](const char* buf, int) { body(buf, false, IntC<1>{}, IntC<1>{}); },
+                           [&](const char* buf, int) { body(buf, false, IntC<0>{}, IntC<1>{}); });
       } else {
-        pipeline3<2 * BPW>(bufs, nk, k2, k1,
-                           [&](char* buf, int kt) {
-                             fill_op(buf, lr, bi, offL, kt, S.lmap);
-                             fill_op(buf + OPBT, rr, bj, offR, kt, S.rmap);
-                           },
-                           [&](const char* buf, int) { body(buf, false, IntC<2>{}); },
-                           [&](const char* buf, int) { body(buf, false, IntC<1>{}); },
-                           [&](const char* buf, int) { body(buf, false, IntC<0>{}); });
+        pipeline3<2 * BPW>(bufs, nk, k2, k1, fill2,
+                           [&](const char* buf, int) { body(buf, false, IntC<2>{}, IntC<0>{}); },
+                           [&](const char* buf, int) { body(buf, false, IntC<1>{}, IntC<0>{}); },
+                           [&](const char* buf, int) { body(buf, false, IntC<0>{}, IntC<0>{}); });
       }
     } else if (single) {
       pipeline<BPW>(bufs, nk, [&](char* buf, int kt) { fill_op(buf, lr, bi, offL, kt, S.lmap); },
-                    [&](const char* buf, int kt) { mma(buf, kt, true); });
+                    [&](const char* buf, int kt) { mma(buf, kt, true, IntC<0>{}); });
     } else {
-      pipeline<2 * BPW>(bufs, nk,
-                        [&](char* buf, int kt) {
-                          fill_op(buf, lr, bi, offL, kt, S.lmap);
-                          fill_op(buf + OPBT, rr, bj, offR, kt, S.rmap);
-                        },
-                        [&](const char* buf, int kt) { mma(buf, kt, false); });
+      auto fill2 = [&](char* buf, int kt) {
+        fill_op(buf, lr, bi, offL, kt, S.lmap);
+        fill_op(buf + OPBT, rr, bj, offR, kt, S.rmap);
+      };
+      if (swap)
+        pipeline<2 * BPW>(bufs, nk, fill2, [&](const char* buf, int kt) { mma(buf, kt, false, IntC<1>{}); });
+      else
+        pipeline<2 * BPW>(bufs, nk, fill2, [&](const char* buf, int kt) { mma(buf, kt, false, IntC<0>{}); });
     }
 
     // epilogue: D[m][n] = (L R)[bi*TT + m][bj*TT + n]; lane: 4 consecutive m
@@ -932,7 +951,26 @@ symprod_bf16_kernel(SymArgs G) {
     __syncthreads();
     sym_to_global<TT>(bufs, O1, O2, static_cast<long long>(bj) * TT * S.s_pad + bi * TT, S.s_pad, S.a2, S.b2, diag);
     }
-    if (!diag) {
+    if (swap) {
+      // acc.c[i][j] register 4 q + r: tile row m = wm WT + 32 i + col, column
+      // n = wn WT + 32 j + 8 q + rq + r (the transposed block)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int mb = wm * WT + i * 32;  // 32-aligned block of m
+        char* buf = bufs[mb >> 6];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n0 = wn * WT + j * 32 + q * 8 + rq;
+            const f32x16_t& c = acc.c[i][j];
+            *reinterpret_cast<u32x2_t*>(buf + sym_slab_off<TT>((mb & 63) + col, n0)) =
+                u32x2_t{pack_bf16x2(b1 * c[4 * q], b1 * c[4 * q + 1]), pack_bf16x2(b1 * c[4 * q + 2], b1 * c[4 * q + 3])};
+          }
+      }
+      __syncthreads();
+      sym_to_global<TT>(bufs, O1, O2, static_cast<long long>(bi) * TT * S.s_pad + bj * TT, S.s_pad, S.a2, S.b2, false);
+    } else if (!diag) {
       if (mirror) __syncthreads();
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
