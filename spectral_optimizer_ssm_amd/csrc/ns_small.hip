@@ -629,16 +629,21 @@ constexpr int kMaxLds = 160 * 1024;
 //    dealt to the waves, each stored with its mirror (A exactly symmetric);
 //  * the combine Y = a X + b A X on 16 x 16 blocks (32 for 64 x 128), dealt
 //    to the waves.
+// Within each 16 contraction indices, MFMA t takes index 4 kq + t from lane
+// group kq (a fixed permutation of the summation order), so the row-wise
+// operands (both of the Gram's, A's in the combine) arrive as one 16-byte
+// read per four MFMAs.
 // A single matrix runs on one CU, so its step time is the dependent chain of
 // each wave's products: sixteen waves on 16 x 16 blocks and the Gram's
 // symmetry cut it to a quarter of four waves on 32 x 32 blocks.
 template <int LMAX>
 __global__ void __launch_bounds__(1024) ns_small_f32_kernel(NsSmallLaunch P) {
-  // odd row strides: the operands are read down columns
-  constexpr int SMAX = 64, XS = LMAX + 1, AS = SMAX + 1, NT = 1024, NW = NT / 64;
-  __shared__ float xa[SMAX][XS];
-  __shared__ float xb[SMAX][XS];
-  __shared__ float am[SMAX][AS];
+  // Row strides keep 16-byte row reads aligned and put the four rows of a
+  // column read 16 (X) or 4 (A) banks apart.
+  constexpr int SMAX = 64, XS = LMAX + 16, AS = SMAX + 4, NT = 1024, NW = NT / 64;
+  __shared__ __attribute__((aligned(16))) float xa[SMAX][XS];
+  __shared__ __attribute__((aligned(16))) float xb[SMAX][XS];
+  __shared__ __attribute__((aligned(16))) float am[SMAX][AS];
   __shared__ float red[NW];
   const int S = P.s, Lw = P.l, tid = threadIdx.x;
   const int Sp = (S + 31) & ~31, Lp = (Lw + 31) & ~31;
@@ -686,11 +691,14 @@ __global__ void __launch_bounds__(1024) ns_small_f32_kernel(NsSmallLaunch P) {
         }
         const int tj = ti + rem;
         f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-        for (int k = 0; k < Lp; k += 4) {
-          const float av = cur[ti * 16 + r16][k + kq];
-          const float bv = cur[tj * 16 + r16][k + kq];
-          g = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, g, 0, 0, 0);
+        // contraction order within 16 columns: MFMA t takes column 4 kq + t
+        // from lane group kq, so one 16-byte read serves four MFMAs
+#pragma unroll 2
+        for (int k = 0; k < Lp; k += 16) {
+          const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&cur[ti * 16 + r16][k + 4 * kq]);
+          const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&cur[tj * 16 + r16][k + 4 * kq]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) g = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], g, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -706,11 +714,13 @@ __global__ void __launch_bounds__(1024) ns_small_f32_kernel(NsSmallLaunch P) {
       for (int blk = w; blk < n16 * n16l; blk += NW) {
         const int ti = blk % n16, tk = blk / n16;
         f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-        for (int j = 0; j < Sp; j += 4) {
-          const float av = am[ti * 16 + r16][j + kq];
-          const float bv = cur[j + kq][tk * 16 + r16];
-          y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, y, 0, 0, 0);
+        // the same order: MFMA t contracts over row 4 kq + t of X
+#pragma unroll 2
+        for (int j = 0; j < Sp; j += 16) {
+          const f32x4_t av = *reinterpret_cast<const f32x4_t*>(&am[ti * 16 + r16][j + 4 * kq]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], cur[j + 4 * kq + t][tk * 16 + r16], y, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
