@@ -53,31 +53,75 @@ constexpr int kWorkBytes = kMats * kGroupF * 4;
 
 // Gram of the 32 staged columns over rows [row0, row0 + rows): lane l holds
 // column l % 32, rows 8 (g / 4) + 4 (l / 32) + g % 4 of the 32 x 32 result.
-__device__ __forceinline__ f32x16_t gram32(const char* vk, int row0, int rows, int lane) {
-  f32x16_t acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+__device__ __forceinline__ bf16x8_t gram_operand(const char* vk, int k0, int lane) {
+  // A operand: row (= staged column) lane % 32, contraction index
+  // k0 + 8 (lane / 32) + 0..7; lane 16g + 4rr + u addresses staged row
+  // k0 + 8 (g >> 1) + 4h + rr, columns colbase + 4u .. + 3 (slot
+  // colbase / 8 + u / 2, bytes 8 (u % 2) ..).
   const int g = lane >> 4;
   const int colbase = 16 * (g & 1);
   const int rr = (lane & 15) >> 2, u = lane & 3;
-  for (int k0 = 0; k0 < rows; k0 += 16) {
-    // A operand: row (= staged column) lane % 32, contraction index
-    // k0 + 8 (lane / 32) + 0..7; lane 16g + 4rr + u addresses staged row
-    // k0 + 8 (g >> 1) + 4h + rr, columns colbase + 4u .. + 3 (slot
-    // colbase / 8 + u / 2, bytes 8 (u % 2) ..).
-    u32x2_t part[2];
+  u32x2_t part[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = row0 + k0 + 8 * (g >> 1) + 4 * h + rr;
-      const char* p = vk + slot(row, (colbase >> 3) + (u >> 1)) + 8 * (u & 1);
-      const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
-      part[h] = __builtin_bit_cast(u32x2_t, v);
-    }
-    const u32x4_t w = {part[0][0], part[0][1], part[1][0], part[1][1]};
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, w);
+  for (int h = 0; h < 2; ++h) {
+    const int row = k0 + 8 * (g >> 1) + 4 * h + rr;
+    const char* p = vk + slot(row, (colbase >> 3) + (u >> 1)) + 8 * (u & 1);
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+    part[h] = __builtin_bit_cast(u32x2_t, v);
+  }
+  const u32x4_t w = {part[0][0], part[0][1], part[1][0], part[1][1]};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  return acc;
+}
+
+__device__ __forceinline__ f32x16_t gram32(const char* vk, int row0, int rows, int lane) {
+  f32x16_t acc = zero16();
+  for (int k0 = 0; k0 < rows; k0 += 16) {
+    const bf16x8_t a = gram_operand(vk, row0 + k0, lane);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc, 0, 0, 0);
   }
   return acc;
+}
+
+// Both Grams for row counts known at compile time, their k-steps interleaved
+// (two independent accumulation chains); each accumulates in the same order
+// as gram32.
+template <int MP, int NP>
+__device__ __forceinline__ void gram32_pair(const char* vk, int lane, f32x16_t& gp, f32x16_t& gq) {
+  static_assert(MP % 16 == 0 && NP % 16 == 0 && MP <= NP, "padded row counts");
+  gp = zero16();
+  gq = zero16();
+#pragma unroll
+  for (int k0 = 0; k0 < NP; k0 += 16) {
+    if (k0 < MP) {
+      const bf16x8_t a = gram_operand(vk, k0, lane);
+      gp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, gp, 0, 0, 0);
+    }
+    const bf16x8_t b = gram_operand(vk, MP + k0, lane);
+    gq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, gq, 0, 0, 0);
+  }
+}
+
+// Sum over the 16 lanes of each row of the wave (DPP: no LDS round trip).
+// The pairing is that of a butterfly over lane bits 0, 1, 2, 3 (the mirrors
+// pair the same groups as bits 2 and 3), so every lane ends with the same
+// sum a shuffle butterfly gives.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f32<0xb1>(v);     // quad_perm [1, 0, 3, 2]: lane ^ 1
+  v += dpp_f32<0x4e>(v);     // quad_perm [2, 3, 0, 1]: lane ^ 2
+  v += dpp_f32<0x141>(v);    // row_half_mirror: lane i <-> 7 - i within 8
+  v += dpp_f32<0x140>(v);    // row_mirror: lane i <-> 15 - i within 16
+  return v;
 }
 
 // Keep the diagonal 8 x 8 blocks of a gram32 result: lane l writes rows
@@ -119,14 +163,22 @@ __device__ __forceinline__ void mm8(const WaveLds& L, int x, int y, int z, int l
 // The cores C of the four matrices staged in L.vk (V rows 0 .. m_pad - 1, K
 // rows m_pad .. m_pad + n_pad - 1), left in L.mat(q, kC).  Args supplies
 // m_pad, n_pad (multiples of 16), r, eps, steps and the per-step
-// coefficients a[], b[], c[].  Both Grams are read before either is stored,
-// so the work matrices may lie over the staged rows.
-template <class Args>
+// coefficients a[], b[], c[]; MP and NP, when nonzero, are m_pad and n_pad
+// known at compile time (the Gram loops then unroll, so the staged rows of
+// later k-steps are read while earlier ones are multiplied).  Both Grams are
+// read before either is stored, so the work matrices may lie over the staged
+// rows.
+template <int MP = 0, int NP = 0, class Args>
 __device__ __forceinline__ void core(const Args& F, const WaveLds& L, int lane) {
   const int r = F.r;
   // P = V^T V and S = K^T K on the matrix cores
-  const f32x16_t gp = gram32(L.vk, 0, F.m_pad, lane);
-  const f32x16_t gq = gram32(L.vk, F.m_pad, F.n_pad, lane);
+  f32x16_t gp, gq;
+  if constexpr (MP > 0 && NP > 0) {
+    gram32_pair<MP, NP>(L.vk, lane, gp, gq);
+  } else {
+    gp = gram32(L.vk, 0, F.m_pad, lane);
+    gq = gram32(L.vk, F.m_pad, F.n_pad, lane);
+  }
   wave_sync();
   store_blocks(gp, L, kP, lane);
   store_blocks(gq, L, kS, lane);
@@ -141,8 +193,7 @@ __device__ __forceinline__ void core(const Args& F, const WaveLds& L, int lane) 
     float t2 = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) t2 = fmaf(P[i * kLd + j0 + e], S[(j0 + e) * kLd + i], t2);
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) t2 += __shfl_xor(t2, d, 64);
+    t2 = row_sum16(t2);
     inv = 1.0f / (sqrtf(t2) + F.eps);
   }
   if (F.steps == 0) {

@@ -67,8 +67,11 @@ template <bool FIXED>
 __device__ __forceinline__ void load_round(const SsmMomLaunch& P, long long tokr, int nvr, int w, int lane,
                                            RoundRegs& R) {
   const int m = FIXED ? kTileM : P.m, n = FIXED ? kTileN : P.n;
-  int nv = nvr - fact::kMats * w;
-  nv = nv < 0 ? 0 : nv > fact::kMats ? fact::kMats : nv;
+  // the clamp compiles to a vector-unit median; moved back to a scalar so
+  // that the resources below stay in scalar registers (a resource in vector
+  // registers is wrapped in a loop over the lanes' distinct values)
+  const int nv0 = nvr - fact::kMats * w;
+  const int nv = __builtin_amdgcn_readfirstlane(nv0 < 0 ? 0 : nv0 > fact::kMats ? fact::kMats : nv0);
   const long long tok = tokr + fact::kMats * w;
   // one 16-byte row per rank-8 row
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -323,7 +326,7 @@ ssm_momentum_fused_kernel(SsmMomLaunch P) {
       }
       const float wmq = qc == 0 ? wm_r[0] : qc == 1 ? wm_r[1] : qc == 2 ? wm_r[2] : wm_r[3];
       const float wsq = qc == 0 ? ws_r[0] : qc == 1 ? ws_r[1] : qc == 2 ? ws_r[2] : ws_r[3];
-      fact::core(P.ns, L, lane);
+      fact::core<kTileM, kTileN>(P.ns, L, lane);   // V rows and K rows padded to the 64 x 128 tile
       int nv = nvr - fact::kMats * w;
       nv = nv < 0 ? 0 : nv;
       write_w(L, nv, wmq, wsq, with_s, lane);
