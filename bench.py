@@ -701,24 +701,32 @@ def bench_injections_factored(args, torch, mu, wl):
 
 def cpu_baseline_ssm_momentum(V, K, a, M0, S0, beta, steps_ns, budget_s=15.0):
     """The oracle's momentum pathway (dense fp64 NS of every token, then the
-    recurrence) on the first tokens of sequence 0 until budget_s, as a token
-    rate; every token costs the same, so the rate scales to the workload."""
+    recurrence) over the sequences in order, 64 tokens at a time, until
+    budget_s, as a token rate; every token costs the same, so the rate scales
+    to the workload."""
     import oracle as orc
-    Vs = V[0].float().cpu().numpy().astype(np.float64)
-    Ks = K[0].float().cpu().numpy().astype(np.float64)
-    As = a[0].cpu().numpy().astype(np.float64)
-    M = M0[0].cpu().numpy().astype(np.float64)
-    S = S0[0].cpu().numpy().astype(np.float64)
-    done, t = 0, 0.0
-    while t < budget_s and done < Vs.shape[0]:
-        c = slice(done, done + 64)
-        t0 = time.perf_counter()
-        M, S = orc.ssm_momentum(Vs[c], Ks[c], As[c], beta, M, S, steps=steps_ns)
-        t += time.perf_counter() - t0
-        done += Vs[c].shape[0]
+    done, t, seqs = 0, 0.0, 0
+    for q in range(V.shape[0]):
+        if t >= budget_s:
+            break
+        Vs = V[q].float().cpu().numpy().astype(np.float64)
+        Ks = K[q].float().cpu().numpy().astype(np.float64)
+        As = a[q].cpu().numpy().astype(np.float64)
+        M = M0[q].cpu().numpy().astype(np.float64)
+        S = S0[q].cpu().numpy().astype(np.float64)
+        seqs += 1
+        for t0_tok in range(0, Vs.shape[0], 64):
+            if t >= budget_s:
+                break
+            c = slice(t0_tok, t0_tok + 64)
+            t0 = time.perf_counter()
+            M, S = orc.ssm_momentum(Vs[c], Ks[c], As[c], beta, M, S, steps=steps_ns)
+            t += time.perf_counter() - t0
+            done += Vs[c].shape[0]
     return {"value": round(done / t, 1), "unit": "injections/s", "cores": int(blas_threads()), "kind": "oracle",
-            "sample": f"the first {done} tokens of sequence 0 (fp64 numpy: dense NS of each 64x128 injection, "
-                      f"{steps_ns} step, then the state recurrence), rate per token", "host_cores": host_cores()}
+            "sample": f"{done} tokens from the first {seqs} of {V.shape[0]} sequences, in order (fp64 numpy: dense "
+                      f"NS of each 64x128 injection, {steps_ns} step, then the state recurrence), rate per token",
+            "host_cores": host_cores()}
 
 
 def bench_ssm_momentum(args, torch, mu, wl):

@@ -15,8 +15,12 @@
 // Gram matrices at once on its diagonal 8 x 8 blocks (operands from two
 // ds_read_b64_tr_b16 per lane); the 8 x 8 recurrence then runs on 16 lanes
 // per matrix, each lane owning 4 entries of one row, through LDS.  Slot q of
-// row t sits at position q ^ ((t / 4) % 4) of the row, so sixteen
-// consecutive rows accessed at one slot fall on distinct LDS banks.
+// row t sits at position q ^ x(t), with bit 0 of x(t) bit 2 of t and bit 1
+// of x(t) bit 1 of t xor bit 3: the rows of equal parity among eight
+// consecutive ones (the rows of a 16-byte access served together by 32
+// four-byte banks) and those of equal residue mod 4 among sixteen (the same
+// by 64 banks) get distinct positions, and rows t and t + 2 of a transposing
+// read's four-row group get disjoint position pairs.
 #pragma once
 
 #include "common.cuh"
@@ -28,18 +32,23 @@ constexpr int kMats = 4;   // matrices per wavefront
 constexpr int kRow = 64;   // bytes per staged row (32 bf16 columns)
 
 // Byte offset of slot q (matrix q's 16 bytes) of staged row t.
-__device__ __forceinline__ int slot(int t, int q) { return t * kRow + 16 * (q ^ ((t >> 2) & 3)); }
+__device__ __forceinline__ int slot(int t, int q) {
+  const int x = ((t >> 2) & 1) | (((t >> 1) ^ (t >> 3)) & 1) << 1;
+  return t * kRow + 16 * (q ^ x);
+}
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
-// The 8 x 8 float32 work matrices: rows kLd = 9 floats apart and each
-// matrix's six in a block of 432 floats, so the column reads of one matrix
-// (rows i = 0..7) and the same reads of its neighbour fall on distinct banks.
+// The 8 x 8 float32 work matrices: rows kLd = 9 floats apart, so the eight
+// rows' entries of one column fall on distinct banks; each matrix's six in a
+// block of 440 floats, so the four matrices of a wave start 24 banks apart
+// (mod 32) and an access to the same entry of all four, or to one column of
+// each, does not collide.
 constexpr int kLd = 9;
-constexpr int kMatF = 8 * kLd, kGroupF = 6 * kMatF;
+constexpr int kMatF = 8 * kLd, kGroupF = 6 * kMatF + 8;
 
 // LDS of one wavefront.
 struct WaveLds {

@@ -49,7 +49,7 @@ constexpr int kWaves = 4;                          // waves per workgroup
 constexpr int kRound = kWaves * fact::kMats;       // tokens per round
 constexpr int kStage = (kTileM + kTileN) * kRow;   // staged V and K rows of a wave
 constexpr int kArea = kStage + fact::kWorkBytes;   // LDS of a wave
-constexpr int kFusedLds = kWaves * kArea;          // 75 KB: two workgroups per CU
+constexpr int kFusedLds = kWaves * kArea;          // 75.5 KB: two workgroups per CU
 static_assert(kSsmMomQ % kRound == 0, "chunks are whole rounds");
 static_assert(kTileM * kRow <= fact::kWorkBytes, "the work area holds the 64 rows of W_S");
 static_assert(2 * kFusedLds <= 160 * 1024, "two workgroups fit a CU");
@@ -435,7 +435,7 @@ hipError_t launch_ssm_momentum(const SsmMomLaunch& P, hipStream_t st, int phase)
     return hipErrorInvalidValue;
   if (phase == 0) {
     const long long items = P.nseq * P.nchunks;
-    const long long slots = 2LL * device_cus();  // 75 KB of LDS: two workgroups per CU
+    const long long slots = 2LL * device_cus();  // 75.5 KB of LDS: two workgroups per CU
     const unsigned blocks = static_cast<unsigned>(items < slots ? items : slots);
     const bool fixed = P.m == kTileM && P.n == kTileN, with_s = P.S != nullptr;
     const void* fn = fixed ? (with_s ? reinterpret_cast<const void*>(ssm_momentum_fused_kernel<true, true>)
