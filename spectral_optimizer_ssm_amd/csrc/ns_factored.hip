@@ -38,6 +38,7 @@ using fact::WaveLds;
 constexpr int kFactWgPerCu = 4;
 
 // Steps 2-6 for the four matrices b0 .. b0 + nm - 1 staged in L.vk.
+template <bool FAST>
 __device__ __forceinline__ void factored_compute(const FactLaunch& F, const WaveLds& L, long long b0, int nm,
                                                  int lane);
 
@@ -99,7 +100,7 @@ __global__ void __launch_bounds__(256) ns_factored_kernel(FactLaunch F) {
         fast_stage(L, lane, R);
         wave_sync();
         if (gi + gstride < full) fast_load(F, (gi + gstride) * kMats, lane, R);
-        factored_compute(F, L, gi * kMats, kMats, lane);
+        factored_compute<true>(F, L, gi * kMats, kMats, lane);
       }
     }
     // the remaining partial group (at most one) takes the general path
@@ -137,15 +138,18 @@ __global__ void __launch_bounds__(256) ns_factored_kernel(FactLaunch F) {
     }
   }
   wave_sync();
-  factored_compute(F, L, b0, nm, lane);
+  factored_compute<false>(F, L, b0, nm, lane);
   }
 }
 
+template <bool FAST>
 __device__ __forceinline__ void factored_compute(const FactLaunch& F, const WaveLds& L, long long b0, int nm,
                                                  int lane) {
   const int m = F.m, n = F.n, r = F.r;
-  // 2-4. Grams, normalisation and the r x r recurrence
-  fact::core(F, L, lane);
+  // 2-4. Grams, normalisation and the r x r recurrence (the fast shape's row
+  // counts as constants)
+  if constexpr (FAST) fact::core<kFastM, kFastN>(F, L, lane);
+  else fact::core(F, L, lane);
   const int q = lane >> 4, i = (lane & 15) >> 1, j0 = 4 * (lane & 1);
 
   // 5. the core, r x r float32 per matrix
