@@ -80,6 +80,12 @@ ns_small_bf16_kernel(NsSmallLaunch P) {
   const int G = lane >> 5, l32 = lane & 31;
   const long long nwaves = static_cast<long long>(gridDim.x) * WPB;
 
+  // The first NPRE chunks per lane of a wave's next matrix are loaded into
+  // registers while the current one is combined (the Gram accumulators are
+  // dead by then), so part of every load latency overlaps the wave's own work.
+  constexpr int NPRE = Geo::CHUNKS / 128;
+  u32x4_t pre[NPRE];
+  bool have_pre = false;
   for (long long mat = static_cast<long long>(blockIdx.x) * WPB + wid; mat < P.count; mat += nwaves) {
     const bf16_t* src = static_cast<const bf16_t*>(P.X) + mat * P.in_stride;
     bf16_t* dst = static_cast<bf16_t*>(P.Y) + mat * P.out_stride;
@@ -90,7 +96,7 @@ ns_small_bf16_kernel(NsSmallLaunch P) {
     for (int p = 0; p < Geo::CHUNKS / 64; ++p) {
       const int q = lane + 64 * p;
       const int r = q / Geo::CPR, c = q % Geo::CPR;
-      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8));
+      const u32x4_t v = (p < NPRE && have_pre) ? pre[p < NPRE ? p : 0] : __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + static_cast<long long>(r) * P.ld_in + c * 8));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float a = lo_bf16(v[e]), b = hi_bf16(v[e]);
@@ -154,6 +160,19 @@ ns_small_bf16_kernel(NsSmallLaunch P) {
       // operations of a wave execute in order) and only one block of Y is
       // held in registers: two waves per SIMD instead of one.
       const float alpha = P.a[step] * sc, beta = P.b[step] * sc;
+      if (step == P.steps - 1) {
+        const long long nxt = mat + nwaves;
+        have_pre = nxt < P.count;
+        if (have_pre) {
+          const bf16_t* nsrc = static_cast<const bf16_t*>(P.X) + nxt * P.in_stride;
+#pragma unroll
+          for (int p = 0; p < NPRE; ++p) {
+            const int q = lane + 64 * p;
+            const int r = q / Geo::CPR, c = q % Geo::CPR;
+            pre[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(nsrc + static_cast<long long>(r) * P.ld_in + c * 8));
+          }
+        }
+      }
 #pragma unroll 1
       for (int kb = 0; kb < NK; ++kb) {
         u32x2_t ypk[NB][4];
