@@ -744,7 +744,9 @@ std::vector<int> list_phases(std::vector<GroupRun>& runs, const NsCoefs& C, floa
 
 // Per device, created on first use and kept until the process ends: one
 // auxiliary stream (default priority, non-blocking) and the fork / join
-// events that order it against the caller's stream.
+// events that order it against the caller's stream.  The table is a fixed
+// array of plain pointers, so the library registers no destructor that would
+// run at exit (devices past 64 run on the caller's stream alone).
 struct Aux {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -752,12 +754,12 @@ struct Aux {
 };
 
 Aux* aux_for_current_device() {
+  constexpr int kMaxDev = 64;
   static std::mutex table_mu;
-  static std::vector<Aux*> table;
+  static Aux* table[kMaxDev] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
   std::lock_guard<std::mutex> lock(table_mu);
-  if (static_cast<int>(table.size()) <= dev) table.resize(dev + 1, nullptr);
   if (table[dev] == nullptr) {
     Aux* a = new Aux();
     if (hipStreamCreateWithFlags(&a->s, hipStreamNonBlocking) != hipSuccess ||
