@@ -325,13 +325,14 @@ std::vector<SymSeg> grams_as_sym(const std::vector<GemmSeg>& gs, bool tri_out = 
 
 int flags_pass(long long nparts, char* ws, hipStream_t st, EventRec& E);
 
-// after_momentum: when non-null, recorded on st once the momentum passes of
-// these groups have been enqueued.  flags_nparts >= 0: after those passes,
-// the call's non-finite flag from the first flags_nparts partial sums (every
+// fork: when non-null, recorded on st once the Gram of the accumulated
+// schedule (if any group of this run takes it), else the momentum passes, of
+// these groups have been enqueued.  flags_nparts >= 0: after the momentum
+// passes, the call's non-finite flag from the first flags_nparts partial sums (every
 // group's partials are complete by then: this run's momentum passes are the
 // call's last ones).
 int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, float* norms_out, hipStream_t st,
-            EventRec& E, hipEvent_t after_momentum = nullptr, long long flags_nparts = -1) {
+            EventRec& E, hipEvent_t fork = nullptr, long long flags_nparts = -1) {
   if (!E.mark(st, 0)) return MUON_EHIP;
   // 1. momentum
   for (GroupRun& R : runs) {
@@ -360,7 +361,15 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
       return MUON_EHIP;
     if (!E.mark(st, MUON_PHASE_MOMENTUM)) return MUON_EHIP;
   }
-  if (after_momentum != nullptr && E.live() && hipEventRecord(after_momentum, st) != hipSuccess) return MUON_EHIP;
+  // the fork point: after the accumulated schedule's Gram when this run has
+  // one (the Gram then runs alone instead of beside the other chain's
+  // bandwidth-bound momentum pass, which overlaps the products instead), else
+  // after the momentum passes
+  bool fork_after_gram = false;
+  if (fork != nullptr)
+    for (GroupRun& R : runs)
+      if (R.plan.count > 0 && R.plan.accumulate) fork_after_gram = true;
+  if (fork != nullptr && !fork_after_gram && E.live() && hipEventRecord(fork, st) != hipSuccess) return MUON_EHIP;
   if (flags_nparts >= 0) {
     const int rc = flags_pass(flags_nparts, ws, st, E);
     if (rc != MUON_OK) return rc;
@@ -549,6 +558,7 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
     if (!launch_segments<SymArgs>(grams_as_sym(gs, true), launch_symprod_bf16, st, E.live()) ||
         !E.mark(st, MUON_PHASE_GRAM))
       return MUON_EHIP;
+    if (fork_after_gram && E.live() && hipEventRecord(fork, st) != hipSuccess) return MUON_EHIP;
     // every s x s matrix of the chain keeps only its upper block triangle
     // (the products read the rest transposed), except the final Q, which the
     // combine reads whole
@@ -844,9 +854,12 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   // and an auxiliary one, joined back before returning), so that one chain's
   // launch tails and bandwidth-bound passes overlap the other's matrix-core
   // work.  Groups are dealt to the chains by estimated cost, heaviest first;
-  // the lighter chain starts once the heavier one's momentum pass is done, so
-  // that the critical chain's first, bandwidth-bound pass runs alone (measured
-  // faster than starting both together).
+  // the lighter chain starts once the heavier one's momentum pass and, with
+  // the accumulated schedule, its Gram are done, so that the critical chain's
+  // bandwidth-bound first pass and its Gram run alone and the lighter chain's
+  // momentum pass overlaps the heavier chain's products (measured faster than
+  // starting after the momentum pass, which was faster than starting both
+  // together).
   std::vector<int> live;
   for (int i = 0; i < ngroups; ++i)
     if (runs[i].plan.count > 0) live.push_back(i);
@@ -866,7 +879,7 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   }
   std::lock_guard<std::mutex> lock(aux->mu);
   EventRec E1;
-  rc = run_all(chain[0], C, cfg->eps, ws, norms_out, st, E, aux->fork);  // fork: after chain 0's momentum
+  rc = run_all(chain[0], C, cfg->eps, ws, norms_out, st, E, aux->fork);  // fork: after chain 0's Gram
   if (hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess) return MUON_EHIP;
   // the second chain's momentum passes are the call's last: the flag follows them on that stream
   const int rc1 = rc == MUON_OK ? run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1, nullptr, nparts)
