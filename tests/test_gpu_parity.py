@@ -301,21 +301,24 @@ def test_batched_small_bf16_wide_shapes(mu, shape, steps):
     assert worst <= BF16_TOL
 
 
-@pytest.mark.parametrize("shape", [(96, 96), (128, 512)])  # rows split / columns split over the waves
-def test_batched_small_bf16_past_the_grid(mu, shape):
+# rows split over the waves (three sizes of X in LDS); columns split
+@pytest.mark.parametrize("shape", [(96, 96), (128, 256), (96, 320), (128, 512)])
+@pytest.mark.parametrize("steps", [1, 3])
+def test_batched_small_bf16_past_the_grid(mu, shape, steps):
     """More matrices than the 65,536 workgroups of one launch: each workgroup
     takes a second matrix; samples on both sides of index 65,536 against the
     oracle and every matrix finite."""
     m, n = shape
     count = 70000
-    gen = torch.Generator(device="cuda").manual_seed(m + n)
+    gen = torch.Generator(device="cuda").manual_seed(m + n + steps)
     X = torch.randn((count, m, n), generator=gen, device="cuda").to(torch.bfloat16)
     Y = torch.empty_like(X)
-    mu.muon_ns_batched_small(X, Y, steps=1)
+    print(f"[parity] past the grid {m}x{n} steps {steps}", flush=True)
+    mu.muon_ns_batched_small(X, Y, steps=steps)
     torch.cuda.synchronize()
     assert torch.isfinite(Y.float()).all()
     for b in (0, 1, 65535, 65536, 65537, count - 1):
-        ref, _ = orc.newton_schulz(t64(X[b]), 1)
+        ref, _ = orc.newton_schulz(t64(X[b]), steps)
         assert orc.rel_frobenius(t64(Y[b]), ref) <= BF16_TOL, b
 
 
