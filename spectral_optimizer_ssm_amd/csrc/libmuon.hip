@@ -327,7 +327,8 @@ int flags_pass(long long nparts, char* ws, hipStream_t st, EventRec& E);
 
 // fork: when non-null, recorded on st once the Gram of the accumulated
 // schedule (if any group of this run takes it), else the momentum passes, of
-// these groups have been enqueued.  flags_nparts >= 0: after the momentum
+// these groups have been enqueued (the momentum partial sums are complete by
+// then either way).  flags_nparts >= 0: after the momentum
 // passes, the call's non-finite flag from the first flags_nparts partial sums (every
 // group's partials are complete by then: this run's momentum passes are the
 // call's last ones).
@@ -760,6 +761,7 @@ std::vector<int> list_phases(std::vector<GroupRun>& runs, const NsCoefs& C, floa
 struct Aux {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t partials = nullptr;  // the auxiliary chain's momentum partial sums are complete
   std::mutex mu;  // one fork / join sequence at a time
 };
 
@@ -774,7 +776,8 @@ Aux* aux_for_current_device() {
     Aux* a = new Aux();
     if (hipStreamCreateWithFlags(&a->s, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&a->fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&a->join, hipEventDisableTiming) != hipSuccess) {
+        hipEventCreateWithFlags(&a->join, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&a->partials, hipEventDisableTiming) != hipSuccess) {
       delete a;  // leaves this device on one stream
       return nullptr;
     }
@@ -881,13 +884,19 @@ int step_impl(const muon_group* groups, int ngroups, const muon_ns_cfg* cfg, voi
   EventRec E1;
   rc = run_all(chain[0], C, cfg->eps, ws, norms_out, st, E, aux->fork);  // fork: after chain 0's Gram
   if (hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess) return MUON_EHIP;
-  // the second chain's momentum passes are the call's last: the flag follows them on that stream
-  const int rc1 = rc == MUON_OK ? run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1, nullptr, nparts)
+  // the second chain records `partials` once its momentum passes (the call's
+  // last) are done, at its own fork point; the call's non-finite flag is then
+  // taken on the caller's stream after the first chain's work, which ends
+  // earlier than the second chain's, so the flag pass is off the longer chain
+  const int rc1 = rc == MUON_OK ? run_all(chain[1], C, cfg->eps, ws, norms_out, aux->s, E1, aux->partials)
                                 : MUON_OK;
+  int rc2 = MUON_OK;
+  if (rc == MUON_OK && rc1 == MUON_OK)
+    rc2 = hipStreamWaitEvent(st, aux->partials, 0) != hipSuccess ? MUON_EHIP : flags_pass(nparts, ws, st, E);
   // join even after a failed launch, so that the caller's stream never runs ahead of the auxiliary work
   if (hipEventRecord(aux->join, aux->s) != hipSuccess || hipStreamWaitEvent(st, aux->join, 0) != hipSuccess)
     return MUON_EHIP;
-  return rc != MUON_OK ? rc : rc1;
+  return rc != MUON_OK ? rc : rc1 != MUON_OK ? rc1 : rc2;
 }
 
 // ---- spectral diagnostics ------------------------------------------------------
