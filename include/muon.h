@@ -260,9 +260,11 @@ int muon_ns_orthogonalize_noalloc(const void* G, void* O, int dtype, int m, int 
  * matrix's update direction U from per-block partial sums; the flag is 1 when
  * any of those sums is not finite (a NaN or Inf in G or M, or an overflow),
  * else 0.  The flag lives in the first bytes of the workspace and is written
- * by the call's last kernel on `stream`, so read it only after that stream
- * has been synchronised (this function copies 4 bytes device -> host with
- * hipMemcpy).  A call with no matrices leaves it unchanged.
+ * by a kernel that the call enqueues on `stream` (with two concurrent chains,
+ * after the first chain's work, once the second chain's momentum passes are
+ * done), so read it only after that stream has been synchronised (this
+ * function copies 4 bytes device -> host with hipMemcpy).  A call with no
+ * matrices leaves it unchanged.
  *   workspace     the workspace passed to that call (16-byte aligned)
  *   nonfinite_out host int receiving 0 or 1
  * Returns MUON_EINVAL on null or misaligned pointers, MUON_EHIP if the copy
