@@ -365,11 +365,17 @@ int run_all(std::vector<GroupRun>& runs, const NsCoefs& C, float eps, char* ws, 
   // the fork point: after the accumulated schedule's Gram when this run has
   // one (the Gram then runs alone instead of beside the other chain's
   // bandwidth-bound momentum pass, which overlaps the products instead), else
-  // after the momentum passes
-  bool fork_after_gram = false;
+  // after the momentum passes.  With the spectral cap (its separate apply and
+  // power-step passes lengthen the end of each chain) the earlier fork
+  // measured faster.
+  bool fork_after_gram = false, any_cap = false;
   if (fork != nullptr)
     for (GroupRun& R : runs)
-      if (R.plan.count > 0 && R.plan.accumulate) fork_after_gram = true;
+      if (R.plan.count > 0) {
+        fork_after_gram = fork_after_gram || R.plan.accumulate;
+        any_cap = any_cap || R.plan.cap;
+      }
+  if (any_cap) fork_after_gram = false;
   if (fork != nullptr && !fork_after_gram && E.live() && hipEventRecord(fork, st) != hipSuccess) return MUON_EHIP;
   if (flags_nparts >= 0) {
     const int rc = flags_pass(flags_nparts, ws, st, E);
